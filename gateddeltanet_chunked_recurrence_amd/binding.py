@@ -1,0 +1,188 @@
+"""ctypes binding of include/gdn.h: argument marshalling only.
+
+The functions below take torch tensors that already live on a ROCm device,
+allocate the outputs with torch (device memory plumbing), fill the C argument
+structs with raw device pointers and call the HIP library on torch's current
+stream. No step of the computation runs here. If libgdn_hip.so is missing the
+import of this module's functions fails loudly; there is no fallback.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'libgdn_hip.so')
+
+GDN_OK, GDN_E_INVALID, GDN_E_UNSUPPORTED, GDN_E_WORKSPACE, GDN_E_HIP = 0, -1, -2, -3, -4
+QDQ_OFF, QDQ_E4M3, QDQ_INT8 = 0, 1, 2
+GDN_BF16, GDN_F32 = 0, 1
+
+c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class QdqPolicy(ctypes.Structure):
+    _fields_ = [('state_fmt', c_i32), ('w_fmt', c_i32), ('block_v', c_i32), ('chunk_size', c_i32)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [('B', c_i32), ('T', c_i32), ('Hqk', c_i32), ('Hv', c_i32), ('Dk', c_i32),
+                ('Dv', c_i32), ('num_seqs', c_i32), ('io_dtype', c_i32), ('scale', c_f32),
+                ('policy', QdqPolicy), ('q', c_vp), ('k', c_vp), ('v', c_vp), ('g', c_vp),
+                ('beta', c_vp), ('h0', c_vp), ('cu_seqlens', c_vp), ('o', c_vp), ('ht', c_vp),
+                ('saved', c_vp)]
+
+
+class SavedLayout(ctypes.Structure):
+    _fields_ = [('num_slots', c_i64), ('off_state', c_i64), ('off_state_scale', c_i64),
+                ('off_w', c_i64), ('off_w_scale', c_i64), ('total_bytes', c_i64)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [('fwd', FwdArgs), ('do_', c_vp), ('dht', c_vp), ('grad_dtype', c_i32),
+                ('dq', c_vp), ('dk', c_vp), ('dv', c_vp), ('dg', c_vp), ('dbeta', c_vp),
+                ('dh0', c_vp), ('workspace', c_vp), ('workspace_bytes', c_sz)]
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libgdn_hip.so (built in-tree by build.py); raise if it is absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f'{LIB_PATH} is missing: build it with '
+                           'python -m gateddeltanet_chunked_recurrence_amd.build')
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_abi_version.restype = c_i32
+    for name, argt in (('gdn_chunk_fwd', [ctypes.POINTER(FwdArgs), c_vp]),
+                       ('gdn_chunk_bwd', [ctypes.POINTER(BwdArgs), c_vp]),
+                       ('gdn_saved_layout', [ctypes.POINTER(FwdArgs), ctypes.POINTER(SavedLayout)]),
+                       ('gdn_qdq_state', [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,
+                                          c_i32, c_vp])):
+        f = getattr(lib, name)
+        f.argtypes = argt
+        f.restype = c_i32
+    lib.gdn_saved_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.gdn_saved_bytes.restype = c_sz
+    lib.gdn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdArgs)]
+    lib.gdn_bwd_workspace_bytes.restype = c_sz
+    _LIB = lib
+    return lib
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f'gdn status {status}: {msg}')
+        self.status = status
+
+
+def _check(status):
+    if status != GDN_OK:
+        raise GdnError(status, load_library().gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v,
+                  o=None, ht=None, saved=None, num_seqs=None):
+    """Fill the forward argument struct from tensor shapes and pointers."""
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    if num_seqs is None:
+        num_seqs = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    io = GDN_F32 if q.dtype == torch.float32 else GDN_BF16
+    a = FwdArgs(B=B, T=T, Hqk=Hqk, Hv=Hv, Dk=Dk, Dv=Dv, num_seqs=num_seqs, io_dtype=io,
+                scale=float(1.0 / math.sqrt(Dk) if scale is None else scale),
+                policy=QdqPolicy(state_fmt, w_fmt, block_v, 64))
+    for name, t in (('q', q), ('k', k), ('v', v), ('g', g), ('beta', beta), ('h0', h0),
+                    ('cu_seqlens', cu_seqlens), ('o', o), ('ht', ht), ('saved', saved)):
+        setattr(a, name, _ptr(t))
+    return a
+
+
+def saved_layout(args):
+    lay = SavedLayout()
+    _check(load_library().gdn_saved_layout(ctypes.byref(args), ctypes.byref(lay)))
+    return lay
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_fmt=QDQ_OFF,
+                  w_fmt=QDQ_OFF, block_v=64, output_final_state=True, save_for_backward=False):
+    """Chunked forward on q's device and torch's current stream.
+
+    q, k [B, T, Hqk, Dk], v [B, T, Hv, Dv] (bf16, or FP32 with Dk = 64);
+    g, beta [B, T, Hv] FP32; h0 [N, Hv, Dk, Dv] FP32 or None; cu_seqlens int32
+    [N + 1] (B = 1) or None. Returns (o, ht or None, saved uint8 buffer or None).
+    """
+    lib = load_library()
+    dev = q.device
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    o = torch.empty(B, T, Hv, Dv, dtype=q.dtype, device=dev)
+    ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
+    a = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v, o, ht)
+    saved = None
+    if save_for_backward:
+        nbytes = lib.gdn_saved_bytes(ctypes.byref(a))
+        if nbytes == 0:
+            _check(lib.gdn_chunk_fwd(ctypes.byref(a), None))     # reports the shape error
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        a.saved = _ptr(saved)
+    _check(lib.gdn_chunk_fwd(ctypes.byref(a), _stream(dev)))
+    return o, ht, saved
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu_seqlens=None,
+                  state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, grad_dtype=None):
+    """Backward of gdn_chunk_fwd (identity straight-through at both QDQ sites)
+    from the forward's `saved` buffer. Returns dict dq, dk, dv, dg, dbeta, dh0."""
+    lib = load_library()
+    dev = q.device
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    out = dict(dq=torch.empty(B, T, Hqk, Dk, dtype=gd, device=dev),
+               dk=torch.empty(B, T, Hqk, Dk, dtype=gd, device=dev),
+               dv=torch.empty(B, T, Hv, Dv, dtype=gd, device=dev),
+               dg=torch.empty(B, T, Hv, dtype=torch.float32, device=dev),
+               dbeta=torch.empty(B, T, Hv, dtype=torch.float32, device=dev),
+               dh0=torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev)
+               if h0 is not None else None)
+    fa = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v,
+                       saved=saved)
+    a = BwdArgs(fwd=fa, do_=_ptr(do), dht=_ptr(dht),
+                grad_dtype=GDN_F32 if gd == torch.float32 else GDN_BF16,
+                dq=_ptr(out['dq']), dk=_ptr(out['dk']), dv=_ptr(out['dv']), dg=_ptr(out['dg']),
+                dbeta=_ptr(out['dbeta']), dh0=_ptr(out['dh0']))
+    nbytes = lib.gdn_bwd_workspace_bytes(ctypes.byref(a))
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = ws.numel()
+    _check(lib.gdn_chunk_bwd(ctypes.byref(a), _stream(dev)))
+    return out
+
+
+def gdn_qdq_state(x, fmt, block_v, return_codes=False, out=None):
+    """QDQ of FP32 states x [n, Dk, Dv] per [Dk, block_v] tile.
+    Returns (y, scales [n, Dv / block_v], codes uint8 or None)."""
+    lib = load_library()
+    n, Dk, Dv = x.shape
+    y = torch.empty_like(x) if out is None else out
+    scales = torch.empty(n, Dv // block_v if block_v and Dv % block_v == 0 else 1,
+                         dtype=torch.float32, device=x.device)
+    codes = torch.empty(n, Dk, Dv, dtype=torch.uint8, device=x.device) if return_codes else None
+    _check(lib.gdn_qdq_state(_ptr(x), _ptr(y), _ptr(scales), _ptr(codes), n, Dk, Dv, block_v, fmt,
+                             _stream(x.device)))
+    return y, scales, codes

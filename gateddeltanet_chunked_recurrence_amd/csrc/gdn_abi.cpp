@@ -1,0 +1,274 @@
+// C ABI of the chunked gated delta rule library (declarations and contract in
+// include/gdn.h). This layer validates every argument before any launch,
+// reports failures through a status code and a thread-local message, and
+// forwards to the HIP launchers. It allocates nothing and never synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+bool valid_fmt(int32_t f) { return f == GDN_QDQ_OFF || f == GDN_QDQ_E4M3 || f == GDN_QDQ_INT8; }
+
+// Shape and policy checks shared by forward and backward.
+gdn_status check_fwd_shape(const gdn_fwd_args* a) {
+  if (!a) return fail(GDN_E_INVALID, "argument struct is NULL");
+  const gdn_qdq_policy& p = a->policy;
+  if (p.chunk_size != 64)
+    return fail(GDN_E_UNSUPPORTED, "chunk_size %d: only 64 is supported", p.chunk_size);
+  if (!valid_fmt(p.state_fmt) || !valid_fmt(p.w_fmt))
+    return fail(GDN_E_UNSUPPORTED, "unknown QDQ format (state %d, w %d): use 0 off, 1 E4M3, 2 INT8",
+                p.state_fmt, p.w_fmt);
+  if (a->B < 0 || a->T < 0 || a->Hqk <= 0 || a->Hv <= 0)
+    return fail(GDN_E_INVALID, "bad sizes B=%d T=%d Hqk=%d Hv=%d", a->B, a->T, a->Hqk, a->Hv);
+  if (a->Hv % a->Hqk != 0)
+    return fail(GDN_E_INVALID, "Hv (%d) must be a multiple of Hqk (%d)", a->Hv, a->Hqk);
+  if (a->Hv > 65535) return fail(GDN_E_UNSUPPORTED, "Hv %d exceeds 65535", a->Hv);
+  if (a->Dk != 64 && a->Dk != 128)
+    return fail(GDN_E_UNSUPPORTED, "Dk %d: supported 64, 128", a->Dk);
+  if (a->Dv != 64 && a->Dv != 128 && a->Dv != 256)
+    return fail(GDN_E_UNSUPPORTED, "Dv %d: supported 64, 128, 256", a->Dv);
+  if (a->io_dtype != GDN_BF16 && a->io_dtype != GDN_F32)
+    return fail(GDN_E_INVALID, "io_dtype %d: use 0 bf16 or 1 f32", a->io_dtype);
+  if (a->io_dtype == GDN_F32 && a->Dk != 64)
+    return fail(GDN_E_UNSUPPORTED, "FP32 inputs are built for Dk = 64 only (got %d)", a->Dk);
+  if (p.state_fmt != GDN_QDQ_OFF) {
+    if (p.block_v != 16 && p.block_v != 32 && p.block_v != 64)
+      return fail(GDN_E_UNSUPPORTED, "block_v %d: supported 16, 32, 64", p.block_v);
+    if (a->Dv % p.block_v != 0)
+      return fail(GDN_E_INVALID, "block_v %d does not divide Dv %d", p.block_v, a->Dv);
+  }
+  if (!std::isfinite(a->scale)) return fail(GDN_E_INVALID, "scale is not finite");
+  if (a->cu_seqlens) {
+    if (a->B != 1) return fail(GDN_E_INVALID, "cu_seqlens needs B == 1 (got %d)", a->B);
+    if (a->num_seqs < 1) return fail(GDN_E_INVALID, "num_seqs %d < 1 with cu_seqlens", a->num_seqs);
+  } else if (a->num_seqs != a->B) {
+    return fail(GDN_E_INVALID, "num_seqs (%d) must equal B (%d) without cu_seqlens",
+                a->num_seqs, a->B);
+  }
+  if (a->num_seqs > 65535) return fail(GDN_E_UNSUPPORTED, "num_seqs %d exceeds 65535", a->num_seqs);
+  if ((int64_t)a->B * a->T > INT32_MAX / 2)
+    return fail(GDN_E_UNSUPPORTED, "B*T = %lld tokens exceeds 2^30", (long long)a->B * a->T);
+  return GDN_OK;
+}
+
+gdn_status check_fwd_ptrs(const gdn_fwd_args* a, bool need_out) {
+  const bool any = (int64_t)a->B * a->T > 0;
+  const struct { const void* p; const char* name; bool required; } ptrs[] = {
+      {a->q, "q", any},        {a->k, "k", any},      {a->v, "v", any},
+      {a->g, "g", any},        {a->beta, "beta", any}, {a->o, "o", need_out && any},
+      {a->h0, "h0", false},    {a->ht, "ht", false},  {a->cu_seqlens, "cu_seqlens", false},
+      {a->saved, "saved", false}};
+  for (const auto& e : ptrs) {
+    if (e.required && !e.p) return fail(GDN_E_INVALID, "%s is NULL", e.name);
+    if (e.p && !aligned16(e.p)) return fail(GDN_E_INVALID, "%s is not 16-byte aligned", e.name);
+  }
+  return GDN_OK;
+}
+
+gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
+  gdn_saved_layout_t L{};
+  const int64_t tokens = (int64_t)a->B * a->T;
+  L.num_slots = a->num_seqs + ceil_div(tokens, 64);
+  const int64_t per_state = (int64_t)a->Hv * a->Dk * a->Dv;
+  const bool sq = a->policy.state_fmt != GDN_QDQ_OFF, wq = a->policy.w_fmt != GDN_QDQ_OFF;
+  int64_t off = 0;
+  L.off_state = off;
+  off = round256(off + L.num_slots * per_state * (sq ? 1 : 4));
+  L.off_state_scale = off;
+  off = round256(off + (sq ? L.num_slots * a->Hv * (a->Dv / a->policy.block_v) * 4 : 0));
+  L.off_w = off;
+  off = round256(off + (wq ? tokens * a->Hv * a->Dk : 0));
+  L.off_w_scale = off;
+  off = round256(off + (wq ? L.num_slots * a->Hv * 4 : 0));
+  L.total_bytes = off;
+  return L;
+}
+
+gdn::FwdKernelArgs kernel_args(const gdn_fwd_args* a, void* saved) {
+  gdn::FwdKernelArgs k{};
+  k.q = a->q;
+  k.k = a->k;
+  k.v = a->v;
+  k.g = a->g;
+  k.beta = a->beta;
+  k.h0 = a->h0;
+  k.cu_seqlens = a->cu_seqlens;
+  k.o = a->o;
+  k.ht = a->ht;
+  if (saved) {
+    const gdn_saved_layout_t L = layout_of(a);
+    char* base = static_cast<char*>(saved);
+    if (a->policy.state_fmt != GDN_QDQ_OFF) {
+      k.s_codes = reinterpret_cast<uint8_t*>(base + L.off_state);
+      k.s_scale = reinterpret_cast<float*>(base + L.off_state_scale);
+    } else {
+      k.s_f32 = reinterpret_cast<float*>(base + L.off_state);
+    }
+    if (a->policy.w_fmt != GDN_QDQ_OFF) {
+      k.w_codes = reinterpret_cast<uint8_t*>(base + L.off_w);
+      k.w_scale = reinterpret_cast<float*>(base + L.off_w_scale);
+    }
+  }
+  k.T = a->T;
+  k.Hqk = a->Hqk;
+  k.Hv = a->Hv;
+  k.Dv = a->Dv;
+  k.block_v = a->policy.state_fmt != GDN_QDQ_OFF ? a->policy.block_v : 64;
+  k.scale = a->scale;
+  return k;
+}
+
+gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
+  gdn::FwdConfig c{};
+  c.Dk = a->Dk;
+  c.Dv = a->Dv;
+  c.N = a->num_seqs;
+  c.Hv = a->Hv;
+  c.state_fmt = a->policy.state_fmt;
+  c.w_fmt = a->policy.w_fmt;
+  c.f32_io = a->io_dtype == GDN_F32;
+  return c;
+}
+
+gdn_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err; }
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_saved_layout(const gdn_fwd_args* a, gdn_saved_layout_t* out) {
+  gdn_status s = check_fwd_shape(a);
+  if (s != GDN_OK) return s;
+  if (!out) return fail(GDN_E_INVALID, "layout output is NULL");
+  *out = layout_of(a);
+  return GDN_OK;
+}
+
+size_t gdn_saved_bytes(const gdn_fwd_args* a) {
+  if (check_fwd_shape(a) != GDN_OK) return 0;
+  return (size_t)layout_of(a).total_bytes;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) {
+  gdn_status s = check_fwd_shape(a);
+  if (s != GDN_OK) return s;
+  if ((s = check_fwd_ptrs(a, true)) != GDN_OK) return s;
+  if ((int64_t)a->B * a->T == 0) return GDN_OK;
+  return hip_status(gdn::launch_fwd(fwd_config(a), kernel_args(a, a->saved),
+                                    static_cast<hipStream_t>(stream)),
+                    "gdn_chunk_fwd launch");
+}
+
+size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a) {
+  if (!a || check_fwd_shape(&a->fwd) != GDN_OK) return 0;
+  const gdn_saved_layout_t L = layout_of(&a->fwd);
+  const int64_t tokens = (int64_t)a->fwd.B * a->fwd.T;
+  const int64_t dstate = round256(L.num_slots * a->fwd.Hv * a->fwd.Dk * a->fwd.Dv * 4);
+  const int64_t dqk = round256(tokens * a->fwd.Hv * 2 * a->fwd.Dk * 4);
+  return (size_t)(dstate + dqk);
+}
+
+gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
+  if (!a) return fail(GDN_E_INVALID, "argument struct is NULL");
+  gdn_status s = check_fwd_shape(&a->fwd);
+  if (s != GDN_OK) return s;
+  if ((s = check_fwd_ptrs(&a->fwd, false)) != GDN_OK) return s;
+  const bool any = (int64_t)a->fwd.B * a->fwd.T > 0;
+  if (a->grad_dtype != GDN_F32 && a->grad_dtype != a->fwd.io_dtype)
+    return fail(GDN_E_INVALID, "grad_dtype must be FP32 or the io dtype");
+  const struct { const void* p; const char* name; bool required; } ptrs[] = {
+      {a->fwd.saved, "saved", any}, {a->do_, "do", any},  {a->dq, "dq", any},
+      {a->dk, "dk", any},           {a->dv, "dv", any},   {a->dg, "dg", any},
+      {a->dbeta, "dbeta", any},     {a->dht, "dht", false}, {a->dh0, "dh0", false},
+      {a->workspace, "workspace", false}};
+  for (const auto& e : ptrs) {
+    if (e.required && !e.p) return fail(GDN_E_INVALID, "%s is NULL", e.name);
+    if (e.p && !aligned16(e.p)) return fail(GDN_E_INVALID, "%s is not 16-byte aligned", e.name);
+  }
+  const size_t need = gdn_bwd_workspace_bytes(a);
+  if (any && (!a->workspace || a->workspace_bytes < need))
+    return fail(GDN_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", a->workspace_bytes, need);
+  if (!any) return GDN_OK;
+  const gdn_saved_layout_t L = layout_of(&a->fwd);
+  const int64_t tokens = (int64_t)a->fwd.B * a->fwd.T;
+  gdn::BwdKernelArgs k{};
+  k.f = kernel_args(&a->fwd, a->fwd.saved);
+  k.dout = a->do_;
+  k.dht = a->dht;
+  k.dq = a->dq;
+  k.dk = a->dk;
+  k.dv = a->dv;
+  k.dg = a->dg;
+  k.dbeta = a->dbeta;
+  k.dh0 = a->dh0;
+  char* ws = static_cast<char*>(a->workspace);
+  k.ws_dstate = reinterpret_cast<float*>(ws);
+  k.ws_dqk = reinterpret_cast<float*>(ws + round256(L.num_slots * a->fwd.Hv * a->fwd.Dk *
+                                                    a->fwd.Dv * 4));
+  k.grad_f32 = a->grad_dtype == GDN_F32;
+  k.total_tokens = (int32_t)tokens;
+  k.num_slots = (int32_t)L.num_slots;
+  gdn::BwdConfig c{};
+  c.Dk = a->fwd.Dk;
+  c.Dv = a->fwd.Dv;
+  c.N = a->fwd.num_seqs;
+  c.Hv = a->fwd.Hv;
+  c.Hqk = a->fwd.Hqk;
+  c.state_fmt = a->fwd.policy.state_fmt;
+  c.w_fmt = a->fwd.policy.w_fmt;
+  c.f32_io = a->fwd.io_dtype == GDN_F32;
+  return hip_status(gdn::launch_bwd(c, k, static_cast<hipStream_t>(stream)),
+                    "gdn_chunk_bwd launch");
+}
+
+gdn_status gdn_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
+                         int64_t n_states, int32_t Dk, int32_t Dv, int32_t block_v,
+                         int32_t fmt, void* stream) {
+  if (fmt != GDN_QDQ_E4M3 && fmt != GDN_QDQ_INT8)
+    return fail(GDN_E_UNSUPPORTED, "gdn_qdq_state format %d: use 1 E4M3 or 2 INT8", fmt);
+  if (n_states < 0 || Dk < 1 || Dk > 1024 || Dv < 1)
+    return fail(GDN_E_INVALID, "bad sizes n_states=%lld Dk=%d Dv=%d", (long long)n_states, Dk, Dv);
+  if (block_v != 16 && block_v != 32 && block_v != 64 && block_v != 128 && block_v != 256)
+    return fail(GDN_E_UNSUPPORTED, "block_v %d: supported 16, 32, 64, 128, 256", block_v);
+  if (Dv % block_v != 0) return fail(GDN_E_INVALID, "block_v %d does not divide Dv %d", block_v, Dv);
+  if (n_states * (Dv / block_v) > INT32_MAX)
+    return fail(GDN_E_UNSUPPORTED, "too many tiles");
+  if (n_states == 0) return GDN_OK;
+  if (!x || !y) return fail(GDN_E_INVALID, "x or y is NULL");
+  const void* ps[] = {x, y, scales, codes};
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return fail(GDN_E_INVALID, "pointer is not 16-byte aligned");
+  return hip_status(gdn::launch_qdq_state(x, y, scales, codes, n_states, Dk, Dv, block_v, fmt,
+                                          static_cast<hipStream_t>(stream)),
+                    "gdn_qdq_state launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Device helpers shared by the gfx950 kernels: bf16 MFMA tiles, hi/lo
+// operand splitting, the FP32 QDQ arithmetic and wave reductions.
+//
+// MFMA tile used throughout: v_mfma_f32_16x16x32_bf16 (one wave, 64 lanes).
+// Lane l, r16 = l & 15, grp = l >> 4:
+//   A (16 x 32, M x K): lane holds A[r16][8*grp + e], e = 0..7
+//   B (32 x 16, K x N): lane holds B[8*grp + e][r16]
+//   C (16 x 16):        lane holds C[4*grp + i][r16], i = 0..3
+// Any permutation of the K index that A and B share gives the same product;
+// the kernels use that to feed accumulator tiles (C layout) straight back as
+// B operands ("paired-tile" K order, see pack_pair below).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int CHUNK = 64;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// float -> bf16 with round-to-nearest-even; exact split x = hi + lo + O(2^-17 x).
+__device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
+__device__ __forceinline__ float from_bf16(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ void split2(float x, bf16& hi, bf16& lo) {
+  hi = to_bf16(x);
+  lo = to_bf16(x - from_bf16(hi));
+}
+
+// Paired-tile K order: a 32-deep K step built from two vertically adjacent
+// accumulator tiles t0 (rows 0..15 of the step) and t1 (rows 16..31). Lane
+// group grp holds rows 4*grp..4*grp+3 of each, so B element e maps to K row
+//   e < 4: 4*grp + e        e >= 4: 16 + 4*grp + (e - 4).
+// The matching A operand reads A[m][k0 + 4*grp .. +3] and A[m][k0 + 16 + 4*grp .. +3].
+__device__ __forceinline__ bf16x8 pack_pair(const f32x4& t0, const f32x4& t1) {
+  bf16x8 r;
+  r[0] = to_bf16(t0[0]); r[1] = to_bf16(t0[1]); r[2] = to_bf16(t0[2]); r[3] = to_bf16(t0[3]);
+  r[4] = to_bf16(t1[0]); r[5] = to_bf16(t1[1]); r[6] = to_bf16(t1[2]); r[7] = to_bf16(t1[3]);
+  return r;
+}
+__device__ __forceinline__ void pack_pair_split(const f32x4& t0, const f32x4& t1,
+                                                bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bf16 h0, l0, h1, l1;
+    split2(t0[e], h0, l0);
+    split2(t1[e], h1, l1);
+    hi[e] = h0; lo[e] = l0; hi[e + 4] = h1; lo[e + 4] = l1;
+  }
+}
+
+// LDS operand loads (bf16 elements, row-major with row stride `ld`).
+// Natural K order: 8 contiguous elements at A[row][k0 + 8*grp].
+__device__ __forceinline__ bf16x8 lds_nat(const bf16* base, int row, int ld, int k0, int grp) {
+  return *reinterpret_cast<const bf16x8*>(base + row * ld + k0 + 8 * grp);
+}
+// Paired-tile K order: elements k0 + 4*grp + 0..3 and k0 + 16 + 4*grp + 0..3.
+__device__ __forceinline__ bf16x8 lds_pair(const bf16* base, int row, int ld, int k0, int grp) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(base + row * ld + k0 + 4 * grp);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(base + row * ld + k0 + 16 + 4 * grp);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, WAVE));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, WAVE);
+  return x;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const float y = __shfl_up(x, off, WAVE);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------- QDQ (FP32)
+// Formats as in gdn.h: 1 = E4M3FN (+-448), 2 = INT8 ([-127, 127]).
+template <int FMT> struct QdqFmt;
+template <> struct QdqFmt<1> { static constexpr float qmax = 448.f; };
+template <> struct QdqFmt<2> { static constexpr float qmax = 127.f; };
+
+// Round to the nearest E4M3FN value, ties to even, saturating at +-448.
+// Normal range (|y| >= 2^-6): keep 3 mantissa bits with an integer RNE on
+// the FP32 bit pattern. Below: the subnormal grid has step 2^-9, and
+// y * 2^9 is exact, so rintf gives the RNE code.
+__device__ __forceinline__ float round_e4m3(float y) {
+  const float a = fabsf(y);
+  if (a >= 448.f) return copysignf(448.f, y);
+  if (a < 0.015625f) return rintf(y * 512.f) * 0.001953125f;
+  uint32_t b = __float_as_uint(a);
+  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+  return copysignf(__uint_as_float(b), y);
+}
+__device__ __forceinline__ float round_int8(float y) {
+  return fminf(fmaxf(rintf(y), -127.f), 127.f);
+}
+template <int FMT> __device__ __forceinline__ float round_code(float y) {
+  if constexpr (FMT == 1) return round_e4m3(y); else return round_int8(y);
+}
+// Scale from the tile amax: d = max(fl(amax / qmax), 2^-126) (IEEE division).
+template <int FMT> __device__ __forceinline__ float qdq_scale(float amax) {
+  const float d = amax / QdqFmt<FMT>::qmax;
+  return fmaxf(d, 1.17549435e-38f);
+}
+// One-byte code: E4M3FN bit pattern of an on-grid value, or int8.
+template <int FMT> __device__ __forceinline__ uint8_t code_byte(float c) {
+  if constexpr (FMT == 2) {
+    return static_cast<uint8_t>(static_cast<int8_t>(c));
+  } else {
+    const uint32_t s = (__float_as_uint(c) >> 24) & 0x80u;
+    const float a = fabsf(c);
+    uint32_t mag;
+    if (a < 0.015625f) {
+      mag = static_cast<uint32_t>(a * 512.f);            // subnormal: m / 8 * 2^-6
+    } else {
+      const uint32_t b = __float_as_uint(a);
+      const uint32_t e = ((b >> 23) & 0xFFu) - 127u + 7u;  // biased E4M3 exponent
+      mag = (e << 3) | ((b >> 20) & 7u);
+    }
+    return static_cast<uint8_t>(s | mag);
+  }
+}
+
+}  // namespace gdn

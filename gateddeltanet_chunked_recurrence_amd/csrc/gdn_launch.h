@@ -1,0 +1,62 @@
+// Internal launch interface between the C-ABI layer (gdn_abi.cpp) and the
+// HIP kernels. Plain C types only; all pointers are device pointers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct FwdKernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* h0;            // nullable
+  const int32_t* cu_seqlens;  // nullable
+  void* o;
+  float* ht;                  // nullable
+  uint8_t* s_codes;           // saved state codes (state QDQ on), nullable
+  float* s_f32;               // saved FP32 state (state QDQ off), nullable
+  float* s_scale;             // saved state scales, nullable
+  uint8_t* w_codes;           // saved W codes (W QDQ on), nullable
+  float* w_scale;             // saved W scales, nullable
+  int32_t T;                  // tokens per sequence (no cu_seqlens)
+  int32_t Hqk, Hv, Dv, block_v;
+  float scale;
+};
+
+struct FwdConfig {
+  int Dk, Dv, N, Hv, state_fmt, w_fmt, f32_io;
+};
+
+hipError_t launch_fwd(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
+
+struct BwdKernelArgs {
+  FwdKernelArgs f;            // forward inputs + saved buffers (read only here)
+  const void* dout;
+  const float* dht;           // nullable
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;                 // nullable
+  float* ws_dstate;           // [num_slots, Hv, Dk, Dv] FP32: dS entering each chunk's end
+  float* ws_dqk;              // [B*T, Hv, 2, Dk] FP32 per-value-head dq, dk before the group sum
+  int32_t grad_f32;
+  int32_t total_tokens;
+  int32_t num_slots;
+};
+
+struct BwdConfig {
+  int Dk, Dv, N, Hv, Hqk, state_fmt, w_fmt, f32_io;
+};
+
+hipError_t launch_bwd(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+
+hipError_t launch_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
+                            int64_t n_states, int Dk, int Dv, int block_v, int fmt,
+                            hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,164 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked gated delta rule with dynamic
+ * fake quantize-dequantize (QDQ) of the recurrent state and of the WY factor W.
+ *
+ * What is computed (the pages print no formulas; the readings are stated
+ * here and checked against a float64 oracle):
+ *   "[1/4] GDN state/W QAT foundation", section "What does this PR do?":
+ *   GatedDeltaNet chunked training path, chunk size 64, exact triangular
+ *   solve, dynamic FP8 E4M3 fake QDQ at the state and WY-activation (W) sites,
+ *   identity straight-through gradients, the forward's quantized W saved for
+ *   the backward, unsupported formats rejected.
+ *   "[2/4] GDN/KDA decode QAT with INT8 recurrent state", section "What does
+ *   this PR do?": signed symmetric dynamic INT8 state with per-head
+ *   [Dk, block_v] scales, zero point zero, codes [-127, 127], nearest-even
+ *   rounding; section "Testing": division by a scale is multiplication by
+ *   its FP32-rounded reciprocal.
+ *
+ * Per (sequence, value head h) and chunk of n <= 64 tokens with incoming
+ * state S (Dk x Dv, FP32):
+ *   gamma_i = chunk-local cumsum of g;  Gam_ij = exp(gamma_i - gamma_j), i >= j
+ *   L_ij = beta_i (k_i . k_j) Gam_ij (i > j);  T = (I + L)^-1 diag(beta)
+ *   W = T diag(exp(gamma)) K;  U = T V
+ *   Wq = QDQ_W(W)  (one scale per sequence, chunk and head over [n, Dk])
+ *   Sq = QDQ_S(S)  (one scale per [Dk, block_v] tile)
+ *   Vnew = U - Wq Sq
+ *   O = scale (diag(exp(gamma)) Q Sq + ((Q K^T) * Gam) Vnew)
+ *   S <- exp(gamma_n) Sq + (diag(exp(gamma_n - gamma)) K)^T Vnew
+ * ht is the final S (not quantized). Grouped heads: value head h reads
+ * query/key head h / (Hv / Hqk).
+ * QDQ of a tile x (FP32):  d = max(fl(max|x| / q_max), 2^-126);
+ *   r = fl(1/d);  c_i = RNE(fl(x_i * r)) on the code grid (E4M3FN, +-448,
+ *   saturating; or integers clamped to [-127, 127]);  out_i = fl(c_i * d).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
+ *     16-byte aligned. The caller allocates and owns every buffer; the library
+ *     allocates nothing, keeps no state between calls, never synchronizes,
+ *     and enqueues work only on `stream` (a hipStream_t; NULL = default).
+ *   - Every argument check runs before any launch. A failed check returns a
+ *     negative gdn_status, launches nothing and sets a message readable with
+ *     gdn_last_error() (thread-local). There is no fallback path.
+ *   - Errors raised by the HIP runtime at launch return GDN_E_HIP; faults
+ *     inside a kernel surface asynchronously on the stream.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_E_INVALID = -1,      /* malformed argument: NULL, misaligned, bad shape */
+  GDN_E_UNSUPPORTED = -2,  /* well formed but outside what is built          */
+  GDN_E_WORKSPACE = -3,    /* workspace missing or too small                 */
+  GDN_E_HIP = -4           /* HIP runtime error at launch                    */
+} gdn_status;
+
+typedef enum { GDN_QDQ_OFF = 0, GDN_QDQ_E4M3 = 1, GDN_QDQ_INT8 = 2 } gdn_qdq_fmt;
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* QDQ policy ("[1/4]", "Usage": quantizer cfg + linear_attention policy). */
+typedef struct {
+  int32_t state_fmt;   /* gdn_qdq_fmt at the state site                      */
+  int32_t w_fmt;       /* gdn_qdq_fmt at the W site                          */
+  int32_t block_v;     /* state scale tile width: 16, 32, 64 or 128; divides Dv
+                          (ignored when state_fmt == OFF)                    */
+  int32_t chunk_size;  /* must be 64                                         */
+} gdn_qdq_policy;
+
+/* Forward arguments. Shapes: without cu_seqlens there are N = B sequences of
+ * T tokens; with cu_seqlens B must be 1, T is the packed length and N =
+ * num_seqs. Sizes: Dk in {64, 128}; Dv in {64, 128, 256}; Hv % Hqk == 0.
+ * io_dtype GDN_F32 needs Dk == 64. */
+typedef struct {
+  int32_t B, T, Hqk, Hv, Dk, Dv;
+  int32_t num_seqs;            /* N (must equal B without cu_seqlens)         */
+  int32_t io_dtype;            /* gdn_dtype of q, k, v and o                  */
+  float scale;                 /* output scale (1/sqrt(Dk) is the usual one)  */
+  gdn_qdq_policy policy;
+  const void* q;               /* [B, T, Hqk, Dk] io_dtype                    */
+  const void* k;               /* [B, T, Hqk, Dk] io_dtype                    */
+  const void* v;               /* [B, T, Hv, Dv]  io_dtype                    */
+  const float* g;              /* [B, T, Hv] log-gate, g <= 0                 */
+  const float* beta;           /* [B, T, Hv] write strength                   */
+  const float* h0;             /* [N, Hv, Dk, Dv] initial state, or NULL = 0  */
+  const int32_t* cu_seqlens;   /* [N + 1] offsets (device), or NULL           */
+  void* o;                     /* out [B, T, Hv, Dv] io_dtype                 */
+  float* ht;                   /* out [N, Hv, Dk, Dv] final state, or NULL    */
+  void* saved;                 /* out: gdn_saved_bytes() bytes for the
+                                  backward (layout gdn_saved_layout), or NULL */
+} gdn_fwd_args;
+
+/* Layout of the `saved` buffer, in bytes from its start. Chunk c of sequence
+ * n (sequence-relative) uses slot n + bos_n / 64 + c (bos_n = first token of
+ * n), so num_slots = N + ceil(B*T / 64).
+ *   state:  state_fmt != OFF: quantized state codes Sq, one byte each
+ *           (E4M3FN bit pattern, or int8), [num_slots, Hv, Dk, Dv];
+ *           state_fmt == OFF: the state S in FP32, same shape.
+ *   state_scale: FP32 d of each tile, [num_slots, Hv, Dv / block_v]
+ *           (state_fmt != OFF only, else 0 bytes).
+ *   w:      w_fmt != OFF: W codes, one byte each, token-major
+ *           [B*T, Hv, Dk]; 0 bytes when w_fmt == OFF (the backward rebuilds W).
+ *   w_scale: FP32 d of each W tile, [num_slots, Hv] (w_fmt != OFF only).
+ * Slots no chunk uses are left unwritten. */
+typedef struct {
+  int64_t num_slots;
+  int64_t off_state, off_state_scale, off_w, off_w_scale;
+  int64_t total_bytes;
+} gdn_saved_layout_t;
+
+gdn_status gdn_saved_layout(const gdn_fwd_args* a, gdn_saved_layout_t* out);
+size_t gdn_saved_bytes(const gdn_fwd_args* a);
+
+/* Chunked forward. Writes o, and ht / saved when not NULL. */
+gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
+
+/* Backward arguments: the forward's arguments and `saved`, plus upstream
+ * gradients. Identity straight-through at both QDQ sites; the saved Wq and
+ * Sq are the values used in every product. grad_dtype applies to dq, dk, dv
+ * (GDN_F32 or io_dtype). */
+typedef struct {
+  gdn_fwd_args fwd;            /* same values as the forward call; fwd.o,
+                                  fwd.ht are not read; fwd.saved must hold the
+                                  forward's saved buffer                      */
+  const void* do_;             /* [B, T, Hv, Dv] io_dtype                     */
+  const float* dht;            /* [N, Hv, Dk, Dv] or NULL (= 0)               */
+  int32_t grad_dtype;          /* gdn_dtype of dq, dk, dv                     */
+  void* dq;                    /* out [B, T, Hqk, Dk] (summed over the group) */
+  void* dk;                    /* out [B, T, Hqk, Dk]                         */
+  void* dv;                    /* out [B, T, Hv, Dv]                          */
+  float* dg;                   /* out [B, T, Hv]                              */
+  float* dbeta;                /* out [B, T, Hv]                              */
+  float* dh0;                  /* out [N, Hv, Dk, Dv], or NULL                */
+  void* workspace;             /* gdn_bwd_workspace_bytes() bytes, device     */
+  size_t workspace_bytes;
+} gdn_bwd_args;
+
+size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a);
+gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream);
+
+/* Standalone state QDQ (the function used at the state site), bit-exact to
+ * the FP32 definition above. x, y: [n_states, Dk, Dv] FP32 (y may alias x);
+ * one scale per [Dk, block_v] tile of each state. scales ([n_states,
+ * Dv / block_v] FP32) and codes ([n_states, Dk, Dv] bytes) are optional
+ * outputs (NULL to skip). fmt must be E4M3 or INT8. Dk in [1, 1024],
+ * block_v in {16, 32, 64, 128, 256} dividing Dv. */
+gdn_status gdn_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
+                         int64_t n_states, int32_t Dk, int32_t Dv, int32_t block_v,
+                         int32_t fmt, void* stream);
+
+const char* gdn_last_error(void);
+int32_t gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

@@ -1,0 +1,129 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/gdn.h declares, and rejects bad arguments before any launch with the
+documented status codes ("explicit early rejection" and "rejected before
+launch": "[1/4] GDN state/W QAT foundation", "What does this PR do?" and
+"Testing"). No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gateddeltanet_chunked_recurrence_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, 'include', 'gdn.h')).read()
+    src = re.sub(r'/\*.*?\*/', '', src, flags=re.S)
+    return sorted(set(re.findall(r'^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(', src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert {'gdn_chunk_fwd', 'gdn_chunk_bwd', 'gdn_qdq_state'} <= set(names)
+    lib = B.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gdn_abi_version() == 1
+
+
+def _args(**kw):
+    fake = ctypes.c_void_p(0x10000)          # aligned, never dereferenced on these paths
+    a = B.FwdArgs(B=1, T=128, Hqk=2, Hv=4, Dk=128, Dv=128, num_seqs=1, io_dtype=B.GDN_BF16,
+                  scale=0.1, policy=B.QdqPolicy(B.QDQ_E4M3, B.QDQ_E4M3, 64, 64))
+    for name in ('q', 'k', 'v', 'g', 'beta', 'o'):
+        setattr(a, name, fake)
+    for k, v in kw.items():
+        if k in ('state_fmt', 'w_fmt', 'block_v', 'chunk_size'):
+            setattr(a.policy, k, v)
+        else:
+            setattr(a, k, v)
+    return a
+
+
+BAD = [
+    (dict(chunk_size=32), B.GDN_E_UNSUPPORTED, 'chunk_size'),
+    (dict(state_fmt=3), B.GDN_E_UNSUPPORTED, 'format'),
+    (dict(w_fmt=-1), B.GDN_E_UNSUPPORTED, 'format'),
+    (dict(block_v=48), B.GDN_E_UNSUPPORTED, 'block_v'),
+    (dict(Dv=64, block_v=128), B.GDN_E_UNSUPPORTED, 'block_v'),
+    (dict(Hv=6, Hqk=4), B.GDN_E_INVALID, 'multiple'),
+    (dict(Dk=96), B.GDN_E_UNSUPPORTED, 'Dk'),
+    (dict(Dv=512), B.GDN_E_UNSUPPORTED, 'Dv'),
+    (dict(io_dtype=1), B.GDN_E_UNSUPPORTED, 'FP32'),
+    (dict(io_dtype=7), B.GDN_E_INVALID, 'io_dtype'),
+    (dict(num_seqs=2), B.GDN_E_INVALID, 'num_seqs'),
+    (dict(B=2, cu_seqlens=ctypes.c_void_p(0x20000)), B.GDN_E_INVALID, 'cu_seqlens'),
+    (dict(scale=float('nan')), B.GDN_E_INVALID, 'scale'),
+    (dict(q=None), B.GDN_E_INVALID, 'q is NULL'),
+    (dict(o=None), B.GDN_E_INVALID, 'o is NULL'),
+    (dict(k=ctypes.c_void_p(0x10004)), B.GDN_E_INVALID, 'aligned'),
+    (dict(T=-1), B.GDN_E_INVALID, 'bad sizes'),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD)
+def test_forward_rejects_before_launch(kw, status, msg):
+    lib = B.load_library()
+    a = _args(**kw)
+    got = lib.gdn_chunk_fwd(ctypes.byref(a), None)
+    assert got == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_empty_problem_is_a_no_op():
+    lib = B.load_library()
+    a = _args(T=0, q=None, k=None, v=None, g=None, beta=None, o=None)
+    assert lib.gdn_chunk_fwd(ctypes.byref(a), None) == B.GDN_OK
+
+
+def test_saved_layout_sizes():
+    lib = B.load_library()
+    a = _args(B=2, T=100, num_seqs=2)
+    lay = B.saved_layout(a)
+    assert lay.num_slots == 2 + 4                            # N + ceil(200 / 64)
+    assert lay.off_state == 0
+    assert lay.off_state_scale >= lay.num_slots * 4 * 128 * 128
+    assert lay.off_w >= lay.off_state_scale + lay.num_slots * 4 * 2 * 4
+    assert lay.off_w_scale >= lay.off_w + 200 * 4 * 128
+    assert lay.total_bytes == lib.gdn_saved_bytes(ctypes.byref(a))
+    a.policy.state_fmt = B.QDQ_OFF
+    a.policy.w_fmt = B.QDQ_OFF
+    lay = B.saved_layout(a)
+    assert lay.off_state_scale >= lay.num_slots * 4 * 128 * 128 * 4
+    assert lay.off_w == lay.off_state_scale and lay.off_w_scale == lay.off_w
+
+
+def test_backward_rejects_before_launch():
+    lib = B.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    a = B.BwdArgs(fwd=_args(saved=fake), do_=fake, dq=fake, dk=fake, dv=fake, dg=fake,
+                  dbeta=fake, grad_dtype=B.GDN_BF16)
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
+    assert 'workspace' in lib.gdn_last_error().decode()
+    a.workspace = fake
+    a.workspace_bytes = lib.gdn_bwd_workspace_bytes(ctypes.byref(a)) - 1
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
+    a.do_ = None
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_INVALID
+    a.do_ = fake
+    a.fwd.saved = None
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_INVALID
+    a.fwd.saved = fake
+    a.grad_dtype = 5
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_INVALID
+
+
+def test_qdq_state_rejects_before_launch():
+    lib = B.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    cases = [((fake, fake, None, None, 2, 128, 128, 64, 0), B.GDN_E_UNSUPPORTED),
+             ((fake, fake, None, None, 2, 128, 128, 48, 1), B.GDN_E_UNSUPPORTED),
+             ((fake, fake, None, None, 2, 128, 96, 64, 1), B.GDN_E_INVALID),
+             ((None, fake, None, None, 2, 128, 128, 64, 1), B.GDN_E_INVALID),
+             ((fake, ctypes.c_void_p(0x10008), None, None, 2, 128, 128, 64, 2), B.GDN_E_INVALID),
+             ((fake, fake, None, None, 0, 128, 128, 64, 1), B.GDN_OK)]
+    for args, status in cases:
+        assert lib.gdn_qdq_state(*args, None) == status, args

@@ -1,0 +1,190 @@
+"""Forward parity of the HIP path (through the C ABI) against the float64
+oracle on the same seeded inputs.
+
+Bars: QDQ off rel-L2 <= 2e-3 on O and ht; QDQ on rel-L2 <= 1e-2. Small cases
+span several chunks and ragged tails and are compared in full; the five
+named workloads run at full size on the GPU and are compared on sampled
+value heads (heads are independent, so the oracle computes exactly those).
+Exported QDQ codes and scales are compared with the oracle's, since the QDQ
+effect on O alone can sit below the tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+from parity_util import (code_bytes, draw, gpu_fwd, head_subset, oracle_fwd, rel, saved_views,
+                         say, seq_bounds)
+
+pytestmark = pytest.mark.gpu
+
+OFF, E4M3, INT8 = 0, 1, 2
+
+
+def _bar(spec):
+    return 2e-3 if (spec['state_fmt'] == OFF and spec['w_fmt'] == OFF) else 1e-2
+
+
+def _check_fwd(spec, seed, heads, save=True, code_checks=True):
+    say(f"fwd {spec} seed={seed} heads={heads}")
+    x = draw(spec, seed)
+    o, ht, saved = gpu_fwd(x, spec, save=save)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(ht).all()
+    sub = head_subset(x, spec, heads)
+    rec = {}
+    o_ref, ht_ref = oracle_fwd(sub, spec, record=rec)
+    r_o = rel(o[:, :, heads].float(), o_ref)
+    r_h = rel(ht[:, heads], ht_ref)
+    say(f"  rel-L2 O={r_o:.3e} ht={r_h:.3e}")
+    bar = _bar(spec)
+    assert r_o <= bar and r_h <= bar
+    if save and code_checks:
+        _check_codes(x, spec, saved, rec, heads)
+    return x, o, ht, r_o, r_h
+
+
+def _canon(codes, fmt):
+    """E4M3 codes 0x80 (-0) and 0x00 (+0) dequantize to the same zero; the
+    GPU can produce an exact zero where the oracle has a tiny signed value."""
+    codes = np.asarray(codes)
+    return np.where(codes == 0x80, 0, codes) if fmt == E4M3 else codes
+
+
+def _check_codes(x, spec, saved, rec, heads):
+    """Exported codes and scales vs the oracle's record of the same sites.
+    Codes may differ where the FP32 value sits within rounding noise of a
+    grid midpoint (a one-step flip); scales follow the tile amax, a computed
+    FP32 value, so they agree to its precision (~2^-16 relative)."""
+    sv = saved_views(saved, x, spec)
+    bounds = seq_bounds(x, spec)
+    n_el = n_flip = 0
+    max_scale_rel = 0.0
+    for n, (bos, eos) in enumerate(bounds):
+        nchunks = (eos - bos + 63) // 64
+        for c in range(nchunks):
+            slot = n + bos // 64 + c
+            if spec['state_fmt']:
+                # oracle record: per sequence n, chunk c: codes [Z, Dk, nb, bv], Z = heads
+                # (varlen) or B*heads (batched)
+                cz, dz = rec['S'][0 if x['cu_list'] is None else n][c]
+                Hs = len(heads)
+                if x['cu_list'] is None:
+                    cz = cz.reshape(-1, Hs, *cz.shape[1:])[n]
+                    dz = dz.reshape(-1, Hs, *dz.shape[1:])[n]
+                want = _canon(code_bytes(cz.reshape(Hs, spec['Dk'], spec['Dv']),
+                                         spec['state_fmt']), spec['state_fmt'])
+                got = _canon(sv['S'][slot, heads].numpy(), spec['state_fmt'])
+                n_el += want.size
+                n_flip += int((got != want).sum())
+                dg = sv['dS'][slot, heads].numpy()
+                dw = dz.reshape(Hs, -1)
+                max_scale_rel = max(max_scale_rel, float(np.max(np.abs(dg / dw - 1))))
+            if spec['w_fmt']:
+                cz, dz = rec['W'][0 if x['cu_list'] is None else n][c]
+                Hs = len(heads)
+                if x['cu_list'] is None:
+                    cz = cz.reshape(-1, Hs, *cz.shape[1:])[n]
+                    dz = dz.reshape(-1, Hs)[n]
+                t0 = bos + 64 * c
+                t1 = min(t0 + 64, eos)
+                want = _canon(code_bytes(cz, spec['w_fmt']), spec['w_fmt'])   # [Hs, nc, Dk]
+                got = _canon(sv['W'][t0:t1][:, heads].permute(1, 0, 2).numpy(), spec['w_fmt'])
+                n_el += want.size
+                n_flip += int((got != want).sum())
+                dg = sv['dW'][slot, heads].numpy()
+                max_scale_rel = max(max_scale_rel, float(np.max(np.abs(dg / dz.reshape(-1) - 1))))
+    frac = n_flip / max(n_el, 1)
+    say(f"  codes: {n_flip}/{n_el} differ ({frac:.2e}); max scale rel diff {max_scale_rel:.2e}")
+    assert frac <= 1e-3
+    assert max_scale_rel <= 1e-4
+
+
+# ------------------------------------------------------------ small, full compare
+
+SMALL = [
+    # (name, overrides)
+    ('tiny_fp32', {}),
+    ('tiny_fp32', dict(T=257, Hqk=1, Hv=3, h0=True)),
+    ('tiny_fp32', dict(T=200, state_fmt=E4M3, w_fmt=E4M3, block_v=32, h0=True)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=257, Hqk=2, Hv=4)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=300, Hqk=1, Hv=2, state_fmt=OFF, w_fmt=OFF,
+                                        shift=0.0, h0=True)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=130, Hqk=1, Hv=2, Dk=64, Dv=256, block_v=16,
+                                        gate='retention')),
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[257, 3, 70, 1, 64, 130], Hqk=2, Hv=4)),
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[100, 65], Hqk=1, Hv=2, state_fmt=INT8,
+                                      w_fmt=INT8, block_v=32, gate='retention')),
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[200, 64], Hqk=1, Hv=2, state_fmt=OFF, w_fmt=E4M3,
+                                      Dv=64)),
+    ('long_e4m3_t65536_h32_dk128_dv256', dict(T=1000, Hqk=2, Hv=2)),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL)
+def test_fwd_small_full_parity(name, over):
+    spec = gdn_inputs.spec(name, **over)
+    _check_fwd(spec, seed=11, heads=list(range(spec['Hv'])))
+
+
+def test_fwd_qdq_off_bf16_meets_2e3_and_internal_error_small():
+    """QDQ off with bf16 I/O: O's own bf16 rounding costs ~1.6e-3, so the
+    kernel's internal error must stay far below it; ht (FP32) shows it."""
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=1, T=1024, Hqk=2, Hv=2,
+                           state_fmt=OFF, w_fmt=OFF, shift=0.0, h0=True)
+    _, _, _, r_o, r_h = _check_fwd(spec, seed=12, heads=[0, 1])
+    assert r_h <= 2e-4
+
+
+# ------------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("name,heads", [
+    ('tiny_fp32', [0, 1]),
+    ('fwd_e4m3_b4_t4096_h16_d128', [0, 9]),
+    ('varlen_int8_gqa4x16_d128', [0, 13]),
+    ('long_e4m3_t65536_h32_dk128_dv256', [5]),
+])
+def test_fwd_workload_parity(name, heads):
+    spec = gdn_inputs.spec(name)
+    _check_fwd(spec, seed=gdn_inputs.ORDER.index(name) + 1, heads=heads)
+
+
+def test_fwd_workload5_forward_parity():
+    spec = gdn_inputs.spec('fwd_bwd_e4m3_b2_t8192_h16_d128')
+    _check_fwd(spec, seed=5, heads=[3])
+
+
+# ------------------------------------------------------------ properties
+
+def test_fwd_deterministic_and_split_carry():
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=1, T=640, Hqk=2, Hv=4, h0=True)
+    x = draw(spec, 21)
+    o1, h1, _ = gpu_fwd(x, spec)
+    o2, h2, _ = gpu_fwd(x, spec)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    # split carry at a chunk boundary: run 384 tokens, continue from ht
+    cut = 384
+    xa = dict(x, q=x['q'][:, :cut].contiguous(), k=x['k'][:, :cut].contiguous(),
+              v=x['v'][:, :cut].contiguous(), g=x['g'][:, :cut].contiguous(),
+              beta=x['beta'][:, :cut].contiguous())
+    xb = dict(x, q=x['q'][:, cut:].contiguous(), k=x['k'][:, cut:].contiguous(),
+              v=x['v'][:, cut:].contiguous(), g=x['g'][:, cut:].contiguous(),
+              beta=x['beta'][:, cut:].contiguous())
+    oa, ha, _ = gpu_fwd(xa, dict(spec, T=cut))
+    xb['h0'] = ha
+    ob, hb, _ = gpu_fwd(xb, dict(spec, T=640 - cut))
+    assert torch.equal(torch.cat([oa, ob], dim=1), o1)
+    assert torch.equal(hb, h1)
+
+
+def test_fwd_qdq_effect_visible_and_tracked():
+    """Slow-decay gates make the state QDQ visible in O; the GPU must sit far
+    closer to the QDQ oracle than the QDQ oracle sits to the QDQ-off one."""
+    spec = gdn_inputs.spec('long_e4m3_t65536_h32_dk128_dv256', T=2048, Hqk=2, Hv=2, Dv=128)
+    x = draw(spec, 31)
+    o, ht, _ = gpu_fwd(x, spec)
+    sub = head_subset(x, spec, [0, 1])
+    o_q, _ = oracle_fwd(sub, spec)
+    o_off, _ = oracle_fwd(sub, spec, state_fmt=OFF, w_fmt=OFF)
+    r_gpu = rel(o.float(), o_q)
+    r_eff = rel(o_q, o_off)
+    say(f"  gpu vs oracle {r_gpu:.3e}; qdq effect {r_eff:.3e}")
+    assert r_eff > 5 * r_gpu

@@ -1,0 +1,69 @@
+"""gdn_qdq_state on the GPU is bit-exact to the oracle's FP32 QDQ on
+identical FP32 tensors: outputs, scales and one-byte codes, for both formats
+and every supported scale-tile width, including zero tiles, subnormal inputs,
+signed zeros and exact rounding ties ("[2/4] GDN/KDA decode QAT with INT8
+recurrent state", "What does this PR do?" and "Testing")."""
+import numpy as np
+import pytest
+import torch
+
+from gateddeltanet_chunked_recurrence_amd import binding as B
+from oracle.qdq import qdq32
+from parity_util import code_bytes, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_states(rng, n, Dk, Dv, block_v, fmt):
+    x = rng.standard_normal((n, Dk, Dv)).astype(np.float32)
+    x[0] = 0.0                                        # zero tiles
+    x[1, :, :block_v] = np.float32(-0.0)
+    x[2] *= np.float32(1e-39)                         # subnormal FP32 inputs
+    x[3] = (x[3] ** 3) * np.float32(1e4)             # heavy tails
+    # exact ties: amax = qmax * 2^k gives d = 2^k, r = 2^-k, so y = x / 2^k is
+    # exact and grid midpoints stay midpoints
+    k = 3.0
+    if fmt == 1:
+        grid = np.array([0.5, 1.0, 1.125, 14.0, 15.0, 224.0, 240.0, 416.0], np.float32)
+        mids = np.concatenate([(grid[:-1] + grid[1:]) / 2, [2.0 ** -9 * 1.5, 2.0 ** -10]])
+        top = 448.0
+    else:
+        mids = np.array([0.5, 1.5, 2.5, 3.5, 100.5, 126.5, -0.5, -2.5], np.float32)
+        top = 127.0
+    vals = np.resize(mids.astype(np.float32), (Dk, Dv)) * np.float32(2.0 ** k)
+    vals *= np.where(rng.random((Dk, Dv)) < 0.5, -1, 1).astype(np.float32)
+    vals[0, :] = np.float32(top * 2.0 ** k)           # amax of every tile
+    x[4] = vals
+    return x
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+@pytest.mark.parametrize("Dk,Dv,block_v", [(128, 128, 64), (128, 256, 16), (64, 64, 32),
+                                           (128, 128, 128), (64, 256, 256), (32, 48, 16)])
+def test_qdq_state_bitexact(fmt, Dk, Dv, block_v):
+    say(f"qdq_state fmt={fmt} Dk={Dk} Dv={Dv} block_v={block_v}")
+    rng = np.random.default_rng(Dk * 7 + Dv + block_v + fmt)
+    n = 12
+    x = _special_states(rng, n, Dk, Dv, block_v, fmt)
+    xd = torch.from_numpy(x).cuda()
+    y, scales, codes = B.gdn_qdq_state(xd, fmt, block_v, return_codes=True)
+    torch.cuda.synchronize()
+    want, c, d = qdq32(x.reshape(n, Dk, Dv // block_v, block_v), fmt, (1, 3))
+    want = want.reshape(n, Dk, Dv)
+    np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32),
+                                  d.reshape(n, Dv // block_v).view(np.uint32))
+    np.testing.assert_array_equal(codes.cpu().numpy(),
+                                  code_bytes(c.reshape(n, Dk, Dv), fmt))
+
+
+def test_qdq_state_in_place_and_idempotent():
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.standard_normal((6, 128, 128)).astype(np.float32)).cuda()
+    y1, _, _ = B.gdn_qdq_state(x.clone(), 1, 64)
+    z = x.clone()
+    B.gdn_qdq_state(z, 1, 64, out=z)                   # y aliases x
+    y2, _, _ = B.gdn_qdq_state(y1, 1, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(z, y1)
+    assert torch.equal(y2, y1)
