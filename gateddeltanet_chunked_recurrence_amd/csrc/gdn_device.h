@@ -29,6 +29,17 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// The lane index, opaque to the optimizer. Kernels call it at the start of
+// each phase so per-lane LDS addresses are rebuilt where they are used:
+// LDS arrays above 64 KB cannot use the 16-bit instruction offset, and
+// otherwise every (lane, constant) address would be hoisted out of the chunk
+// loop and kept live across it.
+__device__ __forceinline__ int fresh_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // float -> bf16 with round-to-nearest-even; exact split x = hi + lo + O(2^-17 x).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
 __device__ __forceinline__ float from_bf16(bf16 x) { return static_cast<float>(x); }
@@ -57,6 +68,15 @@ __device__ __forceinline__ void pack_pair_split(const f32x4& t0, const f32x4& t1
     split2(t1[e], h1, l1);
     hi[e] = h0; lo[e] = l0; hi[e + 4] = h1; lo[e + 4] = l1;
   }
+}
+
+// Paired storage order: within each 32-wide block of a row, logical index
+// 16 h + 4 g + e is stored at 8 g + 4 h + e. The paired-tile K order above
+// then reads 8 contiguous elements (lds_nat at k0 + 8 grp). Any product whose
+// two operands are both stored this way along the contraction index is
+// unchanged, so a matrix can be kept in one order for every use.
+__device__ __forceinline__ int pperm(int k) {
+  return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
 }
 
 // LDS operand loads (bf16 elements, row-major with row stride `ld`).
@@ -101,46 +121,47 @@ template <int FMT> struct QdqFmt;
 template <> struct QdqFmt<1> { static constexpr float qmax = 448.f; };
 template <> struct QdqFmt<2> { static constexpr float qmax = 127.f; };
 
-// Round to the nearest E4M3FN value, ties to even, saturating at +-448.
-// Normal range (|y| >= 2^-6): keep 3 mantissa bits with an integer RNE on
-// the FP32 bit pattern. Below: the subnormal grid has step 2^-9, and
-// y * 2^9 is exact, so rintf gives the RNE code.
-__device__ __forceinline__ float round_e4m3(float y) {
-  const float a = fabsf(y);
-  if (a >= 448.f) return copysignf(448.f, y);
-  if (a < 0.015625f) return rintf(y * 512.f) * 0.001953125f;
-  uint32_t b = __float_as_uint(a);
-  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
-  return copysignf(__uint_as_float(b), y);
+// E4M3 rounding: nearest OCP E4M3FN value (bias 7, 3 mantissa bits,
+// subnormal step 2^-9), ties to even, saturating at +-448. Done with the
+// hardware round trip of two values: v_cvt_pk_fp8_f32 rounds to nearest even
+// and v_cvt_f32_fp8 is exact. For |y| < 464 this equals the definition bit
+// for bit (checked over every such FP32 pattern on gfx950); above 464 the
+// hardware gives NaN instead of saturating, so inputs are clamped to +-448
+// first (448 < |y| < 464 rounds to 448 either way).
+// `bytes` receives the two one-byte codes in bits 0..15.
+__device__ __forceinline__ void e4m3_pair(float y0, float y1, float& c0, float& c1,
+                                          uint32_t& bytes) {
+  y0 = __builtin_amdgcn_fmed3f(y0, -448.f, 448.f);
+  y1 = __builtin_amdgcn_fmed3f(y1, -448.f, 448.f);
+  bytes = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false)) & 0xFFFFu;
+  c0 = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(bytes), 0);
+  c1 = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(bytes), 1);
 }
+
 __device__ __forceinline__ float round_int8(float y) {
   return fminf(fmaxf(rintf(y), -127.f), 127.f);
 }
-template <int FMT> __device__ __forceinline__ float round_code(float y) {
-  if constexpr (FMT == 1) return round_e4m3(y); else return round_int8(y);
+// Codes of four values x * r (one accumulator quad), and their bytes.
+template <int FMT> __device__ __forceinline__ void quant4(const float (&x)[4], float r,
+                                                          float (&c)[4], uint32_t& bytes) {
+  if constexpr (FMT == 1) {
+    uint32_t b0, b1;
+    e4m3_pair(x[0] * r, x[1] * r, c[0], c[1], b0);
+    e4m3_pair(x[2] * r, x[3] * r, c[2], c[3], b1);
+    bytes = b0 | (b1 << 16);
+  } else {
+    bytes = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = round_int8(x[i] * r);
+      bytes |= (static_cast<uint32_t>(static_cast<int8_t>(c[i])) & 0xFFu) << (8 * i);
+    }
+  }
 }
+
 // Scale from the tile amax: d = max(fl(amax / qmax), 2^-126) (IEEE division).
 template <int FMT> __device__ __forceinline__ float qdq_scale(float amax) {
   const float d = amax / QdqFmt<FMT>::qmax;
   return fmaxf(d, 1.17549435e-38f);
 }
-// One-byte code: E4M3FN bit pattern of an on-grid value, or int8.
-template <int FMT> __device__ __forceinline__ uint8_t code_byte(float c) {
-  if constexpr (FMT == 2) {
-    return static_cast<uint8_t>(static_cast<int8_t>(c));
-  } else {
-    const uint32_t s = (__float_as_uint(c) >> 24) & 0x80u;
-    const float a = fabsf(c);
-    uint32_t mag;
-    if (a < 0.015625f) {
-      mag = static_cast<uint32_t>(a * 512.f);            // subnormal: m / 8 * 2^-6
-    } else {
-      const uint32_t b = __float_as_uint(a);
-      const uint32_t e = ((b >> 23) & 0xFFu) - 127u + 7u;  // biased E4M3 exponent
-      mag = (e << 3) | ((b >> 20) & 7u);
-    }
-    return static_cast<uint8_t>(s | mag);
-  }
-}
-
 }  // namespace gdn

@@ -7,28 +7,34 @@
 // 16w..16w+15 in MFMA accumulator layout). Everything a chunk needs that does
 // not depend on the state (gate cumsum, gated K K^T, the exact solve, W and
 // its QDQ, U, masked Q K^T) is rebuilt per chunk in LDS from q, k, v, g, beta,
-// so HBM traffic is one read of the inputs and one write of O (and ht).
+// so HBM traffic is one read of the inputs and one write of O (and ht). The
+// next chunk's inputs are loaded into registers while the current chunk is
+// computed.
 //
 // Precision. Operands that are bf16 inputs (q, k, v) are exact in bf16. Every
-// FP32 operand (T, T', P, Vnew, the unquantized state) is split as hi + lo
-// bf16 and multiplied in two or three MFMA passes (hi*x + lo*x [+ hi*lo]),
-// which keeps ~16 mantissa bits. QDQ codes (E4M3 values, integers <= 127) are
+// FP32 operand of a bf16 MFMA (T, T', P, Vnew, the unquantized state) is split
+// as hi + lo bf16 and multiplied in two or three passes (hi*x + lo*x [+ hi*lo]),
+// keeping ~16 mantissa bits. QDQ codes (E4M3 values, integers <= 127) are
 // exact in bf16, so products with quantized operands are single passes and
-// the scales are applied after accumulation. Diagonal gate factors are moved
-// onto the FP32 side of each product so bf16 inputs stay exact, and
-// exp(gamma_i - gamma_j) is always formed from the difference (the split
-// exp(gamma_i) * exp(-gamma_j) overflows for strong gates).
+// the scales are applied after accumulation. The triangular solve runs in
+// FP32 (VALU substitution and FP32 MFMA). Diagonal gate factors sit on the
+// FP32 side of each product so bf16 inputs stay exact, and exp(gamma_i -
+// gamma_j) is always formed from the difference (the split exp(gamma_i) *
+// exp(-gamma_j) overflows for strong gates).
 //
 // Steps per chunk ("[1/4] GDN state/W QAT foundation", "What does this PR
 // do?"; the chunk equations are listed in include/gdn.h):
-//   P0 load K, K^T, Q, V^T tiles to LDS; wave 0 forms the gates
-//   P1 L = beta_i (K K^T) * Gam (strict lower), P = (Q K^T) * Gam (lower)
-//   P2 16x16 diagonal blocks of X = (I + L)^-1 by substitution (FP32)
-//   P3 off-diagonal blocks of X, block row by block row (FP32)
-//   P4 T = X diag(beta), T' = T diag(exp(gamma)) -> hi/lo bf16
-//   P5 W = T' K -> QDQ_W -> LDS; U = T V -> registers
-//   P6 Sq = QDQ_S(S) per [Dk, block_v] tile (wave max + LDS)
-//   P7 Vnew = U - Wq Sq; O = scale(exp(gamma) Q Sq + P Vnew);
+//   A  store the prefetched K, K^T, Q, V^T tiles to LDS; gates; prefetch c+1
+//   B  L = beta_i (K K^T) * Gam, strictly lower (10 16x16 tiles)
+//   C  wave 0: diagonal 16x16 blocks of X = (I + L)^-1 by right-looking
+//      substitution, then the two 16-block merges X_10 = -X_11 L_10 X_00
+//      (FP32 MFMA); waves 1-3: P = (Q K^T) * Gam (lower incl. diagonal)
+//   D  waves 0-1: 32-block merge X_BA = -X_BB L_BA X_AA (FP32 MFMA);
+//      waves 2-3: rows 0..31 of W = T' K. T = X diag(beta) and
+//      T' = T diag(exp(gamma)) are written as hi/lo bf16 by each producer
+//   E  rows 32..63 of W; U = T V; amax partials of W and of S
+//   F  QDQ_W(W) -> LDS; Sq = QDQ_S(S) per [Dk, block_v] tile
+//   G  Vnew = U - Wq Sq; O = scale (exp(gamma) Q Sq + P Vnew);
 //      S = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew)
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -41,9 +47,12 @@ struct FwdCfg {
   static constexpr int MK = DK / 16;          // 16-row tiles of the state
   static constexpr int LDK = DK + 8;          // bf16 row stride of [64][DK] tiles
   static constexpr int L64 = 64 + 8;          // bf16 row stride of [*][64] tiles
-  static constexpr int LF = 64 + 4;           // FP32 row stride of [64][64] tiles
+  static constexpr int LF = 65;               // FP32 row stride of [64][64] tiles
   static constexpr int NIN = F32IN ? 2 : 1;   // bf16 planes of an input operand
   static constexpr int NW = (WF == 0) ? 2 : 1;
+  static constexpr int KP = DK / 32;          // rows per thread when staging a K/Q tile
+  static constexpr int KCG = DK / 8;          // 8-element column groups of a K/Q row
+  static constexpr int VP = 2;                // rows per thread when staging the V block
 };
 
 template <int DK, bool F32IN, int SF, int WF>
@@ -53,40 +62,47 @@ struct FwdSmem {
   bf16 Kt[C::NIN][DK * C::L64];    // K transposed [dk][pos]
   bf16 Q[C::NIN][64 * C::LDK];
   bf16 Vt[C::NIN][C::BV * C::L64]; // V block transposed [v][pos]
-  bf16 P[2][64 * C::L64];          // (Q K^T) * Gam, hi / lo
-  union {                          // region A
-    struct { float L[64 * C::LF]; float R[3 * 256]; } s;   // P1..P3
-    bf16 T[4][64 * C::L64];        // P4..P5: T hi, T lo, T' hi, T' lo
-  } a;
-  union {                          // region B
-    float X[64 * C::LF];           // P2..P4
-    bf16 W[C::NW][64 * C::LDK];    // P5..P7: W codes, or W hi / lo
-  } b;
-  float gam[64], eg[64], egc[64], bet[64];
-  float red[8];
-  float amax16[C::BV / 16];
+  bf16 P[2][64 * C::L64];          // (Q K^T) * Gam, hi / lo; upper tiles stay 0
+  bf16 T[4][64 * C::L64];          // T hi, T lo, T' hi, T' lo; upper tiles stay 0
+  union {
+    struct { float L[64 * C::LF]; float X[64 * C::LF]; } s;   // B..D
+    bf16 W[C::NW][64 * C::LDK];                              // F..G: W codes or hi / lo
+  } u;
+  float gam2[64], bet[64], eg[64], egc[64];   // log2-scaled cumsum, beta, gates
+  float red[16];                               // 0..3 W amax, 4..7 S amax, 8 exp(gamma_n)
 };
 
-// 8 consecutive input elements starting at `p` as bf16 planes (hi, and lo for
-// FP32 inputs). Rows past the chunk end read as zeros.
+// 8 consecutive input elements as loaded from HBM.
+template <bool F32IN> struct Raw8 { bf16x8 v; };
+template <> struct Raw8<true> { float4 a, b; };
+
 template <bool F32IN>
-__device__ __forceinline__ void load8(const void* base, int64_t off, bool valid,
-                                      bf16x8& hi, bf16x8& lo) {
+__device__ __forceinline__ Raw8<F32IN> load_raw(const void* base, int64_t off, bool valid) {
+  Raw8<F32IN> r;
   if constexpr (!F32IN) {
     if (valid) {
-      hi = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(base) + off);
+      r.v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(base) + off);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hi[e] = to_bf16(0.f);
+      for (int e = 0; e < 8; ++e) r.v[e] = to_bf16(0.f);
     }
   } else {
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    r.a = r.b = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid) {
       const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-      x0 = p[0];
-      x1 = p[1];
+      r.a = p[0];
+      r.b = p[1];
     }
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  }
+  return r;
+}
+
+template <bool F32IN>
+__device__ __forceinline__ void planes(const Raw8<F32IN>& r, bf16x8& hi, bf16x8& lo) {
+  if constexpr (!F32IN) {
+    hi = r.v;
+  } else {
+    const float xs[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       bf16 h, l;
@@ -97,17 +113,32 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, bool valid,
   }
 }
 
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lower 16x16 tiles (mi >= mj) of a 64x64 matrix, in a fixed order.
+__device__ __forceinline__ void lower_tile(int t, int& mi, int& mj) {
+  mi = (t >= 1) + (t >= 3) + (t >= 6);
+  mj = t - (mi * (mi + 1)) / 2;
+}
+
 template <int DK, bool F32IN, int SF, int WF>
 __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
   using C = FwdCfg<DK, F32IN, SF, WF>;
   constexpr int MK = C::MK, LDK = C::LDK, L64 = C::L64, LF = C::LF, NIN = C::NIN;
+  constexpr int KP = C::KP, VP = C::VP;
+  constexpr float LOG2E = 1.4426950408889634f;
   __shared__ __align__(16) FwdSmem<DK, F32IN, SF, WF> sm;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lane = fresh_lane(), tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+#define GDN_REFRESH() \
+  lane = fresh_lane(); tid = wave * 64 + lane; r16 = lane & 15; grp = lane >> 4
   const int vb = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
-  const int Hv = a.Hv, Dv = a.Dv;
-  const int hk = h / (Hv / a.Hqk);
+  const int Hv = a.Hv, Dv = a.Dv, Hqk = a.Hqk;
+  const int hk = h / (Hv / Hqk);
   int bos, eos;
   if (a.cu_seqlens) {
     bos = a.cu_seqlens[n];
@@ -119,278 +150,364 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
   const int slot0 = n + bos / CHUNK;
   const int wcol = vb * C::BV + wave * 16;          // first value column of this wave
-  const int col = wcol + r16;                       // this lane's value column
   const int64_t state_base = ((int64_t)n * Hv + h) * DK * Dv;
+
+  // P and T upper tiles are read as zeros and never written
+  for (int e = tid; e < 64 * L64; e += 256) {
+    sm.P[0][e] = to_bf16(0.f);
+    sm.P[1][e] = to_bf16(0.f);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) sm.T[p][e] = to_bf16(0.f);
+  }
 
   // ---- state in accumulator layout: S[mt][i] = S[16 mt + 4 grp + i][col]
   f32x4 S[MK];
+  if (a.h0) {
+    const float* hp = a.h0 + state_base + wcol + r16;
 #pragma unroll
-  for (int mt = 0; mt < MK; ++mt)
+    for (int mt = 0; mt < MK; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[mt][i] = a.h0 ? a.h0[state_base + (int64_t)(16 * mt + 4 * grp + i) * Dv + col] : 0.f;
+      for (int i = 0; i < 4; ++i) S[mt][i] = hp[(16 * mt + 4 * grp + i) * Dv];
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt) S[mt] = zero4();
+  }
+
+  // ---- prefetch registers for the next chunk
+  Raw8<F32IN> kr[KP], qr[KP], vr[VP];
+  float g_pre = 0.f, b_pre = 0.f;
+  // K/Q: thread -> column group tid % KCG, rows KP * (tid / KCG) + p; a wave
+  // reads whole rows (coalesced). V: column group tid % 8, rows 2 (tid / 8) + p.
+  auto prefetch = [&](int t0, int nc) {
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const int row = KP * (tid / C::KCG) + p, c8 = (tid % C::KCG) * 8;
+      const int64_t off = ((int64_t)(t0 + row) * Hqk + hk) * DK + c8;
+      kr[p] = load_raw<F32IN>(a.k, off, row < nc);
+      qr[p] = load_raw<F32IN>(a.q, off, row < nc);
+    }
+#pragma unroll
+    for (int p = 0; p < VP; ++p) {
+      const int row = VP * (tid / 8) + p, c8 = (tid % 8) * 8;
+      const int64_t off = ((int64_t)(t0 + row) * Hv + h) * Dv + vb * C::BV + c8;
+      vr[p] = load_raw<F32IN>(a.v, off, row < nc);
+    }
+    const int64_t gi = (int64_t)(t0 + lane) * Hv + h;
+    g_pre = lane < nc ? a.g[gi] : 0.f;
+    b_pre = lane < nc ? a.beta[gi] : 0.f;
+  };
+  if (nchunks > 0) prefetch(bos, min(CHUNK, eos - bos));
 
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = bos + c * CHUNK;
     const int nc = min(CHUNK, eos - t0);
     const int slot = slot0 + c;
 
-    // ------------------------------------------------------------ P0: loads
+    // ------------------------------------- A: stage inputs, gates, prefetch
+    GDN_REFRESH();
     {
-      constexpr int PER_ROW = DK / 8;                 // 8-element groups per row
+      // K, Q rows in paired order along dk; K^T and V^T in paired order along
+      // the position index (KP or 2 consecutive rows land contiguously).
+      const int kc8 = (tid % C::KCG) * 8, kr0 = KP * (tid / C::KCG);
+      const int kd0 = pperm(kc8), kd1 = pperm(kc8 + 4), kpos = pperm(kr0);
+      bf16x8 kh[KP], kl[KP];
 #pragma unroll
-      for (int p = 0; p < (64 * PER_ROW) / 256; ++p) {
-        const int e = p * 256 + tid;
-        const int row = e / PER_ROW, c8 = (e % PER_ROW) * 8;
-        const bool valid = row < nc;
-        const int64_t off = ((int64_t)(t0 + row) * a.Hqk + hk) * DK + c8;
-        bf16x8 kh, kl, qh, ql;
-        load8<F32IN>(a.k, off, valid, kh, kl);
-        load8<F32IN>(a.q, off, valid, qh, ql);
-        *reinterpret_cast<bf16x8*>(&sm.K[0][row * LDK + c8]) = kh;
-        *reinterpret_cast<bf16x8*>(&sm.Q[0][row * LDK + c8]) = qh;
+      for (int p = 0; p < KP; ++p) {
+        bf16x8 qh, ql;
+        planes<F32IN>(kr[p], kh[p], kl[p]);
+        planes<F32IN>(qr[p], qh, ql);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.Kt[0][(c8 + j) * L64 + row] = kh[j];
-        if constexpr (F32IN) {
-          *reinterpret_cast<bf16x8*>(&sm.K[1][row * LDK + c8]) = kl;
-          *reinterpret_cast<bf16x8*>(&sm.Q[1][row * LDK + c8]) = ql;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sm.Kt[1][(c8 + j) * L64 + row] = kl[j];
+        for (int pl = 0; pl < NIN; ++pl) {
+          const bf16x8 kv = pl ? kl[p] : kh[p], qv = pl ? ql : qh;
+          bf16* kd = &sm.K[pl][(kr0 + p) * LDK];
+          bf16* qd = &sm.Q[pl][(kr0 + p) * LDK];
+          *reinterpret_cast<bf16x4*>(kd + kd0) = bf16x4{kv[0], kv[1], kv[2], kv[3]};
+          *reinterpret_cast<bf16x4*>(kd + kd1) = bf16x4{kv[4], kv[5], kv[6], kv[7]};
+          *reinterpret_cast<bf16x4*>(qd + kd0) = bf16x4{qv[0], qv[1], qv[2], qv[3]};
+          *reinterpret_cast<bf16x4*>(qd + kd1) = bf16x4{qv[4], qv[5], qv[6], qv[7]};
         }
       }
-      constexpr int VPR = C::BV / 8;
 #pragma unroll
-      for (int p = 0; p < (64 * VPR) / 256; ++p) {
-        const int e = p * 256 + tid;
-        const int row = e / VPR, c8 = (e % VPR) * 8;
-        const bool valid = row < nc;
-        const int64_t off = ((int64_t)(t0 + row) * Hv + h) * Dv + vb * C::BV + c8;
-        bf16x8 vh, vl;
-        load8<F32IN>(a.v, off, valid, vh, vl);
+      for (int pl = 0; pl < NIN; ++pl)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sm.Vt[0][(c8 + j) * L64 + row] = vh[j];
-        if constexpr (F32IN) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sm.Vt[1][(c8 + j) * L64 + row] = vl[j];
+        for (int j = 0; j < 8; ++j) {
+          bf16* kt = &sm.Kt[pl][(kc8 + j) * L64 + kpos];
+          if constexpr (KP == 4) {
+            const bf16x8* src = pl ? kl : kh;
+            *reinterpret_cast<bf16x4*>(kt) = bf16x4{src[0][j], src[1][j], src[2][j], src[3][j]};
+          } else {
+            const bf16x8* src = pl ? kl : kh;
+            *reinterpret_cast<__attribute__((ext_vector_type(2))) bf16*>(kt) =
+                (__attribute__((ext_vector_type(2))) bf16){src[0][j], src[1][j]};
+          }
         }
-      }
+      const int vc8 = (tid % 8) * 8, vpos = pperm(VP * (tid / 8));
+      bf16x8 vh[VP], vl[VP];
+#pragma unroll
+      for (int p = 0; p < VP; ++p) planes<F32IN>(vr[p], vh[p], vl[p]);
+#pragma unroll
+      for (int pl = 0; pl < NIN; ++pl)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bf16x8* src = pl ? vl : vh;
+          *reinterpret_cast<__attribute__((ext_vector_type(2))) bf16*>(
+              &sm.Vt[pl][(vc8 + j) * L64 + vpos]) =
+              (__attribute__((ext_vector_type(2))) bf16){src[0][j], src[1][j]};
+        }
+      // gates, one row per lane (every wave holds them; wave 0 publishes)
       if (wave == 0) {
         const bool valid = lane < nc;
-        const int64_t gi = (int64_t)(t0 + lane) * Hv + h;
-        const float gv = valid ? a.g[gi] : 0.f;
-        const float bv = valid ? a.beta[gi] : 0.f;
-        const float gam = wave_incl_scan(gv, lane);
-        const float gamC = __shfl(gam, nc - 1, WAVE);
-        sm.gam[lane] = gam;
-        sm.eg[lane] = expf(gam);
-        sm.egc[lane] = valid ? expf(gamC - gam) : 0.f;
-        sm.bet[lane] = bv;
-        if (lane == 0) sm.red[4] = expf(gamC);
+        const float g2 = wave_incl_scan(valid ? g_pre * LOG2E : 0.f, lane);
+        const float g2n = __shfl(g2, nc - 1, WAVE);
+        sm.gam2[lane] = g2;
+        sm.bet[lane] = valid ? b_pre : 0.f;
+        sm.eg[lane] = fexp2(g2);
+        sm.egc[lane] = valid ? fexp2(g2n - g2) : 0.f;
+        if (lane == 0) sm.red[8] = fexp2(g2n);
+      }
+      if (c + 1 < nchunks) prefetch(t0 + CHUNK, min(CHUNK, eos - t0 - CHUNK));
+    }
+    __syncthreads();
+
+    // ------------------------------------- B: L = beta_i (K K^T) Gam, strict lower
+    GDN_REFRESH();
+    for (int jb = wave; jb < 10; jb += 4) {
+      int mi, mj;
+      lower_tile(jb, mi, mj);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk) {
+        const bf16x8 a0 = lds_nat(sm.K[0], 16 * mi + r16, LDK, 32 * kk, grp);
+        const bf16x8 b0 = lds_nat(sm.K[0], 16 * mj + r16, LDK, 32 * kk, grp);
+        acc = mfma(a0, b0, acc);
+        if constexpr (F32IN) {
+          const bf16x8 a1 = lds_nat(sm.K[1], 16 * mi + r16, LDK, 32 * kk, grp);
+          const bf16x8 b1 = lds_nat(sm.K[1], 16 * mj + r16, LDK, 32 * kk, grp);
+          acc = mfma(a1, b0, acc);
+          acc = mfma(a0, b1, acc);
+        }
+      }
+      const int cj = 16 * mj + r16;
+      const float gj = sm.gam2[cj];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mi + 4 * grp + i;
+        sm.u.s.L[row * LF + cj] =
+            (row > cj) ? sm.bet[row] * acc[i] * fexp2(sm.gam2[row] - gj) : 0.f;
       }
     }
     __syncthreads();
 
-    // ------------------------------------ P1: L and P (lower 16x16 tiles)
-    {
-      // 20 lower tiles (10 of K K^T, 10 of Q K^T), 5 per wave.
-      for (int job = wave; job < 20; job += 4) {
-        const bool isP = job >= 10;
-        int t = isP ? job - 10 : job;                 // t -> (mi, mj), mj <= mi
-        int mi = 0;
-        while (t > mi) { t -= mi + 1; ++mi; }
-        const int mj = t;
-        const bf16(*X)[64 * LDK] = isP ? sm.Q : sm.K;
+    // Writes one FP32 entry of X as T = x beta_col and T' = T exp(gamma_col).
+    auto put_T = [&](int row, int cj, float x, float bc, float ec) {
+      const float t = x * bc, tp = t * ec;
+      const int o = row * L64 + pperm(cj);
+      bf16 hi, lo;
+      split2(t, hi, lo);
+      sm.T[0][o] = hi;
+      sm.T[1][o] = lo;
+      split2(tp, hi, lo);
+      sm.T[2][o] = hi;
+      sm.T[3][o] = lo;
+    };
+
+    // ----------------- C: wave 0 solve (diagonal blocks, 16-merges); 1-3 P
+    GDN_REFRESH();
+    if (wave == 0) {
+      const int b = lane >> 4, cc = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
+      const float* Lb = &sm.u.s.L[(16 * b) * LF + 16 * b];
+#pragma unroll
+      for (int j = 0; j < 15; ++j)
+#pragma unroll
+        for (int r = j + 1; r < 16; ++r) x[r] -= Lb[r * LF + j] * x[j];
+      {
+        const int cj = 16 * b + cc;
+        const float bc = sm.bet[cj], ec = sm.eg[cj];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sm.u.s.X[(16 * b + r) * LF + cj] = x[r];
+          put_T(16 * b + r, cj, x[r], bc, ec);
+        }
+      }
+      // X_BA = -X_BB (L_BA X_AA) for the block pairs (A, B) = (0, 1), (2, 3)
+      f32x4 y[2], z[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int A = 2 * p, B = 2 * p + 1;
+        y[p] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          y[p] = mfma_f32(sm.u.s.L[(16 * B + r16) * LF + 16 * A + 4 * kk + grp],
+                          sm.u.s.X[(16 * A + 4 * kk + grp) * LF + 16 * A + r16], y[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int B = 2 * p + 1;
+        z[p] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)                  // K order: 4 grp + kk
+          z[p] = mfma_f32(sm.u.s.X[(16 * B + r16) * LF + 16 * B + 4 * grp + kk], y[p][kk], z[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int A = 2 * p, B = 2 * p + 1;
+        const int cj = 16 * A + r16;
+        const float bc = sm.bet[cj], ec = sm.eg[cj];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * B + 4 * grp + i;
+          sm.u.s.X[row * LF + cj] = -z[p][i];
+          put_T(row, cj, -z[p][i], bc, ec);
+        }
+      }
+    } else {
+      for (int jb = wave - 1; jb < 10; jb += 3) {
+        int mi, mj;
+        lower_tile(jb, mi, mj);
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
+          const bf16x8 a0 = lds_nat(sm.Q[0], 16 * mi + r16, LDK, 32 * kk, grp);
           const bf16x8 b0 = lds_nat(sm.K[0], 16 * mj + r16, LDK, 32 * kk, grp);
-          const bf16x8 a0 = lds_nat(X[0], 16 * mi + r16, LDK, 32 * kk, grp);
           acc = mfma(a0, b0, acc);
           if constexpr (F32IN) {
+            const bf16x8 a1 = lds_nat(sm.Q[1], 16 * mi + r16, LDK, 32 * kk, grp);
             const bf16x8 b1 = lds_nat(sm.K[1], 16 * mj + r16, LDK, 32 * kk, grp);
-            const bf16x8 a1 = lds_nat(X[1], 16 * mi + r16, LDK, 32 * kk, grp);
             acc = mfma(a1, b0, acc);
             acc = mfma(a0, b1, acc);
           }
         }
-        const int colj = 16 * mj + r16;
-        const float gj = sm.gam[colj];
+        const int cj = 16 * mj + r16;
+        const float gj = sm.gam2[cj];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * mi + 4 * grp + i;
-          const float gate = expf(sm.gam[row] - gj);
-          if (!isP) {
-            sm.a.s.L[row * LF + colj] = (row > colj) ? sm.bet[row] * acc[i] * gate : 0.f;
-          } else {
-            const float pv = (row >= colj) ? acc[i] * gate : 0.f;
-            bf16 hi, lo;
-            split2(pv, hi, lo);
-            sm.P[0][row * L64 + colj] = hi;
-            sm.P[1][row * L64 + colj] = lo;
-          }
+          const float pv = (row >= cj) ? acc[i] * fexp2(sm.gam2[row] - gj) : 0.f;
+          bf16 hi, lo;
+          split2(pv, hi, lo);
+          sm.P[0][row * L64 + pperm(cj)] = hi;
+          sm.P[1][row * L64 + pperm(cj)] = lo;
         }
-      }
-      // zero the upper tiles of P and of X (X's upper blocks stay zero)
-      for (int e = tid; e < 6 * 256; e += 256) {
-        int t = e / 256, rr = (e / 16) % 16, cc = e % 16;
-        int bi = 0, bj = 1;                              // t -> (bi, bj), bj > bi
-        while (t >= 3 - bi) { t -= 3 - bi; ++bi; }
-        bj = bi + 1 + t;
-        const int row = 16 * bi + rr, colj = 16 * bj + cc;
-        sm.P[0][row * L64 + colj] = to_bf16(0.f);
-        sm.P[1][row * L64 + colj] = to_bf16(0.f);
-        sm.b.X[row * LF + colj] = 0.f;
       }
     }
     __syncthreads();
 
-    // ------------------------------ P2: diagonal blocks of X = (I + L)^-1
-    if (lane < 16) {
-      const int b = wave, cc = lane;
-      float x[16];
+    // --------------- D: waves 0-1 32-block merge; waves 2-3 W rows 0..31
+    GDN_REFRESH();
+    constexpr int NWC = DK / 32;                       // W column tiles per wave
+    f32x4 Wt[2][NWC];                                 // this wave's 2 x NWC tiles of W
+    // waves 2, 3: rows 0..31, column tiles (wave - 2) * NWC + d
+    // waves 0, 1: rows 32..63, column tiles wave * NWC + d
+    const int wrow0 = wave < 2 ? 32 : 0;
+    const int wct0 = (wave & 1) * NWC;
+    if (wave < 2) {
+      const int tj = wave;
+      f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == cc) ? 1.f : 0.f;
-        const float* Lr = &sm.a.s.L[(16 * b + r) * LF + 16 * b];
+      for (int s = 0; s < 8; ++s) {
+        if (s < 4 * tj) continue;                     // X_AA is lower triangular
+        const float bx = sm.u.s.X[(4 * s + grp) * LF + 16 * tj + r16];
 #pragma unroll
-        for (int j = 0; j < r; ++j) s -= Lr[j] * x[j];
-        x[r] = s;
+        for (int ti = 0; ti < 2; ++ti)
+          y[ti] = mfma_f32(sm.u.s.L[(32 + 16 * ti + r16) * LF + 4 * s + grp], bx, y[ti]);
       }
+      const int cj = 16 * tj + r16;
+      const float bc = sm.bet[cj], ec = sm.eg[cj];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.b.X[(16 * b + r) * LF + 16 * b + cc] = x[r];
-    }
-    __syncthreads();
-
-    // ------------------------------ P3: off-diagonal blocks, block row i
-    for (int bi = 1; bi < 4; ++bi) {
-      // R_j = sum_{k=j}^{bi-1} L_{bi,k} X_{k,j}, j < bi
-      for (int e = tid; e < bi * 256; e += 256) {
-        const int j = e / 256, rr = (e / 16) % 16, cc = e % 16;
-        const float* Lr = &sm.a.s.L[(16 * bi + rr) * LF];
-        float s = 0.f;
-        for (int m = 16 * j; m < 16 * bi; ++m) s += Lr[m] * sm.b.X[m * LF + 16 * j + cc];
-        sm.a.s.R[e] = s;
-      }
-      __syncthreads();
-      // X_{bi,j} = -X_{bi,bi} R_j
-      for (int e = tid; e < bi * 256; e += 256) {
-        const int j = e / 256, rr = (e / 16) % 16, cc = e % 16;
-        const float* Xr = &sm.b.X[(16 * bi + rr) * LF + 16 * bi];
-        const float* Rj = &sm.a.s.R[j * 256];
-        float s = 0.f;
+      for (int ti = 0; ti < 2; ++ti) {
+        f32x4 z = zero4();
 #pragma unroll
-        for (int m = 0; m < 16; ++m) s += Xr[m] * Rj[m * 16 + cc];
-        sm.b.X[(16 * bi + rr) * LF + 16 * j + cc] = -s;
-      }
-      __syncthreads();
-    }
-
-    // -------------------- P4: T = X diag(beta), T' = T diag(exp(gamma))
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int row = e / 64, cc = e % 64;
-      const float t = sm.b.X[row * LF + cc] * sm.bet[cc];
-      const float tp = t * sm.eg[cc];
-      bf16 hi, lo;
-      split2(t, hi, lo);
-      sm.a.T[0][row * L64 + cc] = hi;
-      sm.a.T[1][row * L64 + cc] = lo;
-      split2(tp, hi, lo);
-      sm.a.T[2][row * L64 + cc] = hi;
-      sm.a.T[3][row * L64 + cc] = lo;
-    }
-    __syncthreads();
-
-    // ----------------------------------------- P5: W = T' K, U = T V
-    constexpr int DTW = MK / 4;                       // W column tiles per wave
-    f32x4 Wacc[4][DTW];
-    float wmax = 0.f;
+        for (int kt = 0; kt < 2; ++kt) {
+          if (kt > ti) continue;                      // X_BB is lower triangular
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int dt = 0; dt < DTW; ++dt) {
-        const int dtile = wave * DTW + dt;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          if (kk > mt / 2) continue;                  // T' is lower triangular
-          const bf16x8 bk = lds_nat(sm.Kt[0], 16 * dtile + r16, L64, 32 * kk, grp);
-          const bf16x8 th = lds_nat(sm.a.T[2], 16 * mt + r16, L64, 32 * kk, grp);
-          const bf16x8 tl = lds_nat(sm.a.T[3], 16 * mt + r16, L64, 32 * kk, grp);
-          acc = mfma(th, bk, acc);
-          acc = mfma(tl, bk, acc);
-          if constexpr (F32IN) {
-            const bf16x8 bkl = lds_nat(sm.Kt[1], 16 * dtile + r16, L64, 32 * kk, grp);
-            acc = mfma(th, bkl, acc);
-          }
+          for (int kk = 0; kk < 4; ++kk)              // K order: 16 kt + 4 grp + kk
+            z = mfma_f32(sm.u.s.X[(32 + 16 * ti + r16) * LF + 32 + 16 * kt + 4 * grp + kk],
+                         y[kt][kk], z);
         }
-        Wacc[mt][dt] = acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wmax = fmaxf(wmax, fabsf(acc[i]));
+        for (int i = 0; i < 4; ++i) put_T(32 + 16 * ti + 4 * grp + i, cj, -z[i], bc, ec);
       }
-    f32x4 U[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk > mt / 2) continue;
-        const bf16x8 bv = lds_nat(sm.Vt[0], wave * 16 + r16, L64, 32 * kk, grp);
-        const bf16x8 th = lds_nat(sm.a.T[0], 16 * mt + r16, L64, 32 * kk, grp);
-        const bf16x8 tl = lds_nat(sm.a.T[1], 16 * mt + r16, L64, 32 * kk, grp);
-        acc = mfma(th, bv, acc);
-        acc = mfma(tl, bv, acc);
-        if constexpr (F32IN) {
-          const bf16x8 bvl = lds_nat(sm.Vt[1], wave * 16 + r16, L64, 32 * kk, grp);
-          acc = mfma(th, bvl, acc);
-        }
-      }
-      U[mt] = acc;
-    }
-    float dW = 1.f;
-    if constexpr (WF != 0) {
-      wmax = wave_max(wmax);
-      if (lane == 0) sm.red[wave] = wmax;
-    }
-    __syncthreads();                                  // X dead, W region free; amax ready
-    if constexpr (WF != 0) {
-      const float amax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
-      dW = qdq_scale<WF>(amax);
-      const float rW = 1.0f / dW;
-      const bool save = a.w_codes != nullptr && vb == 0;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) {
-          const int dcol = 16 * (wave * DTW + dt) + r16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * mt + 4 * grp + i;
-            const float cq = round_code<WF>(Wacc[mt][dt][i] * rW);
-            sm.b.W[0][row * LDK + dcol] = to_bf16(cq);
-            if (save && row < nc)
-              a.w_codes[((int64_t)(t0 + row) * Hv + h) * DK + dcol] = code_byte<WF>(cq);
-          }
-        }
-      if (save && tid == 0) a.w_scale[(int64_t)slot * Hv + h] = dW;
     } else {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 th = lds_nat(sm.T[2], 16 * mt + r16, L64, 0, grp);
+        const bf16x8 tl = lds_nat(sm.T[3], 16 * mt + r16, L64, 0, grp);
 #pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) {
-          const int dcol = 16 * (wave * DTW + dt) + r16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * mt + 4 * grp + i;
-            bf16 hi, lo;
-            split2(Wacc[mt][dt][i], hi, lo);
-            sm.b.W[0][row * LDK + dcol] = hi;
-            sm.b.W[C::NW - 1][row * LDK + dcol] = lo;
+        for (int d = 0; d < NWC; ++d) {
+          const bf16x8 bk = lds_nat(sm.Kt[0], 16 * (wct0 + d) + r16, L64, 0, grp);
+          f32x4 acc = mfma(th, bk, zero4());
+          acc = mfma(tl, bk, acc);
+          if constexpr (F32IN) {
+            const bf16x8 bkl = lds_nat(sm.Kt[1], 16 * (wct0 + d) + r16, L64, 0, grp);
+            acc = mfma(th, bkl, acc);
           }
+          Wt[mt][d] = acc;
         }
+      }
     }
+    __syncthreads();
 
-    // ---------------------------------------------- P6: state QDQ
-    float dS = 1.f;
+    // ------------------- E: W rows 32..63 (waves 0, 1), U = T V, amax partials
+    GDN_REFRESH();
+    if (wave < 2) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int mt = 2 + t;
+        bf16x8 th[2], tl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          th[kk] = lds_nat(sm.T[2], 16 * mt + r16, L64, 32 * kk, grp);
+          tl[kk] = lds_nat(sm.T[3], 16 * mt + r16, L64, 32 * kk, grp);
+        }
+#pragma unroll
+        for (int d = 0; d < NWC; ++d) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 bk = lds_nat(sm.Kt[0], 16 * (wct0 + d) + r16, L64, 32 * kk, grp);
+            acc = mfma(th[kk], bk, acc);
+            acc = mfma(tl[kk], bk, acc);
+            if constexpr (F32IN) {
+              const bf16x8 bkl = lds_nat(sm.Kt[1], 16 * (wct0 + d) + r16, L64, 32 * kk, grp);
+              acc = mfma(th[kk], bkl, acc);
+            }
+          }
+          Wt[t][d] = acc;
+        }
+      }
+    }
+    f32x4 U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 bv = lds_nat(sm.Vt[0], wave * 16 + r16, L64, 32 * kk, grp);
+      bf16x8 bvl;
+      if constexpr (F32IN) bvl = lds_nat(sm.Vt[1], wave * 16 + r16, L64, 32 * kk, grp);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (kk > mt / 2) continue;                    // T is lower triangular
+        const bf16x8 th = lds_nat(sm.T[0], 16 * mt + r16, L64, 32 * kk, grp);
+        const bf16x8 tl = lds_nat(sm.T[1], 16 * mt + r16, L64, 32 * kk, grp);
+        U[mt] = mfma(th, bv, U[mt]);
+        U[mt] = mfma(tl, bv, U[mt]);
+        if constexpr (F32IN) U[mt] = mfma(th, bvl, U[mt]);
+      }
+    }
+    if constexpr (WF != 0) {
+      float m = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int d = 0; d < NWC; ++d)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(Wt[t][d][i]));
+      m = wave_max(m);
+      if (lane == 0) sm.red[wave] = m;
+    }
     if constexpr (SF != 0) {
       float m = 0.f;
 #pragma unroll
@@ -398,40 +515,87 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
       m = wave_max(m);
-      if (lane == 0) sm.amax16[wave] = m;
+      if (lane == 0) sm.red[4 + wave] = m;
     }
-    __syncthreads();                                  // W in LDS; state amax ready
+    __syncthreads();                                  // L, X dead; amax partials ready
+
+    // ------------------------------------------- F: QDQ of W and of S
+    GDN_REFRESH();
+    float dW = 1.f;
+    {
+      const bool save = WF != 0 && a.w_codes != nullptr && vb == 0;
+      float rW = 1.f;
+      if constexpr (WF != 0) {
+        const float amax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+        dW = qdq_scale<WF>(amax);
+        rW = 1.0f / dW;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int d = 0; d < NWC; ++d) {
+          const int dcol = 16 * (wct0 + d) + r16, pc = pperm(dcol);
+          const int row0 = wrow0 + 16 * t + 4 * grp;
+          const float w[4] = {Wt[t][d][0], Wt[t][d][1], Wt[t][d][2], Wt[t][d][3]};
+          if constexpr (WF != 0) {
+            float cq[4];
+            uint32_t bytes;
+            quant4<WF>(w, rW, cq, bytes);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.u.W[0][(row0 + i) * LDK + pc] = to_bf16(cq[i]);
+            if (save) {
+              uint8_t* wp = a.w_codes + ((int64_t)t0 * Hv + h) * DK + dcol;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (row0 + i < nc) wp[(row0 + i) * Hv * DK] = (bytes >> (8 * i)) & 0xFFu;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bf16 hi, lo;
+              split2(w[i], hi, lo);
+              sm.u.W[0][(row0 + i) * LDK + pc] = hi;
+              sm.u.W[C::NW - 1][(row0 + i) * LDK + pc] = lo;
+            }
+          }
+        }
+      if (save && tid == 0) a.w_scale[(int64_t)slot * Hv + h] = dW;
+    }
+    float dS = 1.f;
     if constexpr (SF != 0) {
       const int gs = a.block_v / 16;                  // 16-col tiles per scale tile
       const int g0 = (wave / gs) * gs;
       float amax = 0.f;
-      for (int t = g0; t < g0 + gs; ++t) amax = fmaxf(amax, sm.amax16[t]);
+      for (int t = g0; t < g0 + gs; ++t) amax = fmaxf(amax, sm.red[4 + t]);
       dS = qdq_scale<SF>(amax);
       const float rS = 1.0f / dS;
+      uint8_t* sb = a.s_codes ? a.s_codes + ((int64_t)slot * Hv + h) * DK * Dv + wcol + r16 : nullptr;
 #pragma unroll
-      for (int mt = 0; mt < MK; ++mt)
+      for (int mt = 0; mt < MK; ++mt) {
+        const float x[4] = {S[mt][0], S[mt][1], S[mt][2], S[mt][3]};
+        float cq[4];
+        uint32_t bytes;
+        quant4<SF>(x, rS, cq, bytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[mt][i] = round_code<SF>(S[mt][i] * rS);   // codes
-      if (a.s_codes) {
-        const int64_t sb = ((int64_t)slot * Hv + h) * DK * Dv;
+        for (int i = 0; i < 4; ++i) S[mt][i] = cq[i];                // codes
+        if (sb) {
 #pragma unroll
-        for (int mt = 0; mt < MK; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            a.s_codes[sb + (int64_t)(16 * mt + 4 * grp + i) * Dv + col] = code_byte<SF>(S[mt][i]);
-        if (wave == g0 && lane == 0)
-          a.s_scale[((int64_t)slot * Hv + h) * (Dv / a.block_v) + wcol / a.block_v] = dS;
+          for (int i = 0; i < 4; ++i) sb[(16 * mt + 4 * grp + i) * Dv] = (bytes >> (8 * i)) & 0xFFu;
+        }
       }
+      if (sb && wave == g0 && lane == 0)
+        a.s_scale[((int64_t)slot * Hv + h) * (Dv / a.block_v) + wcol / a.block_v] = dS;
     } else if (a.s_f32) {
-      const int64_t sb = ((int64_t)slot * Hv + h) * DK * Dv;
+      float* sb = a.s_f32 + ((int64_t)slot * Hv + h) * DK * Dv + wcol + r16;
 #pragma unroll
       for (int mt = 0; mt < MK; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.s_f32[sb + (int64_t)(16 * mt + 4 * grp + i) * Dv + col] = S[mt][i];
+        for (int i = 0; i < 4; ++i) sb[(16 * mt + 4 * grp + i) * Dv] = S[mt][i];
     }
+    __syncthreads();                                  // W in LDS
 
-    // ------------------------------- P7: Vnew, O, state update
+    // ------------------------------- G: Vnew, O, state update
+    GDN_REFRESH();
     // state as B operand (paired-tile K order over dk)
     bf16x8 bSh[MK / 2], bSl[MK / 2];
 #pragma unroll
@@ -442,35 +606,41 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
         pack_pair_split(S[2 * kk], S[2 * kk + 1], bSh[kk], bSl[kk]);
       }
     }
-    f32x4 Vn[4], Oi[4];
+    f32x4 accw[4], accq[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 accw = zero4(), accq = zero4();
+    for (int mt = 0; mt < 4; ++mt) accw[mt] = accq[mt] = zero4();
 #pragma unroll
-      for (int kk = 0; kk < MK / 2; ++kk) {
-        const bf16x8 w0 = lds_pair(sm.b.W[0], 16 * mt + r16, LDK, 32 * kk, grp);
-        const bf16x8 q0 = lds_pair(sm.Q[0], 16 * mt + r16, LDK, 32 * kk, grp);
-        accw = mfma(w0, bSh[kk], accw);
-        accq = mfma(q0, bSh[kk], accq);
+    for (int kk = 0; kk < MK / 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 w0 = lds_nat(sm.u.W[0], 16 * mt + r16, LDK, 32 * kk, grp);
+        const bf16x8 q0 = lds_nat(sm.Q[0], 16 * mt + r16, LDK, 32 * kk, grp);
+        accw[mt] = mfma(w0, bSh[kk], accw[mt]);
+        accq[mt] = mfma(q0, bSh[kk], accq[mt]);
         if constexpr (WF == 0) {
-          const bf16x8 w1 = lds_pair(sm.b.W[C::NW - 1], 16 * mt + r16, LDK, 32 * kk, grp);
-          accw = mfma(w1, bSh[kk], accw);
+          const bf16x8 w1 = lds_nat(sm.u.W[C::NW - 1], 16 * mt + r16, LDK, 32 * kk, grp);
+          accw[mt] = mfma(w1, bSh[kk], accw[mt]);
         }
         if constexpr (F32IN) {
-          const bf16x8 q1 = lds_pair(sm.Q[NIN - 1], 16 * mt + r16, LDK, 32 * kk, grp);
-          accq = mfma(q1, bSh[kk], accq);
+          const bf16x8 q1 = lds_nat(sm.Q[NIN - 1], 16 * mt + r16, LDK, 32 * kk, grp);
+          accq[mt] = mfma(q1, bSh[kk], accq[mt]);
         }
         if constexpr (SF == 0) {
-          accw = mfma(w0, bSl[kk], accw);
-          accq = mfma(q0, bSl[kk], accq);
+          accw[mt] = mfma(w0, bSl[kk], accw[mt]);
+          accq[mt] = mfma(q0, bSl[kk], accq[mt]);
         }
       }
+    }
+    f32x4 Vn[4];
+    {
       const float sc = dW * dS;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Vn[mt][i] = U[mt][i] - sc * accw[i];
-        Oi[mt][i] = dS * accq[i];
-      }
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Vn[mt][i] = U[mt][i] - sc * accw[mt][i];
+          accq[mt][i] *= dS;
+        }
     }
     // Vnew and exp(gamma_n - gamma) Vnew as B operands (paired order over positions)
     bf16x8 bVh[2], bVl[2], bDh[2], bDl[2];
@@ -486,60 +656,68 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
       pack_pair_split(d0, d1, bDh[kk], bDl[kk]);
     }
     // O = scale (exp(gamma) Q Sq + P Vnew)
+    {
+      const int64_t obase = ((int64_t)t0 * Hv + h) * Dv + wcol + r16;
+      f32x4 aco[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = zero4();
+      for (int mt = 0; mt < 4; ++mt) aco[mt] = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        if (kk > mt / 2) continue;
-        const bf16x8 ph = lds_pair(sm.P[0], 16 * mt + r16, L64, 32 * kk, grp);
-        const bf16x8 pl = lds_pair(sm.P[1], 16 * mt + r16, L64, 32 * kk, grp);
-        acc = mfma(ph, bVh[kk], acc);
-        acc = mfma(pl, bVh[kk], acc);
-        acc = mfma(ph, bVl[kk], acc);
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mt + 4 * grp + i;
-        if (row < nc) {
-          const float ov = a.scale * (sm.eg[row] * Oi[mt][i] + acc[i]);
-          const int64_t off = ((int64_t)(t0 + row) * Hv + h) * Dv + col;
-          if constexpr (F32IN) reinterpret_cast<float*>(a.o)[off] = ov;
-          else reinterpret_cast<bf16*>(a.o)[off] = to_bf16(ov);
+        for (int mt = 0; mt < 4; ++mt) {
+          if (kk > mt / 2) continue;
+          const bf16x8 ph = lds_nat(sm.P[0], 16 * mt + r16, L64, 32 * kk, grp);
+          const bf16x8 pl = lds_nat(sm.P[1], 16 * mt + r16, L64, 32 * kk, grp);
+          aco[mt] = mfma(ph, bVh[kk], aco[mt]);
+          aco[mt] = mfma(pl, bVh[kk], aco[mt]);
+          aco[mt] = mfma(ph, bVl[kk], aco[mt]);
         }
       }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * mt + 4 * grp + i;
+          if (row < nc) {
+            const float ov = a.scale * (sm.eg[row] * accq[mt][i] + aco[mt][i]);
+            if constexpr (F32IN) reinterpret_cast<float*>(a.o)[obase + row * Hv * Dv] = ov;
+            else reinterpret_cast<bf16*>(a.o)[obase + row * Hv * Dv] = to_bf16(ov);
+          }
+        }
     }
-    // S = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew)
-    const float egC = sm.red[4];
+    // S = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew), accumulated in place
+    {
+      const float egC = sm.red[8];
 #pragma unroll
-    for (int mt = 0; mt < MK; ++mt) {
-      f32x4 acc = zero4();
+      for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[mt][i] = egC * ((SF != 0) ? S[mt][i] * dS : S[mt][i]);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 kt = lds_pair(sm.Kt[0], 16 * mt + r16, L64, 32 * kk, grp);
-        acc = mfma(kt, bDh[kk], acc);
-        acc = mfma(kt, bDl[kk], acc);
-        if constexpr (F32IN) {
-          const bf16x8 ktl = lds_pair(sm.Kt[1], 16 * mt + r16, L64, 32 * kk, grp);
-          acc = mfma(ktl, bDh[kk], acc);
-        }
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sq = (SF != 0) ? S[mt][i] * dS : S[mt][i];
-        S[mt][i] = egC * sq + acc[i];
+        for (int mt = 0; mt < MK; ++mt) {
+          const bf16x8 kt = lds_nat(sm.Kt[0], 16 * mt + r16, L64, 32 * kk, grp);
+          S[mt] = mfma(kt, bDh[kk], S[mt]);
+          S[mt] = mfma(kt, bDl[kk], S[mt]);
+          if constexpr (F32IN) {
+            const bf16x8 ktl = lds_nat(sm.Kt[1], 16 * mt + r16, L64, 32 * kk, grp);
+            S[mt] = mfma(ktl, bDh[kk], S[mt]);
+          }
+        }
       }
     }
     __syncthreads();                                  // LDS reused by the next chunk
   }
 
   if (a.ht) {
+    GDN_REFRESH();
 #pragma unroll
     for (int mt = 0; mt < MK; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a.ht[state_base + (int64_t)(16 * mt + 4 * grp + i) * Dv + col] = S[mt][i];
+        a.ht[state_base + (int64_t)(16 * mt + 4 * grp + i) * Dv + wcol + r16] = S[mt][i];
   }
+#undef GDN_REFRESH
 }
 
 template <int DK, bool F32IN, int SF, int WF>

@@ -37,9 +37,19 @@ qdq_state_kernel(const float* x, float* y, float* __restrict__ scales,
   const float r = 1.0f / d;
   for (int e = tid; e < n; e += QDQ_THREADS) {
     const int64_t off = base + (int64_t)(e / block_v) * Dv + (e % block_v);
-    const float c = round_code<FMT>(x[off] * r);
+    float c;
+    uint8_t byte;
+    if constexpr (FMT == 1) {
+      float unused;
+      uint32_t b;
+      e4m3_pair(x[off] * r, 0.f, c, unused, b);
+      byte = static_cast<uint8_t>(b & 0xFFu);
+    } else {
+      c = round_int8(x[off] * r);
+      byte = static_cast<uint8_t>(static_cast<int8_t>(c));
+    }
     y[off] = c * d;
-    if (codes) codes[off] = code_byte<FMT>(c);
+    if (codes) codes[off] = byte;
   }
   if (scales && tid == 0) scales[state * tiles_per_state + tile] = d;
 }

@@ -67,3 +67,37 @@ def test_qdq_state_in_place_and_idempotent():
     torch.cuda.synchronize()
     assert torch.equal(z, y1)
     assert torch.equal(y2, y1)
+
+
+def test_qdq_state_e4m3_sweeps_every_rounding_boundary():
+    """Tiles whose amax is 448 * 2^k have d = 2^k and r = 2^-k exactly, so
+    y = x / 2^k is exact and each chosen y reaches the rounding step as is:
+    every E4M3 value, every midpoint between neighbours, and the FP32
+    neighbours of each midpoint (ties go to even, the others to the nearer
+    code), plus dense random values, in both signs."""
+    from oracle.qdq import e4m3_decode_table
+    t = e4m3_decode_table()[:0x7F]                        # 0 .. 448
+    mids = (t[:-1] + t[1:]) / 2
+    m32 = mids.astype(np.float32)
+    up = np.nextafter(m32, np.float32(np.inf))
+    dn = np.nextafter(m32, np.float32(0))
+    rng = np.random.default_rng(9)
+    ys = np.concatenate([t, mids, up, dn, rng.uniform(0, 448, 20000),
+                         rng.uniform(0, 2 ** -6, 4000)]).astype(np.float32)
+    ys = np.concatenate([ys, -ys])
+    Dk, Dv, bv = 128, 64, 64
+    per = Dk * bv - 1
+    n = (ys.size + per - 1) // per
+    ys = np.resize(ys, n * per)
+    k = 2.0 ** 5
+    x = np.empty((n, Dk * bv), np.float32)
+    x[:, 0] = np.float32(448.0 * k)                       # tile amax
+    x[:, 1:] = ys.reshape(n, per) * np.float32(k)
+    x = x.reshape(n, Dk, Dv)
+    y, scales, codes = B.gdn_qdq_state(torch.from_numpy(x).cuda(), 1, bv, return_codes=True)
+    torch.cuda.synchronize()
+    want, c, d = qdq32(x.reshape(n, Dk, 1, bv), 1, (1, 3))
+    assert np.all(d.reshape(-1) == np.float32(k))
+    np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32),
+                                  want.reshape(n, Dk, Dv).view(np.uint32))
+    np.testing.assert_array_equal(codes.cpu().numpy(), code_bytes(c.reshape(n, Dk, Dv), 1))
