@@ -68,7 +68,10 @@ struct FwdSmem {
     struct { float L[64 * C::LF]; float X[64 * C::LF]; } s;   // B..D
     bf16 W[C::NW][64 * C::LDK];                              // F..G: W codes or hi / lo
   } u;
-  float gam2[64], bet[64], eg[64], egc[64];   // log2-scaled cumsum, beta, gates
+  alignas(16) float gam2[64];                  // log2-scaled chunk-local cumsum of g
+  alignas(16) float bet[64];
+  alignas(16) float eg[64];                    // exp(gamma)
+  alignas(16) float egc[64];                   // exp(gamma_n - gamma), 0 past the chunk end
   float red[16];                               // 0..3 W amax, 4..7 S amax, 8 exp(gamma_n)
 };
 
@@ -122,6 +125,35 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ void lower_tile(int t, int& mi, int& mj) {
   mi = (t >= 1) + (t >= 3) + (t >= 6);
   mj = t - (mi * (mi + 1)) / 2;
+}
+
+
+// One 16x16 tile (mi, mj) of A B^T (A, B: [64][DK] row-major bf16 planes in
+// LDS) with all operand loads issued before the MFMA chain.
+template <int DK, int LD, int NIN>
+__device__ __forceinline__ f32x4 tile_abt(const bf16 (*A)[64 * LD], const bf16 (*B)[64 * LD],
+                                          int mi, int mj, int r16, int grp) {
+  constexpr int KS = DK / 32;
+  bf16x8 a0[KS], b0[KS], a1[KS], b1[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    a0[kk] = lds_nat(A[0], 16 * mi + r16, LD, 32 * kk, grp);
+    b0[kk] = lds_nat(B[0], 16 * mj + r16, LD, 32 * kk, grp);
+    if constexpr (NIN == 2) {
+      a1[kk] = lds_nat(A[1], 16 * mi + r16, LD, 32 * kk, grp);
+      b1[kk] = lds_nat(B[1], 16 * mj + r16, LD, 32 * kk, grp);
+    }
+  }
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    acc = mfma(a0[kk], b0[kk], acc);
+    if constexpr (NIN == 2) {
+      acc = mfma(a1[kk], b0[kk], acc);
+      acc = mfma(a0[kk], b1[kk], acc);
+    }
+  }
+  return acc;
 }
 
 template <int DK, bool F32IN, int SF, int WF>
@@ -198,6 +230,28 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
   };
   if (nchunks > 0) prefetch(bos, min(CHUNK, eos - bos));
 
+  // O of the previous chunk, stored once the next chunk's inputs have arrived:
+  // loads and stores share one completion counter, so storing right before
+  // the wait for the prefetched inputs would make that wait cover the stores.
+  f32x4 Oprev[4];
+  int64_t oprev_base = -1;
+  int oprev_nc = 0;
+  auto store_o = [&]() {
+    if (oprev_base < 0) return;
+    const int r16_ = __lane_id() & 15, grp_ = __lane_id() >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * grp_ + i;
+        if (row < oprev_nc) {
+          const int64_t off = oprev_base + r16_ + (int64_t)row * Hv * Dv;
+          if constexpr (F32IN) reinterpret_cast<float*>(a.o)[off] = Oprev[mt][i];
+          else reinterpret_cast<bf16*>(a.o)[off] = to_bf16(Oprev[mt][i]);
+        }
+      }
+  };
+
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = bos + c * CHUNK;
     const int nc = min(CHUNK, eos - t0);
@@ -265,35 +319,33 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
         sm.egc[lane] = valid ? fexp2(g2n - g2) : 0.f;
         if (lane == 0) sm.red[8] = fexp2(g2n);
       }
+      store_o();
       if (c + 1 < nchunks) prefetch(t0 + CHUNK, min(CHUNK, eos - t0 - CHUNK));
     }
     __syncthreads();
 
     // ------------------------------------- B: L = beta_i (K K^T) Gam, strict lower
     GDN_REFRESH();
-    for (int jb = wave; jb < 10; jb += 4) {
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const int jb = wave + 4 * it;
+      if (jb >= 10) break;
       int mi, mj;
       lower_tile(jb, mi, mj);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kk = 0; kk < DK / 32; ++kk) {
-        const bf16x8 a0 = lds_nat(sm.K[0], 16 * mi + r16, LDK, 32 * kk, grp);
-        const bf16x8 b0 = lds_nat(sm.K[0], 16 * mj + r16, LDK, 32 * kk, grp);
-        acc = mfma(a0, b0, acc);
-        if constexpr (F32IN) {
-          const bf16x8 a1 = lds_nat(sm.K[1], 16 * mi + r16, LDK, 32 * kk, grp);
-          const bf16x8 b1 = lds_nat(sm.K[1], 16 * mj + r16, LDK, 32 * kk, grp);
-          acc = mfma(a1, b0, acc);
-          acc = mfma(a0, b1, acc);
-        }
-      }
+      const f32x4 acc = tile_abt<DK, LDK, NIN>(sm.K, sm.K, mi, mj, r16, grp);
       const int cj = 16 * mj + r16;
       const float gj = sm.gam2[cj];
+      float gr[4], br[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gr[i] = sm.gam2[16 * mi + 4 * grp + i];
+        br[i] = sm.bet[16 * mi + 4 * grp + i];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * mi + 4 * grp + i;
-        sm.u.s.L[row * LF + cj] =
-            (row > cj) ? sm.bet[row] * acc[i] * fexp2(sm.gam2[row] - gj) : 0.f;
+        const float lv = br[i] * acc[i] * fexp2(gr[i] - gj);
+        sm.u.s.L[row * LF + cj] = (row > cj) ? lv : 0.f;
       }
     }
     __syncthreads();
@@ -364,32 +416,27 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
         }
       }
     } else {
-      for (int jb = wave - 1; jb < 10; jb += 3) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int jb = wave - 1 + 3 * it;
+        if (jb >= 10) break;
         int mi, mj;
         lower_tile(jb, mi, mj);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-          const bf16x8 a0 = lds_nat(sm.Q[0], 16 * mi + r16, LDK, 32 * kk, grp);
-          const bf16x8 b0 = lds_nat(sm.K[0], 16 * mj + r16, LDK, 32 * kk, grp);
-          acc = mfma(a0, b0, acc);
-          if constexpr (F32IN) {
-            const bf16x8 a1 = lds_nat(sm.Q[1], 16 * mi + r16, LDK, 32 * kk, grp);
-            const bf16x8 b1 = lds_nat(sm.K[1], 16 * mj + r16, LDK, 32 * kk, grp);
-            acc = mfma(a1, b0, acc);
-            acc = mfma(a0, b1, acc);
-          }
-        }
+        const f32x4 acc = tile_abt<DK, LDK, NIN>(sm.Q, sm.K, mi, mj, r16, grp);
         const int cj = 16 * mj + r16;
         const float gj = sm.gam2[cj];
+        float gr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gr[i] = sm.gam2[16 * mi + 4 * grp + i];
+        const int pc = pperm(cj);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * mi + 4 * grp + i;
-          const float pv = (row >= cj) ? acc[i] * fexp2(sm.gam2[row] - gj) : 0.f;
+          const float pv = (row >= cj) ? acc[i] * fexp2(gr[i] - gj) : 0.f;
           bf16 hi, lo;
           split2(pv, hi, lo);
-          sm.P[0][row * L64 + pperm(cj)] = hi;
-          sm.P[1][row * L64 + pperm(cj)] = lo;
+          sm.P[0][row * L64 + pc] = hi;
+          sm.P[1][row * L64 + pc] = lo;
         }
       }
     }
@@ -431,71 +478,87 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
         for (int i = 0; i < 4; ++i) put_T(32 + 16 * ti + 4 * grp + i, cj, -z[i], bc, ec);
       }
     } else {
+      bf16x8 ta[2][2], kb[NWC][NIN];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 th = lds_nat(sm.T[2], 16 * mt + r16, L64, 0, grp);
-        const bf16x8 tl = lds_nat(sm.T[3], 16 * mt + r16, L64, 0, grp);
+        ta[mt][0] = lds_nat(sm.T[2], 16 * mt + r16, L64, 0, grp);
+        ta[mt][1] = lds_nat(sm.T[3], 16 * mt + r16, L64, 0, grp);
+      }
+#pragma unroll
+      for (int d = 0; d < NWC; ++d)
+#pragma unroll
+        for (int pl = 0; pl < NIN; ++pl)
+          kb[d][pl] = lds_nat(sm.Kt[pl], 16 * (wct0 + d) + r16, L64, 0, grp);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int d = 0; d < NWC; ++d) {
-          const bf16x8 bk = lds_nat(sm.Kt[0], 16 * (wct0 + d) + r16, L64, 0, grp);
-          f32x4 acc = mfma(th, bk, zero4());
-          acc = mfma(tl, bk, acc);
-          if constexpr (F32IN) {
-            const bf16x8 bkl = lds_nat(sm.Kt[1], 16 * (wct0 + d) + r16, L64, 0, grp);
-            acc = mfma(th, bkl, acc);
-          }
+          f32x4 acc = mfma(ta[mt][0], kb[d][0], zero4());
+          acc = mfma(ta[mt][1], kb[d][0], acc);
+          if constexpr (F32IN) acc = mfma(ta[mt][0], kb[d][NIN - 1], acc);
           Wt[mt][d] = acc;
         }
-      }
     }
     __syncthreads();
 
     // ------------------- E: W rows 32..63 (waves 0, 1), U = T V, amax partials
     GDN_REFRESH();
     if (wave < 2) {
+      bf16x8 ta[2][2][2], kb[2][NWC][NIN];            // [t][kk][hi/lo], [kk][d][plane]
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int mt = 2 + t;
-        bf16x8 th[2], tl[2];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          th[kk] = lds_nat(sm.T[2], 16 * mt + r16, L64, 32 * kk, grp);
-          tl[kk] = lds_nat(sm.T[3], 16 * mt + r16, L64, 32 * kk, grp);
+          ta[t][kk][0] = lds_nat(sm.T[2], 16 * (2 + t) + r16, L64, 32 * kk, grp);
+          ta[t][kk][1] = lds_nat(sm.T[3], 16 * (2 + t) + r16, L64, 32 * kk, grp);
         }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int d = 0; d < NWC; ++d)
+#pragma unroll
+          for (int pl = 0; pl < NIN; ++pl)
+            kb[kk][d][pl] = lds_nat(sm.Kt[pl], 16 * (wct0 + d) + r16, L64, 32 * kk, grp);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int d = 0; d < NWC; ++d) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 bk = lds_nat(sm.Kt[0], 16 * (wct0 + d) + r16, L64, 32 * kk, grp);
-            acc = mfma(th[kk], bk, acc);
-            acc = mfma(tl[kk], bk, acc);
-            if constexpr (F32IN) {
-              const bf16x8 bkl = lds_nat(sm.Kt[1], 16 * (wct0 + d) + r16, L64, 32 * kk, grp);
-              acc = mfma(th[kk], bkl, acc);
-            }
+            acc = mfma(ta[t][kk][0], kb[kk][d][0], acc);
+            acc = mfma(ta[t][kk][1], kb[kk][d][0], acc);
+            if constexpr (F32IN) acc = mfma(ta[t][kk][0], kb[kk][d][NIN - 1], acc);
           }
           Wt[t][d] = acc;
         }
-      }
     }
     f32x4 U[4];
+    {
+      bf16x8 ua[2][4][2], vb_[2][NIN];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
+      for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 bv = lds_nat(sm.Vt[0], wave * 16 + r16, L64, 32 * kk, grp);
-      bf16x8 bvl;
-      if constexpr (F32IN) bvl = lds_nat(sm.Vt[1], wave * 16 + r16, L64, 32 * kk, grp);
+        for (int pl = 0; pl < NIN; ++pl)
+          vb_[kk][pl] = lds_nat(sm.Vt[pl], wave * 16 + r16, L64, 32 * kk, grp);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (kk > mt / 2) continue;                    // T is lower triangular
-        const bf16x8 th = lds_nat(sm.T[0], 16 * mt + r16, L64, 32 * kk, grp);
-        const bf16x8 tl = lds_nat(sm.T[1], 16 * mt + r16, L64, 32 * kk, grp);
-        U[mt] = mfma(th, bv, U[mt]);
-        U[mt] = mfma(tl, bv, U[mt]);
-        if constexpr (F32IN) U[mt] = mfma(th, bvl, U[mt]);
+        for (int mt = 0; mt < 4; ++mt) {
+          if (kk > mt / 2) continue;                  // T is lower triangular
+          ua[kk][mt][0] = lds_nat(sm.T[0], 16 * mt + r16, L64, 32 * kk, grp);
+          ua[kk][mt][1] = lds_nat(sm.T[1], 16 * mt + r16, L64, 32 * kk, grp);
+        }
       }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          if (kk > mt / 2) continue;
+          U[mt] = mfma(ua[kk][mt][0], vb_[kk][0], U[mt]);
+          U[mt] = mfma(ua[kk][mt][1], vb_[kk][0], U[mt]);
+          if constexpr (F32IN) U[mt] = mfma(ua[kk][mt][0], vb_[kk][NIN - 1], U[mt]);
+        }
     }
     if constexpr (WF != 0) {
       float m = 0.f;
@@ -609,25 +672,36 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
     f32x4 accw[4], accq[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) accw[mt] = accq[mt] = zero4();
+    {
+      // operands of k-step kk + 1 are loaded while k-step kk multiplies
+      constexpr int NA = 2 + (WF == 0 ? 1 : 0) + (F32IN ? 1 : 0);   // A planes per row tile
+      bf16x8 opA[2][4][NA];
+      auto load_k = [&](int kk, bf16x8 (&dst)[4][NA]) {
 #pragma unroll
-    for (int kk = 0; kk < MK / 2; ++kk) {
+        for (int mt = 0; mt < 4; ++mt) {
+          dst[mt][0] = lds_nat(sm.u.W[0], 16 * mt + r16, LDK, 32 * kk, grp);
+          dst[mt][1] = lds_nat(sm.Q[0], 16 * mt + r16, LDK, 32 * kk, grp);
+          int q = 2;
+          if constexpr (WF == 0) dst[mt][q++] = lds_nat(sm.u.W[C::NW - 1], 16 * mt + r16, LDK, 32 * kk, grp);
+          if constexpr (F32IN) dst[mt][q++] = lds_nat(sm.Q[NIN - 1], 16 * mt + r16, LDK, 32 * kk, grp);
+        }
+      };
+      load_k(0, opA[0]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 w0 = lds_nat(sm.u.W[0], 16 * mt + r16, LDK, 32 * kk, grp);
-        const bf16x8 q0 = lds_nat(sm.Q[0], 16 * mt + r16, LDK, 32 * kk, grp);
-        accw[mt] = mfma(w0, bSh[kk], accw[mt]);
-        accq[mt] = mfma(q0, bSh[kk], accq[mt]);
-        if constexpr (WF == 0) {
-          const bf16x8 w1 = lds_nat(sm.u.W[C::NW - 1], 16 * mt + r16, LDK, 32 * kk, grp);
-          accw[mt] = mfma(w1, bSh[kk], accw[mt]);
-        }
-        if constexpr (F32IN) {
-          const bf16x8 q1 = lds_nat(sm.Q[NIN - 1], 16 * mt + r16, LDK, 32 * kk, grp);
-          accq[mt] = mfma(q1, bSh[kk], accq[mt]);
-        }
-        if constexpr (SF == 0) {
-          accw[mt] = mfma(w0, bSl[kk], accw[mt]);
-          accq[mt] = mfma(q0, bSl[kk], accq[mt]);
+      for (int kk = 0; kk < MK / 2; ++kk) {
+        if (kk + 1 < MK / 2) load_k(kk + 1, opA[(kk + 1) & 1]);
+        const auto& op = opA[kk & 1];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          accw[mt] = mfma(op[mt][0], bSh[kk], accw[mt]);
+          accq[mt] = mfma(op[mt][1], bSh[kk], accq[mt]);
+          int q = 2;
+          if constexpr (WF == 0) accw[mt] = mfma(op[mt][q++], bSh[kk], accw[mt]);
+          if constexpr (F32IN) accq[mt] = mfma(op[mt][q++], bSh[kk], accq[mt]);
+          if constexpr (SF == 0) {
+            accw[mt] = mfma(op[mt][0], bSl[kk], accw[mt]);
+            accq[mt] = mfma(op[mt][1], bSl[kk], accq[mt]);
+          }
         }
       }
     }
@@ -647,11 +721,13 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       pack_pair_split(Vn[2 * kk], Vn[2 * kk + 1], bVh[kk], bVl[kk]);
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sm.egc[32 * kk + 4 * grp]);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sm.egc[32 * kk + 16 + 4 * grp]);
       f32x4 d0, d1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        d0[i] = sm.egc[32 * kk + 4 * grp + i] * Vn[2 * kk][i];
-        d1[i] = sm.egc[32 * kk + 16 + 4 * grp + i] * Vn[2 * kk + 1][i];
+        d0[i] = e0[i] * Vn[2 * kk][i];
+        d1[i] = e1[i] * Vn[2 * kk + 1][i];
       }
       pack_pair_split(d0, d1, bDh[kk], bDl[kk]);
     }
@@ -661,29 +737,36 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
       f32x4 aco[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) aco[mt] = zero4();
+      bf16x8 pop[2][4][2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          if (kk > mt / 2) continue;
+          pop[kk][mt][0] = lds_nat(sm.P[0], 16 * mt + r16, L64, 32 * kk, grp);
+          pop[kk][mt][1] = lds_nat(sm.P[1], 16 * mt + r16, L64, 32 * kk, grp);
+        }
+      float egr[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) egr[mt][i] = sm.eg[16 * mt + 4 * grp + i];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           if (kk > mt / 2) continue;
-          const bf16x8 ph = lds_nat(sm.P[0], 16 * mt + r16, L64, 32 * kk, grp);
-          const bf16x8 pl = lds_nat(sm.P[1], 16 * mt + r16, L64, 32 * kk, grp);
-          aco[mt] = mfma(ph, bVh[kk], aco[mt]);
-          aco[mt] = mfma(pl, bVh[kk], aco[mt]);
-          aco[mt] = mfma(ph, bVl[kk], aco[mt]);
+          aco[mt] = mfma(pop[kk][mt][0], bVh[kk], aco[mt]);
+          aco[mt] = mfma(pop[kk][mt][1], bVh[kk], aco[mt]);
+          aco[mt] = mfma(pop[kk][mt][0], bVl[kk], aco[mt]);
         }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * mt + 4 * grp + i;
-          if (row < nc) {
-            const float ov = a.scale * (sm.eg[row] * accq[mt][i] + aco[mt][i]);
-            if constexpr (F32IN) reinterpret_cast<float*>(a.o)[obase + row * Hv * Dv] = ov;
-            else reinterpret_cast<bf16*>(a.o)[obase + row * Hv * Dv] = to_bf16(ov);
-          }
-        }
+        for (int i = 0; i < 4; ++i) Oprev[mt][i] = a.scale * (egr[mt][i] * accq[mt][i] + aco[mt][i]);
+      oprev_base = obase - r16;
+      oprev_nc = nc;
     }
     // S = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew), accumulated in place
     {
@@ -692,23 +775,28 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
       for (int mt = 0; mt < MK; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[mt][i] = egC * ((SF != 0) ? S[mt][i] * dS : S[mt][i]);
+      bf16x8 kop[2][MK][NIN];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+          for (int pl = 0; pl < NIN; ++pl)
+            kop[kk][mt][pl] = lds_nat(sm.Kt[pl], 16 * mt + r16, L64, 32 * kk, grp);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int mt = 0; mt < MK; ++mt) {
-          const bf16x8 kt = lds_nat(sm.Kt[0], 16 * mt + r16, L64, 32 * kk, grp);
-          S[mt] = mfma(kt, bDh[kk], S[mt]);
-          S[mt] = mfma(kt, bDl[kk], S[mt]);
-          if constexpr (F32IN) {
-            const bf16x8 ktl = lds_nat(sm.Kt[1], 16 * mt + r16, L64, 32 * kk, grp);
-            S[mt] = mfma(ktl, bDh[kk], S[mt]);
-          }
+          S[mt] = mfma(kop[kk][mt][0], bDh[kk], S[mt]);
+          S[mt] = mfma(kop[kk][mt][0], bDl[kk], S[mt]);
+          if constexpr (F32IN) S[mt] = mfma(kop[kk][mt][NIN - 1], bDh[kk], S[mt]);
         }
       }
     }
     __syncthreads();                                  // LDS reused by the next chunk
   }
 
+  store_o();
   if (a.ht) {
     GDN_REFRESH();
 #pragma unroll
