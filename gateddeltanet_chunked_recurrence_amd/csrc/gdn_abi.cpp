@@ -152,6 +152,30 @@ gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
   return c;
 }
 
+// Backward workspace sections (FP32, each 256-byte aligned):
+//   X      [num_slots, Hv, 64, 64]   (I + L)^-1 of every chunk
+//   W      [B*T, Hv, Dk]             the W of the products (dequantized Wq, or W)
+//   dstate [num_slots, Hv, Dk, Dv]   gradient of the state at each chunk end
+//   dvn    [num_slots, Hv, 64, Dv]   gradient of Vnew per chunk
+//   dqk    [B*T, Hv, 2, Dk]          dq, dk per value head before the group sum
+struct BwdWsLayout {
+  int64_t X, W, dstate, dvn, dqk, total;
+};
+
+BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
+  const gdn_saved_layout_t L = layout_of(a);
+  const int64_t tokens = (int64_t)a->B * a->T, S = L.num_slots, Hv = a->Hv;
+  BwdWsLayout w{};
+  int64_t off = 0;
+  w.X = off;       off += round256(S * Hv * 64 * 64 * 4);
+  w.W = off;       off += round256(tokens * Hv * a->Dk * 4);
+  w.dstate = off;  off += round256(S * Hv * a->Dk * a->Dv * 4);
+  w.dvn = off;     off += round256(S * Hv * 64 * a->Dv * 4);
+  w.dqk = off;     off += round256(tokens * Hv * 2 * a->Dk * 4);
+  w.total = off;
+  return w;
+}
+
 gdn_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return GDN_OK;
@@ -189,11 +213,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) {
 
 size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a) {
   if (!a || check_fwd_shape(&a->fwd) != GDN_OK) return 0;
-  const gdn_saved_layout_t L = layout_of(&a->fwd);
-  const int64_t tokens = (int64_t)a->fwd.B * a->fwd.T;
-  const int64_t dstate = round256(L.num_slots * a->fwd.Hv * a->fwd.Dk * a->fwd.Dv * 4);
-  const int64_t dqk = round256(tokens * a->fwd.Hv * 2 * a->fwd.Dk * 4);
-  return (size_t)(dstate + dqk);
+  return (size_t)bwd_ws_layout(&a->fwd).total;
 }
 
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
@@ -230,9 +250,12 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   k.dbeta = a->dbeta;
   k.dh0 = a->dh0;
   char* ws = static_cast<char*>(a->workspace);
-  k.ws_dstate = reinterpret_cast<float*>(ws);
-  k.ws_dqk = reinterpret_cast<float*>(ws + round256(L.num_slots * a->fwd.Hv * a->fwd.Dk *
-                                                    a->fwd.Dv * 4));
+  const BwdWsLayout W = bwd_ws_layout(&a->fwd);
+  k.ws_X = reinterpret_cast<float*>(ws + W.X);
+  k.ws_W = reinterpret_cast<float*>(ws + W.W);
+  k.ws_dstate = reinterpret_cast<float*>(ws + W.dstate);
+  k.ws_dvn = reinterpret_cast<float*>(ws + W.dvn);
+  k.ws_dqk = reinterpret_cast<float*>(ws + W.dqk);
   k.grad_f32 = a->grad_dtype == GDN_F32;
   k.total_tokens = (int32_t)tokens;
   k.num_slots = (int32_t)L.num_slots;

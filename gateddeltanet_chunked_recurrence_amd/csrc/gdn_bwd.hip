@@ -1,11 +1,735 @@
-// Backward kernels (identity straight-through at both QDQ sites).
+// Backward of the chunked gated delta rule with the identity straight-through
+// estimator at both QDQ sites ("[1/4] GDN state/W QAT foundation", "What does
+// this PR do?": identity STE, the forward's quantized W reused by the
+// backward). The forward's quantized values Sq and Wq (saved as one-byte codes
+// and scales) are the values used in every product, and their gradients pass
+// through unchanged.
+//
+// Per chunk (forward, see include/gdn.h):
+//   Vnew = U - Wq Sq,  U = T V,  W = T diag(e^gamma) K,  T = X diag(beta),
+//   X = (I + L)^-1,  L_ij = beta_i (k_i . k_j) Gam_ij (i > j)
+//   O = scale (diag(e^gamma) Q Sq + P Vnew),  P = (Q K^T) * Gam (i >= j)
+//   S' = e^gamma_n Sq + Kd^T Vnew,  Kd = diag(e^(gamma_n - gamma)) K
+// Reverse mode, with dS' the gradient of the state after the chunk:
+//   dVnew = scale P^T dO + Kd dS'
+//   dS    = e^gamma_n dS' + scale (diag(e^gamma) Q)^T dO - Wq^T dVnew   (STE)
+//   dW    = -dVnew Sq^T (STE),  dU = dVnew,  dV = T^T dU
+//   dQ    = scale diag(e^gamma) dO Sq^T + G K,      G = scale (dO Vnew^T) * Gam
+//   dK    = G^T Q + Kd-term + diag(e^gamma) T^T dW + (dA + dA^T) K
+//   dT    = dW (diag(e^gamma) K)^T + dU V^T,  dX = dT diag(beta)
+//   dL    = -(X^T dX X^T) strictly lower,  dA_ij = dL_ij beta_i Gam_ij
+// plus the gate terms (d gamma) and d beta; dg is the reverse chunk-local
+// cumsum of d gamma.
+//
+// Kernels (all FP32 arithmetic, FP32 MFMA 16x16x4):
+//   bwd_prep    per (chunk, head): X by the blocked solve; the W of the products
+//   bwd_dstate  per (sequence, head, 64-wide value block), chunks in reverse:
+//               the dS recurrence; writes dS' and dVnew of every chunk, and dh0
+//   bwd_chunk   per (chunk, head): Vnew, dv, and every chunk-local gradient
+//   bwd_group   per (token, query/key head): dq, dk summed over the head group
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-hipError_t launch_bwd(const BwdConfig&, const BwdKernelArgs&, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int NT = 256;          // threads per workgroup
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct Chunk {
+  int n, c, t0, nc;
+  bool valid;
+};
+
+// Chunk of a slot (slot = n + bos_n / 64 + c, increasing in n; see gdn.h).
+__device__ Chunk locate_slot(int slot, const int32_t* cu, int N, int T) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int bos = cu ? cu[mid] : mid * T;
+    if (mid + bos / CHUNK <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int bos = cu ? cu[lo] : lo * T;
+  const int eos = cu ? cu[lo + 1] : (lo + 1) * T;
+  Chunk ch;
+  ch.n = lo;
+  ch.c = slot - (lo + bos / CHUNK);
+  ch.t0 = bos + CHUNK * ch.c;
+  ch.nc = min(CHUNK, eos - ch.t0);
+  ch.valid = ch.c >= 0 && ch.t0 < eos;
+  return ch;
+}
+
+struct Gates {
+  alignas(16) float gam2[64];    // log2-scaled chunk-local cumsum
+  alignas(16) float eg[64];      // e^gamma
+  alignas(16) float egc[64];     // e^(gamma_n - gamma), 0 past the chunk end
+  alignas(16) float bet[64];
+  float egC;                     // e^gamma_n
+};
+
+// Wave 0 forms the gates of one chunk (rows past nc: g = beta = 0).
+__device__ void load_gates(Gates& gs, const float* g, const float* beta, int t0, int nc,
+                           int Hv, int h, int wave, int lane) {
+  if (wave != 0) return;
+  const bool valid = lane < nc;
+  const int64_t gi = (int64_t)(t0 + lane) * Hv + h;
+  const float g2 = wave_incl_scan(valid ? g[gi] * LOG2E : 0.f, lane);
+  const float g2n = __shfl(g2, nc - 1, WAVE);
+  gs.gam2[lane] = g2;
+  gs.eg[lane] = fexp2(g2);
+  gs.egc[lane] = valid ? fexp2(g2n - g2) : 0.f;
+  gs.bet[lane] = valid ? beta[gi] : 0.f;
+  if (lane == 0) gs.egC = fexp2(g2n);
+}
+
+// acc += sum_{k in [k0, k1)} A(i0 + r, k) B(k, j0 + c) for one 16x16 tile, with
+// A(i, k) = A[i * ars + k * acs] and B(k, j) = B[k * brs + j * bcs] (FP32).
+__device__ __forceinline__ f32x4 mm(const float* A, int ars, int acs, const float* B, int brs,
+                                    int bcs, int i0, int j0, int k0, int k1, int r16, int grp,
+                                    f32x4 acc) {
+  for (int k = k0; k < k1; k += 4)
+    acc = mfma_f32(A[(i0 + r16) * ars + (k + grp) * acs], B[(k + grp) * brs + (j0 + r16) * bcs], acc);
+  return acc;
+}
+
+// acc += A(i0 + r, .) Breg, where Breg holds KT accumulator tiles of a
+// [16 KT x 16] B block (Breg[t][i] = B[16 t + 4 grp + i][c]); K runs in the
+// matching order. A(i, k) = A[i * ars + k * acs].
+template <int KT>
+__device__ __forceinline__ f32x4 mm_reg(const float* A, int ars, int acs, const f32x4 (&Breg)[KT],
+                                        int i0, int r16, int grp, f32x4 acc) {
+#pragma unroll
+  for (int t = 0; t < KT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = mfma_f32(A[(i0 + r16) * ars + (16 * t + 4 * grp + i) * acs], Breg[t][i], acc);
+  return acc;
+}
+
+// Loads 64 rows x D columns of a [tokens, H, D_total] input (bf16 or FP32)
+// starting at column col0 into an FP32 LDS tile with row stride ld; rows past
+// nc become 0.
+template <bool F32IN>
+__device__ void stage_rows(float* dst, int ld, const void* src, int t0, int nc, int H, int h,
+                           int Dtot, int col0, int D, int tid) {
+  for (int e = tid; e < 64 * D; e += NT) {
+    const int r = e / D, cc = e % D;
+    float v = 0.f;
+    if (r < nc) {
+      const int64_t off = ((int64_t)(t0 + r) * H + h) * Dtot + col0 + cc;
+      v = F32IN ? reinterpret_cast<const float*>(src)[off]
+                : static_cast<float>(reinterpret_cast<const bf16*>(src)[off]);
+    }
+    dst[r * ld + cc] = v;
+  }
+}
+
+// X = (I + L)^-1 for strictly lower L (FP32 [64][65] in LDS): 16x16 diagonal
+// blocks by substitution, then the 16- and 32-block merges
+// X_BA = -X_BB (L_BA X_AA). Yf is a [32][33] scratch. All threads call it;
+// it ends after a barrier.
+__device__ void solve64(const float* Lf, float* Xf, float* Yf, int wave, int lane) {
+  const int r16 = lane & 15, grp = lane >> 4, tid = wave * 64 + lane;
+  for (int e = tid; e < 64 * 64; e += NT) {
+    const int i = e >> 6, j = e & 63;
+    if ((j >> 4) > (i >> 4)) Xf[i * 65 + j] = 0.f;
+  }
+  if (lane < 16) {
+    const int b = wave, cc = lane;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < r; ++j) s -= Lf[(16 * b + r) * 65 + 16 * b + j] * x[j];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xf[(16 * b + r) * 65 + 16 * b + cc] = x[r];
+  }
+  __syncthreads();
+  if (wave < 2) {
+    const int A = 2 * wave, B = A + 1;
+    const f32x4 y = mm(Lf + 16 * B * 65 + 16 * A, 65, 1, Xf + 16 * A * 65 + 16 * A, 65, 1, 0, 0,
+                       0, 16, r16, grp, zero4());
+    f32x4 z = zero4();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z = mfma_f32(Xf[(16 * B + r16) * 65 + 16 * B + 4 * grp + i], y[i], z);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Xf[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
+  }
+  __syncthreads();
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+    const f32x4 y = mm(Lf + 32 * 65, 65, 1, Xf, 65, 1, 16 * ti, 16 * tj, 0, 32, r16, grp, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Yf[(16 * ti + 4 * grp + i) * 33 + 16 * tj + r16] = y[i];
+  }
+  __syncthreads();
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+    const f32x4 z = mm(Xf + 32 * 65 + 32, 65, 1, Yf, 33, 1, 16 * ti, 16 * tj, 0, 32, r16, grp, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Xf[(32 + 16 * ti + 4 * grp + i) * 65 + 16 * tj + r16] = -z[i];
+  }
+  __syncthreads();
+}
+
+// L_ij = beta_i (K K^T)_ij Gam_ij for i > j (else 0) into Lf [64][65].
+template <int DK>
+__device__ void build_L(const float* Kf, const Gates& gs, float* Lf, int wave, int lane) {
+  constexpr int LK = DK + 1;
+  const int r16 = lane & 15, grp = lane >> 4;
+  for (int t = wave; t < 16; t += 4) {
+    const int mi = t >> 2, mj = t & 3;
+    const f32x4 a = mm(Kf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4());
+    const int cj = 16 * mj + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mi + 4 * grp + i;
+      Lf[row * 65 + cj] = row > cj ? gs.bet[row] * a[i] * fexp2(gs.gam2[row] - gs.gam2[cj]) : 0.f;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bwd_prep
+template <int DK, bool F32IN, int WF>
+__global__ void __launch_bounds__(NT, 1) bwd_prep(BwdKernelArgs a, int N) {
+  constexpr int LK = DK + 1;
+  __shared__ float Kf[64 * LK];
+  __shared__ float Lf[64 * 65], Xf[64 * 65], Yf[32 * 33];
+  __shared__ Gates gs;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const FwdKernelArgs& f = a.f;
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  if (!ch.valid) return;
+  const int Hv = f.Hv, Hqk = f.Hqk, hk = h / (Hv / Hqk);
+
+  stage_rows<F32IN>(Kf, LK, f.k, ch.t0, ch.nc, Hqk, hk, DK, 0, DK, tid);
+  load_gates(gs, f.g, f.beta, ch.t0, ch.nc, Hv, h, wave, lane);
+  __syncthreads();
+  build_L<DK>(Kf, gs, Lf, wave, lane);
+  __syncthreads();
+  solve64(Lf, Xf, Yf, wave, lane);
+
+  float* Xg = a.ws_X + ((int64_t)slot * Hv + h) * 4096;
+  for (int e = tid; e < 4096; e += NT) Xg[e] = Xf[(e >> 6) * 65 + (e & 63)];
+
+  float* Wg = a.ws_W + ((int64_t)ch.t0 * Hv + h) * DK;
+  if constexpr (WF != 0) {
+    const float dW = f.w_scale[(int64_t)slot * Hv + h];
+    const uint8_t* codes = f.w_codes + ((int64_t)ch.t0 * Hv + h) * DK;
+    for (int e = tid; e < ch.nc * DK; e += NT) {
+      const int r = e / DK, cc = e % DK;
+      const int64_t off = (int64_t)r * Hv * DK + cc;
+      const uint8_t b = codes[off];
+      const float cv = WF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(b), 0)
+                               : static_cast<float>(static_cast<int8_t>(b));
+      Wg[off] = cv * dW;
+    }
+  } else {
+    // T' = X diag(beta e^gamma) into Lf, then W = T' K
+    for (int e = tid; e < 4096; e += NT) {
+      const int i = e >> 6, j = e & 63;
+      Lf[i * 65 + j] = Xf[i * 65 + j] * gs.bet[j] * gs.eg[j];
+    }
+    __syncthreads();
+    for (int t = wave; t < 4 * (DK / 16); t += 4) {
+      const int mt = t & 3, nt = t >> 2;
+      const f32x4 w = mm(Lf, 65, 1, Kf, LK, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * grp + i;
+        if (row < ch.nc) Wg[(int64_t)row * Hv * DK + 16 * nt + r16] = w[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_dstate
+template <int DK, bool F32IN>
+__global__ void __launch_bounds__(NT, 1) bwd_dstate(BwdKernelArgs a) {
+  constexpr int LK = DK + 1, MK = DK / 16;
+  __shared__ float Qf[64 * LK], Kf[64 * LK], Wf[64 * LK];
+  __shared__ float dOf[64 * 65], Pf[64 * 65];
+  __shared__ Gates gs;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const FwdKernelArgs& f = a.f;
+  const int vb = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+  const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, hk = h / (Hv / Hqk);
+  int bos, eos;
+  if (f.cu_seqlens) {
+    bos = f.cu_seqlens[n];
+    eos = f.cu_seqlens[n + 1];
+  } else {
+    bos = n * f.T;
+    eos = bos + f.T;
+  }
+  const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
+  const int col = vb * 64 + 16 * wave + r16;        // this lane's value column
+  const int64_t sbase = ((int64_t)n * Hv + h) * DK * Dv;
+
+  f32x4 dS[MK];                                     // dS[mt][i] = dS[16 mt + 4 grp + i][col]
+#pragma unroll
+  for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dS[mt][i] = a.dht ? a.dht[sbase + (int64_t)(16 * mt + 4 * grp + i) * Dv + col] : 0.f;
+
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const int t0 = bos + CHUNK * c, nc = min(CHUNK, eos - t0);
+    const int slot = n + bos / CHUNK + c;
+    stage_rows<F32IN>(Qf, LK, f.q, t0, nc, Hqk, hk, DK, 0, DK, tid);
+    stage_rows<F32IN>(Kf, LK, f.k, t0, nc, Hqk, hk, DK, 0, DK, tid);
+    for (int e = tid; e < 64 * DK; e += NT) {
+      const int r = e / DK, cc = e % DK;
+      Wf[r * LK + cc] = r < nc ? a.ws_W[((int64_t)(t0 + r) * Hv + h) * DK + cc] : 0.f;
+    }
+    stage_rows<F32IN>(dOf, 65, a.dout, t0, nc, Hv, h, Dv, vb * 64, 64, tid);
+    load_gates(gs, f.g, f.beta, t0, nc, Hv, h, wave, lane);
+    __syncthreads();
+
+    // P = (Q K^T) * Gam, lower including the diagonal
+    for (int t = wave; t < 16; t += 4) {
+      const int mi = t >> 2, mj = t & 3;
+      const f32x4 p = mm(Qf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4());
+      const int cj = 16 * mj + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mi + 4 * grp + i;
+        Pf[row * 65 + cj] = row >= cj ? p[i] * fexp2(gs.gam2[row] - gs.gam2[cj]) : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // dS' of this chunk (the gradient at its end), kept for bwd_chunk
+    {
+      float* dsg = a.ws_dstate + ((int64_t)slot * Hv + h) * DK * Dv + col;
+#pragma unroll
+      for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsg[(int64_t)(16 * mt + 4 * grp + i) * Dv] = dS[mt][i];
+    }
+    // dVnew = scale P^T dO + diag(egc) K dS'
+    f32x4 dVn[4];
+    float* dvg = a.ws_dvn + ((int64_t)slot * Hv + h) * 64 * Dv + col;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 p = mm(Pf, 1, 65, dOf, 65, 1, 16 * mt, 16 * wave, 0, 64, r16, grp, zero4());
+      const f32x4 q = mm_reg<MK>(Kf, LK, 1, dS, 16 * mt, r16, grp, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * grp + i;
+        dVn[mt][i] = f.scale * p[i] + gs.egc[row] * q[i];
+        dvg[(int64_t)row * Dv] = dVn[mt][i];
+      }
+    }
+    __syncthreads();                                 // dOf fully read
+    for (int e = tid; e < 64 * 64; e += NT) dOf[(e >> 6) * 65 + (e & 63)] *= gs.eg[e >> 6];
+    __syncthreads();
+    // dS = e^gamma_n dS' + scale Q^T (diag(e^gamma) dO) - W^T dVnew
+    const float egC = gs.egC;
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt) {
+      const f32x4 q = mm(Qf, 1, LK, dOf, 65, 1, 16 * mt, 16 * wave, 0, 64, r16, grp, zero4());
+      const f32x4 w = mm_reg<4>(Wf, 1, LK, dVn, 16 * mt, r16, grp, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[mt][i] = egC * dS[mt][i] + f.scale * q[i] - w[i];
+    }
+    __syncthreads();                                 // LDS reused by the next chunk
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.dh0[sbase + (int64_t)(16 * mt + 4 * grp + i) * Dv + col] = dS[mt][i];
+  }
+}
+
+// ----------------------------------------------------------------- bwd_chunk
+template <int DK>
+struct ChunkSmem {
+  static constexpr int LK = DK + 1;
+  union {
+    struct {                    // value-block loop
+      float Tf[64 * 65];        // T = X diag(beta)
+      float Wf[64 * LK];
+      float Vf[64 * 33], dOf[64 * 33], Vnf[64 * 33], dVnf[64 * 33];
+      float Sqf[DK * 33], dSf[DK * 33];
+    } p1;
+    struct {                    // chunk-local finish
+      float Kf[64 * LK], Qf[64 * LK];
+      float Xf[64 * 65], Gf[64 * 65];
+      float dWf[64 * LK];
+    } p2;
+  } u;
+  Gates gs;
+  // per-wave column partials (summed in a fixed order: deterministic)
+  float colH[4][64];            // column sums of H = G * (Q K^T)
+  float colHL[4][64];           // column sums of dL * L
+  float colDB[4][64];           // column sums of dT * X (d beta from T = X diag(beta))
+  // per-row totals (each row lives in one wave)
+  float rowDG[64];              // d gamma row parts
+  float rowTerm[64];            // egc_j k_j . (Vnew dS'^T)_j  (state-update gate term)
+  float rowDB[64];              // d beta from L
+  float red[4];                 // <dS', Sq> per wave
+};
+
+template <int DK, bool F32IN, int SF>
+__global__ void __launch_bounds__(NT, 1) bwd_chunk(BwdKernelArgs a, int N) {
+  constexpr int LK = DK + 1, NC = DK / 16;         // column tiles of a [64, DK] matrix
+  __shared__ ChunkSmem<DK> sm;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const FwdKernelArgs& f = a.f;
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  if (!ch.valid) return;
+  const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, hk = h / (Hv / Hqk);
+  const int t0 = ch.t0, nc = ch.nc;
+  const float scale = f.scale;
+  Gates& gs = sm.gs;
+  const int64_t ch_base = (int64_t)slot * Hv + h;
+
+  load_gates(gs, f.g, f.beta, t0, nc, Hv, h, wave, lane);
+  __syncthreads();
+  {
+    const float* Xg = a.ws_X + ch_base * 4096;
+    for (int e = tid; e < 4096; e += NT) {
+      const int i = e >> 6, j = e & 63;
+      sm.u.p1.Tf[i * 65 + j] = Xg[e] * gs.bet[j];
+    }
+    for (int e = tid; e < 64 * DK; e += NT) {
+      const int r = e / DK, cc = e % DK;
+      sm.u.p1.Wf[r * LK + cc] = r < nc ? a.ws_W[((int64_t)(t0 + r) * Hv + h) * DK + cc] : 0.f;
+    }
+  }
+
+  // accumulators over value blocks; wave w owns row tile w of each
+  f32x4 dW[NC], dQi[NC], dKs[NC], dP[4], dTU[4];
+#pragma unroll
+  for (int q = 0; q < NC; ++q) dW[q] = dQi[q] = dKs[q] = zero4();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dP[q] = dTU[q] = zero4();
+  float sSq = 0.f;
+
+  for (int v0 = 0; v0 < Dv; v0 += 32) {
+    auto& p1 = sm.u.p1;
+    stage_rows<F32IN>(p1.Vf, 33, f.v, t0, nc, Hv, h, Dv, v0, 32, tid);
+    stage_rows<F32IN>(p1.dOf, 33, a.dout, t0, nc, Hv, h, Dv, v0, 32, tid);
+    {
+      const float* dvg = a.ws_dvn + ch_base * 64 * Dv;
+      const float* dsg = a.ws_dstate + ch_base * DK * Dv;
+      for (int e = tid; e < 64 * 32; e += NT) {
+        const int r = e >> 5, cc = e & 31;
+        p1.dVnf[r * 33 + cc] = dvg[(int64_t)r * Dv + v0 + cc];
+      }
+      for (int e = tid; e < DK * 32; e += NT) {
+        const int r = e >> 5, cc = e & 31;
+        p1.dSf[r * 33 + cc] = dsg[(int64_t)r * Dv + v0 + cc];
+        float sq;
+        if constexpr (SF == 0) {
+          sq = f.s_f32[ch_base * DK * Dv + (int64_t)r * Dv + v0 + cc];
+        } else {
+          const uint8_t b = f.s_codes[ch_base * DK * Dv + (int64_t)r * Dv + v0 + cc];
+          const float cv = SF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(b), 0)
+                                   : static_cast<float>(static_cast<int8_t>(b));
+          sq = cv * f.s_scale[ch_base * (Dv / f.block_v) + (v0 + cc) / f.block_v];
+        }
+        p1.Sqf[r * 33 + cc] = sq;
+      }
+    }
+    __syncthreads();
+    // Vnew = T V - W Sq and dV = T^T dVnew for this block (8 tiles, 2 per wave)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int mt = wave, nt = q;
+      f32x4 u = mm(p1.Tf, 65, 1, p1.Vf, 33, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, zero4());
+      const f32x4 ws = mm(p1.Wf, LK, 1, p1.Sqf, 33, 1, 16 * mt, 16 * nt, 0, DK, r16, grp, zero4());
+      const f32x4 dv = mm(p1.Tf, 1, 65, p1.dVnf, 33, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * mt + 4 * grp + i;
+        p1.Vnf[row * 33 + 16 * nt + r16] = u[i] - ws[i];
+        if (row < nc) {
+          const int64_t off = ((int64_t)(t0 + row) * Hv + h) * Dv + v0 + 16 * nt + r16;
+          if (a.grad_f32) reinterpret_cast<float*>(a.dv)[off] = dv[i];
+          else reinterpret_cast<bf16*>(a.dv)[off] = to_bf16(dv[i]);
+        }
+      }
+    }
+    for (int e = tid; e < DK * 32; e += NT) {
+      const int r = e >> 5, cc = e & 31;
+      sSq += p1.dSf[r * 33 + cc] * p1.Sqf[r * 33 + cc];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      dW[q] = mm(p1.dVnf, 33, 1, p1.Sqf, 1, 33, 16 * wave, 16 * q, 0, 32, r16, grp, dW[q]);
+      dQi[q] = mm(p1.dOf, 33, 1, p1.Sqf, 1, 33, 16 * wave, 16 * q, 0, 32, r16, grp, dQi[q]);
+      dKs[q] = mm(p1.Vnf, 33, 1, p1.dSf, 1, 33, 16 * wave, 16 * q, 0, 32, r16, grp, dKs[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dP[q] = mm(p1.dOf, 33, 1, p1.Vnf, 1, 33, 16 * wave, 16 * q, 0, 32, r16, grp, dP[q]);
+      dTU[q] = mm(p1.dVnf, 33, 1, p1.Vf, 1, 33, 16 * wave, 16 * q, 0, 32, r16, grp, dTU[q]);
+    }
+    __syncthreads();
+  }
+  // block sum of <dS', Sq>
+  sSq = wave_sum(sSq);
+  if (lane == 0) sm.red[wave] = sSq;
+
+  // ----------------------------------------------------------- finish
+  // Row tile `wave` (rows 16 wave + 4 grp + i) is owned by this wave for every
+  // [64, *] result; row sums reduce over the 16 lanes of a row group.
+  auto& p2 = sm.u.p2;
+  stage_rows<F32IN>(p2.Kf, LK, f.k, t0, nc, Hqk, hk, DK, 0, DK, tid);
+  stage_rows<F32IN>(p2.Qf, LK, f.q, t0, nc, Hqk, hk, DK, 0, DK, tid);
+  {
+    const float* Xg = a.ws_X + ch_base * 4096;
+    for (int e = tid; e < 4096; e += NT) p2.Xf[(e >> 6) * 65 + (e & 63)] = Xg[e];
+  }
+  float dg_acc[4] = {0.f, 0.f, 0.f, 0.f};           // d gamma row parts (lane partial)
+  float term_acc[4] = {0.f, 0.f, 0.f, 0.f};         // state gate term (lane partial)
+  float db_acc[4] = {0.f, 0.f, 0.f, 0.f};           // d beta from L (lane partial)
+  // column partial of one 16-column tile: sum the lane's 4 rows and the 4 row groups
+  auto col_store = [&](float (&dst)[4][64], int q, const float (&v)[4]) {
+    float t = v[0] + v[1] + v[2] + v[3];
+    t += __shfl_xor(t, 16, WAVE);
+    t += __shfl_xor(t, 32, WAVE);
+    if (grp == 0) dst[wave][16 * q + r16] = t;
+  };
+  __syncthreads();
+  // (1) G = scale dP * Gam (lower incl. diagonal); H = G * (Q K^T); dW to LDS
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cj = 16 * q + r16;
+    const f32x4 qk = mm(p2.Qf, LK, 1, p2.Kf, 1, LK, 16 * wave, 16 * q, 0, DK, r16, grp, zero4());
+    float hc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * grp + i;
+      const float gv = row >= cj ? scale * dP[q][i] * fexp2(gs.gam2[row] - gs.gam2[cj]) : 0.f;
+      p2.Gf[row * 65 + cj] = gv;
+      hc[i] = gv * qk[i];
+      dg_acc[i] += hc[i];
+    }
+    col_store(sm.colH, q, hc);
+  }
+#pragma unroll
+  for (int q = 0; q < NC; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p2.dWf[(16 * wave + 4 * grp + i) * LK + 16 * q + r16] = -dW[q][i];
+  __syncthreads();
+  // (2) dq = scale diag(e^gamma) dQi + G K; dK = G^T Q + diag(egc) dKs
+  f32x4 dK[NC];
+  {
+    float* dqp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      const int cc = 16 * q + r16;
+      const f32x4 gk = mm(p2.Gf, 65, 1, p2.Kf, LK, 1, 16 * wave, 16 * q, 0, 64, r16, grp, zero4());
+      dK[q] = mm(p2.Gf, 1, 65, p2.Qf, LK, 1, 16 * wave, 16 * q, 0, 64, r16, grp, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * grp + i;
+        const float qi = scale * gs.eg[row] * dQi[q][i];
+        dg_acc[i] += qi * p2.Qf[row * LK + cc];      // gate of the inter-chunk output
+        if (row < nc) dqp[(int64_t)row * Hv * 2 * DK + cc] = qi + gk[i];
+        const float ks = gs.egc[row] * dKs[q][i];
+        dK[q][i] += ks;
+        term_acc[i] += ks * p2.Kf[row * LK + cc];   // egc_j k_j . dKs_j
+      }
+    }
+  }
+  __syncthreads();                                   // Gf, Qf are free from here
+  // (3) dT = dW (diag(e^gamma) K)^T + dU V^T (into Gf); e^gamma T^T dW -> dK, d gamma
+  float* dTf = p2.Gf;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cj = 16 * q + r16;
+    const f32x4 t = mm(p2.dWf, LK, 1, p2.Kf, 1, LK, 16 * wave, 16 * q, 0, DK, r16, grp, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dTf[(16 * wave + 4 * grp + i) * 65 + cj] = t[i] * gs.eg[cj] + dTU[q][i];
+  }
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const f32x4 tw = mm(p2.Xf, 1, 65, p2.dWf, LK, 1, 16 * wave, 16 * q, 0, 64, r16, grp, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * grp + i;
+      const float v = tw[i] * gs.bet[row] * gs.eg[row];
+      dK[q][i] += v;
+      dg_acc[i] += v * p2.Kf[row * LK + 16 * q + r16];
+    }
+  }
+  __syncthreads();
+  // (4) d beta_j += sum_i dT_ij X_ij (this wave's rows); dX = dT diag(beta) in place
+  {
+    const int j = lane;
+    float cs = 0.f;
+#pragma unroll 4
+    for (int r = 16 * wave; r < 16 * wave + 16; ++r) {
+      const float dt = dTf[r * 65 + j];
+      cs += dt * p2.Xf[r * 65 + j];
+      dTf[r * 65 + j] = dt * gs.bet[j];
+    }
+    sm.colDB[wave][j] = cs;
+  }
+  __syncthreads();
+  // (5) M1 = X^T dX (into Qf space)
+  float* M1 = p2.Qf;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 m = mm(p2.Xf, 1, 65, dTf, 65, 1, 16 * wave, 16 * q, 0, 64, r16, grp, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M1[(16 * wave + 4 * grp + i) * 65 + 16 * q + r16] = m[i];
+  }
+  __syncthreads();
+  // (6) dL = -(M1 X^T) on the strict lower part; with A = K K^T and L = beta A Gam:
+  //     d beta_i += dL A Gam, HL = dL L, dA = dL beta_i Gam (into dWf space)
+  float* dAf = p2.dWf;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cj = 16 * q + r16;
+    const f32x4 ml = mm(M1, 65, 1, p2.Xf, 1, 65, 16 * wave, 16 * q, 0, 64, r16, grp, zero4());
+    const f32x4 kk = mm(p2.Kf, LK, 1, p2.Kf, 1, LK, 16 * wave, 16 * q, 0, DK, r16, grp, zero4());
+    float hl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * grp + i;
+      const float gam = row > cj ? fexp2(gs.gam2[row] - gs.gam2[cj]) : 0.f;
+      const float dl = -ml[i];
+      const float ag = kk[i] * gam;
+      db_acc[i] += dl * ag;
+      hl[i] = gs.bet[row] * dl * ag;
+      dg_acc[i] += hl[i];
+      dAf[row * 65 + cj] = dl * gs.bet[row] * gam;
+    }
+    col_store(sm.colHL, q, hl);
+  }
+  __syncthreads();
+  // (7) dK += (dA + dA^T) K; dk partial
+  {
+    float* dkp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK + DK;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      f32x4 acc = mm(dAf, 65, 1, p2.Kf, LK, 1, 16 * wave, 16 * q, 0, 64, r16, grp, zero4());
+      acc = mm(dAf, 1, 65, p2.Kf, LK, 1, 16 * wave, 16 * q, 0, 64, r16, grp, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * grp + i;
+        if (row < nc) dkp[(int64_t)row * Hv * 2 * DK + 16 * q + r16] = dK[q][i] + acc[i];
+      }
+    }
+  }
+  // (8) row totals over the 16 lanes of each row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v3[3] = {dg_acc[i], term_acc[i], db_acc[i]};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      float x = v3[t];
+      x += __shfl_xor(x, 8, WAVE);
+      x += __shfl_xor(x, 4, WAVE);
+      x += __shfl_xor(x, 2, WAVE);
+      x += __shfl_xor(x, 1, WAVE);
+      v3[t] = x;
+    }
+    if (r16 == 0) {
+      const int row = 16 * wave + 4 * grp + i;
+      sm.rowDG[row] = v3[0];
+      sm.rowTerm[row] = v3[1];
+      sm.rowDB[row] = v3[2];
+    }
+  }
+  __syncthreads();
+  // (9) d gamma_j = row part - column parts - state term_j; the last row also
+  //     gets e^gamma_n <dS', Sq> + sum_j term_j; dg = suffix sum of d gamma
+  if (wave == 0) {
+    const int j = lane;
+    const float term = sm.rowTerm[j];
+    const float term_total = wave_sum(term);
+    const float sq_total = sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3];
+    float dgj = sm.rowDG[j] - term - (sm.colH[0][j] + sm.colH[1][j] + sm.colH[2][j] + sm.colH[3][j]) -
+                (sm.colHL[0][j] + sm.colHL[1][j] + sm.colHL[2][j] + sm.colHL[3][j]);
+    if (j == nc - 1) dgj += gs.egC * sq_total + term_total;
+    if (j >= nc) dgj = 0.f;
+    float suf = dgj;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(suf, off, WAVE);
+      if (j + off < 64) suf += y;
+    }
+    const float db = sm.colDB[0][j] + sm.colDB[1][j] + sm.colDB[2][j] + sm.colDB[3][j] + sm.rowDB[j];
+    if (j < nc) {
+      const int64_t gi = (int64_t)(t0 + j) * Hv + h;
+      a.dg[gi] = suf;
+      a.dbeta[gi] = db;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- bwd_group
+template <int DK>
+__global__ void bwd_group(BwdKernelArgs a, int G) {
+  const int tok = blockIdx.x, hk = blockIdx.y, d = threadIdx.x;
+  const int Hv = a.f.Hv, Hqk = a.f.Hqk;
+  if (d >= DK) return;
+  float sq = 0.f, sk = 0.f;
+  for (int j = 0; j < G; ++j) {
+    const float* p = a.ws_dqk + (((int64_t)tok * Hv + hk * G + j) * 2) * DK;
+    sq += p[d];
+    sk += p[DK + d];
+  }
+  const int64_t off = ((int64_t)tok * Hqk + hk) * DK + d;
+  if (a.grad_f32) {
+    reinterpret_cast<float*>(a.dq)[off] = sq;
+    reinterpret_cast<float*>(a.dk)[off] = sk;
+  } else {
+    reinterpret_cast<bf16*>(a.dq)[off] = to_bf16(sq);
+    reinterpret_cast<bf16*>(a.dk)[off] = to_bf16(sk);
+  }
+}
+
+}  // namespace
+
+template <int DK, bool F32IN>
+static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  const dim3 slots(a.num_slots, c.Hv);
+#define GDN_PREP(WFv) \
+  if (c.w_fmt == WFv) hipLaunchKernelGGL((bwd_prep<DK, F32IN, WFv>), slots, dim3(NT), 0, s, a, c.N);
+  GDN_PREP(0) GDN_PREP(1) GDN_PREP(2)
+#undef GDN_PREP
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dstate<DK, F32IN>), dim3(c.Dv / 64, c.Hv, c.N), dim3(NT), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+#define GDN_CHUNK(SFv) \
+  if (c.state_fmt == SFv) hipLaunchKernelGGL((bwd_chunk<DK, F32IN, SFv>), slots, dim3(NT), 0, s, a, c.N);
+  GDN_CHUNK(0) GDN_CHUNK(1) GDN_CHUNK(2)
+#undef GDN_CHUNK
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, s, a, c.Hv / c.Hqk);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  if (a.total_tokens == 0 || c.Hv == 0) return hipSuccess;
+  if (c.f32_io) {
+    if (c.Dk == 64) return launch_bwd_dk<64, true>(c, a, s);
+    return hipErrorInvalidValue;
+  }
+  if (c.Dk == 64) return launch_bwd_dk<64, false>(c, a, s);
+  if (c.Dk == 128) return launch_bwd_dk<128, false>(c, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gdn

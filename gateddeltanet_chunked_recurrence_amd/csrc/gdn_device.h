@@ -29,6 +29,13 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// FP32 MFMA tile (v_mfma_f32_16x16x4_f32): lane l holds A[l & 15][l >> 4] and
+// B[l >> 4][l & 15]; accumulator layout as above.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // The lane index, opaque to the optimizer. Kernels call it at the start of
 // each phase so per-lane LDS addresses are rebuilt where they are used:
 // LDS arrays above 64 KB cannot use the 16-bit instruction offset, and

@@ -116,10 +116,6 @@ __device__ __forceinline__ void planes(const Raw8<F32IN>& r, bf16x8& hi, bf16x8&
   }
 }
 
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Lower 16x16 tiles (mi >= mj) of a 64x64 matrix, in a fixed order.
 __device__ __forceinline__ void lower_tile(int t, int& mi, int& mj) {

@@ -42,7 +42,10 @@ struct BwdKernelArgs {
   float* dg;
   float* dbeta;
   float* dh0;                 // nullable
-  float* ws_dstate;           // [num_slots, Hv, Dk, Dv] FP32: dS entering each chunk's end
+  float* ws_X;                // [num_slots, Hv, 64, 64] FP32: X = (I + L)^-1 per chunk
+  float* ws_W;                // [B*T, Hv, Dk] FP32: the W used in the products (Wq or W)
+  float* ws_dstate;           // [num_slots, Hv, Dk, Dv] FP32: dL/dS at the end of each chunk
+  float* ws_dvn;              // [num_slots, Hv, 64, Dv] FP32: dL/dVnew per chunk
   float* ws_dqk;              // [B*T, Hv, 2, Dk] FP32 per-value-head dq, dk before the group sum
   int32_t grad_f32;
   int32_t total_tokens;

@@ -111,3 +111,13 @@ def code_bytes(codes, fmt):
     if fmt == 1:
         return e4m3_encode(c)
     return c.astype(np.int8).view(np.uint8)
+
+
+def gpu_bwd(x, spec, saved, grad_dtype=torch.float32, **over):
+    p = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+    p.update(over)
+    g = B.gdn_chunk_bwd(x['q'], x['k'], x['v'], x['g'], x['beta'], saved, x['do'],
+                        dht=x['dht'], scale=1.0 / math.sqrt(spec['Dk']), h0=x['h0'],
+                        cu_seqlens=x['cu_seqlens'], grad_dtype=grad_dtype, **p)
+    torch.cuda.synchronize()
+    return g
