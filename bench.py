@@ -46,18 +46,24 @@ def bytes_algorithmic(spec):
     return rd + wr
 
 
-def source_hash():
+# Sources each timed kernel is compiled from; a committed counter summary is
+# used only while these files are unchanged.
+KERNEL_SOURCES = {'gdn_fwd_kernel': ('gdn_device.h', 'gdn_fwd.hip', 'gdn_launch.h')}
+
+
+def source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, 'gateddeltanet_chunked_recurrence_amd', 'csrc')
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith(('.hip', '.h', '.cpp')):
-            h.update(open(os.path.join(csrc, f), 'rb').read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(csrc, f), 'rb').read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, src_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source (else None)."""
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for a device copy of known size) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    (else None)."""
     p = os.path.join(ROOT, 'profiles', f'{kernel}_{WORKLOAD}_traffic.json')
     if not os.path.exists(p):
         return None
@@ -67,25 +73,80 @@ def measured_traffic(kernel, src_hash):
     return d.get('bytes_per_launch')
 
 
-def cpu_baseline(spec, seed):
-    """The float64 oracle on a bounded sample of the same workload: `nseq` of
-    the B sequences, full length, all heads (sequences are independent)."""
+def cpu_baseline(spec, seed, min_seconds=10.0):
+    """The float64 oracle on the same workload (all B sequences, full length,
+    all heads), repeated until at least `min_seconds` of CPU work."""
     import torch
 
     import gdn_inputs
     from oracle import chunked_fwd
-    nseq = 3
-    s = dict(spec, B=nseq)
-    x = gdn_inputs.make_inputs(s, seed, device='cpu')
+    x = gdn_inputs.make_inputs(spec, seed, device='cpu')
     args = [x[n].double() for n in ('q', 'k', 'v', 'g', 'beta')]
-    t = time.perf_counter()
-    chunked_fwd(*args, 1.0 / math.sqrt(spec['Dk']), None, None, state_fmt=spec['state_fmt'],
-                w_fmt=spec['w_fmt'], block_v=spec['block_v'])
-    dt = time.perf_counter() - t
-    ntok = nseq * spec['T']
+    reps, t = 0, time.perf_counter()
+    while True:
+        chunked_fwd(*args, 1.0 / math.sqrt(spec['Dk']), None, None, state_fmt=spec['state_fmt'],
+                    w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
+    ntok = reps * spec['B'] * spec['T']
     return dict(value=ntok / dt, unit='tokens/s', cores=torch.get_num_threads(), kind='oracle',
-                sample=f'{nseq} of {spec["B"]} sequences x {spec["T"]} tokens x {spec["Hv"]} heads '
-                       f'(float64 chunked oracle, {dt:.1f} s)')
+                sample=f'{reps} passes over the whole workload ({spec["B"]} x {spec["T"]} tokens, '
+                       f'{spec["Hv"]} heads; float64 chunked oracle, {dt:.1f} s)')
+
+
+def time_fwd_bwd(steps, warmup):
+    """Forward (saving for the backward) + backward on the forward+backward
+    workload (B=2, T=8192, H=16, Dk=Dv=128, E4M3 state and W, initial state,
+    dO and dS_final given). Returns per-step milliseconds of each part."""
+    import torch
+
+    import gdn_inputs
+    from gateddeltanet_chunked_recurrence_amd import binding as B
+    name = 'fwd_bwd_e4m3_b2_t8192_h16_d128'
+    spec = gdn_inputs.spec(name)
+    x = gdn_inputs.make_inputs(spec, seed=2, device='cuda', bwd=True)
+    scale = 1.0 / math.sqrt(spec['Dk'])
+    kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+
+    def fwd():
+        return B.gdn_chunk_fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], scale=scale,
+                               h0=x['h0'], save_for_backward=True, **kw)
+
+    def bwd(saved):
+        return B.gdn_chunk_bwd(x['q'], x['k'], x['v'], x['g'], x['beta'], saved, x['do'],
+                               x['dht'], scale=scale, h0=x['h0'], **kw)
+
+    for _ in range(warmup):
+        bwd(fwd()[2])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    for i in range(steps):
+        ev[3 * i].record(stream)
+        saved = fwd()[2]
+        ev[3 * i + 1].record(stream)
+        bwd(saved)
+        ev[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    f = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps
+    b = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps
+    tokens = spec['B'] * spec['T']
+    return dict(workload=name, fwd_ms=f, bwd_ms=b, tokens_per_s=tokens / ((f + b) * 1e-3),
+                steps=steps)
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters (each copy reads and writes `nbytes`)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device='cuda').fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(copy_bytes=nbytes, reps=reps)), flush=True)
 
 
 def main():
@@ -94,11 +155,19 @@ def main():
     ap.add_argument('--steps', type=int, default=50)
     ap.add_argument('--warmup', type=int, default=10)
     ap.add_argument('--no-cpu-baseline', action='store_true')
+    ap.add_argument('--no-bwd', action='store_true', help='skip the forward+backward timing')
+    ap.add_argument('--copy-calibration', action='store_true',
+                    help='only run a 1 GiB device copy (counter calibration)')
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get('WORLD_SIZE', '1')) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(heads/sequences shard with no communication; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU and has no multi-GPU path: sequences and heads "
+              "are independent, so a multi-GPU run would shard them with no communication",
+              file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -132,7 +201,7 @@ def main():
     token_heads = tokens * spec['Hv']
     flops = flops_per_token_head(spec['Dk'], spec['Dv']) * token_heads
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    src = source_hash()
+    src = source_hash('gdn_fwd_kernel')
     traffic = measured_traffic('gdn_fwd_kernel', src)
     out = dict(
         metric=METRIC, value=tokens / (ms_per_step * 1e-3), unit='tokens/s', n_gpus=1,
@@ -146,6 +215,8 @@ def main():
         kernel_ms=kern_ms, gflop_per_step=flops / 1e9,
         hbm_gbs_algorithmic=bytes_algorithmic(spec) / (kern_ms * 1e-3) / 1e9,
         source_hash=src)
+    if not args.no_bwd:
+        out['fwd_bwd'] = time_fwd_bwd(steps=max(3, args.steps // 5), warmup=2)
     if not args.no_cpu_baseline:
         out['cpu_baseline'] = cpu_baseline(spec, seed=2)
     print(json.dumps(out), flush=True)

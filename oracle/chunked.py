@@ -11,7 +11,8 @@ straight-through gradients, the forward's quantized W reused by the
 backward. "[2/4] GDN/KDA decode QAT with INT8 recurrent state", "What does
 this PR do?": INT8 state with per-head [Dk, block_v] scales. The pages give
 no formulas; the chunk form below is derived from the token recurrence in
-oracle/recurrent.py (the derivation is in the design doc) and tested equal to it.
+oracle/recurrent.py (substituting the token update into itself over a
+chunk) and tested equal to it.
 
 Per (sequence, value head) and chunk of n <= C tokens (sequence-relative;
 positions i, j = 1..n) with incoming state S:

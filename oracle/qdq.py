@@ -13,7 +13,7 @@ PR do?" and "Testing"):
     FP32-rounded reciprocal ("rounded reciprocal multiplication", [2/4]
     Testing).
 
-Reading taken where the pages are silent (listed in the design doc):
+Reading taken where the pages are silent:
   a   = max |x| over the tile                      (FP32)
   d   = fl32(a / q_max), floored at 2**-126        (q_max = 448 or 127)
   r   = fl32(1 / d)
