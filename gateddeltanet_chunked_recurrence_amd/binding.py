@@ -30,7 +30,7 @@ class FwdArgs(ctypes.Structure):
                 ('Dv', c_i32), ('num_seqs', c_i32), ('io_dtype', c_i32), ('scale', c_f32),
                 ('policy', QdqPolicy), ('q', c_vp), ('k', c_vp), ('v', c_vp), ('g', c_vp),
                 ('beta', c_vp), ('h0', c_vp), ('cu_seqlens', c_vp), ('o', c_vp), ('ht', c_vp),
-                ('saved', c_vp)]
+                ('saved', c_vp), ('workspace', c_vp), ('workspace_bytes', c_sz)]
 
 
 class SavedLayout(ctypes.Structure):
@@ -68,6 +68,8 @@ def load_library():
         f.restype = c_i32
     lib.gdn_saved_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.gdn_saved_bytes.restype = c_sz
+    lib.gdn_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.gdn_fwd_workspace_bytes.restype = c_sz
     lib.gdn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.gdn_bwd_workspace_bytes.restype = c_sz
     _LIB = lib
@@ -139,6 +141,10 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
             _check(lib.gdn_chunk_fwd(ctypes.byref(a), None))     # reports the shape error
         saved = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         a.saved = _ptr(saved)
+    wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
+    ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = wbytes
     _check(lib.gdn_chunk_fwd(ctypes.byref(a), _stream(dev)))
     return o, ht, saved
 

@@ -10,6 +10,7 @@
 #include <cstdint>
 
 #include "../../include/gdn.h"
+#include "gdn_images.h"
 #include "gdn_launch.h"
 
 namespace {
@@ -68,6 +69,8 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
                 a->num_seqs, a->B);
   }
   if (a->num_seqs > 65535) return fail(GDN_E_UNSUPPORTED, "num_seqs %d exceeds 65535", a->num_seqs);
+  if ((ceil_div((int64_t)a->B * a->T, 64) + a->num_seqs) * a->Hv > INT32_MAX)
+    return fail(GDN_E_UNSUPPORTED, "(chunks + sequences) * Hv exceeds 2^31");
   if ((int64_t)a->B * a->T > INT32_MAX / 2)
     return fail(GDN_E_UNSUPPORTED, "B*T = %lld tokens exceeds 2^30", (long long)a->B * a->T);
   return GDN_OK;
@@ -104,6 +107,33 @@ gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
   off = round256(off + (wq ? L.num_slots * a->Hv * 4 : 0));
   L.total_bytes = off;
   return L;
+}
+
+// Forward scratch (bf16 io), per chunk slot and value head, 256-byte aligned
+// sections: the operand image block [W planes | K^T | P] (bf16), U and the W
+// scale (FP32).
+struct FwdWsLayout {
+  int64_t img, u, wscale, total;
+};
+
+template <int DK>
+FwdWsLayout fwd_ws_layout_dk(const gdn_fwd_args* a, int64_t nch) {
+  using I = gdn::Img<DK>;
+  const int64_t img = a->policy.w_fmt == GDN_QDQ_OFF ? I::template img<2>() : I::template img<1>();
+  FwdWsLayout w{};
+  int64_t off = 0;
+  w.img = off;     off += round256(nch * img * 2);
+  w.u = off;       off += round256(nch * (int64_t)a->Dv * 64 * 4);
+  w.wscale = off;  off += round256(nch * 4);
+  w.total = off;
+  return w;
+}
+
+FwdWsLayout fwd_ws_layout(const gdn_fwd_args* a) {
+  FwdWsLayout w{};
+  if (a->io_dtype == GDN_F32 || (int64_t)a->B * a->T == 0) return w;
+  const int64_t nch = layout_of(a).num_slots * a->Hv;
+  return a->Dk == 128 ? fwd_ws_layout_dk<128>(a, nch) : fwd_ws_layout_dk<64>(a, nch);
 }
 
 gdn::FwdKernelArgs kernel_args(const gdn_fwd_args* a, void* saved) {
@@ -201,14 +231,35 @@ size_t gdn_saved_bytes(const gdn_fwd_args* a) {
   return (size_t)layout_of(a).total_bytes;
 }
 
+size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a) {
+  if (check_fwd_shape(a) != GDN_OK) return 0;
+  return (size_t)fwd_ws_layout(a).total;
+}
+
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) {
   gdn_status s = check_fwd_shape(a);
   if (s != GDN_OK) return s;
   if ((s = check_fwd_ptrs(a, true)) != GDN_OK) return s;
+  const FwdWsLayout W = fwd_ws_layout(a);
+  if (W.total > 0 && (!a->workspace || a->workspace_bytes < (size_t)W.total))
+    return fail(GDN_E_WORKSPACE, "forward workspace of %zu bytes given, %lld needed",
+                a->workspace_bytes, (long long)W.total);
+  if (a->workspace && !aligned16(a->workspace))
+    return fail(GDN_E_INVALID, "workspace is not 16-byte aligned");
   if ((int64_t)a->B * a->T == 0) return GDN_OK;
-  return hip_status(gdn::launch_fwd(fwd_config(a), kernel_args(a, a->saved),
-                                    static_cast<hipStream_t>(stream)),
-                    "gdn_chunk_fwd launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  gdn::FwdKernelArgs k = kernel_args(a, a->saved);
+  const gdn::FwdConfig cfg = fwd_config(a);
+  if (a->io_dtype == GDN_F32)
+    return hip_status(gdn::launch_fwd_fused(cfg, k, st), "gdn_chunk_fwd launch");
+  char* ws = static_cast<char*>(a->workspace);
+  k.ws_img = reinterpret_cast<__bf16*>(ws + W.img);
+  k.ws_u = reinterpret_cast<float*>(ws + W.u);
+  k.ws_wscale = reinterpret_cast<float*>(ws + W.wscale);
+  const int num_slots = (int)layout_of(a).num_slots;
+  s = hip_status(gdn::launch_fwd_prep(cfg, k, num_slots, st), "gdn_chunk_fwd prep launch");
+  if (s != GDN_OK) return s;
+  return hip_status(gdn::launch_fwd_state(cfg, k, st), "gdn_chunk_fwd state launch");
 }
 
 size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a) {

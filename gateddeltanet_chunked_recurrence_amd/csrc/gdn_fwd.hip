@@ -1,5 +1,6 @@
 // Chunked gated delta rule forward with dynamic state/W fake QDQ, fused into
-// one kernel per (sequence, value head, 64-wide value block).
+// one kernel per (sequence, value head, 64-wide value block). Used for FP32
+// inputs (Dk = 64); bf16 inputs take the prep + state kernel pair.
 //
 // Work unit and residency. A workgroup of 4 waves owns the state tile
 // S[Dk, 64] of one (sequence, head, value block) and walks the sequence's
@@ -822,14 +823,9 @@ static hipError_t launch_fmt(const FwdConfig& cfg, const FwdKernelArgs& a, hipSt
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_fused(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream) {
   if (cfg.N == 0 || cfg.Hv == 0) return hipSuccess;
-  if (cfg.f32_io) {
-    if (cfg.Dk == 64) return launch_fmt<64, true>(cfg, a, stream);
-    return hipErrorInvalidValue;
-  }
-  if (cfg.Dk == 64) return launch_fmt<64, false>(cfg, a, stream);
-  if (cfg.Dk == 128) return launch_fmt<128, false>(cfg, a, stream);
+  if (cfg.f32_io && cfg.Dk == 64) return launch_fmt<64, true>(cfg, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,63 @@
+// Operand images exchanged between the forward's two kernels.
+//
+// The prep kernel (one workgroup per chunk and head) writes, for every chunk
+// and head, the state-independent operands of the state kernel in exactly the
+// layout the state kernel keeps in LDS, so that kernel stages them with plain
+// 16-byte copies:
+//   W image  [64][DK] bf16 per plane: W^q codes (one plane) or W as hi + lo
+//            (two planes), paired order along dk (pperm), 16-byte chunks
+//            XOR-swizzled by row for DK = 128 (rows padded to 72 for DK = 64)
+//   K^T image [DK][72] bf16: K transposed, paired order along tokens
+//   P image  2 x [64][72] bf16: (Q K^T) * Gam as hi + lo, paired order along
+//            the key token; upper 16x16 tiles zero
+//   U        FP32 in accumulator-fragment order: for value block vb, wave w,
+//            row tile mt and lane l the four values U[16 mt + 4 (l >> 4) + i]
+//            [64 vb + 16 w + (l & 15)], i = 0..3, contiguous
+//   gates    256 FP32: exp(gamma_i) at [i], exp(gamma_n - gamma_i) at [64 + i]
+//            (0 past the chunk end), exp(gamma_n) at [128], rest unused
+//   W scale  one FP32 per chunk and head (1 when W QDQ is off)
+// The W, K^T, P and gate images of one chunk and head are one contiguous
+// block, in that order, as they are in the state kernel's LDS buffer.
+// The Q operand of the state kernel uses the W image layout and is staged
+// from q directly.
+#pragma once
+#include "gdn_device.h"
+
+namespace gdn {
+
+template <int DK>
+struct Img {
+  static constexpr int RS = DK == 128 ? 128 : 72;   // row stride of [64][DK] images
+  static constexpr int SWZ = DK == 128 ? 15 : 0;    // 16-byte chunk swizzle mask
+  static constexpr int R64 = 72;                    // row stride of [*][64] images
+  static constexpr int WQ = 64 * RS;                // elements of one [64][DK] plane
+  static constexpr int KT = DK * R64;               // elements of the K^T image
+  static constexpr int P1 = 64 * R64;               // elements of one P plane
+  static constexpr int GB = 512;                    // gate block: 256 FP32 (1 KB)
+  // one (slot, head) block: [W planes | K^T | P hi, P lo | gates], contiguous
+  template <int NW> static constexpr int img() { return NW * WQ + KT + 2 * P1 + GB; }
+  template <int NW> static constexpr int kt_at() { return NW * WQ; }
+  template <int NW> static constexpr int p_at() { return NW * WQ + KT; }
+  template <int NW> static constexpr int g_at() { return NW * WQ + KT + 2 * P1; }
+};
+
+// Element offset of stored (pperm) position s in row `row` of a [64][DK] image.
+template <int DK>
+__device__ __forceinline__ int wq_off(int row, int s) {
+  using I = Img<DK>;
+  return row * I::RS + ((((s >> 3) ^ (row & I::SWZ))) << 3) + (s & 7);
+}
+
+// A-operand fragment (16 rows from `row0`, stored K positions 32 kk + 8 grp..+7)
+// of a [64][DK] image.
+template <int DK>
+__device__ __forceinline__ bf16x8 ld_wq(const bf16* img, int row, int kk, int grp) {
+  return *reinterpret_cast<const bf16x8*>(img + wq_off<DK>(row, 32 * kk + 8 * grp));
+}
+
+// Float offset of the U fragment (ch, vb, w, mt) of lane `lane`.
+__device__ __forceinline__ int64_t u_off(int64_t ch, int nvb, int vb, int w, int mt, int lane) {
+  return ((((ch * nvb + vb) * 4 + w) * 4 + mt) * 64 + lane) * 4;
+}
+
+}  // namespace gdn

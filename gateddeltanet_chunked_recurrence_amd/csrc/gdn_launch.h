@@ -21,6 +21,10 @@ struct FwdKernelArgs {
   float* s_scale;             // saved state scales, nullable
   uint8_t* w_codes;           // saved W codes (W QDQ on), nullable
   float* w_scale;             // saved W scales, nullable
+  // forward workspace (bf16 io): operand images written by the prep kernel
+  __bf16* ws_img;             // [slots * Hv][W planes | K^T | P] (gdn_images.h)
+  float* ws_u;                // [slots * Hv][Dv * 64] fragment order
+  float* ws_wscale;           // [slots * Hv]
   int32_t T;                  // tokens per sequence (no cu_seqlens)
   int32_t Hqk, Hv, Dv, block_v;
   float scale;
@@ -30,7 +34,12 @@ struct FwdConfig {
   int Dk, Dv, N, Hv, state_fmt, w_fmt, f32_io;
 };
 
-hipError_t launch_fwd(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
+// FP32 io (Dk = 64): one fused kernel per (sequence, head, value block).
+hipError_t launch_fwd_fused(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
+// bf16 io: prep kernel over every (chunk, head), then the state kernel.
+hipError_t launch_fwd_prep(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
+                           hipStream_t stream);
+hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
 
 struct BwdKernelArgs {
   FwdKernelArgs f;            // forward inputs + saved buffers (read only here)

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -95,6 +95,10 @@ typedef struct {
   float* ht;                   /* out [N, Hv, Dk, Dv] final state, or NULL    */
   void* saved;                 /* out: gdn_saved_bytes() bytes for the
                                   backward (layout gdn_saved_layout), or NULL */
+  void* workspace;             /* gdn_fwd_workspace_bytes() bytes of device
+                                  scratch (may be NULL when that is 0); its
+                                  contents are undefined before and after    */
+  size_t workspace_bytes;
 } gdn_fwd_args;
 
 /* Layout of the `saved` buffer, in bytes from its start. Chunk c of sequence
@@ -118,7 +122,20 @@ typedef struct {
 gdn_status gdn_saved_layout(const gdn_fwd_args* a, gdn_saved_layout_t* out);
 size_t gdn_saved_bytes(const gdn_fwd_args* a);
 
-/* Chunked forward. Writes o, and ht / saved when not NULL. */
+/* Device scratch the forward needs (0 on error or for FP32 inputs). With
+ * bf16 inputs the forward runs as two kernels: every (chunk, head) first
+ * builds its state-independent operands (the solve, W and its QDQ, U and the
+ * masked Q K^T) into this scratch; then one workgroup per (sequence, head,
+ * 64-wide value block) runs the state recurrence over the chunks in order.
+ * Per slot (see gdn_saved_layout) and value head: the W operand (128 * Dk
+ * bytes, twice that with W QDQ off; 144 * Dk for Dk = 64), K^T (144 * Dk
+ * bytes), masked Q K^T (18 KB), U (256 * Dv bytes) and one scale; about
+ * 360 MB at B = 4, T = 4096, H = 16, Dk = Dv = 128. */
+size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
+
+/* Chunked forward. Writes o, and ht / saved when not NULL. Needs
+ * a->workspace of gdn_fwd_workspace_bytes(a) bytes (GDN_E_WORKSPACE if
+ * missing or too small). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
 
 /* Backward arguments: the forward's arguments and `saved`, plus upstream

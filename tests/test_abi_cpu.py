@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == 2
 
 
 def _args(**kw):
@@ -71,6 +71,28 @@ def test_forward_rejects_before_launch(kw, status, msg):
     got = lib.gdn_chunk_fwd(ctypes.byref(a), None)
     assert got == status
     assert msg in lib.gdn_last_error().decode()
+
+
+def test_forward_workspace_is_sized_and_required():
+    """bf16 inputs need the prep kernel's scratch: its size follows the
+    per-(slot, head) image sizes, a missing or short workspace is rejected
+    with GDN_E_WORKSPACE, and FP32 inputs (fused path) need none."""
+    lib = B.load_library()
+    a = _args()
+    n = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
+    slots = 1 + 2                                       # N + ceil(128 / 64)
+    per = 64 * 128 * 2 + 128 * 72 * 2 + 2 * 64 * 72 * 2 + 128 * 64 * 4 + 4
+    assert n >= slots * 4 * per and n <= slots * 4 * per + 5 * 256
+    assert lib.gdn_chunk_fwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
+    assert 'workspace' in lib.gdn_last_error().decode()
+    a.workspace = ctypes.c_void_p(0x40000)
+    a.workspace_bytes = n - 1
+    assert lib.gdn_chunk_fwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
+    off = _args(w_fmt=B.QDQ_OFF)                        # W as hi + lo planes
+    assert lib.gdn_fwd_workspace_bytes(ctypes.byref(off)) >= n + slots * 4 * 64 * 128 * 2
+    f32 = _args(io_dtype=B.GDN_F32, Dk=64)
+    assert lib.gdn_fwd_workspace_bytes(ctypes.byref(f32)) == 0
+    assert lib.gdn_fwd_workspace_bytes(ctypes.byref(_args(Dk=96))) == 0
 
 
 def test_empty_problem_is_a_no_op():
