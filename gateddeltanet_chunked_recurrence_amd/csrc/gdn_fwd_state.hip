@@ -27,7 +27,6 @@ namespace gdn {
 namespace {
 
 constexpr int NT = 256;
-constexpr float LOG2E = 1.4426950408889634f;
 
 template <int DK, int NW>
 struct StateBuf {
