@@ -19,6 +19,9 @@ typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 raw bytes as a native vector (copies of HIP's uint4 struct lower to
+// memcpy through private memory, which is not promoted to registers)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 constexpr int CHUNK = 64;
@@ -35,6 +38,17 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations and
+// then for every wave. Unlike __syncthreads() it does not drain the wave's
+// outstanding global loads and stores, so register prefetches and
+// global-to-LDS copies stay in flight across it. LDS data written by
+// global-to-LDS loads is covered by vmcnt, not by this barrier: wait for it
+// (vmcnt) before the barrier that publishes it. The memory clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // The lane index, opaque to the optimizer. Kernels call it at the start of
 // each phase so per-lane LDS addresses are rebuilt where they are used:

@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       G[192 + lane] = 0.f;
     }
     if (nxt.valid) load_kqg(nxt);                  // K, Q, g, beta registers are free again
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
 
     // ---- 2. L (FP32) and P (hi / lo, pperm over columns): 20 tiles over 8 waves
@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
 
     // ---- 3. wave 0: diagonal blocks of X; others: P image out, X upper zero, V^T in
@@ -326,7 +326,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       }
       vs.store_t(sm.a.Vt, nullptr, wave, lane);   // K, Q rows are dead; V^T for U
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
     if (wave == 0) vs.store_t(sm.a.Vt, nullptr, wave, lane);
     if (nxt.valid) load_v(nxt);
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.b.s.X[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
     // 32-block merge, Y = L_BA X_AA: each 16x16 tile of Y is split over two
     // waves along its K range (the first writes, the second adds after a barrier)
@@ -356,13 +356,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int i = 0; i < 4; ++i) yp[i * 33] = y[i];
       }
-      __syncthreads();
+      lds_barrier();
       if (kh == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) yp[i * 33] += y[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
     // X_BA = -X_BB Y (one 16x16 tile per wave 0..3)
     if (wave < 4) {
@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.b.s.X[(32 + 16 * ti + 4 * grp + i) * 65 + 16 * tj + r16] = -z[i];
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
 
     // ---- 4. T = X diag(beta), T' = T diag(exp(gamma)) as hi / lo planes (pperm over columns)
@@ -395,7 +395,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         st4(&sm.c.T[3][o], pl[0], pl[1], pl[2], pl[3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
 
     // ---- 5. W = T' K (row tile wave & 3, column-tile half wave >> 2), U = T V; QDQ of W
@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         }
       }
     }
-    __syncthreads();                              // W amax partials; X, L dead
+    lds_barrier();                              // W amax partials; X, L dead
     GDN_REFRESH();
     {
       float dW = 1.f, rW = 1.f;
@@ -506,14 +506,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         if (save) a.w_scale[ch] = dW;
       }
     }
-    __syncthreads();
+    lds_barrier();
     GDN_REFRESH();
     {
       const uint4* src = reinterpret_cast<const uint4*>(sm.b.W);
       uint4* dst = reinterpret_cast<uint4*>(img);
       for (int e = tid; e < NW * I::WQ / 8; e += NT) dst[e] = src[e];
     }
-    __syncthreads();                              // LDS is reused by the next item
+    lds_barrier();                              // LDS is reused by the next item
     if (!nxt.valid) break;
     cur = nxt;
   }

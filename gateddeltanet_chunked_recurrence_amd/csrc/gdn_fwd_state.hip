@@ -84,15 +84,19 @@ struct Stager {
       *reinterpret_cast<uint2*>(&b.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = make_uint2(q[p].z, q[p].w);
     }
   }
-  // Part `part` of NP of this wave's share of the image block's wave loads.
+  // Part `part` of NP of this wave's wave loads of the image block: j = wave
+  // + 4 k, clamped to the last one (a repeated load rewrites the same bytes),
+  // so every wave issues the same compile-time number of loads and the
+  // compiler can wait for older register loads precisely.
   template <int NP>
   static __device__ void dma_img(const FwdKernelArgs& a, int64_t ch, StateBuf<DK, NW>& b, int wave,
                                  int lane, int part) {
+    constexpr int KW = (NINS + 3) / 4;
     const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + ch * I::template img<NW>());
     uint4* dst = reinterpret_cast<uint4*>(b.W);
-    const int kw = (NINS - wave + 3) / 4;           // this wave's loads: j = wave + 4 k
-    for (int k = kw * part / NP; k < kw * (part + 1) / NP; ++k) {
-      const int j = wave + 4 * k;
+#pragma unroll
+    for (int k = KW * part / NP; k < KW * (part + 1) / NP; ++k) {
+      const int j = min(wave + 4 * k, NINS - 1);
       __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
     }
   }
@@ -190,7 +194,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
     if (lane == 0) sm.red[0][wave] = m;
   }
   wait_vmem();
-  __syncthreads();
+  lds_barrier();
 
   const int gs = (SF != 0) ? a.block_v / 16 : 1;  // waves per scale tile
   const int g0 = (wave / gs) * gs;
@@ -386,7 +390,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
       if (lane == 0) sm.red[(c + 1) & 1][wave] = m;
     }
     if constexpr (C::NBUF == 1) {
-      __syncthreads();                             // every wave is done with the buffer
+      lds_barrier();                             // every wave is done with the buffer
       GDN_REFRESH();
       if (c + 1 < nchunks) {
         Stager<DK, NW>::template dma_img<1>(a, chunk_ch(c + 1), sm.buf[0], wave, lane, 0);
@@ -395,7 +399,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
       }
     }
     wait_vmem();                                   // this wave's staging of chunk c + 1 landed
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Ucur[mt] = Unext[mt];
     dWcur = dWnext;
@@ -435,6 +439,7 @@ static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, 
 }
 
 hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+  if (cfg.state_fmt != 0 && cfg.w_fmt != 0) return launch_fwd_state_pair(cfg, a, s);
   if (cfg.Dk == 128) return launch_state_dk<128>(cfg, a, s);
   if (cfg.Dk == 64) return launch_state_dk<64>(cfg, a, s);
   return hipErrorInvalidValue;
