@@ -2,18 +2,23 @@
 W fake QDQ on one MI355X, against the bf16 MFMA roofline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-bwd] [--copy-calibration]
 
-One step = one gdn_chunk_fwd call over B=4 sequences of T=4096 tokens, 16
-heads, Dk = Dv = 128, state E4M3 with [128, 64] scale tiles, W E4M3 per
-(chunk, head): the whole forward path (gates, gated K K^T, exact solve, W/U,
-both QDQ sites, the sequential state recurrence, the output) runs in one
-kernel launch, with inputs resident in HBM. Prints one JSON line.
+One step = one forward over B=4 sequences of T=4096 tokens, 16 heads,
+Dk = Dv = 128, state E4M3 with [128, 64] scale tiles, W E4M3 per (chunk,
+head), inputs resident in HBM: the forward's two stages, as gdn_chunk_fwd
+runs them (gdn_chunk_fwd_prep: gates, gated K K^T, exact solve, W and its
+QDQ, U, masked Q K^T for every chunk and head; gdn_chunk_fwd_state: the state
+QDQ and sequential recurrence, and the output). Prints one JSON line.
 
-Roofline: algorithmic FLOPs per token and head at full 64x64 tiles,
-F = 2 (3 C Dk + 2 C Dv + 3 Dk Dv) + C^2 / 3 (C = 64; K K^T, W, Q K^T; U, P V;
-W S, K^T Vnew, Q S; the solve) = 181 589 for Dk = Dv = 128, divided by the
-kernel's average duration (HIP events around the timed launches on the
-launch stream), against the dense bf16 MFMA peak of 2.5 PFLOP/s.
+Algorithmic FLOPs per token and head at full 64x64 tiles (C = 64):
+  prep   2 (3 C Dk + C Dv) + C^2 / 3   (K K^T, Q K^T, W; U; the solve)
+  state  2 (3 Dk Dv + C Dv)            (W S, Q S, K^T Vnew; P Vnew)
+  total 181 589 for Dk = Dv = 128.
+`roofline` is the dominant (longer) kernel's own FLOPs per launch divided by
+its average duration, timed with HIP events on the launch stream around each
+stage of every timed step; `roofline_path` is the same for the whole forward.
+Peak: dense bf16 MFMA, 2.5 PFLOP/s.
 """
 import argparse
 import hashlib
@@ -32,8 +37,16 @@ PEAK_BF16_TFLOPS = 2500.0
 CHUNK = 64
 
 
+def flops_prep(Dk, Dv, C=CHUNK):
+    return 2 * (3 * C * Dk + C * Dv) + C * C / 3.0
+
+
+def flops_state(Dk, Dv, C=CHUNK):
+    return 2 * (3 * Dk * Dv + C * Dv)
+
+
 def flops_per_token_head(Dk, Dv, C=CHUNK):
-    return 2 * (3 * C * Dk + 2 * C * Dv + 3 * Dk * Dv) + C * C / 3.0
+    return flops_prep(Dk, Dv, C) + flops_state(Dk, Dv, C)
 
 
 def bytes_algorithmic(spec):
@@ -48,7 +61,11 @@ def bytes_algorithmic(spec):
 
 # Sources each timed kernel is compiled from; a committed counter summary is
 # used only while these files are unchanged.
-KERNEL_SOURCES = {'gdn_fwd_kernel': ('gdn_device.h', 'gdn_fwd.hip', 'gdn_launch.h')}
+KERNEL_SOURCES = {
+    'gdn_state_pair_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h',
+                              'gdn_fwd_state_pair.hip'),
+    'gdn_prep_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_fwd_prep.hip'),
+}
 
 
 def source_hash(kernel):
@@ -179,41 +196,52 @@ def main():
     scale = 1.0 / math.sqrt(spec['Dk'])
     kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
 
-    def step():
-        return B.gdn_chunk_fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], scale=scale, **kw)
+    plan = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], scale=scale, **kw)
 
     for _ in range(args.warmup):
-        step()
+        plan.prep()
+        plan.state()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
+    ev[0].record(stream)
+    for i in range(args.steps):
+        plan.prep()
+        ev[2 * i + 1].record(stream)
+        plan.state()
+        ev[2 * i + 2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = ev0.elapsed_time(ev1) / args.steps          # one launch per step
+    prep_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
+    state_ms = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     tokens = spec['B'] * spec['T']
-    token_heads = tokens * spec['Hv']
-    flops = flops_per_token_head(spec['Dk'], spec['Dv']) * token_heads
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    src = source_hash('gdn_fwd_kernel')
-    traffic = measured_traffic('gdn_fwd_kernel', src)
+    th = tokens * spec['Hv']
+    Dk, Dv = spec['Dk'], spec['Dv']
+    f_prep, f_state = flops_prep(Dk, Dv) * th, flops_state(Dk, Dv) * th
+    dom = 'gdn_state_pair_kernel' if state_ms >= prep_ms else 'gdn_prep_kernel'
+    dom_ms, dom_flops = (state_ms, f_state) if state_ms >= prep_ms else (prep_ms, f_prep)
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    path_ms = prep_ms + state_ms
+    path = (f_prep + f_state) / (path_ms * 1e-3) / 1e12
+    src = source_hash(dom)
+    traffic = measured_traffic(dom, src)
     out = dict(
         metric=METRIC, value=tokens / (ms_per_step * 1e-3), unit='tokens/s', n_gpus=1,
         steps=args.steps, warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True,
         scaling='weak', vs_baseline=None, dtype='bf16', data='synthetic',
         config=dict(workload=WORKLOAD, B=spec['B'], T=spec['T'], Hqk=spec['Hqk'],
-                    Hv=spec['Hv'], Dk=spec['Dk'], Dv=spec['Dv'], chunk=CHUNK,
+                    Hv=spec['Hv'], Dk=Dk, Dv=Dv, chunk=CHUNK,
                     state_qdq='e4m3', w_qdq='e4m3', block_v=spec['block_v'], parallelism='1gpu'),
         roofline=dict(bound='mfma', achieved=achieved, peak=PEAK_BF16_TFLOPS, unit='TFLOP/s',
-                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic),
-        kernel_ms=kern_ms, gflop_per_step=flops / 1e9,
-        hbm_gbs_algorithmic=bytes_algorithmic(spec) / (kern_ms * 1e-3) / 1e9,
+                      frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic, kernel=dom),
+        roofline_path=dict(bound='mfma', achieved=path, peak=PEAK_BF16_TFLOPS, unit='TFLOP/s',
+                           frac=path / PEAK_BF16_TFLOPS),
+        kernel_ms=dict(gdn_prep_kernel=prep_ms, gdn_state_pair_kernel=state_ms),
+        gflop_per_step=(f_prep + f_state) / 1e9,
+        hbm_gbs_algorithmic=bytes_algorithmic(spec) / (path_ms * 1e-3) / 1e9,
         source_hash=src)
     if not args.no_bwd:
         out['fwd_bwd'] = time_fwd_bwd(steps=max(3, args.steps // 5), warmup=2)

@@ -59,6 +59,8 @@ def load_library():
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.restype = c_i32
     for name, argt in (('gdn_chunk_fwd', [ctypes.POINTER(FwdArgs), c_vp]),
+                       ('gdn_chunk_fwd_prep', [ctypes.POINTER(FwdArgs), c_vp]),
+                       ('gdn_chunk_fwd_state', [ctypes.POINTER(FwdArgs), c_vp]),
                        ('gdn_chunk_bwd', [ctypes.POINTER(BwdArgs), c_vp]),
                        ('gdn_saved_layout', [ctypes.POINTER(FwdArgs), ctypes.POINTER(SavedLayout)]),
                        ('gdn_qdq_state', [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,
@@ -147,6 +149,36 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
     a.workspace_bytes = wbytes
     _check(lib.gdn_chunk_fwd(ctypes.byref(a), _stream(dev)))
     return o, ht, saved
+
+
+class FwdPlan:
+    """Forward arguments, outputs and workspace prepared once, for running
+    the two forward stages (prep, state) as separate calls on the current
+    stream: plan.prep(); plan.state(). Outputs: plan.o, plan.ht."""
+
+    def __init__(self, q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None,
+                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64):
+        lib = load_library()
+        dev = q.device
+        B, T, Hqk, Dk = q.shape
+        Hv, Dv = v.shape[2], v.shape[3]
+        N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+        self.o = torch.empty(B, T, Hv, Dv, dtype=q.dtype, device=dev)
+        self.ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev)
+        self._keep = (q, k, v, g, beta, h0, cu_seqlens)
+        self.args = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt,
+                                  block_v, self.o, self.ht)
+        wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(self.args))
+        self.ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
+        self.args.workspace = _ptr(self.ws)
+        self.args.workspace_bytes = wbytes
+        self.dev = dev
+
+    def prep(self):
+        _check(load_library().gdn_chunk_fwd_prep(ctypes.byref(self.args), _stream(self.dev)))
+
+    def state(self):
+        _check(load_library().gdn_chunk_fwd_state(ctypes.byref(self.args), _stream(self.dev)))
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu_seqlens=None,

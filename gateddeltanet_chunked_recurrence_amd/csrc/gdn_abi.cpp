@@ -236,7 +236,12 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a) {
   return (size_t)fwd_ws_layout(a).total;
 }
 
-gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Stages of the forward: 1 = prep (every chunk and head), 2 = state recurrence.
+gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
   gdn_status s = check_fwd_shape(a);
   if (s != GDN_OK) return s;
   if ((s = check_fwd_ptrs(a, true)) != GDN_OK) return s;
@@ -251,15 +256,31 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) {
   gdn::FwdKernelArgs k = kernel_args(a, a->saved);
   const gdn::FwdConfig cfg = fwd_config(a);
   if (a->io_dtype == GDN_F32)
-    return hip_status(gdn::launch_fwd_fused(cfg, k, st), "gdn_chunk_fwd launch");
+    return (stages & 2) ? hip_status(gdn::launch_fwd_fused(cfg, k, st), "gdn_chunk_fwd launch")
+                        : GDN_OK;
   char* ws = static_cast<char*>(a->workspace);
   k.ws_img = reinterpret_cast<__bf16*>(ws + W.img);
   k.ws_u = reinterpret_cast<float*>(ws + W.u);
   k.ws_wscale = reinterpret_cast<float*>(ws + W.wscale);
-  const int num_slots = (int)layout_of(a).num_slots;
-  s = hip_status(gdn::launch_fwd_prep(cfg, k, num_slots, st), "gdn_chunk_fwd prep launch");
-  if (s != GDN_OK) return s;
-  return hip_status(gdn::launch_fwd_state(cfg, k, st), "gdn_chunk_fwd state launch");
+  if (stages & 1) {
+    const int num_slots = (int)layout_of(a).num_slots;
+    s = hip_status(gdn::launch_fwd_prep(cfg, k, num_slots, st), "gdn_chunk_fwd prep launch");
+    if (s != GDN_OK) return s;
+  }
+  if (stages & 2) return hip_status(gdn::launch_fwd_state(cfg, k, st), "gdn_chunk_fwd state launch");
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) { return chunk_fwd_stages(a, stream, 3); }
+gdn_status gdn_chunk_fwd_prep(const gdn_fwd_args* a, void* stream) {
+  return chunk_fwd_stages(a, stream, 1);
+}
+gdn_status gdn_chunk_fwd_state(const gdn_fwd_args* a, void* stream) {
+  return chunk_fwd_stages(a, stream, 2);
 }
 
 size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a) {

@@ -138,6 +138,16 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
  * missing or too small). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
 
+/* The two stages of gdn_chunk_fwd, for callers that schedule or time them
+ * separately: gdn_chunk_fwd_prep (every chunk and head: solve, W and its QDQ,
+ * U, masked Q K^T, into the workspace; the saved W codes) then
+ * gdn_chunk_fwd_state (the state recurrence and the output, from that
+ * workspace) with the same arguments. For FP32 inputs the prep stage does
+ * nothing and the state stage runs the whole forward. Same checks and errors
+ * as gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_prep(const gdn_fwd_args* a, void* stream);
+gdn_status gdn_chunk_fwd_state(const gdn_fwd_args* a, void* stream);
+
 /* Backward arguments: the forward's arguments and `saved`, plus upstream
  * gradients. Identity straight-through at both QDQ sites; the saved Wq and
  * Sq are the values used in every product. grad_dtype applies to dq, dk, dv
