@@ -182,19 +182,24 @@ gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
   return c;
 }
 
-// Backward workspace sections (FP32, each 256-byte aligned):
-//   X      [num_slots, Hv, 64, 64]   (I + L)^-1 of every chunk
-//   W      [B*T, Hv, Dk]             the W of the products (dequantized Wq, or W)
-//   dstate [num_slots, Hv, Dk, Dv]   gradient of the state at each chunk end
-//   dvn    [num_slots, Hv, 64, Dv]   gradient of Vnew per chunk
-//   dqk    [B*T, Hv, 2, Dk]          dq, dk per value head before the group sum
+// Backward workspace sections (each 256-byte aligned):
+//   X      [num_slots, Hv, 64, 64] FP32   (I + L)^-1 of every chunk
+//   W      [B*T, Hv, Dk] FP32             the W of the products (dequantized Wq, or W)
+//   dstate [num_slots, Hv] x Dk x Dv FP32 gradient of the state at each chunk end
+//   dvn    [num_slots, Hv] x 64 x Dv FP32 gradient of Vnew per chunk
+//   dqk    [B*T, Hv, 2, Dk] FP32          dq, dk per value head before the group sum
+// and for bf16 inputs the operands of the reverse recurrence:
+//   bimg   [num_slots, Hv] x image block (K image, W^T planes, gates) bf16
+//   a1     [num_slots, Hv] x 64 x Dv FP32 scale P^T dO
+//   a2     [num_slots, Hv] x Dk x Dv FP32 scale (e^gamma Q)^T dO
 struct BwdWsLayout {
-  int64_t X, W, dstate, dvn, dqk, total;
+  int64_t X, W, dstate, dvn, dqk, bimg, a1, a2, total;
 };
 
 BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
   const gdn_saved_layout_t L = layout_of(a);
   const int64_t tokens = (int64_t)a->B * a->T, S = L.num_slots, Hv = a->Hv;
+  const bool bf = a->io_dtype == GDN_BF16;
   BwdWsLayout w{};
   int64_t off = 0;
   w.X = off;       off += round256(S * Hv * 64 * 64 * 4);
@@ -202,6 +207,9 @@ BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
   w.dstate = off;  off += round256(S * Hv * a->Dk * a->Dv * 4);
   w.dvn = off;     off += round256(S * Hv * 64 * a->Dv * 4);
   w.dqk = off;     off += round256(tokens * Hv * 2 * a->Dk * 4);
+  w.bimg = off;    off += bf ? round256(S * Hv * gdn::bwd_img_elems(a->Dk, a->policy.w_fmt) * 2) : 0;
+  w.a1 = off;      off += bf ? round256(S * Hv * 64 * a->Dv * 4) : 0;
+  w.a2 = off;      off += bf ? round256(S * Hv * a->Dk * a->Dv * 4) : 0;
   w.total = off;
   return w;
 }
@@ -328,6 +336,9 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   k.ws_dstate = reinterpret_cast<float*>(ws + W.dstate);
   k.ws_dvn = reinterpret_cast<float*>(ws + W.dvn);
   k.ws_dqk = reinterpret_cast<float*>(ws + W.dqk);
+  k.ws_bimg = reinterpret_cast<__bf16*>(ws + W.bimg);
+  k.ws_a1 = reinterpret_cast<float*>(ws + W.a1);
+  k.ws_a2 = reinterpret_cast<float*>(ws + W.a2);
   k.grad_f32 = a->grad_dtype == GDN_F32;
   k.total_tokens = (int32_t)tokens;
   k.num_slots = (int32_t)L.num_slots;

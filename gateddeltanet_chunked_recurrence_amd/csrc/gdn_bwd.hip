@@ -25,9 +25,11 @@
 //   bwd_prep    per (chunk, head): X by the blocked solve; the W of the products
 //   bwd_dstate  per (sequence, head, 64-wide value block), chunks in reverse:
 //               the dS recurrence; writes dS' and dVnew of every chunk, and dh0
+//               (FP32 inputs; bf16 inputs use gdn_bwd_state.hip)
 //   bwd_chunk   per (chunk, head): Vnew, dv, and every chunk-local gradient
 //   bwd_group   per (token, query/key head): dq, dk summed over the head group
 #include "gdn_device.h"
+#include "gdn_images.h"
 #include "gdn_launch.h"
 
 namespace gdn {
@@ -36,30 +38,6 @@ namespace {
 
 constexpr int NT = 256;          // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
-
-struct Chunk {
-  int n, c, t0, nc;
-  bool valid;
-};
-
-// Chunk of a slot (slot = n + bos_n / 64 + c, increasing in n; see gdn.h).
-__device__ Chunk locate_slot(int slot, const int32_t* cu, int N, int T) {
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const int bos = cu ? cu[mid] : mid * T;
-    if (mid + bos / CHUNK <= slot) lo = mid; else hi = mid - 1;
-  }
-  const int bos = cu ? cu[lo] : lo * T;
-  const int eos = cu ? cu[lo + 1] : (lo + 1) * T;
-  Chunk ch;
-  ch.n = lo;
-  ch.c = slot - (lo + bos / CHUNK);
-  ch.t0 = bos + CHUNK * ch.c;
-  ch.nc = min(CHUNK, eos - ch.t0);
-  ch.valid = ch.c >= 0 && ch.t0 < eos;
-  return ch;
-}
 
 struct Gates {
   alignas(16) float gam2[64];    // log2-scaled chunk-local cumsum
@@ -271,7 +249,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dstate(BwdKernelArgs a) {
     eos = bos + f.T;
   }
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
-  const int col = vb * 64 + 16 * wave + r16;        // this lane's value column
+  const int col = vb * 64 + 16 * wave + r16;        // this lane's value column (dht, dh0)
   const int64_t sbase = ((int64_t)n * Hv + h) * DK * Dv;
 
   f32x4 dS[MK];                                     // dS[mt][i] = dS[16 mt + 4 grp + i][col]
@@ -308,16 +286,12 @@ __global__ void __launch_bounds__(NT, 1) bwd_dstate(BwdKernelArgs a) {
     __syncthreads();
 
     // dS' of this chunk (the gradient at its end), kept for bwd_chunk
-    {
-      float* dsg = a.ws_dstate + ((int64_t)slot * Hv + h) * DK * Dv + col;
+    const int64_t chb = (int64_t)slot * Hv + h;
 #pragma unroll
-      for (int mt = 0; mt < MK; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dsg[(int64_t)(16 * mt + 4 * grp + i) * Dv] = dS[mt][i];
-    }
+    for (int mt = 0; mt < MK; ++mt)
+      *reinterpret_cast<f32x4*>(a.ws_dstate + frag_off(chb, Dv / 64, vb, wave, MK, mt, lane)) = dS[mt];
     // dVnew = scale P^T dO + diag(egc) K dS'
     f32x4 dVn[4];
-    float* dvg = a.ws_dvn + ((int64_t)slot * Hv + h) * 64 * Dv + col;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const f32x4 p = mm(Pf, 1, 65, dOf, 65, 1, 16 * mt, 16 * wave, 0, 64, r16, grp, zero4());
@@ -326,8 +300,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_dstate(BwdKernelArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * mt + 4 * grp + i;
         dVn[mt][i] = f.scale * p[i] + gs.egc[row] * q[i];
-        dvg[(int64_t)row * Dv] = dVn[mt][i];
       }
+      *reinterpret_cast<f32x4*>(a.ws_dvn + frag_off(chb, Dv / 64, vb, wave, 4, mt, lane)) = dVn[mt];
     }
     __syncthreads();                                 // dOf fully read
     for (int e = tid; e < 64 * 64; e += NT) dOf[(e >> 6) * 65 + (e & 63)] *= gs.eg[e >> 6];
@@ -423,15 +397,21 @@ __global__ void __launch_bounds__(NT, 1) bwd_chunk(BwdKernelArgs a, int N) {
     stage_rows<F32IN>(p1.Vf, 33, f.v, t0, nc, Hv, h, Dv, v0, 32, tid);
     stage_rows<F32IN>(p1.dOf, 33, a.dout, t0, nc, Hv, h, Dv, v0, 32, tid);
     {
-      const float* dvg = a.ws_dvn + ch_base * 64 * Dv;
-      const float* dsg = a.ws_dstate + ch_base * DK * Dv;
+      // dVnew and dS' come in fragment order (frag_off): the two 16-column
+      // groups of columns v0..v0+31 are one contiguous block
+      const int nvb = Dv / 64, vbk = v0 >> 6, w0 = (v0 & 63) >> 4;
+      const float* dvg = a.ws_dvn + frag_off(ch_base, nvb, vbk, w0, 4, 0, 0);
+      const float* dsg = a.ws_dstate + frag_off(ch_base, nvb, vbk, w0, NC, 0, 0);
       for (int e = tid; e < 64 * 32; e += NT) {
-        const int r = e >> 5, cc = e & 31;
-        p1.dVnf[r * 33 + cc] = dvg[(int64_t)r * Dv + v0 + cc];
+        const int i = e & 3, ln = (e >> 2) & 63, mt = (e >> 8) & 3, ws = e >> 10;
+        p1.dVnf[(16 * mt + 4 * (ln >> 4) + i) * 33 + 16 * ws + (ln & 15)] = dvg[e];
+      }
+      for (int e = tid; e < DK * 32; e += NT) {
+        const int i = e & 3, ln = (e >> 2) & 63, mt = (e >> 8) % NC, ws = (e >> 8) / NC;
+        p1.dSf[(16 * mt + 4 * (ln >> 4) + i) * 33 + 16 * ws + (ln & 15)] = dsg[e];
       }
       for (int e = tid; e < DK * 32; e += NT) {
         const int r = e >> 5, cc = e & 31;
-        p1.dSf[r * 33 + cc] = dsg[(int64_t)r * Dv + v0 + cc];
         float sq;
         if constexpr (SF == 0) {
           sq = f.s_f32[ch_base * DK * Dv + (int64_t)r * Dv + v0 + cc];
@@ -710,8 +690,13 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
 #undef GDN_PREP
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dstate<DK, F32IN>), dim3(c.Dv / 64, c.Hv, c.N), dim3(NT), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if constexpr (F32IN) {
+    hipLaunchKernelGGL((bwd_dstate<DK, F32IN>), dim3(c.Dv / 64, c.Hv, c.N), dim3(NT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    if ((e = launch_bwd_img(c, a, s)) != hipSuccess) return e;
+    if ((e = launch_bwd_state(c, a, s)) != hipSuccess) return e;
+  }
 #define GDN_CHUNK(SFv) \
   if (c.state_fmt == SFv) hipLaunchKernelGGL((bwd_chunk<DK, F32IN, SFv>), slots, dim3(NT), 0, s, a, c.N);
   GDN_CHUNK(0) GDN_CHUNK(1) GDN_CHUNK(2)

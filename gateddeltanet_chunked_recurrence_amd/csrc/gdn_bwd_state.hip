@@ -1,0 +1,490 @@
+// Backward, the reverse state recurrence of the chunked gated delta rule for
+// bf16 inputs, as two kernels ("[1/4] GDN state/W QAT foundation", "What does
+// this PR do?": identity STE at both QDQ sites, so the forward's Sq and Wq are
+// the values in every product and pass gradients unchanged).
+//
+// With dS' the gradient of the state after a chunk (dht after the last one),
+// reverse mode through one chunk of the forward (gdn_fwd_state.hip) gives
+//   dVnew = A1 + diag(e^(gamma_n - gamma)) K dS'
+//   dS    = e^gamma_n dS' + A2 - Wq^T dVnew
+// where the state-independent terms are
+//   A1 = scale P^T dO,                 P = (Q K^T) * Gam (i >= j)
+//   A2 = scale (diag(e^gamma) Q)^T dO.
+//
+// bwd_img_kernel, one workgroup per (chunk, value head), computes A1 and A2
+// with bf16 MFMA (bf16 inputs exact, FP32 factors as hi + lo pairs) and writes
+// the recurrence's other operands in the layout its LDS keeps them:
+//   K image    [64][Dk] bf16, the forward's W image layout (pperm along dk)
+//   W^T image  [Dk][72] bf16, the transposed W of the products, pperm along
+//              tokens: the Wq codes (one plane; the scale is applied to the
+//              other factor) or, with W QDQ off, W as hi + lo (two planes)
+//   gates      256 FP32: e^(gamma_n - gamma_i) at [i] (0 past the chunk end),
+//              e^gamma_n at [64], minus the W scale at [65]
+// A1 and A2 are stored in fragment order (frag_off), so the recurrence loads
+// its accumulator tiles with 16-byte loads.
+//
+// bwd_state_kernel, one workgroup per (sequence, value head, 64-wide value
+// block), runs the chunks in reverse with dS in registers (wave w holds value
+// columns 16w..16w+15 in accumulator layout; the columns are independent, as
+// the backward has no QDQ). It stores dS' and dVnew of every chunk, fragment
+// order, for the chunk-local gradients, and dh0 at the end.
+//
+// Transposes go through the matrix core: a bf16 row tile read as an A operand
+// times a 0/1 selection B operand is the same tile in accumulator layout,
+// exactly (one nonzero product per output), and two such tiles stacked along
+// the tokens are an operand with the tokens as contraction index (pack_pair).
+#include "gdn_device.h"
+#include "gdn_images.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int NT = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Image block of one (slot, head) for the reverse recurrence.
+template <int DK>
+struct BImg {
+  using I = Img<DK>;
+  static constexpr int KI = I::WQ;                 // K image [64][RS]
+  static constexpr int WT = I::KT;                 // one W^T plane [DK][72]
+  static constexpr int GB = 512;                   // gate block, 256 FP32
+  static constexpr int size(int nw) { return KI + nw * WT + GB; }
+  static constexpr int g_at(int nw) { return KI + nw * WT; }
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The selection operand: lane (grp, r16) holds B[8 grp + e][r16] = 1 exactly
+// when 8 grp + e = 16 half + r16, so A B = columns 16 half .. 16 half + 15 of A.
+__device__ __forceinline__ bf16x8 select_op(int half, int r16, int grp) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = to_bf16(8 * grp + e == 16 * half + r16 ? 1.f : 0.f);
+  return r;
+}
+
+// Accumulator-layout tile of rows row0..row0+15, columns 16 ct..16 ct + 15 of
+// a bf16 row-major LDS matrix (row stride ld).
+__device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct, int r16, int grp,
+                                         const bf16x8 (&sel)[2]) {
+  return mfma(lds_nat(m, row0 + r16, ld, 32 * (ct >> 1), grp), sel[ct & 1], zero4());
+}
+
+template <int DK>
+struct ImgSmem {
+  static constexpr int LD = DK + 8;                // padded row strides (bf16)
+  static constexpr int LDO = 256 + 8;
+  bf16 Kn[64 * LD];
+  bf16 Qn[64 * LD];
+  bf16 Wn[2][64 * LD];                             // W codes, or W hi and lo
+  bf16 dOn[64 * LDO];
+  bf16x8 dOB[2 * 16 * 64];                         // dO operands [kk][value tile][lane]
+  float gam2[64], eg[64];
+};
+
+// ---------------------------------------------------------------- bwd_img
+template <int DK, int WF>
+__global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) {
+  constexpr int NW = WF == 0 ? 2 : 1;
+  constexpr int MK = DK / 16, DPW = MK / 4;        // dk tiles, dk tiles per wave
+  using S = ImgSmem<DK>;
+  using I = Img<DK>;
+  using BI = BImg<DK>;
+  constexpr int LD = S::LD, LDO = S::LDO;
+  __shared__ __align__(16) S sm;
+  const FwdKernelArgs& f = a.f;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  if (!ch.valid) return;
+  const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, NVT = Dv / 16, nvb = Dv / 64;
+  const int hk = h / (Hv / Hqk), t0 = ch.t0, nc = ch.nc;
+  const int64_t chb = (int64_t)slot * Hv + h;
+  bf16* img = a.ws_bimg + chb * BI::size(NW);
+
+  // ---- rows of K, Q, dO and W into LDS (rows past the chunk end are zero)
+  {
+    const bf16* kg = reinterpret_cast<const bf16*>(f.k);
+    const bf16* qg = reinterpret_cast<const bf16*>(f.q);
+    for (int e = tid; e < 64 * DK / 8; e += NT) {
+      const int row = e / (DK / 8), c8 = e % (DK / 8);
+      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hqk + hk) * DK + 8 * c8;
+      u32x4 kv = *reinterpret_cast<const u32x4*>(kg + off);
+      u32x4 qv = *reinterpret_cast<const u32x4*>(qg + off);
+      if (row >= nc) kv = qv = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sm.Kn[row * LD + 8 * c8]) = kv;
+      *reinterpret_cast<u32x4*>(&sm.Qn[row * LD + 8 * c8]) = qv;
+    }
+    const bf16* dog = reinterpret_cast<const bf16*>(a.dout);
+    const int p8 = Dv / 8;
+    for (int e = tid; e < 64 * p8; e += NT) {
+      const int row = e / p8, c8 = e % p8;
+      u32x4 v = *reinterpret_cast<const u32x4*>(
+          dog + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * Dv + 8 * c8);
+      if (row >= nc) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sm.dOn[row * LDO + 8 * c8]) = v;
+    }
+    if constexpr (WF != 0) {
+      // codes (exact in bf16: E4M3 values and integers up to 127)
+      for (int e = tid; e < 64 * DK / 16; e += NT) {
+        const int row = e / (DK / 16), c16 = e % (DK / 16);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(
+            f.w_codes + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 16 * c16);
+        bf16x8 o[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t word = b[j >> 2];
+          float cv;
+          if constexpr (WF == 1) {
+            cv = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word >> (8 * (j & 3))), 0);
+          } else {
+            cv = static_cast<float>(static_cast<int8_t>((word >> (8 * (j & 3))) & 0xFFu));
+          }
+          o[j >> 3][j & 7] = to_bf16(row < nc ? cv : 0.f);
+        }
+        *reinterpret_cast<bf16x8*>(&sm.Wn[0][row * LD + 16 * c16]) = o[0];
+        *reinterpret_cast<bf16x8*>(&sm.Wn[0][row * LD + 16 * c16 + 8]) = o[1];
+      }
+    } else {
+      for (int e = tid; e < 64 * DK / 4; e += NT) {
+        const int row = e / (DK / 4), c4 = e % (DK / 4);
+        f32x4 w = *reinterpret_cast<const f32x4*>(
+            a.ws_W + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 4 * c4);
+        if (row >= nc) w = zero4();
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16 hj, lj;
+          split2(w[j], hj, lj);
+          hi[j] = hj;
+          lo[j] = lj;
+        }
+        *reinterpret_cast<bf16x4*>(&sm.Wn[0][row * LD + 4 * c4]) = hi;
+        *reinterpret_cast<bf16x4*>(&sm.Wn[1][row * LD + 4 * c4]) = lo;
+      }
+    }
+  }
+  // ---- gates (wave 0): LDS copies for this kernel, the gate block for the recurrence
+  if (wave == 0) {
+    const bool valid = lane < nc;
+    const int64_t gi = (int64_t)(t0 + min(lane, nc - 1)) * Hv + h;
+    const float g2 = wave_incl_scan(valid ? f.g[gi] * LOG2E : 0.f, lane);
+    const float g2n = __shfl(g2, nc - 1, WAVE);
+    sm.gam2[lane] = g2;
+    sm.eg[lane] = fexp2(g2);
+    float* G = reinterpret_cast<float*>(img + BI::g_at(NW));
+    G[lane] = valid ? fexp2(g2n - g2) : 0.f;
+    if (lane == 0) {
+      G[64] = fexp2(g2n);
+      G[65] = WF != 0 ? -f.w_scale[chb] : -1.f;
+    }
+  }
+  __syncthreads();
+
+  bf16x8 sel[2];
+  sel[0] = select_op(0, r16, grp);
+  sel[1] = select_op(1, r16, grp);
+
+  // ---- dO operands, tokens as contraction index (shared by A1 and A2)
+  for (int fi = wave; fi < 2 * NVT; fi += 4) {
+    const int kk = fi & 1, vt = fi >> 1;
+    const f32x4 c0 = tile_of(sm.dOn, LDO, 32 * kk, vt, r16, grp, sel);
+    const f32x4 c1 = tile_of(sm.dOn, LDO, 32 * kk + 16, vt, r16, grp, sel);
+    sm.dOB[(kk * 16 + vt) * 64 + lane] = pack_pair(c0, c1);
+  }
+
+  // ---- (e^gamma Q)^T operands for this wave's dk tiles: hi + lo
+  bf16x8 aQh[DPW][2], aQl[DPW][2];
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int dt = DPW * wave + d;
+    f32x4 cq[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      cq[it] = tile_of(sm.Qn, LD, 16 * it, dt, r16, grp, sel);
+      const f32x4 e = *reinterpret_cast<const f32x4*>(&sm.eg[16 * it + 4 * grp]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cq[it][q] *= e[q];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) pack_pair_split(cq[2 * kk], cq[2 * kk + 1], aQh[d][kk], aQl[d][kk]);
+  }
+
+  // ---- P^T operands for key tile jt = wave: P = (Q K^T) * Gam, i >= j
+  const int jt = wave;
+  bf16x8 aPh[2], aPl[2];
+  {
+    f32x4 pt[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      pt[it] = zero4();
+      if (it < jt) continue;
+#pragma unroll
+      for (int kq = 0; kq < DK / 32; ++kq)
+        pt[it] = mfma(lds_nat(sm.Qn, 16 * it + r16, LD, 32 * kq, grp),
+                      lds_nat(sm.Kn, 16 * jt + r16, LD, 32 * kq, grp), pt[it]);
+      const int j = 16 * jt + r16;
+      const float gj = sm.gam2[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * it + 4 * grp + q;
+        pt[it][q] = i >= j ? pt[it][q] * fexp2(sm.gam2[i] - gj) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) pack_pair_split(pt[2 * kk], pt[2 * kk + 1], aPh[kk], aPl[kk]);
+  }
+  __syncthreads();                                 // dO operands complete
+
+  const float scale = f.scale;
+  // ---- A1 = scale P^T dO, rows of key tile jt
+  for (int vt = 0; vt < NVT; ++vt) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (2 * kk + 1 < jt) continue;               // both query tiles above the diagonal
+      const bf16x8 b = sm.dOB[(kk * 16 + vt) * 64 + lane];
+      acc = mfma(aPh[kk], b, acc);
+      acc = mfma(aPl[kk], b, acc);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] *= scale;
+    *reinterpret_cast<f32x4*>(a.ws_a1 + frag_off(chb, nvb, vt >> 2, vt & 3, 4, jt, lane)) = acc;
+  }
+  // ---- A2 = scale (e^gamma Q)^T dO, this wave's dk tiles
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int dt = DPW * wave + d;
+    for (int vt = 0; vt < NVT; ++vt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 b = sm.dOB[(kk * 16 + vt) * 64 + lane];
+        acc = mfma(aQh[d][kk], b, acc);
+        acc = mfma(aQl[d][kk], b, acc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] *= scale;
+      *reinterpret_cast<f32x4*>(a.ws_a2 + frag_off(chb, nvb, vt >> 2, vt & 3, MK, dt, lane)) = acc;
+    }
+  }
+  // ---- K image: pperm along dk, 16-byte chunks swizzled by row
+  for (int p = tid; p < 64 * DK / 8; p += NT) {
+    const int row = p / (DK / 8), cs = p % (DK / 8), b = cs >> 2, g4 = cs & 3;
+    const uint2 lo = *reinterpret_cast<const uint2*>(&sm.Kn[row * LD + 32 * b + 4 * g4]);
+    const uint2 hi = *reinterpret_cast<const uint2*>(&sm.Kn[row * LD + 32 * b + 16 + 4 * g4]);
+    *reinterpret_cast<u32x4*>(img + row * I::RS + ((cs ^ (row & I::SWZ)) << 3)) =
+        u32x4{lo.x, lo.y, hi.x, hi.y};
+  }
+  // ---- W^T image: dk rows, tokens paired along the row
+  for (int fi = wave; fi < 2 * MK; fi += 4) {
+    const int dt = fi >> 1, kk = fi & 1;
+#pragma unroll
+    for (int pl = 0; pl < NW; ++pl) {
+      const f32x4 c0 = tile_of(sm.Wn[pl], LD, 32 * kk, dt, r16, grp, sel);
+      const f32x4 c1 = tile_of(sm.Wn[pl], LD, 32 * kk + 16, dt, r16, grp, sel);
+      *reinterpret_cast<bf16x8*>(img + BI::KI + pl * BI::WT + (16 * dt + r16) * I::R64 + 32 * kk +
+                                 8 * grp) = pack_pair(c0, c1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_state
+template <int DK, int NW>
+__global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N, int num_heads) {
+  using BI = BImg<DK>;
+  using I = Img<DK>;
+  constexpr int MK = DK / 16;
+  constexpr int SZ = BI::size(NW);
+  static_assert((SZ / 8) % 64 == 0, "image block is a whole number of wave loads");
+  constexpr int NINS = SZ / 8 / 64;                // 1 KB wave loads per block
+  constexpr int KW = (NINS + 3) / 4;               // per wave
+  __shared__ __align__(16) bf16 buf[2][SZ];
+
+  const FwdKernelArgs& f = a.f;
+  const int Hv = f.Hv, Dv = f.Dv, NVB = Dv / 64;
+  // workgroup id -> (head index, value block); the blocks of a head share an XCD
+  const int bid = blockIdx.x, xcd = bid & 7, r8 = bid >> 3;
+  const int vb = r8 % NVB, hidx = xcd + 8 * (r8 / NVB);
+  if (hidx >= num_heads) return;
+  const int n = hidx / Hv, h = hidx % Hv;
+  int bos, eos;
+  if (f.cu_seqlens) {
+    bos = f.cu_seqlens[n];
+    eos = f.cu_seqlens[n + 1];
+  } else {
+    bos = n * f.T;
+    eos = bos + f.T;
+  }
+  const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
+  const int slot0 = n + bos / CHUNK;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int wcol = vb * 64 + wave * 16;
+  const int64_t sbase = ((int64_t)n * Hv + h) * DK * Dv;
+
+  // dS in accumulator layout: dS[mt][i] = dS[16 mt + 4 grp + i][wcol + r16]
+  f32x4 dS[MK];
+#pragma unroll
+  for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dS[mt][i] = a.dht ? a.dht[sbase + (int64_t)(16 * mt + 4 * grp + i) * Dv + wcol + r16] : 0.f;
+
+  auto chunk_ch = [&](int c) { return (int64_t)(slot0 + c) * Hv + h; };
+  auto dma = [&](int c, int b) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.ws_bimg + chunk_ch(c) * SZ);
+    u32x4* dst = reinterpret_cast<u32x4*>(buf[b]);
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      const int j = min(wave + 4 * k, NINS - 1);
+      __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
+    }
+  };
+  f32x4 A1c[4], A1n[4], A2c[MK], A2n[MK];
+  auto load_a = [&](int c, f32x4 (&A1)[4], f32x4 (&A2)[MK]) {
+    const int64_t ch = chunk_ch(c);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      A1[mt] = *reinterpret_cast<const f32x4*>(a.ws_a1 + frag_off(ch, NVB, vb, wave, 4, mt, lane));
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt)
+      A2[mt] = *reinterpret_cast<const f32x4*>(a.ws_a2 + frag_off(ch, NVB, vb, wave, MK, mt, lane));
+  };
+
+  if (nchunks > 0) {
+    dma(nchunks - 1, (nchunks - 1) & 1);
+    load_a(nchunks - 1, A1c, A2c);
+    wait_vmem();
+    lds_barrier();
+  }
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const int64_t ch = chunk_ch(c);
+    const bf16* B = buf[c & 1];
+    if (c > 0) {
+      dma(c - 1, (c - 1) & 1);
+      load_a(c - 1, A1n, A2n);
+    }
+    // dS' of this chunk, for the chunk-local gradients
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt)
+      *reinterpret_cast<f32x4*>(a.ws_dstate + frag_off(ch, NVB, vb, wave, MK, mt, lane)) = dS[mt];
+    // dS' as B operands (paired order over dk), hi + lo
+    bf16x8 bSh[MK / 2], bSl[MK / 2];
+#pragma unroll
+    for (int kk = 0; kk < MK / 2; ++kk) pack_pair_split(dS[2 * kk], dS[2 * kk + 1], bSh[kk], bSl[kk]);
+    // K dS'
+    f32x4 t1[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) t1[mt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < MK / 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 ak = ld_wq<DK>(B, 16 * mt + r16, kk, grp);
+        t1[mt] = mfma(ak, bSh[kk], t1[mt]);
+        t1[mt] = mfma(ak, bSl[kk], t1[mt]);
+      }
+    // dVnew = A1 + e^(gamma_n - gamma) K dS'
+    const float* G = reinterpret_cast<const float*>(B + BI::g_at(NW));
+    f32x4 dvn[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4 egc = *reinterpret_cast<const f32x4*>(&G[16 * mt + 4 * grp]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dvn[mt][i] = fmaf(egc[i], t1[mt][i], A1c[mt][i]);
+      *reinterpret_cast<f32x4*>(a.ws_dvn + frag_off(ch, NVB, vb, wave, 4, mt, lane)) = dvn[mt];
+    }
+    // -dW dVnew as B operands (paired order over tokens), hi + lo
+    const float nsc = G[65], egC = G[64];
+    bf16x8 bVh[2], bVl[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x4 d0, d1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d0[i] = nsc * dvn[2 * kk][i];
+        d1[i] = nsc * dvn[2 * kk + 1][i];
+      }
+      pack_pair_split(d0, d1, bVh[kk], bVl[kk]);
+    }
+    // dS = e^gamma_n dS' + A2 - dW W^T dVnew
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[mt][i] = fmaf(egC, dS[mt][i], A2c[mt][i]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < MK; ++mt) {
+        const bf16x8 aw = lds_nat(B + BI::KI, 16 * mt + r16, I::R64, 32 * kk, grp);
+        dS[mt] = mfma(aw, bVh[kk], dS[mt]);
+        dS[mt] = mfma(aw, bVl[kk], dS[mt]);
+        if constexpr (NW == 2) {
+          const bf16x8 al = lds_nat(B + BI::KI + BI::WT, 16 * mt + r16, I::R64, 32 * kk, grp);
+          dS[mt] = mfma(al, bVh[kk], dS[mt]);
+        }
+      }
+    wait_vmem();                                   // staging of chunk c - 1 landed
+    lds_barrier();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) A1c[mt] = A1n[mt];
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt) A2c[mt] = A2n[mt];
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a.dh0[sbase + (int64_t)(16 * mt + 4 * grp + i) * Dv + wcol + r16] = dS[mt][i];
+  }
+}
+
+template <int DK>
+static hipError_t launch_img_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  const dim3 grid(a.num_slots, c.Hv);
+#define GDN_CASE(WFv) \
+  if (c.w_fmt == WFv) { \
+    hipLaunchKernelGGL((bwd_img_kernel<DK, WFv>), grid, dim3(NT), 0, s, a, c.N); \
+    return hipGetLastError(); \
+  }
+  GDN_CASE(0) GDN_CASE(1) GDN_CASE(2)
+#undef GDN_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int NW>
+static hipError_t launch_state_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  const int num_heads = c.N * c.Hv, nvb = c.Dv / 64;
+  const int64_t nblk = (int64_t)nvb * 8 * ((num_heads + 7) / 8);
+  hipLaunchKernelGGL((bwd_state_kernel<DK, NW>), dim3((unsigned)nblk), dim3(NT), 0, s, a, c.N,
+                     num_heads);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_img_elems(int Dk, int w_fmt) {
+  const int nw = w_fmt == 0 ? 2 : 1;
+  return Dk == 128 ? BImg<128>::size(nw) : BImg<64>::size(nw);
+}
+
+hipError_t launch_bwd_img(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  if (c.Dk == 128) return launch_img_dk<128>(c, a, s);
+  if (c.Dk == 64) return launch_img_dk<64>(c, a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_state(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  const bool w_on = c.w_fmt != 0;
+  if (c.Dk == 128) return w_on ? launch_state_dk<128, 1>(c, a, s) : launch_state_dk<128, 2>(c, a, s);
+  if (c.Dk == 64) return w_on ? launch_state_dk<64, 1>(c, a, s) : launch_state_dk<64, 2>(c, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -55,9 +55,44 @@ __device__ __forceinline__ bf16x8 ld_wq(const bf16* img, int row, int kk, int gr
   return *reinterpret_cast<const bf16x8*>(img + wq_off<DK>(row, 32 * kk + 8 * grp));
 }
 
+// The chunk of a slot (slot = n + bos_n / 64 + c, increasing in n; see
+// gdn.h): sequence n, chunk c, first token t0 and length nc; `valid` is false
+// for the spare slot after each sequence's last chunk.
+struct Chunk {
+  int n, c, t0, nc;
+  bool valid;
+};
+__device__ inline Chunk locate_slot(int slot, const int32_t* cu, int N, int T) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int bos = cu ? cu[mid] : mid * T;
+    if (mid + bos / CHUNK <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int bos = cu ? cu[lo] : lo * T;
+  const int eos = cu ? cu[lo + 1] : (lo + 1) * T;
+  Chunk ch;
+  ch.n = lo;
+  ch.c = slot - (lo + bos / CHUNK);
+  ch.t0 = bos + CHUNK * ch.c;
+  ch.nc = min(CHUNK, eos - ch.t0);
+  ch.valid = ch.c >= 0 && ch.t0 < eos;
+  return ch;
+}
+
 // Float offset of the U fragment (ch, vb, w, mt) of lane `lane`.
 __device__ __forceinline__ int64_t u_off(int64_t ch, int nvb, int vb, int w, int mt, int lane) {
   return ((((ch * nvb + vb) * 4 + w) * 4 + mt) * 64 + lane) * 4;
+}
+
+// Fragment order of an FP32 [MT * 16, Dv] matrix per (slot, head) `ch`: the
+// accumulator tile (row tile mt, value block vb, 16-column group w) of lane
+// `lane` is four contiguous floats, element i at row 16 mt + 4 (lane >> 4) + i,
+// column 64 vb + 16 w + (lane & 15). The two column groups of a 32-column
+// range are adjacent, so a consumer reads them as one contiguous block.
+__device__ __forceinline__ int64_t frag_off(int64_t ch, int nvb, int vb, int w, int MT, int mt,
+                                            int lane) {
+  return (((((ch * nvb + vb) * 4 + w) * MT + mt) * 64) + lane) * 4;
 }
 
 }  // namespace gdn

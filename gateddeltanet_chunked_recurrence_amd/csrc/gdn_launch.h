@@ -55,8 +55,12 @@ struct BwdKernelArgs {
   float* dh0;                 // nullable
   float* ws_X;                // [num_slots, Hv, 64, 64] FP32: X = (I + L)^-1 per chunk
   float* ws_W;                // [B*T, Hv, Dk] FP32: the W used in the products (Wq or W)
-  float* ws_dstate;           // [num_slots, Hv, Dk, Dv] FP32: dL/dS at the end of each chunk
-  float* ws_dvn;              // [num_slots, Hv, 64, Dv] FP32: dL/dVnew per chunk
+  float* ws_dstate;           // [num_slots, Hv] x [Dk, Dv] FP32 fragment order: dL/dS at each chunk end
+  float* ws_dvn;              // [num_slots, Hv] x [64, Dv] FP32 fragment order: dL/dVnew per chunk
+  // bf16 io: operands of the reverse recurrence, written by bwd_img_kernel
+  __bf16* ws_bimg;            // [num_slots * Hv][K image | W^T planes | gates] (gdn_bwd_state.hip)
+  float* ws_a1;               // [num_slots * Hv] x [64, Dv] fragment order: scale P^T dO
+  float* ws_a2;               // [num_slots * Hv] x [Dk, Dv] fragment order: scale (e^gamma Q)^T dO
   float* ws_dqk;              // [B*T, Hv, 2, Dk] FP32 per-value-head dq, dk before the group sum
   int32_t grad_f32;
   int32_t total_tokens;
@@ -68,6 +72,11 @@ struct BwdConfig {
 };
 
 hipError_t launch_bwd(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+// bf16 io: operand images of the reverse recurrence, then the recurrence.
+hipError_t launch_bwd_img(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+hipError_t launch_bwd_state(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+// Elements of the backward image block of one (slot, head).
+int bwd_img_elems(int Dk, int w_fmt);
 
 hipError_t launch_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
                             int64_t n_states, int Dk, int Dv, int block_v, int fmt,
