@@ -697,11 +697,15 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
     if ((e = launch_bwd_img(c, a, s)) != hipSuccess) return e;
     if ((e = launch_bwd_state(c, a, s)) != hipSuccess) return e;
   }
+  if constexpr (F32IN) {
 #define GDN_CHUNK(SFv) \
   if (c.state_fmt == SFv) hipLaunchKernelGGL((bwd_chunk<DK, F32IN, SFv>), slots, dim3(NT), 0, s, a, c.N);
-  GDN_CHUNK(0) GDN_CHUNK(1) GDN_CHUNK(2)
+    GDN_CHUNK(0) GDN_CHUNK(1) GDN_CHUNK(2)
 #undef GDN_CHUNK
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    if ((e = launch_bwd_local(c, a, s)) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((bwd_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, s, a, c.Hv / c.Hqk);
   return hipGetLastError();
 }

@@ -1,0 +1,807 @@
+// Backward, the chunk-local gradients for bf16 inputs: one workgroup per
+// (chunk, value head), after the reverse recurrence has stored dS' (the
+// gradient of the state at the chunk's end) and dVnew of every chunk
+// ("[1/4] GDN state/W QAT foundation", "What does this PR do?": identity STE at
+// both QDQ sites, the forward's quantized W reused; the products use the
+// forward's Sq and Wq).
+//
+// Per chunk (forward in gdn_fwd_state.hip, reverse recurrence in
+// gdn_bwd_state.hip), with T = X diag(beta), X = (I + L)^-1:
+//   Vnew = T V - Wq Sq                          recomputed
+//   dv   = T^T dVnew
+//   dW   = -dVnew Sq^T,  dQi = dO Sq^T,  dKs = Vnew dS'^T
+//   dP   = dO Vnew^T,    dTU = dVnew V^T
+//   G    = scale dP * Gam (t >= s),  dq = scale e^gamma dQi + G K
+//   dT   = dW (e^gamma K)^T + dTU,   dX = dT diag(beta)
+//   dL   = -(X^T dX X^T) below the diagonal,  dA = dL beta_t Gam (t > s)
+//   dk   = G^T Q + e^(gamma_n - gamma) dKs + beta e^gamma X^T dW + (dA + dA^T) K
+// plus d beta and the gate gradient (reverse chunk-local cumsum of d gamma).
+//
+// All products run on bf16 MFMA 16x16x32 with FP32 accumulation: bf16 inputs
+// enter exactly, FP32 factors as hi + lo pairs (three products when both
+// factors are FP32, two when one is exact). An operand of a product needs its
+// contraction index contiguous in each lane. Matrices live in LDS row-major as
+// bf16 planes; an operand contracting over a row's columns is a plain LDS read
+// (paired K order, lds_pair), and one contracting over a matrix's rows comes
+// from accumulator-layout tiles of that matrix, which the matrix core makes
+// exactly from the row-major planes (A times a 0/1 selection operand).
+// Accumulator tiles are published to LDS transposed with 8-byte writes (a
+// tile's lane holds four consecutive rows of one column), or as they are after
+// a transpose through the matrix core.
+//
+// Work split, 8 waves: wave w owns row tile tw = w & 3 and column half
+// hk = w >> 2 of every [64 x *] result (token rows; dk, dq, dW, dQi, dKs over
+// k-tiles of that half, the 64 x 64 results over token tiles of that half).
+#include "gdn_device.h"
+#include "gdn_images.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int NT = 512;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int L64 = 72;                            // row stride of 64-wide LDS matrices
+
+// Selection operand in paired K order (pperm): lane (grp, r16) holds
+// B[k(e)][r16] = 1 exactly when k(e) = 16 h + r16, where position e stands for
+// row 4 grp + e (e < 4) or 16 + 4 grp + e - 4 (e >= 4).
+__device__ __forceinline__ bf16x8 sel_pair(int h, int r16, int grp) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = e < 4 ? 4 * grp + e : 16 + 4 * grp + (e - 4);
+    r[e] = to_bf16(k == 16 * h + r16 ? 1.f : 0.f);
+  }
+  return r;
+}
+
+struct Sel {
+  bf16x8 pair[2];
+};
+
+// Accumulator tile (rows row0..row0+15, columns 16 ct..16 ct+15) of a
+// row-major bf16 LDS matrix, exact (the row read in paired order times the
+// paired selection).
+__device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct, int r16, int grp,
+                                         const Sel& s) {
+  return mfma(lds_pair(m, row0 + r16, ld, 32 * (ct >> 1), grp), s.pair[ct & 1], zero4());
+}
+// Operand contracting over rows r0..r0+31 (paired order), free index = columns
+// 16 ct..16 ct+15.
+__device__ __forceinline__ bf16x8 colp(const bf16* m, int ld, int r0, int ct, int r16, int grp,
+                                       const Sel& s) {
+  return pack_pair(tile_of(m, ld, r0, ct, r16, grp, s), tile_of(m, ld, r0 + 16, ct, r16, grp, s));
+}
+// Operand contracting over columns k0..k0+31 (paired order), free index = rows
+// row0..row0+15.
+__device__ __forceinline__ bf16x8 rowp(const bf16* m, int ld, int row0, int k0, int r16, int grp) {
+  return lds_pair(m, row0 + r16, ld, k0, grp);
+}
+
+// Transpose of accumulator tiles through the matrix core. c0, c1 are the tiles
+// of rows 32p..32p+15 and 32p+16..32p+31 (same 16 columns) of M, already
+// exact in bf16; the result is the accumulator tile of M^T for rows 32p + 16h
+// ..+15 of M: lane holds M[32p + 16h + r16][col0 + 4 grp + i].
+__device__ __forceinline__ f32x4 trans(const f32x4& c0, const f32x4& c1, int h, const Sel& s) {
+  return mfma(pack_pair(c0, c1), s.pair[h], zero4());
+}
+
+// Splits an FP32 tile into exact bf16 hi and lo parts (as FP32 values).
+__device__ __forceinline__ void split_tile(const f32x4& x, f32x4& hi, f32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float h = from_bf16(to_bf16(x[i]));
+    hi[i] = h;
+    lo[i] = from_bf16(to_bf16(x[i] - h));
+  }
+}
+
+// Writes four consecutive elements (FP32, exact in bf16 unless split) of one
+// row of a row-major bf16 matrix (one plane).
+__device__ __forceinline__ void put4(bf16* m, int off, const f32x4& v) {
+  *reinterpret_cast<bf16x4*>(m + off) = bf16x4{to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3])};
+}
+// Publishes an FP32 accumulator tile (rows 16 rt.., columns 16 ct..) of M as
+// rows of M^T (hi and lo planes): M^T[16 ct + r16][16 rt + 4 grp + i].
+__device__ __forceinline__ void put_T(bf16* p0, bf16* p1, int ld, const f32x4& c, int rt, int ct,
+                                      int r16, int grp) {
+  f32x4 h, l;
+  split_tile(c, h, l);
+  const int off = (16 * ct + r16) * ld + 16 * rt + 4 * grp;
+  put4(p0, off, h);
+  put4(p1, off, l);
+}
+// Publishes the same tile as rows of M (through a transpose).
+__device__ __forceinline__ void put_N(bf16* p0, bf16* p1, int ld, const f32x4& c, int rt, int ct,
+                                      int r16, int grp, const Sel& s) {
+  f32x4 h, l;
+  split_tile(c, h, l);
+  const f32x4 z = zero4();
+  const int odd = rt & 1;
+  const f32x4 th = trans(odd ? z : h, odd ? h : z, odd, s);
+  const f32x4 tl = trans(odd ? z : l, odd ? l : z, odd, s);
+  const int off = (16 * rt + r16) * ld + 16 * ct + 4 * grp;
+  put4(p0, off, th);
+  put4(p1, off, tl);
+}
+
+__device__ __forceinline__ f32x4 mm2(f32x4 acc, bf16x8 a0, bf16x8 a1, bf16x8 b) {
+  return mfma(a1, b, mfma(a0, b, acc));
+}
+// (a0 + a1)(b0 + b1) without the lo * lo term
+__device__ __forceinline__ f32x4 mm3(f32x4 acc, bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1) {
+  return mfma(a0, b1, mfma(a1, b0, mfma(a0, b0, acc)));
+}
+
+template <int DK, int VB, int NWP>
+struct VLoopSmem {
+  static constexpr int LDK = DK + 8, LVB = VB + 8;
+  bf16 Wm[NWP][64 * LDK];
+  bf16 Tm[2][64 * L64];
+  bf16 Vm[64 * LVB];
+  bf16 dOm[64 * LVB];
+  bf16 Sqm[2][DK * LVB];
+  bf16 Vnm[2][64 * LVB];
+  bf16 dSm[2][DK * LVB];
+};
+
+template <int DK>
+struct FinSmem {
+  static constexpr int LDK = DK + 8;
+  static constexpr int QM1 = (64 * LDK > 2 * 64 * L64) ? 64 * LDK : 2 * 64 * L64;
+  bf16 Km[64 * LDK];
+  bf16 QM1m[QM1];                                  // Q rows, later M1 planes
+  bf16 Xm[2][64 * L64];
+  bf16 dWm[2][64 * LDK];
+  bf16 GA[2][64 * L64];                            // G rows, later dA rows
+  bf16 GTA[2][64 * L64];                           // G^T rows, later dA^T rows
+  bf16 dXTm[2][64 * L64];
+};
+
+struct LocalGates {
+  alignas(16) float gam2[64];
+  alignas(16) float eg[64];
+  alignas(16) float egc[64];
+  alignas(16) float bet[64];
+  float egC;
+};
+
+template <int DK, int VB, int NWP>
+struct LocalSmem {
+  union {
+    VLoopSmem<DK, VB, NWP> v;
+    FinSmem<DK> f;
+  } u;
+  LocalGates gs;
+  float colH[4][64];      // column sums of H = G * (Q K^T), by row tile
+  float colHL[4][64];     // column sums of dA-side gate terms, by row tile
+  float colDB[4][64];     // column sums of dT * X (d beta from T = X diag(beta))
+  float rowDG[2][64];     // d gamma row parts, by column half
+  float rowTerm[2][64];   // egc_s k_s . dKs_s (state-update gate term), by half
+  float rowDB[2][64];     // d beta from L, by half
+  float red[8];           // <dS', Sq> per wave
+};
+
+template <int DK, int SF, int WF>
+__global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N) {
+  constexpr int VB = WF == 0 ? 32 : 64;            // value columns per pass
+  constexpr int NWP = WF == 0 ? 2 : 1;             // W planes
+  constexpr int MK = DK / 16, KH = MK / 2;         // k tiles, k tiles per half
+  constexpr int NVT = VB / 16, NKV = VB / 32;      // value tiles, value K steps per pass
+  constexpr int NJ = 4 * NVT / 8;                  // (value tile, token tile) units per wave
+  constexpr int NU = MK * NVT / 8;                 // dS' publishing units per wave
+  using VS = VLoopSmem<DK, VB, NWP>;
+  using FS = FinSmem<DK>;
+  constexpr int LDK = VS::LDK, LVB = VS::LVB;
+  static_assert(sizeof(LocalSmem<DK, VB, NWP>) <= 160 * 1024, "LDS");
+  __shared__ __align__(16) LocalSmem<DK, VB, NWP> sm;
+
+  const FwdKernelArgs& f = a.f;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const int tw = wave & 3, hk = wave >> 2;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  if (!ch.valid) return;
+  const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, nvb = Dv / 64, hq = h / (Hv / Hqk);
+  const int t0 = ch.t0, nc = ch.nc;
+  const float scale = f.scale;
+  const int64_t chb = (int64_t)slot * Hv + h;
+  LocalGates& gs = sm.gs;
+  Sel sel;
+  sel.pair[0] = sel_pair(0, r16, grp);
+  sel.pair[1] = sel_pair(1, r16, grp);
+
+  // ---------------------------------------------------------------- set-up
+  auto& V = sm.u.v;
+  if (wave == 0) {
+    const bool valid = lane < nc;
+    const int64_t gi = (int64_t)(t0 + min(lane, nc - 1)) * Hv + h;
+    const float g2 = wave_incl_scan(valid ? f.g[gi] * LOG2E : 0.f, lane);
+    const float g2n = __shfl(g2, nc - 1, WAVE);
+    gs.gam2[lane] = g2;
+    gs.eg[lane] = fexp2(g2);
+    gs.egc[lane] = valid ? fexp2(g2n - g2) : 0.f;
+    gs.bet[lane] = valid ? f.beta[gi] : 0.f;
+    if (lane == 0) gs.egC = fexp2(g2n);
+  }
+  float dWs = 1.f;                                 // W scale (W QDQ on)
+  if constexpr (WF != 0) {
+    dWs = f.w_scale[chb];
+    for (int e = tid; e < 64 * DK / 16; e += NT) {
+      const int row = e / (DK / 16), c16 = e % (DK / 16);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(
+          f.w_codes + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 16 * c16);
+      bf16x8 o[2];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t word = b[j >> 2] >> (8 * (j & 3));
+        const float cv = WF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0)
+                                 : static_cast<float>(static_cast<int8_t>(word & 0xFFu));
+        o[j >> 3][j & 7] = to_bf16(row < nc ? cv : 0.f);
+      }
+      *reinterpret_cast<bf16x8*>(&V.Wm[0][row * LDK + 16 * c16]) = o[0];
+      *reinterpret_cast<bf16x8*>(&V.Wm[0][row * LDK + 16 * c16 + 8]) = o[1];
+    }
+  } else {
+    for (int e = tid; e < 64 * DK / 4; e += NT) {
+      const int row = e / (DK / 4), c4 = e % (DK / 4);
+      f32x4 w = *reinterpret_cast<const f32x4*>(a.ws_W + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 4 * c4);
+      if (row >= nc) w = zero4();
+      f32x4 hi, lo;
+      split_tile(w, hi, lo);
+      put4(V.Wm[0], row * LDK + 4 * c4, hi);
+      put4(V.Wm[NWP - 1], row * LDK + 4 * c4, lo);
+    }
+  }
+  __syncthreads();                                 // gates visible
+  {
+    // T = X diag(beta), hi + lo
+    const float* Xg = a.ws_X + chb * 4096;
+    for (int e = tid; e < 64 * 16; e += NT) {
+      const int row = e >> 4, c4 = e & 15;
+      f32x4 x = *reinterpret_cast<const f32x4*>(Xg + row * 64 + 4 * c4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&gs.bet[4 * c4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= b[i];
+      f32x4 hi, lo;
+      split_tile(x, hi, lo);
+      put4(V.Tm[0], row * L64 + 4 * c4, hi);
+      put4(V.Tm[1], row * L64 + 4 * c4, lo);
+    }
+  }
+  __syncthreads();
+  // (vt, tt) units of this wave for Vnew and dv; B operands T (over token rows)
+  int jv[NJ], jt[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int idx = wave + 8 * j;
+    jv[j] = idx % NVT;
+    jt[j] = idx / NVT;
+  }
+  // accumulators (row tile tw; k tiles hk*KH.. or token tiles 2hk, 2hk+1)
+  f32x4 dW[KH], dQi[KH], dKs[KH], dP[2], dTU[2];
+#pragma unroll
+  for (int j = 0; j < KH; ++j) dW[j] = dQi[j] = dKs[j] = zero4();
+  dP[0] = dP[1] = dTU[0] = dTU[1] = zero4();
+  float sSq = 0.f;
+
+  const bf16* vg = reinterpret_cast<const bf16*>(f.v);
+  const bf16* dog = reinterpret_cast<const bf16*>(a.dout);
+  // ---------------------------------------------------------------- value passes
+  for (int vb0 = 0; vb0 < Dv; vb0 += VB) {
+    // chain outputs of this pass: dVnew tiles (token tile, value tile) and dS' tiles
+    auto dvn_tile = [&](int tt, int vt) {
+      const int col = vb0 + 16 * vt;
+      return *reinterpret_cast<const f32x4*>(a.ws_dvn + frag_off(chb, nvb, col >> 6, (col & 63) >> 4, 4, tt, lane));
+    };
+    auto ds_tile = [&](int kt, int vt) {
+      const int col = vb0 + 16 * vt;
+      return *reinterpret_cast<const f32x4*>(a.ws_dstate + frag_off(chb, nvb, col >> 6, (col & 63) >> 4, MK, kt, lane));
+    };
+    // staging: V, dO rows, Sq (scaled, hi + lo)
+    for (int e = tid; e < 64 * VB / 8; e += NT) {
+      const int row = e / (VB / 8), c8 = e % (VB / 8);
+      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * Dv + vb0 + 8 * c8;
+      u32x4 x = *reinterpret_cast<const u32x4*>(vg + off);
+      u32x4 y = *reinterpret_cast<const u32x4*>(dog + off);
+      if (row >= nc) x = y = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&V.Vm[row * LVB + 8 * c8]) = x;
+      *reinterpret_cast<u32x4*>(&V.dOm[row * LVB + 8 * c8]) = y;
+    }
+    if constexpr (SF != 0) {
+      for (int e = tid; e < DK * VB / 16; e += NT) {
+        const int row = e / (VB / 16), c16 = e % (VB / 16);
+        const int col = vb0 + 16 * c16;
+        const u32x4 b = *reinterpret_cast<const u32x4*>(f.s_codes + chb * DK * Dv + (int64_t)row * Dv + col);
+        const float sc = f.s_scale[chb * (Dv / f.block_v) + col / f.block_v];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t word = b[q4] >> (8 * i);
+            const float cv = SF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0)
+                                     : static_cast<float>(static_cast<int8_t>(word & 0xFFu));
+            x[i] = cv * sc;
+          }
+          f32x4 hi, lo;
+          split_tile(x, hi, lo);
+          put4(V.Sqm[0], row * LVB + 16 * c16 + 4 * q4, hi);
+          put4(V.Sqm[1], row * LVB + 16 * c16 + 4 * q4, lo);
+        }
+      }
+    } else {
+      for (int e = tid; e < DK * VB / 4; e += NT) {
+        const int row = e / (VB / 4), c4 = e % (VB / 4);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(f.s_f32 + chb * DK * Dv + (int64_t)row * Dv + vb0 + 4 * c4);
+        f32x4 hi, lo;
+        split_tile(x, hi, lo);
+        put4(V.Sqm[0], row * LVB + 4 * c4, hi);
+        put4(V.Sqm[1], row * LVB + 4 * c4, lo);
+      }
+    }
+    __syncthreads();
+
+    // (a) dS' as rows (k-major) hi + lo, and <dS', Sq>
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int idx = wave + 8 * u, kt = idx % MK, vt = idx / MK, p = kt >> 1, odd = kt & 1;
+      f32x4 c0h, c0l, c1h, c1l;
+      split_tile(ds_tile(2 * p, vt), c0h, c0l);
+      split_tile(ds_tile(2 * p + 1, vt), c1h, c1l);
+      const f32x4 th = trans(c0h, c1h, odd, sel), tl = trans(c0l, c1l, odd, sel);
+      const int off = (16 * kt + r16) * LVB + 16 * vt + 4 * grp;
+      put4(V.dSm[0], off, th);
+      put4(V.dSm[1], off, tl);
+      const bf16x4 s0 = *reinterpret_cast<const bf16x4*>(&V.Sqm[0][off]);
+      const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(&V.Sqm[1][off]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sSq += (th[i] + tl[i]) * (from_bf16(s0[i]) + from_bf16(s1[i]));
+    }
+    // (1) Vnew^T tiles -> Vnew rows (hi + lo); (7) dv^T tiles -> dv
+    {
+      const int vt = jv[0];                       // the same value tile for every unit
+      f32x4 acc[NJ], accw[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = accw[j] = zero4();
+      // T V: A = V^T over tokens, B = T^T (rows of T)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 av = colp(V.Vm, LVB, 32 * kk, vt, r16, grp, sel);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[j] = mfma(av, rowp(V.Tm[1], L64, 16 * jt[j], 32 * kk, r16, grp),
+                        mfma(av, rowp(V.Tm[0], L64, 16 * jt[j], 32 * kk, r16, grp), acc[j]));
+      }
+      // W Sq: A = Sq^T over k, B = W^T (rows of W)
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk) {
+        const bf16x8 as0 = colp(V.Sqm[0], LVB, 32 * kk, vt, r16, grp, sel);
+        const bf16x8 as1 = colp(V.Sqm[1], LVB, 32 * kk, vt, r16, grp, sel);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bf16x8 w0 = rowp(V.Wm[0], LDK, 16 * jt[j], 32 * kk, r16, grp);
+          accw[j] = mfma(as1, w0, mfma(as0, w0, accw[j]));
+          if constexpr (NWP == 2)
+            accw[j] = mfma(as0, rowp(V.Wm[1], LDK, 16 * jt[j], 32 * kk, r16, grp), accw[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        f32x4 vn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vn[i] = acc[j][i] - dWs * accw[j][i];
+        f32x4 vh, vl;
+        split_tile(vn, vh, vl);
+        const int off = (16 * jt[j] + r16) * LVB + 16 * vt + 4 * grp;
+        put4(V.Vnm[0], off, vh);
+        put4(V.Vnm[1], off, vl);
+      }
+      // dv^T = dVnew^T T: A over tokens from the dVnew tiles, B = T over its rows
+      f32x4 dv[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) dv[j] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 dh, dl;
+        pack_pair_split(dvn_tile(2 * kk, vt), dvn_tile(2 * kk + 1, vt), dh, dl);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          dv[j] = mm3(dv[j], dh, dl, colp(V.Tm[0], L64, 32 * kk, jt[j], r16, grp, sel),
+                      colp(V.Tm[1], L64, 32 * kk, jt[j], r16, grp, sel));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int t = 16 * jt[j] + r16;
+        if (t < nc) {
+          const int64_t o = ((int64_t)(t0 + t) * Hv + h) * Dv + vb0 + 16 * vt + 4 * grp;
+          if (a.grad_f32) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + o) = dv[j];
+          else *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.dv) + o) =
+                   bf16x4{to_bf16(dv[j][0]), to_bf16(dv[j][1]), to_bf16(dv[j][2]), to_bf16(dv[j][3])};
+        }
+      }
+    }
+    // (4)(5)(6): rows tw; dVnew rows through the matrix core
+    bf16x8 AdV[NKV][2], AdO[NKV];
+    {
+      const int p = tw >> 1, odd = tw & 1;
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        f32x4 th[2], tl[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int vt = 2 * kk + e;
+          f32x4 c0h, c0l, c1h, c1l;
+          split_tile(dvn_tile(2 * p, vt), c0h, c0l);
+          split_tile(dvn_tile(2 * p + 1, vt), c1h, c1l);
+          th[e] = trans(c0h, c1h, odd, sel);
+          tl[e] = trans(c0l, c1l, odd, sel);
+        }
+        AdV[kk][0] = pack_pair(th[0], th[1]);
+        AdV[kk][1] = pack_pair(tl[0], tl[1]);
+        AdO[kk] = rowp(V.dOm, LVB, 16 * tw, 32 * kk, r16, grp);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      const int kt = hk * KH + j;
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        const bf16x8 b0 = rowp(V.Sqm[0], LVB, 16 * kt, 32 * kk, r16, grp);
+        const bf16x8 b1 = rowp(V.Sqm[1], LVB, 16 * kt, 32 * kk, r16, grp);
+        dW[j] = mm3(dW[j], AdV[kk][0], AdV[kk][1], b0, b1);
+        dQi[j] = mfma(AdO[kk], b1, mfma(AdO[kk], b0, dQi[j]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int st = 2 * hk + i;
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk)
+        dTU[i] = mm2(dTU[i], AdV[kk][0], AdV[kk][1], rowp(V.Vm, LVB, 16 * st, 32 * kk, r16, grp));
+    }
+    __syncthreads();                               // Vnew and dS' rows complete
+    // (2) dKs = Vnew dS'^T; (3) dP = dO Vnew^T
+    {
+      bf16x8 AVn[NKV][2];
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) AVn[kk][pl] = rowp(V.Vnm[pl], LVB, 16 * tw, 32 * kk, r16, grp);
+#pragma unroll
+      for (int j = 0; j < KH; ++j) {
+        const int kt = hk * KH + j;
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk)
+          dKs[j] = mm3(dKs[j], AVn[kk][0], AVn[kk][1], rowp(V.dSm[0], LVB, 16 * kt, 32 * kk, r16, grp),
+                       rowp(V.dSm[1], LVB, 16 * kt, 32 * kk, r16, grp));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int st = 2 * hk + i;
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk)
+          dP[i] = mfma(AdO[kk], rowp(V.Vnm[1], LVB, 16 * st, 32 * kk, r16, grp),
+                       mfma(AdO[kk], rowp(V.Vnm[0], LVB, 16 * st, 32 * kk, r16, grp), dP[i]));
+      }
+    }
+    __syncthreads();                               // pass buffers free
+  }
+
+  // ---------------------------------------------------------------- finish
+  auto& F = sm.u.f;
+  constexpr int FLDK = FS::LDK;
+  {
+    const bf16* kg = reinterpret_cast<const bf16*>(f.k);
+    const bf16* qg = reinterpret_cast<const bf16*>(f.q);
+    for (int e = tid; e < 64 * DK / 8; e += NT) {
+      const int row = e / (DK / 8), c8 = e % (DK / 8);
+      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hqk + hq) * DK + 8 * c8;
+      u32x4 kv = *reinterpret_cast<const u32x4*>(kg + off);
+      u32x4 qv = *reinterpret_cast<const u32x4*>(qg + off);
+      if (row >= nc) kv = qv = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&F.Km[row * FLDK + 8 * c8]) = kv;
+      *reinterpret_cast<u32x4*>(&F.QM1m[row * FLDK + 8 * c8]) = qv;
+    }
+    const float* Xg = a.ws_X + chb * 4096;
+    for (int e = tid; e < 64 * 16; e += NT) {
+      const int row = e >> 4, c4 = e & 15;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(Xg + row * 64 + 4 * c4);
+      f32x4 hi, lo;
+      split_tile(x, hi, lo);
+      put4(F.Xm[0], row * L64 + 4 * c4, hi);
+      put4(F.Xm[1], row * L64 + 4 * c4, lo);
+    }
+    // dW = -(accumulated dVnew Sq^T), as rows
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      f32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = -dW[j][i];
+      put_N(F.dWm[0], F.dWm[1], FLDK, w, tw, hk * KH + j, r16, grp, sel);
+    }
+  }
+  __syncthreads();
+
+  float dg_acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float term_acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float db_acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 KKt[2];
+  // FA1: Q K^T, K K^T, dW K^T on tiles (tw, 2hk + i) -> G, H, dT, dX
+  {
+    float colh[2][4], coldb[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int st = 2 * hk + i;
+      f32x4 qk = zero4(), kk2 = zero4(), wk = zero4();
+#pragma unroll
+      for (int kk = 0; kk < DK / 32; ++kk) {
+        const bf16x8 bk = lds_nat(F.Km, 16 * st + r16, FLDK, 32 * kk, grp);
+        qk = mfma(lds_nat(F.QM1m, 16 * tw + r16, FLDK, 32 * kk, grp), bk, qk);
+        kk2 = mfma(lds_nat(F.Km, 16 * tw + r16, FLDK, 32 * kk, grp), bk, kk2);
+        wk = mfma(lds_nat(F.dWm[1], 16 * tw + r16, FLDK, 32 * kk, grp), bk,
+                  mfma(lds_nat(F.dWm[0], 16 * tw + r16, FLDK, 32 * kk, grp), bk, wk));
+      }
+      KKt[i] = kk2;
+      const f32x4 xh = tile_of(F.Xm[0], L64, 16 * tw, st, r16, grp, sel);
+      const f32x4 xl = tile_of(F.Xm[1], L64, 16 * tw, st, r16, grp, sel);
+      const int s = 16 * st + r16;
+      const float gs_s = gs.gam2[s], eg_s = gs.eg[s], bet_s = gs.bet[s];
+      f32x4 G, dX;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * tw + 4 * grp + q;
+        const float gv = t >= s ? scale * dP[i][q] * fexp2(gs.gam2[t] - gs_s) : 0.f;
+        G[q] = gv;
+        const float hv = gv * qk[q];
+        dg_acc[q] += hv;
+        colh[i][q] = hv;
+        const float dt = wk[q] * eg_s + dTU[i][q];
+        coldb[i][q] = dt * (xh[q] + xl[q]);
+        dX[q] = dt * bet_s;
+      }
+      put_T(F.GTA[0], F.GTA[1], L64, G, tw, st, r16, grp);
+      put_N(F.GA[0], F.GA[1], L64, G, tw, st, r16, grp, sel);
+      put_T(F.dXTm[0], F.dXTm[1], L64, dX, tw, st, r16, grp);
+    }
+    // column partial sums of this wave's 16 rows
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float th = colh[i][0] + colh[i][1] + colh[i][2] + colh[i][3];
+      float td = coldb[i][0] + coldb[i][1] + coldb[i][2] + coldb[i][3];
+      th += __shfl_xor(th, 16, WAVE);
+      th += __shfl_xor(th, 32, WAVE);
+      td += __shfl_xor(td, 16, WAVE);
+      td += __shfl_xor(td, 32, WAVE);
+      if (grp == 0) {
+        sm.colH[tw][16 * (2 * hk + i) + r16] = th;
+        sm.colDB[tw][16 * (2 * hk + i) + r16] = td;
+      }
+    }
+  }
+  __syncthreads();
+
+  // FB1: dq = scale e^gamma dQi + G K; dK = G^T Q + egc dKs + beta e^gamma X^T dW
+  bf16x8 CK[2][KH];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int j = 0; j < KH; ++j) CK[kk][j] = colp(F.Km, FLDK, 32 * kk, hk * KH + j, r16, grp, sel);
+  f32x4 dK[KH];
+  {
+    float* dqp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK;
+    bf16x8 AX[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) AX[kk][pl] = colp(F.Xm[pl], L64, 32 * kk, tw, r16, grp, sel);
+    const f32x4 eg4 = *reinterpret_cast<const f32x4*>(&gs.eg[16 * tw + 4 * grp]);
+    const f32x4 egc4 = *reinterpret_cast<const f32x4*>(&gs.egc[16 * tw + 4 * grp]);
+    const f32x4 bet4 = *reinterpret_cast<const f32x4*>(&gs.bet[16 * tw + 4 * grp]);
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      const int kt = hk * KH + j, col = 16 * kt + r16;
+      f32x4 gk = zero4(), gq = zero4(), xw = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        gk = mm2(gk, rowp(F.GA[0], L64, 16 * tw, 32 * kk, r16, grp),
+                 rowp(F.GA[1], L64, 16 * tw, 32 * kk, r16, grp), CK[kk][j]);
+        const bf16x8 cq = colp(F.QM1m, FLDK, 32 * kk, kt, r16, grp, sel);
+        gq = mm2(gq, rowp(F.GTA[0], L64, 16 * tw, 32 * kk, r16, grp),
+                 rowp(F.GTA[1], L64, 16 * tw, 32 * kk, r16, grp), cq);
+        const bf16x8 w0 = colp(F.dWm[0], FLDK, 32 * kk, kt, r16, grp, sel);
+        const bf16x8 w1 = colp(F.dWm[1], FLDK, 32 * kk, kt, r16, grp, sel);
+        xw = mm3(xw, AX[kk][0], AX[kk][1], w0, w1);
+      }
+      const f32x4 qv = tile_of(F.QM1m, FLDK, 16 * tw, kt, r16, grp, sel);
+      const f32x4 kv = tile_of(F.Km, FLDK, 16 * tw, kt, r16, grp, sel);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * tw + 4 * grp + q;
+        const float qi = scale * eg4[q] * dQi[j][q];
+        dg_acc[q] += qi * qv[q];
+        if (t < nc) dqp[(int64_t)t * Hv * 2 * DK + col] = qi + gk[q];
+        const float ks = egc4[q] * dKs[j][q];
+        term_acc[q] += ks * kv[q];
+        const float wv = xw[q] * bet4[q] * eg4[q];
+        dg_acc[q] += wv * kv[q];
+        dK[j][q] = gq[q] + ks + wv;
+      }
+    }
+  }
+  // M1^T = dX^T X on tiles (tw, 2hk + i)
+  f32x4 M1T[2];
+  {
+    bf16x8 AD[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) AD[kk][pl] = rowp(F.dXTm[pl], L64, 16 * tw, 32 * kk, r16, grp);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ut = 2 * hk + i;
+      f32x4 m = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        m = mm3(m, AD[kk][0], AD[kk][1], colp(F.Xm[0], L64, 32 * kk, ut, r16, grp, sel),
+                colp(F.Xm[1], L64, 32 * kk, ut, r16, grp, sel));
+      M1T[i] = m;
+    }
+  }
+  __syncthreads();                                 // Q rows, G, G^T, dX^T no longer read
+  // M1 rows (M1[u][s] = M1^T[s][u]) into the Q space
+  bf16* M1p0 = F.QM1m;
+  bf16* M1p1 = F.QM1m + 64 * L64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) put_T(M1p0, M1p1, L64, M1T[i], tw, 2 * hk + i, r16, grp);
+  __syncthreads();
+  // FA3: dL = -(M1 X^T) below the diagonal; dA = dL beta_t Gam
+  {
+    bf16x8 AM[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) AM[kk][pl] = rowp(pl ? M1p1 : M1p0, L64, 16 * tw, 32 * kk, r16, grp);
+    float colhl[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ut = 2 * hk + i;
+      f32x4 ml = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        ml = mm3(ml, AM[kk][0], AM[kk][1], rowp(F.Xm[0], L64, 16 * ut, 32 * kk, r16, grp),
+                 rowp(F.Xm[1], L64, 16 * ut, 32 * kk, r16, grp));
+      const int u = 16 * ut + r16;
+      const float gu = gs.gam2[u];
+      f32x4 dA;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * tw + 4 * grp + q;
+        const float gam = t > u ? fexp2(gs.gam2[t] - gu) : 0.f;
+        const float dl = -ml[q];
+        const float ag = KKt[i][q] * gam;
+        db_acc[q] += dl * ag;
+        const float hl = gs.bet[t] * dl * ag;
+        dg_acc[q] += hl;
+        colhl[i][q] = hl;
+        dA[q] = dl * gs.bet[t] * gam;
+      }
+      put_N(F.GA[0], F.GA[1], L64, dA, tw, ut, r16, grp, sel);
+      put_T(F.GTA[0], F.GTA[1], L64, dA, tw, ut, r16, grp);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float t = colhl[i][0] + colhl[i][1] + colhl[i][2] + colhl[i][3];
+      t += __shfl_xor(t, 16, WAVE);
+      t += __shfl_xor(t, 32, WAVE);
+      if (grp == 0) sm.colHL[tw][16 * (2 * hk + i) + r16] = t;
+    }
+  }
+  __syncthreads();
+  // FB2: dK += (dA + dA^T) K; dk partial out
+  {
+    bf16x8 AA[2][2], AAT[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        AA[kk][pl] = rowp(F.GA[pl], L64, 16 * tw, 32 * kk, r16, grp);
+        AAT[kk][pl] = rowp(F.GTA[pl], L64, 16 * tw, 32 * kk, r16, grp);
+      }
+    float* dkp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK + DK;
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      f32x4 acc = dK[j];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        acc = mm2(acc, AA[kk][0], AA[kk][1], CK[kk][j]);
+        acc = mm2(acc, AAT[kk][0], AAT[kk][1], CK[kk][j]);
+      }
+      const int col = 16 * (hk * KH + j) + r16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * tw + 4 * grp + q;
+        if (t < nc) dkp[(int64_t)t * Hv * 2 * DK + col] = acc[q];
+      }
+    }
+  }
+  // row totals over the 16 lanes of each row (this wave's column half)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v3[3] = {dg_acc[q], term_acc[q], db_acc[q]};
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      float x = v3[t];
+      x += __shfl_xor(x, 8, WAVE);
+      x += __shfl_xor(x, 4, WAVE);
+      x += __shfl_xor(x, 2, WAVE);
+      x += __shfl_xor(x, 1, WAVE);
+      v3[t] = x;
+    }
+    if (r16 == 0) {
+      const int row = 16 * tw + 4 * grp + q;
+      sm.rowDG[hk][row] = v3[0];
+      sm.rowTerm[hk][row] = v3[1];
+      sm.rowDB[hk][row] = v3[2];
+    }
+  }
+  sSq = wave_sum(sSq);
+  if (lane == 0) sm.red[wave] = sSq;
+  __syncthreads();
+  // d gamma_j = row part - column parts - state term_j; the last row also gets
+  // e^gamma_n <dS', Sq> + sum_j term_j; dg = suffix sum of d gamma
+  if (wave == 0) {
+    const int j = lane;
+    const float term = sm.rowTerm[0][j] + sm.rowTerm[1][j];
+    const float term_total = wave_sum(term);
+    float sq_total = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sq_total += sm.red[w];
+    float dgj = sm.rowDG[0][j] + sm.rowDG[1][j] - term -
+                (sm.colH[0][j] + sm.colH[1][j] + sm.colH[2][j] + sm.colH[3][j]) -
+                (sm.colHL[0][j] + sm.colHL[1][j] + sm.colHL[2][j] + sm.colHL[3][j]);
+    if (j == nc - 1) dgj += gs.egC * sq_total + term_total;
+    if (j >= nc) dgj = 0.f;
+    float suf = dgj;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(suf, off, WAVE);
+      if (j + off < 64) suf += y;
+    }
+    const float db = sm.colDB[0][j] + sm.colDB[1][j] + sm.colDB[2][j] + sm.colDB[3][j] +
+                     sm.rowDB[0][j] + sm.rowDB[1][j];
+    if (j < nc) {
+      const int64_t gi = (int64_t)(t0 + j) * Hv + h;
+      a.dg[gi] = suf;
+      a.dbeta[gi] = db;
+    }
+  }
+}
+
+template <int DK>
+static hipError_t launch_local_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  const dim3 grid(a.num_slots, c.Hv);
+#define GDN_CASE(SFv, WFv) \
+  if (c.state_fmt == SFv && c.w_fmt == WFv) { \
+    hipLaunchKernelGGL((bwd_local_kernel<DK, SFv, WFv>), grid, dim3(NT), 0, s, a, c.N); \
+    return hipGetLastError(); \
+  }
+  GDN_CASE(0, 0) GDN_CASE(0, 1) GDN_CASE(0, 2)
+  GDN_CASE(1, 0) GDN_CASE(1, 1) GDN_CASE(1, 2)
+  GDN_CASE(2, 0) GDN_CASE(2, 1) GDN_CASE(2, 2)
+#undef GDN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_local(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  if (c.Dk == 128) return launch_local_dk<128>(c, a, s);
+  if (c.Dk == 64) return launch_local_dk<64>(c, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -75,6 +75,8 @@ hipError_t launch_bwd(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t 
 // bf16 io: operand images of the reverse recurrence, then the recurrence.
 hipError_t launch_bwd_img(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
 hipError_t launch_bwd_state(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+// bf16 io: the chunk-local gradients on bf16 MFMA.
+hipError_t launch_bwd_local(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
 // Elements of the backward image block of one (slot, head).
 int bwd_img_elems(int Dk, int w_fmt);
 
