@@ -57,8 +57,18 @@ __device__ __forceinline__ bf16x8 sel_pair(int h, int r16, int grp) {
   return r;
 }
 
+// Two named operands, not an array: a runtime index into an array of them
+// would place it in private memory. q is the K = 16 selection (lane holds
+// B[4 grp + e][r16] = 1 exactly when 4 grp + e = r16) of v_mfma_f32_16x16x16_bf16.
 struct Sel {
-  bf16x8 pair[2];
+  bf16x8 p0, p1;
+  bf16x4 q;
+  __device__ __forceinline__ bf16x8 get(int h) const {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = h ? p1[e] : p0[e];
+    return r;
+  }
 };
 
 // Accumulator tile (rows row0..row0+15, columns 16 ct..16 ct+15) of a
@@ -66,7 +76,7 @@ struct Sel {
 // paired selection).
 __device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct, int r16, int grp,
                                          const Sel& s) {
-  return mfma(lds_pair(m, row0 + r16, ld, 32 * (ct >> 1), grp), s.pair[ct & 1], zero4());
+  return mfma(lds_pair(m, row0 + r16, ld, 32 * (ct >> 1), grp), s.get(ct & 1), zero4());
 }
 // Operand contracting over rows r0..r0+31 (paired order), free index = columns
 // 16 ct..16 ct+15.
@@ -80,12 +90,16 @@ __device__ __forceinline__ bf16x8 rowp(const bf16* m, int ld, int row0, int k0, 
   return lds_pair(m, row0 + r16, ld, k0, grp);
 }
 
-// Transpose of accumulator tiles through the matrix core. c0, c1 are the tiles
-// of rows 32p..32p+15 and 32p+16..32p+31 (same 16 columns) of M, already
-// exact in bf16; the result is the accumulator tile of M^T for rows 32p + 16h
-// ..+15 of M: lane holds M[32p + 16h + r16][col0 + 4 grp + i].
-__device__ __forceinline__ f32x4 trans(const f32x4& c0, const f32x4& c1, int h, const Sel& s) {
-  return mfma(pack_pair(c0, c1), s.pair[h], zero4());
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// v_mfma_f32_16x16x16_bf16: lane holds A[r16][4 grp + e] and B[4 grp + e][r16].
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                   c, 0, 0, 0);
+}
+// Transpose of one accumulator tile (values exact in bf16): the lane that held
+// M[row0 + 4 grp + i][col0 + r16] gets M[row0 + r16][col0 + 4 grp + i].
+__device__ __forceinline__ f32x4 trans1(const f32x4& c, const Sel& s) {
+  return mfma16(bf16x4{to_bf16(c[0]), to_bf16(c[1]), to_bf16(c[2]), to_bf16(c[3])}, s.q, zero4());
 }
 
 // Splits an FP32 tile into exact bf16 hi and lo parts (as FP32 values).
@@ -118,13 +132,9 @@ __device__ __forceinline__ void put_N(bf16* p0, bf16* p1, int ld, const f32x4& c
                                       int r16, int grp, const Sel& s) {
   f32x4 h, l;
   split_tile(c, h, l);
-  const f32x4 z = zero4();
-  const int odd = rt & 1;
-  const f32x4 th = trans(odd ? z : h, odd ? h : z, odd, s);
-  const f32x4 tl = trans(odd ? z : l, odd ? l : z, odd, s);
   const int off = (16 * rt + r16) * ld + 16 * ct + 4 * grp;
-  put4(p0, off, th);
-  put4(p1, off, tl);
+  put4(p0, off, trans1(h, s));
+  put4(p1, off, trans1(l, s));
 }
 
 __device__ __forceinline__ f32x4 mm2(f32x4 acc, bf16x8 a0, bf16x8 a1, bf16x8 b) {
@@ -184,6 +194,20 @@ struct LocalSmem {
   float red[8];           // <dS', Sq> per wave
 };
 
+// Global loads of one value pass, issued one pass ahead into registers: V and
+// dO rows (bf16), Sq (codes with their scale, or FP32) and this wave's dS'
+// tiles (the first ones used).
+template <int DK, int VB, int SF>
+struct PassLoads {
+  static constexpr int NVP = (64 * VB / 8 + NT - 1) / NT;
+  static constexpr int SPC = SF != 0 ? DK * VB / 16 : DK * VB / 4;
+  static constexpr int NSP = (SPC + NT - 1) / NT;
+  static constexpr int NU = (DK / 16) * (VB / 16) / 8;
+  u32x4 v[NVP], o[NVP], s[NSP];
+  float sc[NSP];
+  f32x4 ds[NU];
+};
+
 template <int DK, int SF, int WF>
 __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N) {
   constexpr int VB = WF == 0 ? 32 : 64;            // value columns per pass
@@ -194,13 +218,18 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   constexpr int NU = MK * NVT / 8;                 // dS' publishing units per wave
   using VS = VLoopSmem<DK, VB, NWP>;
   using FS = FinSmem<DK>;
+  using PL = PassLoads<DK, VB, SF>;
   constexpr int LDK = VS::LDK, LVB = VS::LVB;
   static_assert(sizeof(LocalSmem<DK, VB, NWP>) <= 160 * 1024, "LDS");
   __shared__ __align__(16) LocalSmem<DK, VB, NWP> sm;
 
   const FwdKernelArgs& f = a.f;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
-  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int lane = fresh_lane(), tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  // per-lane addresses are rebuilt in each phase instead of being kept live
+  // across the passes (fresh_lane in gdn_device.h)
+#define GDN_REFRESH() \
+  lane = fresh_lane(); tid = wave * 64 + lane; r16 = lane & 15; grp = lane >> 4
   const int tw = wave & 3, hk = wave >> 2;
   const int slot = blockIdx.x, h = blockIdx.y;
   const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
@@ -211,11 +240,130 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   const int64_t chb = (int64_t)slot * Hv + h;
   LocalGates& gs = sm.gs;
   Sel sel;
-  sel.pair[0] = sel_pair(0, r16, grp);
-  sel.pair[1] = sel_pair(1, r16, grp);
+  sel.p0 = sel_pair(0, r16, grp);
+  sel.p1 = sel_pair(1, r16, grp);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sel.q[e] = to_bf16(4 * grp + e == r16 ? 1.f : 0.f);
+  // (vt, tt) units of this wave for Vnew and dv
+  int jv[NJ], jt[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int idx = wave + 8 * j;
+    jv[j] = idx % NVT;
+    jt[j] = idx / NVT;
+  }
+
+  const bf16* vg = reinterpret_cast<const bf16*>(f.v);
+  const bf16* dog = reinterpret_cast<const bf16*>(a.dout);
+  auto dvn_tile = [&](int vb0, int tt, int vt) {
+    const int col = vb0 + 16 * vt;
+    return *reinterpret_cast<const f32x4*>(a.ws_dvn + frag_off(chb, nvb, col >> 6, (col & 63) >> 4, 4, tt, lane));
+  };
+  auto ds_tile = [&](int vb0, int kt, int vt) {
+    const int col = vb0 + 16 * vt;
+    return *reinterpret_cast<const f32x4*>(a.ws_dstate + frag_off(chb, nvb, col >> 6, (col & 63) >> 4, MK, kt, lane));
+  };
+  auto load_pass = [&](int vb0, PL& L) {
+#pragma unroll
+    for (int p = 0; p < PL::NVP; ++p) {
+      const int e = min(tid + NT * p, 64 * VB / 8 - 1), row = e / (VB / 8), c8 = e % (VB / 8);
+      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * Dv + vb0 + 8 * c8;
+      L.v[p] = *reinterpret_cast<const u32x4*>(vg + off);
+      L.o[p] = *reinterpret_cast<const u32x4*>(dog + off);
+    }
+#pragma unroll
+    for (int p = 0; p < PL::NSP; ++p) {
+      const int e = min(tid + NT * p, PL::SPC - 1);
+      if constexpr (SF != 0) {
+        const int row = e / (VB / 16), col = vb0 + 16 * (e % (VB / 16));
+        L.s[p] = *reinterpret_cast<const u32x4*>(f.s_codes + chb * DK * Dv + (int64_t)row * Dv + col);
+        L.sc[p] = f.s_scale[chb * (Dv / f.block_v) + col / f.block_v];
+      } else {
+        const int row = e / (VB / 4), col = vb0 + 4 * (e % (VB / 4));
+        L.s[p] = *reinterpret_cast<const u32x4*>(f.s_f32 + chb * DK * Dv + (int64_t)row * Dv + col);
+        L.sc[p] = 1.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int idx = wave + 8 * u;
+      L.ds[u] = ds_tile(vb0, idx % MK, idx / MK);
+    }
+  };
+  auto& V = sm.u.v;
+  auto store_pass = [&](const PL& L) {
+#pragma unroll
+    for (int p = 0; p < PL::NVP; ++p) {
+      const int e = tid + NT * p;
+      if (e < 64 * VB / 8) {
+        const int row = e / (VB / 8), c8 = e % (VB / 8);
+        const bool z = row >= nc;
+        *reinterpret_cast<u32x4*>(&V.Vm[row * LVB + 8 * c8]) = z ? u32x4{0u, 0u, 0u, 0u} : L.v[p];
+        *reinterpret_cast<u32x4*>(&V.dOm[row * LVB + 8 * c8]) = z ? u32x4{0u, 0u, 0u, 0u} : L.o[p];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PL::NSP; ++p) {
+      const int e = tid + NT * p;
+      if (e >= PL::SPC) continue;
+      if constexpr (SF != 0) {
+        const int row = e / (VB / 16), c16 = e % (VB / 16);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t word = L.s[p][q4] >> (8 * i);
+            const float cv = SF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0)
+                                     : static_cast<float>(static_cast<int8_t>(word & 0xFFu));
+            x[i] = cv * L.sc[p];
+          }
+          f32x4 hi, lo;
+          split_tile(x, hi, lo);
+          put4(V.Sqm[0], row * LVB + 16 * c16 + 4 * q4, hi);
+          put4(V.Sqm[1], row * LVB + 16 * c16 + 4 * q4, lo);
+        }
+      } else {
+        const int row = e / (VB / 4), c4 = e % (VB / 4);
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(L.s[p][i]);
+        f32x4 hi, lo;
+        split_tile(x, hi, lo);
+        put4(V.Sqm[0], row * LVB + 4 * c4, hi);
+        put4(V.Sqm[1], row * LVB + 4 * c4, lo);
+      }
+    }
+  };
 
   // ---------------------------------------------------------------- set-up
-  auto& V = sm.u.v;
+  // global loads: W, X and the first pass, all in flight together
+  constexpr int WPC = WF != 0 ? 64 * DK / 16 : 64 * DK / 4, NWL = (WPC + NT - 1) / NT;
+  u32x4 wl[NWL];
+#pragma unroll
+  for (int p = 0; p < NWL; ++p) {
+    const int e = min(tid + NT * p, WPC - 1);
+    if constexpr (WF != 0) {
+      const int row = e / (DK / 16), c16 = e % (DK / 16);
+      wl[p] = *reinterpret_cast<const u32x4*>(f.w_codes + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 16 * c16);
+    } else {
+      const int row = e / (DK / 4), c4 = e % (DK / 4);
+      wl[p] = *reinterpret_cast<const u32x4*>(a.ws_W + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 4 * c4);
+    }
+  }
+  constexpr int NXL = 64 * 16 / NT;
+  f32x4 xl[NXL];
+  {
+    const float* Xg = a.ws_X + chb * 4096;
+#pragma unroll
+    for (int p = 0; p < NXL; ++p) {
+      const int e = tid + NT * p;
+      xl[p] = *reinterpret_cast<const f32x4*>(Xg + (e >> 4) * 64 + 4 * (e & 15));
+    }
+  }
+  PL L;
+  load_pass(0, L);
+  const float dWs = WF != 0 ? f.w_scale[chb] : 1.f;   // W scale (W QDQ on)
   if (wave == 0) {
     const bool valid = lane < nc;
     const int64_t gi = (int64_t)(t0 + min(lane, nc - 1)) * Hv + h;
@@ -227,132 +375,74 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     gs.bet[lane] = valid ? f.beta[gi] : 0.f;
     if (lane == 0) gs.egC = fexp2(g2n);
   }
-  float dWs = 1.f;                                 // W scale (W QDQ on)
-  if constexpr (WF != 0) {
-    dWs = f.w_scale[chb];
-    for (int e = tid; e < 64 * DK / 16; e += NT) {
+#pragma unroll
+  for (int p = 0; p < NWL; ++p) {
+    const int e = tid + NT * p;
+    if (e >= WPC) continue;
+    if constexpr (WF != 0) {
       const int row = e / (DK / 16), c16 = e % (DK / 16);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(
-          f.w_codes + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 16 * c16);
       bf16x8 o[2];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const uint32_t word = b[j >> 2] >> (8 * (j & 3));
+        const uint32_t word = wl[p][j >> 2] >> (8 * (j & 3));
         const float cv = WF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0)
                                  : static_cast<float>(static_cast<int8_t>(word & 0xFFu));
         o[j >> 3][j & 7] = to_bf16(row < nc ? cv : 0.f);
       }
       *reinterpret_cast<bf16x8*>(&V.Wm[0][row * LDK + 16 * c16]) = o[0];
       *reinterpret_cast<bf16x8*>(&V.Wm[0][row * LDK + 16 * c16 + 8]) = o[1];
-    }
-  } else {
-    for (int e = tid; e < 64 * DK / 4; e += NT) {
+    } else {
       const int row = e / (DK / 4), c4 = e % (DK / 4);
-      f32x4 w = *reinterpret_cast<const f32x4*>(a.ws_W + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 4 * c4);
-      if (row >= nc) w = zero4();
+      f32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = row < nc ? __uint_as_float(wl[p][i]) : 0.f;
       f32x4 hi, lo;
       split_tile(w, hi, lo);
       put4(V.Wm[0], row * LDK + 4 * c4, hi);
       put4(V.Wm[NWP - 1], row * LDK + 4 * c4, lo);
     }
   }
+  store_pass(L);
   __syncthreads();                                 // gates visible
-  {
-    // T = X diag(beta), hi + lo
-    const float* Xg = a.ws_X + chb * 4096;
-    for (int e = tid; e < 64 * 16; e += NT) {
-      const int row = e >> 4, c4 = e & 15;
-      f32x4 x = *reinterpret_cast<const f32x4*>(Xg + row * 64 + 4 * c4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(&gs.bet[4 * c4]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] *= b[i];
-      f32x4 hi, lo;
-      split_tile(x, hi, lo);
-      put4(V.Tm[0], row * L64 + 4 * c4, hi);
-      put4(V.Tm[1], row * L64 + 4 * c4, lo);
-    }
+  for (int p = 0; p < NXL; ++p) {
+    // T = X diag(beta), hi + lo
+    const int e = tid + NT * p, row = e >> 4, c4 = e & 15;
+    const f32x4 b = *reinterpret_cast<const f32x4*>(&gs.bet[4 * c4]);
+    f32x4 x = xl[p];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] *= b[i];
+    f32x4 hi, lo;
+    split_tile(x, hi, lo);
+    put4(V.Tm[0], row * L64 + 4 * c4, hi);
+    put4(V.Tm[1], row * L64 + 4 * c4, lo);
   }
   __syncthreads();
-  // (vt, tt) units of this wave for Vnew and dv; B operands T (over token rows)
-  int jv[NJ], jt[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int idx = wave + 8 * j;
-    jv[j] = idx % NVT;
-    jt[j] = idx / NVT;
-  }
+
   // accumulators (row tile tw; k tiles hk*KH.. or token tiles 2hk, 2hk+1)
   f32x4 dW[KH], dQi[KH], dKs[KH], dP[2], dTU[2];
 #pragma unroll
   for (int j = 0; j < KH; ++j) dW[j] = dQi[j] = dKs[j] = zero4();
   dP[0] = dP[1] = dTU[0] = dTU[1] = zero4();
   float sSq = 0.f;
+  // finish inputs, loaded during the last pass
+  constexpr int NKL = (64 * DK / 8 + NT - 1) / NT;
+  u32x4 kl[NKL], ql[NKL];
 
-  const bf16* vg = reinterpret_cast<const bf16*>(f.v);
-  const bf16* dog = reinterpret_cast<const bf16*>(a.dout);
   // ---------------------------------------------------------------- value passes
   for (int vb0 = 0; vb0 < Dv; vb0 += VB) {
-    // chain outputs of this pass: dVnew tiles (token tile, value tile) and dS' tiles
-    auto dvn_tile = [&](int tt, int vt) {
-      const int col = vb0 + 16 * vt;
-      return *reinterpret_cast<const f32x4*>(a.ws_dvn + frag_off(chb, nvb, col >> 6, (col & 63) >> 4, 4, tt, lane));
-    };
-    auto ds_tile = [&](int kt, int vt) {
-      const int col = vb0 + 16 * vt;
-      return *reinterpret_cast<const f32x4*>(a.ws_dstate + frag_off(chb, nvb, col >> 6, (col & 63) >> 4, MK, kt, lane));
-    };
-    // staging: V, dO rows, Sq (scaled, hi + lo)
-    for (int e = tid; e < 64 * VB / 8; e += NT) {
-      const int row = e / (VB / 8), c8 = e % (VB / 8);
-      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * Dv + vb0 + 8 * c8;
-      u32x4 x = *reinterpret_cast<const u32x4*>(vg + off);
-      u32x4 y = *reinterpret_cast<const u32x4*>(dog + off);
-      if (row >= nc) x = y = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&V.Vm[row * LVB + 8 * c8]) = x;
-      *reinterpret_cast<u32x4*>(&V.dOm[row * LVB + 8 * c8]) = y;
-    }
-    if constexpr (SF != 0) {
-      for (int e = tid; e < DK * VB / 16; e += NT) {
-        const int row = e / (VB / 16), c16 = e % (VB / 16);
-        const int col = vb0 + 16 * c16;
-        const u32x4 b = *reinterpret_cast<const u32x4*>(f.s_codes + chb * DK * Dv + (int64_t)row * Dv + col);
-        const float sc = f.s_scale[chb * (Dv / f.block_v) + col / f.block_v];
+    GDN_REFRESH();
+    // this pass's dVnew tiles (tw, every value tile)
+    f32x4 dvp[NVT], dvv[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4 x;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t word = b[q4] >> (8 * i);
-            const float cv = SF == 1 ? __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), 0)
-                                     : static_cast<float>(static_cast<int8_t>(word & 0xFFu));
-            x[i] = cv * sc;
-          }
-          f32x4 hi, lo;
-          split_tile(x, hi, lo);
-          put4(V.Sqm[0], row * LVB + 16 * c16 + 4 * q4, hi);
-          put4(V.Sqm[1], row * LVB + 16 * c16 + 4 * q4, lo);
-        }
-      }
-    } else {
-      for (int e = tid; e < DK * VB / 4; e += NT) {
-        const int row = e / (VB / 4), c4 = e % (VB / 4);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(f.s_f32 + chb * DK * Dv + (int64_t)row * Dv + vb0 + 4 * c4);
-        f32x4 hi, lo;
-        split_tile(x, hi, lo);
-        put4(V.Sqm[0], row * LVB + 4 * c4, hi);
-        put4(V.Sqm[1], row * LVB + 4 * c4, lo);
-      }
-    }
-    __syncthreads();
-
+    for (int vt = 0; vt < NVT; ++vt) dvp[vt] = dvn_tile(vb0, tw, vt);
     // (a) dS' as rows (k-major) hi + lo, and <dS', Sq>
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int idx = wave + 8 * u, kt = idx % MK, vt = idx / MK, p = kt >> 1, odd = kt & 1;
-      f32x4 c0h, c0l, c1h, c1l;
-      split_tile(ds_tile(2 * p, vt), c0h, c0l);
-      split_tile(ds_tile(2 * p + 1, vt), c1h, c1l);
-      const f32x4 th = trans(c0h, c1h, odd, sel), tl = trans(c0l, c1l, odd, sel);
+      const int idx = wave + 8 * u, kt = idx % MK, vt = idx / MK;
+      f32x4 ch_, cl_;
+      split_tile(L.ds[u], ch_, cl_);
+      const f32x4 th = trans1(ch_, sel), tl = trans1(cl_, sel);
       const int off = (16 * kt + r16) * LVB + 16 * vt + 4 * grp;
       put4(V.dSm[0], off, th);
       put4(V.dSm[1], off, tl);
@@ -360,6 +450,46 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(&V.Sqm[1][off]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sSq += (th[i] + tl[i]) * (from_bf16(s0[i]) + from_bf16(s1[i]));
+    }
+    // (every token tile, jv) dVnew tiles for dv, in flight during (4)(5)(6)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) dvv[tt] = dvn_tile(vb0, tt, jv[0]);
+    // (4)(5)(6): rows tw; dVnew rows through the matrix core
+    bf16x8 AdV[NKV][2], AdO[NKV];
+    {
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        f32x4 th[2], tl[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          f32x4 ch_, cl_;
+          split_tile(dvp[2 * kk + e], ch_, cl_);
+          th[e] = trans1(ch_, sel);
+          tl[e] = trans1(cl_, sel);
+        }
+        AdV[kk][0] = pack_pair(th[0], th[1]);
+        AdV[kk][1] = pack_pair(tl[0], tl[1]);
+        AdO[kk] = rowp(V.dOm, LVB, 16 * tw, 32 * kk, r16, grp);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KH; ++j) {
+      const int kt = hk * KH + j;
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk) {
+        const bf16x8 b0 = rowp(V.Sqm[0], LVB, 16 * kt, 32 * kk, r16, grp);
+        const bf16x8 b1 = rowp(V.Sqm[1], LVB, 16 * kt, 32 * kk, r16, grp);
+        dW[j] = mm3(dW[j], AdV[kk][0], AdV[kk][1], b0, b1);
+        dQi[j] = mfma(AdO[kk], b1, mfma(AdO[kk], b0, dQi[j]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int st = 2 * hk + i;
+#pragma unroll
+      for (int kk = 0; kk < NKV; ++kk)
+        dTU[i] = mm2(dTU[i], AdV[kk][0], AdV[kk][1], rowp(V.Vm, LVB, 16 * st, 32 * kk, r16, grp));
     }
     // (1) Vnew^T tiles -> Vnew rows (hi + lo); (7) dv^T tiles -> dv
     {
@@ -407,7 +537,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 dh, dl;
-        pack_pair_split(dvn_tile(2 * kk, vt), dvn_tile(2 * kk + 1, vt), dh, dl);
+        pack_pair_split(dvv[2 * kk], dvv[2 * kk + 1], dh, dl);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           dv[j] = mm3(dv[j], dh, dl, colp(V.Tm[0], L64, 32 * kk, jt[j], r16, grp, sel),
@@ -424,46 +554,30 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         }
       }
     }
-    // (4)(5)(6): rows tw; dVnew rows through the matrix core
-    bf16x8 AdV[NKV][2], AdO[NKV];
-    {
-      const int p = tw >> 1, odd = tw & 1;
-#pragma unroll
-      for (int kk = 0; kk < NKV; ++kk) {
-        f32x4 th[2], tl[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int vt = 2 * kk + e;
-          f32x4 c0h, c0l, c1h, c1l;
-          split_tile(dvn_tile(2 * p, vt), c0h, c0l);
-          split_tile(dvn_tile(2 * p + 1, vt), c1h, c1l);
-          th[e] = trans(c0h, c1h, odd, sel);
-          tl[e] = trans(c0l, c1l, odd, sel);
-        }
-        AdV[kk][0] = pack_pair(th[0], th[1]);
-        AdV[kk][1] = pack_pair(tl[0], tl[1]);
-        AdO[kk] = rowp(V.dOm, LVB, 16 * tw, 32 * kk, r16, grp);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < KH; ++j) {
-      const int kt = hk * KH + j;
-#pragma unroll
-      for (int kk = 0; kk < NKV; ++kk) {
-        const bf16x8 b0 = rowp(V.Sqm[0], LVB, 16 * kt, 32 * kk, r16, grp);
-        const bf16x8 b1 = rowp(V.Sqm[1], LVB, 16 * kt, 32 * kk, r16, grp);
-        dW[j] = mm3(dW[j], AdV[kk][0], AdV[kk][1], b0, b1);
-        dQi[j] = mfma(AdO[kk], b1, mfma(AdO[kk], b0, dQi[j]));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int st = 2 * hk + i;
-#pragma unroll
-      for (int kk = 0; kk < NKV; ++kk)
-        dTU[i] = mm2(dTU[i], AdV[kk][0], AdV[kk][1], rowp(V.Vm, LVB, 16 * st, 32 * kk, r16, grp));
-    }
     __syncthreads();                               // Vnew and dS' rows complete
+    GDN_REFRESH();
+    // the next pass's loads (or the finish's), in flight during (2)(3)
+    asm volatile("" ::: "memory");
+    const bool last = vb0 + VB >= Dv;
+    if (!last) {
+      load_pass(vb0 + VB, L);
+    } else {
+      const bf16* kg = reinterpret_cast<const bf16*>(f.k);
+      const bf16* qg = reinterpret_cast<const bf16*>(f.q);
+#pragma unroll
+      for (int p = 0; p < NKL; ++p) {
+        const int e = min(tid + NT * p, 64 * DK / 8 - 1), row = e / (DK / 8), c8 = e % (DK / 8);
+        const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hqk + hq) * DK + 8 * c8;
+        kl[p] = *reinterpret_cast<const u32x4*>(kg + off);
+        ql[p] = *reinterpret_cast<const u32x4*>(qg + off);
+      }
+      const float* Xg = a.ws_X + chb * 4096;
+#pragma unroll
+      for (int p = 0; p < NXL; ++p) {
+        const int e = tid + NT * p;
+        xl[p] = *reinterpret_cast<const f32x4*>(Xg + (e >> 4) * 64 + 4 * (e & 15));
+      }
+    }
     // (2) dKs = Vnew dS'^T; (3) dP = dO Vnew^T
     {
       bf16x8 AVn[NKV][2];
@@ -489,29 +603,32 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       }
     }
     __syncthreads();                               // pass buffers free
+    GDN_REFRESH();
+    if (!last) {
+      store_pass(L);
+      __syncthreads();
+    }
   }
 
   // ---------------------------------------------------------------- finish
   auto& F = sm.u.f;
   constexpr int FLDK = FS::LDK;
+  GDN_REFRESH();
   {
-    const bf16* kg = reinterpret_cast<const bf16*>(f.k);
-    const bf16* qg = reinterpret_cast<const bf16*>(f.q);
-    for (int e = tid; e < 64 * DK / 8; e += NT) {
+#pragma unroll
+    for (int p = 0; p < NKL; ++p) {
+      const int e = tid + NT * p;
+      if (e >= 64 * DK / 8) continue;
       const int row = e / (DK / 8), c8 = e % (DK / 8);
-      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hqk + hq) * DK + 8 * c8;
-      u32x4 kv = *reinterpret_cast<const u32x4*>(kg + off);
-      u32x4 qv = *reinterpret_cast<const u32x4*>(qg + off);
-      if (row >= nc) kv = qv = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&F.Km[row * FLDK + 8 * c8]) = kv;
-      *reinterpret_cast<u32x4*>(&F.QM1m[row * FLDK + 8 * c8]) = qv;
+      const bool z = row >= nc;
+      *reinterpret_cast<u32x4*>(&F.Km[row * FLDK + 8 * c8]) = z ? u32x4{0u, 0u, 0u, 0u} : kl[p];
+      *reinterpret_cast<u32x4*>(&F.QM1m[row * FLDK + 8 * c8]) = z ? u32x4{0u, 0u, 0u, 0u} : ql[p];
     }
-    const float* Xg = a.ws_X + chb * 4096;
-    for (int e = tid; e < 64 * 16; e += NT) {
-      const int row = e >> 4, c4 = e & 15;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(Xg + row * 64 + 4 * c4);
+#pragma unroll
+    for (int p = 0; p < NXL; ++p) {
+      const int e = tid + NT * p, row = e >> 4, c4 = e & 15;
       f32x4 hi, lo;
-      split_tile(x, hi, lo);
+      split_tile(xl[p], hi, lo);
       put4(F.Xm[0], row * L64 + 4 * c4, hi);
       put4(F.Xm[1], row * L64 + 4 * c4, lo);
     }
@@ -525,6 +642,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     }
   }
   __syncthreads();
+  GDN_REFRESH();
 
   float dg_acc[4] = {0.f, 0.f, 0.f, 0.f};
   float term_acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -583,13 +701,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     }
   }
   __syncthreads();
+  GDN_REFRESH();
 
   // FB1: dq = scale e^gamma dQi + G K; dK = G^T Q + egc dKs + beta e^gamma X^T dW
-  bf16x8 CK[2][KH];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int j = 0; j < KH; ++j) CK[kk][j] = colp(F.Km, FLDK, 32 * kk, hk * KH + j, r16, grp, sel);
   f32x4 dK[KH];
   {
     float* dqp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK;
@@ -608,7 +722,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         gk = mm2(gk, rowp(F.GA[0], L64, 16 * tw, 32 * kk, r16, grp),
-                 rowp(F.GA[1], L64, 16 * tw, 32 * kk, r16, grp), CK[kk][j]);
+                 rowp(F.GA[1], L64, 16 * tw, 32 * kk, r16, grp), colp(F.Km, FLDK, 32 * kk, kt, r16, grp, sel));
         const bf16x8 cq = colp(F.QM1m, FLDK, 32 * kk, kt, r16, grp, sel);
         gq = mm2(gq, rowp(F.GTA[0], L64, 16 * tw, 32 * kk, r16, grp),
                  rowp(F.GTA[1], L64, 16 * tw, 32 * kk, r16, grp), cq);
@@ -652,12 +766,14 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     }
   }
   __syncthreads();                                 // Q rows, G, G^T, dX^T no longer read
+  GDN_REFRESH();
   // M1 rows (M1[u][s] = M1^T[s][u]) into the Q space
   bf16* M1p0 = F.QM1m;
   bf16* M1p1 = F.QM1m + 64 * L64;
 #pragma unroll
   for (int i = 0; i < 2; ++i) put_T(M1p0, M1p1, L64, M1T[i], tw, 2 * hk + i, r16, grp);
   __syncthreads();
+  GDN_REFRESH();
   // FA3: dL = -(M1 X^T) below the diagonal; dA = dL beta_t Gam
   {
     bf16x8 AM[2][2];
@@ -701,6 +817,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     }
   }
   __syncthreads();
+  GDN_REFRESH();
   // FB2: dK += (dA + dA^T) K; dk partial out
   {
     bf16x8 AA[2][2], AAT[2][2];
@@ -717,8 +834,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       f32x4 acc = dK[j];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        acc = mm2(acc, AA[kk][0], AA[kk][1], CK[kk][j]);
-        acc = mm2(acc, AAT[kk][0], AAT[kk][1], CK[kk][j]);
+        const bf16x8 ck = colp(F.Km, FLDK, 32 * kk, hk * KH + j, r16, grp, sel);
+        acc = mm2(acc, AA[kk][0], AA[kk][1], ck);
+        acc = mm2(acc, AAT[kk][0], AAT[kk][1], ck);
       }
       const int col = 16 * (hk * KH + j) + r16;
 #pragma unroll
@@ -751,6 +869,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   sSq = wave_sum(sSq);
   if (lane == 0) sm.red[wave] = sSq;
   __syncthreads();
+  GDN_REFRESH();
   // d gamma_j = row part - column parts - state term_j; the last row also gets
   // e^gamma_n <dS', Sq> + sum_j term_j; dg = suffix sum of d gamma
   if (wave == 0) {
@@ -779,6 +898,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       a.dbeta[gi] = db;
     }
   }
+#undef GDN_REFRESH
 }
 
 template <int DK>
