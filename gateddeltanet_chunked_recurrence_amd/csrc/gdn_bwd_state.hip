@@ -55,8 +55,6 @@ struct BImg {
   static constexpr int g_at(int nw) { return KI + nw * WT; }
 };
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // The selection operand: lane (grp, r16) holds B[8 grp + e][r16] = 1 exactly
 // when 8 grp + e = 16 half + r16, so A B = columns 16 half .. 16 half + 15 of A.
 __device__ __forceinline__ bf16x8 select_op(int half, int r16, int grp) {
@@ -359,7 +357,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
   if (nchunks > 0) {
     dma(nchunks - 1, (nchunks - 1) & 1);
     load_a(nchunks - 1, A1c, A2c);
-    wait_vmem();
+    vm_drain();
     lds_barrier();
   }
   for (int c = nchunks - 1; c >= 0; --c) {
@@ -429,7 +427,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
           dS[mt] = mfma(al, bVh[kk], dS[mt]);
         }
       }
-    wait_vmem();                                   // staging of chunk c - 1 landed
+    vm_drain();                                   // staging of chunk c - 1 landed
     lds_barrier();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) A1c[mt] = A1n[mt];

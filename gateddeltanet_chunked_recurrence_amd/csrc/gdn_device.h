@@ -50,6 +50,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Waits for every outstanding vector memory operation of this wave (loads,
+// stores and global-to-LDS copies). It is the s_waitcnt builtin, not inline
+// assembly, so the compiler's own wait insertion knows that everything issued
+// before it has completed: later uses of registers loaded before it need no
+// further wait. (Inline assembly is opaque to that pass, which then waits
+// again at the first use, for every load in flight at that point, prefetches
+// included, whenever loads and stores are both outstanding.)
+// Encoding: vmcnt 0, expcnt 7 and lgkmcnt 15 (no wait on those).
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // The lane index, opaque to the optimizer. Kernels call it at the start of
 // each phase so per-lane LDS addresses are rebuilt where they are used:
 // LDS arrays above 64 KB cannot use the 16-bit instruction offset, and

@@ -102,8 +102,6 @@ struct Stager {
   }
 };
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <int DK, int SF, int WF>
 __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N, int num_heads) {
   constexpr int NW = WF == 0 ? 2 : 1;
@@ -193,7 +191,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
     m = wave_max(m);
     if (lane == 0) sm.red[0][wave] = m;
   }
-  wait_vmem();
+  vm_drain();
   lds_barrier();
 
   const int gs = (SF != 0) ? a.block_v / 16 : 1;  // waves per scale tile
@@ -398,7 +396,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
         if (c + 2 < nchunks) stg.load_q(a, chunk_t0(c + 2), chunk_nc(c + 2), hk, tid);
       }
     }
-    wait_vmem();                                   // this wave's staging of chunk c + 1 landed
+    vm_drain();                                   // this wave's staging of chunk c + 1 landed
     lds_barrier();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Ucur[mt] = Unext[mt];

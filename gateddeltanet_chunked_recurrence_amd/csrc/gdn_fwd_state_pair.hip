@@ -55,8 +55,6 @@ struct PairSmem {
   float red[2][8];                                // per-wave state amax, by chunk parity
 };
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <int DK, int SF, int WF>
 __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
@@ -128,7 +126,11 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
   // Q of a chunk through registers (pperm + swizzle on the way; rows past the
   // chunk end repeat the last row and only feed unstored output rows)
   constexpr int QPT = 64 * DK / 8 / NT;           // 16-byte Q pieces per thread
-  u32x4 qreg[QPT];
+  // Q rows go through registers two chunks ahead: qnext holds chunk c + 1's
+  // (loaded during chunk c - 1, complete by that chunk's final wait), qreg
+  // receives chunk c + 2's during chunk c. The write of qnext to LDS then needs
+  // no wait, which would otherwise also wait for the image copy in flight.
+  u32x4 qreg[QPT], qnext[QPT];
   auto load_q = [&](int c) {
     const bf16* qb = reinterpret_cast<const bf16*>(a.q);
     const int t0 = chunk_t0(c), nc = chunk_nc(c);
@@ -138,17 +140,18 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
       qreg[p] = *reinterpret_cast<const u32x4*>(qb + ((int64_t)(t0 + min(row, nc - 1)) * a.Hqk + hk) * DK + 8 * c8);
     }
   };
-  auto store_q = [&]() {
+  auto store_q = [&](const u32x4 (&q)[QPT]) {
 #pragma unroll
     for (int p = 0; p < QPT; ++p) {
       const int e = tid + NT * p, row = e / (DK / 8), c8 = e % (DK / 8);
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8))]) = qreg[p].xy;
-      *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = qreg[p].zw;
+      *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8))]) = q[p].xy;
+      *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = q[p].zw;
     }
   };
   constexpr int NINS = IMGP / 64;                 // wave loads per image block
   constexpr int KW = (NINS + 7) / 8;               // ... per wave
+  constexpr int KD0 = (KW + 2) / 3, KD1 = KD0 + (KW - KD0 + 1) / 2;   // split points
   static_assert(IMGP % 64 == 0, "whole wave loads");
   auto dma = [&](int c, int b, int k0, int k1) {
     const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
@@ -175,8 +178,11 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
   load_q(0);
   dma(0, 0, 0, KW);
   load_small(0, Ucur, dWcur);
-  store_q();
-  wait_vmem();                                     // chunk 0's image block landed
+  store_q(qreg);
+  load_q(min(1, nchunks - 1));
+  vm_drain();                                     // chunk 0's image block landed
+#pragma unroll
+  for (int p = 0; p < QPT; ++p) qnext[p] = qreg[p];
   {
     float m = 0.f;
 #pragma unroll
@@ -195,12 +201,14 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
     const int t0 = chunk_t0(c), nc = chunk_nc(c);
     const int64_t ch = chunk_ch(c);
     const typename Sm::Buf& B = sm.buf[c & 1];
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_q(c + 1);                               // written to LDS after barrier B
-      dma(c + 1, (c + 1) & 1, 0, KW);
-      load_small(c + 1, Unext, dWnext);
-    }
+    // staging of chunk c + 1 (the last chunk repeats itself: the loads are
+    // unconditional, which keeps the compiler's wait before store_q exact)
+    const int cn = min(c + 1, nchunks - 1);
+    load_q(min(c + 2, nchunks - 1));               // written to LDS in the next chunk
+    // the image copy goes out in three parts (here, after barrier A, after
+    // barrier B): issued at once, its wave loads stall the issuing wave
+    dma(cn, (c + 1) & 1, 0, KD0);
+    load_small(cn, Unext, dWnext);
 
     // ---- gates of this chunk: exp(gamma) of the own row tiles, and
     //      exp(gamma_n - gamma) of all four (for the state update)
@@ -215,23 +223,20 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
     float amax = 0.f;
     for (int t = g0; t < g0 + gs; ++t) amax = fmaxf(amax, fmaxf(sm.red[c & 1][t], sm.red[c & 1][t + 4]));
     const float dS = qdq_scale<SF>(amax);
+    // codes of the saved state, stored after store_q below: with only loads
+    // in flight there, the wait for Q's registers is exact and leaves the
+    // next chunk's image copy and U loads in flight
+    uint32_t sbytes[MKH];
     {
       const float rS = 1.0f / dS;
-      uint8_t* sb = a.s_codes ? a.s_codes + ch * DK * Dv + (int64_t)dk0 * Dv + wcol + r16 : nullptr;
 #pragma unroll
       for (int j = 0; j < MKH; ++j) {
         const float x[4] = {S[j][0], S[j][1], S[j][2], S[j][3]};
         float cq[4];
-        uint32_t bytes;
-        quant4<SF>(x, rS, cq, bytes);
+        quant4<SF>(x, rS, cq, sbytes[j]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[j][i] = cq[i];
-        if (sb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sb[(int64_t)(16 * j + 4 * grp + i) * Dv] = (bytes >> (8 * i)) & 0xFFu;
-        }
       }
-      if (sb && cg == g0 && hf == 0 && lane == 0) a.s_scale[ch * (Dv / a.block_v) + wcol / a.block_v] = dS;
     }
     // own k-steps (KSH of them) to LDS; the operand for k-step kk is then
     // selected from own / partner halves with compile-time indices only
@@ -244,6 +249,7 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
       sm.x1.sqx[wave][j][lane] = bOwn[j];
     }
     lds_barrier();                               // A: Sq halves published
+    dma(cn, (c + 1) & 1, KD0, KD1);
 #pragma unroll
     for (int j = 0; j < KSH; ++j) bPar[j] = sm.x1.sqx[partner][j][lane];
     bf16x8 bS[KS];                                 // k-steps of the first half, then the second
@@ -292,7 +298,16 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
       }
     }
     lds_barrier();                               // B: Vnew halves published; Q, Sq reads done
-    if (more) store_q();                           // chunk c + 1's Q: every wave is done with Q
+    store_q(qnext);                                // chunk c + 1's Q: every wave is done with Q
+    dma(cn, (c + 1) & 1, KD1, KW);
+    if (a.s_codes) {
+      uint8_t* sb = a.s_codes + ch * DK * Dv + (int64_t)dk0 * Dv + wcol + r16;
+#pragma unroll
+      for (int j = 0; j < MKH; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sb[(int64_t)(16 * j + 4 * grp + i) * Dv] = (sbytes[j] >> (8 * i)) & 0xFFu;
+      if (cg == g0 && hf == 0 && lane == 0) a.s_scale[ch * (Dv / a.block_v) + wcol / a.block_v] = dS;
+    }
     // Vnew of all four token row tiles: tiles 0, 3 from half 0, tiles 1, 2 from
     // half 1 (selects with compile-time indices only)
     f32x4 Vt[4];
@@ -375,11 +390,13 @@ gdn_state_pair_kernel(FwdKernelArgs a, int N, int num_heads) {
       m = wave_max(m);
       if (lane == 0) sm.red[(c + 1) & 1][wave] = m;
     }
-    wait_vmem();                                   // this wave's staging of chunk c + 1 landed
+    vm_drain();                                   // this wave's staging of chunk c + 1 landed
     lds_barrier();                                 // C
 #pragma unroll
     for (int r = 0; r < 2; ++r) Ucur[r] = Unext[r];
     dWcur = dWnext;
+#pragma unroll
+    for (int p = 0; p < QPT; ++p) qnext[p] = qreg[p];
   }
   store_ht();
 }
