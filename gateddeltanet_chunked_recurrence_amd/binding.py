@@ -35,7 +35,7 @@ class FwdArgs(ctypes.Structure):
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [('num_slots', c_i64), ('off_state', c_i64), ('off_state_scale', c_i64),
-                ('off_w', c_i64), ('off_w_scale', c_i64), ('total_bytes', c_i64)]
+                ('off_w', c_i64), ('off_w_scale', c_i64), ('off_x', c_i64), ('total_bytes', c_i64)]
 
 
 class BwdArgs(ctypes.Structure):

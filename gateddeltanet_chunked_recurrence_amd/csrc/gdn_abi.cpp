@@ -105,6 +105,8 @@ gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
   off = round256(off + (wq ? tokens * a->Hv * a->Dk : 0));
   L.off_w_scale = off;
   off = round256(off + (wq ? L.num_slots * a->Hv * 4 : 0));
+  L.off_x = off;
+  off = round256(off + (a->io_dtype == GDN_BF16 ? L.num_slots * a->Hv * 64 * 64 * 4 : 0));
   L.total_bytes = off;
   return L;
 }
@@ -160,6 +162,7 @@ gdn::FwdKernelArgs kernel_args(const gdn_fwd_args* a, void* saved) {
       k.w_codes = reinterpret_cast<uint8_t*>(base + L.off_w);
       k.w_scale = reinterpret_cast<float*>(base + L.off_w_scale);
     }
+    if (a->io_dtype == GDN_BF16) k.s_X = reinterpret_cast<float*>(base + L.off_x);
   }
   k.T = a->T;
   k.Hqk = a->Hqk;
@@ -331,7 +334,10 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   k.dh0 = a->dh0;
   char* ws = static_cast<char*>(a->workspace);
   const BwdWsLayout W = bwd_ws_layout(&a->fwd);
-  k.ws_X = reinterpret_cast<float*>(ws + W.X);
+  // bf16 inputs with W QDQ: X comes from the forward (saved); otherwise the
+  // backward's first kernel solves again into the workspace
+  k.ws_X = (k.f.s_X && a->fwd.policy.w_fmt != GDN_QDQ_OFF) ? k.f.s_X
+                                                            : reinterpret_cast<float*>(ws + W.X);
   k.ws_W = reinterpret_cast<float*>(ws + W.W);
   k.ws_dstate = reinterpret_cast<float*>(ws + W.dstate);
   k.ws_dvn = reinterpret_cast<float*>(ws + W.dvn);

@@ -198,7 +198,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_prep(BwdKernelArgs a, int N) {
   for (int e = tid; e < 4096; e += NT) Xg[e] = Xf[(e >> 6) * 65 + (e & 63)];
 
   float* Wg = a.ws_W + ((int64_t)ch.t0 * Hv + h) * DK;
-  if constexpr (WF != 0) {
+  if constexpr (WF != 0 && !F32IN) {
+    // bf16 inputs: the later kernels read the W codes themselves
+  } else if constexpr (WF != 0) {
     const float dW = f.w_scale[(int64_t)slot * Hv + h];
     const uint8_t* codes = f.w_codes + ((int64_t)ch.t0 * Hv + h) * DK;
     for (int e = tid; e < ch.nc * DK; e += NT) {
@@ -684,8 +686,11 @@ __global__ void bwd_group(BwdKernelArgs a, int G) {
 template <int DK, bool F32IN>
 static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
   const dim3 slots(a.num_slots, c.Hv);
+  // bf16 inputs with W QDQ: X comes from the forward's saved buffer and the
+  // later kernels read the W codes, so there is nothing to prepare
 #define GDN_PREP(WFv) \
-  if (c.w_fmt == WFv) hipLaunchKernelGGL((bwd_prep<DK, F32IN, WFv>), slots, dim3(NT), 0, s, a, c.N);
+  if (c.w_fmt == WFv && (F32IN || WFv == 0)) \
+    hipLaunchKernelGGL((bwd_prep<DK, F32IN, WFv>), slots, dim3(NT), 0, s, a, c.N);
   GDN_PREP(0) GDN_PREP(1) GDN_PREP(2)
 #undef GDN_PREP
   hipError_t e = hipGetLastError();
@@ -706,6 +711,7 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
   } else {
     if ((e = launch_bwd_local(c, a, s)) != hipSuccess) return e;
   }
+  if (!F32IN && c.Hv == c.Hqk) return hipSuccess;   // dq, dk written directly
   hipLaunchKernelGGL((bwd_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, s, a, c.Hv / c.Hqk);
   return hipGetLastError();
 }

@@ -613,6 +613,21 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   // ---------------------------------------------------------------- finish
   auto& F = sm.u.f;
   constexpr int FLDK = FS::LDK;
+  // dq, dk rows: straight to the outputs with one value head per query/key
+  // head, else per value head (FP32) for the group sum
+  const bool direct = Hv == Hqk;
+  const bool half = direct && !a.grad_f32;         // bf16 outputs
+  const int esz = half ? 2 : 4;
+  const int64_t rstride = direct ? (int64_t)Hv * DK * esz : (int64_t)Hv * 2 * DK * 4;
+  char* const dq_base = direct ? reinterpret_cast<char*>(a.dq) + ((int64_t)t0 * Hv + h) * DK * esz
+                               : reinterpret_cast<char*>(a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK);
+  char* const dk_base = direct ? reinterpret_cast<char*>(a.dk) + ((int64_t)t0 * Hv + h) * DK * esz
+                               : reinterpret_cast<char*>(a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK + DK);
+  auto put_grad = [&](char* base, int t, int col, float v) {
+    char* p = base + t * rstride + col * esz;
+    if (half) *reinterpret_cast<bf16*>(p) = to_bf16(v);
+    else *reinterpret_cast<float*>(p) = v;
+  };
   GDN_REFRESH();
   {
 #pragma unroll
@@ -706,7 +721,6 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   // FB1: dq = scale e^gamma dQi + G K; dK = G^T Q + egc dKs + beta e^gamma X^T dW
   f32x4 dK[KH];
   {
-    float* dqp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK;
     bf16x8 AX[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -737,7 +751,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         const int t = 16 * tw + 4 * grp + q;
         const float qi = scale * eg4[q] * dQi[j][q];
         dg_acc[q] += qi * qv[q];
-        if (t < nc) dqp[(int64_t)t * Hv * 2 * DK + col] = qi + gk[q];
+        if (t < nc) put_grad(dq_base, t, col, qi + gk[q]);
         const float ks = egc4[q] * dKs[j][q];
         term_acc[q] += ks * kv[q];
         const float wv = xw[q] * bet4[q] * eg4[q];
@@ -828,7 +842,6 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         AA[kk][pl] = rowp(F.GA[pl], L64, 16 * tw, 32 * kk, r16, grp);
         AAT[kk][pl] = rowp(F.GTA[pl], L64, 16 * tw, 32 * kk, r16, grp);
       }
-    float* dkp = a.ws_dqk + ((int64_t)t0 * Hv + h) * 2 * DK + DK;
 #pragma unroll
     for (int j = 0; j < KH; ++j) {
       f32x4 acc = dK[j];
@@ -842,7 +855,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * tw + 4 * grp + q;
-        if (t < nc) dkp[(int64_t)t * Hv * 2 * DK + col] = acc[q];
+        if (t < nc) put_grad(dk_base, t, col, acc[q]);
       }
     }
   }

@@ -71,24 +71,30 @@ __device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct
   return mfma(lds_nat(m, row0 + r16, ld, 32 * (ct >> 1), grp), sel[ct & 1], zero4());
 }
 
-template <int DK>
+template <int DK, int DV, int NW>
 struct ImgSmem {
   static constexpr int LD = DK + 8;                // padded row strides (bf16)
-  static constexpr int LDO = 256 + 8;
+  static constexpr int LDO = DV + 8;
+  static constexpr int QB = 64 * LD * 2;           // bytes of the Q rows
+  static constexpr int OB = 2 * (DV / 16) * 64 * 16;   // bytes of the dO operands
   bf16 Kn[64 * LD];
-  bf16 Qn[64 * LD];
-  bf16 Wn[2][64 * LD];                             // W codes, or W hi and lo
+  union {                                          // Q rows, then the dO operands
+    bf16 Qn[64 * LD];
+    bf16x8 dOB[2 * (DV / 16) * 64];                // [kk][value tile][lane]
+    char raw[QB > OB ? QB : OB];
+  } u;
+  bf16 Wn[NW][64 * LD];                            // W codes, or W hi and lo
   bf16 dOn[64 * LDO];
-  bf16x8 dOB[2 * 16 * 64];                         // dO operands [kk][value tile][lane]
   float gam2[64], eg[64];
 };
 
 // ---------------------------------------------------------------- bwd_img
-template <int DK, int WF>
-__global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) {
+template <int DK, int DV, int WF>
+__global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) {
   constexpr int NW = WF == 0 ? 2 : 1;
   constexpr int MK = DK / 16, DPW = MK / 4;        // dk tiles, dk tiles per wave
-  using S = ImgSmem<DK>;
+  constexpr int NVT = DV / 16, nvb = DV / 64;
+  using S = ImgSmem<DK, DV, NW>;
   using I = Img<DK>;
   using BI = BImg<DK>;
   constexpr int LD = S::LD, LDO = S::LDO;
@@ -99,7 +105,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
   const int slot = blockIdx.x, h = blockIdx.y;
   const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
   if (!ch.valid) return;
-  const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, NVT = Dv / 16, nvb = Dv / 64;
+  const int Hv = f.Hv, Hqk = f.Hqk, Dv = DV;
   const int hk = h / (Hv / Hqk), t0 = ch.t0, nc = ch.nc;
   const int64_t chb = (int64_t)slot * Hv + h;
   bf16* img = a.ws_bimg + chb * BI::size(NW);
@@ -115,7 +121,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
       u32x4 qv = *reinterpret_cast<const u32x4*>(qg + off);
       if (row >= nc) kv = qv = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sm.Kn[row * LD + 8 * c8]) = kv;
-      *reinterpret_cast<u32x4*>(&sm.Qn[row * LD + 8 * c8]) = qv;
+      *reinterpret_cast<u32x4*>(&sm.u.Qn[row * LD + 8 * c8]) = qv;
     }
     const bf16* dog = reinterpret_cast<const bf16*>(a.dout);
     const int p8 = Dv / 8;
@@ -162,7 +168,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
           lo[j] = lj;
         }
         *reinterpret_cast<bf16x4*>(&sm.Wn[0][row * LD + 4 * c4]) = hi;
-        *reinterpret_cast<bf16x4*>(&sm.Wn[1][row * LD + 4 * c4]) = lo;
+        *reinterpret_cast<bf16x4*>(&sm.Wn[NW - 1][row * LD + 4 * c4]) = lo;
       }
     }
   }
@@ -187,14 +193,6 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
   sel[0] = select_op(0, r16, grp);
   sel[1] = select_op(1, r16, grp);
 
-  // ---- dO operands, tokens as contraction index (shared by A1 and A2)
-  for (int fi = wave; fi < 2 * NVT; fi += 4) {
-    const int kk = fi & 1, vt = fi >> 1;
-    const f32x4 c0 = tile_of(sm.dOn, LDO, 32 * kk, vt, r16, grp, sel);
-    const f32x4 c1 = tile_of(sm.dOn, LDO, 32 * kk + 16, vt, r16, grp, sel);
-    sm.dOB[(kk * 16 + vt) * 64 + lane] = pack_pair(c0, c1);
-  }
-
   // ---- (e^gamma Q)^T operands for this wave's dk tiles: hi + lo
   bf16x8 aQh[DPW][2], aQl[DPW][2];
 #pragma unroll
@@ -203,7 +201,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
     f32x4 cq[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      cq[it] = tile_of(sm.Qn, LD, 16 * it, dt, r16, grp, sel);
+      cq[it] = tile_of(sm.u.Qn, LD, 16 * it, dt, r16, grp, sel);
       const f32x4 e = *reinterpret_cast<const f32x4*>(&sm.eg[16 * it + 4 * grp]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) cq[it][q] *= e[q];
@@ -223,7 +221,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
       if (it < jt) continue;
 #pragma unroll
       for (int kq = 0; kq < DK / 32; ++kq)
-        pt[it] = mfma(lds_nat(sm.Qn, 16 * it + r16, LD, 32 * kq, grp),
+        pt[it] = mfma(lds_nat(sm.u.Qn, 16 * it + r16, LD, 32 * kq, grp),
                       lds_nat(sm.Kn, 16 * jt + r16, LD, 32 * kq, grp), pt[it]);
       const int j = 16 * jt + r16;
       const float gj = sm.gam2[j];
@@ -236,6 +234,15 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) pack_pair_split(pt[2 * kk], pt[2 * kk + 1], aPh[kk], aPl[kk]);
   }
+  __syncthreads();                                 // Q rows read: their space takes the dO operands
+  // ---- dO operands, tokens as contraction index (shared by A1 and A2)
+  for (int fi = wave; fi < 2 * NVT; fi += 4) {
+    const int kk = fi & 1, vt = fi >> 1;
+    const f32x4 c0 = tile_of(sm.dOn, LDO, 32 * kk, vt, r16, grp, sel);
+    const f32x4 c1 = tile_of(sm.dOn, LDO, 32 * kk + 16, vt, r16, grp, sel);
+    sm.u.dOB[(kk * NVT + vt) * 64 + lane] = pack_pair(c0, c1);
+  }
+
   __syncthreads();                                 // dO operands complete
 
   const float scale = f.scale;
@@ -245,7 +252,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if (2 * kk + 1 < jt) continue;               // both query tiles above the diagonal
-      const bf16x8 b = sm.dOB[(kk * 16 + vt) * 64 + lane];
+      const bf16x8 b = sm.u.dOB[(kk * NVT + vt) * 64 + lane];
       acc = mfma(aPh[kk], b, acc);
       acc = mfma(aPl[kk], b, acc);
     }
@@ -261,7 +268,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_img_kernel(BwdKernelArgs a, int N) 
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 b = sm.dOB[(kk * 16 + vt) * 64 + lane];
+        const bf16x8 b = sm.u.dOB[(kk * NVT + vt) * 64 + lane];
         acc = mfma(aQh[d][kk], b, acc);
         acc = mfma(aQl[d][kk], b, acc);
       }
@@ -443,16 +450,24 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
   }
 }
 
-template <int DK>
-static hipError_t launch_img_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+template <int DK, int DV>
+static hipError_t launch_img_dv(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
   const dim3 grid(a.num_slots, c.Hv);
 #define GDN_CASE(WFv) \
   if (c.w_fmt == WFv) { \
-    hipLaunchKernelGGL((bwd_img_kernel<DK, WFv>), grid, dim3(NT), 0, s, a, c.N); \
+    hipLaunchKernelGGL((bwd_img_kernel<DK, DV, WFv>), grid, dim3(NT), 0, s, a, c.N); \
     return hipGetLastError(); \
   }
   GDN_CASE(0) GDN_CASE(1) GDN_CASE(2)
 #undef GDN_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int DK>
+static hipError_t launch_img_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  if (c.Dv == 64) return launch_img_dv<DK, 64>(c, a, s);
+  if (c.Dv == 128) return launch_img_dv<DK, 128>(c, a, s);
+  if (c.Dv == 256) return launch_img_dv<DK, 256>(c, a, s);
   return hipErrorInvalidValue;
 }
 

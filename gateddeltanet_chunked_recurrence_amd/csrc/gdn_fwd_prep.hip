@@ -10,7 +10,8 @@
 //   T = X diag(beta);  T' = T diag(exp(gamma))
 //   W = T' K, QDQ_W over the [n, Dk] tile;  U = T V
 // Outputs are the operand images described in gdn_images.h, plus the W codes
-// and scale in the caller's saved buffer when it asks for them.
+// and scale in the caller's saved buffer when it asks for them, with X
+// (= (I + L)^-1) for the backward.
 //
 // Precision: q, k, v are bf16 and exact as MFMA operands; T and T' (FP32) are
 // split as hi + lo bf16 (two passes), so W and U carry ~16 mantissa bits of T
@@ -375,6 +376,15 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     lds_barrier();
     GDN_REFRESH();
 
+    // X for the backward (saved buffer), row-major FP32
+    if (a.s_X) {
+      float* xg = a.s_X + ch * 4096;
+      for (int e = tid; e < 1024; e += NT) {
+        const int row = e >> 4, c4 = e & 15;
+        const float* xs = &sm.b.s.X[row * 65 + 4 * c4];
+        *reinterpret_cast<f32x4*>(xg + row * 64 + 4 * c4) = f32x4{xs[0], xs[1], xs[2], xs[3]};
+      }
+    }
     // ---- 4. T = X diag(beta), T' = T diag(exp(gamma)) as hi / lo planes (pperm over columns)
     {
       const int row = tid >> 3, q = tid & 7;

@@ -21,6 +21,7 @@ struct FwdKernelArgs {
   float* s_scale;             // saved state scales, nullable
   uint8_t* w_codes;           // saved W codes (W QDQ on), nullable
   float* w_scale;             // saved W scales, nullable
+  float* s_X;                 // saved X = (I + L)^-1 per chunk (bf16 io), nullable
   // forward workspace (bf16 io): operand images written by the prep kernel
   __bf16* ws_img;             // [slots * Hv][W planes | K^T | P] (gdn_images.h)
   float* ws_u;                // [slots * Hv][Dv * 64] fragment order

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -112,10 +112,14 @@ typedef struct {
  *   w:      w_fmt != OFF: W codes, one byte each, token-major
  *           [B*T, Hv, Dk]; 0 bytes when w_fmt == OFF (the backward rebuilds W).
  *   w_scale: FP32 d of each W tile, [num_slots, Hv] (w_fmt != OFF only).
+ *   x:      bf16 inputs only: X = (I + L)^-1 of every chunk, the inverse of
+ *           the WY form's unit lower triangular matrix, FP32 row-major
+ *           [num_slots, Hv, 64, 64]; the backward reads it instead of solving
+ *           again. 0 bytes for FP32 inputs.
  * Slots no chunk uses are left unwritten. */
 typedef struct {
   int64_t num_slots;
-  int64_t off_state, off_state_scale, off_w, off_w_scale;
+  int64_t off_state, off_state_scale, off_w, off_w_scale, off_x;
   int64_t total_bytes;
 } gdn_saved_layout_t;
 

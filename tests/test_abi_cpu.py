@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 2
+    assert lib.gdn_abi_version() == 3
 
 
 def _args(**kw):
@@ -111,12 +111,17 @@ def test_saved_layout_sizes():
     assert lay.off_state_scale >= lay.num_slots * 4 * 128 * 128
     assert lay.off_w >= lay.off_state_scale + lay.num_slots * 4 * 2 * 4
     assert lay.off_w_scale >= lay.off_w + 200 * 4 * 128
+    assert lay.off_x >= lay.off_w_scale + lay.num_slots * 4 * 4
+    assert lay.total_bytes >= lay.off_x + lay.num_slots * 4 * 64 * 64 * 4   # X, bf16 inputs
     assert lay.total_bytes == lib.gdn_saved_bytes(ctypes.byref(a))
     a.policy.state_fmt = B.QDQ_OFF
     a.policy.w_fmt = B.QDQ_OFF
     lay = B.saved_layout(a)
     assert lay.off_state_scale >= lay.num_slots * 4 * 128 * 128 * 4
     assert lay.off_w == lay.off_state_scale and lay.off_w_scale == lay.off_w
+    f32 = _args(B=2, T=100, num_seqs=2, io_dtype=B.GDN_F32, Dk=64, Dv=64)
+    lay = B.saved_layout(f32)
+    assert lay.total_bytes == lay.off_x                      # no X for FP32 inputs
 
 
 def test_backward_rejects_before_launch():
