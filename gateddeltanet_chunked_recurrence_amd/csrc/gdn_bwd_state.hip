@@ -299,22 +299,27 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
 }
 
 // ---------------------------------------------------------------- bwd_state
-template <int DK, int NW>
-__global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N, int num_heads) {
+// WG waves per workgroup, each owning 16 value columns: the columns are
+// independent here, so a (sequence, head) can spread over several compute
+// units, which share its image block through the XCD's L2. A chunk step moves
+// the image block plus 28 KB per wave through the compute unit's vector memory
+// path, which bounds the step when four waves share one.
+template <int DK, int NW, int WG>
+__global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, int N, int num_heads) {
   using BI = BImg<DK>;
   using I = Img<DK>;
   constexpr int MK = DK / 16;
   constexpr int SZ = BI::size(NW);
   static_assert((SZ / 8) % 64 == 0, "image block is a whole number of wave loads");
   constexpr int NINS = SZ / 8 / 64;                // 1 KB wave loads per block
-  constexpr int KW = (NINS + 3) / 4;               // per wave
+  constexpr int KW = (NINS + WG - 1) / WG;         // per wave
   __shared__ __align__(16) bf16 buf[2][SZ];
 
   const FwdKernelArgs& f = a.f;
-  const int Hv = f.Hv, Dv = f.Dv, NVB = Dv / 64;
-  // workgroup id -> (head index, value block); the blocks of a head share an XCD
+  const int Hv = f.Hv, Dv = f.Dv, NVB = Dv / 64, GH = Dv / 16 / WG;
+  // workgroup id -> (head index, column group); the groups of a head share an XCD
   const int bid = blockIdx.x, xcd = bid & 7, r8 = bid >> 3;
-  const int vb = r8 % NVB, hidx = xcd + 8 * (r8 / NVB);
+  const int g = r8 % GH, hidx = xcd + 8 * (r8 / GH);
   if (hidx >= num_heads) return;
   const int n = hidx / Hv, h = hidx % Hv;
   int bos, eos;
@@ -329,7 +334,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
   const int slot0 = n + bos / CHUNK;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
   const int r16 = lane & 15, grp = lane >> 4;
-  const int wcol = vb * 64 + wave * 16;
+  const int cgi = g * WG + wave;                   // 16-column group of this wave
+  const int vb = cgi >> 2, wq = cgi & 3;           // its 64-wide block and place in it
+  const int wcol = 16 * cgi;
   const int64_t sbase = ((int64_t)n * Hv + h) * DK * Dv;
 
   // dS in accumulator layout: dS[mt][i] = dS[16 mt + 4 grp + i][wcol + r16]
@@ -346,7 +353,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
     u32x4* dst = reinterpret_cast<u32x4*>(buf[b]);
 #pragma unroll
     for (int k = 0; k < KW; ++k) {
-      const int j = min(wave + 4 * k, NINS - 1);
+      const int j = min(wave + WG * k, NINS - 1);
       __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
     }
   };
@@ -355,10 +362,10 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
     const int64_t ch = chunk_ch(c);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-      A1[mt] = *reinterpret_cast<const f32x4*>(a.ws_a1 + frag_off(ch, NVB, vb, wave, 4, mt, lane));
+      A1[mt] = *reinterpret_cast<const f32x4*>(a.ws_a1 + frag_off(ch, NVB, vb, wq, 4, mt, lane));
 #pragma unroll
     for (int mt = 0; mt < MK; ++mt)
-      A2[mt] = *reinterpret_cast<const f32x4*>(a.ws_a2 + frag_off(ch, NVB, vb, wave, MK, mt, lane));
+      A2[mt] = *reinterpret_cast<const f32x4*>(a.ws_a2 + frag_off(ch, NVB, vb, wq, MK, mt, lane));
   };
 
   if (nchunks > 0) {
@@ -370,14 +377,15 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
   for (int c = nchunks - 1; c >= 0; --c) {
     const int64_t ch = chunk_ch(c);
     const bf16* B = buf[c & 1];
+    // dS' of this chunk, for the chunk-local gradients (stores first: issued
+    // behind the staging loads they would wait for them)
+#pragma unroll
+    for (int mt = 0; mt < MK; ++mt)
+      *reinterpret_cast<f32x4*>(a.ws_dstate + frag_off(ch, NVB, vb, wq, MK, mt, lane)) = dS[mt];
     if (c > 0) {
       dma(c - 1, (c - 1) & 1);
       load_a(c - 1, A1n, A2n);
     }
-    // dS' of this chunk, for the chunk-local gradients
-#pragma unroll
-    for (int mt = 0; mt < MK; ++mt)
-      *reinterpret_cast<f32x4*>(a.ws_dstate + frag_off(ch, NVB, vb, wave, MK, mt, lane)) = dS[mt];
     // dS' as B operands (paired order over dk), hi + lo
     bf16x8 bSh[MK / 2], bSl[MK / 2];
 #pragma unroll
@@ -402,7 +410,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_state_kernel(BwdKernelArgs a, int N
       const f32x4 egc = *reinterpret_cast<const f32x4*>(&G[16 * mt + 4 * grp]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dvn[mt][i] = fmaf(egc[i], t1[mt][i], A1c[mt][i]);
-      *reinterpret_cast<f32x4*>(a.ws_dvn + frag_off(ch, NVB, vb, wave, 4, mt, lane)) = dvn[mt];
+      *reinterpret_cast<f32x4*>(a.ws_dvn + frag_off(ch, NVB, vb, wq, 4, mt, lane)) = dvn[mt];
     }
     // -dW dVnew as B operands (paired order over tokens), hi + lo
     const float nsc = G[65], egC = G[64];
@@ -471,13 +479,22 @@ static hipError_t launch_img_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
   return hipErrorInvalidValue;
 }
 
+template <int DK, int NW, int WG>
+static hipError_t launch_state_wg(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  const int num_heads = c.N * c.Hv, gh = c.Dv / 16 / WG;
+  const int64_t nblk = (int64_t)gh * 8 * ((num_heads + 7) / 8);
+  hipLaunchKernelGGL((bwd_state_kernel<DK, NW, WG>), dim3((unsigned)nblk), dim3(64 * WG), 0, s, a,
+                     c.N, num_heads);
+  return hipGetLastError();
+}
+
+// As few waves per workgroup as keep every compute unit busy with one.
 template <int DK, int NW>
 static hipError_t launch_state_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
-  const int num_heads = c.N * c.Hv, nvb = c.Dv / 64;
-  const int64_t nblk = (int64_t)nvb * 8 * ((num_heads + 7) / 8);
-  hipLaunchKernelGGL((bwd_state_kernel<DK, NW>), dim3((unsigned)nblk), dim3(NT), 0, s, a, c.N,
-                     num_heads);
-  return hipGetLastError();
+  const int64_t units = (int64_t)c.N * c.Hv * (c.Dv / 64), cus = device_cus();
+  if (4 * units <= cus) return launch_state_wg<DK, NW, 1>(c, a, s);
+  if (2 * units <= cus) return launch_state_wg<DK, NW, 2>(c, a, s);
+  return launch_state_wg<DK, NW, 4>(c, a, s);
 }
 
 }  // namespace

@@ -533,7 +533,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 }  // namespace
 
 // Compute units of the current device (queried once per device).
-static int device_cus() {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

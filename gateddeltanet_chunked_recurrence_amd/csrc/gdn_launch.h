@@ -73,6 +73,8 @@ struct BwdConfig {
 };
 
 hipError_t launch_bwd(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+// Compute units of the current device (queried once per device).
+int device_cus();
 // bf16 io: operand images of the reverse recurrence, then the recurrence.
 hipError_t launch_bwd_img(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
 hipError_t launch_bwd_state(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);

@@ -66,6 +66,9 @@ SMALL = [
      dict(lengths=[70, 129, 5], Hqk=1, Hv=2, Dk=64, Dv=256, state_fmt=E4M3, w_fmt=E4M3,
           block_v=32)),
     ('retention_dv256_e4m3', 'long_e4m3_t65536_h32_dk128_dv256', dict(T=333, Hqk=2, Hv=2)),
+    # 96 (sequence, head, 64-column) units: the reverse recurrence runs two
+    # waves per workgroup here (one below 65 units, four above 128)
+    ('gqa_96_units_e4m3', 'fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=150, Hqk=8, Hv=24)),
 ]
 
 
