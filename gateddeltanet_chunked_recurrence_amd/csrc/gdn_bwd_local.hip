@@ -79,10 +79,18 @@ __device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct
   return mfma(lds_pair(m, row0 + r16, ld, 32 * (ct >> 1), grp), s.get(ct & 1), zero4());
 }
 // Operand contracting over rows r0..r0+31 (paired order), free index = columns
-// 16 ct..16 ct+15.
+// 16 ct..16 ct+15: eight 16-bit LDS reads per lane, rows r0 + 4 grp + e and
+// r0 + 16 + 4 grp + e of column 16 ct + r16 (no arithmetic).
 __device__ __forceinline__ bf16x8 colp(const bf16* m, int ld, int r0, int ct, int r16, int grp,
-                                       const Sel& s) {
-  return pack_pair(tile_of(m, ld, r0, ct, r16, grp, s), tile_of(m, ld, r0 + 16, ct, r16, grp, s));
+                                       const Sel&) {
+  const bf16* p = m + (r0 + 4 * grp) * ld + 16 * ct + r16;
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = p[e * ld];
+    r[4 + e] = p[(16 + e) * ld];
+  }
+  return r;
 }
 // Operand contracting over columns k0..k0+31 (paired order), free index = rows
 // row0..row0+15.
@@ -96,42 +104,47 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
                                                    c, 0, 0, 0);
 }
-// Transpose of one accumulator tile (values exact in bf16): the lane that held
-// M[row0 + 4 grp + i][col0 + r16] gets M[row0 + r16][col0 + 4 grp + i].
-__device__ __forceinline__ f32x4 trans1(const f32x4& c, const Sel& s) {
-  return mfma16(bf16x4{to_bf16(c[0]), to_bf16(c[1]), to_bf16(c[2]), to_bf16(c[3])}, s.q, zero4());
+// Transpose of one accumulator tile given as bf16: the lane that held
+// M[row0 + 4 grp + i][col0 + r16] gets M[row0 + r16][col0 + 4 grp + i] (exact).
+__device__ __forceinline__ f32x4 trans1(const bf16x4& c, const Sel& s) {
+  return mfma16(c, s.q, zero4());
 }
 
-// Splits an FP32 tile into exact bf16 hi and lo parts (as FP32 values).
-__device__ __forceinline__ void split_tile(const f32x4& x, f32x4& hi, f32x4& lo) {
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
+  return bf16x4{to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3])};
+}
+// x = hi + lo + O(2^-17 |x|): hi = bf16(x) (nearest even), lo = bf16(x - hi).
+__device__ __forceinline__ void split4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
+  hi = to_bf16x4(x);
+  f32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float h = from_bf16(to_bf16(x[i]));
-    hi[i] = h;
-    lo[i] = from_bf16(to_bf16(x[i] - h));
-  }
+  for (int i = 0; i < 4; ++i) r[i] = x[i] - from_bf16(hi[i]);
+  lo = to_bf16x4(r);
 }
 
-// Writes four consecutive elements (FP32, exact in bf16 unless split) of one
-// row of a row-major bf16 matrix (one plane).
-__device__ __forceinline__ void put4(bf16* m, int off, const f32x4& v) {
-  *reinterpret_cast<bf16x4*>(m + off) = bf16x4{to_bf16(v[0]), to_bf16(v[1]), to_bf16(v[2]), to_bf16(v[3])};
+// Writes four consecutive elements of one row of a row-major bf16 matrix.
+__device__ __forceinline__ void put4(bf16* m, int off, const bf16x4& v) {
+  *reinterpret_cast<bf16x4*>(m + off) = v;
+}
+__device__ __forceinline__ void put4(bf16* m, int off, const f32x4& v) { put4(m, off, to_bf16x4(v)); }
+// Splits four FP32 values into the hi and lo planes.
+__device__ __forceinline__ void put4s(bf16* p0, bf16* p1, int off, const f32x4& v) {
+  bf16x4 h, l;
+  split4(v, h, l);
+  put4(p0, off, h);
+  put4(p1, off, l);
 }
 // Publishes an FP32 accumulator tile (rows 16 rt.., columns 16 ct..) of M as
 // rows of M^T (hi and lo planes): M^T[16 ct + r16][16 rt + 4 grp + i].
 __device__ __forceinline__ void put_T(bf16* p0, bf16* p1, int ld, const f32x4& c, int rt, int ct,
                                       int r16, int grp) {
-  f32x4 h, l;
-  split_tile(c, h, l);
-  const int off = (16 * ct + r16) * ld + 16 * rt + 4 * grp;
-  put4(p0, off, h);
-  put4(p1, off, l);
+  put4s(p0, p1, (16 * ct + r16) * ld + 16 * rt + 4 * grp, c);
 }
 // Publishes the same tile as rows of M (through a transpose).
 __device__ __forceinline__ void put_N(bf16* p0, bf16* p1, int ld, const f32x4& c, int rt, int ct,
                                       int r16, int grp, const Sel& s) {
-  f32x4 h, l;
-  split_tile(c, h, l);
+  bf16x4 h, l;
+  split4(c, h, l);
   const int off = (16 * rt + r16) * ld + 16 * ct + 4 * grp;
   put4(p0, off, trans1(h, s));
   put4(p1, off, trans1(l, s));
@@ -318,20 +331,14 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
                                      : static_cast<float>(static_cast<int8_t>(word & 0xFFu));
             x[i] = cv * L.sc[p];
           }
-          f32x4 hi, lo;
-          split_tile(x, hi, lo);
-          put4(V.Sqm[0], row * LVB + 16 * c16 + 4 * q4, hi);
-          put4(V.Sqm[1], row * LVB + 16 * c16 + 4 * q4, lo);
+          put4s(V.Sqm[0], V.Sqm[1], row * LVB + 16 * c16 + 4 * q4, x);
         }
       } else {
         const int row = e / (VB / 4), c4 = e % (VB / 4);
         f32x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(L.s[p][i]);
-        f32x4 hi, lo;
-        split_tile(x, hi, lo);
-        put4(V.Sqm[0], row * LVB + 4 * c4, hi);
-        put4(V.Sqm[1], row * LVB + 4 * c4, lo);
+        put4s(V.Sqm[0], V.Sqm[1], row * LVB + 4 * c4, x);
       }
     }
   };
@@ -396,10 +403,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       f32x4 w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = row < nc ? __uint_as_float(wl[p][i]) : 0.f;
-      f32x4 hi, lo;
-      split_tile(w, hi, lo);
-      put4(V.Wm[0], row * LDK + 4 * c4, hi);
-      put4(V.Wm[NWP - 1], row * LDK + 4 * c4, lo);
+      put4s(V.Wm[0], V.Wm[NWP - 1], row * LDK + 4 * c4, w);
     }
   }
   store_pass(L);
@@ -412,10 +416,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     f32x4 x = xl[p];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] *= b[i];
-    f32x4 hi, lo;
-    split_tile(x, hi, lo);
-    put4(V.Tm[0], row * L64 + 4 * c4, hi);
-    put4(V.Tm[1], row * L64 + 4 * c4, lo);
+    put4s(V.Tm[0], V.Tm[1], row * L64 + 4 * c4, x);
   }
   __syncthreads();
 
@@ -440,8 +441,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int idx = wave + 8 * u, kt = idx % MK, vt = idx / MK;
-      f32x4 ch_, cl_;
-      split_tile(L.ds[u], ch_, cl_);
+      bf16x4 ch_, cl_;
+      split4(L.ds[u], ch_, cl_);
       const f32x4 th = trans1(ch_, sel), tl = trans1(cl_, sel);
       const int off = (16 * kt + r16) * LVB + 16 * vt + 4 * grp;
       put4(V.dSm[0], off, th);
@@ -463,8 +464,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         f32x4 th[2], tl[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          f32x4 ch_, cl_;
-          split_tile(dvp[2 * kk + e], ch_, cl_);
+          bf16x4 ch_, cl_;
+          split4(dvp[2 * kk + e], ch_, cl_);
           th[e] = trans1(ch_, sel);
           tl[e] = trans1(cl_, sel);
         }
@@ -524,11 +525,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         f32x4 vn;
 #pragma unroll
         for (int i = 0; i < 4; ++i) vn[i] = acc[j][i] - dWs * accw[j][i];
-        f32x4 vh, vl;
-        split_tile(vn, vh, vl);
-        const int off = (16 * jt[j] + r16) * LVB + 16 * vt + 4 * grp;
-        put4(V.Vnm[0], off, vh);
-        put4(V.Vnm[1], off, vl);
+        put4s(V.Vnm[0], V.Vnm[1], (16 * jt[j] + r16) * LVB + 16 * vt + 4 * grp, vn);
       }
       // dv^T = dVnew^T T: A over tokens from the dVnew tiles, B = T over its rows
       f32x4 dv[NJ];
@@ -642,10 +639,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
 #pragma unroll
     for (int p = 0; p < NXL; ++p) {
       const int e = tid + NT * p, row = e >> 4, c4 = e & 15;
-      f32x4 hi, lo;
-      split_tile(xl[p], hi, lo);
-      put4(F.Xm[0], row * L64 + 4 * c4, hi);
-      put4(F.Xm[1], row * L64 + 4 * c4, lo);
+      put4s(F.Xm[0], F.Xm[1], row * L64 + 4 * c4, xl[p]);
     }
     // dW = -(accumulated dVnew Sq^T), as rows
 #pragma unroll
