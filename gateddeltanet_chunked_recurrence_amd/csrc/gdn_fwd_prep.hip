@@ -253,7 +253,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     }
     ks.store_rows(sm.a.kq.K, LDK, wave, lane);
     qs.store_rows(sm.a.kq.Q, LDK, wave, lane);
-    ks.store_t(sm.Kt, img + I::template kt_at<NW>(), wave, lane);
+    ks.store_t(sm.Kt, nullptr, wave, lane);       // the image copy goes out during the solve
     if (wave == 0) {
       const float gv = lane < nc ? graw : 0.f;
       const float g2 = wave_incl_scan(gv * LOG2E, lane);
@@ -279,23 +279,31 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       if (job >= 20) break;
       int mi, mj;
       lower_tile(job % 10, mi, mj);
-      const bool isL = job < 10;
-      const f32x4 acc = tile_abt<DK, LDK>(isL ? sm.a.kq.K : sm.a.kq.Q, sm.a.kq.K, mi, mj, r16, grp);
-      const int cj = 16 * mj + r16;
-      const float gj = sm.gam2[cj];
+      if (job < 10) {
+        const f32x4 acc = tile_abt<DK, LDK>(sm.a.kq.K, sm.a.kq.K, mi, mj, r16, grp);
+        const int cj = 16 * mj + r16;
+        const float gj = sm.gam2[cj];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mi + 4 * grp + i;
-        const float e = fexp2(sm.gam2[row] - gj);
-        if (isL) {
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * mi + 4 * grp + i;
+          const float e = fexp2(sm.gam2[row] - gj);
           sm.b.s.L[row * 65 + cj] = row > cj ? sm.bet[row] * acc[i] * e : 0.f;
-        } else {
-          const float pv = row >= cj ? acc[i] * e : 0.f;
-          bf16 hi, lo;
-          split2(pv, hi, lo);
-          sm.c.P[0][row * 72 + pperm(cj)] = hi;
-          sm.c.P[1][row * 72 + pperm(cj)] = lo;
         }
+      } else {
+        // P^T tile (K_mj Q_mi^T): the lane holds P[16 mi + r16][16 mj + 4 grp + i],
+        // four consecutive columns, so hi and lo go out as 8-byte writes
+        const f32x4 acc = tile_abt<DK, LDK>(sm.a.kq.K, sm.a.kq.Q, mj, mi, r16, grp);
+        const int row = 16 * mi + r16, c0 = 16 * mj + 4 * grp;
+        const float gr = sm.gam2[row];
+        bf16 hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cj = c0 + i;
+          const float pv = row >= cj ? acc[i] * fexp2(gr - sm.gam2[cj]) : 0.f;
+          split2(pv, hi[i], lo[i]);
+        }
+        st4(&sm.c.P[0][row * 72 + pperm(c0)], hi[0], hi[1], hi[2], hi[3]);
+        st4(&sm.c.P[1][row * 72 + pperm(c0)], lo[0], lo[1], lo[2], lo[3]);
       }
     }
     lds_barrier();
@@ -319,6 +327,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       const uint4* src = reinterpret_cast<const uint4*>(&sm.c.P[0][0]);
       uint4* dst = reinterpret_cast<uint4*>(img + I::template p_at<NW>());
       for (int e = t; e < 2 * I::P1 / 8; e += NT - 64) dst[e] = src[e];
+      // K^T image: 16-byte copies of the LDS tile (K^T and P are adjacent in the image)
+      const uint4* ksrc = reinterpret_cast<const uint4*>(&sm.Kt[0]);
+      uint4* kdst = reinterpret_cast<uint4*>(img + I::template kt_at<NW>());
+      for (int e = t; e < I::KT / 8; e += NT - 64) kdst[e] = ksrc[e];
       for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
         const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
         const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
