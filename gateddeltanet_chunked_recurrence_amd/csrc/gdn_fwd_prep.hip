@@ -49,6 +49,7 @@ struct PrepSmem {
     float Y[32 * 33];                            // 32-block merge scratch
     bf16 T[4][64 * 72];                          // T hi, T lo, T' hi, T' lo
   } c;
+  alignas(16) float Ld[4][16 * 16];              // diagonal 16x16 blocks of L, row-major
   alignas(16) float gam2[64];                    // log2-scaled gamma
   alignas(16) float bet[64];
   alignas(16) float eg[64];                      // exp(gamma)
@@ -287,7 +288,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * mi + 4 * grp + i;
           const float e = fexp2(sm.gam2[row] - gj);
-          sm.b.s.L[row * 65 + cj] = row > cj ? sm.bet[row] * acc[i] * e : 0.f;
+          const float lv = row > cj ? sm.bet[row] * acc[i] * e : 0.f;
+          sm.b.s.L[row * 65 + cj] = lv;
+          if (mi == mj) sm.Ld[mi][(4 * grp + i) * 16 + r16] = lv;   // aligned copy for the substitution
         }
       } else {
         // P^T tile (K_mj Q_mi^T): the lane holds P[16 mi + r16][16 mj + 4 grp + i],
@@ -311,15 +314,36 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 
     // ---- 3. wave 0: diagonal blocks of X; others: P image out, X upper zero, V^T in
     if (wave == 0) {
+      // lane (b, cc): column cc of the inverse of diagonal block b, by rows;
+      // row r of the block is read as 16-byte pieces (all 16 lanes of a
+      // block read the same row), independent of the substitution itself
       const int b = lane >> 4, cc = lane & 15;
+      const f32x4* Lr = reinterpret_cast<const f32x4*>(&sm.Ld[b][0]);
       float x[16];
+      // rows go through a two-row-ahead register ring, so LDS latency overlaps
+      // the substitution instead of being paid row by row
+      f32x4 ring[3][4];
+      auto fetch = [&](int r, f32x4 (&dst)[4]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == cc) ? 1.f : 0.f;
-      const float* Lb = &sm.b.s.L[(16 * b) * 65 + 16 * b];
+        for (int j4 = 0; j4 < 4; ++j4)
+          if (j4 < (r + 3) / 4) dst[j4] = Lr[r * 4 + j4];
+      };
+      fetch(1, ring[1]);
+      fetch(2, ring[2]);
+      x[0] = cc == 0 ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < 15; ++j)
+      for (int r = 1; r < 16; ++r) {
+        if (r + 2 < 16) fetch(r + 2, ring[(r + 2) % 3]);
+        float s = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int r = j + 1; r < 16; ++r) x[r] -= Lb[r * 65 + j] * x[j];
+        for (int j4 = 0; j4 < (r + 3) / 4; ++j4) {
+          const f32x4 l = ring[r % 3][j4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * j4 + e < r) s -= l[e] * x[4 * j4 + e];
+        }
+        x[r] = s;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sm.b.s.X[(16 * b + r) * 65 + 16 * b + cc] = x[r];
     } else {
