@@ -62,8 +62,8 @@ def bytes_algorithmic(spec):
 # Sources each timed kernel is compiled from; a committed counter summary is
 # used only while these files are unchanged.
 KERNEL_SOURCES = {
-    'gdn_state_pair_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h',
-                              'gdn_fwd_state_pair.hip'),
+    'gdn_state_split_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h',
+                               'gdn_fwd_state_split.hip'),
     'gdn_prep_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_fwd_prep.hip'),
 }
 
@@ -221,7 +221,7 @@ def main():
     th = tokens * spec['Hv']
     Dk, Dv = spec['Dk'], spec['Dv']
     f_prep, f_state = flops_prep(Dk, Dv) * th, flops_state(Dk, Dv) * th
-    dom = 'gdn_state_pair_kernel' if state_ms >= prep_ms else 'gdn_prep_kernel'
+    dom = 'gdn_state_split_kernel' if state_ms >= prep_ms else 'gdn_prep_kernel'
     dom_ms, dom_flops = (state_ms, f_state) if state_ms >= prep_ms else (prep_ms, f_prep)
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     path_ms = prep_ms + state_ms
@@ -239,7 +239,7 @@ def main():
                       frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic, kernel=dom),
         roofline_path=dict(bound='mfma', achieved=path, peak=PEAK_BF16_TFLOPS, unit='TFLOP/s',
                            frac=path / PEAK_BF16_TFLOPS),
-        kernel_ms=dict(gdn_prep_kernel=prep_ms, gdn_state_pair_kernel=state_ms),
+        kernel_ms=dict(gdn_prep_kernel=prep_ms, gdn_state_split_kernel=state_ms),
         gflop_per_step=(f_prep + f_state) / 1e9,
         hbm_gbs_algorithmic=bytes_algorithmic(spec) / (path_ms * 1e-3) / 1e9,
         source_hash=src)

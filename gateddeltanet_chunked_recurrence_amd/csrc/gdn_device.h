@@ -90,14 +90,24 @@ __device__ __forceinline__ bf16x8 pack_pair(const f32x4& t0, const f32x4& t1) {
   r[4] = to_bf16(t1[0]); r[5] = to_bf16(t1[1]); r[6] = to_bf16(t1[2]); r[7] = to_bf16(t1[3]);
   return r;
 }
+// The hi values are rounded once, as packed pairs; each one's FP32 value for
+// the remainder is then a half of its packed word (bf16 is the upper half of
+// an FP32 pattern).
 __device__ __forceinline__ void pack_pair_split(const f32x4& t0, const f32x4& t1,
                                                 bf16x8& hi, bf16x8& lo) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  hi = pack_pair(t0, t1);
+  const u32x4v hw = __builtin_bit_cast(u32x4v, hi);
+  float hv[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    hv[2 * p] = __builtin_bit_cast(float, hw[p] << 16);
+    hv[2 * p + 1] = __builtin_bit_cast(float, hw[p] & 0xFFFF0000u);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    bf16 h0, l0, h1, l1;
-    split2(t0[e], h0, l0);
-    split2(t1[e], h1, l1);
-    hi[e] = h0; lo[e] = l0; hi[e + 4] = h1; lo[e + 4] = l1;
+    lo[e] = to_bf16(t0[e] - hv[e]);
+    lo[e + 4] = to_bf16(t1[e] - hv[e + 4]);
   }
 }
 
@@ -126,10 +136,26 @@ __device__ __forceinline__ bf16x8 lds_pair(const bf16* base, int row, int ld, in
 }
 
 // ---------------------------------------------------------------- reductions
+// A float moved between lanes by a DPP pattern within rows of 16 lanes
+// (CTRL: quad_perm 0x00..0xFF, row_mirror 0x140, row_half_mirror 0x141).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float read_lane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+// Maximum over the 64 lanes (all active), in every lane. DPP within each row
+// of 16 lanes, then the four row maxima through scalar registers: no LDS
+// round trip (a shuffle through the LDS crossbar costs a full LDS latency per
+// step). The maximum is exact in any order.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, WAVE));
-  return x;
+  x = fmaxf(x, dpp_f<0xB1>(x));                   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f<0x4E>(x));                   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f<0x141>(x));                  // lanes i, 7 - i of each 8
+  x = fmaxf(x, dpp_f<0x140>(x));                  // lanes i, 15 - i of each 16
+  return fmaxf(fmaxf(read_lane(x, 0), read_lane(x, 16)), fmaxf(read_lane(x, 32), read_lane(x, 48)));
 }
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -437,7 +437,7 @@ static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, 
 }
 
 hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
-  if (cfg.state_fmt != 0 && cfg.w_fmt != 0) return launch_fwd_state_pair(cfg, a, s);
+  if (cfg.state_fmt != 0 && cfg.w_fmt != 0) return launch_fwd_state_split(cfg, a, s);
   if (cfg.Dk == 128) return launch_state_dk<128>(cfg, a, s);
   if (cfg.Dk == 64) return launch_state_dk<64>(cfg, a, s);
   return hipErrorInvalidValue;

@@ -1,0 +1,455 @@
+// Forward state recurrence with both QDQ sites on ("[1/4] GDN state/W QAT
+// foundation", "What does this PR do?"; "[2/4] GDN/KDA decode QAT with INT8
+// recurrent state", "What does this PR do?": per-head [Dk, block_v] state
+// scales). One 8-wave workgroup per (sequence, value head, 64-wide value
+// block), in two roles that share the block's four 16-column groups:
+//   recurrence waves 0..3 (one per SIMD): wave w keeps columns [16 w, 16 w + 16)
+//     of the state, all Dk rows, in VGPRs for the whole sequence and runs only
+//     the chain the next chunk depends on:
+//       Sq = QDQ_S(S);  Vnew = U - dW dS (Wc Sc);
+//       S  = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew)
+//   output waves 4..7 (one per SIMD): wave 4 + w forms the output of the same
+//     columns from the published state codes and Vnew,
+//       O = scale (exp(gamma) dS (Q Sc) + P Vnew),
+//     writes the saved state codes, and stages the next chunk's operands.
+// Per chunk, two LDS barriers:
+//   recurrence: scale, QDQ, codes to LDS, W Sq, Vnew to LDS | M | K^T D, amax | X
+//   output:     last chunk's stores, Q to LDS, next copies issued | M | O, codes | X
+// The output products are computed transposed (O^T = Sc^T Q^T + Vnew^T P^T):
+// the published code and Vnew fragments are then A operands as they stand, and
+// a lane's accumulator holds four adjacent output columns of one token, which
+// leave as one 8-byte store. The output waves' global stores are issued at the
+// top of the next chunk, so the wait for the staged copies before barrier X
+// does not also wait for them.
+#include "gdn_device.h"
+#include "gdn_images.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int NT = 512;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DK>
+struct SplitSmem {
+  using I = Img<DK>;
+  struct Buf {                                    // one image block (W codes, K^T, P, gates)
+    bf16 W[I::WQ];
+    bf16 Kt[I::KT];
+    bf16 P[2 * I::P1];
+    alignas(16) float G[I::GB / 2];
+  };
+  Buf buf[2];
+  bf16 Q[I::WQ];                                  // W image layout, single buffer
+  // state code bytes: codes[jj][col][g] holds, for block column col, the rows
+  // 32 jj + 4 g + i (x, byte i) and 32 jj + 16 + 4 g + i (y, byte i)
+  u32x2 codes[DK / 32][64][4];
+  f32x4 vnx[4][4][64];                            // Vnew: column group, row tile, lane
+  alignas(16) float red[2][4];                    // per-column-group state amax, by chunk parity
+};
+
+// Eight state codes (bytes) as bf16, exact: E4M3 codes have 4 significant
+// bits and INT8 codes at most 7.
+// E4M3 pairs go through the scaled fp8 -> bf16 conversion with scale 1 (exact
+// for every E4M3 value, subnormals included; checked against the FP32
+// conversion for all 256 codes on gfx950).
+template <int SF>
+__device__ __forceinline__ bf16x8 codes_bf16(u32x2 w) {
+  if constexpr (SF == 1) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  } else {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = to_bf16(static_cast<float>(static_cast<int8_t>((w.x >> (8 * e)) & 0xFFu)));
+      r[4 + e] = to_bf16(static_cast<float>(static_cast<int8_t>((w.y >> (8 * e)) & 0xFFu)));
+    }
+    return r;
+  }
+}
+
+template <int DK, int SF, int WF>
+__global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
+  static_assert(SF != 0 && WF != 0, "both QDQ sites on");
+  using I = Img<DK>;
+  using Sm = SplitSmem<DK>;
+  constexpr int MK = DK / 16;                     // 16-row tiles of a state column group
+  constexpr int KS = DK / 32;                     // 32-deep k-steps over dk
+  constexpr int IMGP = I::template img<1>() / 8;  // 16-byte pieces of an image block
+  static_assert(sizeof(typename Sm::Buf) == 16 * IMGP, "image block layout");
+  __shared__ __align__(16) Sm sm;
+
+  const int Hv = a.Hv, Dv = a.Dv, NVB = Dv / 64;
+  // workgroup id -> (head index, value block); the blocks of a head share an XCD
+  const int bid = blockIdx.x, xcd = bid & 7, r8 = bid >> 3;
+  const int vb = r8 % NVB, hidx = xcd + 8 * (r8 / NVB);
+  if (hidx >= num_heads) return;
+  const int n = hidx / Hv, h = hidx % Hv;
+  const int hk = h / (Hv / a.Hqk);
+  int bos, eos;
+  if (a.cu_seqlens) {
+    bos = a.cu_seqlens[n];
+    eos = a.cu_seqlens[n + 1];
+  } else {
+    bos = n * a.T;
+    eos = bos + a.T;
+  }
+  const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
+  const int slot0 = n + bos / CHUNK;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cg = wave & 3;                        // column group of either role
+  const int lane = __lane_id(), r16 = lane & 15, grp = lane >> 4;
+  const int wcol = vb * 64 + cg * 16;             // first value column of the group
+  const int64_t state_base = ((int64_t)n * Hv + h) * DK * Dv;
+  const int gs = a.block_v / 16;                  // column groups per scale tile
+  const int g0 = (cg / gs) * gs;
+
+  auto chunk_t0 = [&](int c) { return bos + CHUNK * c; };
+  auto chunk_nc = [&](int c) { return min(CHUNK, eos - bos - CHUNK * c); };
+  auto chunk_ch = [&](int c) { return (int64_t)(slot0 + c) * Hv + h; };
+  // state scale of chunk c from the four published column-group maxima
+  auto scale_of = [&](int c) {
+    const f32x4 rv = *reinterpret_cast<const f32x4*>(&sm.red[c & 1][0]);
+    float amax = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (t >= g0 && t < g0 + gs) amax = fmaxf(amax, rv[t]);
+    return qdq_scale<SF>(amax);
+  };
+
+  if (wave < 4) {
+    // ======================= recurrence role =======================
+    __builtin_amdgcn_s_setprio(2);
+    // S[j][i] = S[16 j + 4 grp + i][wcol + r16]
+    f32x4 S[MK];
+    if (a.h0) {
+      const float* hp = a.h0 + state_base + wcol + r16;
+#pragma unroll
+      for (int j = 0; j < MK; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[j][i] = hp[(int64_t)(16 * j + 4 * grp + i) * Dv];
+    } else {
+#pragma unroll
+      for (int j = 0; j < MK; ++j) S[j] = zero4();
+    }
+    auto store_ht = [&]() {
+      if (!a.ht) return;
+      float* hp = a.ht + state_base + wcol + r16;
+#pragma unroll
+      for (int j = 0; j < MK; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hp[(int64_t)(16 * j + 4 * grp + i) * Dv] = S[j][i];
+    };
+    if (nchunks == 0) {
+      store_ht();
+      return;
+    }
+    // U fragments of the four row tiles of this column group, and the W scale
+    f32x4 Ucur[4], Unext[4];
+    float dWcur = 1.f, dWnext = 1.f;
+    auto load_u = [&](int c, f32x4 (&U)[4], float& dW) {
+      const int64_t ch = chunk_ch(c);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        U[mt] = *reinterpret_cast<const f32x4*>(a.ws_u + u_off(ch, NVB, vb, cg, mt, lane));
+      dW = a.ws_wscale[ch];
+    };
+    load_u(0, Ucur, dWcur);
+    {
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < MK; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[j][i]));
+      m = wave_max(m);
+      if (lane == 0) sm.red[0][cg] = m;
+    }
+    vm_drain();
+    lds_barrier();                                 // P
+
+    for (int c = 0; c < nchunks; ++c) {
+      const typename Sm::Buf& B = sm.buf[c & 1];
+      load_u(min(c + 1, nchunks - 1), Unext, dWnext);
+      // operands read ahead of their products: the W fragments here, over the
+      // QDQ; the K^T fragments after W Sq is issued, over Vnew and barrier M
+      bf16x8 op[KS][4];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) op[kk][mt] = ld_wq<DK>(B.W, 16 * mt + r16, kk, grp);
+      const float dS = scale_of(c);
+
+      // ---- QDQ; code bytes to LDS; Sq as the B operand of W Sq
+      uint32_t sb[MK];
+      {
+        const float rS = 1.0f / dS;
+#pragma unroll
+        for (int j = 0; j < MK; ++j) {
+          const float x[4] = {S[j][0], S[j][1], S[j][2], S[j][3]};
+          float cq[4];
+          quant4<SF>(x, rS, cq, sb[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[j][i] = cq[i];
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < KS; ++jj) sm.codes[jj][16 * cg + r16][grp] = u32x2{sb[2 * jj], sb[2 * jj + 1]};
+
+      // ---- W Sq over the four token row tiles
+      f32x4 accw[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) accw[mt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 b = pack_pair(S[2 * kk], S[2 * kk + 1]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) accw[mt] = mfma(op[kk][mt], b, accw[mt]);
+      }
+      bf16x8 kop[2][MK];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < MK; ++j) kop[t][j] = lds_nat(B.Kt, 16 * j + r16, I::R64, 32 * t, grp);
+      f32x4 Vn[4];
+      {
+        const float sc = dWcur * dS;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Vn[mt][i] = Ucur[mt][i] - sc * accw[mt][i];
+          sm.vnx[cg][mt][lane] = Vn[mt];
+        }
+      }
+      const f32x4 e0[2] = {*reinterpret_cast<const f32x4*>(&B.G[64 + 4 * grp]),
+                           *reinterpret_cast<const f32x4*>(&B.G[96 + 4 * grp])};
+      const f32x4 e1[2] = {*reinterpret_cast<const f32x4*>(&B.G[80 + 4 * grp]),
+                           *reinterpret_cast<const f32x4*>(&B.G[112 + 4 * grp])};
+      const float sdec = B.G[128] * dS;
+      lds_barrier();                               // M: codes and Vnew published
+
+      // ---- S = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew)
+      bf16x8 bDh[2], bDl[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 d0, d1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          d0[i] = e0[t][i] * Vn[2 * t][i];
+          d1[i] = e1[t][i] * Vn[2 * t + 1][i];
+        }
+        pack_pair_split(d0, d1, bDh[t], bDl[t]);
+      }
+#pragma unroll
+      for (int j = 0; j < MK; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[j][i] *= sdec;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int j = 0; j < MK; ++j) S[j] = mfma(kop[t][j], bDh[t], S[j]);
+#pragma unroll
+        for (int j = 0; j < MK; ++j) S[j] = mfma(kop[t][j], bDl[t], S[j]);
+      }
+      {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < MK; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[j][i]));
+        m = wave_max(m);
+        if (lane == 0) sm.red[(c + 1) & 1][cg] = m;
+      }
+      vm_drain();                                  // next chunk's U landed
+      lds_barrier();                               // X
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Ucur[mt] = Unext[mt];
+      dWcur = dWnext;
+    }
+    store_ht();
+  } else {
+    // ========================= output role =========================
+    if (nchunks == 0) return;
+    const int otid = cg * 64 + lane;               // 0..255 over the output waves
+    constexpr int QPT = 64 * DK / 8 / 256;         // 16-byte Q pieces per lane
+    u32x4 qreg[QPT];
+    auto load_q = [&](int c) {
+      const bf16* qb = reinterpret_cast<const bf16*>(a.q);
+      const int t0 = chunk_t0(c), nc = chunk_nc(c);
+#pragma unroll
+      for (int p = 0; p < QPT; ++p) {
+        const int e = otid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
+        qreg[p] = *reinterpret_cast<const u32x4*>(qb + ((int64_t)(t0 + min(row, nc - 1)) * a.Hqk + hk) * DK + 8 * c8);
+      }
+    };
+    auto store_q = [&]() {
+#pragma unroll
+      for (int p = 0; p < QPT; ++p) {
+        const int e = otid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
+        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8))]) = qreg[p].xy;
+        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = qreg[p].zw;
+      }
+    };
+    constexpr int NINS = IMGP / 64;               // wave loads per image block
+    constexpr int KW = (NINS + 3) / 4;            // ... per output wave
+    static_assert(IMGP % 64 == 0, "whole wave loads");
+    auto dma = [&](int c, int b) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
+      uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].W);
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        const int j = min(cg + 4 * k, NINS - 1);  // a repeated last load rewrites the same bytes
+        __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
+      }
+    };
+    // stores held over to the next chunk: the output rows of the four row
+    // tiles (four bf16 each) and the saved code words
+    constexpr int CPL = DK / 64;                   // 4x4 code blocks per lane
+    u32x2 ov[4];
+    uint32_t cw[CPL][4];
+    int pc = -1;                                   // chunk whose stores are pending
+    float pdS = 0.f;
+    auto flush = [&]() {
+      if (pc < 0) return;
+      const int t0 = chunk_t0(pc), nc = chunk_nc(pc);
+      const int64_t ch = chunk_ch(pc);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int tok = 16 * mt + r16;
+        if (tok < nc) {
+          bf16* op = reinterpret_cast<bf16*>(a.o) + ((int64_t)(t0 + tok) * Hv + h) * Dv + wcol + 4 * grp;
+          *reinterpret_cast<u32x2*>(op) = ov[mt];
+        }
+      }
+      if (a.s_codes) {
+        uint8_t* sbase = a.s_codes + ch * DK * Dv + wcol;
+#pragma unroll
+        for (int p = 0; p < CPL; ++p) {
+          const int cb = lane + 64 * p, q = cb & 3, g = (cb >> 2) & 3, hh = (cb >> 4) & 1, jj = cb >> 5;
+          const int row0 = 32 * jj + 16 * hh + 4 * g;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint32_t*>(sbase + (int64_t)(row0 + i) * Dv + 4 * q) = cw[p][i];
+        }
+        if (cg == g0 && lane == 0) a.s_scale[ch * (Dv / a.block_v) + wcol / a.block_v] = pdS;
+      }
+    };
+
+    load_q(0);
+    dma(0, 0);
+    vm_drain();
+    lds_barrier();                                 // P
+
+    for (int c = 0; c < nchunks; ++c) {
+      const typename Sm::Buf& B = sm.buf[c & 1];
+      flush();
+      store_q();                                   // this chunk's Q: every wave is past the last one
+      const int cn = min(c + 1, nchunks - 1);
+      load_q(cn);
+      dma(cn, (c + 1) & 1);
+      lds_barrier();                               // M: codes and Vnew published
+
+      const float dS = scale_of(c);
+      // ---- O^T = dS exp(gamma) (Sc^T Q^T) + Vnew^T P^T, four token row tiles
+      f32x4 acc[4];
+      {
+        bf16x8 aS[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) aS[kk] = codes_bf16<SF>(sm.codes[kk][16 * cg + r16][grp]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          acc[mt] = zero4();
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc[mt] = mfma(aS[kk], ld_wq<DK>(sm.Q, 16 * mt + r16, kk, grp), acc[mt]);
+          const float f = dS * B.G[16 * mt + r16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] *= f;
+        }
+      }
+      {
+        bf16x8 aVh[2], aVl[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const f32x4 v0 = sm.vnx[cg][2 * t][lane], v1 = sm.vnx[cg][2 * t + 1][lane];
+          pack_pair_split(v0, v1, aVh[t], aVl[t]);
+        }
+        // under the lower-triangular P, row tiles 0 and 1 need k-step 0 only
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int kk = 0; kk <= (mt >> 1); ++kk) {
+            const bf16x8 ph = lds_nat(B.P, 16 * mt + r16, I::R64, 32 * kk, grp);
+            const bf16x8 pl = lds_nat(B.P + I::P1, 16 * mt + r16, I::R64, 32 * kk, grp);
+            acc[mt] = mfma(aVh[kk], ph, acc[mt]);
+            acc[mt] = mfma(aVl[kk], ph, acc[mt]);
+            acc[mt] = mfma(aVh[kk], pl, acc[mt]);
+          }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        bf16x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = to_bf16(a.scale * acc[mt][i]);
+        ov[mt] = __builtin_bit_cast(u32x2, o4);
+      }
+      // ---- saved state codes: 4x4 byte blocks (rows row0 + i, columns 4 q..4 q + 3)
+      if (a.s_codes) {
+#pragma unroll
+        for (int p = 0; p < CPL; ++p) {
+          const int cb = lane + 64 * p, q = cb & 3, g = (cb >> 2) & 3, hh = (cb >> 4) & 1, jj = cb >> 5;
+          uint32_t w[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x2 v = sm.codes[jj][16 * cg + 4 * q + m][g];
+            w[m] = hh ? v.y : v.x;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            cw[p][i] = ((w[0] >> (8 * i)) & 0xFFu) | (((w[1] >> (8 * i)) & 0xFFu) << 8) |
+                       (((w[2] >> (8 * i)) & 0xFFu) << 16) | (((w[3] >> (8 * i)) & 0xFFu) << 24);
+        }
+      }
+      pc = c;
+      pdS = dS;
+      vm_drain();                                  // next chunk's copies and Q landed
+      lds_barrier();                               // X
+    }
+    flush();
+  }
+}
+
+}  // namespace
+
+template <int DK, int SF, int WF>
+static hipError_t launch_split_one(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+  const int num_heads = cfg.N * cfg.Hv, nvb = cfg.Dv / 64;
+  const int64_t nblk = (int64_t)nvb * 8 * ((num_heads + 7) / 8);
+  hipLaunchKernelGGL((gdn_state_split_kernel<DK, SF, WF>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
+                     cfg.N, num_heads);
+  return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_split_dk(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+#define GDN_CASE(SFv, WFv) \
+  if (cfg.state_fmt == SFv && cfg.w_fmt == WFv) return launch_split_one<DK, SFv, WFv>(cfg, a, s);
+  GDN_CASE(1, 1) GDN_CASE(1, 2) GDN_CASE(2, 1) GDN_CASE(2, 2)
+#undef GDN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+  if (cfg.Dk == 128) return launch_split_dk<128>(cfg, a, s);
+  if (cfg.Dk == 64) return launch_split_dk<64>(cfg, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

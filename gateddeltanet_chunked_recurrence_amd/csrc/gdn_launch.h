@@ -41,8 +41,8 @@ hipError_t launch_fwd_fused(const FwdConfig& cfg, const FwdKernelArgs& a, hipStr
 hipError_t launch_fwd_prep(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
                            hipStream_t stream);
 hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
-// Both QDQ sites on: 8-wave variant of the state kernel (two waves per SIMD).
-hipError_t launch_fwd_state_pair(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
+// Both QDQ sites on: recurrence and output in separate waves (gdn_fwd_state_split.hip).
+hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
 
 struct BwdKernelArgs {
   FwdKernelArgs f;            // forward inputs + saved buffers (read only here)
