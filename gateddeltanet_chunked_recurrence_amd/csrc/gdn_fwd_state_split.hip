@@ -1,26 +1,29 @@
 // Forward state recurrence with both QDQ sites on ("[1/4] GDN state/W QAT
 // foundation", "What does this PR do?"; "[2/4] GDN/KDA decode QAT with INT8
 // recurrent state", "What does this PR do?": per-head [Dk, block_v] state
-// scales). One 8-wave workgroup per (sequence, value head, 64-wide value
-// block), in two roles that share the block's four 16-column groups:
-//   recurrence waves 0..3 (one per SIMD): wave w keeps columns [16 w, 16 w + 16)
-//     of the state, all Dk rows, in VGPRs for the whole sequence and runs only
-//     the chain the next chunk depends on:
+// scales). One 12-wave workgroup per (sequence, value head, 64-wide value
+// block), in three roles, one wave of each per SIMD:
+//   recurrence waves 0..3: wave w keeps columns [16 w, 16 w + 16) of the
+//     state, all Dk rows, in VGPRs for the whole sequence and runs only the
+//     chain the next chunk depends on:
 //       Sq = QDQ_S(S);  Vnew = U - dW dS (Wc Sc);
 //       S  = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew)
-//   output waves 4..7 (one per SIMD): wave 4 + w forms the output of the same
-//     columns from the published state codes and Vnew,
+//   output waves 4..7: wave 4 + w forms the output of the same columns from
+//     the published state codes and Vnew,
 //       O = scale (exp(gamma) dS (Q Sc) + P Vnew),
-//     writes the saved state codes, and stages the next chunk's operands.
-// Per chunk, two LDS barriers:
-//   recurrence: scale, QDQ, codes to LDS, W Sq, Vnew to LDS | M | K^T D, amax | X
-//   output:     last chunk's stores, Q to LDS, next copies issued | M | O, codes | X
+//     and writes the saved state codes;
+//   staging waves 8..11: this chunk's Q to LDS, the next chunk's image block
+//     and Q copied in (their issue stalls while the CU's memory pipeline is
+//     busy, which is why no other role issues them).
+// One workgroup barrier per chunk (X, at its end). Within a chunk the output
+// waves wait on LDS counters that the recurrence waves (codes, then Vnew) and
+// the staging waves (Q) raise after their LDS writes complete; the counters
+// only grow, and nothing the recurrence or staging waves do waits on the
+// output waves before X, so every wait ends. Each wait is also bounded.
 // The output products are computed transposed (O^T = Sc^T Q^T + Vnew^T P^T):
 // the published code and Vnew fragments are then A operands as they stand, and
 // a lane's accumulator holds four adjacent output columns of one token, which
-// leave as one 8-byte store. The output waves' global stores are issued at the
-// top of the next chunk, so the wait for the staged copies before barrier X
-// does not also wait for them.
+// leave as one 8-byte store.
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -29,7 +32,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int NT = 512;
+constexpr int NT = 768;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int DK>
@@ -48,7 +51,23 @@ struct SplitSmem {
   u32x2 codes[DK / 32][64][4];
   f32x4 vnx[4][4][64];                            // Vnew: column group, row tile, lane
   alignas(16) float red[2][4];                    // per-column-group state amax, by chunk parity
+  unsigned flag[3];                               // counters: codes, Vnew (recurrence), Q (staging)
 };
+
+// Raises an LDS counter once this wave's earlier LDS writes have completed.
+__device__ __forceinline__ void lds_signal(unsigned* flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt 0 (vmcnt, expcnt not waited)
+  if (__lane_id() == 0) __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Waits until an LDS counter reaches `target` (bounded: about 2^18 polls).
+__device__ __forceinline__ void lds_wait(unsigned* flag, unsigned target) {
+  for (int it = 0; it < (1 << 18); ++it) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Eight state codes (bytes) as bf16, exact: E4M3 codes have 4 significant
 // bits and INT8 codes at most 7.
@@ -76,7 +95,7 @@ __device__ __forceinline__ bf16x8 codes_bf16(u32x2 w) {
 }
 
 template <int DK, int SF, int WF>
-__global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(3, 3)))
 gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   static_assert(SF != 0 && WF != 0, "both QDQ sites on");
   using I = Img<DK>;
@@ -128,7 +147,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
 
   if (wave < 4) {
     // ======================= recurrence role =======================
-    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(3);
     // S[j][i] = S[16 j + 4 grp + i][wcol + r16]
     f32x4 S[MK];
     if (a.h0) {
@@ -173,6 +192,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       m = wave_max(m);
       if (lane == 0) sm.red[0][cg] = m;
     }
+    if (wave == 0 && lane < 3) sm.flag[lane] = 0;
     vm_drain();
     lds_barrier();                                 // P
 
@@ -180,10 +200,11 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       const typename Sm::Buf& B = sm.buf[c & 1];
       load_u(min(c + 1, nchunks - 1), Unext, dWnext);
       // operands read ahead of their products: the W fragments here, over the
-      // QDQ; the K^T fragments after W Sq is issued, over Vnew and barrier M
-      bf16x8 op[KS][4];
+      // QDQ; the K^T fragments after W Sq is issued, over Vnew
+      // (two k-steps ahead: three waves per SIMD leave 168 VGPRs per wave)
+      bf16x8 op[2][4];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) op[kk][mt] = ld_wq<DK>(B.W, 16 * mt + r16, kk, grp);
       const float dS = scale_of(c);
@@ -203,6 +224,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       }
 #pragma unroll
       for (int jj = 0; jj < KS; ++jj) sm.codes[jj][16 * cg + r16][grp] = u32x2{sb[2 * jj], sb[2 * jj + 1]};
+      lds_signal(&sm.flag[0]);
 
       // ---- W Sq over the four token row tiles
       f32x4 accw[4];
@@ -212,13 +234,14 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       for (int kk = 0; kk < KS; ++kk) {
         const bf16x8 b = pack_pair(S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) accw[mt] = mfma(op[kk][mt], b, accw[mt]);
+        for (int mt = 0; mt < 4; ++mt) accw[mt] = mfma(op[kk & 1][mt], b, accw[mt]);
+        if (kk + 2 < KS)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) op[kk & 1][mt] = ld_wq<DK>(B.W, 16 * mt + r16, kk + 2, grp);
       }
-      bf16x8 kop[2][MK];
+      bf16x8 kop[MK];                              // token k-step 0; k-step 1 reloads in place
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < MK; ++j) kop[t][j] = lds_nat(B.Kt, 16 * j + r16, I::R64, 32 * t, grp);
+      for (int j = 0; j < MK; ++j) kop[j] = lds_nat(B.Kt, 16 * j + r16, I::R64, 0, grp);
       f32x4 Vn[4];
       {
         const float sc = dWcur * dS;
@@ -234,7 +257,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       const f32x4 e1[2] = {*reinterpret_cast<const f32x4*>(&B.G[80 + 4 * grp]),
                            *reinterpret_cast<const f32x4*>(&B.G[112 + 4 * grp])};
       const float sdec = B.G[128] * dS;
-      lds_barrier();                               // M: codes and Vnew published
+      lds_signal(&sm.flag[1]);
 
       // ---- S = exp(gamma_n) Sq + K^T (exp(gamma_n - gamma) Vnew)
       bf16x8 bDh[2], bDl[2];
@@ -255,9 +278,12 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int j = 0; j < MK; ++j) S[j] = mfma(kop[t][j], bDh[t], S[j]);
+        for (int j = 0; j < MK; ++j) S[j] = mfma(kop[j], bDh[t], S[j]);
 #pragma unroll
-        for (int j = 0; j < MK; ++j) S[j] = mfma(kop[t][j], bDl[t], S[j]);
+        for (int j = 0; j < MK; ++j) {
+          S[j] = mfma(kop[j], bDl[t], S[j]);
+          if (t == 0) kop[j] = lds_nat(B.Kt, 16 * j + r16, I::R64, 32, grp);
+        }
       }
       {
         float m = 0.f;
@@ -275,88 +301,18 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       dWcur = dWnext;
     }
     store_ht();
-  } else {
+  } else if (wave < 8) {
     // ========================= output role =========================
     if (nchunks == 0) return;
-    const int otid = cg * 64 + lane;               // 0..255 over the output waves
-    constexpr int QPT = 64 * DK / 8 / 256;         // 16-byte Q pieces per lane
-    u32x4 qreg[QPT];
-    auto load_q = [&](int c) {
-      const bf16* qb = reinterpret_cast<const bf16*>(a.q);
-      const int t0 = chunk_t0(c), nc = chunk_nc(c);
-#pragma unroll
-      for (int p = 0; p < QPT; ++p) {
-        const int e = otid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
-        qreg[p] = *reinterpret_cast<const u32x4*>(qb + ((int64_t)(t0 + min(row, nc - 1)) * a.Hqk + hk) * DK + 8 * c8);
-      }
-    };
-    auto store_q = [&]() {
-#pragma unroll
-      for (int p = 0; p < QPT; ++p) {
-        const int e = otid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
-        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8))]) = qreg[p].xy;
-        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = qreg[p].zw;
-      }
-    };
-    constexpr int NINS = IMGP / 64;               // wave loads per image block
-    constexpr int KW = (NINS + 3) / 4;            // ... per output wave
-    static_assert(IMGP % 64 == 0, "whole wave loads");
-    auto dma = [&](int c, int b) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
-      uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].W);
-#pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        const int j = min(cg + 4 * k, NINS - 1);  // a repeated last load rewrites the same bytes
-        __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
-      }
-    };
-    // stores held over to the next chunk: the output rows of the four row
-    // tiles (four bf16 each) and the saved code words
+    __builtin_amdgcn_s_setprio(1);
     constexpr int CPL = DK / 64;                   // 4x4 code blocks per lane
-    u32x2 ov[4];
-    uint32_t cw[CPL][4];
-    int pc = -1;                                   // chunk whose stores are pending
-    float pdS = 0.f;
-    auto flush = [&]() {
-      if (pc < 0) return;
-      const int t0 = chunk_t0(pc), nc = chunk_nc(pc);
-      const int64_t ch = chunk_ch(pc);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int tok = 16 * mt + r16;
-        if (tok < nc) {
-          bf16* op = reinterpret_cast<bf16*>(a.o) + ((int64_t)(t0 + tok) * Hv + h) * Dv + wcol + 4 * grp;
-          *reinterpret_cast<u32x2*>(op) = ov[mt];
-        }
-      }
-      if (a.s_codes) {
-        uint8_t* sbase = a.s_codes + ch * DK * Dv + wcol;
-#pragma unroll
-        for (int p = 0; p < CPL; ++p) {
-          const int cb = lane + 64 * p, q = cb & 3, g = (cb >> 2) & 3, hh = (cb >> 4) & 1, jj = cb >> 5;
-          const int row0 = 32 * jj + 16 * hh + 4 * g;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint32_t*>(sbase + (int64_t)(row0 + i) * Dv + 4 * q) = cw[p][i];
-        }
-        if (cg == g0 && lane == 0) a.s_scale[ch * (Dv / a.block_v) + wcol / a.block_v] = pdS;
-      }
-    };
-
-    load_q(0);
-    dma(0, 0);
-    vm_drain();
     lds_barrier();                                 // P
-
     for (int c = 0; c < nchunks; ++c) {
       const typename Sm::Buf& B = sm.buf[c & 1];
-      flush();
-      store_q();                                   // this chunk's Q: every wave is past the last one
-      const int cn = min(c + 1, nchunks - 1);
-      load_q(cn);
-      dma(cn, (c + 1) & 1);
-      lds_barrier();                               // M: codes and Vnew published
-
+      const int t0 = chunk_t0(c), nc = chunk_nc(c);
+      const int64_t ch = chunk_ch(c);
+      lds_wait(&sm.flag[0], 4u * (c + 1));        // this chunk's codes
+      lds_wait(&sm.flag[2], 4u * (c + 1));        // this chunk's Q
       const float dS = scale_of(c);
       // ---- O^T = dS exp(gamma) (Sc^T Q^T) + Vnew^T P^T, four token row tiles
       f32x4 acc[4];
@@ -374,6 +330,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
           for (int i = 0; i < 4; ++i) acc[mt][i] *= f;
         }
       }
+      lds_wait(&sm.flag[1], 4u * (c + 1));        // this chunk's Vnew
       {
         bf16x8 aVh[2], aVl[2];
 #pragma unroll
@@ -395,16 +352,22 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        const int tok = 16 * mt + r16;
         bf16x4 o4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o4[i] = to_bf16(a.scale * acc[mt][i]);
-        ov[mt] = __builtin_bit_cast(u32x2, o4);
+        if (tok < nc) {
+          bf16* op = reinterpret_cast<bf16*>(a.o) + ((int64_t)(t0 + tok) * Hv + h) * Dv + wcol + 4 * grp;
+          *reinterpret_cast<u32x2*>(op) = __builtin_bit_cast(u32x2, o4);
+        }
       }
       // ---- saved state codes: 4x4 byte blocks (rows row0 + i, columns 4 q..4 q + 3)
       if (a.s_codes) {
+        uint8_t* sbase = a.s_codes + ch * DK * Dv + wcol;
 #pragma unroll
         for (int p = 0; p < CPL; ++p) {
           const int cb = lane + 64 * p, q = cb & 3, g = (cb >> 2) & 3, hh = (cb >> 4) & 1, jj = cb >> 5;
+          const int row0 = 32 * jj + 16 * hh + 4 * g;
           uint32_t w[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -413,16 +376,63 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            cw[p][i] = ((w[0] >> (8 * i)) & 0xFFu) | (((w[1] >> (8 * i)) & 0xFFu) << 8) |
-                       (((w[2] >> (8 * i)) & 0xFFu) << 16) | (((w[3] >> (8 * i)) & 0xFFu) << 24);
+            *reinterpret_cast<uint32_t*>(sbase + (int64_t)(row0 + i) * Dv + 4 * q) =
+                ((w[0] >> (8 * i)) & 0xFFu) | (((w[1] >> (8 * i)) & 0xFFu) << 8) |
+                (((w[2] >> (8 * i)) & 0xFFu) << 16) | (((w[3] >> (8 * i)) & 0xFFu) << 24);
         }
+        if (cg == g0 && lane == 0) a.s_scale[ch * (Dv / a.block_v) + wcol / a.block_v] = dS;
       }
-      pc = c;
-      pdS = dS;
+      lds_barrier();                               // X
+    }
+  } else {
+    // ========================= staging role =========================
+    if (nchunks == 0) return;
+    __builtin_amdgcn_s_setprio(2);
+    const int stid = cg * 64 + lane;               // 0..255 over the staging waves
+    constexpr int QPT = 64 * DK / 8 / 256;         // 16-byte Q pieces per lane
+    u32x4 qreg[QPT];
+    auto load_q = [&](int c) {
+      const bf16* qb = reinterpret_cast<const bf16*>(a.q);
+      const int t0 = chunk_t0(c), nc = chunk_nc(c);
+#pragma unroll
+      for (int p = 0; p < QPT; ++p) {
+        const int e = stid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
+        qreg[p] = *reinterpret_cast<const u32x4*>(qb + ((int64_t)(t0 + min(row, nc - 1)) * a.Hqk + hk) * DK + 8 * c8);
+      }
+    };
+    auto store_q = [&]() {
+#pragma unroll
+      for (int p = 0; p < QPT; ++p) {
+        const int e = stid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
+        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8))]) = qreg[p].xy;
+        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = qreg[p].zw;
+      }
+    };
+    constexpr int NINS = IMGP / 64;               // wave loads per image block
+    constexpr int KW = (NINS + 3) / 4;            // ... per staging wave
+    static_assert(IMGP % 64 == 0, "whole wave loads");
+    auto dma = [&](int c, int b) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
+      uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].W);
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        const int j = min(cg + 4 * k, NINS - 1);  // a repeated last load rewrites the same bytes
+        __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
+      }
+    };
+    load_q(0);
+    dma(0, 0);
+    vm_drain();
+    lds_barrier();                                 // P
+    for (int c = 0; c < nchunks; ++c) {
+      store_q();                                   // this chunk's Q: the output waves are past the last one
+      lds_signal(&sm.flag[2]);
+      const int cn = min(c + 1, nchunks - 1);
+      load_q(cn);
+      dma(cn, (c + 1) & 1);
       vm_drain();                                  // next chunk's copies and Q landed
       lds_barrier();                               // X
     }
-    flush();
   }
 }
 
