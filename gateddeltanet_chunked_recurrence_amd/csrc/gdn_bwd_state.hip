@@ -49,7 +49,7 @@ template <int DK>
 struct BImg {
   using I = Img<DK>;
   static constexpr int KI = I::WQ;                 // K image [64][RS]
-  static constexpr int WT = I::KT;                 // one W^T plane [DK][72]
+  static constexpr int WT = DK * I::R64;           // one W^T plane [DK][72]
   static constexpr int GB = 512;                   // gate block, 256 FP32
   static constexpr int size(int nw) { return KI + nw * WT + GB; }
   static constexpr int g_at(int nw) { return KI + nw * WT; }

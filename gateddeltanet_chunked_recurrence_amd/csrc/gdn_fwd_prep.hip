@@ -39,13 +39,13 @@ struct PrepSmem {
     struct { bf16 K[64 * LDK]; bf16 Q[64 * LDK]; } kq;   // until the L / P tiles
     bf16 Vt[256 * 72];                                    // V^T (pperm over tokens)
   } a;
-  bf16 Kt[DK * 72];                              // K^T (pperm over tokens)
+  bf16 Kt[DK * 64];                              // K^T (pperm over tokens, r64_off)
   union {
     struct { float L[64 * 65]; float X[64 * 65]; } s;    // solve
     bf16 W[2 * Img<DK>::WQ];                              // W image planes
   } b;
   union {
-    bf16 P[2][64 * 72];                          // P hi / lo, until copied out
+    bf16 P[2][64 * 64];                          // P hi / lo (r64_off), until copied out
     float Y[32 * 33];                            // 32-block merge scratch
     bf16 T[4][64 * 72];                          // T hi, T lo, T' hi, T' lo
   } c;
@@ -122,7 +122,9 @@ struct Stage {
     const uint4 v = TPG * tg(lane) + p < nc ? raw[p] : z;
     return *reinterpret_cast<const bf16x8*>(&v);
   }
-  // dst[(8 c8 + j) * 72 + pperm(token)]; also to gdst if given
+  // dst[(8 c8 + j) * 72 + pperm(token)] (or the unpadded r64_off layout when
+  // R64S); also to gdst if given
+  template <bool R64S = false>
   __device__ void store_t(bf16* dst, bf16* gdst, int wave, int lane) const {
     bf16x8 r[TPG];
 #pragma unroll
@@ -130,8 +132,9 @@ struct Stage {
     const int t0 = TPG * tg(lane), col0 = 8 * c8(wave, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      bf16* d = dst + (col0 + j) * 72 + pperm(t0);
-      bf16* g = gdst ? gdst + (col0 + j) * 72 + pperm(t0) : nullptr;
+      const int off = R64S ? r64_off(col0 + j, pperm(t0)) : (col0 + j) * 72 + pperm(t0);
+      bf16* d = dst + off;
+      bf16* g = gdst ? gdst + off : nullptr;
       if constexpr (TPG == 1) {
         *d = r[0][j];
         if (g) *g = r[0][j];
@@ -250,11 +253,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     // P upper tiles (0, 1) and (2, 3) are read as zeros by the state kernel
     for (int e = tid; e < 2 * 2 * 256; e += NT) {
       const int pl = e >> 9, t = (e >> 8) & 1, r = (e >> 4) & 15, cc = e & 15;
-      sm.c.P[pl][(32 * t + r) * 72 + pperm(32 * t + 16 + cc)] = to_bf16(0.f);
+      sm.c.P[pl][r64_off(32 * t + r, pperm(32 * t + 16 + cc))] = to_bf16(0.f);
     }
     ks.store_rows(sm.a.kq.K, LDK, wave, lane);
     qs.store_rows(sm.a.kq.Q, LDK, wave, lane);
-    ks.store_t(sm.Kt, nullptr, wave, lane);       // the image copy goes out during the solve
+    ks.template store_t<true>(sm.Kt, nullptr, wave, lane);   // the image copy goes out during the solve
     if (wave == 0) {
       const float gv = lane < nc ? graw : 0.f;
       const float g2 = wave_incl_scan(gv * LOG2E, lane);
@@ -305,8 +308,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
           const float pv = row >= cj ? acc[i] * fexp2(gr - sm.gam2[cj]) : 0.f;
           split2(pv, hi[i], lo[i]);
         }
-        st4(&sm.c.P[0][row * 72 + pperm(c0)], hi[0], hi[1], hi[2], hi[3]);
-        st4(&sm.c.P[1][row * 72 + pperm(c0)], lo[0], lo[1], lo[2], lo[3]);
+        st4(&sm.c.P[0][r64_off(row, pperm(c0))], hi[0], hi[1], hi[2], hi[3]);
+        st4(&sm.c.P[1][r64_off(row, pperm(c0))], lo[0], lo[1], lo[2], lo[3]);
       }
     }
     lds_barrier();
@@ -461,7 +464,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (kk > mt / 2) continue;              // T' is lower triangular
-          const bf16x8 b = lds_nat(sm.Kt, 16 * ct + r16, 72, 32 * kk, grp);
+          const bf16x8 b = ld_r64(sm.Kt, 16 * ct + r16, 32 * kk, grp);
           acc = mfma(ah[kk], b, acc);
           acc = mfma(al[kk], b, acc);
         }

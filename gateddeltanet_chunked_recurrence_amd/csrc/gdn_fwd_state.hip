@@ -331,8 +331,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (kk > mt / 2) continue;              // P is lower triangular
-          ph[mt][kk] = lds_nat(B.P, 16 * mt + r16, I::R64, 32 * kk, grp);
-          pl[mt][kk] = lds_nat(B.P + I::P1, 16 * mt + r16, I::R64, 32 * kk, grp);
+          ph[mt][kk] = ld_r64(B.P, 16 * mt + r16, 32 * kk, grp);
+          pl[mt][kk] = ld_r64(B.P + I::P1, 16 * mt + r16, 32 * kk, grp);
         }
       bf16* ot = sm.ost[wave];
 #pragma unroll
@@ -369,7 +369,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int mt = 0; mt < MK; ++mt) kop[kk][mt] = lds_nat(B.Kt, 16 * mt + r16, I::R64, 32 * kk, grp);
+        for (int mt = 0; mt < MK; ++mt) kop[kk][mt] = ld_r64(B.Kt, 16 * mt + r16, 32 * kk, grp);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll

@@ -54,11 +54,14 @@ struct SplitSmem {
   unsigned flag[3];                               // counters: codes, Vnew (recurrence), Q (staging)
 };
 
-// Raises an LDS counter once this wave's earlier LDS writes have completed.
+// Raises an LDS counter after this wave's earlier LDS writes. The LDS executes
+// one wave's operations in issue order, so the increment lands after the data
+// without a wait; the fence keeps the compiler from moving LDS accesses
+// across it.
 __device__ __forceinline__ void lds_signal(unsigned* flag) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt 0 (vmcnt, expcnt not waited)
   if (__lane_id() == 0) __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 // Waits until an LDS counter reaches `target` (bounded: about 2^18 polls).
 __device__ __forceinline__ void lds_wait(unsigned* flag, unsigned target) {
@@ -241,7 +244,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       }
       bf16x8 kop[MK];                              // token k-step 0; k-step 1 reloads in place
 #pragma unroll
-      for (int j = 0; j < MK; ++j) kop[j] = lds_nat(B.Kt, 16 * j + r16, I::R64, 0, grp);
+      for (int j = 0; j < MK; ++j) kop[j] = ld_r64(B.Kt, 16 * j + r16, 0, grp);
       f32x4 Vn[4];
       {
         const float sc = dWcur * dS;
@@ -282,7 +285,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
 #pragma unroll
         for (int j = 0; j < MK; ++j) {
           S[j] = mfma(kop[j], bDl[t], S[j]);
-          if (t == 0) kop[j] = lds_nat(B.Kt, 16 * j + r16, I::R64, 32, grp);
+          if (t == 0) kop[j] = ld_r64(B.Kt, 16 * j + r16, 32, grp);
         }
       }
       {
@@ -304,7 +307,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   } else if (wave < 8) {
     // ========================= output role =========================
     if (nchunks == 0) return;
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(2);
     constexpr int CPL = DK / 64;                   // 4x4 code blocks per lane
     lds_barrier();                                 // P
     for (int c = 0; c < nchunks; ++c) {
@@ -343,8 +346,8 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int kk = 0; kk <= (mt >> 1); ++kk) {
-            const bf16x8 ph = lds_nat(B.P, 16 * mt + r16, I::R64, 32 * kk, grp);
-            const bf16x8 pl = lds_nat(B.P + I::P1, 16 * mt + r16, I::R64, 32 * kk, grp);
+            const bf16x8 ph = ld_r64(B.P, 16 * mt + r16, 32 * kk, grp);
+            const bf16x8 pl = ld_r64(B.P + I::P1, 16 * mt + r16, 32 * kk, grp);
             acc[mt] = mfma(aVh[kk], ph, acc[mt]);
             acc[mt] = mfma(aVl[kk], ph, acc[mt]);
             acc[mt] = mfma(aVh[kk], pl, acc[mt]);
@@ -387,7 +390,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   } else {
     // ========================= staging role =========================
     if (nchunks == 0) return;
-    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(1);
     const int stid = cg * 64 + lane;               // 0..255 over the staging waves
     constexpr int QPT = 64 * DK / 8 / 256;         // 16-byte Q pieces per lane
     u32x4 qreg[QPT];

@@ -7,9 +7,11 @@
 //   W image  [64][DK] bf16 per plane: W^q codes (one plane) or W as hi + lo
 //            (two planes), paired order along dk (pperm), 16-byte chunks
 //            XOR-swizzled by row for DK = 128 (rows padded to 72 for DK = 64)
-//   K^T image [DK][72] bf16: K transposed, paired order along tokens
-//   P image  2 x [64][72] bf16: (Q K^T) * Gam as hi + lo, paired order along
+//   K^T image [DK][64] bf16: K transposed, paired order along tokens
+//   P image  2 x [64][64] bf16: (Q K^T) * Gam as hi + lo, paired order along
 //            the key token; upper 16x16 tiles zero
+//            (both [*][64] images unpadded, 16-byte pieces XOR-swizzled by
+//            row, see r64_off)
 //   U        FP32 in accumulator-fragment order: for value block vb, wave w,
 //            row tile mt and lane l the four values U[16 mt + 4 (l >> 4) + i]
 //            [64 vb + 16 w + (l & 15)], i = 0..3, contiguous
@@ -29,10 +31,10 @@ template <int DK>
 struct Img {
   static constexpr int RS = DK == 128 ? 128 : 72;   // row stride of [64][DK] images
   static constexpr int SWZ = DK == 128 ? 15 : 0;    // 16-byte chunk swizzle mask
-  static constexpr int R64 = 72;                    // row stride of [*][64] images
+  static constexpr int R64 = 72;                    // row stride of padded [*][64] tiles
   static constexpr int WQ = 64 * RS;                // elements of one [64][DK] plane
-  static constexpr int KT = DK * R64;               // elements of the K^T image
-  static constexpr int P1 = 64 * R64;               // elements of one P plane
+  static constexpr int KT = DK * 64;                // elements of the K^T image (r64_off)
+  static constexpr int P1 = 64 * 64;                // elements of one P plane (r64_off)
   static constexpr int GB = 512;                    // gate block: 256 FP32 (1 KB)
   // one (slot, head) block: [W planes | K^T | P hi, P lo | gates], contiguous
   template <int NW> static constexpr int img() { return NW * WQ + KT + 2 * P1 + GB; }
@@ -46,6 +48,18 @@ template <int DK>
 __device__ __forceinline__ int wq_off(int row, int s) {
   using I = Img<DK>;
   return row * I::RS + ((((s >> 3) ^ (row & I::SWZ))) << 3) + (s & 7);
+}
+
+// Element offset of stored (pperm) position s in row `row` of an unpadded
+// [*][64] image: row r's 16-byte pieces are XOR-swizzled by (r >> 1) & 7, so
+// the 16 rows of one operand fragment read at one piece position hit 16
+// distinct 16-byte bank groups (two 128-byte rows span all 64 banks).
+__device__ __forceinline__ int r64_off(int row, int s) {
+  return row * 64 + ((((s >> 3) ^ ((row >> 1) & 7))) << 3) + (s & 7);
+}
+// Operand fragment (row `row`, stored positions k0 + 8 grp..+7) of such an image.
+__device__ __forceinline__ bf16x8 ld_r64(const bf16* img, int row, int k0, int grp) {
+  return *reinterpret_cast<const bf16x8*>(img + r64_off(row, k0 + 8 * grp));
 }
 
 // A-operand fragment (16 rows from `row0`, stored K positions 32 kk + 8 grp..+7)
