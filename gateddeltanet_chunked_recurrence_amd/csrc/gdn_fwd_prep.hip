@@ -174,15 +174,21 @@ __device__ PrepItem prep_item(const FwdKernelArgs& a, int N, int i) {
   it.i = i;
   it.slot = i / a.Hv;
   it.h = i % a.Hv;
-  // sequence of this slot (slot = n + bos_n / 64 + c, increasing in n)
+  // sequence of this slot (slot = n + bos_n / 64 + c, increasing in n).
+  // cu_seqlens is read through the constant address space: the item index is
+  // wave-uniform, so these become scalar loads, which no vector-memory wait
+  // covers (a vector load here made every item start by waiting for the
+  // previous item's stores)
+  typedef const int32_t __attribute__((address_space(4)))* cptr;
+  const cptr cu = (cptr)a.cu_seqlens;
   int lo = 0, hi = N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int bos = a.cu_seqlens ? a.cu_seqlens[mid] : mid * a.T;
+    const int bos = cu ? cu[mid] : mid * a.T;
     if (mid + bos / CHUNK <= it.slot) lo = mid; else hi = mid - 1;
   }
-  const int bos = a.cu_seqlens ? a.cu_seqlens[lo] : lo * a.T;
-  const int eos = a.cu_seqlens ? a.cu_seqlens[lo + 1] : (lo + 1) * a.T;
+  const int bos = cu ? cu[lo] : lo * a.T;
+  const int eos = cu ? cu[lo + 1] : (lo + 1) * a.T;
   const int c = it.slot - (lo + bos / CHUNK);
   it.t0 = bos + CHUNK * c;
   it.valid = c >= 0 && it.t0 < eos;               // some slots are used by no chunk

@@ -116,6 +116,11 @@ SMALL = [
     ('varlen_int8_gqa4x16_d128', dict(lengths=[200, 64], Hqk=1, Hv=2, state_fmt=OFF, w_fmt=E4M3,
                                       Dv=64)),
     ('long_e4m3_t65536_h32_dk128_dv256', dict(T=1000, Hqk=2, Hv=2)),
+    # mixed formats at the two sites (each state-kernel format pair is covered)
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=260, Hqk=1, Hv=2, state_fmt=INT8, w_fmt=E4M3,
+                                        h0=True)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=199, Hqk=1, Hv=2, state_fmt=E4M3, w_fmt=INT8,
+                                        Dk=64, Dv=128, block_v=32)),
 ]
 
 
