@@ -307,7 +307,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   } else if (wave < 8) {
     // ========================= output role =========================
     if (nchunks == 0) return;
-    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(3);
     constexpr int CPL = DK / 64;                   // 4x4 code blocks per lane
     lds_barrier();                                 // P
     for (int c = 0; c < nchunks; ++c) {

@@ -81,8 +81,8 @@ def test_forward_workspace_is_sized_and_required():
     a = _args()
     n = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
     slots = 1 + 2                                       # N + ceil(128 / 64)
-    # W codes, K^T, P hi/lo (bf16), gate block (1 KB), U (FP32), W scale
-    per = 64 * 128 * 2 + 128 * 72 * 2 + 2 * 64 * 72 * 2 + 1024 + 128 * 64 * 4 + 4
+    # W codes, K^T, P hi/lo (bf16, K^T and P rows unpadded), gate block (1 KB), U (FP32), W scale
+    per = 64 * 128 * 2 + 128 * 64 * 2 + 2 * 64 * 64 * 2 + 1024 + 128 * 64 * 4 + 4
     assert n >= slots * 4 * per and n <= slots * 4 * per + 3 * 256
     assert lib.gdn_chunk_fwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
     assert 'workspace' in lib.gdn_last_error().decode()
