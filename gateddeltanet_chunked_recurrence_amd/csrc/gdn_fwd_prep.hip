@@ -357,13 +357,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       for (int r = 0; r < 16; ++r) sm.b.s.X[(16 * b + r) * 65 + 16 * b + cc] = x[r];
     } else {
       const int t = tid - 64;
-      const uint4* src = reinterpret_cast<const uint4*>(&sm.c.P[0][0]);
-      uint4* dst = reinterpret_cast<uint4*>(img + I::template p_at<NW>());
-      for (int e = t; e < 2 * I::P1 / 8; e += NT - 64) dst[e] = src[e];
-      // K^T image: 16-byte copies of the LDS tile (K^T and P are adjacent in the image)
+      // K^T and P images: 16-byte copies of the LDS tiles (adjacent in the
+      // image, as they are in LDS), fixed trip counts
+      static_assert(sizeof(sm.c.P) == 2 * I::P1 * 2, "P tile is the image's P section");
+      constexpr int NKP = (I::KT + 2 * I::P1) / 8, NCP = (NKP + NT - 65) / (NT - 64);
       const uint4* ksrc = reinterpret_cast<const uint4*>(&sm.Kt[0]);
+      const uint4* psrc = reinterpret_cast<const uint4*>(&sm.c.P[0][0]);
       uint4* kdst = reinterpret_cast<uint4*>(img + I::template kt_at<NW>());
-      for (int e = t; e < I::KT / 8; e += NT - 64) kdst[e] = ksrc[e];
+#pragma unroll
+      for (int k = 0; k < NCP; ++k) {
+        const int e = t + (NT - 64) * k;
+        if (e < NKP) kdst[e] = e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8];
+      }
       for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
         const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
         const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
@@ -463,6 +468,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         ah[kk] = lds_nat(sm.c.T[2], 16 * mt + r16, 72, 32 * kk, grp);
         al[kk] = lds_nat(sm.c.T[3], 16 * mt + r16, 72, 32 * kk, grp);
       }
+      // computed transposed (W^T = K^T T'^T, the same fragments with A and B
+      // swapped): a lane then holds four adjacent dk of one token, which go
+      // to LDS as one 8-byte write
 #pragma unroll
       for (int d = 0; d < NCTW; ++d) {
         const int ct = ct0 + d;
@@ -471,10 +479,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         for (int kk = 0; kk < 2; ++kk) {
           if (kk > mt / 2) continue;              // T' is lower triangular
           const bf16x8 b = ld_r64(sm.Kt, 16 * ct + r16, 32 * kk, grp);
-          acc = mfma(ah[kk], b, acc);
-          acc = mfma(al[kk], b, acc);
+          acc = mfma(b, ah[kk], acc);
+          acc = mfma(b, al[kk], acc);
         }
-        Wt[d] = acc;
+        Wt[d] = acc;                              // W[16 mt + r16][16 ct + 4 grp + i]
       }
     }
     if constexpr (WF != 0) {
@@ -529,31 +537,24 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         rW = 1.0f / dW;
       }
       const bool save = WF != 0 && a.w_codes != nullptr;
+      const int tok = 16 * mt + r16;
 #pragma unroll
       for (int d = 0; d < NCTW; ++d) {
-        const int col = 16 * (ct0 + d) + r16, s = pperm(col);
-        const int row0 = 16 * mt + 4 * grp;
+        const int dk0 = 16 * (ct0 + d) + 4 * grp, o = wq_off<DK>(tok, pperm(dk0));   // dk0..dk0 + 3 adjacent
         const float w[4] = {Wt[d][0], Wt[d][1], Wt[d][2], Wt[d][3]};
         if constexpr (WF != 0) {
           float cq[4];
           uint32_t bytes;
           quant4<WF>(w, rW, cq, bytes);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm.b.W[wq_off<DK>(row0 + i, s)] = to_bf16(cq[i]);
-          if (save) {
-            uint8_t* wp = a.w_codes + ((int64_t)t0 * Hv + h) * DK + col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (row0 + i < nc) wp[(int64_t)(row0 + i) * Hv * DK] = (bytes >> (8 * i)) & 0xFFu;
-          }
+          st4(&sm.b.W[o], to_bf16(cq[0]), to_bf16(cq[1]), to_bf16(cq[2]), to_bf16(cq[3]));
+          if (save && tok < nc)
+            *reinterpret_cast<uint32_t*>(a.w_codes + ((int64_t)(t0 + tok) * Hv + h) * DK + dk0) = bytes;
         } else {
+          bf16 hi[4], lo[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bf16 hi, lo;
-            split2(w[i], hi, lo);
-            sm.b.W[wq_off<DK>(row0 + i, s)] = hi;
-            sm.b.W[I::WQ + wq_off<DK>(row0 + i, s)] = lo;
-          }
+          for (int i = 0; i < 4; ++i) split2(w[i], hi[i], lo[i]);
+          st4(&sm.b.W[o], hi[0], hi[1], hi[2], hi[3]);
+          st4(&sm.b.W[I::WQ + o], lo[0], lo[1], lo[2], lo[3]);
         }
       }
       if (tid == 0) {
@@ -566,7 +567,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     {
       const uint4* src = reinterpret_cast<const uint4*>(sm.b.W);
       uint4* dst = reinterpret_cast<uint4*>(img);
-      for (int e = tid; e < NW * I::WQ / 8; e += NT) dst[e] = src[e];
+      constexpr int NWP = NW * I::WQ / 8;          // 16-byte pieces of the W planes
+#pragma unroll
+      for (int k = 0; k < (NWP + NT - 1) / NT; ++k)
+        if (NWP % NT == 0 || tid + NT * k < NWP) dst[tid + NT * k] = src[tid + NT * k];
     }
     lds_barrier();                              // LDS is reused by the next item
     if (!nxt.valid) break;
