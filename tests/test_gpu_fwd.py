@@ -121,6 +121,9 @@ SMALL = [
                                         h0=True)),
     ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=199, Hqk=1, Hv=2, state_fmt=E4M3, w_fmt=INT8,
                                         Dk=64, Dv=128, block_v=32)),
+    # one 64-wide value block per head, varlen with short and empty-tail sequences
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[130, 64, 1, 65], Hqk=1, Hv=2, Dv=64,
+                                      state_fmt=E4M3, w_fmt=E4M3, block_v=64, h0=True)),
 ]
 
 
