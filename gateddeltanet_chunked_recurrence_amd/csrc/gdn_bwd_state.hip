@@ -299,20 +299,22 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
 }
 
 // ---------------------------------------------------------------- bwd_state
-// WG waves per workgroup, each owning 16 value columns: the columns are
-// independent here, so a (sequence, head) can spread over several compute
-// units, which share its image block through the XCD's L2. A chunk step moves
-// the image block plus 28 KB per wave through the compute unit's vector memory
-// path, which bounds the step when four waves share one.
+// WG waves per workgroup, each owning 16 value columns, plus one staging wave:
+// the columns are independent here, so a (sequence, head) can spread over
+// several compute units, which share its image block through the XCD's L2. A
+// chunk step moves the image block plus 28 KB per column wave through the
+// compute unit's vector memory path, which bounds the step when four waves
+// share one. The image copies are issued by the staging wave alone: issuing
+// them stalls the issuing wave while the memory path is busy, and the column
+// waves carry the recurrence.
 template <int DK, int NW, int WG>
-__global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, int N, int num_heads) {
+__global__ void __launch_bounds__(64 * (WG + 1), 1) bwd_state_kernel(BwdKernelArgs a, int N, int num_heads) {
   using BI = BImg<DK>;
   using I = Img<DK>;
   constexpr int MK = DK / 16;
   constexpr int SZ = BI::size(NW);
   static_assert((SZ / 8) % 64 == 0, "image block is a whole number of wave loads");
-  constexpr int NINS = SZ / 8 / 64;                // 1 KB wave loads per block
-  constexpr int KW = (NINS + WG - 1) / WG;         // per wave
+  constexpr int NINS = SZ / 8 / 64;                // 1 KB wave loads per block, all from the staging wave
   __shared__ __align__(16) bf16 buf[2][SZ];
 
   const FwdKernelArgs& f = a.f;
@@ -334,6 +336,27 @@ __global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, 
   const int slot0 = n + bos / CHUNK;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
   const int r16 = lane & 15, grp = lane >> 4;
+  auto chunk_ch = [&](int c) { return (int64_t)(slot0 + c) * Hv + h; };
+  if (wave == WG) {
+    // ---- staging wave: the image block of each chunk, one chunk ahead
+    auto dma = [&](int c, int b) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.ws_bimg + chunk_ch(c) * SZ);
+      u32x4* dst = reinterpret_cast<u32x4*>(buf[b]);
+#pragma unroll
+      for (int j = 0; j < NINS; ++j) __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
+    };
+    if (nchunks > 0) {
+      dma(nchunks - 1, (nchunks - 1) & 1);
+      vm_drain();
+      lds_barrier();
+    }
+    for (int c = nchunks - 1; c >= 0; --c) {
+      if (c > 0) dma(c - 1, (c - 1) & 1);
+      vm_drain();                                 // staging of chunk c - 1 landed
+      lds_barrier();
+    }
+    return;
+  }
   const int cgi = g * WG + wave;                   // 16-column group of this wave
   const int vb = cgi >> 2, wq = cgi & 3;           // its 64-wide block and place in it
   const int wcol = 16 * cgi;
@@ -347,16 +370,6 @@ __global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, 
     for (int i = 0; i < 4; ++i)
       dS[mt][i] = a.dht ? a.dht[sbase + (int64_t)(16 * mt + 4 * grp + i) * Dv + wcol + r16] : 0.f;
 
-  auto chunk_ch = [&](int c) { return (int64_t)(slot0 + c) * Hv + h; };
-  auto dma = [&](int c, int b) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.ws_bimg + chunk_ch(c) * SZ);
-    u32x4* dst = reinterpret_cast<u32x4*>(buf[b]);
-#pragma unroll
-    for (int k = 0; k < KW; ++k) {
-      const int j = min(wave + WG * k, NINS - 1);
-      __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
-    }
-  };
   f32x4 A1c[4], A1n[4], A2c[MK], A2n[MK];
   auto load_a = [&](int c, f32x4 (&A1)[4], f32x4 (&A2)[MK]) {
     const int64_t ch = chunk_ch(c);
@@ -369,7 +382,6 @@ __global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, 
   };
 
   if (nchunks > 0) {
-    dma(nchunks - 1, (nchunks - 1) & 1);
     load_a(nchunks - 1, A1c, A2c);
     vm_drain();
     lds_barrier();
@@ -382,10 +394,7 @@ __global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, 
 #pragma unroll
     for (int mt = 0; mt < MK; ++mt)
       *reinterpret_cast<f32x4*>(a.ws_dstate + frag_off(ch, NVB, vb, wq, MK, mt, lane)) = dS[mt];
-    if (c > 0) {
-      dma(c - 1, (c - 1) & 1);
-      load_a(c - 1, A1n, A2n);
-    }
+    if (c > 0) load_a(c - 1, A1n, A2n);
     // dS' as B operands (paired order over dk), hi + lo
     bf16x8 bSh[MK / 2], bSl[MK / 2];
 #pragma unroll
@@ -442,7 +451,7 @@ __global__ void __launch_bounds__(64 * WG, 1) bwd_state_kernel(BwdKernelArgs a, 
           dS[mt] = mfma(al, bVh[kk], dS[mt]);
         }
       }
-    vm_drain();                                   // staging of chunk c - 1 landed
+    vm_drain();                                   // this wave's loads of chunk c - 1 landed
     lds_barrier();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) A1c[mt] = A1n[mt];
@@ -483,7 +492,7 @@ template <int DK, int NW, int WG>
 static hipError_t launch_state_wg(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
   const int num_heads = c.N * c.Hv, gh = c.Dv / 16 / WG;
   const int64_t nblk = (int64_t)gh * 8 * ((num_heads + 7) / 8);
-  hipLaunchKernelGGL((bwd_state_kernel<DK, NW, WG>), dim3((unsigned)nblk), dim3(64 * WG), 0, s, a,
+  hipLaunchKernelGGL((bwd_state_kernel<DK, NW, WG>), dim3((unsigned)nblk), dim3(64 * (WG + 1)), 0, s, a,
                      c.N, num_heads);
   return hipGetLastError();
 }
