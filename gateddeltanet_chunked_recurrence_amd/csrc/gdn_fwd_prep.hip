@@ -95,8 +95,10 @@ __device__ __forceinline__ void st4(bf16* dst, bf16 a, bf16 b, bf16 c, bf16 d) {
 }
 
 // A [64 tokens][D] bf16 tile of q, k or v staged through registers: TPG
-// tokens x 8 columns per thread, token groups fastest within a wave, so the
-// lanes of one column group write one LDS row of the transposed tile. The
+// tokens x 8 columns per thread. Eight consecutive lanes hold 64 adjacent
+// columns (128 bytes) of one token, so a load instruction touches eight
+// 128-byte lines (issuing a load costs about a cycle per line it touches);
+// wave w covers column slab w % NS and token groups 8 (w / NS) .. + 7. The
 // loads are unconditional (row clamped to the chunk); rows past the chunk end
 // are zeroed when the registers are written out, not when they arrive, so
 // nothing waits for a prefetch until its data is used.
@@ -104,22 +106,23 @@ template <int D>
 struct Stage {
   static constexpr int TPG = 8 * D / NT;         // tokens per thread (1, 2, 4)
   static constexpr int NTG = 64 / TPG;           // token groups
-  static_assert(TPG >= 1 && TPG <= 4 && 64 % NTG == 0, "thread layout");
+  static constexpr int NS = D / 64;              // 64-column slabs
+  static_assert(TPG >= 1 && TPG <= 4 && NS == TPG && NTG * NS == 64, "thread layout");
   uint4 raw[TPG];
   int nc;
-  __device__ int tg(int lane) const { return lane % NTG; }
-  __device__ int c8(int wave, int lane) const { return lane / NTG + (64 / NTG) * wave; }
+  __device__ int tg(int wave, int lane) const { return 8 * (wave / NS) + (lane >> 3); }
+  __device__ int c8(int wave, int lane) const { return 8 * (wave % NS) + (lane & 7); }
   __device__ void load(const bf16* src, int64_t row_stride, int nc_, int wave, int lane) {
     nc = nc_;
 #pragma unroll
     for (int p = 0; p < TPG; ++p) {
-      const int row = TPG * tg(lane) + p;
+      const int row = TPG * tg(wave, lane) + p;
       raw[p] = *reinterpret_cast<const uint4*>(src + min(row, nc - 1) * row_stride + 8 * c8(wave, lane));
     }
   }
-  __device__ bf16x8 row8(int p, int lane) const {
+  __device__ bf16x8 row8(int p, int wave, int lane) const {
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 v = TPG * tg(lane) + p < nc ? raw[p] : z;
+    const uint4 v = TPG * tg(wave, lane) + p < nc ? raw[p] : z;
     return *reinterpret_cast<const bf16x8*>(&v);
   }
   // dst[(8 c8 + j) * 72 + pperm(token)] (or the unpadded r64_off layout when
@@ -128,8 +131,8 @@ struct Stage {
   __device__ void store_t(bf16* dst, bf16* gdst, int wave, int lane) const {
     bf16x8 r[TPG];
 #pragma unroll
-    for (int p = 0; p < TPG; ++p) r[p] = row8(p, lane);
-    const int t0 = TPG * tg(lane), col0 = 8 * c8(wave, lane);
+    for (int p = 0; p < TPG; ++p) r[p] = row8(p, wave, lane);
+    const int t0 = TPG * tg(wave, lane), col0 = 8 * c8(wave, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int off = R64S ? r64_off(col0 + j, pperm(t0)) : (col0 + j) * 72 + pperm(t0);
@@ -155,8 +158,8 @@ struct Stage {
     const int col0 = 8 * c8(wave, lane);
 #pragma unroll
     for (int p = 0; p < TPG; ++p) {
-      bf16* d = dst + (TPG * tg(lane) + p) * ld;
-      const bf16x8 r = row8(p, lane);
+      bf16* d = dst + (TPG * tg(wave, lane) + p) * ld;
+      const bf16x8 r = row8(p, wave, lane);
       st4(d + pperm(col0), r[0], r[1], r[2], r[3]);
       st4(d + pperm(col0 + 4), r[4], r[5], r[6], r[7]);
     }
@@ -179,6 +182,14 @@ __device__ PrepItem prep_item(const FwdKernelArgs& a, int N, int i) {
   // wave-uniform, so these become scalar loads, which no vector-memory wait
   // covers (a vector load here made every item start by waiting for the
   // previous item's stores)
+  if (!a.cu_seqlens && a.T % CHUNK == 0) {
+    // equal lengths: T / 64 chunk slots and one spare slot per sequence
+    const int per = a.T / CHUNK + 1, n = it.slot / per, c = it.slot - n * per;
+    it.t0 = n * a.T + CHUNK * c;
+    it.valid = c < per - 1;
+    it.nc = it.valid ? CHUNK : 0;
+    return it;
+  }
   typedef const int32_t __attribute__((address_space(4)))* cptr;
   const cptr cu = (cptr)a.cu_seqlens;
   int lo = 0, hi = N - 1;
@@ -234,9 +245,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
             it.nc, wave, lane);
     qs.load(reinterpret_cast<const bf16*>(a.q) + ((int64_t)it.t0 * Hqk + hk) * DK, (int64_t)Hqk * DK,
             it.nc, wave, lane);
-    const int64_t gi = (int64_t)(it.t0 + min(lane, it.nc - 1)) * Hv + it.h;
-    graw = a.g[gi];
-    braw = a.beta[gi];
+    if (wave == 0) {                               // the wave that forms the gates
+      const int64_t gi = (int64_t)(it.t0 + min(lane, it.nc - 1)) * Hv + it.h;
+      graw = a.g[gi];
+      braw = a.beta[gi];
+    }
   };
   auto load_v = [&](const PrepItem& it) {
     vs.load(reinterpret_cast<const bf16*>(a.v) + ((int64_t)it.t0 * Hv + it.h) * DV, (int64_t)Hv * DV,
@@ -257,7 +270,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 
     // ---- 1. K, Q rows (pperm over dk), K^T (LDS + image) and gates from registers
     // P upper tiles (0, 1) and (2, 3) are read as zeros by the state kernel
-    for (int e = tid; e < 2 * 2 * 256; e += NT) {
+#pragma unroll
+    for (int k = 0; k < 2 * 2 * 256 / NT; ++k) {
+      const int e = tid + NT * k;
       const int pl = e >> 9, t = (e >> 8) & 1, r = (e >> 4) & 15, cc = e & 15;
       sm.c.P[pl][r64_off(32 * t + r, pperm(32 * t + 16 + cc))] = to_bf16(0.f);
     }
@@ -278,7 +293,6 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       G[128 + lane] = lane == 0 ? fexp2(g2n) : 0.f;
       G[192 + lane] = 0.f;
     }
-    if (nxt.valid) load_kqg(nxt);                  // K, Q, g, beta registers are free again
     lds_barrier();
     GDN_REFRESH();
 
@@ -380,9 +394,17 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     lds_barrier();
     GDN_REFRESH();
     if (wave == 0) vs.store_t(sm.a.Vt, nullptr, wave, lane);
-    if (nxt.valid) load_v(nxt);
+    // The next item's loads are issued here, where six of the eight waves
+    // have no other work (issue stalls while the CU's memory path is busy);
+    // the two merging waves issue theirs after the merge. Every register they
+    // fill has been written out to LDS by now.
+    const bool merger = wave == 1 || wave == 2;
+    if (nxt.valid && !merger) {
+      load_kqg(nxt);
+      load_v(nxt);
+    }
     // 16-block merges X_BA = -X_BB (L_BA X_AA), (A, B) = (0, 1) and (2, 3)
-    if (wave == 1 || wave == 2) {
+    if (merger) {
       const int A = 2 * (wave - 1), B = A + 1;
       const f32x4 y = mm32(&sm.b.s.L[(16 * B) * 65 + 16 * A], 65, &sm.b.s.X[(16 * A) * 65 + 16 * A],
                            65, 0, 0, 0, 16, r16, grp, zero4());
@@ -392,6 +414,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         z = mfma_f32(sm.b.s.X[(16 * B + r16) * 65 + 16 * B + 4 * grp + i], y[i], z);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.b.s.X[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
+      if (nxt.valid) {
+        load_kqg(nxt);
+        load_v(nxt);
+      }
     }
     lds_barrier();
     GDN_REFRESH();
