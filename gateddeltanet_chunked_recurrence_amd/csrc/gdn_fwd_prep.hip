@@ -394,15 +394,12 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     lds_barrier();
     GDN_REFRESH();
     if (wave == 0) vs.store_t(sm.a.Vt, nullptr, wave, lane);
-    // The next item's loads are issued here, where six of the eight waves
-    // have no other work (issue stalls while the CU's memory path is busy);
-    // the two merging waves issue theirs after the merge. Every register they
-    // fill has been written out to LDS by now.
+    // The next item's loads are issued where most waves have no other work
+    // (issue stalls while the CU's memory path is busy): K, Q, g, beta here,
+    // the merging waves after their merge; V in the X_BA phase. Every
+    // register they fill has been written out to LDS by now.
     const bool merger = wave == 1 || wave == 2;
-    if (nxt.valid && !merger) {
-      load_kqg(nxt);
-      load_v(nxt);
-    }
+    if (nxt.valid && !merger) load_kqg(nxt);
     // 16-block merges X_BA = -X_BB (L_BA X_AA), (A, B) = (0, 1) and (2, 3)
     if (merger) {
       const int A = 2 * (wave - 1), B = A + 1;
@@ -414,10 +411,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         z = mfma_f32(sm.b.s.X[(16 * B + r16) * 65 + 16 * B + 4 * grp + i], y[i], z);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.b.s.X[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
-      if (nxt.valid) {
-        load_kqg(nxt);
-        load_v(nxt);
-      }
+      if (nxt.valid) load_kqg(nxt);
     }
     lds_barrier();
     GDN_REFRESH();
@@ -441,13 +435,15 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     }
     lds_barrier();
     GDN_REFRESH();
-    // X_BA = -X_BB Y (one 16x16 tile per wave 0..3)
+    // X_BA = -X_BB Y (one 16x16 tile per wave 0..3; waves 4..7 issue their V loads first)
+    if (wave >= 4 && nxt.valid) load_v(nxt);
     if (wave < 4) {
       const int ti = wave >> 1, tj = wave & 1;
       const f32x4 z = mm32(&sm.b.s.X[32 * 65 + 32], 65, sm.c.Y, 33, 16 * ti, 16 * tj, 0, 16 * ti + 16,
                            r16, grp, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.b.s.X[(32 + 16 * ti + 4 * grp + i) * 65 + 16 * tj + r16] = -z[i];
+      if (nxt.valid) load_v(nxt);
     }
     lds_barrier();
     GDN_REFRESH();
