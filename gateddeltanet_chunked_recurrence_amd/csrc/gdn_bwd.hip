@@ -53,8 +53,8 @@ __device__ void load_gates(Gates& gs, const float* g, const float* beta, int t0,
   if (wave != 0) return;
   const bool valid = lane < nc;
   const int64_t gi = (int64_t)(t0 + lane) * Hv + h;
-  const float g2 = wave_incl_scan(valid ? g[gi] * LOG2E : 0.f, lane);
-  const float g2n = __shfl(g2, nc - 1, WAVE);
+  const float g2 = wave_incl_scan(valid ? g[gi] * LOG2E : 0.f);
+  const float g2n = read_lane(g2, nc - 1);
   gs.gam2[lane] = g2;
   gs.eg[lane] = fexp2(g2);
   gs.egc[lane] = valid ? fexp2(g2n - g2) : 0.f;

@@ -374,8 +374,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   if (wave == 0) {
     const bool valid = lane < nc;
     const int64_t gi = (int64_t)(t0 + min(lane, nc - 1)) * Hv + h;
-    const float g2 = wave_incl_scan(valid ? f.g[gi] * LOG2E : 0.f, lane);
-    const float g2n = __shfl(g2, nc - 1, WAVE);
+    const float g2 = wave_incl_scan(valid ? f.g[gi] * LOG2E : 0.f);
+    const float g2n = read_lane(g2, nc - 1);
     gs.gam2[lane] = g2;
     gs.eg[lane] = fexp2(g2);
     gs.egc[lane] = valid ? fexp2(g2n - g2) : 0.f;

@@ -176,8 +176,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   if (wave == 0) {
     const bool valid = lane < nc;
     const int64_t gi = (int64_t)(t0 + min(lane, nc - 1)) * Hv + h;
-    const float g2 = wave_incl_scan(valid ? f.g[gi] * LOG2E : 0.f, lane);
-    const float g2n = __shfl(g2, nc - 1, WAVE);
+    const float g2 = wave_incl_scan(valid ? f.g[gi] * LOG2E : 0.f);
+    const float g2n = read_lane(g2, nc - 1);
     sm.gam2[lane] = g2;
     sm.eg[lane] = fexp2(g2);
     float* G = reinterpret_cast<float*>(img + BI::g_at(NW));

@@ -162,13 +162,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, WAVE);
   return x;
 }
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const float y = __shfl_up(x, off, WAVE);
-    if (lane >= off) x += y;
-  }
+// A float moved by a DPP pattern with a row mask (rows the mask leaves out,
+// and lanes without a source, read 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of a wave, all in registers:
+// shifts by 1, 2, 4, 8 within each row of 16 lanes (row_shr), then each
+// row's total carried forward (lane 15 to row 1 and lane 47 to row 3 by
+// row_bcast:15; lane 31 to rows 2 and 3 by row_bcast:31).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x += dpp_rows<0x111, 0xF>(x);
+  x += dpp_rows<0x112, 0xF>(x);
+  x += dpp_rows<0x114, 0xF>(x);
+  x += dpp_rows<0x118, 0xF>(x);
+  x += dpp_rows<0x142, 0xA>(x);
+  x += dpp_rows<0x143, 0xC>(x);
   return x;
 }
 

@@ -308,8 +308,8 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
       // gates, one row per lane (every wave holds them; wave 0 publishes)
       if (wave == 0) {
         const bool valid = lane < nc;
-        const float g2 = wave_incl_scan(valid ? g_pre * LOG2E : 0.f, lane);
-        const float g2n = __shfl(g2, nc - 1, WAVE);
+        const float g2 = wave_incl_scan(valid ? g_pre * LOG2E : 0.f);
+        const float g2n = read_lane(g2, nc - 1);
         sm.gam2[lane] = g2;
         sm.bet[lane] = valid ? b_pre : 0.f;
         sm.eg[lane] = fexp2(g2);

@@ -281,8 +281,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     ks.template store_t<true>(sm.Kt, nullptr, wave, lane);   // the image copy goes out during the solve
     if (wave == 0) {
       const float gv = lane < nc ? graw : 0.f;
-      const float g2 = wave_incl_scan(gv * LOG2E, lane);
-      const float g2n = __shfl(g2, nc - 1, WAVE);
+      const float g2 = wave_incl_scan(gv * LOG2E);
+      const float g2n = read_lane(g2, nc - 1);
       const float eg = fexp2(g2);
       sm.gam2[lane] = g2;
       sm.bet[lane] = lane < nc ? braw : 0.f;
