@@ -56,28 +56,25 @@ struct PrepSmem {
   float red[NWAVE];
 };
 
-// Lower 16x16 tiles (mi >= mj) of a 64x64 matrix in a fixed order.
-__device__ __forceinline__ void lower_tile(int t, int& mi, int& mj) {
-  mi = (t >= 1) + (t >= 3) + (t >= 6);
-  mj = t - (mi * (mi + 1)) / 2;
-}
-
-// One 16x16 tile (mi, mj) of A B^T for [64][DK] bf16 row tiles in LDS (row
-// stride LD, same K order in both), operands loaded before the MFMA chain.
-template <int DK, int LD>
-__device__ __forceinline__ f32x4 tile_abt(const bf16* A, const bf16* B, int mi, int mj, int r16,
-                                          int grp) {
-  constexpr int KS = DK / 32;
-  bf16x8 a[KS], b[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    a[kk] = lds_nat(A, 16 * mi + r16, LD, 32 * kk, grp);
-    b[kk] = lds_nat(B, 16 * mj + r16, LD, 32 * kk, grp);
+// The L and P tiles (mi >= mj) of one wave: all share the key block mj; kind
+// 0 is L(mi, mj), 1 is P(mi, mj). Every lower tile of each matrix appears once
+// over the 8 waves, at most three per wave.
+struct PrepJobs {
+  int n, mj, mi[3], kind[3];
+};
+__device__ __forceinline__ PrepJobs prep_jobs(int wave) {
+  PrepJobs j;
+  switch (wave) {
+    case 0: j = {3, 0, {0, 1, 0}, {0, 0, 1}}; break;   // L(0,0) L(1,0) P(0,0)
+    case 1: j = {3, 0, {2, 3, 1}, {0, 0, 1}}; break;   // L(2,0) L(3,0) P(1,0)
+    case 2: j = {2, 0, {2, 3, 0}, {1, 1, 0}}; break;   // P(2,0) P(3,0)
+    case 3: j = {3, 1, {1, 2, 1}, {0, 0, 1}}; break;   // L(1,1) L(2,1) P(1,1)
+    case 4: j = {3, 1, {3, 2, 3}, {0, 1, 1}}; break;   // L(3,1) P(2,1) P(3,1)
+    case 5: j = {3, 2, {2, 3, 2}, {0, 0, 1}}; break;   // L(2,2) L(3,2) P(2,2)
+    case 6: j = {1, 2, {3, 0, 0}, {1, 0, 0}}; break;   // P(3,2)
+    default: j = {2, 3, {3, 3, 0}, {0, 1, 0}}; break;  // L(3,3) P(3,3)
   }
-  f32x4 acc = zero4();
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) acc = mfma(a[kk], b[kk], acc);
-  return acc;
+  return j;
 }
 
 // acc += A(i0 + r, k) B(k, j0 + c) over k in [k0, k1) (FP32 MFMA 16x16x4),
@@ -296,41 +293,68 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     lds_barrier();
     GDN_REFRESH();
 
-    // ---- 2. L (FP32) and P (hi / lo, pperm over columns): 20 tiles over 8 waves
+    // ---- 2. L (FP32) and P (hi / lo, pperm over columns): 20 tiles over 8 waves.
+    // Every tile of a wave shares its key block mj, whose fragments are read
+    // once and serve as B of L(mi, mj) = K_mi K_mj^T and as A of the P^T tile
+    // K_mj Q_mi^T (the phase is bound by LDS reads: 96 KB of operands
+    // instead of 160 KB with a fresh pair per tile).
+    {
+      constexpr int KS = DK / 32;
+      const PrepJobs jb = prep_jobs(wave);
+      bf16x8 bk[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) bk[kk] = lds_nat(sm.a.kq.K, 16 * jb.mj + r16, LDK, 32 * kk, grp);
+      // gate values of the key block, read with the operands (16-byte reads)
+      const float gj = sm.gam2[16 * jb.mj + r16];
+      const f32x4 gc = *reinterpret_cast<const f32x4*>(&sm.gam2[16 * jb.mj + 4 * grp]);
 #pragma unroll
     for (int t3 = 0; t3 < 3; ++t3) {
-      const int job = wave + NWAVE * t3;
-      if (job >= 20) break;
-      int mi, mj;
-      lower_tile(job % 10, mi, mj);
-      if (job < 10) {
-        const f32x4 acc = tile_abt<DK, LDK>(sm.a.kq.K, sm.a.kq.K, mi, mj, r16, grp);
+      if (t3 >= jb.n) break;
+      const int mi = jb.mi[t3], mj = jb.mj;
+      const bool isP = jb.kind[t3] != 0;
+      bf16x8 ao[KS];
+      if (isP || mi != mj) {
+        const bf16* src = isP ? sm.a.kq.Q : sm.a.kq.K;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) ao[kk] = lds_nat(src, 16 * mi + r16, LDK, 32 * kk, grp);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) ao[kk] = bk[kk];
+      }
+      // this tile's row gates, also in flight over the products
+      const f32x4 gr4 = *reinterpret_cast<const f32x4*>(&sm.gam2[16 * mi + 4 * grp]);
+      const f32x4 br4 = *reinterpret_cast<const f32x4*>(&sm.bet[16 * mi + 4 * grp]);
+      const float gr1 = sm.gam2[16 * mi + r16];
+      f32x4 acc = zero4();
+      if (!isP) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma(ao[kk], bk[kk], acc);
         const int cj = 16 * mj + r16;
-        const float gj = sm.gam2[cj];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * mi + 4 * grp + i;
-          const float e = fexp2(sm.gam2[row] - gj);
-          const float lv = row > cj ? sm.bet[row] * acc[i] * e : 0.f;
+          const float e = fexp2(gr4[i] - gj);
+          const float lv = row > cj ? br4[i] * acc[i] * e : 0.f;
           sm.b.s.L[row * 65 + cj] = lv;
           if (mi == mj) sm.Ld[mi][(4 * grp + i) * 16 + r16] = lv;   // aligned copy for the substitution
         }
       } else {
         // P^T tile (K_mj Q_mi^T): the lane holds P[16 mi + r16][16 mj + 4 grp + i],
         // four consecutive columns, so hi and lo go out as 8-byte writes
-        const f32x4 acc = tile_abt<DK, LDK>(sm.a.kq.K, sm.a.kq.Q, mj, mi, r16, grp);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) acc = mfma(bk[kk], ao[kk], acc);
         const int row = 16 * mi + r16, c0 = 16 * mj + 4 * grp;
-        const float gr = sm.gam2[row];
         bf16 hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int cj = c0 + i;
-          const float pv = row >= cj ? acc[i] * fexp2(gr - sm.gam2[cj]) : 0.f;
+          const float pv = row >= cj ? acc[i] * fexp2(gr1 - gc[i]) : 0.f;
           split2(pv, hi[i], lo[i]);
         }
         st4(&sm.c.P[0][r64_off(row, pperm(c0))], hi[0], hi[1], hi[2], hi[3]);
         st4(&sm.c.P[1][r64_off(row, pperm(c0))], lo[0], lo[1], lo[2], lo[3]);
       }
+    }
     }
     lds_barrier();
     GDN_REFRESH();
