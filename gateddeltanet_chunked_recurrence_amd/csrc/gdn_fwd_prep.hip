@@ -53,7 +53,7 @@ struct PrepSmem {
   alignas(16) float gam2[64];                    // log2-scaled gamma
   alignas(16) float bet[64];
   alignas(16) float eg[64];                      // exp(gamma)
-  float red[NWAVE];
+  alignas(16) float red[NWAVE];
 };
 
 // The L and P tiles (mi >= mj) of one wave: all share the key block mj; kind
@@ -487,12 +487,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c0 = 8 * q + 4 * u;
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sm.bet[c0]);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sm.eg[c0]);
         bf16 th[4], tl[4], ph[4], pl[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float t = sm.b.s.X[row * 65 + c0 + e] * sm.bet[c0 + e];
+          const float t = sm.b.s.X[row * 65 + c0 + e] * b4[e];
           split2(t, th[e], tl[e]);
-          split2(t * sm.eg[c0 + e], ph[e], pl[e]);
+          split2(t * e4[e], ph[e], pl[e]);
         }
         const int o = row * 72 + pperm(c0);
         st4(&sm.c.T[0][o], th[0], th[1], th[2], th[3]);
@@ -576,9 +578,12 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     {
       float dW = 1.f, rW = 1.f;
       if constexpr (WF != 0) {
+        static_assert(NWAVE == 8, "two 4-wide reads of the partial maxima");
+        const f32x4 r0 = *reinterpret_cast<const f32x4*>(&sm.red[0]);
+        const f32x4 r1 = *reinterpret_cast<const f32x4*>(&sm.red[4]);
         float amax = 0.f;
 #pragma unroll
-        for (int w = 0; w < NWAVE; ++w) amax = fmaxf(amax, sm.red[w]);
+        for (int w = 0; w < 4; ++w) amax = fmaxf(amax, fmaxf(r0[w], r1[w]));
         dW = qdq_scale<WF>(amax);
         rW = 1.0f / dW;
       }
