@@ -72,33 +72,17 @@ struct Sel {
 };
 
 // Accumulator tile (rows row0..row0+15, columns 16 ct..16 ct+15) of a
-// row-major bf16 LDS matrix, exact (the row read in paired order times the
-// paired selection).
+// row-major bf16 LDS matrix, exact (a transposing LDS read).
 __device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct, int r16, int grp,
-                                         const Sel& s) {
-  return mfma(lds_pair(m, row0 + r16, ld, 32 * (ct >> 1), grp), s.get(ct & 1), zero4());
+                                         const Sel&) {
+  return lds_tile(m, ld, row0, 16 * ct, r16, grp);
 }
 // Operand contracting over rows r0..r0+31 (paired order), free index = columns
 // 16 ct..16 ct+15: the lane holds rows r0 + 4 grp + e and r0 + 16 + 4 grp + e
 // of column 16 ct + r16 (no arithmetic).
 __device__ __forceinline__ bf16x8 colp(const bf16* m, int ld, int r0, int ct, int r16, int grp,
                                        const Sel&) {
-  // Two transposing LDS reads (ds_read_b64_tr_b16). Within each group of 16
-  // lanes, lane j receives as element e the element (j & 3) of the 8 bytes
-  // that lane 4 e + (j >> 2) addresses (established on gfx950 with an in-LDS
-  // index pattern). Lane i of the group therefore addresses row
-  // r0 + 4 grp + (i >> 2), columns 16 ct + 4 (i & 3) .. + 3, and receives
-  // column 16 ct + i of rows r0 + 4 grp + 0..3; the second read is the same
-  // 16 rows further down. Every lane of the wave must be active; ld is a
-  // multiple of 4 elements, so each address is 8-byte aligned.
-  typedef short s16x4v __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4v* lds_s16x4;
-  const bf16* p = m + (r0 + 4 * grp + (r16 >> 2)) * ld + 16 * ct + 4 * (r16 & 3);
-  const s16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(const_cast<bf16*>(p)));
-  const s16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(const_cast<bf16*>(p + 16 * ld)));
-  typedef short s16x8v __attribute__((ext_vector_type(8)));
-  const s16x8v r = s16x8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, r);
+  return lds_col8(m, ld, r0, 16 * ct, r16, grp);
 }
 // Operand contracting over columns k0..k0+31 (paired order), free index = rows
 // row0..row0+15.

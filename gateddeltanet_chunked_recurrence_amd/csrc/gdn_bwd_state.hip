@@ -29,10 +29,9 @@
 // the backward has no QDQ). It stores dS' and dVnew of every chunk, fragment
 // order, for the chunk-local gradients, and dh0 at the end.
 //
-// Transposes go through the matrix core: a bf16 row tile read as an A operand
-// times a 0/1 selection B operand is the same tile in accumulator layout,
-// exactly (one nonzero product per output), and two such tiles stacked along
-// the tokens are an operand with the tokens as contraction index (pack_pair).
+// Transposes are transposing LDS reads (ds_read_b64_tr_b16): a row-major bf16
+// tile read by columns is the tile in accumulator layout, and two such reads
+// 16 rows apart are an operand with the tokens as contraction index.
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -55,20 +54,10 @@ struct BImg {
   static constexpr int g_at(int nw) { return KI + nw * WT; }
 };
 
-// The selection operand: lane (grp, r16) holds B[8 grp + e][r16] = 1 exactly
-// when 8 grp + e = 16 half + r16, so A B = columns 16 half .. 16 half + 15 of A.
-__device__ __forceinline__ bf16x8 select_op(int half, int r16, int grp) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = to_bf16(8 * grp + e == 16 * half + r16 ? 1.f : 0.f);
-  return r;
-}
-
 // Accumulator-layout tile of rows row0..row0+15, columns 16 ct..16 ct + 15 of
-// a bf16 row-major LDS matrix (row stride ld).
-__device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct, int r16, int grp,
-                                         const bf16x8 (&sel)[2]) {
-  return mfma(lds_nat(m, row0 + r16, ld, 32 * (ct >> 1), grp), sel[ct & 1], zero4());
+// a bf16 row-major LDS matrix (row stride ld), by a transposing LDS read.
+__device__ __forceinline__ f32x4 tile_of(const bf16* m, int ld, int row0, int ct, int r16, int grp) {
+  return lds_tile(m, ld, row0, 16 * ct, r16, grp);
 }
 
 template <int DK, int DV, int NW>
@@ -189,9 +178,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   }
   __syncthreads();
 
-  bf16x8 sel[2];
-  sel[0] = select_op(0, r16, grp);
-  sel[1] = select_op(1, r16, grp);
 
   // ---- (e^gamma Q)^T operands for this wave's dk tiles: hi + lo
   bf16x8 aQh[DPW][2], aQl[DPW][2];
@@ -201,7 +187,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
     f32x4 cq[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      cq[it] = tile_of(sm.u.Qn, LD, 16 * it, dt, r16, grp, sel);
+      cq[it] = tile_of(sm.u.Qn, LD, 16 * it, dt, r16, grp);
       const f32x4 e = *reinterpret_cast<const f32x4*>(&sm.eg[16 * it + 4 * grp]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) cq[it][q] *= e[q];
@@ -238,9 +224,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   // ---- dO operands, tokens as contraction index (shared by A1 and A2)
   for (int fi = wave; fi < 2 * NVT; fi += 4) {
     const int kk = fi & 1, vt = fi >> 1;
-    const f32x4 c0 = tile_of(sm.dOn, LDO, 32 * kk, vt, r16, grp, sel);
-    const f32x4 c1 = tile_of(sm.dOn, LDO, 32 * kk + 16, vt, r16, grp, sel);
-    sm.u.dOB[(kk * NVT + vt) * 64 + lane] = pack_pair(c0, c1);
+    sm.u.dOB[(kk * NVT + vt) * 64 + lane] = lds_col8(sm.dOn, LDO, 32 * kk, 16 * vt, r16, grp);
   }
 
   __syncthreads();                                 // dO operands complete
@@ -290,10 +274,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
     const int dt = fi >> 1, kk = fi & 1;
 #pragma unroll
     for (int pl = 0; pl < NW; ++pl) {
-      const f32x4 c0 = tile_of(sm.Wn[pl], LD, 32 * kk, dt, r16, grp, sel);
-      const f32x4 c1 = tile_of(sm.Wn[pl], LD, 32 * kk + 16, dt, r16, grp, sel);
       *reinterpret_cast<bf16x8*>(img + BI::KI + pl * BI::WT + (16 * dt + r16) * I::R64 + 32 * kk +
-                                 8 * grp) = pack_pair(c0, c1);
+                                 8 * grp) = lds_col8(sm.Wn[pl], LD, 32 * kk, 16 * dt, r16, grp);
     }
   }
 }

@@ -120,6 +120,33 @@ __device__ __forceinline__ int pperm(int k) {
   return (k & ~31) + 8 * ((k & 15) >> 2) + 4 * ((k >> 4) & 1) + (k & 3);
 }
 
+// Column reads of a row-major bf16 LDS matrix by the transposing LDS read
+// (ds_read_b64_tr_b16). Within each group of 16 lanes, lane j receives as
+// element e the element (j & 3) of the 8 bytes that lane 4 e + (j >> 2)
+// addresses (established on gfx950 with an in-LDS index pattern). So if lane
+// i of the group addresses row r + (i >> 2), columns c + 4 (i & 3) .. + 3, lane
+// j receives column c + j of rows r .. r + 3: the accumulator layout of a
+// 16x16 tile, or half of a paired-order operand. Every lane of the wave must
+// be active, and ld must be a multiple of 4 elements (8-byte alignment).
+// lds_col4: lane (r16, grp) gets m[r0 + 4 grp + e][c0 + r16], e = 0..3.
+__device__ __forceinline__ bf16x4 lds_col4(const bf16* m, int ld, int r0, int c0, int r16, int grp) {
+  typedef short s16x4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4v* lds_s16x4;
+  const bf16* p = m + (r0 + 4 * grp + (r16 >> 2)) * ld + c0 + 4 * (r16 & 3);
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(const_cast<bf16*>(p))));
+}
+// lds_col8: paired order over rows r0 .. r0 + 31 (rows r0 + 4 grp + e, then
+// r0 + 16 + 4 grp + e) of column c0 + r16.
+__device__ __forceinline__ bf16x8 lds_col8(const bf16* m, int ld, int r0, int c0, int r16, int grp) {
+  const bf16x4 a = lds_col4(m, ld, r0, c0, r16, grp), b = lds_col4(m, ld, r0 + 16, c0, r16, grp);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// The accumulator tile (rows r0 .. r0 + 15, columns c0 .. c0 + 15) as FP32 (exact).
+__device__ __forceinline__ f32x4 lds_tile(const bf16* m, int ld, int r0, int c0, int r16, int grp) {
+  const bf16x4 a = lds_col4(m, ld, r0, c0, r16, grp);
+  return f32x4{from_bf16(a[0]), from_bf16(a[1]), from_bf16(a[2]), from_bf16(a[3])};
+}
+
 // LDS operand loads (bf16 elements, row-major with row stride `ld`).
 // Natural K order: 8 contiguous elements at A[row][k0 + 8*grp].
 __device__ __forceinline__ bf16x8 lds_nat(const bf16* base, int row, int ld, int k0, int grp) {
