@@ -273,6 +273,9 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
   k.ws_img = reinterpret_cast<__bf16*>(ws + W.img);
   k.ws_u = reinterpret_cast<float*>(ws + W.u);
   k.ws_wscale = reinterpret_cast<float*>(ws + W.wscale);
+  // with both QDQ sites on, the state kernel widens the W codes itself, so
+  // the images carry them as bytes
+  k.w_img_bytes = (a->policy.state_fmt != GDN_QDQ_OFF && a->policy.w_fmt != GDN_QDQ_OFF) ? 1 : 0;
   if (stages & 1) {
     const int num_slots = (int)layout_of(a).num_slots;
     s = hip_status(gdn::launch_fwd_prep(cfg, k, num_slots, st), "gdn_chunk_fwd prep launch");

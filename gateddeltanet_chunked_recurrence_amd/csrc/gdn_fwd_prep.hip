@@ -597,7 +597,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
           float cq[4];
           uint32_t bytes;
           quant4<WF>(w, rW, cq, bytes);
-          st4(&sm.b.W[o], to_bf16(cq[0]), to_bf16(cq[1]), to_bf16(cq[2]), to_bf16(cq[3]));
+          if (a.w_img_bytes)                      // the code bytes, same element order
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sm.b.W) + o) = bytes;
+          else
+            st4(&sm.b.W[o], to_bf16(cq[0]), to_bf16(cq[1]), to_bf16(cq[2]), to_bf16(cq[3]));
           if (save && tok < nc)
             *reinterpret_cast<uint32_t*>(a.w_codes + ((int64_t)(t0 + tok) * Hv + h) * DK + dk0) = bytes;
         } else {
@@ -619,9 +622,16 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       const uint4* src = reinterpret_cast<const uint4*>(sm.b.W);
       uint4* dst = reinterpret_cast<uint4*>(img);
       constexpr int NWP = NW * I::WQ / 8;          // 16-byte pieces of the W planes
+      constexpr int NWB = I::WQ / 16;              // ... of the code bytes
+      if (WF != 0 && a.w_img_bytes) {
 #pragma unroll
-      for (int k = 0; k < (NWP + NT - 1) / NT; ++k)
-        if (NWP % NT == 0 || tid + NT * k < NWP) dst[tid + NT * k] = src[tid + NT * k];
+        for (int k = 0; k < (NWB + NT - 1) / NT; ++k)
+          if (NWB % NT == 0 || tid + NT * k < NWB) dst[tid + NT * k] = src[tid + NT * k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < (NWP + NT - 1) / NT; ++k)
+          if (NWP % NT == 0 || tid + NT * k < NWP) dst[tid + NT * k] = src[tid + NT * k];
+      }
     }
     lds_barrier();                              // LDS is reused by the next item
     if (!nxt.valid) break;

@@ -38,8 +38,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <int DK>
 struct SplitSmem {
   using I = Img<DK>;
-  struct Buf {                                    // one image block (W codes, K^T, P, gates)
-    bf16 W[I::WQ];
+  // W code bytes padded to whole 64-lane copies of 16 bytes (each lane of a
+  // copy writes its own 16 bytes, so the copy of the last partial piece group
+  // lands in this padding, not in K^T)
+  static constexpr int WBP = (I::WQ / 16 + 63) / 64 * 64 * 16;
+  struct Buf {                                    // one image block (W code bytes, K^T, P, gates)
+    uint8_t Wb[WBP];                              // W^q codes, one byte each, W image element order
     bf16 Kt[I::KT];
     bf16 P[2 * I::P1];
     alignas(16) float G[I::GB / 2];
@@ -97,6 +101,13 @@ __device__ __forceinline__ bf16x8 codes_bf16(u32x2 w) {
   }
 }
 
+// A-operand fragment of the W codes (row `row`, stored positions 32 kk + 8 grp
+// .. + 7) from the byte copy of a W image plane: the eight code bytes.
+template <int DK>
+__device__ __forceinline__ u32x2 ld_wb(const uint8_t* wb, int row, int kk, int grp) {
+  return *reinterpret_cast<const u32x2*>(wb + wq_off<DK>(row, 32 * kk + 8 * grp));
+}
+
 template <int DK, int SF, int WF>
 __global__ void __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(3, 3)))
 gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
@@ -106,7 +117,8 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   constexpr int MK = DK / 16;                     // 16-row tiles of a state column group
   constexpr int KS = DK / 32;                     // 32-deep k-steps over dk
   constexpr int IMGP = I::template img<1>() / 8;  // 16-byte pieces of an image block
-  static_assert(sizeof(typename Sm::Buf) == 16 * IMGP, "image block layout");
+  // the LDS block: the image block with its W slot replaced by the padded code bytes
+  static_assert(sizeof(typename Sm::Buf) == 16 * IMGP - 2 * I::WQ + Sm::WBP, "image block layout");
   __shared__ __align__(16) Sm sm;
 
   const int Hv = a.Hv, Dv = a.Dv, NVB = Dv / 64;
@@ -205,11 +217,12 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       // operands read ahead of their products: the W fragments here, over the
       // QDQ; the K^T fragments after W Sq is issued, over Vnew
       // (two k-steps ahead: three waves per SIMD leave 168 VGPRs per wave)
-      bf16x8 op[2][4];
+      // W fragments stay code bytes until their product (8 bytes per read)
+      u32x2 op[2][4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) op[kk][mt] = ld_wq<DK>(B.W, 16 * mt + r16, kk, grp);
+        for (int mt = 0; mt < 4; ++mt) op[kk][mt] = ld_wb<DK>(B.Wb, 16 * mt + r16, kk, grp);
       const float dS = scale_of(c);
 
       // ---- QDQ; code bytes to LDS; Sq as the B operand of W Sq
@@ -237,10 +250,10 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       for (int kk = 0; kk < KS; ++kk) {
         const bf16x8 b = pack_pair(S[2 * kk], S[2 * kk + 1]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) accw[mt] = mfma(op[kk & 1][mt], b, accw[mt]);
+        for (int mt = 0; mt < 4; ++mt) accw[mt] = mfma(codes_bf16<WF>(op[kk & 1][mt]), b, accw[mt]);
         if (kk + 2 < KS)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) op[kk & 1][mt] = ld_wq<DK>(B.W, 16 * mt + r16, kk + 2, grp);
+          for (int mt = 0; mt < 4; ++mt) op[kk & 1][mt] = ld_wb<DK>(B.Wb, 16 * mt + r16, kk + 2, grp);
       }
       bf16x8 kop[MK];                              // token k-step 0; k-step 1 reloads in place
 #pragma unroll
@@ -411,16 +424,25 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
         *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = qreg[p].zw;
       }
     };
-    constexpr int NINS = IMGP / 64;               // wave loads per image block
-    constexpr int KW = (NINS + 3) / 4;            // ... per staging wave
-    static_assert(IMGP % 64 == 0, "whole wave loads");
+    // Two ranges of the image block: the W code bytes (the first WQ bytes of
+    // its W slot) and K^T, P, gates after the slot; the LDS block holds them
+    // back to back (the codes padded to whole wave loads).
+    constexpr int WOFF = I::WQ / 8;               // 16-byte pieces of the W slot
+    constexpr int NWB = I::WQ / 16;               // ... of the W code bytes
+    constexpr int NI1 = Sm::WBP / 16 / 64;        // wave loads of the codes
+    constexpr int NI2 = (IMGP - WOFF) / 64;       // wave loads of K^T, P and the gates
+    constexpr int KW = (NI1 + NI2 + 3) / 4;       // ... per staging wave
+    static_assert((IMGP - WOFF) % 64 == 0 && NI1 * 64 >= NWB, "whole wave loads");
     auto dma = [&](int c, int b) {
       const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
-      uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].W);
+      uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].Wb);
 #pragma unroll
       for (int k = 0; k < KW; ++k) {
-        const int j = min(cg + 4 * k, NINS - 1);  // a repeated last load rewrites the same bytes
-        __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
+        const int j = min(cg + 4 * k, NI1 + NI2 - 1);   // a repeated last load rewrites the same bytes
+        if (j < NI1)                               // lanes past the codes read the last piece into the padding
+          __builtin_amdgcn_global_load_lds(src + min(64 * j + lane, NWB - 1), dst + 64 * j, 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(src + WOFF + 64 * (j - NI1) + lane, dst + 64 * j, 16, 0, 0);
       }
     };
     load_q(0);
@@ -460,6 +482,7 @@ static hipError_t launch_split_dk(const FwdConfig& cfg, const FwdKernelArgs& a, 
 }
 
 hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+  if (!a.w_img_bytes) return hipErrorInvalidValue;   // its images carry W as code bytes
   if (cfg.Dk == 128) return launch_split_dk<128>(cfg, a, s);
   if (cfg.Dk == 64) return launch_split_dk<64>(cfg, a, s);
   return hipErrorInvalidValue;

@@ -6,7 +6,10 @@
 // 16-byte copies:
 //   W image  [64][DK] bf16 per plane: W^q codes (one plane) or W as hi + lo
 //            (two planes), paired order along dk (pperm), 16-byte chunks
-//            XOR-swizzled by row for DK = 128 (rows padded to 72 for DK = 64)
+//            XOR-swizzled by row for DK = 128 (rows padded to 72 for DK = 64).
+//            With both QDQ sites on, the plane holds the code bytes instead
+//            (the same element order, in the first WQ bytes of the plane's
+//            slot), and the state kernel widens them to bf16 in LDS
 //   K^T image [DK][64] bf16: K transposed, paired order along tokens
 //   P image  2 x [64][64] bf16: (Q K^T) * Gam as hi + lo, paired order along
 //            the key token; upper 16x16 tiles zero

@@ -26,6 +26,7 @@ struct FwdKernelArgs {
   __bf16* ws_img;             // [slots * Hv][W planes | K^T | P] (gdn_images.h)
   float* ws_u;                // [slots * Hv][Dv * 64] fragment order
   float* ws_wscale;           // [slots * Hv]
+  int32_t w_img_bytes;        // 1: the W plane of the images holds code bytes (both QDQ sites on)
   int32_t T;                  // tokens per sequence (no cu_seqlens)
   int32_t Hqk, Hv, Dv, block_v;
   float scale;
