@@ -284,7 +284,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       sm.gam2[lane] = g2;
       sm.bet[lane] = lane < nc ? braw : 0.f;
       sm.eg[lane] = eg;
-      float* G = reinterpret_cast<float*>(img + I::template g_at<NW>());
+      // the gate block follows the single fp16 P plane in the byte variant
+      const int goff = a.w_img_bytes ? I::template p_at<NW>() + I::P1 : I::template g_at<NW>();
+      float* G = reinterpret_cast<float*>(img + goff);
       G[lane] = eg;
       G[64 + lane] = lane < nc ? fexp2(g2n - g2) : 0.f;
       G[128 + lane] = lane == 0 ? fexp2(g2n) : 0.f;
@@ -344,15 +346,21 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) acc = mfma(bk[kk], ao[kk], acc);
         const int row = 16 * mi + r16, c0 = 16 * mj + 4 * grp;
-        bf16 hi[4], lo[4];
+        float pv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int cj = c0 + i;
-          const float pv = row >= cj ? acc[i] * fexp2(gr1 - gc[i]) : 0.f;
-          split2(pv, hi[i], lo[i]);
+        for (int i = 0; i < 4; ++i) pv[i] = row >= c0 + i ? acc[i] * fexp2(gr1 - gc[i]) : 0.f;
+        if (a.w_img_bytes) {
+          // one fp16 plane (11-bit significand: relative error <= 2^-12)
+          typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+          const f16x4 h = f16x4{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+          *reinterpret_cast<f16x4*>(&sm.c.P[0][r64_off(row, pperm(c0))]) = h;
+        } else {
+          bf16 hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) split2(pv[i], hi[i], lo[i]);
+          st4(&sm.c.P[0][r64_off(row, pperm(c0))], hi[0], hi[1], hi[2], hi[3]);
+          st4(&sm.c.P[1][r64_off(row, pperm(c0))], lo[0], lo[1], lo[2], lo[3]);
         }
-        st4(&sm.c.P[0][r64_off(row, pperm(c0))], hi[0], hi[1], hi[2], hi[3]);
-        st4(&sm.c.P[1][r64_off(row, pperm(c0))], lo[0], lo[1], lo[2], lo[3]);
       }
     }
     }
@@ -399,13 +407,15 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       // image, as they are in LDS), fixed trip counts
       static_assert(sizeof(sm.c.P) == 2 * I::P1 * 2, "P tile is the image's P section");
       constexpr int NKP = (I::KT + 2 * I::P1) / 8, NCP = (NKP + NT - 65) / (NT - 64);
+      // one P plane in the byte variant: its second slot holds the gate block
+      const int nkp = a.w_img_bytes ? (I::KT + I::P1) / 8 : NKP;
       const uint4* ksrc = reinterpret_cast<const uint4*>(&sm.Kt[0]);
       const uint4* psrc = reinterpret_cast<const uint4*>(&sm.c.P[0][0]);
       uint4* kdst = reinterpret_cast<uint4*>(img + I::template kt_at<NW>());
 #pragma unroll
       for (int k = 0; k < NCP; ++k) {
         const int e = t + (NT - 64) * k;
-        if (e < NKP) kdst[e] = e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8];
+        if (e < nkp) kdst[e] = e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8];
       }
       for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
         const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;

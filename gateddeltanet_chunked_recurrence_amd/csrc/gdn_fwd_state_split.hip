@@ -45,7 +45,7 @@ struct SplitSmem {
   struct Buf {                                    // one image block (W code bytes, K^T, P, gates)
     uint8_t Wb[WBP];                              // W^q codes, one byte each, W image element order
     bf16 Kt[I::KT];
-    bf16 P[2 * I::P1];
+    _Float16 P[I::P1];                            // masked Q K^T, one fp16 plane
     alignas(16) float G[I::GB / 2];
   };
   Buf buf[2];
@@ -118,7 +118,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   constexpr int KS = DK / 32;                     // 32-deep k-steps over dk
   constexpr int IMGP = I::template img<1>() / 8;  // 16-byte pieces of an image block
   // the LDS block: the image block with its W slot replaced by the padded code bytes
-  static_assert(sizeof(typename Sm::Buf) == 16 * IMGP - 2 * I::WQ + Sm::WBP, "image block layout");
+  static_assert(sizeof(typename Sm::Buf) == Sm::WBP + 2 * (I::KT + I::P1 + I::GB), "image block layout");
   __shared__ __align__(16) Sm sm;
 
   const int Hv = a.Hv, Dv = a.Dv, NVB = Dv / 64;
@@ -348,22 +348,27 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       }
       lds_wait(&sm.flag[1], 4u * (c + 1));        // this chunk's Vnew
       {
-        bf16x8 aVh[2], aVl[2];
+        // P is one fp16 plane; Vnew enters as fp16 hi + lo (22 significant bits)
+        f16x8 aVh[2], aVl[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const f32x4 v0 = sm.vnx[cg][2 * t][lane], v1 = sm.vnx[cg][2 * t + 1][lane];
-          pack_pair_split(v0, v1, aVh[t], aVl[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            aVh[t][e] = (_Float16)v0[e];
+            aVh[t][4 + e] = (_Float16)v1[e];
+            aVl[t][e] = (_Float16)(v0[e] - (float)aVh[t][e]);
+            aVl[t][4 + e] = (_Float16)(v1[e] - (float)aVh[t][4 + e]);
+          }
         }
         // under the lower-triangular P, row tiles 0 and 1 need k-step 0 only
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int kk = 0; kk <= (mt >> 1); ++kk) {
-            const bf16x8 ph = ld_r64(B.P, 16 * mt + r16, 32 * kk, grp);
-            const bf16x8 pl = ld_r64(B.P + I::P1, 16 * mt + r16, 32 * kk, grp);
-            acc[mt] = mfma(aVh[kk], ph, acc[mt]);
-            acc[mt] = mfma(aVl[kk], ph, acc[mt]);
-            acc[mt] = mfma(aVh[kk], pl, acc[mt]);
+            const f16x8 p = *reinterpret_cast<const f16x8*>(B.P + r64_off(16 * mt + r16, 32 * kk + 8 * grp));
+            acc[mt] = mfma(aVh[kk], p, acc[mt]);
+            acc[mt] = mfma(aVl[kk], p, acc[mt]);
           }
       }
 #pragma unroll
@@ -425,14 +430,14 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       }
     };
     // Two ranges of the image block: the W code bytes (the first WQ bytes of
-    // its W slot) and K^T, P, gates after the slot; the LDS block holds them
-    // back to back (the codes padded to whole wave loads).
+    // its W slot) and K^T, the fp16 P plane and the gates after the slot; the
+    // LDS block holds them back to back (the codes padded to whole wave loads).
     constexpr int WOFF = I::WQ / 8;               // 16-byte pieces of the W slot
     constexpr int NWB = I::WQ / 16;               // ... of the W code bytes
     constexpr int NI1 = Sm::WBP / 16 / 64;        // wave loads of the codes
-    constexpr int NI2 = (IMGP - WOFF) / 64;       // wave loads of K^T, P and the gates
+    constexpr int NI2 = (I::KT + I::P1 + I::GB) / 8 / 64;   // wave loads of K^T, P and the gates
     constexpr int KW = (NI1 + NI2 + 3) / 4;       // ... per staging wave
-    static_assert((IMGP - WOFF) % 64 == 0 && NI1 * 64 >= NWB, "whole wave loads");
+    static_assert((I::KT + I::P1 + I::GB) % 512 == 0 && NI1 * 64 >= NWB, "whole wave loads");
     auto dma = [&](int c, int b) {
       const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
       uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].Wb);

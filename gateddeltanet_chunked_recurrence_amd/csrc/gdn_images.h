@@ -9,7 +9,10 @@
 //            XOR-swizzled by row for DK = 128 (rows padded to 72 for DK = 64).
 //            With both QDQ sites on, the plane holds the code bytes instead
 //            (the same element order, in the first WQ bytes of the plane's
-//            slot), and the state kernel widens them to bf16 in LDS
+//            slot), and the state kernel widens them to bf16 per fragment.
+//            In that variant P is one fp16 plane and the gate block follows
+//            it (in the second P plane's slot), so K^T, P and the gates are
+//            one contiguous range
 //   K^T image [DK][64] bf16: K transposed, paired order along tokens
 //   P image  2 x [64][64] bf16: (Q K^T) * Gam as hi + lo, paired order along
 //            the key token; upper 16x16 tiles zero
