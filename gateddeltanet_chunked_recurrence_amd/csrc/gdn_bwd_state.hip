@@ -99,38 +99,59 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   const int64_t chb = (int64_t)slot * Hv + h;
   bf16* img = a.ws_bimg + chb * BI::size(NW);
 
-  // ---- rows of K, Q, dO and W into LDS (rows past the chunk end are zero)
+  // ---- rows of K, Q, dO and W into LDS (rows past the chunk end are zero).
+  // Every load is issued before the first LDS write, so the item pays one
+  // memory latency, not one per loop trip.
   {
     const bf16* kg = reinterpret_cast<const bf16*>(f.k);
     const bf16* qg = reinterpret_cast<const bf16*>(f.q);
-    for (int e = tid; e < 64 * DK / 8; e += NT) {
-      const int row = e / (DK / 8), c8 = e % (DK / 8);
-      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hqk + hk) * DK + 8 * c8;
-      u32x4 kv = *reinterpret_cast<const u32x4*>(kg + off);
-      u32x4 qv = *reinterpret_cast<const u32x4*>(qg + off);
-      if (row >= nc) kv = qv = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.Kn[row * LD + 8 * c8]) = kv;
-      *reinterpret_cast<u32x4*>(&sm.u.Qn[row * LD + 8 * c8]) = qv;
-    }
     const bf16* dog = reinterpret_cast<const bf16*>(a.dout);
-    const int p8 = Dv / 8;
-    for (int e = tid; e < 64 * p8; e += NT) {
-      const int row = e / p8, c8 = e % p8;
-      u32x4 v = *reinterpret_cast<const u32x4*>(
-          dog + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * Dv + 8 * c8);
-      if (row >= nc) v = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sm.dOn[row * LDO + 8 * c8]) = v;
+    constexpr int NKQ = 64 * DK / 8 / NT, NDO = 64 * DV / 8 / NT;
+    constexpr int WPR = WF != 0 ? DK / 16 : DK / 4;   // 16-byte pieces per W row
+    constexpr int NWL = 64 * WPR / NT;
+    static_assert(NKQ * NT == 64 * DK / 8 && NDO * NT == 64 * DV / 8 && NWL * NT == 64 * WPR,
+                  "whole trips");
+    u32x4 kv[NKQ], qv[NKQ], dv[NDO], wv[NWL];
+#pragma unroll
+    for (int p = 0; p < NKQ; ++p) {
+      const int e = tid + NT * p, row = e / (DK / 8), c8 = e % (DK / 8);
+      const int64_t off = ((int64_t)(t0 + min(row, nc - 1)) * Hqk + hk) * DK + 8 * c8;
+      kv[p] = *reinterpret_cast<const u32x4*>(kg + off);
+      qv[p] = *reinterpret_cast<const u32x4*>(qg + off);
     }
-    if constexpr (WF != 0) {
-      // codes (exact in bf16: E4M3 values and integers up to 127)
-      for (int e = tid; e < 64 * DK / 16; e += NT) {
-        const int row = e / (DK / 16), c16 = e % (DK / 16);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(
-            f.w_codes + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 16 * c16);
+#pragma unroll
+    for (int p = 0; p < NDO; ++p) {
+      const int e = tid + NT * p, row = e / (DV / 8), c8 = e % (DV / 8);
+      dv[p] = *reinterpret_cast<const u32x4*>(dog + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * Dv + 8 * c8);
+    }
+#pragma unroll
+    for (int p = 0; p < NWL; ++p) {
+      const int e = tid + NT * p, row = e / WPR, cw = e % WPR;
+      const int64_t rb = ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK;
+      if constexpr (WF != 0) wv[p] = *reinterpret_cast<const u32x4*>(f.w_codes + rb + 16 * cw);
+      else wv[p] = *reinterpret_cast<const u32x4*>(a.ws_W + rb + 4 * cw);
+    }
+#pragma unroll
+    for (int p = 0; p < NKQ; ++p) {
+      const int e = tid + NT * p, row = e / (DK / 8), c8 = e % (DK / 8);
+      const bool z = row >= nc;
+      *reinterpret_cast<u32x4*>(&sm.Kn[row * LD + 8 * c8]) = z ? u32x4{0u, 0u, 0u, 0u} : kv[p];
+      *reinterpret_cast<u32x4*>(&sm.u.Qn[row * LD + 8 * c8]) = z ? u32x4{0u, 0u, 0u, 0u} : qv[p];
+    }
+#pragma unroll
+    for (int p = 0; p < NDO; ++p) {
+      const int e = tid + NT * p, row = e / (DV / 8), c8 = e % (DV / 8);
+      *reinterpret_cast<u32x4*>(&sm.dOn[row * LDO + 8 * c8]) = row >= nc ? u32x4{0u, 0u, 0u, 0u} : dv[p];
+    }
+#pragma unroll
+    for (int p = 0; p < NWL; ++p) {
+      const int e = tid + NT * p, row = e / WPR, cw = e % WPR;
+      if constexpr (WF != 0) {
+        // codes (exact in bf16: E4M3 values and integers up to 127)
         bf16x8 o[2];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const uint32_t word = b[j >> 2];
+          const uint32_t word = wv[p][j >> 2];
           float cv;
           if constexpr (WF == 1) {
             cv = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word >> (8 * (j & 3))), 0);
@@ -139,14 +160,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
           }
           o[j >> 3][j & 7] = to_bf16(row < nc ? cv : 0.f);
         }
-        *reinterpret_cast<bf16x8*>(&sm.Wn[0][row * LD + 16 * c16]) = o[0];
-        *reinterpret_cast<bf16x8*>(&sm.Wn[0][row * LD + 16 * c16 + 8]) = o[1];
-      }
-    } else {
-      for (int e = tid; e < 64 * DK / 4; e += NT) {
-        const int row = e / (DK / 4), c4 = e % (DK / 4);
-        f32x4 w = *reinterpret_cast<const f32x4*>(
-            a.ws_W + ((int64_t)(t0 + min(row, nc - 1)) * Hv + h) * DK + 4 * c4);
+        *reinterpret_cast<bf16x8*>(&sm.Wn[0][row * LD + 16 * cw]) = o[0];
+        *reinterpret_cast<bf16x8*>(&sm.Wn[0][row * LD + 16 * cw + 8]) = o[1];
+      } else {
+        f32x4 w = __builtin_bit_cast(f32x4, wv[p]);
         if (row >= nc) w = zero4();
         bf16x4 hi, lo;
 #pragma unroll
@@ -156,8 +173,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
           hi[j] = hj;
           lo[j] = lj;
         }
-        *reinterpret_cast<bf16x4*>(&sm.Wn[0][row * LD + 4 * c4]) = hi;
-        *reinterpret_cast<bf16x4*>(&sm.Wn[NW - 1][row * LD + 4 * c4]) = lo;
+        *reinterpret_cast<bf16x4*>(&sm.Wn[0][row * LD + 4 * cw]) = hi;
+        *reinterpret_cast<bf16x4*>(&sm.Wn[NW - 1][row * LD + 4 * cw]) = lo;
       }
     }
   }
