@@ -15,6 +15,11 @@
 //   staging waves 8..11: this chunk's Q to LDS, the next chunk's image block
 //     and Q copied in (their issue stalls while the CU's memory pipeline is
 //     busy, which is why no other role issues them).
+// The image block arrives as W^q code bytes (kept as bytes in LDS and widened
+// to bf16 per 8-byte fragment just before each W^q S^q product), K^T, P as
+// one fp16 plane, and the gates: about 33 KB per chunk instead of 49 KB with
+// bf16 codes and P as bf16 hi + lo, since the per-CU memory path bounds the
+// chunk.
 // One workgroup barrier per chunk (X, at its end). Within a chunk the output
 // waves wait on LDS counters that the recurrence waves (codes, then Vnew) and
 // the staging waves (Q) raise after their LDS writes complete; the counters

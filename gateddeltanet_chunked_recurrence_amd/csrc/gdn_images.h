@@ -15,7 +15,8 @@
 //            one contiguous range
 //   K^T image [DK][64] bf16: K transposed, paired order along tokens
 //   P image  2 x [64][64] bf16: (Q K^T) * Gam as hi + lo, paired order along
-//            the key token; upper 16x16 tiles zero
+//            the key token; upper 16x16 tiles zero (one fp16 plane in the
+//            byte variant above)
 //            (both [*][64] images unpadded, 16-byte pieces XOR-swizzled by
 //            row, see r64_off)
 //   U        FP32 in accumulator-fragment order: for value block vb, wave w,
@@ -25,7 +26,9 @@
 //            (0 past the chunk end), exp(gamma_n) at [128], rest unused
 //   W scale  one FP32 per chunk and head (1 when W QDQ is off)
 // The W, K^T, P and gate images of one chunk and head are one contiguous
-// block, in that order, as they are in the state kernel's LDS buffer.
+// block, in that order, as they are in the state kernel's LDS buffer (in the
+// byte variant that buffer holds the code bytes, padded to whole 1 KB
+// copies, then K^T, the fp16 P plane and the gates).
 // The Q operand of the state kernel uses the W image layout and is staged
 // from q directly.
 #pragma once
