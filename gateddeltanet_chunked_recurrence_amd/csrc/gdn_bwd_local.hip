@@ -650,8 +650,19 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   float db_acc[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4 KKt[2];
   // FA1: Q K^T, K K^T, dW K^T on tiles (tw, 2hk + i) -> G, H, dT, dX
+  // (the gate values are read up front, as 16-byte reads where they are
+  // contiguous, so no LDS read waits behind the products)
+  const f32x4 gt4 = *reinterpret_cast<const f32x4*>(&gs.gam2[16 * tw + 4 * grp]);
   {
     float colh[2][4], coldb[2][4];
+    float gs_s2[2], eg_s2[2], bet_s2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int s = 16 * (2 * hk + i) + r16;
+      gs_s2[i] = gs.gam2[s];
+      eg_s2[i] = gs.eg[s];
+      bet_s2[i] = gs.bet[s];
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int st = 2 * hk + i;
@@ -668,12 +679,12 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       const f32x4 xh = tile_of(F.Xm[0], L64, 16 * tw, st, r16, grp, sel);
       const f32x4 xl = tile_of(F.Xm[1], L64, 16 * tw, st, r16, grp, sel);
       const int s = 16 * st + r16;
-      const float gs_s = gs.gam2[s], eg_s = gs.eg[s], bet_s = gs.bet[s];
+      const float gs_s = gs_s2[i], eg_s = eg_s2[i], bet_s = bet_s2[i];
       f32x4 G, dX;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * tw + 4 * grp + q;
-        const float gv = t >= s ? scale * dP[i][q] * fexp2(gs.gam2[t] - gs_s) : 0.f;
+        const float gv = t >= s ? scale * dP[i][q] * fexp2(gt4[q] - gs_s) : 0.f;
         G[q] = gv;
         const float hv = gv * qk[q];
         dg_acc[q] += hv;
@@ -782,6 +793,10 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
 #pragma unroll
       for (int pl = 0; pl < 2; ++pl) AM[kk][pl] = rowp(pl ? M1p1 : M1p0, L64, 16 * tw, 32 * kk, r16, grp);
     float colhl[2][4];
+    const f32x4 bt4 = *reinterpret_cast<const f32x4*>(&gs.bet[16 * tw + 4 * grp]);
+    float gu2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) gu2[i] = gs.gam2[16 * (2 * hk + i) + r16];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int ut = 2 * hk + i;
@@ -791,19 +806,19 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         ml = mm3(ml, AM[kk][0], AM[kk][1], rowp(F.Xm[0], L64, 16 * ut, 32 * kk, r16, grp),
                  rowp(F.Xm[1], L64, 16 * ut, 32 * kk, r16, grp));
       const int u = 16 * ut + r16;
-      const float gu = gs.gam2[u];
+      const float gu = gu2[i];
       f32x4 dA;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * tw + 4 * grp + q;
-        const float gam = t > u ? fexp2(gs.gam2[t] - gu) : 0.f;
+        const float gam = t > u ? fexp2(gt4[q] - gu) : 0.f;
         const float dl = -ml[q];
         const float ag = KKt[i][q] * gam;
         db_acc[q] += dl * ag;
-        const float hl = gs.bet[t] * dl * ag;
+        const float hl = bt4[q] * dl * ag;
         dg_acc[q] += hl;
         colhl[i][q] = hl;
-        dA[q] = dl * gs.bet[t] * gam;
+        dA[q] = dl * bt4[q] * gam;
       }
       put_N(F.GA[0], F.GA[1], L64, dA, tw, ut, r16, grp, sel);
       put_T(F.GTA[0], F.GTA[1], L64, dA, tw, ut, r16, grp);
