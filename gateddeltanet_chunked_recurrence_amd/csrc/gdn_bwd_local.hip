@@ -617,6 +617,16 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     if (half) *reinterpret_cast<bf16*>(p) = to_bf16(v);
     else *reinterpret_cast<float*>(p) = v;
   };
+  // One bf16 gradient tile (rows 16 tw.., columns 16 kt..; accumulator
+  // layout) stored through a matrix-core transpose: the rounded values are
+  // exact in bf16, and each lane then holds four adjacent columns of one row,
+  // one 8-byte store instead of four 2-byte ones. (bf16 outputs only.)
+  auto put_tile_half = [&](char* base, int kt, const f32x4& v) {
+    const f32x4 tt = trans1(to_bf16x4(v), sel);
+    const int t = 16 * tw + r16;
+    if (t < nc)
+      *reinterpret_cast<bf16x4*>(base + t * rstride + (16 * kt + 4 * grp) * 2) = to_bf16x4(tt);
+  };
   GDN_REFRESH();
   {
 #pragma unroll
@@ -743,18 +753,21 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       }
       const f32x4 qv = tile_of(F.QM1m, FLDK, 16 * tw, kt, r16, grp, sel);
       const f32x4 kv = tile_of(F.Km, FLDK, 16 * tw, kt, r16, grp, sel);
+      f32x4 dqv;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * tw + 4 * grp + q;
         const float qi = scale * eg4[q] * dQi[j][q];
         dg_acc[q] += qi * qv[q];
-        if (t < nc) put_grad(dq_base, t, col, qi + gk[q]);
+        dqv[q] = qi + gk[q];
+        if (!half && t < nc) put_grad(dq_base, t, col, dqv[q]);
         const float ks = egc4[q] * dKs[j][q];
         term_acc[q] += ks * kv[q];
         const float wv = xw[q] * bet4[q] * eg4[q];
         dg_acc[q] += wv * kv[q];
         dK[j][q] = gq[q] + ks + wv;
       }
+      if (half) put_tile_half(dq_base, kt, dqv);
     }
   }
   // M1^T = dX^T X on tiles (tw, 2hk + i)
@@ -853,10 +866,14 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
         acc = mm2(acc, AAT[kk][0], AAT[kk][1], ck);
       }
       const int col = 16 * (hk * KH + j) + r16;
+      if (half) {
+        put_tile_half(dk_base, hk * KH + j, acc);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = 16 * tw + 4 * grp + q;
-        if (t < nc) put_grad(dk_base, t, col, acc[q]);
+        for (int q = 0; q < 4; ++q) {
+          const int t = 16 * tw + 4 * grp + q;
+          if (t < nc) put_grad(dk_base, t, col, acc[q]);
+        }
       }
     }
   }
