@@ -124,6 +124,9 @@ SMALL = [
     # one 64-wide value block per head, varlen with short and empty-tail sequences
     ('varlen_int8_gqa4x16_d128', dict(lengths=[130, 64, 1, 65], Hqk=1, Hv=2, Dv=64,
                                       state_fmt=E4M3, w_fmt=E4M3, block_v=64, h0=True)),
+    # empty sequences first, between and last: their ht is h0, they own no chunk
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[0, 130, 0, 64, 1, 0], Hqk=1, Hv=2,
+                                      state_fmt=E4M3, w_fmt=E4M3, h0=True)),
 ]
 
 
