@@ -31,6 +31,16 @@ positions i, j = 1..n) with incoming state S:
 ht is the last S_next, not quantized. Each QDQ is the FP32 function of
 oracle/qdq.py applied to fl32 of its float64 argument; its backward is the
 identity.
+
+Opt-in approximate inverse ("[7/7] Experimental GDN/KDA approximate-inverse
+QAT", "What does this PR do?"): a solve policy with an explicit Neumann
+polynomial degree d replaces the exact solve by
+
+    T_d       = (sum_{m=0..d} (-L)^m) diag(beta)
+
+and the backward differentiates that polynomial (autograd through the same
+sum). L is strictly lower triangular, so (-L)^n = 0 for n >= n_c and any
+d >= n_c - 1 gives the exact inverse.
 """
 import math
 
@@ -70,21 +80,35 @@ def gate_matrix(gam):
     return torch.exp(diff) * lower
 
 
-def wy_factor(Kc, gc, bc):
-    """Chunk-local gate cumsum, L, and T with (I + L) T = diag(beta).
-    Kc: [Z, n, Dk], gc, bc: [Z, n]. Returns (gamma, Gam, L, T)."""
+def neumann_poly(L, degree):
+    """sum_{m=0..degree} (-L)^m, term by term ("[7/7]", "What does this PR
+    do?": the explicit Neumann polynomial of the approximate inverse)."""
+    eye = torch.eye(L.shape[-1], dtype=L.dtype).expand_as(L)
+    term, acc = eye, eye
+    for _ in range(degree):
+        term = term @ (-L)
+        acc = acc + term
+    return acc
+
+
+def wy_factor(Kc, gc, bc, solve_degree=0):
+    """Chunk-local gate cumsum, L, and T with (I + L) T = diag(beta), or with
+    solve_degree > 0 the Neumann polynomial of that degree in place of
+    (I + L)^-1. Kc: [Z, n, Dk], gc, bc: [Z, n]. Returns (gamma, Gam, L, T)."""
     gam = torch.cumsum(gc, dim=-1)
     Gam = gate_matrix(gam)
     n = Kc.shape[1]
     strict = torch.ones(n, n, dtype=torch.bool).tril(-1)
     L = (bc[:, :, None] * (Kc @ Kc.transpose(1, 2)) * Gam) * strict
+    if solve_degree:
+        return gam, Gam, L, neumann_poly(L, solve_degree) @ torch.diag_embed(bc)
     eye = torch.eye(n, dtype=Kc.dtype).expand_as(L)
     T = torch.linalg.solve_triangular(eye + L, torch.diag_embed(bc), upper=False)
     return gam, Gam, L, T
 
 
 def _chunk_loop(Q, K, V, g, beta, S, scale, state_fmt, w_fmt, block_v, chunk,
-                rec, site_fn):
+                rec, site_fn, solve_degree=0):
     """Z independent (sequence, head) streams of equal length.
     Q, K: [Z, L, Dk]; V: [Z, L, Dv]; g, beta: [Z, L]; S: [Z, Dk, Dv]."""
     Z, Lseq, Dk = Q.shape
@@ -93,7 +117,7 @@ def _chunk_loop(Q, K, V, g, beta, S, scale, state_fmt, w_fmt, block_v, chunk,
     for r0 in range(0, Lseq, chunk):
         r1 = min(r0 + chunk, Lseq)
         Qc, Kc, Vc = Q[:, r0:r1], K[:, r0:r1], V[:, r0:r1]
-        gam, Gam, _, T = wy_factor(Kc, g[:, r0:r1], beta[:, r0:r1])
+        gam, Gam, _, T = wy_factor(Kc, g[:, r0:r1], beta[:, r0:r1], solve_degree)
         W = T @ (torch.exp(gam)[:, :, None] * Kc)
         U = T @ Vc
         Wq = W if w_fmt == FMT_OFF else site_fn(W, w_fmt, (1, 2),
@@ -122,7 +146,7 @@ def _as64(x):
 
 def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
                 state_fmt=FMT_OFF, w_fmt=FMT_OFF, block_v=64, chunk=64,
-                record=None, site_fn=None):
+                record=None, site_fn=None, solve_degree=0):
     """q, k: [B, T, Hqk, Dk]; v: [B, T, Hv, Dv]; g, beta: [B, T, Hv];
     h0: [N, Hv, Dk, Dv] or None; cu_seqlens: N+1 offsets (B must be 1).
     float64 torch tensors (autograd flows through them) or arrays.
@@ -134,8 +158,13 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
 
     site_fn: optional replacement for the QDQ step, called as
     site_fn(x, fmt, tile_axes, sink) at every site in a fixed order (W then
-    S, chunk by chunk); used by the tests' frozen-offset surrogate."""
+    S, chunk by chunk); used by the tests' frozen-offset surrogate.
+
+    solve_degree: 0 for the exact solve, else the Neumann polynomial degree
+    (any d >= 1) in its place."""
     site_fn = qdq_ste if site_fn is None else site_fn
+    if solve_degree < 0:
+        raise ValueError("solve_degree must be 0 (exact) or a polynomial degree >= 1")
     q, k, v, g, beta, h0 = map(_as64, (q, k, v, g, beta, h0))
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -172,7 +201,7 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
                                    streams(g[..., None], lo, hi)[..., 0],
                                    streams(beta[..., None], lo, hi)[..., 0],
                                    S0, scale, state_fmt, w_fmt, block_v, chunk, rec,
-                                   site_fn)
+                                   site_fn, solve_degree)
         else:
             o_n, S_n = torch.zeros(S0.shape[0], 0, Dv, dtype=torch.float64), S0
         if record is not None:
@@ -187,7 +216,8 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
 
 
 def chunked_bwd(q, k, v, g, beta, scale, do, dht=None, h0=None, cu_seqlens=None,
-                state_fmt=FMT_OFF, w_fmt=FMT_OFF, block_v=64, chunk=64, site_fn=None):
+                state_fmt=FMT_OFF, w_fmt=FMT_OFF, block_v=64, chunk=64, site_fn=None,
+                solve_degree=0):
     """Reverse-mode derivative of chunked_fwd with every QDQ's Jacobian taken
     as the identity (identity straight-through estimator). The forward values
     of Sq and Wq are used inside every product, as the saved quantized W is
@@ -203,7 +233,8 @@ def chunked_bwd(q, k, v, g, beta, scale, do, dht=None, h0=None, cu_seqlens=None,
         leaves[name] = t
     o, ht = chunked_fwd(leaves['q'], leaves['k'], leaves['v'], leaves['g'],
                         leaves['beta'], scale, leaves.get('h0'), cu_seqlens,
-                        state_fmt, w_fmt, block_v, chunk, site_fn=site_fn)
+                        state_fmt, w_fmt, block_v, chunk, site_fn=site_fn,
+                        solve_degree=solve_degree)
     outs, grads = [o], [_as64(do)]
     if dht is not None:
         outs.append(ht)
