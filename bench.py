@@ -154,6 +154,30 @@ def time_fwd_bwd(steps, warmup):
                 steps=steps)
 
 
+def time_neumann_prep(x, spec, scale, kw, steps, degrees=(3, 31)):
+    """Prep-stage milliseconds on the same workload with the opt-in Neumann
+    solve of each degree in place of the exact solve (the state stage does
+    not change)."""
+    import torch
+
+    from gateddeltanet_chunked_recurrence_amd import binding as B
+    out = {}
+    stream = torch.cuda.current_stream()
+    for d in degrees:
+        plan = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], scale=scale, solve_degree=d,
+                         **kw)
+        plan.prep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            plan.prep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[str(d)] = e0.elapsed_time(e1) / steps
+    return dict(prep_ms_by_degree=out, steps=steps)
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """A plain device copy of known size, for scaling the FETCH_SIZE and
     WRITE_SIZE counters (each copy reads and writes `nbytes`)."""
@@ -172,7 +196,7 @@ def main():
     ap.add_argument('--steps', type=int, default=50)
     ap.add_argument('--warmup', type=int, default=10)
     ap.add_argument('--no-cpu-baseline', action='store_true')
-    ap.add_argument('--no-bwd', action='store_true', help='skip the forward+backward timing')
+    ap.add_argument('--no-bwd', action='store_true', help='skip the forward+backward and Neumann-solve timings')
     ap.add_argument('--copy-calibration', action='store_true',
                     help='only run a 1 GiB device copy (counter calibration)')
     args = ap.parse_args()
@@ -245,6 +269,7 @@ def main():
         source_hash=src)
     if not args.no_bwd:
         out['fwd_bwd'] = time_fwd_bwd(steps=max(3, args.steps // 5), warmup=2)
+        out['neumann_solve'] = time_neumann_prep(x, spec, scale, kw, steps=max(3, args.steps // 5))
     if not args.no_cpu_baseline:
         out['cpu_baseline'] = cpu_baseline(spec, seed=2)
     print(json.dumps(out), flush=True)

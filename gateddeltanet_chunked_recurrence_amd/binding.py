@@ -22,7 +22,8 @@ c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 
 
 class QdqPolicy(ctypes.Structure):
-    _fields_ = [('state_fmt', c_i32), ('w_fmt', c_i32), ('block_v', c_i32), ('chunk_size', c_i32)]
+    _fields_ = [('state_fmt', c_i32), ('w_fmt', c_i32), ('block_v', c_i32), ('chunk_size', c_i32),
+                ('solve_degree', c_i32)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -98,7 +99,7 @@ def _stream(device):
 
 
 def make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v,
-                  o=None, ht=None, saved=None, num_seqs=None):
+                  o=None, ht=None, saved=None, num_seqs=None, solve_degree=0):
     """Fill the forward argument struct from tensor shapes and pointers."""
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -107,7 +108,7 @@ def make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, blo
     io = GDN_F32 if q.dtype == torch.float32 else GDN_BF16
     a = FwdArgs(B=B, T=T, Hqk=Hqk, Hv=Hv, Dk=Dk, Dv=Dv, num_seqs=num_seqs, io_dtype=io,
                 scale=float(1.0 / math.sqrt(Dk) if scale is None else scale),
-                policy=QdqPolicy(state_fmt, w_fmt, block_v, 64))
+                policy=QdqPolicy(state_fmt, w_fmt, block_v, 64, solve_degree))
     for name, t in (('q', q), ('k', k), ('v', v), ('g', g), ('beta', beta), ('h0', h0),
                     ('cu_seqlens', cu_seqlens), ('o', o), ('ht', ht), ('saved', saved)):
         setattr(a, name, _ptr(t))
@@ -121,12 +122,15 @@ def saved_layout(args):
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_fmt=QDQ_OFF,
-                  w_fmt=QDQ_OFF, block_v=64, output_final_state=True, save_for_backward=False):
+                  w_fmt=QDQ_OFF, block_v=64, output_final_state=True, save_for_backward=False,
+                  solve_degree=0):
     """Chunked forward on q's device and torch's current stream.
 
     q, k [B, T, Hqk, Dk], v [B, T, Hv, Dv] (bf16, or FP32 with Dk = 64);
     g, beta [B, T, Hv] FP32; h0 [N, Hv, Dk, Dv] FP32 or None; cu_seqlens int32
-    [N + 1] (B = 1) or None. Returns (o, ht or None, saved uint8 buffer or None).
+    [N + 1] (B = 1) or None. solve_degree: 0 for the exact solve, or a
+    Neumann degree 1, 3, 7, 15, 31, 63 (bf16 inputs, forward only).
+    Returns (o, ht or None, saved uint8 buffer or None).
     """
     lib = load_library()
     dev = q.device
@@ -135,7 +139,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
     N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
     o = torch.empty(B, T, Hv, Dv, dtype=q.dtype, device=dev)
     ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
-    a = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v, o, ht)
+    a = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v, o, ht,
+                      solve_degree=solve_degree)
     saved = None
     if save_for_backward:
         nbytes = lib.gdn_saved_bytes(ctypes.byref(a))
@@ -157,7 +162,7 @@ class FwdPlan:
     stream: plan.prep(); plan.state(). Outputs: plan.o, plan.ht."""
 
     def __init__(self, q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None,
-                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64):
+                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0):
         lib = load_library()
         dev = q.device
         B, T, Hqk, Dk = q.shape
@@ -167,7 +172,7 @@ class FwdPlan:
         self.ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev)
         self._keep = (q, k, v, g, beta, h0, cu_seqlens)
         self.args = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt,
-                                  block_v, self.o, self.ht)
+                                  block_v, self.o, self.ht, solve_degree=solve_degree)
         wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(self.args))
         self.ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
         self.args.workspace = _ptr(self.ws)
@@ -182,9 +187,11 @@ class FwdPlan:
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu_seqlens=None,
-                  state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, grad_dtype=None):
+                  state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, grad_dtype=None, solve_degree=0):
     """Backward of gdn_chunk_fwd (identity straight-through at both QDQ sites)
-    from the forward's `saved` buffer. Returns dict dq, dk, dv, dg, dbeta, dh0."""
+    from the forward's `saved` buffer. Returns dict dq, dk, dv, dg, dbeta, dh0.
+    The library rejects solve_degree > 0 (the Neumann solve's backward is not
+    built)."""
     lib = load_library()
     dev = q.device
     B, T, Hqk, Dk = q.shape
@@ -199,7 +206,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu
                dh0=torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev)
                if h0 is not None else None)
     fa = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v,
-                       saved=saved)
+                       saved=saved, solve_degree=solve_degree)
     a = BwdArgs(fwd=fa, do_=_ptr(do), dht=_ptr(dht),
                 grad_dtype=GDN_F32 if gd == torch.float32 else GDN_BF16,
                 dq=_ptr(out['dq']), dk=_ptr(out['dk']), dv=_ptr(out['dv']), dg=_ptr(out['dg']),

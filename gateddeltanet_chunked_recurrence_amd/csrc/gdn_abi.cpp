@@ -38,6 +38,11 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
   const gdn_qdq_policy& p = a->policy;
   if (p.chunk_size != 64)
     return fail(GDN_E_UNSUPPORTED, "chunk_size %d: only 64 is supported", p.chunk_size);
+  if (p.solve_degree != 0 && p.solve_degree != 1 && p.solve_degree != 3 && p.solve_degree != 7 &&
+      p.solve_degree != 15 && p.solve_degree != 31 && p.solve_degree != 63)
+    return fail(GDN_E_UNSUPPORTED,
+                "solve_degree %d: 0 (exact) or a Neumann degree 1, 3, 7, 15, 31 or 63",
+                p.solve_degree);
   if (!valid_fmt(p.state_fmt) || !valid_fmt(p.w_fmt))
     return fail(GDN_E_UNSUPPORTED, "unknown QDQ format (state %d, w %d): use 0 off, 1 E4M3, 2 INT8",
                 p.state_fmt, p.w_fmt);
@@ -54,6 +59,8 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
     return fail(GDN_E_INVALID, "io_dtype %d: use 0 bf16 or 1 f32", a->io_dtype);
   if (a->io_dtype == GDN_F32 && a->Dk != 64)
     return fail(GDN_E_UNSUPPORTED, "FP32 inputs are built for Dk = 64 only (got %d)", a->Dk);
+  if (a->io_dtype == GDN_F32 && p.solve_degree != 0)
+    return fail(GDN_E_UNSUPPORTED, "the Neumann solve is built for bf16 inputs only");
   if (p.state_fmt != GDN_QDQ_OFF) {
     if (p.block_v != 16 && p.block_v != 32 && p.block_v != 64)
       return fail(GDN_E_UNSUPPORTED, "block_v %d: supported 16, 32, 64", p.block_v);
@@ -276,6 +283,7 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
   // with both QDQ sites on, the state kernel widens the W codes itself, so
   // the images carry them as bytes
   k.w_img_bytes = (a->policy.state_fmt != GDN_QDQ_OFF && a->policy.w_fmt != GDN_QDQ_OFF) ? 1 : 0;
+  k.solve_degree = a->policy.solve_degree;
   if (stages & 1) {
     const int num_slots = (int)layout_of(a).num_slots;
     s = hip_status(gdn::launch_fwd_prep(cfg, k, num_slots, st), "gdn_chunk_fwd prep launch");
@@ -306,6 +314,9 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   if (!a) return fail(GDN_E_INVALID, "argument struct is NULL");
   gdn_status s = check_fwd_shape(&a->fwd);
   if (s != GDN_OK) return s;
+  if (a->fwd.policy.solve_degree != 0)
+    return fail(GDN_E_UNSUPPORTED, "the backward of the Neumann solve (degree %d) is not built",
+                a->fwd.policy.solve_degree);
   if ((s = check_fwd_ptrs(&a->fwd, false)) != GDN_OK) return s;
   const bool any = (int64_t)a->fwd.B * a->fwd.T > 0;
   if (a->grad_dtype != GDN_F32 && a->grad_dtype != a->fwd.io_dtype)

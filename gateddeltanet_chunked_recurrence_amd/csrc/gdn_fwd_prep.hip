@@ -86,6 +86,38 @@ __device__ __forceinline__ f32x4 mm32(const float* A, int ars, const float* B, i
   return acc;
 }
 
+// acc += A(16 ti + r, k) B(k, 16 tj + c) over the key blocks tj..ti of two
+// lower triangular FP32 64x65 matrices; a block's eight reads are issued
+// before its four products.
+__device__ __forceinline__ f32x4 mm_lower(const float* A, const float* B, int ti, int tj, int r16,
+                                          int grp, f32x4 acc) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (kb < tj || kb > ti) continue;
+    float av[4], bv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      av[s] = A[(16 * ti + r16) * 65 + 16 * kb + 4 * s + grp];
+      bv[s] = B[(16 * kb + 4 * s + grp) * 65 + 16 * tj + r16];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_f32(av[s], bv[s], acc);
+  }
+  return acc;
+}
+
+// The two 16x16 output tiles (ti, tj) of a wave in a product of lower
+// triangular 64x64 matrices: the ten lower tiles (1 to 4 key blocks each, 20
+// in all) at most 4 blocks per wave, the six upper tiles (zero) on the rest.
+__device__ __forceinline__ void lower_tiles(int wave, int (&ti)[2], int (&tj)[2]) {
+  static constexpr int8_t tab[8][4] = {{3, 0, 2, 3}, {3, 1, 0, 0}, {2, 0, 1, 1}, {2, 1, 3, 2},
+                                       {1, 0, 2, 2}, {3, 3, 0, 1}, {0, 2, 0, 3}, {1, 2, 1, 3}};
+  ti[0] = tab[wave][0];
+  tj[0] = tab[wave][1];
+  ti[1] = tab[wave][2];
+  tj[1] = tab[wave][3];
+}
+
 // Writes 4 consecutive bf16 at dst (8-byte aligned).
 __device__ __forceinline__ void st4(bf16* dst, bf16 a, bf16 b, bf16 c, bf16 d) {
   *reinterpret_cast<bf16x4*>(dst) = bf16x4{a, b, c, d};
@@ -481,6 +513,71 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     }
     lds_barrier();
     GDN_REFRESH();
+
+    // Opt-in approximate inverse: X = sum_{m <= d} (-L)^m, d = 2^j - 1 (the
+    // library admits no other degree), in place of the exact X above. The
+    // polynomial is the product (I - L)(I + L^2)(I + L^4)...: with P =
+    // (-L)^(2^i), each step squares P and sets X <- X + X P. The factors are
+    // lower triangular, so an output tile (ti, tj), ti >= tj, sums the key
+    // blocks tj..ti only; upper tiles of X are written as zero, those of P are
+    // never read. FP32 MFMA; four 64x65 buffers rotate: L, X and two in the
+    // T-plane area, which phase 4 fills only after this.
+    if (a.solve_degree > 0) {
+      static_assert(sizeof(sm.c) >= 2 * 64 * 65 * sizeof(float), "two FP32 64x65 buffers");
+      float* const C0 = reinterpret_cast<float*>(&sm.c);
+      auto buf = [&](int b) -> float* {
+        return b == 0 ? sm.b.s.L : (b == 1 ? sm.b.s.X : (b == 2 ? C0 : C0 + 64 * 65));
+      };
+      for (int e = tid; e < 64 * 64; e += NT) {
+        const int i = e >> 6, j = e & 63;
+        const float l = (i >> 4) >= (j >> 4) ? sm.b.s.L[i * 65 + j] : 0.f;   // strict lower (masked)
+        C0[i * 65 + j] = -l;
+        sm.b.s.X[i * 65 + j] = j > i ? 0.f : (i == j ? 1.f : -l);
+      }
+      lds_barrier();
+      int ip = 2, ix = 1;                          // P = -L in buffer 2, X = I - L in buffer 1
+      for (int d = 1; d < a.solve_degree; d = 2 * d + 1) {
+        const int np = ip == 2 ? 0 : 2, nx = ix == 1 ? 3 : 1;
+        const float* P = buf(ip);
+        float* Pn = buf(np);
+        int ti[2], tj[2];
+        lower_tiles(wave, ti, tj);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (ti[hh] >= tj[hh]) {
+            const f32x4 z = mm_lower(P, P, ti[hh], tj[hh], r16, grp, zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Pn[(16 * ti[hh] + 4 * grp + i) * 65 + 16 * tj[hh] + r16] = z[i];
+          }
+        }
+        lds_barrier();
+        const float* X = buf(ix);
+        float* Xn = buf(nx);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f32x4 z = zero4();
+          if (ti[hh] >= tj[hh]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = X[(16 * ti[hh] + 4 * grp + i) * 65 + 16 * tj[hh] + r16];
+            z = mm_lower(X, Pn, ti[hh], tj[hh], r16, grp, z);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Xn[(16 * ti[hh] + 4 * grp + i) * 65 + 16 * tj[hh] + r16] = z[i];
+        }
+        lds_barrier();
+        ip = np;
+        ix = nx;
+      }
+      if (ix != 1) {                               // an odd number of steps leaves X in buffer 3
+        const float* X = buf(ix);
+        for (int e = tid; e < 64 * 64; e += NT) {
+          const int i = e >> 6, j = e & 63;
+          sm.b.s.X[i * 65 + j] = X[i * 65 + j];
+        }
+        lds_barrier();
+      }
+      GDN_REFRESH();
+    }
 
     // X for the backward (saved buffer), row-major FP32
     if (a.s_X) {

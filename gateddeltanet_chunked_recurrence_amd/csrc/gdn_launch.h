@@ -27,6 +27,7 @@ struct FwdKernelArgs {
   float* ws_u;                // [slots * Hv][Dv * 64] fragment order
   float* ws_wscale;           // [slots * Hv]
   int32_t w_img_bytes;        // 1: the W plane of the images holds code bytes (both QDQ sites on)
+  int32_t solve_degree;       // 0: exact (I + L)^-1; else the Neumann polynomial of this degree (2^j - 1)
   int32_t T;                  // tokens per sequence (no cu_seqlens)
   int32_t Hqk, Hv, Dv, block_v;
   float scale;

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
   GDN_OK = 0,
@@ -72,6 +72,17 @@ typedef struct {
   int32_t block_v;     /* state scale tile width: 16, 32, 64 or 128; divides Dv
                           (ignored when state_fmt == OFF)                    */
   int32_t chunk_size;  /* must be 64                                         */
+  int32_t solve_degree;/* 0: exact solve of the WY form (the default). d > 0:
+                          opt-in approximate inverse ("[7/7] Experimental
+                          GDN/KDA approximate-inverse QAT", "What does this PR
+                          do?"): (I + L)^-1 is replaced by the Neumann
+                          polynomial sum_{m=0..d} (-L)^m, in FP32. d must be
+                          2^j - 1 for j = 1..6 (1, 3, 7, 15, 31, 63); any
+                          other value is GDN_E_UNSUPPORTED, never rounded to
+                          a supported one. Built for bf16 inputs and the
+                          forward only: FP32 inputs and gdn_chunk_bwd return
+                          GDN_E_UNSUPPORTED for d > 0. The saved buffer's x
+                          section then holds the polynomial, not the inverse. */
 } gdn_qdq_policy;
 
 /* Forward arguments. Shapes: without cu_seqlens there are N = B sequences of

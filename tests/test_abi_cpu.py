@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 3
+    assert lib.gdn_abi_version() == 4
 
 
 def _args(**kw):
@@ -36,7 +36,7 @@ def _args(**kw):
     for name in ('q', 'k', 'v', 'g', 'beta', 'o'):
         setattr(a, name, fake)
     for k, v in kw.items():
-        if k in ('state_fmt', 'w_fmt', 'block_v', 'chunk_size'):
+        if k in ('state_fmt', 'w_fmt', 'block_v', 'chunk_size', 'solve_degree'):
             setattr(a.policy, k, v)
         else:
             setattr(a, k, v)
@@ -61,6 +61,12 @@ BAD = [
     (dict(o=None), B.GDN_E_INVALID, 'o is NULL'),
     (dict(k=ctypes.c_void_p(0x10004)), B.GDN_E_INVALID, 'aligned'),
     (dict(T=-1), B.GDN_E_INVALID, 'bad sizes'),
+    # the Neumann degree is 2^j - 1 (j = 1..6), never rounded to a supported one
+    (dict(solve_degree=2), B.GDN_E_UNSUPPORTED, 'solve_degree'),
+    (dict(solve_degree=5), B.GDN_E_UNSUPPORTED, 'solve_degree'),
+    (dict(solve_degree=127), B.GDN_E_UNSUPPORTED, 'solve_degree'),
+    (dict(solve_degree=-1), B.GDN_E_UNSUPPORTED, 'solve_degree'),
+    (dict(solve_degree=3, io_dtype=1, Dk=64), B.GDN_E_UNSUPPORTED, 'Neumann'),
 ]
 
 
@@ -142,6 +148,21 @@ def test_backward_rejects_before_launch():
     a.fwd.saved = fake
     a.grad_dtype = 5
     assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_INVALID
+
+
+def test_backward_of_the_neumann_solve_is_rejected():
+    """The Neumann polynomial's backward is not built: a valid degree is
+    refused by gdn_chunk_bwd (never run with the exact solve's gradient),
+    before any pointer or workspace check."""
+    lib = B.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    a = B.BwdArgs(fwd=_args(saved=fake, solve_degree=7), do_=fake, dq=fake, dk=fake, dv=fake,
+                  dg=fake, dbeta=fake, grad_dtype=B.GDN_BF16)
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_UNSUPPORTED
+    assert 'Neumann' in lib.gdn_last_error().decode()
+    for d in (1, 3, 7, 15, 31, 63):                   # every admitted degree passes the forward checks
+        f = _args(solve_degree=d)
+        assert lib.gdn_fwd_workspace_bytes(ctypes.byref(f)) > 0
 
 
 def test_qdq_state_rejects_before_launch():
