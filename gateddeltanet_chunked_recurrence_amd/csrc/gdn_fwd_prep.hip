@@ -247,7 +247,9 @@ __device__ PrepItem next_item(const FwdKernelArgs& a, int N, int i, int stride, 
   return it;
 }
 
-template <int DK, int DV, int WF>
+// NEU: the instantiation that carries the approximate inverse (the exact-solve
+// instantiation does not contain its code).
+template <int DK, int DV, int WF, bool NEU>
 __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
   using I = Img<DK>;
   constexpr int LDK = PrepSmem<DK>::LDK;
@@ -522,7 +524,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     // blocks tj..ti only; upper tiles of X are written as zero, those of P are
     // never read. FP32 MFMA; four 64x65 buffers rotate: L, X and two in the
     // T-plane area, which phase 4 fills only after this.
-    if (a.solve_degree > 0) {
+    if (NEU && a.solve_degree > 0) {
       static_assert(sizeof(sm.c) >= 2 * 64 * 65 * sizeof(float), "two FP32 64x65 buffers");
       float* const C0 = reinterpret_cast<float*>(&sm.c);
       auto buf = [&](int b) -> float* {
@@ -768,8 +770,12 @@ static hipError_t launch_prep_one(const FwdConfig& cfg, const FwdKernelArgs& a, 
                                   hipStream_t s) {
   const int64_t items = (int64_t)num_slots * cfg.Hv;
   const int64_t nblk = items < device_cus() ? items : device_cus();   // one workgroup per CU
-  hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF>), dim3((unsigned)nblk), dim3(NT), 0, s, a, cfg.N,
-                     num_slots);
+  if (a.solve_degree > 0)
+    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
+                       cfg.N, num_slots);
+  else
+    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, false>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
+                       cfg.N, num_slots);
   return hipGetLastError();
 }
 
