@@ -8,7 +8,8 @@ same degree, over ragged chunks, grouped heads, packed sequences and both
 state-kernel paths (both QDQ sites on, and QDQ off), with the forward's bars
 (rel-L2 2e-3 with QDQ off, 1e-2 with QDQ on). With QDQ off the kernel's
 final state is over a hundred times closer to the degree-1 oracle than to the
-exact solve's, so a kernel that ignored the degree would fail there."""
+exact solve's, so a kernel that ignored the degree would fail there. The forward workload runs
+at full size at degrees 3 and 31 on sampled heads."""
 import pytest
 import torch
 
@@ -56,6 +57,22 @@ def test_neumann_forward_matches_oracle(name, over, degree):
         say(f"  oracle ht, degree 1 vs exact: {gap:.3e}")
         assert gap > 1e-3
         assert rel(ht[:, heads], ht_x) > 100 * r_h
+
+
+@pytest.mark.parametrize("degree", [3, 31])
+def test_neumann_forward_workload_sampled_heads(degree):
+    """The forward workload at full size (B=4, T=4096, H=16, D=128, E4M3 at
+    both sites), as bench.py times the Neumann prep stage, on two sampled
+    heads (heads are independent, so the oracle computes exactly those)."""
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128')
+    say(f"neumann workload degree={degree}")
+    x = draw(spec, 2)
+    o, ht, _ = gpu_fwd(x, spec, solve_degree=degree)
+    heads = [4, 13]
+    o_ref, ht_ref = oracle_fwd(head_subset(x, spec, heads), spec, solve_degree=degree)
+    r_o, r_h = rel(o[:, :, heads].float(), o_ref), rel(ht[:, heads], ht_ref)
+    say(f"  rel-L2 O={r_o:.3e} ht={r_h:.3e}")
+    assert r_o <= 1e-2 and r_h <= 1e-2
 
 
 def test_neumann_backward_is_refused():
