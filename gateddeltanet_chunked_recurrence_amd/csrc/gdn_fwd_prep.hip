@@ -402,7 +402,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     GDN_REFRESH();
 
     // ---- 3. wave 0: diagonal blocks of X; others: P image out, X upper zero, V^T in
+    // (the approximate-inverse instantiation skips the solve's arithmetic here
+    // and in the merges below, keeping their loads and barriers: X is formed
+    // from L after this phase)
     if (wave == 0) {
+      if constexpr (!NEU) {
       // lane (b, cc): column cc of the inverse of diagonal block b, by rows;
       // row r of the block is read as 16-byte pieces (all 16 lanes of a
       // block read the same row), independent of the substitution itself
@@ -435,6 +439,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) sm.b.s.X[(16 * b + r) * 65 + 16 * b + cc] = x[r];
+      }
     } else {
       const int t = tid - 64;
       // K^T and P images: 16-byte copies of the LDS tiles (adjacent in the
@@ -470,15 +475,17 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     if (nxt.valid && !merger) load_kqg(nxt);
     // 16-block merges X_BA = -X_BB (L_BA X_AA), (A, B) = (0, 1) and (2, 3)
     if (merger) {
-      const int A = 2 * (wave - 1), B = A + 1;
-      const f32x4 y = mm32(&sm.b.s.L[(16 * B) * 65 + 16 * A], 65, &sm.b.s.X[(16 * A) * 65 + 16 * A],
-                           65, 0, 0, 0, 16, r16, grp, zero4());
-      f32x4 z = zero4();
+      if constexpr (!NEU) {
+        const int A = 2 * (wave - 1), B = A + 1;
+        const f32x4 y = mm32(&sm.b.s.L[(16 * B) * 65 + 16 * A], 65, &sm.b.s.X[(16 * A) * 65 + 16 * A],
+                             65, 0, 0, 0, 16, r16, grp, zero4());
+        f32x4 z = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i)                 // K order 4 grp + i
-        z = mfma_f32(sm.b.s.X[(16 * B + r16) * 65 + 16 * B + 4 * grp + i], y[i], z);
+        for (int i = 0; i < 4; ++i)               // K order 4 grp + i
+          z = mfma_f32(sm.b.s.X[(16 * B + r16) * 65 + 16 * B + 4 * grp + i], y[i], z);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.b.s.X[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
+        for (int i = 0; i < 4; ++i) sm.b.s.X[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
+      }
       if (nxt.valid) load_kqg(nxt);
     }
     lds_barrier();
@@ -488,15 +495,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     {
       const int t4 = wave & 3, ti = t4 >> 1, tj = t4 & 1, kh = wave >> 2;
       const int k0 = 16 * tj, km = 16 + 8 * tj;    // X_AA rows < 16 tj are zero in column tile tj
-      const f32x4 y = mm32(&sm.b.s.L[32 * 65], 65, sm.b.s.X, 65, 16 * ti, 16 * tj, kh ? km : k0,
-                           kh ? 32 : km, r16, grp, zero4());
+      f32x4 y = zero4();
       float* yp = &sm.c.Y[(16 * ti + 4 * grp) * 33 + 16 * tj + r16];
-      if (kh == 0) {
+      if constexpr (!NEU) {
+        y = mm32(&sm.b.s.L[32 * 65], 65, sm.b.s.X, 65, 16 * ti, 16 * tj, kh ? km : k0, kh ? 32 : km,
+                 r16, grp, zero4());
+        if (kh == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) yp[i * 33] = y[i];
+          for (int i = 0; i < 4; ++i) yp[i * 33] = y[i];
+        }
       }
       lds_barrier();
-      if (kh == 1) {
+      if (!NEU && kh == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) yp[i * 33] += y[i];
       }
@@ -506,25 +516,27 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     // X_BA = -X_BB Y (one 16x16 tile per wave 0..3; waves 4..7 issue their V loads first)
     if (wave >= 4 && nxt.valid) load_v(nxt);
     if (wave < 4) {
-      const int ti = wave >> 1, tj = wave & 1;
-      const f32x4 z = mm32(&sm.b.s.X[32 * 65 + 32], 65, sm.c.Y, 33, 16 * ti, 16 * tj, 0, 16 * ti + 16,
-                           r16, grp, zero4());
+      if constexpr (!NEU) {
+        const int ti = wave >> 1, tj = wave & 1;
+        const f32x4 z = mm32(&sm.b.s.X[32 * 65 + 32], 65, sm.c.Y, 33, 16 * ti, 16 * tj, 0,
+                             16 * ti + 16, r16, grp, zero4());
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.b.s.X[(32 + 16 * ti + 4 * grp + i) * 65 + 16 * tj + r16] = -z[i];
+        for (int i = 0; i < 4; ++i) sm.b.s.X[(32 + 16 * ti + 4 * grp + i) * 65 + 16 * tj + r16] = -z[i];
+      }
       if (nxt.valid) load_v(nxt);
     }
     lds_barrier();
     GDN_REFRESH();
 
     // Opt-in approximate inverse: X = sum_{m <= d} (-L)^m, d = 2^j - 1 (the
-    // library admits no other degree), in place of the exact X above. The
+    // library admits no other degree), in place of the exact solve. The
     // polynomial is the product (I - L)(I + L^2)(I + L^4)...: with P =
     // (-L)^(2^i), each step squares P and sets X <- X + X P. The factors are
     // lower triangular, so an output tile (ti, tj), ti >= tj, sums the key
     // blocks tj..ti only; upper tiles of X are written as zero, those of P are
     // never read. FP32 MFMA; four 64x65 buffers rotate: L, X and two in the
     // T-plane area, which phase 4 fills only after this.
-    if (NEU && a.solve_degree > 0) {
+    if constexpr (NEU) {
       static_assert(sizeof(sm.c) >= 2 * 64 * 65 * sizeof(float), "two FP32 64x65 buffers");
       float* const C0 = reinterpret_cast<float*>(&sm.c);
       auto buf = [&](int b) -> float* {
