@@ -101,3 +101,31 @@ def test_qdq_state_e4m3_sweeps_every_rounding_boundary():
     np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32),
                                   want.reshape(n, Dk, Dv).view(np.uint32))
     np.testing.assert_array_equal(codes.cpu().numpy(), code_bytes(c.reshape(n, Dk, Dv), 1))
+
+
+def test_qdq_state_rounded_reciprocal_tiles():
+    """The fixture tiles of tests/golden/qdq_reciprocal.json (values on which
+    x * fl32(1/d) and x / d round to different codes, both formats) through
+    gdn_qdq_state as [16, 16] state tiles: the kernel's codes are the
+    reciprocal-form codes stored there ("[2/4] GDN/KDA decode QAT with INT8
+    recurrent state", "Testing"), and differ from the division form's."""
+    import json
+    import os
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'golden', 'qdq_reciprocal.json')
+    tiles = json.load(open(p))['tiles']
+    for fmt in (1, 2):
+        sel = [t for t in tiles if t['fmt'] == fmt]
+        say(f"qdq_state reciprocal fixture fmt={fmt}: {len(sel)} tiles")
+        x = np.stack([np.array(t['x_bits'], np.uint32).view(np.float32).reshape(16, 16)
+                      for t in sel])
+        y, scales, codes = B.gdn_qdq_state(torch.from_numpy(x).cuda(), fmt, 16, return_codes=True)
+        torch.cuda.synchronize()
+        want = np.stack([np.float32(t['codes']).reshape(16, 16) for t in sel])
+        div = np.stack([np.float32(t['div_codes']).reshape(16, 16) for t in sel])
+        np.testing.assert_array_equal(codes.cpu().numpy(), code_bytes(want, fmt))
+        d = np.array([t['d_bits'] for t in sel], np.uint32)
+        np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32)[:, 0], d)
+        np.testing.assert_array_equal(
+            y.cpu().numpy().view(np.uint32),
+            (want * d.view(np.float32)[:, None, None]).astype(np.float32).view(np.uint32))
+        assert np.sum(want != div) >= 30 * len(sel)

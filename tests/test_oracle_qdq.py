@@ -143,18 +143,33 @@ def test_qdq_tiles_are_independent():
     np.testing.assert_array_equal(out[:, :, 0], out2[:, :, 0])
 
 
+def _reciprocal_fixture():
+    import json
+    import os
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'golden', 'qdq_reciprocal.json')
+    return json.load(open(p))['tiles']
+
+
 def test_qdq_uses_rounded_reciprocal():
-    """y = x * fl32(1/d), not x / d: find an input where the two differ on
-    the E4M3 grid and check the reciprocal form is the one taken."""
-    rng = np.random.default_rng(4)
-    found = 0
-    for _ in range(200):
-        x = rng.standard_normal((1, 64)).astype(np.float32)
-        out, c, d = qdq32(x, FMT_E4M3, (1,))
-        r = np.float32(1.0) / d
-        y_mul = (x * r).astype(np.float32)
-        y_div = (x / d).astype(np.float32)
-        c_div = round_e4m3(y_div)
-        np.testing.assert_array_equal(c, round_e4m3(y_mul))
-        found += int(np.any(c_div != c) or np.any(y_mul != y_div))
-    assert found > 0
+    """y = x * fl32(1/d), not x / d ("[2/4] GDN/KDA decode QAT with INT8
+    recurrent state", "Testing": rounded reciprocal multiplication). The
+    fixture tiles (tests/golden/make_qdq_reciprocal.py) hold, for both
+    formats and non-power-of-two scales, 40 values each whose codes differ
+    between the two forms; the oracle must give the reciprocal-form codes on
+    every element, which plain division misses on those 40."""
+    tiles = _reciprocal_fixture()
+    assert {t['fmt'] for t in tiles} == {FMT_E4M3, FMT_INT8}
+    for t in tiles:
+        x = np.array(t['x_bits'], np.uint32).view(np.float32)[None]
+        out, c, d = qdq32(x, t['fmt'], (1,))
+        assert np.array(d[0, 0], np.float32).view(np.uint32) == t['d_bits']
+        np.testing.assert_array_equal(c[0], np.float32(t['codes']))
+        # the stored codes separate the two conventions on many elements
+        differ = np.float32(t['codes']) != np.float32(t['div_codes'])
+        assert differ.sum() >= 30, differ.sum()
+        # and the division form really gives the other codes on this input
+        dd = np.float32(d[0, 0])
+        c_div = round_e4m3((x[0] / dd).astype(np.float32)) if t['fmt'] == FMT_E4M3 else \
+            np.clip(np.rint((x[0] / dd).astype(np.float32).astype(np.float64)), -127, 127)
+        np.testing.assert_array_equal(np.float32(c_div)[differ], np.float32(t['div_codes'])[differ])
+        assert np.all(np.float32(c_div)[differ] != c[0][differ])
