@@ -36,7 +36,8 @@ class FwdArgs(ctypes.Structure):
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [('num_slots', c_i64), ('off_state', c_i64), ('off_state_scale', c_i64),
-                ('off_w', c_i64), ('off_w_scale', c_i64), ('off_x', c_i64), ('total_bytes', c_i64)]
+                ('off_w', c_i64), ('off_w_scale', c_i64), ('off_x', c_i64), ('off_meta', c_i64),
+                ('total_bytes', c_i64)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -69,6 +70,8 @@ def load_library():
         f = getattr(lib, name)
         f.argtypes = argt
         f.restype = c_i32
+    lib.gdn_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+    lib.gdn_device_errors.restype = c_i32
     lib.gdn_saved_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.gdn_saved_bytes.restype = c_sz
     lib.gdn_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
@@ -88,6 +91,17 @@ class GdnError(RuntimeError):
 def _check(status):
     if status != GDN_OK:
         raise GdnError(status, load_library().gdn_last_error().decode())
+
+
+DEVERR_LDS_WAIT, DEVERR_FLAG_WAIT, DEVERR_SAVED_STAMP = 1, 2, 4
+
+
+def device_errors():
+    """Sticky device error flags of the current device (synchronizes, then
+    reads and clears them); 0 when no kernel reported a problem."""
+    v = ctypes.c_uint32(0)
+    _check(load_library().gdn_device_errors(ctypes.byref(v)))
+    return int(v.value)
 
 
 def _ptr(t):
@@ -147,6 +161,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
         if nbytes == 0:
             _check(lib.gdn_chunk_fwd(ctypes.byref(a), None))     # reports the shape error
         saved = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        # the policy travels with the buffer, so the backward cannot pick another
+        saved.gdn_policy = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v,
+                                solve_degree=solve_degree)
         a.saved = _ptr(saved)
     wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
     ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
@@ -187,11 +204,24 @@ class FwdPlan:
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu_seqlens=None,
-                  state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, grad_dtype=None, solve_degree=0):
+                  state_fmt=None, w_fmt=None, block_v=None, grad_dtype=None, solve_degree=None):
     """Backward of gdn_chunk_fwd (identity straight-through at both QDQ sites)
     from the forward's `saved` buffer. Returns dict dq, dk, dv, dg, dbeta, dh0.
-    The library rejects solve_degree > 0 (the Neumann solve's backward is not
-    built)."""
+    Policy arguments left as None are taken from the policy the forward
+    attached to `saved`; one that is given must equal it."""
+    pol = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v, solve_degree=solve_degree)
+    fwd_pol = getattr(saved, 'gdn_policy', None)
+    for key, val in pol.items():
+        if fwd_pol is not None:
+            if val is None:
+                pol[key] = fwd_pol[key]
+            elif val != fwd_pol[key] and not (key == 'block_v' and fwd_pol['state_fmt'] == QDQ_OFF):
+                raise ValueError(f'{key}={val} differs from the forward that wrote `saved` '
+                                 f'({key}={fwd_pol[key]})')
+        elif val is None:
+            pol[key] = dict(state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0)[key]
+    state_fmt, w_fmt, block_v, solve_degree = (pol[k_] for k_ in ('state_fmt', 'w_fmt', 'block_v',
+                                                                 'solve_degree'))
     lib = load_library()
     dev = q.device
     B, T, Hqk, Dk = q.shape

@@ -8,14 +8,38 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <cstring>
+#include <mutex>
 
 #include "../../include/gdn.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
 
+// Sticky device error flags (gdn::kErr* bits): kernels set them instead of
+// failing silently, gdn_device_errors() reads and clears them. One copy per
+// device (a file-scope device variable exists once on every GPU the library
+// runs on).
+__device__ __align__(256) uint32_t gdn_err_flags[64];
+
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Device address of gdn_err_flags on the current device, looked up once per
+// device (the host name of a device variable is not its device address).
+uint32_t* err_word() {
+  static std::mutex mu;
+  static uint32_t* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(gdn_err_flags)) != hipSuccess) return nullptr;
+    ptrs[dev] = static_cast<uint32_t*>(p);
+  }
+  return ptrs[dev];
+}
 
 gdn_status fail(gdn_status s, const char* fmt, ...) {
   va_list ap;
@@ -114,6 +138,8 @@ gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
   off = round256(off + (wq ? L.num_slots * a->Hv * 4 : 0));
   L.off_x = off;
   off = round256(off + (a->io_dtype == GDN_BF16 ? L.num_slots * a->Hv * 64 * 64 * 4 : 0));
+  L.off_meta = off;
+  off = round256(off + 64);
   L.total_bytes = off;
   return L;
 }
@@ -170,7 +196,9 @@ gdn::FwdKernelArgs kernel_args(const gdn_fwd_args* a, void* saved) {
       k.w_scale = reinterpret_cast<float*>(base + L.off_w_scale);
     }
     if (a->io_dtype == GDN_BF16) k.s_X = reinterpret_cast<float*>(base + L.off_x);
+    k.s_meta = reinterpret_cast<uint32_t*>(base + L.off_meta);
   }
+  k.err = err_word();
   k.T = a->T;
   k.Hqk = a->Hqk;
   k.Hv = a->Hv;
@@ -224,6 +252,24 @@ BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
   return w;
 }
 
+// The policy and shape a saved buffer is written under.
+gdn::SavedStamp stamp_of(const gdn_fwd_args* a) {
+  gdn::SavedStamp st{};
+  const gdn_qdq_policy& p = a->policy;
+  const uint32_t w[] = {gdn::SavedStamp::kMagic, (uint32_t)GDN_ABI_VERSION, (uint32_t)p.state_fmt,
+                        (uint32_t)p.w_fmt,
+                        (uint32_t)(p.state_fmt != GDN_QDQ_OFF ? p.block_v : 0),
+                        (uint32_t)p.solve_degree, (uint32_t)a->B, (uint32_t)a->T,
+                        (uint32_t)a->Hqk, (uint32_t)a->Hv, (uint32_t)a->Dk, (uint32_t)a->Dv,
+                        (uint32_t)a->num_seqs, (uint32_t)a->io_dtype};
+  static_assert(sizeof(w) / sizeof(w[0]) <= 15, "stamp words");
+  for (size_t i = 0; i < sizeof(w) / sizeof(w[0]); ++i) st.w[i] = w[i];
+  uint32_t sb;
+  std::memcpy(&sb, &a->scale, 4);
+  st.w[15] = sb;
+  return st;
+}
+
 gdn_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(GDN_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return GDN_OK;
@@ -234,6 +280,19 @@ gdn_status hip_status(hipError_t e, const char* what) {
 extern "C" {
 
 const char* gdn_last_error(void) { return g_err; }
+
+gdn_status gdn_device_errors(uint32_t* flags) {
+  if (!flags) return fail(GDN_E_INVALID, "flags is NULL");
+  uint32_t* w = err_word();
+  if (!w) return fail(GDN_E_HIP, "device error word unavailable on the current device");
+  gdn_status s = hip_status(hipDeviceSynchronize(), "gdn_device_errors synchronize");
+  if (s != GDN_OK) return s;
+  if ((s = hip_status(hipMemcpy(flags, w, 4, hipMemcpyDeviceToHost), "gdn_device_errors read")) !=
+      GDN_OK)
+    return s;
+  const uint32_t zero = 0;
+  return hip_status(hipMemcpy(w, &zero, 4, hipMemcpyHostToDevice), "gdn_device_errors clear");
+}
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 gdn_status gdn_saved_layout(const gdn_fwd_args* a, gdn_saved_layout_t* out) {
@@ -272,7 +331,12 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
   if ((int64_t)a->B * a->T == 0) return GDN_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   gdn::FwdKernelArgs k = kernel_args(a, a->saved);
+  if (!k.err) return fail(GDN_E_HIP, "device error word unavailable on the current device");
   const gdn::FwdConfig cfg = fwd_config(a);
+  if (k.s_meta && (stages & 2)) {
+    s = hip_status(gdn::launch_write_stamp(k.s_meta, stamp_of(a), st), "gdn_chunk_fwd stamp");
+    if (s != GDN_OK) return s;
+  }
   if (a->io_dtype == GDN_F32)
     return (stages & 2) ? hip_status(gdn::launch_fwd_fused(cfg, k, st), "gdn_chunk_fwd launch")
                         : GDN_OK;
@@ -371,8 +435,16 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   c.state_fmt = a->fwd.policy.state_fmt;
   c.w_fmt = a->fwd.policy.w_fmt;
   c.f32_io = a->fwd.io_dtype == GDN_F32;
-  return hip_status(gdn::launch_bwd(c, k, static_cast<hipStream_t>(stream)),
-                    "gdn_chunk_bwd launch");
+  if (!k.f.err) return fail(GDN_E_HIP, "device error word unavailable on the current device");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  s = hip_status(gdn::launch_bwd(c, k, st), "gdn_chunk_bwd launch");
+  if (s != GDN_OK) return s;
+  // the saved buffer must come from a forward with this policy and shape
+  const int64_t n_dqk = tokens * a->fwd.Hqk * a->fwd.Dk, n_dv = tokens * a->fwd.Hv * a->fwd.Dv;
+  const int64_t n_h0 = (int64_t)a->fwd.num_seqs * a->fwd.Hv * a->fwd.Dk * a->fwd.Dv;
+  return hip_status(gdn::launch_check_stamp(k, stamp_of(&a->fwd), n_dqk, n_dv, tokens * a->fwd.Hv,
+                                            n_h0, st),
+                    "gdn_chunk_bwd stamp check");
 }
 
 gdn_status gdn_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,

@@ -73,11 +73,20 @@ __device__ __forceinline__ void lds_signal(unsigned* flag) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 // Waits until an LDS counter reaches `target` (bounded: about 2^18 polls).
-__device__ __forceinline__ void lds_wait(unsigned* flag, unsigned target) {
+// A wait that gives up records kErrLdsWait in the device error word (one
+// atomic from lane 0): the outputs of that chunk are then not valid, and the
+// host finds out through gdn_device_errors instead of by silent drift.
+__device__ __forceinline__ void lds_wait(unsigned* flag, unsigned target, uint32_t* err) {
+  bool ok = false;
   for (int it = 0; it < (1 << 18); ++it) {
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+      ok = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  if (!ok && __lane_id() == 0)
+    __hip_atomic_fetch_or(err, kErrLdsWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
@@ -332,8 +341,8 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       const typename Sm::Buf& B = sm.buf[c & 1];
       const int t0 = chunk_t0(c), nc = chunk_nc(c);
       const int64_t ch = chunk_ch(c);
-      lds_wait(&sm.flag[0], 4u * (c + 1));        // this chunk's codes
-      lds_wait(&sm.flag[2], 4u * (c + 1));        // this chunk's Q
+      lds_wait(&sm.flag[0], 4u * (c + 1), a.err);        // this chunk's codes
+      lds_wait(&sm.flag[2], 4u * (c + 1), a.err);        // this chunk's Q
       const float dS = scale_of(c);
       // ---- O^T = dS exp(gamma) (Sc^T Q^T) + Vnew^T P^T, four token row tiles
       f32x4 acc[4];
@@ -351,7 +360,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
           for (int i = 0; i < 4; ++i) acc[mt][i] *= f;
         }
       }
-      lds_wait(&sm.flag[1], 4u * (c + 1));        // this chunk's Vnew
+      lds_wait(&sm.flag[1], 4u * (c + 1), a.err);        // this chunk's Vnew
       {
         // P is one fp16 plane; Vnew enters as fp16 hi + lo (22 significant bits)
         f16x8 aVh[2], aVl[2];

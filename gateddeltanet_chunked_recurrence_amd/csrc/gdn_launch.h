@@ -22,6 +22,8 @@ struct FwdKernelArgs {
   uint8_t* w_codes;           // saved W codes (W QDQ on), nullable
   float* w_scale;             // saved W scales, nullable
   float* s_X;                 // saved X = (I + L)^-1 per chunk (bf16 io), nullable
+  uint32_t* s_meta;           // saved policy stamp (SavedStamp words), nullable
+  uint32_t* err;              // sticky device error flags (kErr* bits), never NULL
   // forward workspace (bf16 io): operand images written by the prep kernel
   __bf16* ws_img;             // [slots * Hv][W planes | K^T | P] (gdn_images.h)
   float* ws_u;                // [slots * Hv][Dv * 64] fragment order
@@ -31,6 +33,18 @@ struct FwdKernelArgs {
   int32_t T;                  // tokens per sequence (no cu_seqlens)
   int32_t Hqk, Hv, Dv, block_v;
   float scale;
+};
+
+// Bits of the sticky device error word (gdn_device_errors in gdn.h).
+constexpr uint32_t kErrLdsWait = 1u;      // a bounded LDS-counter wait gave up
+constexpr uint32_t kErrFlagWait = 2u;     // a bounded wait on another workgroup gave up
+constexpr uint32_t kErrSavedStamp = 4u;   // saved buffer written under another policy or shape
+
+// The policy and shape a forward wrote its saved buffer under; the backward
+// compares it with its own arguments on the device.
+struct SavedStamp {
+  static constexpr uint32_t kMagic = 0x53444E47u;   // "GDNS"
+  uint32_t w[16];
 };
 
 struct FwdConfig {
@@ -84,6 +98,13 @@ hipError_t launch_bwd_state(const BwdConfig& cfg, const BwdKernelArgs& a, hipStr
 hipError_t launch_bwd_local(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
 // Elements of the backward image block of one (slot, head).
 int bwd_img_elems(int Dk, int w_fmt);
+
+// Writes the stamp into the saved buffer's meta section.
+hipError_t launch_write_stamp(uint32_t* meta, const SavedStamp& st, hipStream_t s);
+// After the backward's kernels: if the saved stamp differs from `want`, sets
+// kErrSavedStamp and overwrites every gradient output with NaN.
+hipError_t launch_check_stamp(const BwdKernelArgs& a, const SavedStamp& want, int64_t n_dqk,
+                              int64_t n_dv, int64_t n_tok, int64_t n_h0, hipStream_t s);
 
 hipError_t launch_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
                             int64_t n_states, int Dk, int Dv, int block_v, int fmt,

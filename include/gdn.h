@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
   GDN_OK = 0,
@@ -69,7 +69,7 @@ typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 typedef struct {
   int32_t state_fmt;   /* gdn_qdq_fmt at the state site                      */
   int32_t w_fmt;       /* gdn_qdq_fmt at the W site                          */
-  int32_t block_v;     /* state scale tile width: 16, 32, 64 or 128; divides Dv
+  int32_t block_v;     /* state scale tile width: 16, 32 or 64; divides Dv
                           (ignored when state_fmt == OFF)                    */
   int32_t chunk_size;  /* must be 64                                         */
   int32_t solve_degree;/* 0: exact solve of the WY form (the default). d > 0:
@@ -127,10 +127,18 @@ typedef struct {
  *           the WY form's unit lower triangular matrix, FP32 row-major
  *           [num_slots, Hv, 64, 64]; the backward reads it instead of solving
  *           again. 0 bytes for FP32 inputs.
+ *   meta:   64 bytes: the policy (formats, block_v, solve_degree), shape and
+ *           scale the forward ran under. gdn_chunk_bwd compares it with its
+ *           own arguments on the device; on any difference every gradient
+ *           output is set to NaN and GDN_DEVERR_SAVED_STAMP is raised in the
+ *           device error flags (see gdn_device_errors), so a saved buffer
+ *           is never read under another policy ("[7/7] Experimental GDN/KDA
+ *           approximate-inverse QAT", "What does this PR do?": no silent
+ *           change of degree or fallback).
  * Slots no chunk uses are left unwritten. */
 typedef struct {
   int64_t num_slots;
-  int64_t off_state, off_state_scale, off_w, off_w_scale, off_x;
+  int64_t off_state, off_state_scale, off_w, off_w_scale, off_x, off_meta;
   int64_t total_bytes;
 } gdn_saved_layout_t;
 
@@ -199,6 +207,20 @@ gdn_status gdn_qdq_state(const float* x, float* y, float* scales, uint8_t* codes
 
 const char* gdn_last_error(void);
 int32_t gdn_abi_version(void);
+
+/* Sticky device error flags of the current device. Kernels set them where a
+ * check can only run on the device, instead of failing silently:
+ *   GDN_DEVERR_LDS_WAIT     a bounded wait for another wave of the same
+ *                           workgroup gave up (its outputs are not valid);
+ *   GDN_DEVERR_FLAG_WAIT    a bounded wait for another workgroup gave up;
+ *   GDN_DEVERR_SAVED_STAMP  gdn_chunk_bwd got a saved buffer written under
+ *                           another policy or shape (its gradients are NaN).
+ * Diagnostic query: unlike every other entry point it synchronizes the
+ * device, then writes the flags to *flags and clears them. */
+#define GDN_DEVERR_LDS_WAIT 1u
+#define GDN_DEVERR_FLAG_WAIT 2u
+#define GDN_DEVERR_SAVED_STAMP 4u
+gdn_status gdn_device_errors(uint32_t* flags);
 
 #ifdef __cplusplus
 }

@@ -120,4 +120,5 @@ def gpu_bwd(x, spec, saved, grad_dtype=torch.float32, **over):
                         dht=x['dht'], scale=1.0 / math.sqrt(spec['Dk']), h0=x['h0'],
                         cu_seqlens=x['cu_seqlens'], grad_dtype=grad_dtype, **p)
     torch.cuda.synchronize()
+    assert B.device_errors() == 0                   # saved stamp matched, no wait gave up
     return g

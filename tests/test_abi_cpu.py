@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 4
+    assert lib.gdn_abi_version() == 5
 
 
 def _args(**kw):
@@ -118,7 +118,8 @@ def test_saved_layout_sizes():
     assert lay.off_w >= lay.off_state_scale + lay.num_slots * 4 * 2 * 4
     assert lay.off_w_scale >= lay.off_w + 200 * 4 * 128
     assert lay.off_x >= lay.off_w_scale + lay.num_slots * 4 * 4
-    assert lay.total_bytes >= lay.off_x + lay.num_slots * 4 * 64 * 64 * 4   # X, bf16 inputs
+    assert lay.off_meta >= lay.off_x + lay.num_slots * 4 * 64 * 64 * 4   # X, bf16 inputs
+    assert lay.total_bytes == lay.off_meta + 256                        # the policy stamp
     assert lay.total_bytes == lib.gdn_saved_bytes(ctypes.byref(a))
     a.policy.state_fmt = B.QDQ_OFF
     a.policy.w_fmt = B.QDQ_OFF
@@ -127,7 +128,7 @@ def test_saved_layout_sizes():
     assert lay.off_w == lay.off_state_scale and lay.off_w_scale == lay.off_w
     f32 = _args(B=2, T=100, num_seqs=2, io_dtype=B.GDN_F32, Dk=64, Dv=64)
     lay = B.saved_layout(f32)
-    assert lay.total_bytes == lay.off_x                      # no X for FP32 inputs
+    assert lay.off_meta == lay.off_x                         # no X for FP32 inputs
 
 
 def test_backward_rejects_before_launch():
@@ -176,3 +177,17 @@ def test_qdq_state_rejects_before_launch():
              ((fake, fake, None, None, 0, 128, 128, 64, 1), B.GDN_OK)]
     for args, status in cases:
         assert lib.gdn_qdq_state(*args, None) == status, args
+
+
+def test_binding_backward_takes_the_forward_policy():
+    """The saved buffer carries the policy of the forward that wrote it; the
+    binding's backward takes omitted policy arguments from it and refuses a
+    different one (the C ABI checks the same stamp on the device)."""
+    import torch
+    saved = torch.zeros(16, dtype=torch.uint8)
+    saved.gdn_policy = dict(state_fmt=B.QDQ_E4M3, w_fmt=B.QDQ_E4M3, block_v=64, solve_degree=3)
+    x = torch.zeros(1, 4, 1, 64)
+    g = torch.zeros(1, 4, 1)
+    for bad in (dict(solve_degree=0), dict(state_fmt=B.QDQ_INT8), dict(block_v=32)):
+        with pytest.raises(ValueError, match=list(bad)[0]):
+            B.gdn_chunk_bwd(x, x, x, g, g, saved, x, **bad)

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import gdn_inputs
+from gateddeltanet_chunked_recurrence_amd import binding as B
 from parity_util import (code_bytes, draw, gpu_fwd, head_subset, oracle_fwd, rel, saved_views,
                          say, seq_bounds)
 
@@ -39,6 +40,7 @@ def _check_fwd(spec, seed, heads, save=True, code_checks=True):
     assert r_o <= bar and r_h <= bar
     if save and code_checks:
         _check_codes(x, spec, saved, rec, heads)
+    assert B.device_errors() == 0                  # no bounded wait gave up
     return x, o, ht, r_o, r_h
 
 

@@ -83,3 +83,33 @@ def test_neumann_backward_is_refused():
         B.gdn_chunk_bwd(x['q'], x['k'], x['v'], x['g'], x['beta'], saved, x['do'], x['dht'],
                         h0=x['h0'], state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'],
                         block_v=spec['block_v'], solve_degree=3)
+
+
+def test_neumann_saved_read_by_exact_backward_is_poisoned():
+    """A saved buffer written by a Neumann forward and handed to the C ABI's
+    backward under the default exact solve (the binding's own policy check
+    bypassed) must not give plausible gradients: the device compares the
+    saved policy stamp, sets every gradient to NaN and raises the saved-stamp
+    error flag ("[7/7] ...", "What does this PR do?": no silent change of
+    degree or fallback)."""
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=1, T=128, Hqk=1, Hv=2)
+    x = draw(spec, 8, bwd=True)
+    assert B.device_errors() == 0
+    _, _, saved = gpu_fwd(x, spec, save=True, solve_degree=3)
+    del saved.gdn_policy                            # what a raw C caller would pass
+    g = B.gdn_chunk_bwd(x['q'], x['k'], x['v'], x['g'], x['beta'], saved, x['do'], x['dht'],
+                        h0=x['h0'], state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'],
+                        block_v=spec['block_v'], solve_degree=0)
+    torch.cuda.synchronize()
+    for name, t in g.items():
+        if t is not None:
+            assert torch.isnan(t.float()).all(), name
+    assert B.device_errors() == B.DEVERR_SAVED_STAMP
+    assert B.device_errors() == 0                    # read clears the flags
+    # the same forward with its own policy passes the check
+    _, _, saved = gpu_fwd(x, spec, save=True)
+    g = B.gdn_chunk_bwd(x['q'], x['k'], x['v'], x['g'], x['beta'], saved, x['do'], x['dht'],
+                        h0=x['h0'])
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t.float()).all() for t in g.values() if t is not None)
+    assert B.device_errors() == 0
