@@ -61,6 +61,7 @@ def load_library():
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_abi_version.restype = c_i32
     for name, argt in (('gdn_chunk_fwd', [ctypes.POINTER(FwdArgs), c_vp]),
+                       ('gdn_chunk_fwd_noalloc', [ctypes.POINTER(FwdArgs), c_vp]),
                        ('gdn_chunk_fwd_prep', [ctypes.POINTER(FwdArgs), c_vp]),
                        ('gdn_chunk_fwd_state', [ctypes.POINTER(FwdArgs), c_vp]),
                        ('gdn_chunk_bwd', [ctypes.POINTER(BwdArgs), c_vp]),
@@ -171,6 +172,32 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
     a.workspace_bytes = wbytes
     _check(lib.gdn_chunk_fwd(ctypes.byref(a), _stream(dev)))
     return o, ht, saved
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None,
+                          state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, output_final_state=True,
+                          out=None):
+    """gdn_chunk_fwd through the allocation-free entry point: the library
+    uses its fixed per-GPU scratch array instead of a workspace. `out` may
+    pass preallocated (o, ht); otherwise they are allocated here (by torch,
+    outside the library call). Returns (o, ht or None)."""
+    lib = load_library()
+    dev = q.device
+    B, T, Hqk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    if out is None:
+        o = torch.empty(B, T, Hv, Dv, dtype=q.dtype, device=dev)
+        ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev) \
+            if output_final_state else None
+    else:
+        o, ht = out
+    a = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v, o, ht)
+    _check(lib.gdn_chunk_fwd_noalloc(ctypes.byref(a), _stream(dev)))
+    return o, ht
 
 
 class FwdPlan:

@@ -21,6 +21,13 @@
 // runs on).
 __device__ __align__(256) uint32_t gdn_err_flags[64];
 
+// Forward scratch of gdn_chunk_fwd_noalloc: a file-scope device array, so
+// that entry point calls no allocator. Every GPU the library runs on holds
+// its own copy until the process ends. Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol): it uses the
+// per-device address from scratch_ptr().
+static __device__ __align__(256) uint8_t scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -37,6 +44,22 @@ uint32_t* err_word() {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(gdn_err_flags)) != hipSuccess) return nullptr;
     ptrs[dev] = static_cast<uint32_t*>(p);
+  }
+  return ptrs[dev];
+}
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress
+// once per device (with that device current), then the cached pointer.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
   }
   return ptrs[dev];
 }
@@ -318,16 +341,31 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a) {
 namespace {
 
 // Stages of the forward: 1 = prep (every chunk and head), 2 = state recurrence.
-gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
+// noalloc: the workspace is the library's `scratch` array instead of the
+// caller's (a->workspace and a->workspace_bytes are not read).
+gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages, bool noalloc = false) {
   gdn_status s = check_fwd_shape(a);
   if (s != GDN_OK) return s;
   if ((s = check_fwd_ptrs(a, true)) != GDN_OK) return s;
   const FwdWsLayout W = fwd_ws_layout(a);
-  if (W.total > 0 && (!a->workspace || a->workspace_bytes < (size_t)W.total))
-    return fail(GDN_E_WORKSPACE, "forward workspace of %zu bytes given, %lld needed",
-                a->workspace_bytes, (long long)W.total);
-  if (a->workspace && !aligned16(a->workspace))
-    return fail(GDN_E_INVALID, "workspace is not 16-byte aligned");
+  void* wsp = a->workspace;
+  if (noalloc) {
+    if (W.total > (int64_t)GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_E_UNSUPPORTED,
+                  "gdn_chunk_fwd_noalloc: this problem needs %lld bytes of forward scratch, above "
+                  "the library's fixed %lld (use gdn_chunk_fwd with a workspace)",
+                  (long long)W.total, (long long)GDN_NOALLOC_SCRATCH_BYTES);
+    if ((int64_t)a->B * a->T == 0) return GDN_OK;
+    wsp = W.total > 0 ? scratch_ptr() : nullptr;
+    if (W.total > 0 && !wsp)
+      return fail(GDN_E_HIP, "gdn_chunk_fwd_noalloc: no device address for the scratch array");
+  } else {
+    if (W.total > 0 && (!a->workspace || a->workspace_bytes < (size_t)W.total))
+      return fail(GDN_E_WORKSPACE, "forward workspace of %zu bytes given, %lld needed",
+                  a->workspace_bytes, (long long)W.total);
+    if (a->workspace && !aligned16(a->workspace))
+      return fail(GDN_E_INVALID, "workspace is not 16-byte aligned");
+  }
   if ((int64_t)a->B * a->T == 0) return GDN_OK;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   gdn::FwdKernelArgs k = kernel_args(a, a->saved);
@@ -340,7 +378,7 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
   if (a->io_dtype == GDN_F32)
     return (stages & 2) ? hip_status(gdn::launch_fwd_fused(cfg, k, st), "gdn_chunk_fwd launch")
                         : GDN_OK;
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = static_cast<char*>(wsp);
   k.ws_img = reinterpret_cast<__bf16*>(ws + W.img);
   k.ws_u = reinterpret_cast<float*>(ws + W.u);
   k.ws_wscale = reinterpret_cast<float*>(ws + W.wscale);
@@ -362,6 +400,9 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages) {
 extern "C" {
 
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream) { return chunk_fwd_stages(a, stream, 3); }
+gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_args* a, void* stream) {
+  return chunk_fwd_stages(a, stream, 3, true);
+}
 gdn_status gdn_chunk_fwd_prep(const gdn_fwd_args* a, void* stream) {
   return chunk_fwd_stages(a, stream, 1);
 }

@@ -161,6 +161,20 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
  * missing or too small). */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
 
+/* gdn_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, checks, kernels and results as gdn_chunk_fwd, except that
+ * a->workspace and a->workspace_bytes are not read: the forward scratch is a
+ * fixed array inside the library, GDN_NOALLOC_SCRATCH_BYTES bytes on every
+ * GPU it runs on, held until the process ends. A problem whose
+ * gdn_fwd_workspace_bytes() exceeds that returns GDN_E_UNSUPPORTED before
+ * any launch. The call allocates nothing. All calls on one GPU share that
+ * GPU's array: calls that overlap on one GPU (several streams or host
+ * threads at once) race on it and must be serialized by the caller. The
+ * caller still owns o, ht and saved. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ll << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_args* a, void* stream);
+
 /* The two stages of gdn_chunk_fwd, for callers that schedule or time them
  * separately: gdn_chunk_fwd_prep (every chunk and head: solve, W and its QDQ,
  * U, masked Q K^T, into the workspace; the saved W codes) then

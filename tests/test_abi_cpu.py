@@ -191,3 +191,17 @@ def test_binding_backward_takes_the_forward_policy():
     for bad in (dict(solve_degree=0), dict(state_fmt=B.QDQ_INT8), dict(block_v=32)):
         with pytest.raises(ValueError, match=list(bad)[0]):
             B.gdn_chunk_bwd(x, x, x, g, g, saved, x, **bad)
+
+
+def test_noalloc_forward_refuses_above_its_scratch():
+    """gdn_chunk_fwd_noalloc has a fixed scratch array (64 MiB per GPU): a
+    problem whose forward workspace is larger is refused before any launch,
+    with GDN_E_UNSUPPORTED and a message naming the entry point."""
+    lib = B.load_library()
+    a = _args(T=4096, Hqk=16, Hv=16)
+    assert lib.gdn_fwd_workspace_bytes(ctypes.byref(a)) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.gdn_chunk_fwd_noalloc(ctypes.byref(a), None) == B.GDN_E_UNSUPPORTED
+    assert 'noalloc' in lib.gdn_last_error().decode()
+    bad = _args(chunk_size=32)                        # the ordinary checks come first
+    assert lib.gdn_chunk_fwd_noalloc(ctypes.byref(bad), None) == B.GDN_E_UNSUPPORTED
+    assert 'chunk_size' in lib.gdn_last_error().decode()
