@@ -49,7 +49,9 @@ def build(jobs=4, debug=False, verbose=False):
             raise RuntimeError(f'hipcc failed on {src}')
         objs.append(out)
     tmp = LIB + '.tmp'
-    cmd = [HIPCC, '-shared', '-fPIC', '--offload-arch=gfx950', '-o', tmp] + objs
+    # --no-undefined: a kernel whose host stub was not emitted fails the build,
+    # not the first dlopen
+    cmd = [HIPCC, '-shared', '-fPIC', '--offload-arch=gfx950', '-Wl,--no-undefined', '-o', tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError('link failed:\n' + r.stdout + r.stderr)

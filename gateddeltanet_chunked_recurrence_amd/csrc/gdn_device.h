@@ -241,19 +241,27 @@ __device__ __forceinline__ void e4m3_pair(float y0, float y1, float& c0, float& 
 __device__ __forceinline__ float round_int8(float y) {
   return fminf(fmaxf(rintf(y), -127.f), 127.f);
 }
-// Codes of four values x * r (one accumulator quad), and their bytes.
+// Codes of four values x * r (one accumulator quad), and their bytes, where
+// r = fl(1/d) and d is derived from the maximum |x| of the values' own tile:
+// then |fl(x r)| <= q_max (1 + 4 * 2^-24) (d >= amax / q_max (1 - 2^-24),
+// r <= (1 / d)(1 + 2^-24)), so no clamp is needed before the conversion:
+// E4M3 values below 464 round to at most 448 (the hardware gives NaN only
+// from 464 up), and rint of |y| < 127.5 is at most 127. The two E4M3 pairs
+// are converted into the low and high halves of one word.
 template <int FMT> __device__ __forceinline__ void quant4(const float (&x)[4], float r,
                                                           float (&c)[4], uint32_t& bytes) {
   if constexpr (FMT == 1) {
-    uint32_t b0, b1;
-    e4m3_pair(x[0] * r, x[1] * r, c[0], c[1], b0);
-    e4m3_pair(x[2] * r, x[3] * r, c[2], c[3], b1);
-    bytes = b0 | (b1 << 16);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * r, x[1] * r, 0, false);
+    bytes = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x[2] * r, x[3] * r, lo, true));
+    c[0] = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(bytes), 0);
+    c[1] = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(bytes), 1);
+    c[2] = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(bytes), 2);
+    c[3] = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(bytes), 3);
   } else {
     bytes = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      c[i] = round_int8(x[i] * r);
+      c[i] = rintf(x[i] * r);
       bytes |= (static_cast<uint32_t>(static_cast<int8_t>(c[i])) & 0xFFu) << (8 * i);
     }
   }

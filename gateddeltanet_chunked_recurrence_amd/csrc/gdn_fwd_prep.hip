@@ -323,7 +323,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       float* G = reinterpret_cast<float*>(img + goff);
       G[lane] = eg;
       G[64 + lane] = lane < nc ? fexp2(g2n - g2) : 0.f;
-      G[128 + lane] = lane == 0 ? fexp2(g2n) : 0.f;
+      if (lane != 1) G[128 + lane] = lane == 0 ? fexp2(g2n) : 0.f;   // [129]: the W scale, below
       G[192 + lane] = 0.f;
     }
     lds_barrier();
@@ -734,6 +734,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       }
       if (tid == 0) {
         a.ws_wscale[ch] = dW;
+        const int goff = a.w_img_bytes ? I::template p_at<NW>() + I::P1 : I::template g_at<NW>();
+        reinterpret_cast<float*>(img + goff)[129] = dW;
         if (save) a.w_scale[ch] = dW;
       }
     }

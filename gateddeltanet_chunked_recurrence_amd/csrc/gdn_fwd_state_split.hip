@@ -12,23 +12,26 @@
 //     the published state codes and Vnew,
 //       O = scale (exp(gamma) dS (Q Sc) + P Vnew),
 //     and writes the saved state codes;
-//   staging waves 8..11: this chunk's Q to LDS, the next chunk's image block
-//     and Q copied in (their issue stalls while the CU's memory pipeline is
-//     busy, which is why no other role issues them).
-// The image block arrives as W^q code bytes (kept as bytes in LDS and widened
-// to bf16 per 8-byte fragment just before each W^q S^q product), K^T, P as
-// one fp16 plane, and the gates: about 33 KB per chunk instead of 49 KB with
-// bf16 codes and P as bf16 hi + lo, since the per-CU memory path bounds the
-// chunk.
+//   staging waves 8..11: copy the next chunk's operands straight from global
+//     memory into LDS (global-to-LDS loads): the image block (W^q code bytes,
+//     K^T, P as one fp16 plane, the gates with the W scale), the rows of q,
+//     and this value block's U. They are the only waves that issue global
+//     loads inside the chunk loop: a wave's load issue stalls while the CU's
+//     memory pipeline is busy, so the recurrence and output waves never queue
+//     behind the copies.
+// Every operand of a chunk sits in one double-buffered LDS block (65 KB).
 // One workgroup barrier per chunk (X, at its end). Within a chunk the output
-// waves wait on LDS counters that the recurrence waves (codes, then Vnew) and
-// the staging waves (Q) raise after their LDS writes complete; the counters
-// only grow, and nothing the recurrence or staging waves do waits on the
-// output waves before X, so every wait ends. Each wait is also bounded.
+// waves wait on LDS counters that the recurrence waves (codes, then Vnew)
+// raise after their LDS writes; the counters only grow, and nothing the
+// recurrence or staging waves do waits on the output waves before X, so every
+// wait ends. Each wait is also bounded, and one that gives up is recorded in
+// the device error word.
 // The output products are computed transposed (O^T = Sc^T Q^T + Vnew^T P^T):
 // the published code and Vnew fragments are then A operands as they stand, and
 // a lane's accumulator holds four adjacent output columns of one token, which
-// leave as one 8-byte store.
+// leave as one 8-byte store. Sc^T Q^T contracts over dk in natural order (Q
+// rows are copied unpermuted, 16-byte pieces XOR-swizzled by row); the
+// recurrence waves publish the codes in that order.
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -47,21 +50,32 @@ struct SplitSmem {
   // copy writes its own 16 bytes, so the copy of the last partial piece group
   // lands in this padding, not in K^T)
   static constexpr int WBP = (I::WQ / 16 + 63) / 64 * 64 * 16;
-  struct Buf {                                    // one image block (W code bytes, K^T, P, gates)
+  static constexpr int QP = DK / 8;               // 16-byte pieces of a q row
+  struct Buf {                                    // all operands of one chunk
     uint8_t Wb[WBP];                              // W^q codes, one byte each, W image element order
     bf16 Kt[I::KT];
     _Float16 P[I::P1];                            // masked Q K^T, one fp16 plane
-    alignas(16) float G[I::GB / 2];
+    alignas(16) float G[I::GB / 2];               // gates; [129] holds the W scale
+    bf16 Q[64 * DK];                              // q rows, natural order, pieces swizzled (q_off)
+    f32x4 U[4][4][64];                            // U fragments: column group, row tile, lane
   };
   Buf buf[2];
-  bf16 Q[I::WQ];                                  // W image layout, single buffer
-  // state code bytes: codes[jj][col][g] holds, for block column col, the rows
-  // 32 jj + 4 g + i (x, byte i) and 32 jj + 16 + 4 g + i (y, byte i)
+  // state code bytes in natural dk order: codes[kk][col][g] holds rows
+  // 32 kk + 8 g + e (byte e) of block column col
   u32x2 codes[DK / 32][64][4];
   f32x4 vnx[4][4][64];                            // Vnew: column group, row tile, lane
   alignas(16) float red[2][4];                    // per-column-group state amax, by chunk parity
-  unsigned flag[3];                               // counters: codes, Vnew (recurrence), Q (staging)
+  unsigned flag[2];                               // counters raised by the recurrence: codes, Vnew
 };
+
+// Element offset of 16-byte piece j (elements 8 j .. 8 j + 7) of q row `row`
+// in the Q operand: pieces XOR-swizzled by row so that the 16 rows one
+// fragment read touches fall in 16 distinct bank groups.
+template <int DK>
+__device__ __forceinline__ int q_off(int row, int j) {
+  const int sw = DK == 128 ? (row & 15) : ((row >> 1) & 7);
+  return row * DK + 8 * (j ^ sw);
+}
 
 // Raises an LDS counter after this wave's earlier LDS writes. The LDS executes
 // one wave's operations in issue order, so the increment lands after the data
@@ -130,9 +144,12 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   using Sm = SplitSmem<DK>;
   constexpr int MK = DK / 16;                     // 16-row tiles of a state column group
   constexpr int KS = DK / 32;                     // 32-deep k-steps over dk
-  constexpr int IMGP = I::template img<1>() / 8;  // 16-byte pieces of an image block
-  // the LDS block: the image block with its W slot replaced by the padded code bytes
-  static_assert(sizeof(typename Sm::Buf) == Sm::WBP + 2 * (I::KT + I::P1 + I::GB), "image block layout");
+  // the LDS block: the image block with its W slot replaced by the padded code
+  // bytes, then the q rows and U
+  static_assert(sizeof(typename Sm::Buf) ==
+                    Sm::WBP + 2 * (I::KT + I::P1 + I::GB) + 2 * 64 * DK + 4 * 4 * 64 * 16,
+                "operand block layout");
+  static_assert(sizeof(Sm) <= 160 * 1024, "LDS");
   __shared__ __align__(16) Sm sm;
 
   const int Hv = a.Hv, Dv = a.Dv, NVB = Dv / 64;
@@ -201,17 +218,6 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       store_ht();
       return;
     }
-    // U fragments of the four row tiles of this column group, and the W scale
-    f32x4 Ucur[4], Unext[4];
-    float dWcur = 1.f, dWnext = 1.f;
-    auto load_u = [&](int c, f32x4 (&U)[4], float& dW) {
-      const int64_t ch = chunk_ch(c);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        U[mt] = *reinterpret_cast<const f32x4*>(a.ws_u + u_off(ch, NVB, vb, cg, mt, lane));
-      dW = a.ws_wscale[ch];
-    };
-    load_u(0, Ucur, dWcur);
     {
       float m = 0.f;
 #pragma unroll
@@ -221,13 +227,12 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       m = wave_max(m);
       if (lane == 0) sm.red[0][cg] = m;
     }
-    if (wave == 0 && lane < 3) sm.flag[lane] = 0;
+    if (wave == 0 && lane < 2) sm.flag[lane] = 0;
     vm_drain();
     lds_barrier();                                 // P
 
     for (int c = 0; c < nchunks; ++c) {
       const typename Sm::Buf& B = sm.buf[c & 1];
-      load_u(min(c + 1, nchunks - 1), Unext, dWnext);
       // operands read ahead of their products: the W fragments here, over the
       // QDQ; the K^T fragments after W Sq is issued, over Vnew
       // (two k-steps ahead: three waves per SIMD leave 168 VGPRs per wave)
@@ -252,8 +257,15 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
           for (int i = 0; i < 4; ++i) S[j][i] = cq[i];
         }
       }
+      // rows 16 j + 4 grp + i are natural-order bytes 4 (grp & 1) + i of
+      // piece 2 (j & 1) + (grp >> 1) of k-step j >> 1
+      {
+        uint8_t* cb = reinterpret_cast<uint8_t*>(&sm.codes[0][16 * cg + r16][0]);
 #pragma unroll
-      for (int jj = 0; jj < KS; ++jj) sm.codes[jj][16 * cg + r16][grp] = u32x2{sb[2 * jj], sb[2 * jj + 1]};
+        for (int j = 0; j < MK; ++j)
+          *reinterpret_cast<uint32_t*>(cb + (j >> 1) * (64 * 4 * 8) + 8 * (2 * (j & 1) + (grp >> 1)) +
+                                       4 * (grp & 1)) = sb[j];
+      }
       lds_signal(&sm.flag[0]);
 
       // ---- W Sq over the four token row tiles
@@ -274,11 +286,12 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       for (int j = 0; j < MK; ++j) kop[j] = ld_r64(B.Kt, 16 * j + r16, 0, grp);
       f32x4 Vn[4];
       {
-        const float sc = dWcur * dS;
+        const float sc = B.G[129] * dS;            // dW dS
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 u = B.U[cg][mt][lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Vn[mt][i] = Ucur[mt][i] - sc * accw[mt][i];
+          for (int i = 0; i < 4; ++i) Vn[mt][i] = u[i] - sc * accw[mt][i];
           sm.vnx[cg][mt][lane] = Vn[mt];
         }
       }
@@ -324,11 +337,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
         m = wave_max(m);
         if (lane == 0) sm.red[(c + 1) & 1][cg] = m;
       }
-      vm_drain();                                  // next chunk's U landed
       lds_barrier();                               // X
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) Ucur[mt] = Unext[mt];
-      dWcur = dWnext;
     }
     store_ht();
   } else if (wave < 8) {
@@ -342,7 +351,6 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
       const int t0 = chunk_t0(c), nc = chunk_nc(c);
       const int64_t ch = chunk_ch(c);
       lds_wait(&sm.flag[0], 4u * (c + 1), a.err);        // this chunk's codes
-      lds_wait(&sm.flag[2], 4u * (c + 1), a.err);        // this chunk's Q
       const float dS = scale_of(c);
       // ---- O^T = dS exp(gamma) (Sc^T Q^T) + Vnew^T P^T, four token row tiles
       f32x4 acc[4];
@@ -354,7 +362,9 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
         for (int mt = 0; mt < 4; ++mt) {
           acc[mt] = zero4();
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc[mt] = mfma(aS[kk], ld_wq<DK>(sm.Q, 16 * mt + r16, kk, grp), acc[mt]);
+          for (int kk = 0; kk < KS; ++kk)
+            acc[mt] = mfma(aS[kk], *reinterpret_cast<const bf16x8*>(
+                                       &B.Q[q_off<DK>(16 * mt + r16, 4 * kk + grp)]), acc[mt]);
           const float f = dS * B.G[16 * mt + r16];
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] *= f;
@@ -402,7 +412,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
 #pragma unroll
         for (int p = 0; p < CPL; ++p) {
           const int cb = lane + 64 * p, q = cb & 3, g = (cb >> 2) & 3, hh = (cb >> 4) & 1, jj = cb >> 5;
-          const int row0 = 32 * jj + 16 * hh + 4 * g;
+          const int row0 = 32 * jj + 8 * g + 4 * hh;
           uint32_t w[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -423,58 +433,80 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
     // ========================= staging role =========================
     if (nchunks == 0) return;
     __builtin_amdgcn_s_setprio(1);
-    const int stid = cg * 64 + lane;               // 0..255 over the staging waves
-    constexpr int QPT = 64 * DK / 8 / 256;         // 16-byte Q pieces per lane
-    u32x4 qreg[QPT];
-    auto load_q = [&](int c) {
-      const bf16* qb = reinterpret_cast<const bf16*>(a.q);
-      const int t0 = chunk_t0(c), nc = chunk_nc(c);
-#pragma unroll
-      for (int p = 0; p < QPT; ++p) {
-        const int e = stid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
-        qreg[p] = *reinterpret_cast<const u32x4*>(qb + ((int64_t)(t0 + min(row, nc - 1)) * a.Hqk + hk) * DK + 8 * c8);
-      }
-    };
-    auto store_q = [&]() {
-#pragma unroll
-      for (int p = 0; p < QPT; ++p) {
-        const int e = stid + 256 * p, row = e / (DK / 8), c8 = e % (DK / 8);
-        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8))]) = qreg[p].xy;
-        *reinterpret_cast<u32x2*>(&sm.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = qreg[p].zw;
-      }
-    };
-    // Two ranges of the image block: the W code bytes (the first WQ bytes of
-    // its W slot) and K^T, the fp16 P plane and the gates after the slot; the
-    // LDS block holds them back to back (the codes padded to whole wave loads).
+    // One chunk's copies, as whole 64-lane global-to-LDS loads of 16 bytes
+    // (each lane's 16 bytes land at LDS base + 16 lane): the W code bytes (the
+    // first WQ bytes of the image block's W slot; lanes past them read the
+    // last piece into the padding), K^T, P and the gates (after the W slot),
+    // the q rows (source pieces permuted so the LDS pieces come out
+    // swizzled, rows past the chunk end repeat its last row), and U.
     constexpr int WOFF = I::WQ / 8;               // 16-byte pieces of the W slot
     constexpr int NWB = I::WQ / 16;               // ... of the W code bytes
     constexpr int NI1 = Sm::WBP / 16 / 64;        // wave loads of the codes
-    constexpr int NI2 = (I::KT + I::P1 + I::GB) / 8 / 64;   // wave loads of K^T, P and the gates
-    constexpr int KW = (NI1 + NI2 + 3) / 4;       // ... per staging wave
+    constexpr int NI2 = (I::KT + I::P1 + I::GB) / 8 / 64;   // ... of K^T, P and the gates
+    constexpr int NI3 = 64 * DK / 8 / 64;         // ... of the q rows
+    constexpr int NI4 = 4 * 4 * 64 * 16 / 16 / 64;           // ... of U
+    constexpr int NI = NI1 + NI2 + NI3 + NI4;
+    constexpr int KW = (NI + 3) / 4;              // ... per staging wave
     static_assert((I::KT + I::P1 + I::GB) % 512 == 0 && NI1 * 64 >= NWB, "whole wave loads");
+    static_assert(offsetof(typename Sm::Buf, Kt) == Sm::WBP &&
+                  offsetof(typename Sm::Buf, Q) == Sm::WBP + 2 * (I::KT + I::P1 + I::GB) &&
+                  offsetof(typename Sm::Buf, U) == offsetof(typename Sm::Buf, Q) + 2 * 64 * DK,
+                  "the copies fill the buffer back to back");
+    // Each lane's source offset of each of its KW copies is fixed for a full
+    // chunk (bytes from a wave-uniform base: the image block, this chunk's
+    // first q row of the head, or this value block's U), so a copy costs a
+    // scalar base update and no vector address arithmetic.
+    const char* qbase = reinterpret_cast<const char*>(a.q) + (int64_t)hk * DK * 2;
+    const int64_t qrow = (int64_t)a.Hqk * DK * 2;   // bytes between consecutive tokens' q rows
+    int off[KW];
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      const int j = min(cg + 4 * k, NI - 1);       // a repeated last load rewrites the same bytes
+      if (j < NI1) {
+        off[k] = 16 * min(64 * j + lane, NWB - 1);
+      } else if (j < NI1 + NI2) {
+        off[k] = 16 * (WOFF + 64 * (j - NI1) + lane);
+      } else if (j < NI1 + NI2 + NI3) {
+        const int pc = 64 * (j - NI1 - NI2) + lane, row = pc / Sm::QP, jp = pc % Sm::QP;
+        const int sw = DK == 128 ? (row & 15) : ((row >> 1) & 7);
+        off[k] = (int)(row * qrow) + 16 * (jp ^ sw);
+      } else {
+        off[k] = 16 * (64 * (j - NI1 - NI2 - NI3) + lane);
+      }
+    }
     auto dma = [&](int c, int b) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + chunk_ch(c) * I::template img<1>());
+      const int64_t ch = chunk_ch(c);
+      const char* img = reinterpret_cast<const char*>(a.ws_img + ch * I::template img<1>());
+      const char* u = reinterpret_cast<const char*>(a.ws_u + u_off(ch, NVB, vb, 0, 0, 0));
+      const int t0 = chunk_t0(c), nc = chunk_nc(c);
+      const char* q0 = qbase + (int64_t)t0 * qrow;
       uint4* dst = reinterpret_cast<uint4*>(sm.buf[b].Wb);
 #pragma unroll
       for (int k = 0; k < KW; ++k) {
-        const int j = min(cg + 4 * k, NI1 + NI2 - 1);   // a repeated last load rewrites the same bytes
-        if (j < NI1)                               // lanes past the codes read the last piece into the padding
-          __builtin_amdgcn_global_load_lds(src + min(64 * j + lane, NWB - 1), dst + 64 * j, 16, 0, 0);
-        else
-          __builtin_amdgcn_global_load_lds(src + WOFF + 64 * (j - NI1) + lane, dst + 64 * j, 16, 0, 0);
+        const int j = min(cg + 4 * k, NI - 1);
+        const char* src;
+        if (j < NI1 + NI2) {
+          src = img + off[k];
+        } else if (j < NI1 + NI2 + NI3) {
+          if (nc == CHUNK) {
+            src = q0 + off[k];
+          } else {                                 // the last, partial chunk: rows past its end repeat its last row
+            const int pc = 64 * (j - NI1 - NI2) + lane, row = pc / Sm::QP, jp = pc % Sm::QP;
+            const int sw = DK == 128 ? (row & 15) : ((row >> 1) & 7);
+            src = q0 + min(row, nc - 1) * qrow + 16 * (jp ^ sw);
+          }
+        } else {
+          src = u + off[k];
+        }
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src), dst + 64 * j, 16, 0, 0);
       }
     };
-    load_q(0);
     dma(0, 0);
     vm_drain();
     lds_barrier();                                 // P
     for (int c = 0; c < nchunks; ++c) {
-      store_q();                                   // this chunk's Q: the output waves are past the last one
-      lds_signal(&sm.flag[2]);
-      const int cn = min(c + 1, nchunks - 1);
-      load_q(cn);
-      dma(cn, (c + 1) & 1);
-      vm_drain();                                  // next chunk's copies and Q landed
+      dma(min(c + 1, nchunks - 1), (c + 1) & 1);
+      vm_drain();                                  // next chunk's copies landed
       lds_barrier();                               // X
     }
   }

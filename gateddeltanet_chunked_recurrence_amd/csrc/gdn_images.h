@@ -23,8 +23,10 @@
 //            row tile mt and lane l the four values U[16 mt + 4 (l >> 4) + i]
 //            [64 vb + 16 w + (l & 15)], i = 0..3, contiguous
 //   gates    256 FP32: exp(gamma_i) at [i], exp(gamma_n - gamma_i) at [64 + i]
-//            (0 past the chunk end), exp(gamma_n) at [128], rest unused
-//   W scale  one FP32 per chunk and head (1 when W QDQ is off)
+//            (0 past the chunk end), exp(gamma_n) at [128], the W scale at
+//            [129], rest unused
+//   W scale  one FP32 per chunk and head (1 when W QDQ is off), also in a
+//            separate array
 // The W, K^T, P and gate images of one chunk and head are one contiguous
 // block, in that order, as they are in the state kernel's LDS buffer (in the
 // byte variant that buffer holds the code bytes, padded to whole 1 KB
