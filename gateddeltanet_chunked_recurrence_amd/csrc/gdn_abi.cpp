@@ -109,10 +109,14 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
   if (a->io_dtype == GDN_F32 && p.solve_degree != 0)
     return fail(GDN_E_UNSUPPORTED, "the Neumann solve is built for bf16 inputs only");
   if (p.state_fmt != GDN_QDQ_OFF) {
-    if (p.block_v != 16 && p.block_v != 32 && p.block_v != 64)
-      return fail(GDN_E_UNSUPPORTED, "block_v %d: supported 16, 32, 64", p.block_v);
+    if (p.block_v != 16 && p.block_v != 32 && p.block_v != 64 && p.block_v != 128 &&
+        p.block_v != 256)
+      return fail(GDN_E_UNSUPPORTED, "block_v %d: supported 16, 32, 64, 128, 256", p.block_v);
     if (a->Dv % p.block_v != 0)
       return fail(GDN_E_INVALID, "block_v %d does not divide Dv %d", p.block_v, a->Dv);
+    if (a->io_dtype == GDN_F32 && p.block_v > 64)
+      return fail(GDN_E_UNSUPPORTED, "FP32 inputs are built for block_v up to 64 (got %d)",
+                  p.block_v);
   }
   if (!std::isfinite(a->scale)) return fail(GDN_E_INVALID, "scale is not finite");
   if (a->cu_seqlens) {
@@ -240,6 +244,7 @@ gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
   c.state_fmt = a->policy.state_fmt;
   c.w_fmt = a->policy.w_fmt;
   c.f32_io = a->io_dtype == GDN_F32;
+  c.block_v = a->policy.state_fmt != GDN_QDQ_OFF ? a->policy.block_v : 64;
   return c;
 }
 
@@ -384,7 +389,10 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages, boo
   k.ws_wscale = reinterpret_cast<float*>(ws + W.wscale);
   // with both QDQ sites on, the state kernel widens the W codes itself, so
   // the images carry them as bytes
-  k.w_img_bytes = (a->policy.state_fmt != GDN_QDQ_OFF && a->policy.w_fmt != GDN_QDQ_OFF) ? 1 : 0;
+  // (the split state kernel, which takes them, spans 64 columns: scale tiles
+  // up to 64 wide)
+  k.w_img_bytes = (a->policy.state_fmt != GDN_QDQ_OFF && a->policy.w_fmt != GDN_QDQ_OFF &&
+                   a->policy.block_v <= 64) ? 1 : 0;
   k.solve_degree = a->policy.solve_degree;
   if (stages & 1) {
     const int num_slots = (int)layout_of(a).num_slots;

@@ -1,5 +1,8 @@
 // Forward, part 2: the sequential state recurrence and the output, one
-// workgroup per (sequence, value head, 64-wide value block), chunks in order
+// workgroup per (sequence, value head, value block), chunks in order. A value
+// block is 64 columns (four waves of 16), or 128 / 256 columns (8 / 16 waves)
+// when the state scale tile is that wide, so that every [Dk, block_v] tile's
+// maximum is reduced inside one workgroup
 // ("[1/4] GDN state/W QAT foundation", "What does this PR do?": state QDQ at
 // every chunk; "[2/4] GDN/KDA decode QAT with INT8 recurrent state", "What
 // does this PR do?": per-head [Dk, block_v] state scales).
@@ -26,8 +29,6 @@ namespace gdn {
 
 namespace {
 
-constexpr int NT = 256;
-
 template <int DK, int NW>
 struct StateBuf {
   bf16 Q[Img<DK>::WQ];
@@ -37,20 +38,22 @@ struct StateBuf {
   alignas(16) float G[Img<DK>::GB / 2];                   // exp(gamma), exp(gamma_n - gamma), exp(gamma_n)
 };
 
-template <int DK, int NW>
+// NWV waves of 16 value columns each (4, 8 or 16).
+template <int DK, int NW, int NWV>
 struct StateCfg {
   using I = Img<DK>;
-  static constexpr int NBUF = (DK == 128 && NW == 2) ? 1 : 2;
-  static constexpr int QPT = 64 * DK / 8 / NT;            // 16-byte Q pieces per thread
+  static constexpr int NT = 64 * NWV;
+  static constexpr int NBUF = ((DK == 128 && NW == 2) || NWV == 16) ? 1 : 2;
+  static constexpr int QN = 64 * DK / 8;                  // 16-byte Q pieces of a chunk
+  static constexpr int QPT = (QN + NT - 1) / NT;          // ... per thread (the last ones guarded)
   static constexpr int IMGP = I::template img<NW>() / 8;  // 16-byte pieces of one image block
-  static constexpr int NPI = (IMGP + NT - 1) / NT;        // image pieces per thread
 };
 
-template <int DK, int NW>
+template <int DK, int NW, int NWV>
 struct StateSmem {
-  StateBuf<DK, NW> buf[StateCfg<DK, NW>::NBUF];
-  alignas(16) bf16 ost[4][64 * 16];                       // per wave: O tile, row-major
-  float red[2][4];                                        // per-wave state amax, by chunk parity
+  StateBuf<DK, NW> buf[StateCfg<DK, NW, NWV>::NBUF];
+  alignas(16) bf16 ost[NWV][64 * 16];                     // per wave: O tile, row-major
+  float red[2][NWV];                                      // per-wave state amax, by chunk parity
 };
 
 // Staging of one chunk's operands into an LDS buffer. The image block (W
@@ -60,9 +63,10 @@ struct StateSmem {
 // by the vmcnt(0) before the chunk's barrier. Q is reordered (pperm +
 // swizzle) on the way, through 16-byte register loads; rows past the chunk
 // end repeat the last row (they only feed output rows that are not stored).
-template <int DK, int NW>
+template <int DK, int NW, int NWV>
 struct Stager {
-  using C = StateCfg<DK, NW>;
+  using C = StateCfg<DK, NW, NWV>;
+  static constexpr int NT = C::NT;
   using I = Img<DK>;
   static constexpr int NINS = C::IMGP / 64;               // wave instructions per image block
   static_assert(C::IMGP % 64 == 0, "image block is a whole number of wave loads");
@@ -71,7 +75,7 @@ struct Stager {
     const bf16* qb = reinterpret_cast<const bf16*>(a.q);
 #pragma unroll
     for (int p = 0; p < C::QPT; ++p) {
-      const int e = tid + NT * p, row = e / (DK / 8), c8 = e % (DK / 8);
+      const int e = min(tid + NT * p, C::QN - 1), row = e / (DK / 8), c8 = e % (DK / 8);
       q[p] = *reinterpret_cast<const uint4*>(
           qb + ((int64_t)(t0 + min(row, nc - 1)) * a.Hqk + hk) * DK + 8 * c8);
     }
@@ -80,42 +84,45 @@ struct Stager {
 #pragma unroll
     for (int p = 0; p < C::QPT; ++p) {
       const int e = tid + NT * p, row = e / (DK / 8), c8 = e % (DK / 8);
+      if (C::QN % NT != 0 && e >= C::QN) continue;
       *reinterpret_cast<uint2*>(&b.Q[wq_off<DK>(row, pperm(8 * c8))]) = make_uint2(q[p].x, q[p].y);
       *reinterpret_cast<uint2*>(&b.Q[wq_off<DK>(row, pperm(8 * c8 + 4))]) = make_uint2(q[p].z, q[p].w);
     }
   }
   // Part `part` of NP of this wave's wave loads of the image block: j = wave
-  // + 4 k, clamped to the last one (a repeated load rewrites the same bytes),
-  // so every wave issues the same compile-time number of loads and the
-  // compiler can wait for older register loads precisely.
+  // + NWV k, clamped to the last one (a repeated load rewrites the same
+  // bytes), so every wave issues the same compile-time number of loads and
+  // the compiler can wait for older register loads precisely.
   template <int NP>
   static __device__ void dma_img(const FwdKernelArgs& a, int64_t ch, StateBuf<DK, NW>& b, int wave,
                                  int lane, int part) {
-    constexpr int KW = (NINS + 3) / 4;
+    constexpr int KW = (NINS + NWV - 1) / NWV;
     const uint4* src = reinterpret_cast<const uint4*>(a.ws_img + ch * I::template img<NW>());
     uint4* dst = reinterpret_cast<uint4*>(b.W);
 #pragma unroll
     for (int k = KW * part / NP; k < KW * (part + 1) / NP; ++k) {
-      const int j = min(wave + 4 * k, NINS - 1);
+      const int j = min(wave + NWV * k, NINS - 1);
       __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
     }
   }
 };
 
-template <int DK, int SF, int WF>
-__global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N, int num_heads) {
+template <int DK, int SF, int WF, int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a, int N, int num_heads) {
   constexpr int NW = WF == 0 ? 2 : 1;
-  using C = StateCfg<DK, NW>;
+  using C = StateCfg<DK, NW, NWV>;
   using I = Img<DK>;
   constexpr int MK = DK / 16;                      // 16-row tiles of the state
   static_assert(sizeof(StateBuf<DK, NW>) == 2 * (I::WQ + I::template img<NW>()),
                 "W, K^T, P and gate images are contiguous after Q");
-  __shared__ __align__(16) StateSmem<DK, NW> sm;
+  static_assert(sizeof(StateSmem<DK, NW, NWV>) <= 160 * 1024, "LDS");
+  __shared__ __align__(16) StateSmem<DK, NW, NWV> sm;
 
-  const int Hv = a.Hv, Dv = a.Dv, NVB = Dv / 64;
+  const int Hv = a.Hv, Dv = a.Dv, NVB = Dv / 64;  // NVB: 64-column blocks (U fragment order)
+  const int NWB = Dv / (16 * NWV);                 // value blocks of this kernel
   // workgroup id -> (head index, value block); the blocks of a head share an XCD
   const int bid = blockIdx.x, xcd = bid & 7, r8 = bid >> 3;
-  const int vb = r8 % NVB, hidx = xcd + 8 * (r8 / NVB);
+  const int vb = r8 % NWB, hidx = xcd + 8 * (r8 / NWB);
   if (hidx >= num_heads) return;
   const int n = hidx / Hv, h = hidx % Hv;
   const int hk = h / (Hv / a.Hqk);
@@ -136,7 +143,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
   // across the chunk loop (fresh_lane in gdn_device.h)
 #define GDN_REFRESH() \
   lane = fresh_lane(); tid = wave * 64 + lane; r16 = lane & 15; grp = lane >> 4
-  const int wcol = vb * 64 + wave * 16;            // first value column of this wave
+  const int wcol = vb * 16 * NWV + wave * 16;      // first value column of this wave
+  const int ug = wcol / 16;                        // 16-column group in U's fragment order
   const int64_t state_base = ((int64_t)n * Hv + h) * DK * Dv;
 
   // state in accumulator layout: S[mt][i] = S[16 mt + 4 grp + i][wcol + r16]
@@ -172,13 +180,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
   auto load_small = [&](int c, f32x4 (&U)[4], float& dW) {
     const int64_t ch = chunk_ch(c);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) U[mt] = *reinterpret_cast<const f32x4*>(a.ws_u + u_off(ch, NVB, vb, wave, mt, lane));
+    for (int mt = 0; mt < 4; ++mt)
+      U[mt] = *reinterpret_cast<const f32x4*>(a.ws_u + u_off(ch, NVB, ug >> 2, ug & 3, mt, lane));
     dW = a.ws_wscale[ch];
   };
 
-  Stager<DK, NW> stg;
+  Stager<DK, NW, NWV> stg;
   stg.load_q(a, chunk_t0(0), chunk_nc(0), hk, tid);
-  Stager<DK, NW>::template dma_img<1>(a, chunk_ch(0), sm.buf[0], wave, lane, 0);
+  Stager<DK, NW, NWV>::template dma_img<1>(a, chunk_ch(0), sm.buf[0], wave, lane, 0);
   load_small(0, Ucur, dWcur);
   stg.store_q(sm.buf[0], tid);
   if (nchunks > 1) stg.load_q(a, chunk_t0(1), chunk_nc(1), hk, tid);
@@ -207,7 +216,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
     const bool more = C::NBUF == 2 && c + 1 < nchunks;
     auto stage_part = [&](int part) {
       if constexpr (C::NBUF == 2) {
-        if (more) Stager<DK, NW>::template dma_img<3>(a, chunk_ch(c + 1), sm.buf[(c + 1) & 1], wave, lane, part);
+        if (more) Stager<DK, NW, NWV>::template dma_img<3>(a, chunk_ch(c + 1), sm.buf[(c + 1) & 1], wave, lane, part);
       }
     };
     stage_part(0);
@@ -391,7 +400,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
       lds_barrier();                             // every wave is done with the buffer
       GDN_REFRESH();
       if (c + 1 < nchunks) {
-        Stager<DK, NW>::template dma_img<1>(a, chunk_ch(c + 1), sm.buf[0], wave, lane, 0);
+        Stager<DK, NW, NWV>::template dma_img<1>(a, chunk_ch(c + 1), sm.buf[0], wave, lane, 0);
         stg.store_q(sm.buf[0], tid);
         if (c + 2 < nchunks) stg.load_q(a, chunk_t0(c + 2), chunk_nc(c + 2), hk, tid);
       }
@@ -416,13 +425,23 @@ __global__ void __launch_bounds__(NT, 1) gdn_state_kernel(FwdKernelArgs a, int N
 
 }  // namespace
 
+template <int DK, int SF, int WF, int NWV>
+static hipError_t launch_state_w(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+  const int num_heads = cfg.N * cfg.Hv, nwb = cfg.Dv / (16 * NWV);
+  const int64_t nblk = (int64_t)nwb * 8 * ((num_heads + 7) / 8);
+  hipLaunchKernelGGL((gdn_state_kernel<DK, SF, WF, NWV>), dim3((unsigned)nblk), dim3(64 * NWV), 0, s,
+                     a, cfg.N, num_heads);
+  return hipGetLastError();
+}
+
+// Value block width: the state scale tile when it is wider than 64 columns.
 template <int DK, int SF, int WF>
 static hipError_t launch_state_one(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
-  const int num_heads = cfg.N * cfg.Hv, nvb = cfg.Dv / 64;
-  const int64_t nblk = (int64_t)nvb * 8 * ((num_heads + 7) / 8);
-  hipLaunchKernelGGL((gdn_state_kernel<DK, SF, WF>), dim3((unsigned)nblk), dim3(NT), 0, s, a, cfg.N,
-                     num_heads);
-  return hipGetLastError();
+  if constexpr (SF != 0) {
+    if (cfg.block_v == 256) return launch_state_w<DK, SF, WF, 16>(cfg, a, s);
+    if (cfg.block_v == 128) return launch_state_w<DK, SF, WF, 8>(cfg, a, s);
+  }
+  return launch_state_w<DK, SF, WF, 4>(cfg, a, s);
 }
 
 template <int DK>
@@ -437,7 +456,7 @@ static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, 
 }
 
 hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
-  if (cfg.state_fmt != 0 && cfg.w_fmt != 0) return launch_fwd_state_split(cfg, a, s);
+  if (a.w_img_bytes) return launch_fwd_state_split(cfg, a, s);
   if (cfg.Dk == 128) return launch_state_dk<128>(cfg, a, s);
   if (cfg.Dk == 64) return launch_state_dk<64>(cfg, a, s);
   return hipErrorInvalidValue;

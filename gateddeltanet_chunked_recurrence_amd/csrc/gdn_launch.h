@@ -49,6 +49,7 @@ struct SavedStamp {
 
 struct FwdConfig {
   int Dk, Dv, N, Hv, state_fmt, w_fmt, f32_io;
+  int block_v;                // state scale tile width (state QDQ on)
 };
 
 // FP32 io (Dk = 64): one fused kernel per (sequence, head, value block).

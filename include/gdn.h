@@ -69,8 +69,11 @@ typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 typedef struct {
   int32_t state_fmt;   /* gdn_qdq_fmt at the state site                      */
   int32_t w_fmt;       /* gdn_qdq_fmt at the W site                          */
-  int32_t block_v;     /* state scale tile width: 16, 32 or 64; divides Dv
-                          (ignored when state_fmt == OFF)                    */
+  int32_t block_v;     /* state scale tile width: 16, 32, 64, 128 or 256;
+                          divides Dv; at most 64 with FP32 inputs (ignored
+                          when state_fmt == OFF). "[2/4] GDN/KDA decode QAT
+                          with INT8 recurrent state", "Testing": all state
+                          scale widths                                       */
   int32_t chunk_size;  /* must be 64                                         */
   int32_t solve_degree;/* 0: exact solve of the WY form (the default). d > 0:
                           opt-in approximate inverse ("[7/7] Experimental

@@ -48,7 +48,9 @@ BAD = [
     (dict(state_fmt=3), B.GDN_E_UNSUPPORTED, 'format'),
     (dict(w_fmt=-1), B.GDN_E_UNSUPPORTED, 'format'),
     (dict(block_v=48), B.GDN_E_UNSUPPORTED, 'block_v'),
-    (dict(Dv=64, block_v=128), B.GDN_E_UNSUPPORTED, 'block_v'),
+    (dict(Dv=64, block_v=128), B.GDN_E_INVALID, 'does not divide'),
+    (dict(block_v=512), B.GDN_E_UNSUPPORTED, 'block_v'),
+    (dict(io_dtype=1, Dk=64, block_v=128), B.GDN_E_UNSUPPORTED, 'block_v up to 64'),
     (dict(Hv=6, Hqk=4), B.GDN_E_INVALID, 'multiple'),
     (dict(Dk=96), B.GDN_E_UNSUPPORTED, 'Dk'),
     (dict(Dv=512), B.GDN_E_UNSUPPORTED, 'Dv'),

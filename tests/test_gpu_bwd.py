@@ -69,6 +69,11 @@ SMALL = [
     # 96 (sequence, head, 64-column) units: the reverse recurrence runs two
     # waves per workgroup here (one below 65 units, four above 128)
     ('gqa_96_units_e4m3', 'fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=150, Hqk=8, Hv=24)),
+    # state scale tiles of 128 and 256 columns (the saved scales per tile)
+    ('e4m3_block_v128', 'fwd_e4m3_b4_t4096_h16_d128',
+     dict(B=1, T=200, Hqk=1, Hv=2, block_v=128, h0=True)),
+    ('int8_dv256_block_v256', 'long_e4m3_t65536_h32_dk128_dv256',
+     dict(T=170, Hqk=1, Hv=2, block_v=256, state_fmt=INT8, w_fmt=E4M3)),
     ('mixed_int8_state_e4m3_w', 'fwd_e4m3_b4_t4096_h16_d128',
      dict(B=1, T=200, Hqk=1, Hv=2, state_fmt=INT8, w_fmt=E4M3, h0=True)),
 ]

@@ -126,6 +126,14 @@ SMALL = [
     # one 64-wide value block per head, varlen with short and empty-tail sequences
     ('varlen_int8_gqa4x16_d128', dict(lengths=[130, 64, 1, 65], Hqk=1, Hv=2, Dv=64,
                                       state_fmt=E4M3, w_fmt=E4M3, block_v=64, h0=True)),
+    # state scale tiles wider than one 64-column value block: the workgroup
+    # spans the tile (8 or 16 waves), both QDQ sites on or mixed formats
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=200, Hqk=1, Hv=2, block_v=128, h0=True)),
+    ('long_e4m3_t65536_h32_dk128_dv256', dict(T=300, Hqk=1, Hv=2, block_v=256, w_fmt=INT8)),
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[130, 3, 70], Hqk=1, Hv=2, Dv=256, block_v=128,
+                                      h0=True)),
+    ('varlen_int8_gqa4x16_d128', dict(lengths=[100, 65], Hqk=1, Hv=2, Dk=64, Dv=256, block_v=256,
+                                      state_fmt=E4M3, w_fmt=E4M3)),
     # empty sequences first, between and last: their ht is h0, they own no chunk
     ('varlen_int8_gqa4x16_d128', dict(lengths=[0, 130, 0, 64, 1, 0], Hqk=1, Hv=2,
                                       state_fmt=E4M3, w_fmt=E4M3, h0=True)),
