@@ -259,7 +259,7 @@ gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
 //   a1     [num_slots, Hv] x 64 x Dv FP32 scale P^T dO
 //   a2     [num_slots, Hv] x Dk x Dv FP32 scale (e^gamma Q)^T dO
 struct BwdWsLayout {
-  int64_t X, W, dstate, dvn, dqk, bimg, a1, a2, total;
+  int64_t X, W, dstate, dvn, dqk, bimg, a1, a2, dX, total;
 };
 
 BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
@@ -276,6 +276,7 @@ BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
   w.bimg = off;    off += bf ? round256(S * Hv * gdn::bwd_img_elems(a->Dk, a->policy.w_fmt) * 2) : 0;
   w.a1 = off;      off += bf ? round256(S * Hv * 64 * a->Dv * 4) : 0;
   w.a2 = off;      off += bf ? round256(S * Hv * a->Dk * a->Dv * 4) : 0;
+  w.dX = off;      off += a->policy.solve_degree > 0 ? round256(S * Hv * 64 * 64 * 4) : 0;
   w.total = off;
   return w;
 }
@@ -427,9 +428,6 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   if (!a) return fail(GDN_E_INVALID, "argument struct is NULL");
   gdn_status s = check_fwd_shape(&a->fwd);
   if (s != GDN_OK) return s;
-  if (a->fwd.policy.solve_degree != 0)
-    return fail(GDN_E_UNSUPPORTED, "the backward of the Neumann solve (degree %d) is not built",
-                a->fwd.policy.solve_degree);
   if ((s = check_fwd_ptrs(&a->fwd, false)) != GDN_OK) return s;
   const bool any = (int64_t)a->fwd.B * a->fwd.T > 0;
   if (a->grad_dtype != GDN_F32 && a->grad_dtype != a->fwd.io_dtype)
@@ -463,8 +461,13 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   const BwdWsLayout W = bwd_ws_layout(&a->fwd);
   // bf16 inputs with W QDQ: X comes from the forward (saved); otherwise the
   // backward's first kernel solves again into the workspace
-  k.ws_X = (k.f.s_X && a->fwd.policy.w_fmt != GDN_QDQ_OFF) ? k.f.s_X
-                                                            : reinterpret_cast<float*>(ws + W.X);
+  // (with the approximate inverse the saved X is the polynomial, which no
+  // exact solve may replace)
+  k.ws_X = (k.f.s_X && (a->fwd.policy.w_fmt != GDN_QDQ_OFF || a->fwd.policy.solve_degree > 0))
+               ? k.f.s_X
+               : reinterpret_cast<float*>(ws + W.X);
+  k.ws_dX = reinterpret_cast<float*>(ws + W.dX);
+  k.f.solve_degree = a->fwd.policy.solve_degree;
   k.ws_W = reinterpret_cast<float*>(ws + W.W);
   k.ws_dstate = reinterpret_cast<float*>(ws + W.dstate);
   k.ws_dvn = reinterpret_cast<float*>(ws + W.dvn);

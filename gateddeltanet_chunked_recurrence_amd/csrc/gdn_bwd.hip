@@ -189,13 +189,19 @@ __global__ void __launch_bounds__(NT, 1) bwd_prep(BwdKernelArgs a, int N) {
 
   stage_rows<F32IN>(Kf, LK, f.k, ch.t0, ch.nc, Hqk, hk, DK, 0, DK, tid);
   load_gates(gs, f.g, f.beta, ch.t0, ch.nc, Hv, h, wave, lane);
-  __syncthreads();
-  build_L<DK>(Kf, gs, Lf, wave, lane);
-  __syncthreads();
-  solve64(Lf, Xf, Yf, wave, lane);
-
   float* Xg = a.ws_X + ((int64_t)slot * Hv + h) * 4096;
-  for (int e = tid; e < 4096; e += NT) Xg[e] = Xf[(e >> 6) * 65 + (e & 63)];
+  if (f.solve_degree > 0) {
+    // approximate inverse: X is the forward's saved polynomial (ws_X points
+    // at it), never a fresh exact solve
+    for (int e = tid; e < 4096; e += NT) Xf[(e >> 6) * 65 + (e & 63)] = Xg[e];
+    __syncthreads();
+  } else {
+    __syncthreads();
+    build_L<DK>(Kf, gs, Lf, wave, lane);
+    __syncthreads();
+    solve64(Lf, Xf, Yf, wave, lane);
+    for (int e = tid; e < 4096; e += NT) Xg[e] = Xf[(e >> 6) * 65 + (e & 63)];
+  }
 
   float* Wg = a.ws_W + ((int64_t)ch.t0 * Hv + h) * DK;
   if constexpr (WF != 0 && !F32IN) {
@@ -226,6 +232,174 @@ __global__ void __launch_bounds__(NT, 1) bwd_prep(BwdKernelArgs a, int N) {
         const int row = 16 * mt + 4 * grp + i;
         if (row < ch.nc) Wg[(int64_t)row * Hv * DK + 16 * nt + r16] = w[i];
       }
+    }
+  }
+}
+
+// --------------------------------------------------------------- bwd_neumann
+// Gradient through the approximate inverse ("[7/7] Experimental GDN/KDA
+// approximate-inverse QAT", "What does this PR do?": the backward
+// differentiates the actual polynomial). With X = sum_{m=0..d} (-L)^m and
+// G = dL/dX (its strict lower part: X's other entries do not depend on L),
+//   dL = -sum_{m=1..d} sum_{a+b=m-1} (-L^T)^a G (-L^T)^b
+// (the adjoint of the directional derivative of the polynomial). That double
+// sum is the top-right block of sum_{m=0..d} M^m for the block matrix
+// M = [[-L^T, G], [0, -L^T]] (the top-right block of M^m is exactly
+// sum_{a+b=m-1} (-L^T)^a G (-L^T)^b), and for d = 2^j - 1 that sum is the
+// product (I + M)(I + M^2)(I + M^4)..., the same factorization the forward
+// uses. Each block product needs the diagonal block D and the top-right
+// block E: P = M^(2^i) is [[Pd, Pe], [0, Pd]], the partial product is
+// [[Xd, Xe], [0, Xd]], and per step
+//   Pd' = Pd Pd,  Pe' = Pd Pe + Pe Pd,  Xd' = Xd + Xd Pd',  Xe' = Xd Pe' + Xe + Xe Pd'.
+// Then dL = -Xe below the diagonal, and the terms of L_ij = beta_i (k_i . k_j)
+// Gam_ij that bwd_local_kernel leaves out for this policy are added here:
+//   dk += (dA + dA^T) K with dA = dL beta Gam;  d beta_i += sum_j dL_ij (K K^T)_ij Gam_ij;
+//   d gamma_i += sum_j dL_ij L_ij, d gamma_j -= sum_i dL_ij L_ij, and dg gets
+// the chunk-local suffix sums of those d gamma. dk goes to the per-value-head
+// FP32 rows (the group sum follows); d beta and dg are read, added to and
+// written back (one workgroup per chunk and head owns those entries).
+// FP32 throughout (FP32 MFMA 16x16x4).
+template <int DK>
+__global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
+  constexpr int LK = DK + 1;
+  constexpr int M65 = 64 * 65;
+  __shared__ float Kf[64 * LK];
+  __shared__ float Lf[M65];
+  __shared__ float Mb[6][M65];
+  __shared__ Gates gs;
+  __shared__ float rowB[64], rowG[64], colG[64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
+  const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const FwdKernelArgs& f = a.f;
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  if (!ch.valid) return;
+  const int Hv = f.Hv, Hqk = f.Hqk, hk = h / (Hv / Hqk), nc = ch.nc;
+  const int64_t chb = (int64_t)slot * Hv + h;
+
+  stage_rows<false>(Kf, LK, f.k, ch.t0, nc, Hqk, hk, DK, 0, DK, tid);
+  load_gates(gs, f.g, f.beta, ch.t0, nc, Hv, h, wave, lane);
+  __syncthreads();
+  build_L<DK>(Kf, gs, Lf, wave, lane);
+  __syncthreads();
+  // M = [[-L^T, G], [0, -L^T]]: P = M, partial product I + M
+  int iPd = 0, iPe = 1, iXd = 2, iXe = 3, iT1 = 4, iT2 = 5;
+  {
+    const float* dXg = a.ws_dX + chb * 4096;
+    for (int e = tid; e < 4096; e += NT) {
+      const int i = e >> 6, j = e & 63;
+      const float g = (j < i && i < nc) ? dXg[e] : 0.f;
+      const float lt = Lf[j * 65 + i];
+      Mb[iPd][i * 65 + j] = -lt;
+      Mb[iXd][i * 65 + j] = (i == j ? 1.f : 0.f) - lt;
+      Mb[iPe][i * 65 + j] = g;
+      Mb[iXe][i * 65 + j] = g;
+    }
+  }
+  __syncthreads();
+  for (int d = 1; d < f.solve_degree; d = 2 * d + 1) {
+    const float *Pd = Mb[iPd], *Pe = Mb[iPe];
+    float *T1 = Mb[iT1], *T2 = Mb[iT2];
+    for (int t = wave; t < 16; t += 4) {
+      const int i0 = 16 * (t >> 2), j0 = 16 * (t & 3);
+      f32x4 pe = mm(Pd, 65, 1, Pe, 65, 1, i0, j0, 0, 64, r16, grp, zero4());
+      pe = mm(Pe, 65, 1, Pd, 65, 1, i0, j0, 0, 64, r16, grp, pe);
+      const f32x4 pd = mm(Pd, 65, 1, Pd, 65, 1, i0, j0, 0, 64, r16, grp, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        T1[(i0 + 4 * grp + i) * 65 + j0 + r16] = pe[i];
+        T2[(i0 + 4 * grp + i) * 65 + j0 + r16] = pd[i];
+      }
+    }
+    __syncthreads();
+    // new Xe and Xd into the buffers of the old Pe and Pd (no longer read)
+    const float *Xd = Mb[iXd], *Xe = Mb[iXe];
+    float *nXe = Mb[iPe], *nXd = Mb[iPd];
+    for (int t = wave; t < 16; t += 4) {
+      const int i0 = 16 * (t >> 2), j0 = 16 * (t & 3);
+      f32x4 xe, xd;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xe[i] = Xe[(i0 + 4 * grp + i) * 65 + j0 + r16];
+        xd[i] = Xd[(i0 + 4 * grp + i) * 65 + j0 + r16];
+      }
+      xe = mm(Xd, 65, 1, T1, 65, 1, i0, j0, 0, 64, r16, grp, xe);
+      xe = mm(Xe, 65, 1, T2, 65, 1, i0, j0, 0, 64, r16, grp, xe);
+      xd = mm(Xd, 65, 1, T2, 65, 1, i0, j0, 0, 64, r16, grp, xd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nXe[(i0 + 4 * grp + i) * 65 + j0 + r16] = xe[i];
+        nXd[(i0 + 4 * grp + i) * 65 + j0 + r16] = xd[i];
+      }
+    }
+    __syncthreads();
+    const int oXd = iXd, oXe = iXe;
+    iXd = iPd; iXe = iPe; iPd = iT2; iPe = iT1; iT1 = oXd; iT2 = oXe;
+  }
+  // dL = -Xe below the diagonal (rows and columns of the chunk); dA = dL beta Gam
+  const float* Xe = Mb[iXe];
+  float* DA = Mb[iT1];
+  float* AG = Mb[iT2];
+  for (int e = tid; e < 4096; e += NT) {
+    const int i = e >> 6, j = e & 63;
+    const float dl = (j < i && i < nc) ? -Xe[i * 65 + j] : 0.f;
+    DA[i * 65 + j] = dl * gs.bet[i] * fexp2(gs.gam2[i] - gs.gam2[j]);
+  }
+  // (K K^T)_ij Gam_ij below the diagonal
+  for (int t = wave; t < 16; t += 4) {
+    const int mi = t >> 2, mj = t & 3;
+    const f32x4 kk = mm(Kf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4());
+    const int cj = 16 * mj + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mi + 4 * grp + i;
+      AG[row * 65 + cj] = row > cj ? kk[i] * fexp2(gs.gam2[row] - gs.gam2[cj]) : 0.f;
+    }
+  }
+  __syncthreads();
+  // row and column sums: d beta_i = sum_j dL_ij AG_ij; d gamma parts from dL_ij L_ij
+  if (tid < 64) {
+    const int i = tid;
+    float sb = 0.f, sg = 0.f;
+    for (int j = 0; j < i; ++j) {
+      const float dl = i < nc ? -Xe[i * 65 + j] : 0.f;
+      sb += dl * AG[i * 65 + j];
+      sg += dl * Lf[i * 65 + j];
+    }
+    rowB[i] = sb;
+    rowG[i] = sg;
+  } else if (tid < 128) {
+    const int j = tid - 64;
+    float cg = 0.f;
+    for (int i = j + 1; i < nc; ++i) cg += -Xe[i * 65 + j] * Lf[i * 65 + j];
+    colG[j] = cg;
+  }
+  // C = dA + dA^T into the Xe buffer's place is not needed: K products read DA twice
+  __syncthreads();
+  // dk += (dA + dA^T) K, added to this value head's FP32 dk rows
+  for (int t = wave; t < 4 * (DK / 16); t += 4) {
+    const int mt = t & 3, nt = t >> 2;
+    f32x4 acc = mm(DA, 65, 1, Kf, LK, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, zero4());
+    acc = mm(DA, 1, 65, Kf, LK, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * grp + i;
+      if (row < nc) a.ws_dqk[(((int64_t)(ch.t0 + row) * Hv + h) * 2 + 1) * DK + 16 * nt + r16] += acc[i];
+    }
+  }
+  if (wave == 0) {
+    const int j = lane;
+    const float dgam = j < nc ? rowG[j] - colG[j] : 0.f;
+    float suf = dgam;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(suf, off, WAVE);
+      if (j + off < 64) suf += y;
+    }
+    if (j < nc) {
+      const int64_t gi = (int64_t)(ch.t0 + j) * Hv + h;
+      a.dg[gi] += suf;
+      a.dbeta[gi] += rowB[j];
     }
   }
 }
@@ -710,8 +884,12 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {
     if ((e = launch_bwd_local(c, a, s)) != hipSuccess) return e;
+    if (a.f.solve_degree > 0) {                      // the dL terms of the approximate inverse
+      hipLaunchKernelGGL((bwd_neumann<DK>), slots, dim3(NT), 0, s, a, c.N);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  if (!F32IN && c.Hv == c.Hqk) return hipSuccess;   // dq, dk written directly
+  if (!F32IN && c.Hv == c.Hqk && a.f.solve_degree == 0) return hipSuccess;   // dq, dk written directly
   hipLaunchKernelGGL((bwd_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, s, a, c.Hv / c.Hqk);
   return hipGetLastError();
 }

@@ -213,7 +213,10 @@ struct PassLoads {
   f32x4 ds[NU];
 };
 
-template <int DK, int SF, int WF>
+// NEU: the chunk's X is the approximate inverse (a polynomial in L). Its dL
+// terms (dA, the d beta and d gamma parts from L) are left out here and dX
+// is exported instead; bwd_neumann adds them (gdn_bwd.hip).
+template <int DK, int SF, int WF, bool NEU>
 __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N) {
   constexpr int VB = WF == 0 ? 32 : 64;            // value columns per pass
   constexpr int NWP = WF == 0 ? 2 : 1;             // W planes
@@ -604,7 +607,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   constexpr int FLDK = FS::LDK;
   // dq, dk rows: straight to the outputs with one value head per query/key
   // head, else per value head (FP32) for the group sum
-  const bool direct = Hv == Hqk;
+  const bool direct = Hv == Hqk && !NEU;           // NEU: bwd_neumann adds to dk first
   const bool half = direct && !a.grad_f32;         // bf16 outputs
   const int esz = half ? 2 : 4;
   const int64_t rstride = direct ? (int64_t)Hv * DK * esz : (int64_t)Hv * 2 * DK * 4;
@@ -706,6 +709,11 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
       put_T(F.GTA[0], F.GTA[1], L64, G, tw, st, r16, grp);
       put_N(F.GA[0], F.GA[1], L64, G, tw, st, r16, grp, sel);
       put_T(F.dXTm[0], F.dXTm[1], L64, dX, tw, st, r16, grp);
+      if constexpr (NEU) {
+        float* dxg = a.ws_dX + chb * 4096 + 16 * st + r16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dxg[(16 * tw + 4 * grp + q) * 64] = dX[q];
+      }
     }
     // column partial sums of this wave's 16 rows
 #pragma unroll
@@ -814,10 +822,12 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
     for (int i = 0; i < 2; ++i) {
       const int ut = 2 * hk + i;
       f32x4 ml = zero4();
+      if constexpr (!NEU) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        ml = mm3(ml, AM[kk][0], AM[kk][1], rowp(F.Xm[0], L64, 16 * ut, 32 * kk, r16, grp),
-                 rowp(F.Xm[1], L64, 16 * ut, 32 * kk, r16, grp));
+        for (int kk = 0; kk < 2; ++kk)
+          ml = mm3(ml, AM[kk][0], AM[kk][1], rowp(F.Xm[0], L64, 16 * ut, 32 * kk, r16, grp),
+                   rowp(F.Xm[1], L64, 16 * ut, 32 * kk, r16, grp));
+      }
       const int u = 16 * ut + r16;
       const float gu = gu2[i];
       f32x4 dA;
@@ -937,7 +947,10 @@ static hipError_t launch_local_dk(const BwdConfig& c, const BwdKernelArgs& a, hi
   const dim3 grid(a.num_slots, c.Hv);
 #define GDN_CASE(SFv, WFv) \
   if (c.state_fmt == SFv && c.w_fmt == WFv) { \
-    hipLaunchKernelGGL((bwd_local_kernel<DK, SFv, WFv>), grid, dim3(NT), 0, s, a, c.N); \
+    if (a.f.solve_degree > 0) \
+      hipLaunchKernelGGL((bwd_local_kernel<DK, SFv, WFv, true>), grid, dim3(NT), 0, s, a, c.N); \
+    else \
+      hipLaunchKernelGGL((bwd_local_kernel<DK, SFv, WFv, false>), grid, dim3(NT), 0, s, a, c.N); \
     return hipGetLastError(); \
   }
   GDN_CASE(0, 0) GDN_CASE(0, 1) GDN_CASE(0, 2)

@@ -80,6 +80,7 @@ struct BwdKernelArgs {
   float* ws_a1;               // [num_slots * Hv] x [64, Dv] fragment order: scale P^T dO
   float* ws_a2;               // [num_slots * Hv] x [Dk, Dv] fragment order: scale (e^gamma Q)^T dO
   float* ws_dqk;              // [B*T, Hv, 2, Dk] FP32 per-value-head dq, dk before the group sum
+  float* ws_dX;               // [num_slots, Hv, 64, 64] FP32 dL/dX per chunk (approximate inverse only)
   int32_t grad_f32;
   int32_t total_tokens;
   int32_t num_slots;

@@ -82,10 +82,12 @@ typedef struct {
                           polynomial sum_{m=0..d} (-L)^m, in FP32. d must be
                           2^j - 1 for j = 1..6 (1, 3, 7, 15, 31, 63); any
                           other value is GDN_E_UNSUPPORTED, never rounded to
-                          a supported one. Built for bf16 inputs and the
-                          forward only: FP32 inputs and gdn_chunk_bwd return
-                          GDN_E_UNSUPPORTED for d > 0. The saved buffer's x
-                          section then holds the polynomial, not the inverse. */
+                          a supported one. Built for bf16 inputs (FP32
+                          inputs return GDN_E_UNSUPPORTED for d > 0). The
+                          saved buffer's x section then holds the
+                          polynomial, not the inverse, and gdn_chunk_bwd
+                          differentiates the polynomial itself: dL =
+                          -sum_{m=1..d} sum_{a+b=m-1} (-L^T)^a dX (-L^T)^b. */
 } gdn_qdq_policy;
 
 /* Forward arguments. Shapes: without cu_seqlens there are N = B sequences of

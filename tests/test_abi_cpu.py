@@ -153,16 +153,20 @@ def test_backward_rejects_before_launch():
     assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_INVALID
 
 
-def test_backward_of_the_neumann_solve_is_rejected():
-    """The Neumann polynomial's backward is not built: a valid degree is
-    refused by gdn_chunk_bwd (never run with the exact solve's gradient),
-    before any pointer or workspace check."""
+def test_backward_of_the_neumann_solve_is_accepted():
+    """The backward differentiates the approximate inverse's polynomial: a
+    valid degree passes the backward's policy checks (it stops at the missing
+    workspace here) and its workspace includes the dL/dX section."""
     lib = B.load_library()
     fake = ctypes.c_void_p(0x10000)
     a = B.BwdArgs(fwd=_args(saved=fake, solve_degree=7), do_=fake, dq=fake, dk=fake, dv=fake,
                   dg=fake, dbeta=fake, grad_dtype=B.GDN_BF16)
-    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_UNSUPPORTED
-    assert 'Neumann' in lib.gdn_last_error().decode()
+    assert lib.gdn_chunk_bwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
+    exact = B.BwdArgs(fwd=_args(saved=fake), do_=fake, dq=fake, dk=fake, dv=fake, dg=fake,
+                      dbeta=fake, grad_dtype=B.GDN_BF16)
+    slots = 1 + 2
+    assert (lib.gdn_bwd_workspace_bytes(ctypes.byref(a)) -
+            lib.gdn_bwd_workspace_bytes(ctypes.byref(exact))) >= slots * 4 * 64 * 64 * 4
     for d in (1, 3, 7, 15, 31, 63):                   # every admitted degree passes the forward checks
         f = _args(solve_degree=d)
         assert lib.gdn_fwd_workspace_bytes(ctypes.byref(f)) > 0
