@@ -41,6 +41,18 @@ polynomial degree d replaces the exact solve by
 and the backward differentiates that polynomial (autograd through the same
 sum). L is strictly lower triangular, so (-L)^n = 0 for n >= n_c and any
 d >= n_c - 1 gives the exact inverse.
+
+Opt-in two-precision profile ("[5/8] ReplaySSM state QAT and two-precision
+GDN", "What does this PR do?" and "Usage": the state quantizer disabled, an
+FP32 recurrence anchor, and a dynamic E4M3 read quantizer grouped by 128 key
+channels per value row, whose errors never overwrite the anchor). On the
+chunk path, read here as: with read_fmt set (state_fmt must be off) every
+read of the chunk's incoming state uses Sr = QDQ_R(S), one scale per value
+column over all Dk key channels, while the carry keeps S:
+
+    Vnew      = U - Wq Sr
+    O         = scale (diag(exp(gamma)) Q Sr + ((Q K^T) * Gam) Vnew)
+    S_next    = exp(gamma_n) S + (diag(exp(gamma_n - gamma)) K)^T Vnew
 """
 import math
 
@@ -108,7 +120,7 @@ def wy_factor(Kc, gc, bc, solve_degree=0):
 
 
 def _chunk_loop(Q, K, V, g, beta, S, scale, state_fmt, w_fmt, block_v, chunk,
-                rec, site_fn, solve_degree=0):
+                rec, site_fn, solve_degree=0, read_fmt=FMT_OFF):
     """Z independent (sequence, head) streams of equal length.
     Q, K: [Z, L, Dk]; V: [Z, L, Dv]; g, beta: [Z, L]; S: [Z, Dk, Dv]."""
     Z, Lseq, Dk = Q.shape
@@ -127,9 +139,13 @@ def _chunk_loop(Q, K, V, g, beta, S, scale, state_fmt, w_fmt, block_v, chunk,
         else:
             Sq = site_fn(S.reshape(Z, Dk, Dv // block_v, block_v), state_fmt, (1, 3),
                          None if rec is None else rec['S']).reshape(Z, Dk, Dv)
-        Vnew = U - Wq @ Sq
+        # the state as read: Sq, or the two-precision read copy (one scale
+        # per value column over the Dk key channels)
+        Sr = Sq if read_fmt == FMT_OFF else site_fn(S, read_fmt, (1,),
+                                                    None if rec is None else rec['R'])
+        Vnew = U - Wq @ Sr
         P = (Qc @ Kc.transpose(1, 2)) * Gam
-        outs.append(scale * (torch.exp(gam)[:, :, None] * (Qc @ Sq) + P @ Vnew))
+        outs.append(scale * (torch.exp(gam)[:, :, None] * (Qc @ Sr) + P @ Vnew))
         gl = gam[:, -1]
         Kd = torch.exp(gl[:, None] - gam)[:, :, None] * Kc
         S = torch.exp(gl)[:, None, None] * Sq + Kd.transpose(1, 2) @ Vnew
@@ -146,7 +162,7 @@ def _as64(x):
 
 def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
                 state_fmt=FMT_OFF, w_fmt=FMT_OFF, block_v=64, chunk=64,
-                record=None, site_fn=None, solve_degree=0):
+                record=None, site_fn=None, solve_degree=0, read_fmt=FMT_OFF):
     """q, k: [B, T, Hqk, Dk]; v: [B, T, Hv, Dv]; g, beta: [B, T, Hv];
     h0: [N, Hv, Dk, Dv] or None; cu_seqlens: N+1 offsets (B must be 1).
     float64 torch tensors (autograd flows through them) or arrays.
@@ -161,10 +177,16 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
     S, chunk by chunk); used by the tests' frozen-offset surrogate.
 
     solve_degree: 0 for the exact solve, else the Neumann polynomial degree
-    (any d >= 1) in its place."""
+    (any d >= 1) in its place.
+
+    read_fmt: the two-precision profile's read quantizer (state_fmt must be
+    off); record['R'][n][c] = (codes [Z, Dk, Dv], d [Z, 1, Dv]). Site order
+    per chunk: W, S, then R."""
     site_fn = qdq_ste if site_fn is None else site_fn
     if solve_degree < 0:
         raise ValueError("solve_degree must be 0 (exact) or a polynomial degree >= 1")
+    if read_fmt != FMT_OFF and state_fmt != FMT_OFF:
+        raise ValueError("the two-precision read copy replaces the state quantizer")
     q, k, v, g, beta, h0 = map(_as64, (q, k, v, g, beta, h0))
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -176,6 +198,7 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
     if record is not None:
         record.setdefault('S', [])
         record.setdefault('W', [])
+        record.setdefault('R', [])
 
     def streams(x, lo, hi):      # [B, T, H, D] -> [B*H, hi-lo, D]
         x = x[:, lo:hi]
@@ -194,19 +217,20 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
     for n, (lo, hi) in enumerate(bounds):
         if cu_seqlens is not None:
             S0 = torch.zeros(Hv, Dk, Dv, dtype=torch.float64) if h0 is None else h0[n]
-        rec = None if record is None else {'S': [], 'W': []}
+        rec = None if record is None else {'S': [], 'W': [], 'R': []}
         if hi > lo:
             o_n, S_n = _chunk_loop(streams(qv, lo, hi), streams(kv, lo, hi),
                                    streams(v, lo, hi),
                                    streams(g[..., None], lo, hi)[..., 0],
                                    streams(beta[..., None], lo, hi)[..., 0],
                                    S0, scale, state_fmt, w_fmt, block_v, chunk, rec,
-                                   site_fn, solve_degree)
+                                   site_fn, solve_degree, read_fmt)
         else:
             o_n, S_n = torch.zeros(S0.shape[0], 0, Dv, dtype=torch.float64), S0
         if record is not None:
             record['S'].append(rec['S'])
             record['W'].append(rec['W'])
+            record['R'].append(rec['R'])
         Bn = B if cu_seqlens is None else 1
         o_parts.append(o_n.reshape(Bn, Hv, hi - lo, Dv).permute(0, 2, 1, 3))
         ht_parts.append(S_n.reshape(Bn, Hv, Dk, Dv))
@@ -217,7 +241,7 @@ def chunked_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
 
 def chunked_bwd(q, k, v, g, beta, scale, do, dht=None, h0=None, cu_seqlens=None,
                 state_fmt=FMT_OFF, w_fmt=FMT_OFF, block_v=64, chunk=64, site_fn=None,
-                solve_degree=0):
+                solve_degree=0, read_fmt=FMT_OFF):
     """Reverse-mode derivative of chunked_fwd with every QDQ's Jacobian taken
     as the identity (identity straight-through estimator). The forward values
     of Sq and Wq are used inside every product, as the saved quantized W is
@@ -234,7 +258,7 @@ def chunked_bwd(q, k, v, g, beta, scale, do, dht=None, h0=None, cu_seqlens=None,
     o, ht = chunked_fwd(leaves['q'], leaves['k'], leaves['v'], leaves['g'],
                         leaves['beta'], scale, leaves.get('h0'), cu_seqlens,
                         state_fmt, w_fmt, block_v, chunk, site_fn=site_fn,
-                        solve_degree=solve_degree)
+                        solve_degree=solve_degree, read_fmt=read_fmt)
     outs, grads = [o], [_as64(do)]
     if dht is not None:
         outs.append(ht)

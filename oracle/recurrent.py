@@ -23,6 +23,15 @@ path, "[1/4]" "What does this PR do?"): before the first token of every
 chunk of `chunk` tokens (sequence-relative), S <- QDQ(S) with one scale per
 [Dk, block_v] tile, evaluated in FP32 on fl32(S). The final state is
 returned without QDQ.
+
+Optional two-precision read copy ("[5/8] ReplaySSM state QAT and
+two-precision GDN", "What does this PR do?": an FP32 recurrence anchor and a
+quantized copy used for reads, whose errors never overwrite the anchor),
+chunk-path reading: at the first token of every chunk the read offset
+E = S - QDQ_R(S) is taken (one scale per value column over all Dk key
+channels) and decays with the state, so every read in the chunk (the
+delta-rule prediction S^T k_t and the readout S^T q_t) sees S - a E, a the
+decay since the chunk start, while the writes go to the anchor S itself.
 """
 import numpy as np
 
@@ -47,7 +56,7 @@ def qdq_state64(S, fmt, block_v):
 
 
 def recurrent_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
-                  state_fmt=FMT_OFF, block_v=64, chunk=64):
+                  state_fmt=FMT_OFF, block_v=64, chunk=64, read_fmt=FMT_OFF):
     """q, k: [B, T, Hqk, Dk]; v: [B, T, Hv, Dv]; g, beta: [B, T, Hv].
     With cu_seqlens (length N+1) B must be 1 and T is the packed length.
     h0: [N, Hv, Dk, Dv] or None.  Returns (o [B, T, Hv, Dv], ht [N, Hv, Dk, Dv])
@@ -70,12 +79,19 @@ def recurrent_fwd(q, k, v, g, beta, scale, h0=None, cu_seqlens=None,
     ht = np.zeros((len(seqs), Hv, Dk, Dv))
     for n, (bos, eos) in enumerate(seqs):
         S = np.zeros((Hv, Dk, Dv)) if h0 is None else np.array(h0[n], np.float64)
+        E = np.zeros((Hv, Dk, Dv))                   # read offset (two-precision)
+        a = np.ones(Hv)                              # its decay since the chunk start
         for t in range(bos, eos):
             if state_fmt != FMT_OFF and (t - bos) % chunk == 0:
                 S = qdq_state64(S, state_fmt, block_v)
+            if read_fmt != FMT_OFF and (t - bos) % chunk == 0:
+                r, _, _ = qdq32(S.astype(np.float32), read_fmt, tile_axes=(1,))
+                E = S - r.astype(np.float64)
+                a = np.ones(Hv)
             S = np.exp(gf[t])[:, None, None] * S
-            u = bf[t][:, None] * (vf[t] - np.einsum('hkv,hk->hv', S, kf[t]))
+            a = np.exp(gf[t]) * a
+            u = bf[t][:, None] * (vf[t] - np.einsum('hkv,hk->hv', S - a[:, None, None] * E, kf[t]))
             S = S + kf[t][:, :, None] * u[:, None, :]
-            o[t] = scale * np.einsum('hkv,hk->hv', S, qf[t])
+            o[t] = scale * np.einsum('hkv,hk->hv', S - a[:, None, None] * E, qf[t])
         ht[n] = S
     return o.reshape(B, T, Hv, Dv), ht

@@ -115,14 +115,19 @@ class _Frozen:
         return x + e
 
 
-@pytest.mark.parametrize("state_fmt,w_fmt,block_v", [(FMT_E4M3, FMT_E4M3, 4),
-                                                     (FMT_INT8, FMT_OFF, 8),
-                                                     (FMT_OFF, FMT_E4M3, 8)])
-def test_bwd_ste_equals_frozen_offset_surrogate_gradient(state_fmt, w_fmt, block_v):
+@pytest.mark.parametrize("state_fmt,w_fmt,block_v,read_fmt", [(FMT_E4M3, FMT_E4M3, 4, FMT_OFF),
+                                                              (FMT_INT8, FMT_OFF, 8, FMT_OFF),
+                                                              (FMT_OFF, FMT_E4M3, 8, FMT_OFF),
+                                                              (FMT_OFF, FMT_OFF, 8, FMT_E4M3),
+                                                              (FMT_OFF, FMT_INT8, 8, FMT_E4M3)])
+def test_bwd_ste_equals_frozen_offset_surrogate_gradient(state_fmt, w_fmt, block_v, read_fmt):
+    """read_fmt: the two-precision read copy ("[5/8] ReplaySSM state QAT and
+    two-precision GDN", "Testing": first-order gradients) through the same
+    surrogate: its offset is frozen at every read, the FP32 carry is not."""
     c = rand_case(54, lengths=[100, 3, 64], Hqk=1, Hv=2, Dk=4, Dv=8, retention=True)
     do, dht = _upstream(c, 4)
     scale = 0.5
-    kw = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v)
+    kw = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v, read_fmt=read_fmt)
     grads = chunked_bwd(c['q'], c['k'], c['v'], c['g'], c['beta'], scale, do, dht,
                         c['h0'], c['cu_seqlens'], **kw)
     fr = _Frozen()

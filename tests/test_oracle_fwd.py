@@ -262,3 +262,51 @@ def test_power_of_two_equivariance_with_qdq():
     o2, h2 = chunked_fwd(c['q'], c['k'], 8.0 * c['v'], c['g'], c['beta'], 0.3,
                          8.0 * c['h0'], **args)
     assert torch.equal(o2, 8.0 * o1) and torch.equal(h2, 8.0 * h1)
+
+
+# ------------------------------------------------- two-precision read copy
+
+def test_read_profile_chunked_equals_token_recurrence_with_read_offsets():
+    """The chunk form of the two-precision profile (reads through the
+    per-column E4M3 copy of the chunk's incoming state, carry in FP32)
+    equals the token recurrence that reads S - a E, E the read offset taken
+    at each chunk start and a its decay ("[5/8] ReplaySSM state QAT and
+    two-precision GDN", "What does this PR do?")."""
+    c = rand_case(31, lengths=[130, 64, 5], Hqk=1, Hv=2, Dk=8, Dv=16, retention=True)
+    (o1, h1), (o2, h2) = _both(c, read_fmt=FMT_E4M3)
+    assert rel(o2, o1) < 1e-12
+    assert rel(h2, h1) < 1e-12
+    (o0, h0), _ = _both(c)
+    assert rel(o1, o0) > 1e-4 and rel(h1, h0) > 1e-5        # the read copy did something
+    (oq, hq), _ = _both(c, state_fmt=FMT_E4M3, block_v=16)
+    assert rel(h1, hq) > 1e-5                              # and it is not the quantized carry
+
+
+def test_read_profile_zero_beta_keeps_the_anchor_exact():
+    """With beta = 0 nothing is written: the anchor only decays, so ht is
+    the exact decay of h0 (read errors never reach it), while each output
+    reads the per-column E4M3 copy of the chunk's incoming state, decayed:
+    o_t = scale (exp(gamma_t) QDQ_R(S_c))^T q_t."""
+    c = rand_case(32, T=150, Hqk=1, Hv=2, Dk=8, Dv=4)
+    c['beta'] = np.zeros_like(c['beta'])
+    scale = 0.6
+    o, ht = chunked_fwd(c['q'], c['k'], c['v'], c['g'], c['beta'], scale, c['h0'],
+                        read_fmt=FMT_E4M3)
+    o, ht = o.numpy(), ht.numpy()
+    cum = np.cumsum(c['g'][0], axis=0)                       # [T, Hv]
+    np.testing.assert_allclose(ht[0], np.exp(cum[-1])[:, None, None] * c['h0'][0], rtol=1e-13)
+    for t in (0, 5, 63, 64, 100, 149):
+        c0 = 64 * (t // 64)
+        Sc = c['h0'][0] * (np.exp(cum[c0 - 1]) if c0 > 0 else np.ones(2))[:, None, None]
+        r, _, _ = qdq32(Sc.astype(np.float32), FMT_E4M3, (1,))
+        decay = np.exp(cum[t] - (cum[c0 - 1] if c0 > 0 else 0.0))
+        want = scale * np.einsum('hkv,hk->hv', decay[:, None, None] * r.astype(np.float64),
+                                 c['q'][0, t, [0, 0]])
+        np.testing.assert_allclose(o[0, t], want, rtol=1e-12, atol=1e-15)
+
+
+def test_read_profile_refuses_a_quantized_carry():
+    c = rand_case(33, T=10, Hqk=1, Hv=1, Dk=4, Dv=4)
+    with pytest.raises(ValueError):
+        chunked_fwd(c['q'], c['k'], c['v'], c['g'], c['beta'], 0.5, c['h0'],
+                    state_fmt=FMT_E4M3, read_fmt=FMT_E4M3)
