@@ -23,7 +23,7 @@ c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 
 class QdqPolicy(ctypes.Structure):
     _fields_ = [('state_fmt', c_i32), ('w_fmt', c_i32), ('block_v', c_i32), ('chunk_size', c_i32),
-                ('solve_degree', c_i32)]
+                ('solve_degree', c_i32), ('read_fmt', c_i32)]
 
 
 class FwdArgs(ctypes.Structure):
@@ -36,8 +36,8 @@ class FwdArgs(ctypes.Structure):
 
 class SavedLayout(ctypes.Structure):
     _fields_ = [('num_slots', c_i64), ('off_state', c_i64), ('off_state_scale', c_i64),
-                ('off_w', c_i64), ('off_w_scale', c_i64), ('off_x', c_i64), ('off_meta', c_i64),
-                ('total_bytes', c_i64)]
+                ('off_w', c_i64), ('off_w_scale', c_i64), ('off_x', c_i64), ('off_anchor', c_i64),
+                ('off_meta', c_i64), ('total_bytes', c_i64)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -114,7 +114,7 @@ def _stream(device):
 
 
 def make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v,
-                  o=None, ht=None, saved=None, num_seqs=None, solve_degree=0):
+                  o=None, ht=None, saved=None, num_seqs=None, solve_degree=0, read_fmt=0):
     """Fill the forward argument struct from tensor shapes and pointers."""
     B, T, Hqk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
@@ -123,7 +123,7 @@ def make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, blo
     io = GDN_F32 if q.dtype == torch.float32 else GDN_BF16
     a = FwdArgs(B=B, T=T, Hqk=Hqk, Hv=Hv, Dk=Dk, Dv=Dv, num_seqs=num_seqs, io_dtype=io,
                 scale=float(1.0 / math.sqrt(Dk) if scale is None else scale),
-                policy=QdqPolicy(state_fmt, w_fmt, block_v, 64, solve_degree))
+                policy=QdqPolicy(state_fmt, w_fmt, block_v, 64, solve_degree, read_fmt))
     for name, t in (('q', q), ('k', k), ('v', v), ('g', g), ('beta', beta), ('h0', h0),
                     ('cu_seqlens', cu_seqlens), ('o', o), ('ht', ht), ('saved', saved)):
         setattr(a, name, _ptr(t))
@@ -138,13 +138,14 @@ def saved_layout(args):
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_fmt=QDQ_OFF,
                   w_fmt=QDQ_OFF, block_v=64, output_final_state=True, save_for_backward=False,
-                  solve_degree=0):
+                  solve_degree=0, read_fmt=QDQ_OFF):
     """Chunked forward on q's device and torch's current stream.
 
     q, k [B, T, Hqk, Dk], v [B, T, Hv, Dv] (bf16, or FP32 with Dk = 64);
     g, beta [B, T, Hv] FP32; h0 [N, Hv, Dk, Dv] FP32 or None; cu_seqlens int32
     [N + 1] (B = 1) or None. solve_degree: 0 for the exact solve, or a
-    Neumann degree 1, 3, 7, 15, 31, 63 (bf16 inputs, forward only).
+    Neumann degree 1, 3, 7, 15, 31, 63 (bf16 inputs). read_fmt: QDQ_E4M3 for
+    the two-precision profile (FP32 carry, E4M3 read copy; state_fmt off).
     Returns (o, ht or None, saved uint8 buffer or None).
     """
     lib = load_library()
@@ -155,7 +156,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
     o = torch.empty(B, T, Hv, Dv, dtype=q.dtype, device=dev)
     ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev) if output_final_state else None
     a = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v, o, ht,
-                      solve_degree=solve_degree)
+                      solve_degree=solve_degree, read_fmt=read_fmt)
     saved = None
     if save_for_backward:
         nbytes = lib.gdn_saved_bytes(ctypes.byref(a))
@@ -164,7 +165,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None, state_
         saved = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         # the policy travels with the buffer, so the backward cannot pick another
         saved.gdn_policy = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v,
-                                solve_degree=solve_degree)
+                                solve_degree=solve_degree, read_fmt=read_fmt)
         a.saved = _ptr(saved)
     wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
     ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
@@ -206,7 +207,7 @@ class FwdPlan:
     stream: plan.prep(); plan.state(). Outputs: plan.o, plan.ht."""
 
     def __init__(self, q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None,
-                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0):
+                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0, read_fmt=QDQ_OFF):
         lib = load_library()
         dev = q.device
         B, T, Hqk, Dk = q.shape
@@ -216,7 +217,8 @@ class FwdPlan:
         self.ht = torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev)
         self._keep = (q, k, v, g, beta, h0, cu_seqlens)
         self.args = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt,
-                                  block_v, self.o, self.ht, solve_degree=solve_degree)
+                                  block_v, self.o, self.ht, solve_degree=solve_degree,
+                                  read_fmt=read_fmt)
         wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(self.args))
         self.ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
         self.args.workspace = _ptr(self.ws)
@@ -231,12 +233,14 @@ class FwdPlan:
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu_seqlens=None,
-                  state_fmt=None, w_fmt=None, block_v=None, grad_dtype=None, solve_degree=None):
+                  state_fmt=None, w_fmt=None, block_v=None, grad_dtype=None, solve_degree=None,
+                  read_fmt=None):
     """Backward of gdn_chunk_fwd (identity straight-through at both QDQ sites)
     from the forward's `saved` buffer. Returns dict dq, dk, dv, dg, dbeta, dh0.
     Policy arguments left as None are taken from the policy the forward
     attached to `saved`; one that is given must equal it."""
-    pol = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v, solve_degree=solve_degree)
+    pol = dict(state_fmt=state_fmt, w_fmt=w_fmt, block_v=block_v, solve_degree=solve_degree,
+               read_fmt=read_fmt)
     fwd_pol = getattr(saved, 'gdn_policy', None)
     for key, val in pol.items():
         if fwd_pol is not None:
@@ -246,9 +250,10 @@ def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu
                 raise ValueError(f'{key}={val} differs from the forward that wrote `saved` '
                                  f'({key}={fwd_pol[key]})')
         elif val is None:
-            pol[key] = dict(state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0)[key]
-    state_fmt, w_fmt, block_v, solve_degree = (pol[k_] for k_ in ('state_fmt', 'w_fmt', 'block_v',
-                                                                 'solve_degree'))
+            pol[key] = dict(state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0,
+                            read_fmt=QDQ_OFF)[key]
+    state_fmt, w_fmt, block_v, solve_degree, read_fmt = (
+        pol[k_] for k_ in ('state_fmt', 'w_fmt', 'block_v', 'solve_degree', 'read_fmt'))
     lib = load_library()
     dev = q.device
     B, T, Hqk, Dk = q.shape
@@ -263,7 +268,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, saved, do, dht=None, scale=None, h0=None, cu
                dh0=torch.empty(N, Hv, Dk, Dv, dtype=torch.float32, device=dev)
                if h0 is not None else None)
     fa = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt, block_v,
-                       saved=saved, solve_degree=solve_degree)
+                       saved=saved, solve_degree=solve_degree, read_fmt=read_fmt)
     a = BwdArgs(fwd=fa, do_=_ptr(do), dht=_ptr(dht),
                 grad_dtype=GDN_F32 if gd == torch.float32 else GDN_BF16,
                 dq=_ptr(out['dq']), dk=_ptr(out['dk']), dv=_ptr(out['dv']), dg=_ptr(out['dg']),

@@ -93,6 +93,9 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
   if (!valid_fmt(p.state_fmt) || !valid_fmt(p.w_fmt))
     return fail(GDN_E_UNSUPPORTED, "unknown QDQ format (state %d, w %d): use 0 off, 1 E4M3, 2 INT8",
                 p.state_fmt, p.w_fmt);
+  if (p.read_fmt != GDN_QDQ_OFF && p.read_fmt != GDN_QDQ_E4M3)
+    return fail(GDN_E_UNSUPPORTED, "read_fmt %d: the two-precision read copy is E4M3 (1) or off (0)",
+                p.read_fmt);
   if (a->B < 0 || a->T < 0 || a->Hqk <= 0 || a->Hv <= 0)
     return fail(GDN_E_INVALID, "bad sizes B=%d T=%d Hqk=%d Hv=%d", a->B, a->T, a->Hqk, a->Hv);
   if (a->Hv % a->Hqk != 0)
@@ -108,6 +111,14 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
     return fail(GDN_E_UNSUPPORTED, "FP32 inputs are built for Dk = 64 only (got %d)", a->Dk);
   if (a->io_dtype == GDN_F32 && p.solve_degree != 0)
     return fail(GDN_E_UNSUPPORTED, "the Neumann solve is built for bf16 inputs only");
+  if (p.read_fmt != GDN_QDQ_OFF) {
+    if (p.state_fmt != GDN_QDQ_OFF)
+      return fail(GDN_E_INVALID, "read_fmt: the two-precision read copy replaces the state "
+                                 "quantizer (state_fmt must be 0)");
+    if (a->Dk != 128 || a->io_dtype != GDN_BF16)
+      return fail(GDN_E_UNSUPPORTED, "read_fmt: the two-precision profile is built for Dk = 128 "
+                                     "and bf16 inputs (Dk %d)", a->Dk);
+  }
   if (p.state_fmt != GDN_QDQ_OFF) {
     if (p.block_v != 16 && p.block_v != 32 && p.block_v != 64 && p.block_v != 128 &&
         p.block_v != 256)
@@ -165,6 +176,8 @@ gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
   off = round256(off + (wq ? L.num_slots * a->Hv * 4 : 0));
   L.off_x = off;
   off = round256(off + (a->io_dtype == GDN_BF16 ? L.num_slots * a->Hv * 64 * 64 * 4 : 0));
+  L.off_anchor = off;
+  off = round256(off + (a->policy.read_fmt != GDN_QDQ_OFF ? L.num_slots * per_state * 4 : 0));
   L.off_meta = off;
   off = round256(off + 64);
   L.total_bytes = off;
@@ -223,6 +236,7 @@ gdn::FwdKernelArgs kernel_args(const gdn_fwd_args* a, void* saved) {
       k.w_scale = reinterpret_cast<float*>(base + L.off_w_scale);
     }
     if (a->io_dtype == GDN_BF16) k.s_X = reinterpret_cast<float*>(base + L.off_x);
+    if (a->policy.read_fmt != GDN_QDQ_OFF) k.s_anchor = reinterpret_cast<float*>(base + L.off_anchor);
     k.s_meta = reinterpret_cast<uint32_t*>(base + L.off_meta);
   }
   k.err = err_word();
@@ -245,6 +259,7 @@ gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
   c.w_fmt = a->policy.w_fmt;
   c.f32_io = a->io_dtype == GDN_F32;
   c.block_v = a->policy.state_fmt != GDN_QDQ_OFF ? a->policy.block_v : 64;
+  c.read_fmt = a->policy.read_fmt;
   return c;
 }
 
@@ -290,7 +305,7 @@ gdn::SavedStamp stamp_of(const gdn_fwd_args* a) {
                         (uint32_t)(p.state_fmt != GDN_QDQ_OFF ? p.block_v : 0),
                         (uint32_t)p.solve_degree, (uint32_t)a->B, (uint32_t)a->T,
                         (uint32_t)a->Hqk, (uint32_t)a->Hv, (uint32_t)a->Dk, (uint32_t)a->Dv,
-                        (uint32_t)a->num_seqs, (uint32_t)a->io_dtype};
+                        (uint32_t)a->num_seqs, (uint32_t)a->io_dtype, (uint32_t)p.read_fmt};
   static_assert(sizeof(w) / sizeof(w[0]) <= 15, "stamp words");
   for (size_t i = 0; i < sizeof(w) / sizeof(w[0]); ++i) st.w[i] = w[i];
   uint32_t sb;
@@ -491,6 +506,10 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   const hipStream_t st = static_cast<hipStream_t>(stream);
   s = hip_status(gdn::launch_bwd(c, k, st), "gdn_chunk_bwd launch");
   if (s != GDN_OK) return s;
+  if (a->fwd.policy.read_fmt != GDN_QDQ_OFF) {
+    s = hip_status(gdn::launch_bwd_read_anchor(c, k, st), "gdn_chunk_bwd anchor term");
+    if (s != GDN_OK) return s;
+  }
   // the saved buffer must come from a forward with this policy and shape
   const int64_t n_dqk = tokens * a->fwd.Hqk * a->fwd.Dk, n_dv = tokens * a->fwd.Hv * a->fwd.Dv;
   const int64_t n_h0 = (int64_t)a->fwd.num_seqs * a->fwd.Hv * a->fwd.Dk * a->fwd.Dv;

@@ -404,6 +404,51 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   }
 }
 
+// ----------------------------------------------------------- bwd_read_anchor
+// Two-precision profile ("[5/8] ReplaySSM state QAT and two-precision GDN",
+// "What does this PR do?"): the chunk's carry is exp(gamma_n) S with the FP32
+// state S, while its reads use Sr. The other kernels take the saved Sr as the
+// chunk's state (s_f32), which is right for every product and for the
+// identity straight-through gradient of the reads, but gives the gate term of
+// the carry as exp(gamma_n) <dS', Sr>. This kernel adds the rest,
+// exp(gamma_n) <dS', S - Sr>, to d gamma_n, that is to dg of every token of
+// the chunk (dg is the chunk-local suffix sum of d gamma). dS' (the gradient
+// of the state after the chunk) is read in the reverse recurrence's fragment
+// order; the sum is in a fixed order.
+__global__ void __launch_bounds__(NT) bwd_read_anchor(BwdKernelArgs a, int N, int DK) {
+  __shared__ float red[NT / 64];
+  const int wave = threadIdx.x >> 6, lane = __lane_id(), tid = threadIdx.x;
+  const int slot = blockIdx.x, h = blockIdx.y;
+  const FwdKernelArgs& f = a.f;
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  if (!ch.valid) return;
+  const int Hv = f.Hv, Dv = f.Dv, MT = DK / 16;
+  const int64_t chb = (int64_t)slot * Hv + h, n = (int64_t)DK * Dv;
+  const float* dSp = a.ws_dstate + chb * n;          // fragment order (frag_off)
+  const float* Sa = f.s_anchor + chb * n;            // row-major
+  const float* Sr = f.s_f32 + chb * n;
+  float acc = 0.f;
+  for (int64_t e = tid; e < n; e += NT) {
+    const int i = (int)(e & 3), ln = (int)((e >> 2) & 63);
+    const int64_t rest = e >> 8;
+    const int mt = (int)(rest % MT), w = (int)((rest / MT) & 3), vb = (int)(rest / MT / 4);
+    const int row = 16 * mt + 4 * (ln >> 4) + i, col = 64 * vb + 16 * w + (ln & 15);
+    const int64_t rc = (int64_t)row * Dv + col;
+    acc += dSp[e] * (Sa[rc] - Sr[rc]);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+    const float gv = lane < ch.nc ? f.g[(int64_t)(ch.t0 + lane) * Hv + h] : 0.f;
+    const float add = expf(wave_sum(gv)) * tot;
+    if (lane < ch.nc) a.dg[(int64_t)(ch.t0 + lane) * Hv + h] += add;
+  }
+}
+
 // ---------------------------------------------------------------- bwd_dstate
 template <int DK, bool F32IN>
 __global__ void __launch_bounds__(NT, 1) bwd_dstate(BwdKernelArgs a) {
@@ -856,6 +901,11 @@ __global__ void bwd_group(BwdKernelArgs a, int G) {
 }
 
 }  // namespace
+
+hipError_t launch_bwd_read_anchor(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_read_anchor, dim3(a.num_slots, c.Hv), dim3(NT), 0, s, a, c.N, c.Dk);
+  return hipGetLastError();
+}
 
 template <int DK, bool F32IN>
 static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {

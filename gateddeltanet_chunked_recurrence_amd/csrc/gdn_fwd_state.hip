@@ -107,8 +107,15 @@ struct Stager {
   }
 };
 
-template <int DK, int SF, int WF, int NWV>
+// RF: the two-precision profile ("[5/8] ReplaySSM state QAT and two-precision
+// GDN", "What does this PR do?"; SF = 0): the state S is carried in FP32 and
+// only its reads (W S and Q S) use a dynamic E4M3 copy with one scale per
+// value column over the Dk key channels. For the backward, the read copy of
+// each chunk's incoming state (codes times scales, FP32) goes to s_f32 and the
+// FP32 state itself to s_anchor.
+template <int DK, int SF, int WF, int NWV, bool RF>
 __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a, int N, int num_heads) {
+  static_assert(!RF || (SF == 0 && NWV == 4), "the read copy replaces the state quantizer");
   constexpr int NW = WF == 0 ? 2 : 1;
   using C = StateCfg<DK, NW, NWV>;
   using I = Img<DK>;
@@ -257,7 +264,7 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
         }
       }
       if (sb && wave == g0 && lane == 0) a.s_scale[ch * (Dv / a.block_v) + wcol / a.block_v] = dS;
-    } else if (a.s_f32) {
+    } else if (!RF && a.s_f32) {
       float* sb = a.s_f32 + ch * DK * Dv + wcol + r16;
 #pragma unroll
       for (int mt = 0; mt < MK; ++mt)
@@ -265,10 +272,48 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
         for (int i = 0; i < 4; ++i) sb[(int64_t)(16 * mt + 4 * grp + i) * Dv] = S[mt][i];
     }
     bf16x8 bSh[MK / 2], bSl[MK / 2];
+    float dR = 1.f;                                // this lane's column scale of the read copy
+    if constexpr (RF) {
+      // the column's maximum: 32 values in this lane, then the four lanes
+      // (one per lane group) that hold the same column
+      float m = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < MK / 2; ++kk) {
-      if constexpr (SF != 0) bSh[kk] = pack_pair(S[2 * kk], S[2 * kk + 1]);
-      else pack_pair_split(S[2 * kk], S[2 * kk + 1], bSh[kk], bSl[kk]);
+      for (int mt = 0; mt < MK; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[mt][i]));
+      m = fmaxf(m, __shfl_xor(m, 16, WAVE));
+      m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+      dR = qdq_scale<1>(m);
+      const float rR = 1.0f / dR;
+      float* sr = a.s_f32 ? a.s_f32 + ch * DK * Dv + wcol + r16 : nullptr;
+      float* sa = a.s_anchor ? a.s_anchor + ch * DK * Dv + wcol + r16 : nullptr;
+#pragma unroll
+      for (int kk = 0; kk < MK / 2; ++kk) {
+        f32x4 c2[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int mt = 2 * kk + h2;
+          const float x[4] = {S[mt][0], S[mt][1], S[mt][2], S[mt][3]};
+          float cq[4];
+          uint32_t bytes;
+          quant4<1>(x, rR, cq, bytes);
+          c2[h2] = f32x4{cq[0], cq[1], cq[2], cq[3]};
+          if (sr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sr[(int64_t)(16 * mt + 4 * grp + i) * Dv] = cq[i] * dR;
+              sa[(int64_t)(16 * mt + 4 * grp + i) * Dv] = x[i];
+            }
+          }
+        }
+        bSh[kk] = pack_pair(c2[0], c2[1]);         // codes, exact in bf16
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < MK / 2; ++kk) {
+        if constexpr (SF != 0) bSh[kk] = pack_pair(S[2 * kk], S[2 * kk + 1]);
+        else pack_pair_split(S[2 * kk], S[2 * kk + 1], bSh[kk], bSl[kk]);
+      }
     }
 
     stage_part(1);
@@ -299,7 +344,7 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
           accw[mt] = mfma(w[0], bSh[kk], accw[mt]);
           accq[mt] = mfma(q, bSh[kk], accq[mt]);
           if constexpr (NW == 2) accw[mt] = mfma(w[NW - 1], bSh[kk], accw[mt]);
-          if constexpr (SF == 0) {
+          if constexpr (SF == 0 && !RF) {
             accw[mt] = mfma(w[0], bSl[kk], accw[mt]);
             accq[mt] = mfma(q, bSl[kk], accq[mt]);
           }
@@ -308,13 +353,13 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
     }
     f32x4 Vn[4];
     {
-      const float sc = dWcur * dS;
+      const float sc = dWcur * dS * dR;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           Vn[mt][i] = Ucur[mt][i] - sc * accw[mt][i];
-          accq[mt][i] *= dS * egr[mt][i];
+          accq[mt][i] *= dS * dR * egr[mt][i];
         }
     }
     // Vnew and exp(gamma_n - gamma) Vnew as B operands (paired order over tokens)
@@ -425,12 +470,12 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
 
 }  // namespace
 
-template <int DK, int SF, int WF, int NWV>
+template <int DK, int SF, int WF, int NWV, bool RF = false>
 static hipError_t launch_state_w(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
   const int num_heads = cfg.N * cfg.Hv, nwb = cfg.Dv / (16 * NWV);
   const int64_t nblk = (int64_t)nwb * 8 * ((num_heads + 7) / 8);
-  hipLaunchKernelGGL((gdn_state_kernel<DK, SF, WF, NWV>), dim3((unsigned)nblk), dim3(64 * NWV), 0, s,
-                     a, cfg.N, num_heads);
+  hipLaunchKernelGGL((gdn_state_kernel<DK, SF, WF, NWV, RF>), dim3((unsigned)nblk), dim3(64 * NWV), 0,
+                     s, a, cfg.N, num_heads);
   return hipGetLastError();
 }
 
@@ -440,6 +485,11 @@ static hipError_t launch_state_one(const FwdConfig& cfg, const FwdKernelArgs& a,
   if constexpr (SF != 0) {
     if (cfg.block_v == 256) return launch_state_w<DK, SF, WF, 16>(cfg, a, s);
     if (cfg.block_v == 128) return launch_state_w<DK, SF, WF, 8>(cfg, a, s);
+  } else {
+    if (cfg.read_fmt != 0) {
+      if constexpr (DK == 128) return launch_state_w<DK, SF, WF, 4, true>(cfg, a, s);
+      return hipErrorInvalidValue;                 // the read copy is built for Dk = 128
+    }
   }
   return launch_state_w<DK, SF, WF, 4>(cfg, a, s);
 }

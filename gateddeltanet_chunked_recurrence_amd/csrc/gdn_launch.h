@@ -23,6 +23,7 @@ struct FwdKernelArgs {
   float* w_scale;             // saved W scales, nullable
   float* s_X;                 // saved X = (I + L)^-1 per chunk (bf16 io), nullable
   uint32_t* s_meta;           // saved policy stamp (SavedStamp words), nullable
+  float* s_anchor;            // saved FP32 state of each chunk (two-precision profile), nullable
   uint32_t* err;              // sticky device error flags (kErr* bits), never NULL
   // forward workspace (bf16 io): operand images written by the prep kernel
   __bf16* ws_img;             // [slots * Hv][W planes | K^T | P] (gdn_images.h)
@@ -50,6 +51,7 @@ struct SavedStamp {
 struct FwdConfig {
   int Dk, Dv, N, Hv, state_fmt, w_fmt, f32_io;
   int block_v;                // state scale tile width (state QDQ on)
+  int read_fmt;               // two-precision read copy format (0 off, 1 E4M3)
 };
 
 // FP32 io (Dk = 64): one fused kernel per (sequence, head, value block).
@@ -100,6 +102,11 @@ hipError_t launch_bwd_state(const BwdConfig& cfg, const BwdKernelArgs& a, hipStr
 hipError_t launch_bwd_local(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
 // Elements of the backward image block of one (slot, head).
 int bwd_img_elems(int Dk, int w_fmt);
+
+// Two-precision profile backward: dg += exp(gamma_n) <dS', S - Sr> over each
+// chunk (the FP32 carry's gate term, which the backward's products took with
+// the read copy Sr).
+hipError_t launch_bwd_read_anchor(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t s);
 
 // Writes the stamp into the saved buffer's meta section.
 hipError_t launch_write_stamp(uint32_t* meta, const SavedStamp& st, hipStream_t s);

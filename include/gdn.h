@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
   GDN_OK = 0,
@@ -88,6 +88,17 @@ typedef struct {
                           polynomial, not the inverse, and gdn_chunk_bwd
                           differentiates the polynomial itself: dL =
                           -sum_{m=1..d} sum_{a+b=m-1} (-L^T)^a dX (-L^T)^b. */
+  int32_t read_fmt;    /* two-precision profile ("[5/8] ReplaySSM state QAT and
+                          two-precision GDN", "What does this PR do?" and
+                          "Usage"): GDN_QDQ_E4M3 keeps the state in FP32 (the
+                          recurrence anchor, never quantized) and gives every
+                          read of a chunk's incoming state, Vnew = U - Wq Sr
+                          and O's Q Sr, a dynamic E4M3 copy Sr with one scale
+                          per value column over the Dk key channels. Needs
+                          state_fmt == OFF (GDN_E_INVALID otherwise), Dk == 128
+                          and bf16 inputs (GDN_E_UNSUPPORTED otherwise; the
+                          pages enable it for K = 128 only). INT8 reads are
+                          GDN_E_UNSUPPORTED. GDN_QDQ_OFF (0): no read copy.  */
 } gdn_qdq_policy;
 
 /* Forward arguments. Shapes: without cu_seqlens there are N = B sequences of
@@ -132,6 +143,9 @@ typedef struct {
  *           the WY form's unit lower triangular matrix, FP32 row-major
  *           [num_slots, Hv, 64, 64]; the backward reads it instead of solving
  *           again. 0 bytes for FP32 inputs.
+ *   anchor: read_fmt != OFF only: the FP32 state of every chunk before its
+ *           reads, [num_slots, Hv, Dk, Dv]; the state section then holds the
+ *           read copy Sr (FP32 values of codes times column scales).
  *   meta:   64 bytes: the policy (formats, block_v, solve_degree), shape and
  *           scale the forward ran under. gdn_chunk_bwd compares it with its
  *           own arguments on the device; on any difference every gradient
@@ -143,7 +157,7 @@ typedef struct {
  * Slots no chunk uses are left unwritten. */
 typedef struct {
   int64_t num_slots;
-  int64_t off_state, off_state_scale, off_w, off_w_scale, off_x, off_meta;
+  int64_t off_state, off_state_scale, off_w, off_w_scale, off_x, off_anchor, off_meta;
   int64_t total_bytes;
 } gdn_saved_layout_t;
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 5
+    assert lib.gdn_abi_version() == 6
 
 
 def _args(**kw):
@@ -36,7 +36,7 @@ def _args(**kw):
     for name in ('q', 'k', 'v', 'g', 'beta', 'o'):
         setattr(a, name, fake)
     for k, v in kw.items():
-        if k in ('state_fmt', 'w_fmt', 'block_v', 'chunk_size', 'solve_degree'):
+        if k in ('state_fmt', 'w_fmt', 'block_v', 'chunk_size', 'solve_degree', 'read_fmt'):
             setattr(a.policy, k, v)
         else:
             setattr(a, k, v)
@@ -69,6 +69,12 @@ BAD = [
     (dict(solve_degree=127), B.GDN_E_UNSUPPORTED, 'solve_degree'),
     (dict(solve_degree=-1), B.GDN_E_UNSUPPORTED, 'solve_degree'),
     (dict(solve_degree=3, io_dtype=1, Dk=64), B.GDN_E_UNSUPPORTED, 'Neumann'),
+    # the two-precision read copy: E4M3 or off, never with a quantized carry,
+    # built for Dk = 128 and bf16 inputs
+    (dict(read_fmt=2, state_fmt=0), B.GDN_E_UNSUPPORTED, 'read_fmt'),
+    (dict(read_fmt=5, state_fmt=0), B.GDN_E_UNSUPPORTED, 'read_fmt'),
+    (dict(read_fmt=1), B.GDN_E_INVALID, 'replaces the state'),
+    (dict(read_fmt=1, state_fmt=0, Dk=64), B.GDN_E_UNSUPPORTED, 'Dk = 128'),
 ]
 
 
