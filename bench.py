@@ -82,7 +82,22 @@ KERNEL_SOURCES = {
     'gdn_state_split_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h',
                                'gdn_fwd_state_split.hip'),
     'gdn_prep_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_fwd_prep.hip'),
+    'gdn_state_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_fwd_state.hip'),
+    'gdn_fwd_kernel': ('gdn_device.h', 'gdn_launch.h', 'gdn_fwd.hip'),
+    'bwd_img_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_bwd_state.hip'),
+    'bwd_state_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_bwd_state.hip'),
+    'bwd_local_kernel': ('gdn_device.h', 'gdn_images.h', 'gdn_launch.h', 'gdn_bwd_local.hip'),
 }
+BWD_KERNELS = ('bwd_img_kernel', 'bwd_state_kernel', 'bwd_local_kernel')
+FWD_KERNELS = ('gdn_state_split_kernel', 'gdn_prep_kernel', 'gdn_state_kernel', 'gdn_fwd_kernel')
+
+
+def state_kernel_of(spec):
+    """The kernel that runs the state stage of a forward workload."""
+    if spec['dtype'] == 'f32':
+        return 'gdn_fwd_kernel'
+    split = spec['state_fmt'] != 0 and spec['w_fmt'] != 0 and spec['block_v'] <= 64
+    return 'gdn_state_split_kernel' if split else 'gdn_state_kernel'
 
 
 def source_hash(kernel):
@@ -255,7 +270,7 @@ def time_fwd_bwd(steps, warmup, flush):
     tot = f['median'] + b['median']
     ach = fl / (tot * 1e-3) / 1e12
     return dict(workload=name, fwd_ms=f, bwd_ms=b, tokens_per_s=tokens / (tot * 1e-3),
-                steps=steps,
+                steps=steps, bwd_bytes_counted={k: measured_traffic(k, name) for k in BWD_KERNELS},
                 roofline_path=dict(bound='mfma', achieved=ach, peak=PEAK_BF16_TFLOPS,
                                    unit='TFLOP/s', frac=ach / PEAK_BF16_TFLOPS))
 
@@ -325,8 +340,7 @@ def main():
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device='cuda')
     spec = gdn_inputs.spec(args.workload)
     t = time_fwd(spec, 2, args.steps, args.warmup, flush)
-    split = spec['state_fmt'] != 0 and spec['w_fmt'] != 0 and spec['block_v'] <= 64
-    head = fwd_record(args.workload, spec, t, 'gdn_state_split_kernel' if split else 'gdn_state_kernel')
+    head = fwd_record(args.workload, spec, t, state_kernel_of(spec))
     ms = t['total']['median']
     tokens = spec_tokens(spec)
     out = dict(
@@ -334,8 +348,9 @@ def main():
         steps=args.steps, warmup=args.warmup, ms_per_step=ms,
         ms_per_step_p10=t['total']['p10'], ms_per_step_p90=t['total']['p90'],
         higher_is_better=True, scaling='weak', vs_baseline=None, dtype='bf16', data='synthetic',
-        config=dict(workload=args.workload, B=spec['B'], T=spec['T'], Hqk=spec['Hqk'],
-                    Hv=spec['Hv'], Dk=spec['Dk'], Dv=spec['Dv'], chunk=CHUNK,
+        config=dict(workload=args.workload, B=spec['B'],
+                    **({'lengths': spec['lengths']} if 'lengths' in spec else {'T': spec['T']}),
+                    Hqk=spec['Hqk'], Hv=spec['Hv'], Dk=spec['Dk'], Dv=spec['Dv'], chunk=CHUNK,
                     state_qdq=['off', 'e4m3', 'int8'][spec['state_fmt']],
                     w_qdq=['off', 'e4m3', 'int8'][spec['w_fmt']], block_v=spec['block_v'],
                     parallelism='1gpu'),
@@ -344,7 +359,8 @@ def main():
         hbm_gbs_algorithmic=head['hbm_gbs_algorithmic'],
         whole_forward_traffic=dict(
             bytes_algorithmic=bytes_algorithmic(spec),
-            bytes_counted={k: measured_traffic(k, args.workload) for k in KERNEL_SOURCES}),
+            bytes_counted={k: measured_traffic(k, args.workload) for k in FWD_KERNELS
+                           if k in ('gdn_prep_kernel', state_kernel_of(spec))}),
         protocol=dict(flush_bytes_between_steps=FLUSH_BYTES, stat='median over steps',
                       timed_wall_s=t['wall_s']),
         source_hash={k: source_hash(k) for k in KERNEL_SOURCES})
@@ -353,10 +369,7 @@ def main():
         for name, steps in (('tiny_fp32', 20), ('varlen_int8_gqa4x16_d128', 20),
                             ('long_e4m3_t65536_h32_dk128_dv256', 5)):
             s = gdn_inputs.spec(name)
-            sp = s['state_fmt'] != 0 and s['w_fmt'] != 0 and s['block_v'] <= 64
-            kern = 'gdn_fwd_kernel' if s['dtype'] == 'f32' else (
-                'gdn_state_split_kernel' if sp else 'gdn_state_kernel')
-            cfgs[name] = fwd_record(name, s, time_fwd(s, 2, steps, 2, flush), kern)
+            cfgs[name] = fwd_record(name, s, time_fwd(s, 2, steps, 2, flush), state_kernel_of(s))
             torch.cuda.empty_cache()
         out['configs'] = cfgs
     if not args.no_bwd:
