@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, 'libgdn_hip.so')
 BUILD_DIR = os.path.join(os.path.dirname(HERE), '_build')
 SOURCES = ['gdn_abi.cpp', 'gdn_qdq.hip', 'gdn_guard.hip', 'gdn_fwd.hip', 'gdn_fwd_prep.hip',
            'gdn_fwd_state.hip', 'gdn_fwd_state_split.hip', 'gdn_bwd.hip',
-           'gdn_bwd_state.hip', 'gdn_bwd_local.hip']
+           'gdn_bwd_state.hip', 'gdn_bwd_local.hip', 'gdn_decode.hip']
 HIPCC = os.environ.get('HIPCC', '/opt/rocm/bin/hipcc')
 
 COMMON = ['-std=c++17', '-O3', '-fPIC', '--offload-arch=gfx950',

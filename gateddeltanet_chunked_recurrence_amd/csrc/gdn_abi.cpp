@@ -130,6 +130,7 @@ gdn_status check_fwd_shape(const gdn_fwd_args* a) {
                   p.block_v);
   }
   if (!std::isfinite(a->scale)) return fail(GDN_E_INVALID, "scale is not finite");
+  if (a->prefix_len < 0) return fail(GDN_E_INVALID, "prefix_len %d < 0", a->prefix_len);
   if (a->cu_seqlens) {
     if (a->B != 1) return fail(GDN_E_INVALID, "cu_seqlens needs B == 1 (got %d)", a->B);
     if (a->num_seqs < 1) return fail(GDN_E_INVALID, "num_seqs %d < 1 with cu_seqlens", a->num_seqs);
@@ -241,6 +242,7 @@ gdn::FwdKernelArgs kernel_args(const gdn_fwd_args* a, void* saved) {
   }
   k.err = err_word();
   k.T = a->T;
+  k.prefix_len = a->prefix_len;
   k.Hqk = a->Hqk;
   k.Hv = a->Hv;
   k.Dv = a->Dv;
@@ -300,12 +302,12 @@ BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
 gdn::SavedStamp stamp_of(const gdn_fwd_args* a) {
   gdn::SavedStamp st{};
   const gdn_qdq_policy& p = a->policy;
-  const uint32_t w[] = {gdn::SavedStamp::kMagic, (uint32_t)GDN_ABI_VERSION, (uint32_t)p.state_fmt,
-                        (uint32_t)p.w_fmt,
+  const uint32_t fmts = (uint32_t)p.state_fmt | (uint32_t)p.w_fmt << 8 | (uint32_t)p.read_fmt << 16;
+  const uint32_t w[] = {gdn::SavedStamp::kMagic, (uint32_t)GDN_ABI_VERSION, fmts,
                         (uint32_t)(p.state_fmt != GDN_QDQ_OFF ? p.block_v : 0),
                         (uint32_t)p.solve_degree, (uint32_t)a->B, (uint32_t)a->T,
                         (uint32_t)a->Hqk, (uint32_t)a->Hv, (uint32_t)a->Dk, (uint32_t)a->Dv,
-                        (uint32_t)a->num_seqs, (uint32_t)a->io_dtype, (uint32_t)p.read_fmt};
+                        (uint32_t)a->num_seqs, (uint32_t)a->io_dtype, (uint32_t)a->prefix_len};
   static_assert(sizeof(w) / sizeof(w[0]) <= 15, "stamp words");
   for (size_t i = 0; i < sizeof(w) / sizeof(w[0]); ++i) st.w[i] = w[i];
   uint32_t sb;
@@ -419,6 +421,140 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages, boo
   return GDN_OK;
 }
 
+// ------------------------------------------------------------------ decode
+gdn_status check_decode(const gdn_decode_args* a) {
+  if (!a) return fail(GDN_E_INVALID, "argument struct is NULL");
+  if (a->B < 0 || a->T < 0 || a->Hqk <= 0 || a->Hv <= 0)
+    return fail(GDN_E_INVALID, "bad sizes B=%d T=%d Hqk=%d Hv=%d", a->B, a->T, a->Hqk, a->Hv);
+  if (a->Hv % a->Hqk != 0)
+    return fail(GDN_E_INVALID, "Hv (%d) must be a multiple of Hqk (%d)", a->Hv, a->Hqk);
+  if (a->Dk != 64 && a->Dk != 128) return fail(GDN_E_UNSUPPORTED, "Dk %d: supported 64, 128", a->Dk);
+  if (a->Dv != 64 && a->Dv != 128 && a->Dv != 256)
+    return fail(GDN_E_UNSUPPORTED, "Dv %d: supported 64, 128, 256", a->Dv);
+  if (a->io_dtype != GDN_BF16 && a->io_dtype != GDN_F32)
+    return fail(GDN_E_INVALID, "io_dtype %d: use 0 bf16 or 1 f32", a->io_dtype);
+  if (!valid_fmt(a->state_fmt))
+    return fail(GDN_E_UNSUPPORTED, "unknown state format %d: use 0 off, 1 E4M3, 2 INT8",
+                a->state_fmt);
+  if (a->state_fmt != GDN_QDQ_OFF) {
+    if (a->block_v != 16 && a->block_v != 32 && a->block_v != 64 && a->block_v != 128 &&
+        a->block_v != 256)
+      return fail(GDN_E_UNSUPPORTED, "block_v %d: supported 16, 32, 64, 128, 256", a->block_v);
+    if (a->Dv % a->block_v != 0)
+      return fail(GDN_E_INVALID, "block_v %d does not divide Dv %d", a->block_v, a->Dv);
+  }
+  if (a->readout != GDN_READOUT_BEFORE_WRITE && a->readout != GDN_READOUT_AFTER_WRITE)
+    return fail(GDN_E_INVALID, "readout %d: 0 before the write, 1 after it", a->readout);
+  if (a->start < 0) return fail(GDN_E_INVALID, "start %d < 0", a->start);
+  if (!std::isfinite(a->scale)) return fail(GDN_E_INVALID, "scale is not finite");
+  if (a->cu_seqlens) {
+    if (a->B != 1) return fail(GDN_E_INVALID, "cu_seqlens needs B == 1 (got %d)", a->B);
+    if (a->num_seqs < 1) return fail(GDN_E_INVALID, "num_seqs %d < 1 with cu_seqlens", a->num_seqs);
+  } else if (a->num_seqs != a->B) {
+    return fail(GDN_E_INVALID, "num_seqs (%d) must equal B (%d) without cu_seqlens",
+                a->num_seqs, a->B);
+  }
+  if ((int64_t)a->num_seqs * a->Hv > INT32_MAX)
+    return fail(GDN_E_UNSUPPORTED, "num_seqs * Hv exceeds 2^31");
+  if ((int64_t)a->B * a->T > INT32_MAX / 2)
+    return fail(GDN_E_UNSUPPORTED, "B*T = %lld tokens exceeds 2^30", (long long)a->B * a->T);
+  return GDN_OK;
+}
+
+gdn_status check_decode_ptrs(const gdn_decode_args* a, bool need_out) {
+  const bool any = (int64_t)a->B * a->T > 0;
+  const struct { const void* p; const char* name; bool required; } ptrs[] = {
+      {a->q, "q", any},          {a->k, "k", any},      {a->v, "v", any},
+      {a->g, "g", any},          {a->beta, "beta", any}, {a->o, "o", need_out && any},
+      {a->h_in, "h_in", false},  {a->ht, "ht", false},  {a->cu_seqlens, "cu_seqlens", false},
+      {a->saved, "saved", false}};
+  for (const auto& e : ptrs) {
+    if (e.required && !e.p) return fail(GDN_E_INVALID, "%s is NULL", e.name);
+    if (e.p && !aligned16(e.p)) return fail(GDN_E_INVALID, "%s is not 16-byte aligned", e.name);
+  }
+  return GDN_OK;
+}
+
+// Saved written states: codes (or FP32 states), tile scales, the stamp.
+struct DecodeLayout {
+  int64_t slots, off_state, off_scale, off_meta, total;
+};
+DecodeLayout decode_layout(const gdn_decode_args* a) {
+  DecodeLayout L{};
+  L.slots = (int64_t)a->B * a->T + a->num_seqs;
+  const int64_t per = (int64_t)a->Hv * a->Dk * a->Dv;
+  const bool sq = a->state_fmt != GDN_QDQ_OFF;
+  int64_t off = 0;
+  L.off_state = off;
+  off = round256(off + L.slots * per * (sq ? 1 : 4));
+  L.off_scale = off;
+  off = round256(off + (sq ? L.slots * a->Hv * (a->Dv / a->block_v) * 4 : 0));
+  L.off_meta = off;
+  L.total = round256(off + 64);
+  return L;
+}
+
+gdn::SavedStamp decode_stamp(const gdn_decode_args* a) {
+  gdn::SavedStamp st{};
+  const uint32_t w[] = {0x44444E47u /* "GNDD" */, (uint32_t)GDN_ABI_VERSION,
+                        (uint32_t)a->state_fmt,
+                        (uint32_t)(a->state_fmt != GDN_QDQ_OFF ? a->block_v : 0),
+                        (uint32_t)a->readout, (uint32_t)a->start, (uint32_t)a->B,
+                        (uint32_t)a->T, (uint32_t)a->Hqk, (uint32_t)a->Hv, (uint32_t)a->Dk,
+                        (uint32_t)a->Dv, (uint32_t)a->num_seqs, (uint32_t)a->io_dtype};
+  static_assert(sizeof(w) / sizeof(w[0]) <= 15, "stamp words");
+  for (size_t i = 0; i < sizeof(w) / sizeof(w[0]); ++i) st.w[i] = w[i];
+  uint32_t sb;
+  std::memcpy(&sb, &a->scale, 4);
+  st.w[15] = sb;
+  return st;
+}
+
+gdn::DecodeKernelArgs decode_kernel_args(const gdn_decode_args* a) {
+  gdn::DecodeKernelArgs k{};
+  k.q = a->q;
+  k.k = a->k;
+  k.v = a->v;
+  k.g = a->g;
+  k.beta = a->beta;
+  k.h_in = a->h_in;
+  k.cu_seqlens = a->cu_seqlens;
+  k.o = a->o;
+  k.ht = a->ht;
+  if (a->saved) {
+    const DecodeLayout L = decode_layout(a);
+    char* base = static_cast<char*>(a->saved);
+    if (a->state_fmt != GDN_QDQ_OFF) {
+      k.s_codes = reinterpret_cast<uint8_t*>(base + L.off_state);
+      k.s_scale = reinterpret_cast<float*>(base + L.off_scale);
+    } else {
+      k.s_f32 = reinterpret_cast<float*>(base + L.off_state);
+    }
+  }
+  k.T = a->T;
+  k.start = a->start;
+  k.Hqk = a->Hqk;
+  k.Hv = a->Hv;
+  k.Dv = a->Dv;
+  k.block_v = a->state_fmt != GDN_QDQ_OFF ? a->block_v : 64;
+  k.readout = a->readout;
+  k.scale = a->scale;
+  k.total_tokens = (int32_t)((int64_t)a->B * a->T);
+  return k;
+}
+
+gdn::DecodeConfig decode_config(const gdn_decode_args* a) {
+  gdn::DecodeConfig c{};
+  c.Dk = a->Dk;
+  c.Dv = a->Dv;
+  c.N = a->num_seqs;
+  c.Hv = a->Hv;
+  c.Hqk = a->Hqk;
+  c.state_fmt = a->state_fmt;
+  c.f32_io = a->io_dtype == GDN_F32;
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -516,6 +652,90 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   return hip_status(gdn::launch_check_stamp(k, stamp_of(&a->fwd), n_dqk, n_dv, tokens * a->fwd.Hv,
                                             n_h0, st),
                     "gdn_chunk_bwd stamp check");
+}
+
+size_t gdn_decode_saved_bytes(const gdn_decode_args* a) {
+  if (check_decode(a) != GDN_OK) return 0;
+  return (size_t)decode_layout(a).total;
+}
+
+gdn_status gdn_decode_fwd(const gdn_decode_args* a, void* stream) {
+  gdn_status s = check_decode(a);
+  if (s != GDN_OK) return s;
+  if ((s = check_decode_ptrs(a, true)) != GDN_OK) return s;
+  if (a->num_seqs == 0 || (int64_t)a->B * a->T + a->num_seqs == 0) return GDN_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const gdn::DecodeKernelArgs k = decode_kernel_args(a);
+  if (a->saved) {
+    s = hip_status(gdn::launch_write_stamp(reinterpret_cast<uint32_t*>(
+                                               static_cast<char*>(a->saved) + decode_layout(a).off_meta),
+                                           decode_stamp(a), st),
+                   "gdn_decode_fwd stamp");
+    if (s != GDN_OK) return s;
+  }
+  return hip_status(gdn::launch_decode_fwd(decode_config(a), k, st), "gdn_decode_fwd launch");
+}
+
+size_t gdn_decode_bwd_workspace_bytes(const gdn_decode_bwd_args* a) {
+  if (!a || check_decode(&a->fwd) != GDN_OK) return 0;
+  if (a->fwd.Hv == a->fwd.Hqk) return 0;
+  return (size_t)round256((int64_t)a->fwd.B * a->fwd.T * a->fwd.Hv * 2 * a->fwd.Dk * 4);
+}
+
+gdn_status gdn_decode_bwd(const gdn_decode_bwd_args* a, void* stream) {
+  if (!a) return fail(GDN_E_INVALID, "argument struct is NULL");
+  gdn_status s = check_decode(&a->fwd);
+  if (s != GDN_OK) return s;
+  if ((s = check_decode_ptrs(&a->fwd, false)) != GDN_OK) return s;
+  const int64_t tokens = (int64_t)a->fwd.B * a->fwd.T;
+  if (a->grad_dtype != GDN_F32 && a->grad_dtype != a->fwd.io_dtype)
+    return fail(GDN_E_INVALID, "grad_dtype must be FP32 or the io dtype");
+  const bool any = tokens > 0;
+  const struct { const void* p; const char* name; bool required; } ptrs[] = {
+      {a->fwd.saved, "saved", true}, {a->do_, "do", any},    {a->dq, "dq", any},
+      {a->dk, "dk", any},            {a->dv, "dv", any},     {a->dg, "dg", any},
+      {a->dbeta, "dbeta", any},      {a->dht, "dht", false}, {a->dh_in, "dh_in", false},
+      {a->workspace, "workspace", false}};
+  for (const auto& e : ptrs) {
+    if (e.required && !e.p) return fail(GDN_E_INVALID, "%s is NULL", e.name);
+    if (e.p && !aligned16(e.p)) return fail(GDN_E_INVALID, "%s is not 16-byte aligned", e.name);
+  }
+  const size_t need = gdn_decode_bwd_workspace_bytes(a);
+  if (need && (!a->workspace || a->workspace_bytes < need))
+    return fail(GDN_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", a->workspace_bytes, need);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  gdn::DecodeKernelArgs k = decode_kernel_args(&a->fwd);
+  k.dout = a->do_;
+  k.dht = a->dht;
+  k.dq = a->dq;
+  k.dk = a->dk;
+  k.dv = a->dv;
+  k.dg = a->dg;
+  k.dbeta = a->dbeta;
+  k.dh_in = a->dh_in;
+  k.ws_dqk = need ? static_cast<float*>(a->workspace) : nullptr;
+  k.grad_f32 = a->grad_dtype == GDN_F32;
+  uint32_t* err = err_word();
+  if (!err) return fail(GDN_E_HIP, "device error word unavailable on the current device");
+  s = hip_status(gdn::launch_decode_bwd(decode_config(&a->fwd), k, st), "gdn_decode_bwd launch");
+  if (s != GDN_OK) return s;
+  // the saved buffer must come from a decode forward with this policy and shape
+  gdn::BwdKernelArgs c{};
+  c.f.s_meta = reinterpret_cast<uint32_t*>(static_cast<char*>(a->fwd.saved) +
+                                           decode_layout(&a->fwd).off_meta);
+  c.f.err = err;
+  c.dq = a->dq;
+  c.dk = a->dk;
+  c.dv = a->dv;
+  c.dg = a->dg;
+  c.dbeta = a->dbeta;
+  c.dh0 = a->dh_in;
+  c.grad_f32 = k.grad_f32;
+  const int64_t n_h = (int64_t)a->fwd.num_seqs * a->fwd.Hv * a->fwd.Dk * a->fwd.Dv;
+  return hip_status(gdn::launch_check_stamp(c, decode_stamp(&a->fwd), tokens * a->fwd.Hqk * a->fwd.Dk,
+                                            tokens * a->fwd.Hv * a->fwd.Dv, tokens * a->fwd.Hv, n_h,
+                                            st),
+                    "gdn_decode_bwd stamp check");
 }
 
 gdn_status gdn_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,

@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_prep(BwdKernelArgs a, int N) {
   const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
   const int slot = blockIdx.x, h = blockIdx.y;
   const FwdKernelArgs& f = a.f;
-  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
   const int Hv = f.Hv, Hqk = f.Hqk, hk = h / (Hv / Hqk);
 
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
   const int slot = blockIdx.x, h = blockIdx.y;
   const FwdKernelArgs& f = a.f;
-  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
   const int Hv = f.Hv, Hqk = f.Hqk, hk = h / (Hv / Hqk), nc = ch.nc;
   const int64_t chb = (int64_t)slot * Hv + h;
@@ -420,7 +420,7 @@ __global__ void __launch_bounds__(NT) bwd_read_anchor(BwdKernelArgs a, int N, in
   const int wave = threadIdx.x >> 6, lane = __lane_id(), tid = threadIdx.x;
   const int slot = blockIdx.x, h = blockIdx.y;
   const FwdKernelArgs& f = a.f;
-  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
   const int Hv = f.Hv, Dv = f.Dv, MT = DK / 16;
   const int64_t chb = (int64_t)slot * Hv + h, n = (int64_t)DK * Dv;
@@ -462,13 +462,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_dstate(BwdKernelArgs a) {
   const int vb = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
   const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, hk = h / (Hv / Hqk);
   int bos, eos;
-  if (f.cu_seqlens) {
-    bos = f.cu_seqlens[n];
-    eos = f.cu_seqlens[n + 1];
-  } else {
-    bos = n * f.T;
-    eos = bos + f.T;
-  }
+  seq_span(f, n, bos, eos);
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
   const int col = vb * 64 + 16 * wave + r16;        // this lane's value column (dht, dh0)
   const int64_t sbase = ((int64_t)n * Hv + h) * DK * Dv;
@@ -583,7 +577,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_chunk(BwdKernelArgs a, int N) {
   const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
   const int slot = blockIdx.x, h = blockIdx.y;
   const FwdKernelArgs& f = a.f;
-  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
   const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, hk = h / (Hv / Hqk);
   const int t0 = ch.t0, nc = ch.nc;
@@ -880,10 +874,10 @@ __global__ void __launch_bounds__(NT, 1) bwd_chunk(BwdKernelArgs a, int N) {
 
 // ----------------------------------------------------------------- bwd_group
 template <int DK>
-__global__ void bwd_group(BwdKernelArgs a, int G) {
+__global__ void bwd_group(BwdKernelArgs a, int G, int N) {
   const int tok = blockIdx.x, hk = blockIdx.y, d = threadIdx.x;
   const int Hv = a.f.Hv, Hqk = a.f.Hqk;
-  if (d >= DK) return;
+  if (d >= DK || !token_in_span(a.f, N, tok)) return;
   float sq = 0.f, sk = 0.f;
   for (int j = 0; j < G; ++j) {
     const float* p = a.ws_dqk + (((int64_t)tok * Hv + hk * G + j) * 2) * DK;
@@ -940,7 +934,8 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
     }
   }
   if (!F32IN && c.Hv == c.Hqk && a.f.solve_degree == 0) return hipSuccess;   // dq, dk written directly
-  hipLaunchKernelGGL((bwd_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, s, a, c.Hv / c.Hqk);
+  hipLaunchKernelGGL((bwd_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, s, a, c.Hv / c.Hqk,
+                     c.N);
   return hipGetLastError();
 }
 

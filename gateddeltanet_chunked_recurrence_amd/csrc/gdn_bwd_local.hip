@@ -240,7 +240,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_local_kernel(BwdKernelArgs a, int N
   lane = fresh_lane(); tid = wave * 64 + lane; r16 = lane & 15; grp = lane >> 4
   const int tw = wave & 3, hk = wave >> 2;
   const int slot = blockIdx.x, h = blockIdx.y;
-  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
   const int Hv = f.Hv, Hqk = f.Hqk, Dv = f.Dv, nvb = Dv / 64, hq = h / (Hv / Hqk);
   const int t0 = ch.t0, nc = ch.nc;

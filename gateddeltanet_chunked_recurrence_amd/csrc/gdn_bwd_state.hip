@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
   const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
   const int slot = blockIdx.x, h = blockIdx.y;
-  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T);
+  const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
   const int Hv = f.Hv, Hqk = f.Hqk, Dv = DV;
   const int hk = h / (Hv / Hqk), t0 = ch.t0, nc = ch.nc;
@@ -324,13 +324,7 @@ __global__ void __launch_bounds__(64 * (WG + 1), 1) bwd_state_kernel(BwdKernelAr
   if (hidx >= num_heads) return;
   const int n = hidx / Hv, h = hidx % Hv;
   int bos, eos;
-  if (f.cu_seqlens) {
-    bos = f.cu_seqlens[n];
-    eos = f.cu_seqlens[n + 1];
-  } else {
-    bos = n * f.T;
-    eos = bos + f.T;
-  }
+  seq_span(f, n, bos, eos);
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
   const int slot0 = n + bos / CHUNK;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();

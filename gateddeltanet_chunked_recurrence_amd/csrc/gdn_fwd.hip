@@ -169,13 +169,7 @@ __global__ void __launch_bounds__(256, 1) gdn_fwd_kernel(FwdKernelArgs a) {
   const int Hv = a.Hv, Dv = a.Dv, Hqk = a.Hqk;
   const int hk = h / (Hv / Hqk);
   int bos, eos;
-  if (a.cu_seqlens) {
-    bos = a.cu_seqlens[n];
-    eos = a.cu_seqlens[n + 1];
-  } else {
-    bos = n * a.T;
-    eos = bos + a.T;
-  }
+  seq_span(a, n, bos, eos);
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
   const int slot0 = n + bos / CHUNK;
   const int wcol = vb * C::BV + wave * 16;          // first value column of this wave

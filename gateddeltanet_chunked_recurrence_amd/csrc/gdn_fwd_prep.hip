@@ -214,9 +214,10 @@ __device__ PrepItem prep_item(const FwdKernelArgs& a, int N, int i) {
   if (!a.cu_seqlens && a.T % CHUNK == 0) {
     // equal lengths: T / 64 chunk slots and one spare slot per sequence
     const int per = a.T / CHUNK + 1, n = it.slot / per, c = it.slot - n * per;
+    const int len = a.prefix_len > 0 ? min(a.T, a.prefix_len) : a.T;
     it.t0 = n * a.T + CHUNK * c;
-    it.valid = c < per - 1;
-    it.nc = it.valid ? CHUNK : 0;
+    it.valid = CHUNK * c < len;
+    it.nc = it.valid ? min(CHUNK, len - CHUNK * c) : 0;
     return it;
   }
   typedef const int32_t __attribute__((address_space(4)))* cptr;
@@ -228,7 +229,8 @@ __device__ PrepItem prep_item(const FwdKernelArgs& a, int N, int i) {
     if (mid + bos / CHUNK <= it.slot) lo = mid; else hi = mid - 1;
   }
   const int bos = cu ? cu[lo] : lo * a.T;
-  const int eos = cu ? cu[lo + 1] : (lo + 1) * a.T;
+  int eos = cu ? cu[lo + 1] : (lo + 1) * a.T;
+  if (a.prefix_len > 0) eos = min(eos, bos + a.prefix_len);   // prefix cap (see seq_span)
   const int c = it.slot - (lo + bos / CHUNK);
   it.t0 = bos + CHUNK * c;
   it.valid = c >= 0 && it.t0 < eos;               // some slots are used by no chunk

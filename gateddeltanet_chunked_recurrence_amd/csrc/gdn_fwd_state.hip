@@ -134,13 +134,7 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
   const int n = hidx / Hv, h = hidx % Hv;
   const int hk = h / (Hv / a.Hqk);
   int bos, eos;
-  if (a.cu_seqlens) {
-    bos = a.cu_seqlens[n];
-    eos = a.cu_seqlens[n + 1];
-  } else {
-    bos = n * a.T;
-    eos = bos + a.T;
-  }
+  seq_span(a, n, bos, eos);
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
   const int slot0 = n + bos / CHUNK;
 

@@ -160,13 +160,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
   const int n = hidx / Hv, h = hidx % Hv;
   const int hk = h / (Hv / a.Hqk);
   int bos, eos;
-  if (a.cu_seqlens) {
-    bos = a.cu_seqlens[n];
-    eos = a.cu_seqlens[n + 1];
-  } else {
-    bos = n * a.T;
-    eos = bos + a.T;
-  }
+  seq_span(a, n, bos, eos);
   const int nchunks = (eos - bos + CHUNK - 1) / CHUNK;
   const int slot0 = n + bos / CHUNK;
 

@@ -87,7 +87,7 @@ struct Chunk {
   int n, c, t0, nc;
   bool valid;
 };
-__device__ inline Chunk locate_slot(int slot, const int32_t* cu, int N, int T) {
+__device__ inline Chunk locate_slot(int slot, const int32_t* cu, int N, int T, int prefix_len) {
   int lo = 0, hi = N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -95,7 +95,8 @@ __device__ inline Chunk locate_slot(int slot, const int32_t* cu, int N, int T) {
     if (mid + bos / CHUNK <= slot) lo = mid; else hi = mid - 1;
   }
   const int bos = cu ? cu[lo] : lo * T;
-  const int eos = cu ? cu[lo + 1] : (lo + 1) * T;
+  int eos = cu ? cu[lo + 1] : (lo + 1) * T;
+  if (prefix_len > 0) eos = min(eos, bos + prefix_len);   // prefix cap (see seq_span)
   Chunk ch;
   ch.n = lo;
   ch.c = slot - (lo + bos / CHUNK);

@@ -32,9 +32,40 @@ struct FwdKernelArgs {
   int32_t w_img_bytes;        // 1: the W plane of the images holds code bytes (both QDQ sites on)
   int32_t solve_degree;       // 0: exact (I + L)^-1; else the Neumann polynomial of this degree (2^j - 1)
   int32_t T;                  // tokens per sequence (no cu_seqlens)
+  int32_t prefix_len;         // > 0: only the first prefix_len tokens of every sequence
   int32_t Hqk, Hv, Dv, block_v;
   float scale;
 };
+
+// Tokens [bos, eos) of sequence n that the chunk path runs over: the whole
+// sequence, or its first prefix_len tokens when that is set.
+__device__ __forceinline__ void seq_span(const FwdKernelArgs& a, int n, int& bos, int& eos) {
+  if (a.cu_seqlens) {
+    bos = a.cu_seqlens[n];
+    eos = a.cu_seqlens[n + 1];
+  } else {
+    bos = n * a.T;
+    eos = bos + a.T;
+  }
+  if (a.prefix_len > 0) eos = min(eos, bos + a.prefix_len);
+}
+
+// Whether packed token `tok` lies in the span seq_span gives its sequence.
+__device__ inline bool token_in_span(const FwdKernelArgs& a, int N, int tok) {
+  if (a.prefix_len <= 0) return true;
+  int bos;
+  if (a.cu_seqlens) {
+    int lo = 0, hi = N - 1;          // last sequence starting at or before tok
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_seqlens[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    bos = a.cu_seqlens[lo];
+  } else {
+    bos = tok - tok % a.T;
+  }
+  return tok - bos < a.prefix_len;
+}
 
 // Bits of the sticky device error word (gdn_device_errors in gdn.h).
 constexpr uint32_t kErrLdsWait = 1u;      // a bounded LDS-counter wait gave up
@@ -118,5 +149,43 @@ hipError_t launch_check_stamp(const BwdKernelArgs& a, const SavedStamp& want, in
 hipError_t launch_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
                             int64_t n_states, int Dk, int Dv, int block_v, int fmt,
                             hipStream_t stream);
+
+// Decode continuation (gdn_decode.hip): token-state writes through the state
+// quantizer, forward and straight-through backward.
+struct DecodeKernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const float* h_in;          // nullable (zero state)
+  const int32_t* cu_seqlens;  // nullable
+  void* o;
+  float* ht;                  // nullable
+  uint8_t* s_codes;           // saved written states (state QDQ on), nullable
+  float* s_scale;             // their tile scales, nullable
+  float* s_f32;               // saved written states (state QDQ off), nullable
+  int32_t T, start, Hqk, Hv, Dv, block_v, readout;
+  float scale;
+  // backward
+  const void* dout;
+  const float* dht;           // nullable
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dh_in;               // nullable
+  float* ws_dqk;              // [B*T, Hv, 2, Dk] FP32 when Hv > Hqk, else NULL
+  int32_t grad_f32;
+  int32_t total_tokens;
+};
+
+struct DecodeConfig {
+  int Dk, Dv, N, Hv, Hqk, state_fmt, f32_io;
+};
+
+hipError_t launch_decode_fwd(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t s);
+hipError_t launch_decode_bwd(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t s);
 
 }  // namespace gdn

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
   GDN_OK = 0,
@@ -110,6 +110,18 @@ typedef struct {
   int32_t num_seqs;            /* N (must equal B without cu_seqlens)         */
   int32_t io_dtype;            /* gdn_dtype of q, k, v and o                  */
   float scale;                 /* output scale (1/sqrt(Dk) is the usual one)  */
+  int32_t prefix_len;          /* 0: whole sequences. > 0: only the first
+                                  prefix_len tokens of every sequence are run
+                                  (the exact chunk prefill of a decode
+                                  continuation, "[2/4] GDN/KDA decode QAT with
+                                  INT8 recurrent state", "What does this PR
+                                  do?": an explicit prefix length selects
+                                  chunk prefill, then token-state writes; see
+                                  gdn_decode_fwd). ht is the state after the
+                                  prefix; o, the saved buffer and every
+                                  gradient are written for prefix tokens only,
+                                  later tokens are left untouched. Negative:
+                                  GDN_E_INVALID.                              */
   gdn_qdq_policy policy;
   const void* q;               /* [B, T, Hqk, Dk] io_dtype                    */
   const void* k;               /* [B, T, Hqk, Dk] io_dtype                    */
@@ -237,6 +249,97 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream);
 gdn_status gdn_qdq_state(const float* x, float* y, float* scales, uint8_t* codes,
                          int64_t n_states, int32_t Dk, int32_t Dv, int32_t block_v,
                          int32_t fmt, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode continuation ("[2/4] GDN/KDA decode QAT with INT8 recurrent state",
+ * "What does this PR do?": an explicit prefix length selects exact chunk
+ * prefill followed by token-state writes, gradients through initial states
+ * and the continuation; "Testing": 257-token trajectories, nonzero initial
+ * states, grouped heads, packed tails, both readouts, split carry, all state
+ * scale widths, first-order input/state gradients).
+ *
+ * The prefill is gdn_chunk_fwd / gdn_chunk_bwd with prefix_len = P; the
+ * decode steps are gdn_decode_fwd / gdn_decode_bwd with start = P on the same
+ * token buffers, from the prefill's ht (and its dht from the decode's
+ * dh_in). Per (sequence, value head h), from the state handed over S (h_in):
+ *   S <- QDQ_S(S)                                    (the state as written)
+ *   each decode token t (tokens start .. len-1 of the sequence):
+ *     S <- exp(g_t) S;  u = beta_t (v_t - S^T k_t);  S <- S + k_t u^T
+ *     o_before = scale S^T q_t;  S <- QDQ_S(S);  o_after = scale S^T q_t
+ *     o_t = o_before or o_after, as `readout` selects
+ *   ht = S, the last state written.
+ * QDQ_S is the state QDQ above (one scale per [Dk, block_v] tile); with
+ * state_fmt OFF it is the identity and the decode is the plain recurrence.
+ * The arithmetic is FP32. */
+typedef enum { GDN_READOUT_BEFORE_WRITE = 0, GDN_READOUT_AFTER_WRITE = 1 } gdn_readout;
+
+/* Shapes as gdn_fwd_args (Dk in {64, 128}, Dv in {64, 128, 256}, either
+ * io_dtype for any Dk). */
+typedef struct {
+  int32_t B, T, Hqk, Hv, Dk, Dv;
+  int32_t num_seqs;            /* N (must equal B without cu_seqlens)         */
+  int32_t io_dtype;            /* gdn_dtype of q, k, v and o                  */
+  float scale;
+  int32_t start;               /* first decode token of every sequence
+                                  (sequence-relative, >= 0); earlier tokens
+                                  are neither read nor written               */
+  int32_t state_fmt;           /* gdn_qdq_fmt of the token-state writes       */
+  int32_t block_v;             /* state scale tile width: 16, 32, 64, 128 or
+                                  256 dividing Dv (ignored when OFF)          */
+  int32_t readout;             /* gdn_readout                                 */
+  const void* q;               /* [B, T, Hqk, Dk] io_dtype                    */
+  const void* k;               /* [B, T, Hqk, Dk] io_dtype                    */
+  const void* v;               /* [B, T, Hv, Dv]  io_dtype                    */
+  const float* g;              /* [B, T, Hv] log-gate                         */
+  const float* beta;           /* [B, T, Hv]                                  */
+  const float* h_in;           /* [N, Hv, Dk, Dv] state handed over, or NULL  */
+  const int32_t* cu_seqlens;   /* [N + 1] offsets (device), or NULL           */
+  void* o;                     /* out [B, T, Hv, Dv]: decode tokens only      */
+  float* ht;                   /* out [N, Hv, Dk, Dv] last written state, or NULL */
+  void* saved;                 /* out: gdn_decode_saved_bytes() bytes for the
+                                  backward, or NULL. Every written state: the
+                                  first write of sequence n in slot
+                                  lo_n + n (lo_n its first decode token, packed
+                                  index), the write after decode token t in
+                                  slot t + n + 1; state_fmt != OFF: codes
+                                  [B*T + N, Hv, Dk, Dv] bytes, then (256-byte
+                                  aligned) FP32 tile scales [B*T + N, Hv,
+                                  Dv / block_v]; OFF: FP32 states
+                                  [B*T + N, Hv, Dk, Dv]                      */
+} gdn_decode_args;
+
+size_t gdn_decode_saved_bytes(const gdn_decode_args* a);   /* 0 on error */
+
+/* Decode steps. Writes o for decode tokens, ht and saved when not NULL.
+ * Allocates nothing; no workspace. */
+gdn_status gdn_decode_fwd(const gdn_decode_args* a, void* stream);
+
+/* Backward of gdn_decode_fwd, identity straight-through at every write; the
+ * saved written states are the values used in every product. Gradients are
+ * written for decode tokens only (earlier tokens are left untouched, so the
+ * prefill's gdn_chunk_bwd may fill them); dh_in (the gradient of h_in) is
+ * the prefill's dht. grad_dtype applies to dq, dk, dv. */
+typedef struct {
+  gdn_decode_args fwd;         /* same values as the forward call; fwd.o,
+                                  fwd.ht are not read; fwd.saved must hold the
+                                  forward's saved buffer                      */
+  const void* do_;             /* [B, T, Hv, Dv] io_dtype                     */
+  const float* dht;            /* [N, Hv, Dk, Dv] or NULL (= 0)               */
+  int32_t grad_dtype;
+  void* dq;                    /* out [B, T, Hqk, Dk] (summed over the group) */
+  void* dk;                    /* out [B, T, Hqk, Dk]                         */
+  void* dv;                    /* out [B, T, Hv, Dv]                          */
+  float* dg;                   /* out [B, T, Hv]                              */
+  float* dbeta;                /* out [B, T, Hv]                              */
+  float* dh_in;                /* out [N, Hv, Dk, Dv], or NULL                */
+  void* workspace;             /* gdn_decode_bwd_workspace_bytes() bytes (per
+                                  value head dq, dk before the group sum when
+                                  Hv > Hqk; 0 bytes otherwise)               */
+  size_t workspace_bytes;
+} gdn_decode_bwd_args;
+
+size_t gdn_decode_bwd_workspace_bytes(const gdn_decode_bwd_args* a);
+gdn_status gdn_decode_bwd(const gdn_decode_bwd_args* a, void* stream);
 
 const char* gdn_last_error(void);
 int32_t gdn_abi_version(void);

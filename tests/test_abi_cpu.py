@@ -22,11 +22,12 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _header_functions()
-    assert {'gdn_chunk_fwd', 'gdn_chunk_bwd', 'gdn_qdq_state'} <= set(names)
+    assert {'gdn_chunk_fwd', 'gdn_chunk_bwd', 'gdn_qdq_state', 'gdn_decode_fwd',
+            'gdn_decode_bwd', 'gdn_decode_saved_bytes', 'gdn_decode_bwd_workspace_bytes'} <= set(names)
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 6
+    assert lib.gdn_abi_version() == 7
 
 
 def _args(**kw):
@@ -75,6 +76,7 @@ BAD = [
     (dict(read_fmt=5, state_fmt=0), B.GDN_E_UNSUPPORTED, 'read_fmt'),
     (dict(read_fmt=1), B.GDN_E_INVALID, 'replaces the state'),
     (dict(read_fmt=1, state_fmt=0, Dk=64), B.GDN_E_UNSUPPORTED, 'Dk = 128'),
+    (dict(prefix_len=-1), B.GDN_E_INVALID, 'prefix_len'),
 ]
 
 
@@ -217,3 +219,71 @@ def test_noalloc_forward_refuses_above_its_scratch():
     bad = _args(chunk_size=32)                        # the ordinary checks come first
     assert lib.gdn_chunk_fwd_noalloc(ctypes.byref(bad), None) == B.GDN_E_UNSUPPORTED
     assert 'chunk_size' in lib.gdn_last_error().decode()
+
+
+# ------------------------------------------------------------------ decode
+def _dargs(**kw):
+    fake = ctypes.c_void_p(0x10000)
+    a = B.DecodeArgs(B=1, T=257, Hqk=2, Hv=4, Dk=128, Dv=128, num_seqs=1, io_dtype=B.GDN_BF16,
+                     scale=0.1, start=64, state_fmt=B.QDQ_INT8, block_v=64,
+                     readout=B.READOUT_BEFORE_WRITE)
+    for name in ('q', 'k', 'v', 'g', 'beta', 'o'):
+        setattr(a, name, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+DECODE_BAD = [
+    (dict(state_fmt=3), B.GDN_E_UNSUPPORTED, 'format'),
+    (dict(block_v=48), B.GDN_E_UNSUPPORTED, 'block_v'),
+    (dict(Dv=64, block_v=128), B.GDN_E_INVALID, 'does not divide'),
+    (dict(readout=2), B.GDN_E_INVALID, 'readout'),
+    (dict(start=-1), B.GDN_E_INVALID, 'start'),
+    (dict(Hv=6, Hqk=4), B.GDN_E_INVALID, 'multiple'),
+    (dict(Dk=96), B.GDN_E_UNSUPPORTED, 'Dk'),
+    (dict(Dv=32), B.GDN_E_UNSUPPORTED, 'Dv'),
+    (dict(io_dtype=3), B.GDN_E_INVALID, 'io_dtype'),
+    (dict(num_seqs=2), B.GDN_E_INVALID, 'num_seqs'),
+    (dict(scale=float('inf')), B.GDN_E_INVALID, 'scale'),
+    (dict(v=None), B.GDN_E_INVALID, 'v is NULL'),
+    (dict(o=None), B.GDN_E_INVALID, 'o is NULL'),
+    (dict(h_in=ctypes.c_void_p(0x10008)), B.GDN_E_INVALID, 'aligned'),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", DECODE_BAD)
+def test_decode_forward_rejects_before_launch(kw, status, msg):
+    lib = B.load_library()
+    a = _dargs(**kw)
+    assert lib.gdn_decode_fwd(ctypes.byref(a), None) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_decode_saved_bytes_and_backward_checks():
+    """Saved written states: one per decode step plus the first write of each
+    sequence, in B*T + N slots (codes, then scales, then the stamp); the
+    backward needs that buffer and, with grouped heads, its workspace."""
+    lib = B.load_library()
+    a = _dargs()
+    slots = 257 + 1
+    codes = slots * 4 * 128 * 128
+    scales = slots * 4 * 2 * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.gdn_decode_saved_bytes(ctypes.byref(a)) == r256(r256(codes) + scales) + 256
+    off = _dargs(state_fmt=B.QDQ_OFF)
+    assert lib.gdn_decode_saved_bytes(ctypes.byref(off)) == r256(codes * 4) + 256
+    assert lib.gdn_decode_saved_bytes(ctypes.byref(_dargs(readout=7))) == 0
+    fake = ctypes.c_void_p(0x10000)
+    b = B.DecodeBwdArgs(fwd=_dargs(), do_=fake, dq=fake, dk=fake, dv=fake, dg=fake, dbeta=fake,
+                        grad_dtype=B.GDN_BF16)
+    assert lib.gdn_decode_bwd(ctypes.byref(b), None) == B.GDN_E_INVALID      # no saved buffer
+    assert 'saved' in lib.gdn_last_error().decode()
+    b.fwd.saved = fake
+    need = lib.gdn_decode_bwd_workspace_bytes(ctypes.byref(b))
+    assert need == r256(257 * 4 * 2 * 128 * 4)                   # per value head dq, dk
+    assert lib.gdn_decode_bwd(ctypes.byref(b), None) == B.GDN_E_WORKSPACE
+    b.fwd.Hqk = 4                                                 # no groups: no workspace
+    assert lib.gdn_decode_bwd_workspace_bytes(ctypes.byref(b)) == 0
+    b.grad_dtype = 9
+    assert lib.gdn_decode_bwd(ctypes.byref(b), None) == B.GDN_E_INVALID
