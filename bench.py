@@ -227,7 +227,7 @@ def fwd_record(name, spec, t, state_kernel):
         gflop=(f_prep + f_state) / 1e9)
 
 
-def time_fwd_bwd(steps, warmup, flush):
+def time_fwd_bwd(steps, warmup, flush, solve_degree=0):
     """Forward (saving for the backward) + backward on the forward+backward
     workload (B=2, T=8192, H=16, Dk=Dv=128, E4M3 state and W, initial state,
     dO and dS_final given), per-step medians."""
@@ -243,7 +243,8 @@ def time_fwd_bwd(steps, warmup, flush):
 
     def fwd():
         return B.gdn_chunk_fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], scale=scale,
-                               h0=x['h0'], save_for_backward=True, **kw)
+                               h0=x['h0'], save_for_backward=True, solve_degree=solve_degree,
+                               **kw)
 
     def bwd(saved):
         return B.gdn_chunk_bwd(x['q'], x['k'], x['v'], x['g'], x['beta'], saved, x['do'],
@@ -269,10 +270,53 @@ def time_fwd_bwd(steps, warmup, flush):
     fl = (flops_prep(128, 128) + flops_state(128, 128) + flops_bwd(128, 128)) * th
     tot = f['median'] + b['median']
     ach = fl / (tot * 1e-3) / 1e12
-    return dict(workload=name, fwd_ms=f, bwd_ms=b, tokens_per_s=tokens / (tot * 1e-3),
+    return dict(workload=name, solve_degree=solve_degree, fwd_ms=f, bwd_ms=b,
+                tokens_per_s=tokens / (tot * 1e-3),
                 steps=steps, bwd_bytes_counted={k: measured_traffic(k, name) for k in BWD_KERNELS},
                 roofline_path=dict(bound='mfma', achieved=ach, peak=PEAK_BF16_TFLOPS,
                                    unit='TFLOP/s', frac=ach / PEAK_BF16_TFLOPS))
+
+
+def time_decode(steps, warmup, flush):
+    """Decode continuation on the 257-token workload: the 64-token chunk
+    prefill plus 193 token-state writes (E4M3, readout after the write),
+    forward (saving for the backward) and backward, per-step medians."""
+    import torch
+
+    import gdn_inputs
+    from gateddeltanet_chunked_recurrence_amd import binding as B
+    name = 'decode_e4m3_b4_t257_p64_h16_d128'
+    spec = gdn_inputs.spec(name)
+    x = gdn_inputs.make_inputs(spec, seed=2, device='cuda')
+    P, scale = spec['prefix_len'], 1.0 / math.sqrt(spec['Dk'])
+    kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'],
+              readout=B.READOUT_AFTER_WRITE)
+    args = [x[n] for n in ('q', 'k', 'v', 'g', 'beta')]
+
+    def fwd():
+        return B.gdn_prefill_decode_fwd(*args, P, scale, x['h0'], save_for_backward=True, **kw)
+
+    def bwd(saved):
+        return B.gdn_prefill_decode_bwd(*args, saved, x['do'], x['dht'], scale, x['h0'])
+
+    for _ in range(warmup):
+        bwd(fwd()[2])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        saved = fwd()[2]
+        ev[i][1].record(stream)
+        bwd(saved)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    f = _stats([e[0].elapsed_time(e[1]) for e in ev])
+    b = _stats([e[1].elapsed_time(e[2]) for e in ev])
+    tokens = spec['B'] * spec['T']
+    return dict(workload=name, fwd_ms=f, bwd_ms=b, decode_tokens_per_seq=spec['T'] - P,
+                tokens_per_s=tokens / ((f['median'] + b['median']) * 1e-3), steps=steps)
 
 
 def time_neumann_prep(x, spec, scale, kw, steps, degrees=(3, 31)):
@@ -378,6 +422,9 @@ def main():
         kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
         out['neumann_solve'] = time_neumann_prep(x, spec, 1.0 / math.sqrt(spec['Dk']), kw,
                                                  steps=max(3, args.steps // 5))
+        out['fwd_bwd_neumann_d3'] = time_fwd_bwd(steps=max(3, args.steps // 5), warmup=2,
+                                                 flush=flush, solve_degree=3)
+        out['decode'] = time_decode(steps=max(3, args.steps // 5), warmup=2, flush=flush)
     if not args.no_cpu_baseline:
         out['cpu_baseline'] = cpu_baseline(spec, seed=2)
     print(json.dumps(out), flush=True)

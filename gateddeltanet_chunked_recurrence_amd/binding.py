@@ -117,7 +117,7 @@ def _check(status):
         raise GdnError(status, load_library().gdn_last_error().decode())
 
 
-DEVERR_LDS_WAIT, DEVERR_FLAG_WAIT, DEVERR_SAVED_STAMP = 1, 2, 4
+DEVERR_LDS_WAIT, DEVERR_FLAG_WAIT, DEVERR_SAVED_STAMP, DEVERR_P_RANGE = 1, 2, 4, 8
 
 
 def device_errors():

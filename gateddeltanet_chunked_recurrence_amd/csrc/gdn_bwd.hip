@@ -72,6 +72,17 @@ __device__ __forceinline__ f32x4 mm(const float* A, int ars, int acs, const floa
   return acc;
 }
 
+// mm with the k loop unrolled by four (k1 - k0 a multiple of 16), so the LDS
+// reads of four steps are in flight before their products.
+__device__ __forceinline__ f32x4 mm_u(const float* A, int ars, int acs, const float* B, int brs,
+                                      int bcs, int i0, int j0, int k0, int k1, int r16, int grp,
+                                      f32x4 acc) {
+#pragma unroll 4
+  for (int k = k0; k < k1; k += 4)
+    acc = mfma_f32(A[(i0 + r16) * ars + (k + grp) * acs], B[(k + grp) * brs + (j0 + r16) * bcs], acc);
+  return acc;
+}
+
 // acc += A(i0 + r, .) Breg, where Breg holds KT accumulator tiles of a
 // [16 KT x 16] B block (Breg[t][i] = B[16 t + 4 grp + i][c]); K runs in the
 // matching order. A(i, k) = A[i * ars + k * acs].
@@ -92,6 +103,8 @@ __device__ __forceinline__ f32x4 mm_reg(const float* A, int ars, int acs, const 
 template <bool F32IN>
 __device__ void stage_rows(float* dst, int ld, const void* src, int t0, int nc, int H, int h,
                            int Dtot, int col0, int D, int tid) {
+  // unrolled so that several rows' loads are in flight before their LDS writes
+#pragma unroll 8
   for (int e = tid; e < 64 * D; e += NT) {
     const int r = e / D, cc = e % D;
     float v = 0.f;
@@ -101,6 +114,32 @@ __device__ void stage_rows(float* dst, int ld, const void* src, int t0, int nc, 
                 : static_cast<float>(reinterpret_cast<const bf16*>(src)[off]);
     }
     dst[r * ld + cc] = v;
+  }
+}
+
+// stage_rows for bf16 rows of D (a multiple of 8) columns: 16-byte loads,
+// all of a thread's issued before its LDS writes.
+template <int D>
+__device__ void stage_rows_bf16(float* dst, int ld, const void* src, int t0, int nc, int H, int h,
+                                int tid) {
+  constexpr int V = 64 * D / 8, PER = (V + NT - 1) / NT;
+  bf16x8 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + NT * u, r = e / (D / 8), c8 = e % (D / 8);
+    if (e < V && r < nc)
+      v[u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(src) +
+                                              ((int64_t)(t0 + r) * H + h) * D + 8 * c8);
+    else
+      v[u] = bf16x8{};
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + NT * u, r = e / (D / 8), c8 = e % (D / 8);
+    if (e < V) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[r * ld + 8 * c8 + i] = static_cast<float>(v[u][i]);
+    }
   }
 }
 
@@ -162,7 +201,7 @@ __device__ void build_L(const float* Kf, const Gates& gs, float* Lf, int wave, i
   const int r16 = lane & 15, grp = lane >> 4;
   for (int t = wave; t < 16; t += 4) {
     const int mi = t >> 2, mj = t & 3;
-    const f32x4 a = mm(Kf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4());
+    const f32x4 a = mm_u(Kf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4());
     const int cj = 16 * mj + r16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -258,7 +297,11 @@ __global__ void __launch_bounds__(NT, 1) bwd_prep(BwdKernelArgs a, int N) {
 // the chunk-local suffix sums of those d gamma. dk goes to the per-value-head
 // FP32 rows (the group sum follows); d beta and dg are read, added to and
 // written back (one workgroup per chunk and head owns those entries).
-// FP32 throughout (FP32 MFMA 16x16x4).
+// FP32 throughout (FP32 MFMA 16x16x4). -L^T and its powers (Pd) and the
+// partial products Xd are upper triangular, L and dL strictly lower, so each
+// product runs only over the 16-wide key blocks where both factors can be
+// nonzero (the skipped steps would add exact zeros) and tiles known to be
+// zero are written as zeros.
 template <int DK>
 __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   constexpr int LK = DK + 1;
@@ -277,7 +320,7 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   const int Hv = f.Hv, Hqk = f.Hqk, hk = h / (Hv / Hqk), nc = ch.nc;
   const int64_t chb = (int64_t)slot * Hv + h;
 
-  stage_rows<false>(Kf, LK, f.k, ch.t0, nc, Hqk, hk, DK, 0, DK, tid);
+  stage_rows_bf16<DK>(Kf, LK, f.k, ch.t0, nc, Hqk, hk, tid);
   load_gates(gs, f.g, f.beta, ch.t0, nc, Hv, h, wave, lane);
   __syncthreads();
   build_L<DK>(Kf, gs, Lf, wave, lane);
@@ -285,10 +328,17 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   // M = [[-L^T, G], [0, -L^T]]: P = M, partial product I + M
   int iPd = 0, iPe = 1, iXd = 2, iXe = 3, iT1 = 4, iT2 = 5;
   {
+    // every load of dX is issued before the first use (one memory latency,
+    // not one per element)
     const float* dXg = a.ws_dX + chb * 4096;
-    for (int e = tid; e < 4096; e += NT) {
-      const int i = e >> 6, j = e & 63;
-      const float g = (j < i && i < nc) ? dXg[e] : 0.f;
+    constexpr int PER = 4096 / NT;
+    float gv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) gv[u] = dXg[tid + NT * u];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + NT * u, i = e >> 6, j = e & 63;
+      const float g = (j < i && i < nc) ? gv[u] : 0.f;
       const float lt = Lf[j * 65 + i];
       Mb[iPd][i * 65 + j] = -lt;
       Mb[iXd][i * 65 + j] = (i == j ? 1.f : 0.f) - lt;
@@ -302,9 +352,11 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
     float *T1 = Mb[iT1], *T2 = Mb[iT2];
     for (int t = wave; t < 16; t += 4) {
       const int i0 = 16 * (t >> 2), j0 = 16 * (t & 3);
-      f32x4 pe = mm(Pd, 65, 1, Pe, 65, 1, i0, j0, 0, 64, r16, grp, zero4());
-      pe = mm(Pe, 65, 1, Pd, 65, 1, i0, j0, 0, 64, r16, grp, pe);
-      const f32x4 pd = mm(Pd, 65, 1, Pd, 65, 1, i0, j0, 0, 64, r16, grp, zero4());
+      // Pd(i, k) = 0 for k below i's block, Pd(k, j) = 0 for k above j's block
+      f32x4 pe = mm_u(Pd, 65, 1, Pe, 65, 1, i0, j0, i0, 64, r16, grp, zero4());
+      pe = mm_u(Pe, 65, 1, Pd, 65, 1, i0, j0, 0, j0 + 16, r16, grp, pe);
+      const f32x4 pd = i0 <= j0 ? mm_u(Pd, 65, 1, Pd, 65, 1, i0, j0, i0, j0 + 16, r16, grp, zero4())
+                                : zero4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         T1[(i0 + 4 * grp + i) * 65 + j0 + r16] = pe[i];
@@ -323,9 +375,9 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
         xe[i] = Xe[(i0 + 4 * grp + i) * 65 + j0 + r16];
         xd[i] = Xd[(i0 + 4 * grp + i) * 65 + j0 + r16];
       }
-      xe = mm(Xd, 65, 1, T1, 65, 1, i0, j0, 0, 64, r16, grp, xe);
-      xe = mm(Xe, 65, 1, T2, 65, 1, i0, j0, 0, 64, r16, grp, xe);
-      xd = mm(Xd, 65, 1, T2, 65, 1, i0, j0, 0, 64, r16, grp, xd);
+      xe = mm_u(Xd, 65, 1, T1, 65, 1, i0, j0, i0, 64, r16, grp, xe);         // Xd upper
+      xe = mm_u(Xe, 65, 1, T2, 65, 1, i0, j0, 0, j0 + 16, r16, grp, xe);     // Pd' upper
+      if (i0 <= j0) xd = mm_u(Xd, 65, 1, T2, 65, 1, i0, j0, i0, j0 + 16, r16, grp, xd);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         nXe[(i0 + 4 * grp + i) * 65 + j0 + r16] = xe[i];
@@ -348,7 +400,8 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   // (K K^T)_ij Gam_ij below the diagonal
   for (int t = wave; t < 16; t += 4) {
     const int mi = t >> 2, mj = t & 3;
-    const f32x4 kk = mm(Kf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4());
+    const f32x4 kk = mi >= mj ? mm_u(Kf, LK, 1, Kf, 1, LK, 16 * mi, 16 * mj, 0, DK, r16, grp, zero4())
+                              : zero4();
     const int cj = 16 * mj + r16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -358,33 +411,66 @@ __global__ void __launch_bounds__(NT, 1) bwd_neumann(BwdKernelArgs a, int N) {
   }
   __syncthreads();
   // row and column sums: d beta_i = sum_j dL_ij AG_ij; d gamma parts from dL_ij L_ij
-  if (tid < 64) {
-    const int i = tid;
-    float sb = 0.f, sg = 0.f;
-    for (int j = 0; j < i; ++j) {
-      const float dl = i < nc ? -Xe[i * 65 + j] : 0.f;
+  // (four threads per row and per column, 16 entries each, combined within
+  // their quad; fixed trip counts with masks so the LDS reads are issued ahead)
+  {
+    const int i = tid >> 2, part = tid & 3;
+    float sb = 0.f, sg = 0.f, cg = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = 16 * part + jj;
+      const float dl = (j < i && i < nc) ? -Xe[i * 65 + j] : 0.f;
       sb += dl * AG[i * 65 + j];
       sg += dl * Lf[i * 65 + j];
+      // column i: rows j of the same range (the roles of i and j swapped)
+      cg += (j > i && j < nc) ? -Xe[j * 65 + i] * Lf[j * 65 + i] : 0.f;
     }
-    rowB[i] = sb;
-    rowG[i] = sg;
-  } else if (tid < 128) {
-    const int j = tid - 64;
-    float cg = 0.f;
-    for (int i = j + 1; i < nc; ++i) cg += -Xe[i * 65 + j] * Lf[i * 65 + j];
-    colG[j] = cg;
+    sb += dpp_f<0xB1>(sb);
+    sb += dpp_f<0x4E>(sb);
+    sg += dpp_f<0xB1>(sg);
+    sg += dpp_f<0x4E>(sg);
+    cg += dpp_f<0xB1>(cg);
+    cg += dpp_f<0x4E>(cg);
+    if (part == 0) {
+      rowB[i] = sb;
+      rowG[i] = sg;
+      colG[i] = cg;
+    }
   }
   // C = dA + dA^T into the Xe buffer's place is not needed: K products read DA twice
   __syncthreads();
   // dk += (dA + dA^T) K, added to this value head's FP32 dk rows
-  for (int t = wave; t < 4 * (DK / 16); t += 4) {
-    const int mt = t & 3, nt = t >> 2;
-    f32x4 acc = mm(DA, 65, 1, Kf, LK, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, zero4());
-    acc = mm(DA, 1, 65, Kf, LK, 1, 16 * mt, 16 * nt, 0, 64, r16, grp, acc);
+  // (all of a wave's tiles first, then every read of the rows they add to,
+  // then the writes: one memory latency per wave, not one per tile)
+  constexpr int NTW = DK / 16;                  // tiles per wave: 4 row blocks x DK / 16 over 4 waves
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int t = wave + 4 * u, mt = t & 3, nt = t >> 2;
+    // DA(i, k) = 0 for k >= i; DA^T(i, k) = DA(k, i) = 0 for k <= i
+    acc[u] = mm_u(DA, 65, 1, Kf, LK, 1, 16 * mt, 16 * nt, 0, 16 * mt + 16, r16, grp, zero4());
+    acc[u] = mm_u(DA, 1, 65, Kf, LK, 1, 16 * mt, 16 * nt, 16 * mt, 64, r16, grp, acc[u]);
+  }
+  float old[NTW][4];
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int t = wave + 4 * u, mt = t & 3, nt = t >> 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * mt + 4 * grp + i;
-      if (row < nc) a.ws_dqk[(((int64_t)(ch.t0 + row) * Hv + h) * 2 + 1) * DK + 16 * nt + r16] += acc[i];
+      old[u][i] = row < nc ? a.ws_dqk[(((int64_t)(ch.t0 + row) * Hv + h) * 2 + 1) * DK + 16 * nt + r16]
+                           : 0.f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int t = wave + 4 * u, mt = t & 3, nt = t >> 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * grp + i;
+      if (row < nc)
+        a.ws_dqk[(((int64_t)(ch.t0 + row) * Hv + h) * 2 + 1) * DK + 16 * nt + r16] =
+            old[u][i] + acc[u][i];
     }
   }
   if (wave == 0) {

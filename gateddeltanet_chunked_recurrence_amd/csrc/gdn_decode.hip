@@ -102,13 +102,67 @@ __device__ __forceinline__ void st_vec(void* base, int64_t off, const float (&x)
   }
 }
 
+// The values of lanes l ^ 16 and l ^ 32, by the gfx950 lane swaps (VALU, no
+// LDS crossbar): v_permlane16_swap on two copies of x leaves rows (0, 0, 2, 2)
+// in one and (1, 1, 3, 3) in the other, v_permlane32_swap halves (0, 0) and
+// (1, 1); each lane then holds its own value and its partner's, one in each.
+// (Written as one VALU instruction in asm: this compiler's builtin returns
+// the first result in both places. The s_nop covers the wait states the
+// swap needs after a VALU write of its operands.)
+struct LanePair {
+  float a, b;
+};
+__device__ __forceinline__ LanePair swap16(float x) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return {a, b};
+}
+__device__ __forceinline__ LanePair swap32(float x) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return {a, b};
+}
+// N consecutive bf16 or FP32 elements at byte offset `off` of an LDS buffer.
+template <int N, bool F32>
+__device__ __forceinline__ void lds_vec(const char* base, int off, float (&x)[N]) {
+  if constexpr (F32) {
+    if constexpr (N == 2) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(base + off);
+      x[0] = v[0];
+      x[1] = v[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < N / 4; ++h) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(base + off + 16 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * h + e] = v[e];
+      }
+    }
+  } else {
+    if constexpr (N == 2) {
+      const bf16x2 v = *reinterpret_cast<const bf16x2*>(base + off);
+      x[0] = from_bf16(v[0]);
+      x[1] = from_bf16(v[1]);
+    } else if constexpr (N == 4) {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(base + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = from_bf16(v[e]);
+    } else {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(base + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = from_bf16(v[e]);
+    }
+  }
+}
+
 // Sum over the eight row groups of a wave (lanes l, l ^ 8, l ^ 16, ...):
-// row_ror:8 within each row of 16 lanes, then two exchanges across rows.
+// row_ror:8 within each row of 16 lanes, then the two swaps across rows.
 __device__ __forceinline__ float sum_rows8(float x) {
   x += dpp_f<0x128>(x);
-  x += __shfl_xor(x, 16, WAVE);
-  x += __shfl_xor(x, 32, WAVE);
-  return x;
+  LanePair p = swap16(x);
+  x = p.a + p.b;
+  p = swap32(x);
+  return p.a + p.b;
 }
 // Sum over the eight column groups of a wave (lanes 8 m .. 8 m + 7): quad
 // swaps, then the half-row mirror (after the quad steps all lanes of a quad
@@ -123,8 +177,10 @@ __device__ __forceinline__ float sum_cols8(float x) {
 // within a wave (block_v / 8 column groups, all row groups).
 __device__ __forceinline__ float max_tile_lanes(float m, int block_v) {
   m = fmaxf(m, dpp_f<0x128>(m));
-  m = fmaxf(m, __shfl_xor(m, 16, WAVE));
-  m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+  LanePair p = swap16(m);
+  m = fmaxf(p.a, p.b);
+  p = swap32(m);
+  m = fmaxf(p.a, p.b);
   m = fmaxf(m, dpp_f<0xB1>(m));                     // block_v >= 16
   if (block_v >= 32) m = fmaxf(m, dpp_f<0x4E>(m));
   if (block_v >= 64) m = fmaxf(m, dpp_f<0x141>(m));
@@ -155,6 +211,24 @@ __device__ __forceinline__ void decode8(uint32_t w0, uint32_t w1, float d, float
 struct Span {
   int bos, eos, lo;
 };
+
+// The gates of a window of 64 decode tokens, one token per lane (vector
+// loads, read back with readlane): scalar loads of g and beta per token
+// would be waited for by every LDS barrier (which waits lgkmcnt), so the
+// windows are loaded one window ahead instead.
+struct GateWin {
+  float g, b;
+};
+__device__ __forceinline__ GateWin load_gate_win(const DecodeKernelArgs& a, int h, const Span& sp,
+                                                 int w) {
+  GateWin gw{0.f, 0.f};
+  const int t = sp.lo + 64 * w + __lane_id();
+  if (w >= 0 && t < sp.eos) {
+    gw.g = a.g[(int64_t)t * a.Hv + h];
+    gw.b = a.beta[(int64_t)t * a.Hv + h];
+  }
+  return gw;
+}
 __device__ __forceinline__ Span decode_span(const DecodeKernelArgs& a, int n) {
   Span sp;
   if (a.cu_seqlens) {
@@ -172,6 +246,15 @@ __device__ __forceinline__ Span decode_span(const DecodeKernelArgs& a, int n) {
 template <int DK, bool F32, int SF, int NS>
 __global__ void __launch_bounds__(256 * NS, 1) decode_fwd_kernel(DecodeKernelArgs a) {
   constexpr int RPL = DK / 32;
+  // Token inputs arrive in LDS windows of W tokens by global-to-LDS copies
+  // issued one window ahead, so no token waits on a global load (a wait for a
+  // register load would also wait for the stores issued after it): per
+  // window K and Q [W][DK], V [W][Dv] in the input dtype, then g and beta
+  // [W] each (FP32).
+  constexpr int ES = F32 ? 4 : 2, W = 32, NWV = 4 * NS;
+  constexpr int KB = W * DK * ES, VB = W * 64 * NS * ES, NBLK = (2 * KB + VB) / 1024;
+  static_assert((2 * KB + VB) % 1024 == 0, "1 KB copy blocks");
+  __shared__ __attribute__((aligned(16))) char win[2][2 * KB + VB + 2 * W * 4];
   __shared__ float xp[NS][4][64];   // S^T k per row quarter
   __shared__ float xo[NS][4][64];   // S^T q per row quarter
   __shared__ float xa[NS][4][8];    // tile amax per row quarter and column group
@@ -242,6 +325,36 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_fwd_kernel(DecodeKernelArg
     }
   };
 
+  // copies of window w (tokens lo + W w ..) into buffer b; tokens past the
+  // end repeat the last one (their values are never read)
+  const int nwin = (sp.eos - sp.lo + W - 1) / W;
+  auto issue_window = [&](int w, int b) {
+    const int t0 = sp.lo + W * w;
+    char* base = win[b];
+    for (int j = wave; j < NBLK; j += NWV) {
+      const int off = 1024 * j + 16 * lane;
+      const char* src;
+      if (off < 2 * KB) {
+        const int o = off < KB ? off : off - KB;
+        const int tok = min(t0 + o / (DK * ES), sp.eos - 1);
+        src = reinterpret_cast<const char*>(off < KB ? a.k : a.q) +
+              ((int64_t)tok * a.Hqk + hk) * (DK * ES) + o % (DK * ES);
+      } else {
+        const int o = off - 2 * KB;
+        const int tok = min(t0 + o / (Dv * ES), sp.eos - 1);
+        src = reinterpret_cast<const char*>(a.v) + ((int64_t)tok * Hv + h) * (Dv * ES) + o % (Dv * ES);
+      }
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src),
+                                       reinterpret_cast<uint4*>(base + 1024 * j), 16, 0, 0);
+    }
+    if (wave == NWV - 1) {                          // g (lanes 0..31) and beta (32..63)
+      const int tok = min(t0 + (lane & 31), sp.eos - 1);
+      const float* src = (lane < 32 ? a.g : a.beta) + (int64_t)tok * Hv + h;
+      __builtin_amdgcn_global_load_lds(src, reinterpret_cast<float*>(base + 2 * KB + VB), 4, 0, 0);
+    }
+  };
+  if (nwin > 0) issue_window(0, 0);
+
   // first write: the state handed over, as the cache holds it
   const int64_t slot0 = (int64_t)sp.lo + n;
   if constexpr (SF != 0) {
@@ -250,28 +363,20 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_fwd_kernel(DecodeKernelArg
   }
   write_state(slot0);
 
-  float kn[RPL], qn[RPL], vn[8], gn = 0.f, bn = 0.f;
-  auto load_token = [&](int t) {
-    const int64_t qk = ((int64_t)t * a.Hqk + hk) * DK + row0;
-    ld_vec<RPL, F32>(a.k, qk, kn);
-    ld_vec<RPL, F32>(a.q, qk, qn);
-    ld_vec<8, F32>(a.v, ((int64_t)t * Hv + h) * Dv + col0, vn);
-    gn = a.g[(int64_t)t * Hv + h];
-    bn = a.beta[(int64_t)t * Hv + h];
-  };
-  if (sp.lo < sp.eos) load_token(sp.lo);
-
   for (int t = sp.lo; t < sp.eos; ++t) {
-    float kk[RPL], qq[RPL], vv[8];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      kk[i] = kn[i];
-      qq[i] = qn[i];
+    const int j = t - sp.lo, w = j / W, tok = j % W;
+    const char* wb = win[w & 1];
+    if (tok == 0) {
+      vm_drain();                                   // this window's copies have landed
+      lds_barrier();
+      if (w + 1 < nwin) issue_window(w + 1, (w + 1) & 1);
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vv[c] = vn[c];
-    const float eg = expf(gn), bt = bn;
-    if (t + 1 < sp.eos) load_token(t + 1);          // next token, in flight meanwhile
+    float kk[RPL], qq[RPL], vv[8];
+    lds_vec<RPL, F32>(wb, (tok * DK + row0) * ES, kk);
+    lds_vec<RPL, F32>(wb, KB + (tok * DK + row0) * ES, qq);
+    lds_vec<8, F32>(wb, 2 * KB + (tok * Dv + col0) * ES, vv);
+    const float* gb = reinterpret_cast<const float*>(wb + 2 * KB + VB);
+    const float eg = expf(gb[tok]), bt = gb[W + tok];
 
     // decay and the delta-rule prediction S^T k
     float pp[8];
@@ -419,19 +524,43 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
     }
   };
 
-  const int64_t slot0 = (int64_t)sp.lo + n;
-  Held cur, prev;                  // written state after token t, and before it
+  Held cur, prev, pnext;           // written state after token t, before it, before t - 1
   if (sp.lo < sp.eos && !before) load_state((int64_t)(sp.eos - 1) + n + 1, cur);
+  // token inputs and the written state before the token, one token ahead
+  float kn[RPL], qn[RPL], vn[8], dn[8];
+  auto load_token = [&](int t) {
+    const int64_t qk = ((int64_t)t * a.Hqk + hk) * DK + row0;
+    ld_vec<RPL, F32>(a.k, qk, kn);
+    ld_vec<RPL, F32>(a.q, qk, qn);
+    ld_vec<8, F32>(a.v, ((int64_t)t * Hv + h) * Dv + col0, vn);
+    ld_vec<8, F32>(a.dout, ((int64_t)t * Hv + h) * Dv + col0, dn);
+    load_state((int64_t)t + n, pnext);
+  };
+  if (sp.lo < sp.eos) load_token(sp.eos - 1);
+  int wcur = sp.lo < sp.eos ? (sp.eos - 1 - sp.lo) >> 6 : 0;
+  GateWin gcur = load_gate_win(a, h, sp, wcur), gnxt = load_gate_win(a, h, sp, wcur - 1);
 
   for (int t = sp.eos - 1; t >= sp.lo; --t) {
-    load_state((int64_t)t + n, prev);
     float kk[RPL], qq[RPL], vv[8], dd[8];
-    const int64_t qk = ((int64_t)t * a.Hqk + hk) * DK + row0;
-    ld_vec<RPL, F32>(a.k, qk, kk);
-    ld_vec<RPL, F32>(a.q, qk, qq);
-    ld_vec<8, F32>(a.v, ((int64_t)t * Hv + h) * Dv + col0, vv);
-    ld_vec<8, F32>(a.dout, ((int64_t)t * Hv + h) * Dv + col0, dd);
-    const float eg = expf(a.g[(int64_t)t * Hv + h]), bt = a.beta[(int64_t)t * Hv + h];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      kk[i] = kn[i];
+      qq[i] = qn[i];
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      vv[c] = vn[c];
+      dd[c] = dn[c];
+    }
+    prev = pnext;
+    const int j = t - sp.lo;
+    if ((j >> 6) != wcur) {                         // previous window of gates
+      wcur = j >> 6;
+      gcur = gnxt;
+      gnxt = load_gate_win(a, h, sp, wcur - 1);
+    }
+    const float eg = expf(read_lane(gcur.g, j & 63)), bt = read_lane(gcur.b, j & 63);
+    if (t > sp.lo) load_token(t - 1);               // in flight during this token
 
     // P1: the prediction A^T k
     float pp[8];
@@ -586,7 +715,6 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
     }
     cur = prev;
   }
-  (void)slot0;
   if (a.dh_in) {
 #pragma unroll
     for (int i = 0; i < RPL; ++i)

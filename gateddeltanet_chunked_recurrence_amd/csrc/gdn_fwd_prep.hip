@@ -386,7 +386,12 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = row >= c0 + i ? acc[i] * fexp2(gr1 - gc[i]) : 0.f;
         if (a.w_img_bytes) {
-          // one fp16 plane (11-bit significand: relative error <= 2^-12)
+          // one fp16 plane (11-bit significand: relative error <= 2^-12). Its
+          // range is +-65504: an entry beyond it (|q . k| that large, which
+          // L2-normalised q and k never reach) raises a device error flag
+          // instead of passing an infinity on silently
+          if (fmaxf(fmaxf(fabsf(pv[0]), fabsf(pv[1])), fmaxf(fabsf(pv[2]), fabsf(pv[3]))) > 65504.f)
+            __hip_atomic_fetch_or(a.err, kErrPRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
           const f16x4 h = f16x4{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
           *reinterpret_cast<f16x4*>(&sm.c.P[0][r64_off(row, pperm(c0))]) = h;

@@ -71,6 +71,7 @@ __device__ inline bool token_in_span(const FwdKernelArgs& a, int N, int tok) {
 constexpr uint32_t kErrLdsWait = 1u;      // a bounded LDS-counter wait gave up
 constexpr uint32_t kErrFlagWait = 2u;     // a bounded wait on another workgroup gave up
 constexpr uint32_t kErrSavedStamp = 4u;   // saved buffer written under another policy or shape
+constexpr uint32_t kErrPRange = 8u;       // a masked Q K^T entry beyond the fp16 range
 
 // The policy and shape a forward wrote its saved buffer under; the backward
 // compares it with its own arguments on the device.

@@ -37,6 +37,12 @@ WORKLOADS = {
                                            dtype='bf16', gate='softplus', shift=0.0, h0=True,
                                            state_fmt=FMT_E4M3, w_fmt=FMT_E4M3, block_v=64,
                                            bwd=True),
+    # decode continuation: 257-token trajectories, a 64-token chunk prefill,
+    # then token-state writes
+    'decode_e4m3_b4_t257_p64_h16_d128': dict(B=4, T=257, Hqk=16, Hv=16, Dk=128, Dv=128,
+                                             dtype='bf16', gate='softplus', shift=0.0, h0=True,
+                                             state_fmt=FMT_E4M3, w_fmt=FMT_E4M3, block_v=64,
+                                             bwd=True, prefix_len=64),
 }
 
 # The five workloads in the order the parity suite and the bench refer to them.

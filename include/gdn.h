@@ -349,13 +349,23 @@ int32_t gdn_abi_version(void);
  *   GDN_DEVERR_LDS_WAIT     a bounded wait for another wave of the same
  *                           workgroup gave up (its outputs are not valid);
  *   GDN_DEVERR_FLAG_WAIT    a bounded wait for another workgroup gave up;
- *   GDN_DEVERR_SAVED_STAMP  gdn_chunk_bwd got a saved buffer written under
- *                           another policy or shape (its gradients are NaN).
+ *   GDN_DEVERR_SAVED_STAMP  gdn_chunk_bwd (or gdn_decode_bwd) got a saved
+ *                           buffer written under another policy or shape
+ *                           (its gradients are NaN);
+ *   GDN_DEVERR_P_RANGE      with both QDQ sites on (state_fmt and w_fmt not
+ *                           OFF, block_v <= 64, bf16 inputs) the forward
+ *                           keeps the masked Q K^T operand, (q_i . k_j)
+ *                           exp(gamma_i - gamma_j), in fp16 (11-bit
+ *                           significand, range +-65504). Precondition:
+ *                           |q_i . k_j| < 65504, which L2-normalised q and k
+ *                           (GatedDeltaNet's) always meet. An entry beyond
+ *                           it sets this flag (o and ht are then invalid).
  * Diagnostic query: unlike every other entry point it synchronizes the
  * device, then writes the flags to *flags and clears them. */
 #define GDN_DEVERR_LDS_WAIT 1u
 #define GDN_DEVERR_FLAG_WAIT 2u
 #define GDN_DEVERR_SAVED_STAMP 4u
+#define GDN_DEVERR_P_RANGE 8u
 gdn_status gdn_device_errors(uint32_t* flags);
 
 #ifdef __cplusplus

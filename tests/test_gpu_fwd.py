@@ -209,3 +209,20 @@ def test_fwd_qdq_effect_visible_and_tracked():
     r_eff = rel(o_q, o_off)
     say(f"  gpu vs oracle {r_gpu:.3e}; qdq effect {r_eff:.3e}")
     assert r_eff > 5 * r_gpu
+
+
+def test_fwd_fp16_operand_range_is_checked():
+    """With both QDQ sites on, the masked Q K^T operand is kept in fp16; an
+    entry beyond its +-65504 range (q . k that large: unnormalised inputs)
+    raises the device error flag instead of passing an infinity on silently.
+    Normalised inputs of the same shape raise nothing."""
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=1, T=128, Hqk=1, Hv=1)
+    x = draw(spec, 77)
+    assert B.device_errors() == 0
+    gpu_fwd(x, spec)
+    assert B.device_errors() == 0
+    big = dict(x)
+    big["q"] = (x["q"].float() * 1000.0).to(torch.bfloat16).contiguous()
+    big["k"] = (x["k"].float() * 1000.0).to(torch.bfloat16).contiguous()
+    gpu_fwd(big, spec)
+    assert B.device_errors() == B.DEVERR_P_RANGE
