@@ -168,8 +168,11 @@ def _stats(xs):
 
 
 def time_fwd(spec, seed, steps, warmup, flush):
-    """Per-step stage times (ms) of the forward on one workload, flushing the
-    last-level cache before each step (outside the timed events)."""
+    """Per-step times (ms) of the forward on one workload, flushing the
+    last-level cache before each step (outside the timed events): `total`
+    times gdn_chunk_fwd (the overlapped schedule where it applies); `prep`
+    and `state` time the two stages run one after the other, for the
+    per-kernel rooflines, and `serial` their sum."""
     import torch
 
     import gdn_inputs
@@ -179,25 +182,34 @@ def time_fwd(spec, seed, steps, warmup, flush):
     plan = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], scale=1.0 / math.sqrt(spec['Dk']),
                      h0=x['h0'], cu_seqlens=x['cu_seqlens'], **kw)
     for _ in range(warmup):
+        plan.forward()
         plan.prep()
         plan.state()
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         flush.fill_(i & 0xFF)
         ev[i][0].record(stream)
-        plan.prep()
+        plan.forward()
         ev[i][1].record(stream)
-        plan.state()
-        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prep = [e[0].elapsed_time(e[1]) for e in ev]
-    state = [e[1].elapsed_time(e[2]) for e in ev]
-    total = [e[0].elapsed_time(e[2]) for e in ev]
-    return dict(total=_stats(total), prep=_stats(prep), state=_stats(state), wall_s=wall)
+    for i in range(steps):
+        flush.fill_((i + 1) & 0xFF)
+        ev[i][2].record(stream)
+        plan.prep()
+        ev[i][3].record(stream)
+        plan.state()
+        ev[i][4].record(stream)
+    torch.cuda.synchronize()
+    total = [e[0].elapsed_time(e[1]) for e in ev]
+    prep = [e[2].elapsed_time(e[3]) for e in ev]
+    state = [e[3].elapsed_time(e[4]) for e in ev]
+    serial = [e[2].elapsed_time(e[4]) for e in ev]
+    return dict(total=_stats(total), prep=_stats(prep), state=_stats(state), serial=_stats(serial),
+                wall_s=wall)
 
 
 def fwd_record(name, spec, t, state_kernel):
@@ -218,7 +230,7 @@ def fwd_record(name, spec, t, state_kernel):
     traffic = measured_traffic(dom, name)
     return dict(
         workload=name, tokens=tokens, ms=t['total'], tokens_per_s=tokens / (tot * 1e-3),
-        kernel_ms=dict(prep=t['prep'], state=t['state']),
+        kernel_ms=dict(prep=t['prep'], state=t['state']), serial_ms=t['serial'],
         roofline=dict(bound='mfma', achieved=ach, peak=PEAK_BF16_TFLOPS, unit='TFLOP/s',
                       frac=ach / PEAK_BF16_TFLOPS, traffic=traffic, kernel=dom),
         roofline_path=dict(bound='mfma', achieved=path, peak=PEAK_BF16_TFLOPS, unit='TFLOP/s',
@@ -399,7 +411,7 @@ def main():
                     w_qdq=['off', 'e4m3', 'int8'][spec['w_fmt']], block_v=spec['block_v'],
                     parallelism='1gpu'),
         roofline=head['roofline'], roofline_path=head['roofline_path'],
-        kernel_ms=head['kernel_ms'], gflop_per_step=head['gflop'],
+        kernel_ms=head['kernel_ms'], ms_serial_stages=head['serial_ms'], gflop_per_step=head['gflop'],
         hbm_gbs_algorithmic=head['hbm_gbs_algorithmic'],
         whole_forward_traffic=dict(
             bytes_algorithmic=bytes_algorithmic(spec),

@@ -90,6 +90,8 @@ def load_library():
         f = getattr(lib, name)
         f.argtypes = argt
         f.restype = c_i32
+    lib.gdn_fwd_schedule.argtypes = [ctypes.POINTER(FwdArgs), c_i32, ctypes.POINTER(c_i32)]
+    lib.gdn_fwd_schedule.restype = c_i32
     lib.gdn_device_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     lib.gdn_device_errors.restype = c_i32
     lib.gdn_saved_bytes.argtypes = [ctypes.POINTER(FwdArgs)]
@@ -118,6 +120,15 @@ def _check(status):
 
 
 DEVERR_LDS_WAIT, DEVERR_FLAG_WAIT, DEVERR_SAVED_STAMP, DEVERR_P_RANGE = 1, 2, 4, 8
+
+
+def fwd_schedule(args, cus=0):
+    """gdn_fwd_schedule: the schedule gdn_chunk_fwd takes for these FwdArgs on
+    a device of `cus` CUs (0: the current one), as a dict (overlapped, items,
+    head_items, rest_blocks)."""
+    out = (c_i32 * 4)()
+    _check(load_library().gdn_fwd_schedule(ctypes.byref(args), cus, out))
+    return dict(overlapped=bool(out[0]), items=out[1], head_items=out[2], rest_blocks=out[3])
 
 
 def device_errors():
@@ -232,10 +243,13 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None
 class FwdPlan:
     """Forward arguments, outputs and workspace prepared once, for running
     the two forward stages (prep, state) as separate calls on the current
-    stream: plan.prep(); plan.state(). Outputs: plan.o, plan.ht."""
+    stream: plan.prep(); plan.state(), or both in one call: plan.forward().
+    Outputs: plan.o, plan.ht, and plan.saved (the backward's saved buffer)
+    with save=True."""
 
     def __init__(self, q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None,
-                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0, read_fmt=QDQ_OFF):
+                 state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0, read_fmt=QDQ_OFF,
+                 save=False):
         lib = load_library()
         dev = q.device
         B, T, Hqk, Dk = q.shape
@@ -247,11 +261,24 @@ class FwdPlan:
         self.args = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt,
                                   block_v, self.o, self.ht, solve_degree=solve_degree,
                                   read_fmt=read_fmt)
+        self.saved = None
+        if save:
+            self.saved = torch.empty(lib.gdn_saved_bytes(ctypes.byref(self.args)), dtype=torch.uint8,
+                                     device=dev)
+            self.args.saved = _ptr(self.saved)
         wbytes = lib.gdn_fwd_workspace_bytes(ctypes.byref(self.args))
         self.ws = torch.empty(wbytes, dtype=torch.uint8, device=dev) if wbytes else None
         self.args.workspace = _ptr(self.ws)
         self.args.workspace_bytes = wbytes
         self.dev = dev
+
+    def forward(self):
+        """The whole forward in one call (gdn_chunk_fwd: the overlapped
+        schedule where it applies)."""
+        _check(load_library().gdn_chunk_fwd(ctypes.byref(self.args), _stream(self.dev)))
+
+    def schedule(self, cus=0):
+        return fwd_schedule(self.args, cus)
 
     def prep(self):
         _check(load_library().gdn_chunk_fwd_prep(ctypes.byref(self.args), _stream(self.dev)))

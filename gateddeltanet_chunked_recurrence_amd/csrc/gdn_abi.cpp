@@ -4,6 +4,7 @@
 // forwards to the HIP launchers. It allocates nothing and never synchronizes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -189,7 +190,7 @@ gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
 // sections: the operand image block [W planes | K^T | P] (bf16), U and the W
 // scale (FP32).
 struct FwdWsLayout {
-  int64_t img, u, wscale, total;
+  int64_t img, u, wscale, flags, total;
 };
 
 template <int DK>
@@ -201,6 +202,7 @@ FwdWsLayout fwd_ws_layout_dk(const gdn_fwd_args* a, int64_t nch) {
   w.img = off;     off += round256(nch * img * 2);
   w.u = off;       off += round256(nch * (int64_t)a->Dv * 64 * 4);
   w.wscale = off;  off += round256(nch * 4);
+  w.flags = off;   off += round256(nch * 4 + 8);    // ready flags and two item counters of the overlapped forward
   w.total = off;
   return w;
 }
@@ -364,6 +366,118 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a) {
 namespace {
 
 // Stages of the forward: 1 = prep (every chunk and head), 2 = state recurrence.
+// ------------------------------------------------------- overlapped forward
+// With equal-length sequences and both QDQ sites on (the split state
+// kernel), the state kernel's U = N Hv Dv / 64 workgroups leave CUs idle.
+// The forward then takes the prep items in chunk-major order (chunk c of
+// every sequence and head before chunk c + 1): the first H on every CU, on
+// the caller's stream; then the state kernel there, and at the same time the
+// remaining items on the R = CUs - U CUs it leaves, on a second stream of
+// the library's, each publishing a ready flag per (chunk slot, head) that
+// the state kernel waits for. H makes the remainder take about as long as
+// the state chain: with per-item prep time t_item ~ 3.7 t_chunk (the
+// measured per-chunk state step), H = items - R chunks t_chunk / t_item,
+// rounded to whole rounds of CUs items. The kernels, their arithmetic and its
+// order are those of the serial schedule, so the results are the same bits.
+struct OverlapPlan {
+  int items = -1;             // -1: run serially
+  int head = 0, rest_blocks = 0, c_split = 0;
+};
+
+// with both QDQ sites on, the state kernel widens the W codes itself, so the
+// images carry them as bytes (the split state kernel, which takes them, spans
+// 64 columns: scale tiles up to 64 wide)
+int w_img_bytes_of(const gdn_fwd_args* a) {
+  return (a->policy.state_fmt != GDN_QDQ_OFF && a->policy.w_fmt != GDN_QDQ_OFF &&
+          a->policy.block_v <= 64) ? 1 : 0;
+}
+
+OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
+  OverlapPlan op;
+  if (!w_img_bytes_of(a) || a->cu_seqlens || a->io_dtype != GDN_BF16 || a->policy.read_fmt != 0)
+    return op;
+  const int len = a->prefix_len > 0 ? std::min(a->T, a->prefix_len) : a->T;
+  const int maxc = (len + 63) / 64;
+  const int64_t nh = (int64_t)a->num_seqs * a->Hv;
+  const int64_t units = nh * (a->Dv / 64);                  // state workgroups
+  const int64_t rest = cus - units;
+  if (maxc < 4 || rest < 16) return op;
+  const int64_t items = (int64_t)maxc * nh;
+  const double h = (double)items - (double)rest * maxc / 3.7;
+  const int64_t head = h <= 0.0 ? 0 : (int64_t)(h / cus + 0.5) * cus;
+  if (head >= items) return op;
+  op.items = (int)items;
+  op.head = (int)head;
+  op.rest_blocks = (int)rest;
+  op.c_split = (int)(head / nh);        // chunks the head covers whole
+  return op;
+}
+
+// Per-device second stream and fork / join events, created once. The record /
+// wait sequence of one call runs under the device's lock, so host threads
+// calling at once do not interleave on the shared events.
+struct OverlapRes {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ok = false, tried = false;
+  std::mutex mu;
+};
+OverlapRes* overlap_res() {
+  static OverlapRes res[64];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  OverlapRes& r = res[dev];
+  if (!r.tried) {
+    r.tried = true;
+    // both streams are on this device: a device-scope release orders them,
+    // without the system-scope write-back of the device's L2 per event
+    constexpr unsigned kFlags = hipEventDisableTiming | hipEventReleaseToDevice;
+    r.ok = hipStreamCreateWithFlags(&r.s2, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&r.fork, kFlags) == hipSuccess &&
+           hipEventCreateWithFlags(&r.join, kFlags) == hipSuccess;
+  }
+  return r.ok ? &r : nullptr;
+}
+
+hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn::FwdKernelArgs k,
+                          const OverlapPlan& op, char* flags_mem, hipStream_t st) {
+  OverlapRes* r = overlap_res();
+  if (!r) return hipErrorNotReady;
+  const int num_slots = (int)layout_of(a).num_slots;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(flags_mem);
+  const int64_t nflags = (int64_t)num_slots * a->Hv;
+  hipError_t e = gdn::launch_fill_u32(flags, nflags + 2, 0u, st);   // flags and two item counters
+  if (e != hipSuccess) return e;
+  gdn::FwdKernelArgs prep = k;
+  prep.chunk_major = 1;
+  prep.flags = flags;
+  if (op.head > 0) {
+    // the head ends before the state kernel starts: its flags (read only in
+    // a chunk it covers in part) need no device-scope stores
+    prep.item_lo = 0;
+    prep.item_hi = op.head;
+    prep.ticket = flags + nflags;
+    if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, st)) != hipSuccess) return e;
+  }
+  prep.item_lo = op.head;
+  prep.item_hi = op.items;
+  prep.ticket = flags + nflags + 1;
+  prep.publish = 1;
+  prep.prep_blocks = op.rest_blocks;
+  gdn::FwdKernelArgs state = k;
+  state.flags = flags;
+  state.c_split = op.c_split;
+  std::lock_guard<std::mutex> lk(r->mu);
+  if ((e = hipEventRecord(r->fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(r->s2, r->fork, 0)) != hipSuccess) return e;
+  if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, r->s2)) != hipSuccess) return e;
+  if ((e = hipEventRecord(r->join, r->s2)) != hipSuccess) return e;
+  if ((e = gdn::launch_fwd_state(cfg, state, st)) != hipSuccess) return e;
+  return hipStreamWaitEvent(st, r->join, 0);
+}
+
 // noalloc: the workspace is the library's `scratch` array instead of the
 // caller's (a->workspace and a->workspace_bytes are not read).
 gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages, bool noalloc = false) {
@@ -405,13 +519,15 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages, boo
   k.ws_img = reinterpret_cast<__bf16*>(ws + W.img);
   k.ws_u = reinterpret_cast<float*>(ws + W.u);
   k.ws_wscale = reinterpret_cast<float*>(ws + W.wscale);
-  // with both QDQ sites on, the state kernel widens the W codes itself, so
-  // the images carry them as bytes
-  // (the split state kernel, which takes them, spans 64 columns: scale tiles
-  // up to 64 wide)
-  k.w_img_bytes = (a->policy.state_fmt != GDN_QDQ_OFF && a->policy.w_fmt != GDN_QDQ_OFF &&
-                   a->policy.block_v <= 64) ? 1 : 0;
+  k.w_img_bytes = w_img_bytes_of(a);
   k.solve_degree = a->policy.solve_degree;
+  if (stages == 3 && !noalloc) {
+    const OverlapPlan op = overlap_plan(a, gdn::device_cus());
+    // (without the second stream the same kernels run one after the other)
+    if (op.items >= 0 && overlap_res())
+      return hip_status(run_overlapped(a, cfg, k, op, ws + W.flags, st),
+                        "gdn_chunk_fwd overlapped launch");
+  }
   if (stages & 1) {
     const int num_slots = (int)layout_of(a).num_slots;
     s = hip_status(gdn::launch_fwd_prep(cfg, k, num_slots, st), "gdn_chunk_fwd prep launch");
@@ -568,6 +684,19 @@ gdn_status gdn_chunk_fwd_prep(const gdn_fwd_args* a, void* stream) {
 }
 gdn_status gdn_chunk_fwd_state(const gdn_fwd_args* a, void* stream) {
   return chunk_fwd_stages(a, stream, 2);
+}
+
+gdn_status gdn_fwd_schedule(const gdn_fwd_args* a, int32_t cus, int32_t* out) {
+  gdn_status s = check_fwd_shape(a);
+  if (s != GDN_OK) return s;
+  if (!out) return fail(GDN_E_INVALID, "out is NULL");
+  if (cus < 0) return fail(GDN_E_INVALID, "cus %d < 0", cus);
+  const OverlapPlan op = overlap_plan(a, cus > 0 ? cus : gdn::device_cus());
+  out[0] = op.items >= 0 ? 1 : 0;
+  out[1] = op.items >= 0 ? op.items : 0;
+  out[2] = op.head;
+  out[3] = op.rest_blocks;
+  return GDN_OK;
 }
 
 size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a) {

@@ -118,6 +118,28 @@ __device__ __forceinline__ void lower_tiles(int wave, int (&ti)[2], int (&tj)[2]
   tj[1] = tab[wave][3];
 }
 
+// Stores of the operand images, U and the W scale. With a concurrent state
+// kernel (flags set) they are device-scope stores (sc1: written through to
+// the device's coherence point, leaving no dirty L2 line behind), so waiting
+// for them (vmcnt) before the item's ready flag makes them visible on every
+// XCD; a release fence would instead write back the whole L2 (buffer_wbl2),
+// which took about 40 us per item. Otherwise plain stores.
+__device__ __forceinline__ void st_out(float* p, float v, bool coh) {
+  if (coh) __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+// 16 bytes at base + off (base wave-uniform): a device-scope buffer store
+// (one instruction, cache policy sc1) or a plain store.
+__device__ __forceinline__ void st_out16(void* base, int off, u32x4 v, bool coh) {
+  if (coh) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFF0, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 16);
+  } else {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off) = v;
+  }
+}
+
 // Writes 4 consecutive bf16 at dst (8-byte aligned).
 __device__ __forceinline__ void st4(bf16* dst, bf16 a, bf16 b, bf16 c, bf16 d) {
   *reinterpret_cast<bf16x4*>(dst) = bf16x4{a, b, c, d};
@@ -211,6 +233,18 @@ __device__ PrepItem prep_item(const FwdKernelArgs& a, int N, int i) {
   // wave-uniform, so these become scalar loads, which no vector-memory wait
   // covers (a vector load here made every item start by waiting for the
   // previous item's stores)
+  if (a.chunk_major) {
+    // equal-length sequences, chunk c of every (sequence, head) before chunk
+    // c + 1 (the overlapped forward): item = (c N + n) Hv + h
+    const int nh = N * a.Hv, c = i / nh, r = i - c * nh, n = r / a.Hv;
+    const int len = a.prefix_len > 0 ? min(a.T, a.prefix_len) : a.T;
+    it.h = r - n * a.Hv;
+    it.slot = n + (n * a.T) / CHUNK + c;
+    it.t0 = n * a.T + CHUNK * c;
+    it.valid = CHUNK * c < len;
+    it.nc = it.valid ? min(CHUNK, len - CHUNK * c) : 0;
+    return it;
+  }
   if (!a.cu_seqlens && a.T % CHUNK == 0) {
     // equal lengths: T / 64 chunk slots and one spare slot per sequence
     const int per = a.T / CHUNK + 1, n = it.slot / per, c = it.slot - n * per;
@@ -261,7 +295,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
   __shared__ __align__(16) PrepSmem<DK> sm;
 
   const int Hv = a.Hv, Hqk = a.Hqk;
-  const int total = num_slots * Hv;
+  const int total = a.item_hi > 0 ? a.item_hi : num_slots * Hv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int lane = fresh_lane(), tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
   // per-lane LDS addresses are rebuilt in each phase, not kept live across the
@@ -289,14 +323,40 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
             it.nc, wave, lane);
   };
 
-  PrepItem cur = next_item(a, N, blockIdx.x, gridDim.x, total);
+  // Items in a fixed stride per workgroup, or (publishing to a concurrent
+  // state kernel) from a shared counter: then the workgroups that are
+  // resident take the lowest items left, whatever else occupies the device,
+  // so the state kernel never waits on an item no running workgroup holds.
+  __shared__ int tk_next;
+  const bool dyn = a.ticket != nullptr;
+  auto take = [&]() -> int {                       // tid 0: the next item, or -1
+    const int t = a.item_lo + (int)atomicAdd(a.ticket, 1u);
+    return t < total ? t : -1;
+  };
+  PrepItem cur;
+  if (dyn) {
+    if (threadIdx.x == 0) tk_next = take();
+    __syncthreads();
+    const int i0 = tk_next;
+    cur = i0 >= 0 ? prep_item(a, N, i0) : PrepItem{};
+    if (i0 < 0) cur.valid = false;
+    __syncthreads();                               // every wave has read it before the next ticket
+  } else {
+    cur = next_item(a, N, a.item_lo + blockIdx.x, gridDim.x, total);
+  }
   if (!cur.valid) return;
   load_kqg(cur);
   load_v(cur);
 
   while (true) {
     GDN_REFRESH();
-    const PrepItem nxt = next_item(a, N, cur.i + gridDim.x, gridDim.x, total);
+    PrepItem nxt;
+    if (dyn) {
+      nxt.valid = false;
+      if (tid == 0) tk_next = take();              // read after this item's first barrier
+    } else {
+      nxt = next_item(a, N, cur.i + gridDim.x, gridDim.x, total);
+    }
     const int h = cur.h, t0 = cur.t0, nc = cur.nc;
     const int64_t ch = (int64_t)cur.slot * Hv + h;
     bf16* img = a.ws_img + ch * I::template img<NW>();   // [W planes | K^T | P | gates]
@@ -323,13 +383,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       // the gate block follows the single fp16 P plane in the byte variant
       const int goff = a.w_img_bytes ? I::template p_at<NW>() + I::P1 : I::template g_at<NW>();
       float* G = reinterpret_cast<float*>(img + goff);
-      G[lane] = eg;
-      G[64 + lane] = lane < nc ? fexp2(g2n - g2) : 0.f;
-      if (lane != 1) G[128 + lane] = lane == 0 ? fexp2(g2n) : 0.f;   // [129]: the W scale, below
-      G[192 + lane] = 0.f;
+      const bool coh = a.publish != 0;
+      st_out(G + lane, eg, coh);
+      st_out(G + 64 + lane, lane < nc ? fexp2(g2n - g2) : 0.f, coh);
+      if (lane != 1) st_out(G + 128 + lane, lane == 0 ? fexp2(g2n) : 0.f, coh);   // [129]: the W scale, below
+      st_out(G + 192 + lane, 0.f, coh);
     }
     lds_barrier();
     GDN_REFRESH();
+    if (dyn) {
+      const int i1 = tk_next;
+      if (i1 >= 0) nxt = prep_item(a, N, i1);
+    }
 
     // ---- 2. L (FP32) and P (hi / lo, pperm over columns): 20 tiles over 8 waves.
     // Every tile of a wave shares its key block mj, whose fragments are read
@@ -455,13 +520,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       constexpr int NKP = (I::KT + 2 * I::P1) / 8, NCP = (NKP + NT - 65) / (NT - 64);
       // one P plane in the byte variant: its second slot holds the gate block
       const int nkp = a.w_img_bytes ? (I::KT + I::P1) / 8 : NKP;
-      const uint4* ksrc = reinterpret_cast<const uint4*>(&sm.Kt[0]);
-      const uint4* psrc = reinterpret_cast<const uint4*>(&sm.c.P[0][0]);
-      uint4* kdst = reinterpret_cast<uint4*>(img + I::template kt_at<NW>());
+      const u32x4* ksrc = reinterpret_cast<const u32x4*>(&sm.Kt[0]);
+      const u32x4* psrc = reinterpret_cast<const u32x4*>(&sm.c.P[0][0]);
+      u32x4* kdst = reinterpret_cast<u32x4*>(img + I::template kt_at<NW>());
+      const bool coh = a.publish != 0;
 #pragma unroll
       for (int k = 0; k < NCP; ++k) {
         const int e = t + (NT - 64) * k;
-        if (e < nkp) kdst[e] = e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8];
+        if (e < nkp) st_out16(kdst, 16 * e, e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8], coh);
       }
       for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
         const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
@@ -697,7 +763,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
             acc = mfma(th[m][kk], vbk[kk], acc);
             acc = mfma(tl[m][kk], vbk[kk], acc);
           }
-          *reinterpret_cast<f32x4*>(a.ws_u + u_off(ch, NVB, vb, w4, m, lane)) = acc;
+          st_out16(a.ws_u + u_off(ch, NVB, vb, w4, m, 0), 16 * lane, __builtin_bit_cast(u32x4, acc),
+                   a.publish != 0);
         }
       }
     }
@@ -740,30 +807,37 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         }
       }
       if (tid == 0) {
-        a.ws_wscale[ch] = dW;
+        st_out(a.ws_wscale + ch, dW, a.publish != 0);
         const int goff = a.w_img_bytes ? I::template p_at<NW>() + I::P1 : I::template g_at<NW>();
-        reinterpret_cast<float*>(img + goff)[129] = dW;
+        st_out(reinterpret_cast<float*>(img + goff) + 129, dW, a.publish != 0);
         if (save) a.w_scale[ch] = dW;
       }
     }
     lds_barrier();
     GDN_REFRESH();
     {
-      const uint4* src = reinterpret_cast<const uint4*>(sm.b.W);
-      uint4* dst = reinterpret_cast<uint4*>(img);
+      const u32x4* src = reinterpret_cast<const u32x4*>(sm.b.W);
+      u32x4* dst = reinterpret_cast<u32x4*>(img);
       constexpr int NWP = NW * I::WQ / 8;          // 16-byte pieces of the W planes
       constexpr int NWB = I::WQ / 16;              // ... of the code bytes
+      const bool coh = a.publish != 0;
       if (WF != 0 && a.w_img_bytes) {
 #pragma unroll
         for (int k = 0; k < (NWB + NT - 1) / NT; ++k)
-          if (NWB % NT == 0 || tid + NT * k < NWB) dst[tid + NT * k] = src[tid + NT * k];
+          if (NWB % NT == 0 || tid + NT * k < NWB) st_out16(dst, 16 * (tid + NT * k), src[tid + NT * k], coh);
       } else {
 #pragma unroll
         for (int k = 0; k < (NWP + NT - 1) / NT; ++k)
-          if (NWP % NT == 0 || tid + NT * k < NWP) dst[tid + NT * k] = src[tid + NT * k];
+          if (NWP % NT == 0 || tid + NT * k < NWP) st_out16(dst, 16 * (tid + NT * k), src[tid + NT * k], coh);
       }
     }
+    // publishing to a concurrent state kernel: every wave waits for its
+    // device-scope stores of this item, then after the barrier one flag store
+    if (a.publish) vm_drain();
     lds_barrier();                              // LDS is reused by the next item
+    if (a.flags && tid == 0)
+      __hip_atomic_store(a.flags + (int64_t)cur.slot * Hv + h, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     if (!nxt.valid) break;
     cur = nxt;
   }
@@ -789,8 +863,10 @@ int device_cus() {
 template <int DK, int DV, int WF>
 static hipError_t launch_prep_one(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
                                   hipStream_t s) {
-  const int64_t items = (int64_t)num_slots * cfg.Hv;
-  const int64_t nblk = items < device_cus() ? items : device_cus();   // one workgroup per CU
+  const int64_t items = a.item_hi > 0 ? (int64_t)a.item_hi - a.item_lo : (int64_t)num_slots * cfg.Hv;
+  const int64_t cap = a.prep_blocks > 0 ? a.prep_blocks : device_cus();   // one workgroup per CU
+  const int64_t nblk = items < cap ? items : cap;
+  if (nblk <= 0) return hipSuccess;
   if (a.solve_degree > 0)
     hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
                        cfg.N, num_slots);

@@ -468,7 +468,23 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
         off[k] = 16 * (64 * (j - NI1 - NI2 - NI3) + lane);
       }
     }
+    // chunks the concurrent prep kernel is still producing: wait for their
+    // flags (bounded to about 2^27 clocks per chunk, some 60 ms: on give-up
+    // the error flag is set and the copies go on)
+    auto wait_ready = [&](int c) {
+      if (!a.flags || c < a.c_split) return;
+      uint32_t* f = a.flags + chunk_ch(c);
+      const uint64_t t0 = __builtin_amdgcn_s_memtime();
+      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (__builtin_amdgcn_s_memtime() - t0 > (1ull << 27)) {
+          if (lane == 0) __hip_atomic_fetch_or(a.err, kErrFlagWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    };
     auto dma = [&](int c, int b) {
+      wait_ready(c);
       const int64_t ch = chunk_ch(c);
       const char* img = reinterpret_cast<const char*>(a.ws_img + ch * I::template img<1>());
       const char* u = reinterpret_cast<const char*>(a.ws_u + u_off(ch, NVB, vb, 0, 0, 0));

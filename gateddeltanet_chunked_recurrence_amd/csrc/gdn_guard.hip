@@ -52,7 +52,20 @@ __global__ void check_stamp_kernel(BwdKernelArgs a, SavedStamp want, int64_t n_d
   if (a.dh0) fill_nan(a.dh0, n_h0);
 }
 
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_write_stamp(uint32_t* meta, const SavedStamp& st, hipStream_t s) {
   hipLaunchKernelGGL(write_stamp_kernel, dim3(1), dim3(64), 0, s, meta, st);

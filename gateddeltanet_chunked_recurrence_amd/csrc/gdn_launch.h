@@ -30,6 +30,20 @@ struct FwdKernelArgs {
   float* ws_u;                // [slots * Hv][Dv * 64] fragment order
   float* ws_wscale;           // [slots * Hv]
   int32_t w_img_bytes;        // 1: the W plane of the images holds code bytes (both QDQ sites on)
+  // overlapped forward (gdn_chunk_fwd with equal-length sequences): the prep
+  // kernel runs items [item_lo, item_hi) of the chunk-major order (chunk c of
+  // every sequence and head before chunk c + 1) and, when flags is set,
+  // sets each item's flag [slot * Hv + head] after its outputs; the state
+  // kernel waits for the flag of every chunk c >= c_split
+  uint32_t* flags;            // nullable
+  int32_t publish;            // with flags: a state kernel runs meanwhile, so outputs are stored at
+                              // device scope and drained before the flag
+  uint32_t* ticket;           // nullable: items are taken from this counter (zeroed per call), so
+                              // the resident workgroups always hold the lowest items left
+  int32_t item_lo, item_hi;   // item_hi == 0: every slot-major item [0, slots * Hv)
+  int32_t chunk_major;        // 1: items in chunk-major order (no cu_seqlens)
+  int32_t c_split;            // chunks below this were finished before the state kernel started
+  int32_t prep_blocks;        // prep grid size (0: one workgroup per CU)
   int32_t solve_degree;       // 0: exact (I + L)^-1; else the Neumann polynomial of this degree (2^j - 1)
   int32_t T;                  // tokens per sequence (no cu_seqlens)
   int32_t prefix_len;         // > 0: only the first prefix_len tokens of every sequence
@@ -139,6 +153,9 @@ int bwd_img_elems(int Dk, int w_fmt);
 // chunk (the FP32 carry's gate term, which the backward's products took with
 // the read copy Sr).
 hipError_t launch_bwd_read_anchor(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t s);
+
+// Sets n words to v (a fill kernel: safe under graph capture, unlike a memset node).
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 
 // Writes the stamp into the saved buffer's meta section.
 hipError_t launch_write_stamp(uint32_t* meta, const SavedStamp& st, hipStream_t s);

@@ -34,8 +34,10 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
  *     16-byte aligned. The caller allocates and owns every buffer; the library
- *     allocates nothing, keeps no state between calls, never synchronizes,
- *     and enqueues work only on `stream` (a hipStream_t; NULL = default).
+ *     allocates no device memory, keeps no data between calls, never
+ *     synchronizes, and enqueues work only on `stream` (a hipStream_t;
+ *     NULL = default), except gdn_chunk_fwd's overlapped schedule below, whose
+ *     second stream joins back into `stream` within the call's work.
  *   - Every argument check runs before any launch. A failed check returns a
  *     negative gdn_status, launches nothing and sets a message readable with
  *     gdn_last_error() (thread-local). There is no fallback path.
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum {
   GDN_OK = 0,
@@ -189,8 +191,30 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
 
 /* Chunked forward. Writes o, and ht / saved when not NULL. Needs
  * a->workspace of gdn_fwd_workspace_bytes(a) bytes (GDN_E_WORKSPACE if
- * missing or too small). */
+ * missing or too small).
+ * Overlapped schedule: with bf16 inputs, equal-length sequences (no
+ * cu_seqlens), both QDQ sites on with block_v <= 64 and full-precision reads,
+ * at least 4 chunks per sequence and at least 16 CUs that the state
+ * recurrence's N * Hv * Dv / 64 workgroups leave free, the state recurrence
+ * starts once the first chunks' operands are built, and the remaining ones
+ * are built meanwhile on those free CUs, from a second stream that the
+ * library creates on the device's first such call (with two events, kept
+ * until the process ends). Later work on `stream` waits for both. The
+ * kernels, their arithmetic and its order are those of gdn_chunk_fwd_prep
+ * then gdn_chunk_fwd_state, so the results are the same bits. Host threads
+ * enqueue it under a per-device lock. Code under HIP graph capture uses
+ * gdn_chunk_fwd_noalloc, which always runs on `stream` alone. */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
+
+/* The schedule gdn_chunk_fwd takes for these arguments on a device of `cus`
+ * compute units (0: the current device's count): out[0] = 1 overlapped,
+ * 0 one stage after the other; out[1] the (chunk, head) items of the
+ * operand build; out[2] how many of them (whole rounds of cus, chunk-major)
+ * run on every CU before the state recurrence starts; out[3] the workgroups
+ * that build the rest meanwhile. Checks the shapes only; launches nothing.
+ * The call itself runs one stage after the other if it cannot create its
+ * second stream. */
+gdn_status gdn_fwd_schedule(const gdn_fwd_args* a, int32_t cus, int32_t* out);
 
 /* gdn_chunk_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation).

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gdn_abi_version() == 7
+    assert lib.gdn_abi_version() == 8
 
 
 def _args(**kw):
@@ -89,6 +89,42 @@ def test_forward_rejects_before_launch(kw, status, msg):
     assert msg in lib.gdn_last_error().decode()
 
 
+def test_forward_schedule_host_logic():
+    """gdn_fwd_schedule: where gdn_chunk_fwd overlaps the operand build with
+    the state recurrence, and how it splits the (chunk, head) items. The head
+    is items - R * chunks / 3.7 (R = CUs - N Hv Dv / 64) in whole rounds of
+    CUs; numbers worked by hand here."""
+    big = dict(B=4, T=4096, Hqk=16, Hv=16, num_seqs=4)
+    sch = B.fwd_schedule(_args(**big), 256)
+    # 64 chunks x 64 (sequence, head) pairs; 128 state workgroups leave R = 128;
+    # 4096 - 128 * 64 / 3.7 = 1881.9 -> 7 rounds of 256
+    assert sch == dict(overlapped=True, items=4096, head_items=1792, rest_blocks=128)
+    # 304 CUs: R = 176; 4096 - 176 * 64 / 3.7 = 1051.7 -> 3 rounds of 304
+    assert B.fwd_schedule(_args(**big), 304) == dict(overlapped=True, items=4096, head_items=912,
+                                                      rest_blocks=176)
+    # a long sequence: the remainder alone outlasts the chain, so no head
+    sch = B.fwd_schedule(_args(B=1, T=65536, Hqk=32, Hv=32, Dv=256, num_seqs=1), 256)
+    assert sch == dict(overlapped=True, items=32768, head_items=0, rest_blocks=128)
+    serial = [
+        dict(big, state_fmt=B.QDQ_OFF),                     # no split state kernel
+        dict(big, w_fmt=B.QDQ_OFF),
+        dict(big, block_v=128),
+        dict(big, state_fmt=B.QDQ_OFF, read_fmt=B.QDQ_E4M3),   # two-precision profile
+        dict(big, io_dtype=B.GDN_F32, Dk=64, Dv=64),
+        dict(big, T=192),                                   # 3 chunks
+        dict(big, prefix_len=128),                          # 2 chunks
+        dict(B=2, T=4096, Hqk=32, Hv=32, Dv=256, num_seqs=2),   # 256 state workgroups
+        dict(B=1, T=4096, Hqk=16, Hv=16, num_seqs=2, cu_seqlens=ctypes.c_void_p(0x20000)),
+    ]
+    for kw in serial:
+        sch = B.fwd_schedule(_args(**kw), 256)
+        assert sch['overlapped'] is False, kw
+    with pytest.raises(B.GdnError):
+        B.fwd_schedule(_args(**big), -1)
+    with pytest.raises(B.GdnError):
+        B.fwd_schedule(_args(Hv=3), 256)
+
+
 def test_forward_workspace_is_sized_and_required():
     """bf16 inputs need the prep kernel's scratch: its size follows the
     per-(slot, head) image sizes, a missing or short workspace is rejected
@@ -97,9 +133,10 @@ def test_forward_workspace_is_sized_and_required():
     a = _args()
     n = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
     slots = 1 + 2                                       # N + ceil(128 / 64)
-    # W codes, K^T, P hi/lo (bf16, K^T and P rows unpadded), gate block (1 KB), U (FP32), W scale
-    per = 64 * 128 * 2 + 128 * 64 * 2 + 2 * 64 * 64 * 2 + 1024 + 128 * 64 * 4 + 4
-    assert n >= slots * 4 * per and n <= slots * 4 * per + 3 * 256
+    # W codes, K^T, P hi/lo (bf16, K^T and P rows unpadded), gate block (1 KB), U (FP32), W
+    # scale, the ready flag of the overlapped schedule
+    per = 64 * 128 * 2 + 128 * 64 * 2 + 2 * 64 * 64 * 2 + 1024 + 128 * 64 * 4 + 4 + 4
+    assert n >= slots * 4 * per and n <= slots * 4 * per + 4 * 256
     assert lib.gdn_chunk_fwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
     assert 'workspace' in lib.gdn_last_error().decode()
     a.workspace = ctypes.c_void_p(0x40000)

@@ -226,3 +226,40 @@ def test_fwd_fp16_operand_range_is_checked():
     big["k"] = (x["k"].float() * 1000.0).to(torch.bfloat16).contiguous()
     gpu_fwd(big, spec)
     assert B.device_errors() == B.DEVERR_P_RANGE
+
+
+@pytest.mark.parametrize("name,over", [
+    ('fwd_e4m3_b4_t4096_h16_d128', dict()),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=1000, Hqk=4, Hv=8, state_fmt=INT8)),
+    ('long_e4m3_t65536_h32_dk128_dv256', dict(T=8192)),
+    ('fwd_bwd_e4m3_b2_t8192_h16_d128', dict()),
+])
+def test_fwd_overlapped_schedule_equals_serial(name, over):
+    """gdn_chunk_fwd runs the prep's remainder concurrently with the state
+    chain (ready flags per chunk) where the state kernel leaves CUs idle; its
+    outputs and saved buffer equal the serial two-stage schedule bit for bit,
+    and no bounded wait gives up."""
+    import math
+    spec = gdn_inputs.spec(name, **over)
+    x = draw(spec, 31)
+    kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+    sc = 1.0 / math.sqrt(spec['Dk'])
+    o1, h1, s1 = B.gdn_chunk_fwd(x['q'], x['k'], x['v'], x['g'], x['beta'], sc, x['h0'],
+                                 save_for_backward=True, **kw)
+    plan = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], sc, x['h0'], save=True, **kw)
+    assert plan.schedule()['overlapped']
+    plan.saved.zero_()
+    plan.prep()
+    plan.state()
+    torch.cuda.synchronize()
+    assert B.device_errors() == 0
+    assert torch.equal(o1, plan.o) and torch.equal(h1, plan.ht)
+    s_serial = plan.saved.clone()
+    plan.saved.zero_()
+    plan.o.zero_()
+    plan.forward()
+    torch.cuda.synchronize()
+    assert B.device_errors() == 0
+    assert torch.equal(o1, plan.o) and torch.equal(h1, plan.ht)
+    assert torch.equal(s_serial, plan.saved)
+    say(f"  {name} {over}: overlapped == serial")
