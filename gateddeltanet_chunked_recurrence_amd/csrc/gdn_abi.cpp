@@ -369,19 +369,23 @@ namespace {
 // ------------------------------------------------------- overlapped forward
 // With equal-length sequences and both QDQ sites on (the split state
 // kernel), the state kernel's U = N Hv Dv / 64 workgroups leave CUs idle.
-// The forward then takes the prep items in chunk-major order (chunk c of
-// every sequence and head before chunk c + 1): the first H on every CU, on
-// the caller's stream; then the state kernel there, and at the same time the
-// remaining items on the R = CUs - U CUs it leaves, on a second stream of
-// the library's, each publishing a ready flag per (chunk slot, head) that
-// the state kernel waits for. H makes the remainder take about as long as
-// the state chain: with per-item prep time t_item ~ 3.7 t_chunk (the
-// measured per-chunk state step), H = items - R chunks t_chunk / t_item,
-// rounded to whole rounds of CUs items. The kernels, their arithmetic and its
-// order are those of the serial schedule, so the results are the same bits.
+// The forward then runs one prep launch on the caller's stream, taking the
+// (chunk, head) items in chunk-major order (chunk c of every sequence and
+// head before chunk c + 1) from a shared counter: the first H items on every
+// CU; past them, U of its workgroups end and the other R = CUs - U go on
+// with the rest. The state kernel, on a second stream of the library's, is
+// enqueued behind the flag reset only, so it finds every CU held by the prep
+// and starts on the CUs the ending workgroups free, with no kernel boundary
+// in between; it waits for each chunk's ready flags, which every prep item
+// sets after draining its device-scope stores. H makes the remainder on R
+// CUs take about as long as the state chain: with per-item prep time
+// t_item ~ 3.7 t_chunk (the measured per-chunk state step), H = items -
+// R chunks t_chunk / t_item, rounded to whole rounds of CUs items. The
+// kernels, their arithmetic and its order are those of the serial schedule,
+// so the results are the same bits.
 struct OverlapPlan {
   int items = -1;             // -1: run serially
-  int head = 0, rest_blocks = 0, c_split = 0;
+  int head = 0, rest_blocks = 0;
 };
 
 // with both QDQ sites on, the state kernel widens the W codes itself, so the
@@ -409,7 +413,6 @@ OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
   op.items = (int)items;
   op.head = (int)head;
   op.rest_blocks = (int)rest;
-  op.c_split = (int)(head / nh);        // chunks the head covers whole
   return op;
 }
 
@@ -431,9 +434,9 @@ OverlapRes* overlap_res() {
   OverlapRes& r = res[dev];
   if (!r.tried) {
     r.tried = true;
-    // both streams are on this device: a device-scope release orders them,
-    // without the system-scope write-back of the device's L2 per event
-    constexpr unsigned kFlags = hipEventDisableTiming | hipEventReleaseToDevice;
+    // both streams are on this device: the events order them without the
+    // system-scope fences (for the host and other devices) of an event
+    constexpr unsigned kFlags = hipEventDisableTiming | hipEventDisableSystemFence;
     r.ok = hipStreamCreateWithFlags(&r.s2, hipStreamNonBlocking) == hipSuccess &&
            hipEventCreateWithFlags(&r.fork, kFlags) == hipSuccess &&
            hipEventCreateWithFlags(&r.join, kFlags) == hipSuccess;
@@ -448,33 +451,27 @@ hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn:
   const int num_slots = (int)layout_of(a).num_slots;
   uint32_t* flags = reinterpret_cast<uint32_t*>(flags_mem);
   const int64_t nflags = (int64_t)num_slots * a->Hv;
-  hipError_t e = gdn::launch_fill_u32(flags, nflags + 2, 0u, st);   // flags and two item counters
-  if (e != hipSuccess) return e;
   gdn::FwdKernelArgs prep = k;
   prep.chunk_major = 1;
   prep.flags = flags;
-  if (op.head > 0) {
-    // the head ends before the state kernel starts: its flags (read only in
-    // a chunk it covers in part) need no device-scope stores
-    prep.item_lo = 0;
-    prep.item_hi = op.head;
-    prep.ticket = flags + nflags;
-    if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, st)) != hipSuccess) return e;
-  }
-  prep.item_lo = op.head;
-  prep.item_hi = op.items;
-  prep.ticket = flags + nflags + 1;
   prep.publish = 1;
-  prep.prep_blocks = op.rest_blocks;
+  prep.ticket = flags + nflags;
+  prep.item_lo = 0;
+  prep.item_hi = op.items;
+  prep.item_split = op.head;
+  prep.prep_rest = op.rest_blocks;
+  prep.prep_blocks = op.head > 0 ? 0 : op.rest_blocks;   // every CU while there is a head
   gdn::FwdKernelArgs state = k;
   state.flags = flags;
-  state.c_split = op.c_split;
+  state.c_split = 0;
+  // The fork and join events are recorded by the launches themselves, at
+  // their end, with no marker packet of their own.
   std::lock_guard<std::mutex> lk(r->mu);
-  if ((e = hipEventRecord(r->fork, st)) != hipSuccess) return e;
+  hipError_t e = gdn::launch_fill_u32(flags, nflags + 2, 0u, st, r->fork);   // flags, two counters
+  if (e != hipSuccess) return e;
+  if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(r->s2, r->fork, 0)) != hipSuccess) return e;
-  if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, r->s2)) != hipSuccess) return e;
-  if ((e = hipEventRecord(r->join, r->s2)) != hipSuccess) return e;
-  if ((e = gdn::launch_fwd_state(cfg, state, st)) != hipSuccess) return e;
+  if ((e = gdn::launch_fwd_state(cfg, state, r->s2, r->join)) != hipSuccess) return e;
   return hipStreamWaitEvent(st, r->join, 0);
 }
 

@@ -20,6 +20,8 @@
 // Launch: persistent, one 8-wave workgroup per CU (two waves per SIMD), each
 // walking (chunk, head) items in slot-major order and loading the next item's
 // q, k, v, g, beta into registers while it computes the current one.
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -331,7 +333,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
   const bool dyn = a.ticket != nullptr;
   auto take = [&]() -> int {                       // tid 0: the next item, or -1
     const int t = a.item_lo + (int)atomicAdd(a.ticket, 1u);
-    return t < total ? t : -1;
+    if (a.item_split <= 0 || t < a.item_split) return t < total ? t : -1;
+    if ((int)blockIdx.x >= a.prep_rest) return -1;
+    const int r = a.item_split + (int)atomicAdd(a.ticket + 1, 1u);
+    return r < total ? r : -1;
   };
   PrepItem cur;
   if (dyn) {
@@ -862,38 +867,46 @@ int device_cus() {
 
 template <int DK, int DV, int WF>
 static hipError_t launch_prep_one(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
-                                  hipStream_t s) {
+                                  hipStream_t s, hipEvent_t stop) {
   const int64_t items = a.item_hi > 0 ? (int64_t)a.item_hi - a.item_lo : (int64_t)num_slots * cfg.Hv;
   const int64_t cap = a.prep_blocks > 0 ? a.prep_blocks : device_cus();   // one workgroup per CU
   const int64_t nblk = items < cap ? items : cap;
-  if (nblk <= 0) return hipSuccess;
-  if (a.solve_degree > 0)
-    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
-                       cfg.N, num_slots);
-  else
-    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, false>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
-                       cfg.N, num_slots);
+  if (nblk <= 0) return stop ? hipEventRecord(stop, s) : hipSuccess;
+  const dim3 grid((unsigned)nblk), block(NT);
+  if (stop) {
+    if (a.solve_degree > 0)
+      hipExtLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), grid, block, 0, s, nullptr, stop, 0, a,
+                            cfg.N, num_slots);
+    else
+      hipExtLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, false>), grid, block, 0, s, nullptr, stop, 0, a,
+                            cfg.N, num_slots);
+  } else if (a.solve_degree > 0) {
+    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), grid, block, 0, s, a, cfg.N, num_slots);
+  } else {
+    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, false>), grid, block, 0, s, a, cfg.N, num_slots);
+  }
   return hipGetLastError();
 }
 
 template <int DK, int DV>
-static hipError_t launch_prep_w(const FwdConfig& cfg, const FwdKernelArgs& a, int ns, hipStream_t s) {
-  if (cfg.w_fmt == 0) return launch_prep_one<DK, DV, 0>(cfg, a, ns, s);
-  if (cfg.w_fmt == 1) return launch_prep_one<DK, DV, 1>(cfg, a, ns, s);
-  if (cfg.w_fmt == 2) return launch_prep_one<DK, DV, 2>(cfg, a, ns, s);
+static hipError_t launch_prep_w(const FwdConfig& cfg, const FwdKernelArgs& a, int ns, hipStream_t s,
+                                hipEvent_t stop) {
+  if (cfg.w_fmt == 0) return launch_prep_one<DK, DV, 0>(cfg, a, ns, s, stop);
+  if (cfg.w_fmt == 1) return launch_prep_one<DK, DV, 1>(cfg, a, ns, s, stop);
+  if (cfg.w_fmt == 2) return launch_prep_one<DK, DV, 2>(cfg, a, ns, s, stop);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_prep(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
-                           hipStream_t s) {
+                           hipStream_t s, hipEvent_t stop) {
   if (cfg.Dk == 128) {
-    if (cfg.Dv == 64) return launch_prep_w<128, 64>(cfg, a, num_slots, s);
-    if (cfg.Dv == 128) return launch_prep_w<128, 128>(cfg, a, num_slots, s);
-    if (cfg.Dv == 256) return launch_prep_w<128, 256>(cfg, a, num_slots, s);
+    if (cfg.Dv == 64) return launch_prep_w<128, 64>(cfg, a, num_slots, s, stop);
+    if (cfg.Dv == 128) return launch_prep_w<128, 128>(cfg, a, num_slots, s, stop);
+    if (cfg.Dv == 256) return launch_prep_w<128, 256>(cfg, a, num_slots, s, stop);
   } else if (cfg.Dk == 64) {
-    if (cfg.Dv == 64) return launch_prep_w<64, 64>(cfg, a, num_slots, s);
-    if (cfg.Dv == 128) return launch_prep_w<64, 128>(cfg, a, num_slots, s);
-    if (cfg.Dv == 256) return launch_prep_w<64, 256>(cfg, a, num_slots, s);
+    if (cfg.Dv == 64) return launch_prep_w<64, 64>(cfg, a, num_slots, s, stop);
+    if (cfg.Dv == 128) return launch_prep_w<64, 128>(cfg, a, num_slots, s, stop);
+    if (cfg.Dv == 256) return launch_prep_w<64, 256>(cfg, a, num_slots, s, stop);
   }
   return hipErrorInvalidValue;
 }

@@ -499,8 +499,10 @@ static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
-  if (a.w_img_bytes) return launch_fwd_state_split(cfg, a, s);
+hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                            hipEvent_t stop) {
+  if (a.w_img_bytes) return launch_fwd_state_split(cfg, a, s, stop);
+  if (stop) return hipErrorInvalidValue;           // only the split kernel runs beside the prep
   if (cfg.Dk == 128) return launch_state_dk<128>(cfg, a, s);
   if (cfg.Dk == 64) return launch_state_dk<64>(cfg, a, s);
   return hipErrorInvalidValue;

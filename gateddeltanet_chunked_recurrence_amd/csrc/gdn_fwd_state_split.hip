@@ -32,6 +32,8 @@
 // leave as one 8-byte store. Sc^T Q^T contracts over dk in natural order (Q
 // rows are copied unpermuted, 16-byte pieces XOR-swizzled by row); the
 // recurrence waves publish the codes in that order.
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -525,27 +527,34 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
 }  // namespace
 
 template <int DK, int SF, int WF>
-static hipError_t launch_split_one(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+static hipError_t launch_split_one(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                                   hipEvent_t stop) {
   const int num_heads = cfg.N * cfg.Hv, nvb = cfg.Dv / 64;
   const int64_t nblk = (int64_t)nvb * 8 * ((num_heads + 7) / 8);
-  hipLaunchKernelGGL((gdn_state_split_kernel<DK, SF, WF>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
-                     cfg.N, num_heads);
+  if (stop)
+    hipExtLaunchKernelGGL((gdn_state_split_kernel<DK, SF, WF>), dim3((unsigned)nblk), dim3(NT), 0, s,
+                          nullptr, stop, 0, a, cfg.N, num_heads);
+  else
+    hipLaunchKernelGGL((gdn_state_split_kernel<DK, SF, WF>), dim3((unsigned)nblk), dim3(NT), 0, s, a,
+                       cfg.N, num_heads);
   return hipGetLastError();
 }
 
 template <int DK>
-static hipError_t launch_split_dk(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+static hipError_t launch_split_dk(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                                  hipEvent_t stop) {
 #define GDN_CASE(SFv, WFv) \
-  if (cfg.state_fmt == SFv && cfg.w_fmt == WFv) return launch_split_one<DK, SFv, WFv>(cfg, a, s);
+  if (cfg.state_fmt == SFv && cfg.w_fmt == WFv) return launch_split_one<DK, SFv, WFv>(cfg, a, s, stop);
   GDN_CASE(1, 1) GDN_CASE(1, 2) GDN_CASE(2, 1) GDN_CASE(2, 2)
 #undef GDN_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                                  hipEvent_t stop) {
   if (!a.w_img_bytes) return hipErrorInvalidValue;   // its images carry W as code bytes
-  if (cfg.Dk == 128) return launch_split_dk<128>(cfg, a, s);
-  if (cfg.Dk == 64) return launch_split_dk<64>(cfg, a, s);
+  if (cfg.Dk == 128) return launch_split_dk<128>(cfg, a, s, stop);
+  if (cfg.Dk == 64) return launch_split_dk<64>(cfg, a, s, stop);
   return hipErrorInvalidValue;
 }
 

@@ -6,6 +6,8 @@
 // error word records it, so a wrong pairing never passes silently ("[7/7]
 // Experimental GDN/KDA approximate-inverse QAT", "What does this PR do?": no
 // silent change of degree and no fallback).
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -60,10 +62,13 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 
 }  // namespace
 
-hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s, hipEvent_t stop) {
+  if (n <= 0) return stop ? hipEventRecord(stop, s) : hipSuccess;
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  if (stop)
+    hipExtLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, nullptr, stop, 0, p, n, v);
+  else
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

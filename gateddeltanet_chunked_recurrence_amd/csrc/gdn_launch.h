@@ -39,7 +39,11 @@ struct FwdKernelArgs {
   int32_t publish;            // with flags: a state kernel runs meanwhile, so outputs are stored at
                               // device scope and drained before the flag
   uint32_t* ticket;           // nullable: items are taken from this counter (zeroed per call), so
-                              // the resident workgroups always hold the lowest items left
+                              // the resident workgroups always hold the lowest items left; with
+                              // item_split > 0, [0] over items below item_split (every workgroup),
+                              // then [1] over the rest (only workgroups below prep_rest: the
+                              // others end, and free their CUs)
+  int32_t item_split, prep_rest;
   int32_t item_lo, item_hi;   // item_hi == 0: every slot-major item [0, slots * Hv)
   int32_t chunk_major;        // 1: items in chunk-major order (no cu_seqlens)
   int32_t c_split;            // chunks below this were finished before the state kernel started
@@ -103,11 +107,15 @@ struct FwdConfig {
 // FP32 io (Dk = 64): one fused kernel per (sequence, head, value block).
 hipError_t launch_fwd_fused(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
 // bf16 io: prep kernel over every (chunk, head), then the state kernel.
+// stop (nullable): an event that the launch itself records at its end, with
+// no marker of its own on the stream
 hipError_t launch_fwd_prep(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
-                           hipStream_t stream);
-hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
+                           hipStream_t stream, hipEvent_t stop = nullptr);
+hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream,
+                            hipEvent_t stop = nullptr);
 // Both QDQ sites on: recurrence and output in separate waves (gdn_fwd_state_split.hip).
-hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream);
+hipError_t launch_fwd_state_split(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream,
+                                  hipEvent_t stop = nullptr);
 
 struct BwdKernelArgs {
   FwdKernelArgs f;            // forward inputs + saved buffers (read only here)
@@ -155,7 +163,7 @@ int bwd_img_elems(int Dk, int w_fmt);
 hipError_t launch_bwd_read_anchor(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t s);
 
 // Sets n words to v (a fill kernel: safe under graph capture, unlike a memset node).
-hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s, hipEvent_t stop = nullptr);
 
 // Writes the stamp into the saved buffer's meta section.
 hipError_t launch_write_stamp(uint32_t* meta, const SavedStamp& st, hipStream_t s);

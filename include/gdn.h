@@ -197,13 +197,15 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
  * at least 4 chunks per sequence and at least 16 CUs that the state
  * recurrence's N * Hv * Dv / 64 workgroups leave free, the state recurrence
  * starts once the first chunks' operands are built, and the remaining ones
- * are built meanwhile on those free CUs, from a second stream that the
- * library creates on the device's first such call (with two events, kept
- * until the process ends). Later work on `stream` waits for both. The
- * kernels, their arithmetic and its order are those of gdn_chunk_fwd_prep
- * then gdn_chunk_fwd_state, so the results are the same bits. Host threads
- * enqueue it under a per-device lock. Code under HIP graph capture uses
- * gdn_chunk_fwd_noalloc, which always runs on `stream` alone. */
+ * are built meanwhile on those free CUs. The operand build runs on `stream`;
+ * the state recurrence runs on a second stream that the library creates on
+ * the device's first such call (with two events, kept until the process
+ * ends), forked from `stream` and joined back into it, so later work on
+ * `stream` waits for both. The kernels, their arithmetic and its order are
+ * those of gdn_chunk_fwd_prep then gdn_chunk_fwd_state, so the results are
+ * the same bits. Host threads enqueue it under a per-device lock. Code under
+ * HIP graph capture uses gdn_chunk_fwd_noalloc, which always runs on
+ * `stream` alone. */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
 
 /* The schedule gdn_chunk_fwd takes for these arguments on a device of `cus`

@@ -263,3 +263,31 @@ def test_fwd_overlapped_schedule_equals_serial(name, over):
     assert torch.equal(o1, plan.o) and torch.equal(h1, plan.ht)
     assert torch.equal(s_serial, plan.saved)
     say(f"  {name} {over}: overlapped == serial")
+
+
+def test_fwd_overlapped_reads_no_stale_workspace():
+    """The overlapped forward reads each chunk's operands after its ready
+    flag: with the workspace still holding another input's operands from the
+    call before, every call equals the serial schedule on its own input."""
+    import math
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=2, T=2048)
+    xs = [draw(spec, 41), draw(spec, 42)]
+    kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+    sc = 1.0 / math.sqrt(spec['Dk'])
+    ref = []
+    for x in xs:
+        p = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], sc, x['h0'], **kw)
+        p.prep()
+        p.state()
+        ref.append((p.o.clone(), p.ht.clone()))
+    live = {n: xs[0][n].clone() for n in ('q', 'k', 'v', 'g', 'beta')}
+    plan = B.FwdPlan(live['q'], live['k'], live['v'], live['g'], live['beta'], sc, None, **kw)
+    assert plan.schedule()['overlapped']
+    for i in (0, 1, 0, 1, 1, 0):
+        for n in live:
+            live[n].copy_(xs[i][n])
+        plan.forward()
+        torch.cuda.synchronize()
+        assert B.device_errors() == 0
+        assert torch.equal(plan.o, ref[i][0]) and torch.equal(plan.ht, ref[i][1]), i
+    say("  overlapped calls alternating inputs on one workspace: each equals its serial run")
