@@ -278,7 +278,7 @@ gdn::FwdConfig fwd_config(const gdn_fwd_args* a) {
 //   a1     [num_slots, Hv] x 64 x Dv FP32 scale P^T dO
 //   a2     [num_slots, Hv] x Dk x Dv FP32 scale (e^gamma Q)^T dO
 struct BwdWsLayout {
-  int64_t X, W, dstate, dvn, dqk, bimg, a1, a2, dX, total;
+  int64_t X, W, dstate, dvn, dqk, bimg, a1, a2, dX, flags, total;
 };
 
 BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
@@ -296,6 +296,7 @@ BwdWsLayout bwd_ws_layout(const gdn_fwd_args* a) {
   w.a1 = off;      off += bf ? round256(S * Hv * 64 * a->Dv * 4) : 0;
   w.a2 = off;      off += bf ? round256(S * Hv * a->Dk * a->Dv * 4) : 0;
   w.dX = off;      off += a->policy.solve_degree > 0 ? round256(S * Hv * 64 * 64 * 4) : 0;
+  w.flags = off;   off += bf ? round256(S * Hv * 4) : 0;   // ready flags of the overlapped backward
   w.total = off;
   return w;
 }
@@ -442,6 +443,21 @@ OverlapRes* overlap_res() {
            hipEventCreateWithFlags(&r.join, kFlags) == hipSuccess;
   }
   return r.ok ? &r : nullptr;
+}
+
+// Chunks of every sequence whose backward images are built on every CU before
+// the reverse recurrence starts (it consumes the last chunk first). Beside
+// the recurrence the image kernel runs one workgroup per CU and delivers a
+// chunk of nh (sequence, head) items every nh t_img / CUs; the recurrence
+// takes t_chunk per chunk. With t_img ~ kImgPerChunk t_chunk (measured on
+// the forward+backward workload: about 21 us per item against 2.35 us per
+// chunk step), the head covers the deficit, plus two chunks the first
+// steps look ahead for.
+int bwd_head_chunks(int maxc, int64_t nh) {
+  constexpr double kImgPerChunk = 21.0 / 2.35;
+  const double r = (double)nh * kImgPerChunk / gdn::device_cus();   // image / recurrence time per chunk
+  const int deficit = r > 1.0 ? (int)std::ceil(maxc * (1.0 - 1.0 / r)) : 0;
+  return std::min(maxc, deficit + 2);
 }
 
 hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn::FwdKernelArgs k,
@@ -766,7 +782,27 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
   c.f32_io = a->fwd.io_dtype == GDN_F32;
   if (!k.f.err) return fail(GDN_E_HIP, "device error word unavailable on the current device");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  s = hip_status(gdn::launch_bwd(c, k, st), "gdn_chunk_bwd launch");
+  // Overlapped backward (equal-length bf16 sequences, where the image and the
+  // state kernel fit on one CU together): the image kernel runs beside the
+  // reverse recurrence on the library's second stream, in the chunk order the
+  // recurrence consumes (its ready flags in the workspace), instead of before
+  // it. Same kernels and arithmetic, so the same bits.
+  {
+    const int len = a->fwd.prefix_len > 0 ? std::min(a->fwd.T, a->fwd.prefix_len) : a->fwd.T;
+    const int maxc = (len + 63) / 64;
+    OverlapRes* r = nullptr;
+    if (!c.f32_io && !a->fwd.cu_seqlens && maxc >= 4 && gdn::bwd_overlap_fits(c) &&
+        (r = overlap_res())) {
+      k.flags = reinterpret_cast<uint32_t*>(ws + W.flags);
+      k.rev_maxc = maxc;
+      k.rev_done = bwd_head_chunks(maxc, (int64_t)a->fwd.num_seqs * a->fwd.Hv);
+      const gdn::BwdOverlap ov{r->s2, r->fork, r->join};
+      std::lock_guard<std::mutex> lk(r->mu);
+      s = hip_status(gdn::launch_bwd(c, k, st, &ov), "gdn_chunk_bwd overlapped launch");
+    } else {
+      s = hip_status(gdn::launch_bwd(c, k, st), "gdn_chunk_bwd launch");
+    }
+  }
   if (s != GDN_OK) return s;
   if (a->fwd.policy.read_fmt != GDN_QDQ_OFF) {
     s = hip_status(gdn::launch_bwd_read_anchor(c, k, st), "gdn_chunk_bwd anchor term");

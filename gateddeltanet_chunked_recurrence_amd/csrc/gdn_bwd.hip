@@ -988,7 +988,8 @@ hipError_t launch_bwd_read_anchor(const BwdConfig& c, const BwdKernelArgs& a, hi
 }
 
 template <int DK, bool F32IN>
-static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s,
+                                const BwdOverlap* ov) {
   const dim3 slots(a.num_slots, c.Hv);
   // bf16 inputs with W QDQ: X comes from the forward's saved buffer and the
   // later kernels read the W codes, so there is nothing to prepare
@@ -1002,6 +1003,26 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
   if constexpr (F32IN) {
     hipLaunchKernelGGL((bwd_dstate<DK, F32IN>), dim3(c.Dv / 64, c.Hv, c.N), dim3(NT), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if (ov && a.flags) {
+    // The images of the last rev_done chunks first, on every CU; then the
+    // state kernel, and beside it on the second stream the image kernel for
+    // the rest, in the reverse chunk-major order the state kernel consumes.
+    // The flag reset records the fork.
+    const int64_t nflags = (int64_t)a.num_slots * c.Hv;
+    const int items = a.rev_maxc * c.N * c.Hv, head = a.rev_done * c.N * c.Hv;
+    BwdKernelArgs img = a;
+    img.flags = nullptr;
+    img.rev_lo = 0;
+    img.rev_hi = head;
+    if ((e = launch_bwd_img(c, img, s)) != hipSuccess) return e;
+    if ((e = launch_fill_u32(a.flags, nflags, 0u, s, ov->fork)) != hipSuccess) return e;
+    if ((e = launch_bwd_state(c, a, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ov->s2, ov->fork, 0)) != hipSuccess) return e;
+    img = a;
+    img.rev_lo = head;
+    img.rev_hi = items;
+    if ((e = launch_bwd_img(c, img, ov->s2, ov->join)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, ov->join, 0)) != hipSuccess) return e;
   } else {
     if ((e = launch_bwd_img(c, a, s)) != hipSuccess) return e;
     if ((e = launch_bwd_state(c, a, s)) != hipSuccess) return e;
@@ -1025,14 +1046,14 @@ static hipError_t launch_bwd_dk(const BwdConfig& c, const BwdKernelArgs& a, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
+hipError_t launch_bwd(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s, const BwdOverlap* ov) {
   if (a.total_tokens == 0 || c.Hv == 0) return hipSuccess;
   if (c.f32_io) {
-    if (c.Dk == 64) return launch_bwd_dk<64, true>(c, a, s);
+    if (c.Dk == 64) return launch_bwd_dk<64, true>(c, a, s, nullptr);
     return hipErrorInvalidValue;
   }
-  if (c.Dk == 64) return launch_bwd_dk<64, false>(c, a, s);
-  if (c.Dk == 128) return launch_bwd_dk<128, false>(c, a, s);
+  if (c.Dk == 64) return launch_bwd_dk<64, false>(c, a, s, ov);
+  if (c.Dk == 128) return launch_bwd_dk<128, false>(c, a, s, ov);
   return hipErrorInvalidValue;
 }
 

@@ -32,6 +32,8 @@
 // Transposes are transposing LDS reads (ds_read_b64_tr_b16): a row-major bf16
 // tile read by columns is the tile in accumulator layout, and two such reads
 // 16 rows apart are an operand with the tokens as contraction index.
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -91,10 +93,18 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   const FwdKernelArgs& f = a.f;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = __lane_id();
   const int tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
-  const int slot = blockIdx.x, h = blockIdx.y;
+  const int Hv = f.Hv, Hqk = f.Hqk, Dv = DV;
+  int slot = blockIdx.x, h = blockIdx.y;
+  if (a.rev_maxc > 0) {
+    // for the overlapped backward: item i in reverse chunk-major order, chunk
+    // rev_maxc - 1 - i / (N Hv) of every (sequence, head) before the one below
+    const int nh = N * Hv, i = a.rev_lo + blockIdx.x, cr = i / nh, r = i - cr * nh, n = r / Hv;
+    h = r - n * Hv;
+    slot = n + (n * f.T) / CHUNK + (a.rev_maxc - 1 - cr);
+  }
+  const bool coh = a.flags != nullptr;             // device-scope stores, then the item's flag
   const Chunk ch = locate_slot(slot, f.cu_seqlens, N, f.T, f.prefix_len);
   if (!ch.valid) return;
-  const int Hv = f.Hv, Hqk = f.Hqk, Dv = DV;
   const int hk = h / (Hv / Hqk), t0 = ch.t0, nc = ch.nc;
   const int64_t chb = (int64_t)slot * Hv + h;
   bf16* img = a.ws_bimg + chb * BI::size(NW);
@@ -187,10 +197,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
     sm.gam2[lane] = g2;
     sm.eg[lane] = fexp2(g2);
     float* G = reinterpret_cast<float*>(img + BI::g_at(NW));
-    G[lane] = valid ? fexp2(g2n - g2) : 0.f;
+    st_out(G + lane, valid ? fexp2(g2n - g2) : 0.f, coh);
     if (lane == 0) {
-      G[64] = fexp2(g2n);
-      G[65] = WF != 0 ? -f.w_scale[chb] : -1.f;
+      st_out(G + 64, fexp2(g2n), coh);
+      st_out(G + 65, WF != 0 ? -f.w_scale[chb] : -1.f, coh);
     }
   }
   __syncthreads();
@@ -247,6 +257,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
   __syncthreads();                                 // dO operands complete
 
   const float scale = f.scale;
+  float* a1b = a.ws_a1 + frag_off(chb, nvb, 0, 0, 4, 0, 0);      // this item's A1 and A2 blocks
+  float* a2b = a.ws_a2 + frag_off(chb, nvb, 0, 0, MK, 0, 0);
   // ---- A1 = scale P^T dO, rows of key tile jt
   for (int vt = 0; vt < NVT; ++vt) {
     f32x4 acc = zero4();
@@ -259,7 +271,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] *= scale;
-    *reinterpret_cast<f32x4*>(a.ws_a1 + frag_off(chb, nvb, vt >> 2, vt & 3, 4, jt, lane)) = acc;
+    st_out16(a1b, 4 * (int)frag_off(0, nvb, vt >> 2, vt & 3, 4, jt, lane), __builtin_bit_cast(u32x4, acc),
+             coh);
   }
   // ---- A2 = scale (e^gamma Q)^T dO, this wave's dk tiles
 #pragma unroll
@@ -275,7 +288,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] *= scale;
-      *reinterpret_cast<f32x4*>(a.ws_a2 + frag_off(chb, nvb, vt >> 2, vt & 3, MK, dt, lane)) = acc;
+      st_out16(a2b, 4 * (int)frag_off(0, nvb, vt >> 2, vt & 3, MK, dt, lane),
+               __builtin_bit_cast(u32x4, acc), coh);
     }
   }
   // ---- K image: pperm along dk, 16-byte chunks swizzled by row
@@ -283,17 +297,23 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
     const int row = p / (DK / 8), cs = p % (DK / 8), b = cs >> 2, g4 = cs & 3;
     const uint2 lo = *reinterpret_cast<const uint2*>(&sm.Kn[row * LD + 32 * b + 4 * g4]);
     const uint2 hi = *reinterpret_cast<const uint2*>(&sm.Kn[row * LD + 32 * b + 16 + 4 * g4]);
-    *reinterpret_cast<u32x4*>(img + row * I::RS + ((cs ^ (row & I::SWZ)) << 3)) =
-        u32x4{lo.x, lo.y, hi.x, hi.y};
+    st_out16(img, 2 * (row * I::RS + ((cs ^ (row & I::SWZ)) << 3)), u32x4{lo.x, lo.y, hi.x, hi.y}, coh);
   }
   // ---- W^T image: dk rows, tokens paired along the row
   for (int fi = wave; fi < 2 * MK; fi += 4) {
     const int dt = fi >> 1, kk = fi & 1;
 #pragma unroll
     for (int pl = 0; pl < NW; ++pl) {
-      *reinterpret_cast<bf16x8*>(img + BI::KI + pl * BI::WT + (16 * dt + r16) * I::R64 + 32 * kk +
-                                 8 * grp) = lds_col8(sm.Wn[pl], LD, 32 * kk, 16 * dt, r16, grp);
+      st_out16(img, 2 * (BI::KI + pl * BI::WT + (16 * dt + r16) * I::R64 + 32 * kk + 8 * grp),
+               __builtin_bit_cast(u32x4, lds_col8(sm.Wn[pl], LD, 32 * kk, 16 * dt, r16, grp)), coh);
     }
+  }
+  if (coh) {
+    // every wave's stores of this item have reached the device's coherence
+    // point before the one flag store
+    vm_drain();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.flags + chb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -338,12 +358,34 @@ __global__ void __launch_bounds__(64 * (WG + 1), 1) bwd_state_kernel(BwdKernelAr
 #pragma unroll
       for (int j = 0; j < NINS; ++j) __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, 0);
     };
+    // Beside the image kernel: chunk c's flag, before the barrier after which
+    // the column waves load its A1 and A2 (two chunks ahead of the copies'
+    // own use), bounded to about 2^27 clocks (on give-up the error flag is
+    // set and the work goes on).
+    auto wait_ready = [&](int c) {
+      if (!a.flags || c < 0 || c >= nchunks - a.rev_done) return;
+      const uint32_t* fl = a.flags + chunk_ch(c);
+      const uint64_t t0 = __builtin_amdgcn_s_memtime();
+      while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (__builtin_amdgcn_s_memtime() - t0 > (1ull << 27)) {
+          if (lane == 0) __hip_atomic_fetch_or(f.err, kErrFlagWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    };
     if (nchunks > 0) {
+      if (a.flags) {
+        wait_ready(nchunks - 1);
+        wait_ready(nchunks - 2);
+        lds_barrier();                            // the column waves' first loads may start
+      }
       dma(nchunks - 1, (nchunks - 1) & 1);
       vm_drain();
       lds_barrier();
     }
     for (int c = nchunks - 1; c >= 0; --c) {
+      wait_ready(c - 2);                          // A1, A2 of chunk c - 2, loaded after this barrier
       if (c > 0) dma(c - 1, (c - 1) & 1);
       vm_drain();                                 // staging of chunk c - 1 landed
       lds_barrier();
@@ -375,6 +417,7 @@ __global__ void __launch_bounds__(64 * (WG + 1), 1) bwd_state_kernel(BwdKernelAr
   };
 
   if (nchunks > 0) {
+    if (a.flags) lds_barrier();                   // the staging wave saw the last two chunks' flags
     load_a(nchunks - 1, A1c, A2c);
     vm_drain();
     lds_barrier();
@@ -461,11 +504,18 @@ __global__ void __launch_bounds__(64 * (WG + 1), 1) bwd_state_kernel(BwdKernelAr
 }
 
 template <int DK, int DV>
-static hipError_t launch_img_dv(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
-  const dim3 grid(a.num_slots, c.Hv);
+static hipError_t launch_img_dv(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s,
+                                hipEvent_t stop) {
+  // beside the state kernel: one workgroup per item of the reverse
+  // chunk-major order (dispatched in that order)
+  const dim3 grid = a.rev_maxc > 0 ? dim3((unsigned)(a.rev_hi - a.rev_lo)) : dim3(a.num_slots, c.Hv);
+  if (grid.x == 0) return stop ? hipEventRecord(stop, s) : hipSuccess;
 #define GDN_CASE(WFv) \
   if (c.w_fmt == WFv) { \
-    hipLaunchKernelGGL((bwd_img_kernel<DK, DV, WFv>), grid, dim3(NT), 0, s, a, c.N); \
+    if (stop) \
+      hipExtLaunchKernelGGL((bwd_img_kernel<DK, DV, WFv>), grid, dim3(NT), 0, s, nullptr, stop, 0, a, c.N); \
+    else \
+      hipLaunchKernelGGL((bwd_img_kernel<DK, DV, WFv>), grid, dim3(NT), 0, s, a, c.N); \
     return hipGetLastError(); \
   }
   GDN_CASE(0) GDN_CASE(1) GDN_CASE(2)
@@ -474,10 +524,10 @@ static hipError_t launch_img_dv(const BwdConfig& c, const BwdKernelArgs& a, hipS
 }
 
 template <int DK>
-static hipError_t launch_img_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
-  if (c.Dv == 64) return launch_img_dv<DK, 64>(c, a, s);
-  if (c.Dv == 128) return launch_img_dv<DK, 128>(c, a, s);
-  if (c.Dv == 256) return launch_img_dv<DK, 256>(c, a, s);
+static hipError_t launch_img_dk(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s, hipEvent_t stop) {
+  if (c.Dv == 64) return launch_img_dv<DK, 64>(c, a, s, stop);
+  if (c.Dv == 128) return launch_img_dv<DK, 128>(c, a, s, stop);
+  if (c.Dv == 256) return launch_img_dv<DK, 256>(c, a, s, stop);
   return hipErrorInvalidValue;
 }
 
@@ -506,10 +556,41 @@ int bwd_img_elems(int Dk, int w_fmt) {
   return Dk == 128 ? BImg<128>::size(nw) : BImg<64>::size(nw);
 }
 
-hipError_t launch_bwd_img(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {
-  if (c.Dk == 128) return launch_img_dk<128>(c, a, s);
-  if (c.Dk == 64) return launch_img_dk<64>(c, a, s);
+hipError_t launch_bwd_img(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s, hipEvent_t stop) {
+  if (c.Dk == 128) return launch_img_dk<128>(c, a, s, stop);
+  if (c.Dk == 64) return launch_img_dk<64>(c, a, s, stop);
   return hipErrorInvalidValue;
+}
+
+namespace {
+template <int DK, int DV, int NW>
+int64_t img_state_lds() {                          // one image and one state workgroup (bytes)
+  return (int64_t)sizeof(ImgSmem<DK, DV, NW>) + 2 * 2 * (int64_t)BImg<DK>::size(NW);
+}
+template <int DK>
+int64_t img_state_lds_dk(int dv, int nw) {
+  if (dv == 64) return nw == 1 ? img_state_lds<DK, 64, 1>() : img_state_lds<DK, 64, 2>();
+  if (dv == 128) return nw == 1 ? img_state_lds<DK, 128, 1>() : img_state_lds<DK, 128, 2>();
+  return nw == 1 ? img_state_lds<DK, 256, 1>() : img_state_lds<DK, 256, 2>();
+}
+}  // namespace
+
+bool bwd_overlap_fits(const BwdConfig& c) {
+  if (c.f32_io) return false;
+  const int nw = c.w_fmt != 0 ? 1 : 2;
+  const int64_t lds = c.Dk == 128 ? img_state_lds_dk<128>(c.Dv, nw) : img_state_lds_dk<64>(c.Dv, nw);
+  int dev = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess)
+    return false;
+  if (lds > per_cu) return false;
+  // the state kernel's grid, as launch_state_dk sizes it
+  const int64_t units = (int64_t)c.N * c.Hv * (c.Dv / 64), cus = device_cus();
+  const int wg = 4 * units <= cus ? 1 : 2 * units <= cus ? 2 : 4;
+  const int64_t heads = (int64_t)c.N * c.Hv;
+  const int64_t nblk = (int64_t)(c.Dv / 16 / wg) * 8 * ((heads + 7) / 8);
+  return nblk <= cus;
 }
 
 hipError_t launch_bwd_state(const BwdConfig& c, const BwdKernelArgs& a, hipStream_t s) {

@@ -120,28 +120,6 @@ __device__ __forceinline__ void lower_tiles(int wave, int (&ti)[2], int (&tj)[2]
   tj[1] = tab[wave][3];
 }
 
-// Stores of the operand images, U and the W scale. With a concurrent state
-// kernel (flags set) they are device-scope stores (sc1: written through to
-// the device's coherence point, leaving no dirty L2 line behind), so waiting
-// for them (vmcnt) before the item's ready flag makes them visible on every
-// XCD; a release fence would instead write back the whole L2 (buffer_wbl2),
-// which took about 40 us per item. Otherwise plain stores.
-__device__ __forceinline__ void st_out(float* p, float v, bool coh) {
-  if (coh) __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v),
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = v;
-}
-// 16 bytes at base + off (base wave-uniform): a device-scope buffer store
-// (one instruction, cache policy sc1) or a plain store.
-__device__ __forceinline__ void st_out16(void* base, int off, u32x4 v, bool coh) {
-  if (coh) {
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFF0, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 16);
-  } else {
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off) = v;
-  }
-}
-
 // Writes 4 consecutive bf16 at dst (8-byte aligned).
 __device__ __forceinline__ void st4(bf16* dst, bf16 a, bf16 b, bf16 c, bf16 d) {
   *reinterpret_cast<bf16x4*>(dst) = bf16x4{a, b, c, d};

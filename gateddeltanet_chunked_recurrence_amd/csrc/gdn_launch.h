@@ -137,6 +137,15 @@ struct BwdKernelArgs {
   float* ws_a2;               // [num_slots * Hv] x [Dk, Dv] fragment order: scale (e^gamma Q)^T dO
   float* ws_dqk;              // [B*T, Hv, 2, Dk] FP32 per-value-head dq, dk before the group sum
   float* ws_dX;               // [num_slots, Hv, 64, 64] FP32 dL/dX per chunk (approximate inverse only)
+  // overlapped backward (bf16 io, equal-length sequences): bwd_img_kernel
+  // runs its items in reverse chunk-major order (the last chunk of every
+  // sequence and head first) beside bwd_state_kernel, storing at device
+  // scope and setting flags[slot * Hv + head] after each item; the state
+  // kernel waits for each chunk's flag
+  uint32_t* flags;            // nullable
+  int32_t rev_maxc;           // > 0: chunks per sequence, and bwd_img_kernel runs items
+  int32_t rev_lo, rev_hi;     // [rev_lo, rev_hi) of that order, one workgroup each
+  int32_t rev_done;           // the last rev_done chunks of every sequence were built before
   int32_t grad_f32;
   int32_t total_tokens;
   int32_t num_slots;
@@ -146,11 +155,26 @@ struct BwdConfig {
   int Dk, Dv, N, Hv, Hqk, state_fmt, w_fmt, f32_io;
 };
 
-hipError_t launch_bwd(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+// The second stream and the fork / join events of an overlapped backward
+// (a.flags set): the flag reset records fork, the image kernel runs on s2
+// after it and records join, and `stream` waits for join before the
+// chunk-local kernels.
+struct BwdOverlap {
+  hipStream_t s2;
+  hipEvent_t fork, join;
+};
+hipError_t launch_bwd(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream,
+                      const BwdOverlap* ov = nullptr);
+// Whether the image kernel and the state kernel of this backward fit on one
+// CU together (LDS), with the state kernel's grid at most one workgroup per
+// CU: then some CU always has room for an image workgroup while every state
+// workgroup is resident, and the overlapped backward cannot stall.
+bool bwd_overlap_fits(const BwdConfig& cfg);
 // Compute units of the current device (queried once per device).
 int device_cus();
 // bf16 io: operand images of the reverse recurrence, then the recurrence.
-hipError_t launch_bwd_img(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
+hipError_t launch_bwd_img(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream,
+                          hipEvent_t stop = nullptr);
 hipError_t launch_bwd_state(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
 // bf16 io: the chunk-local gradients on bf16 MFMA.
 hipError_t launch_bwd_local(const BwdConfig& cfg, const BwdKernelArgs& a, hipStream_t stream);
