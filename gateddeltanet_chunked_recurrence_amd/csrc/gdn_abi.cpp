@@ -7,8 +7,9 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
-#include <cstdio>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -389,6 +390,15 @@ struct OverlapPlan {
   int head = 0, rest_blocks = 0;
 };
 
+// GDN_NO_OVERLAP in the environment (read once): every call runs its stages
+// one after the other on the caller's stream. For profilers that serialize
+// kernels, under which a kernel waiting for another one's ready flags would
+// wait out its bound.
+bool overlap_disabled() {
+  static const bool off = std::getenv("GDN_NO_OVERLAP") != nullptr;
+  return off;
+}
+
 // with both QDQ sites on, the state kernel widens the W codes itself, so the
 // images carry them as bytes (the split state kernel, which takes them, spans
 // 64 columns: scale tiles up to 64 wide)
@@ -399,7 +409,8 @@ int w_img_bytes_of(const gdn_fwd_args* a) {
 
 OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
   OverlapPlan op;
-  if (!w_img_bytes_of(a) || a->cu_seqlens || a->io_dtype != GDN_BF16 || a->policy.read_fmt != 0)
+  if (overlap_disabled() || !w_img_bytes_of(a) || a->cu_seqlens || a->io_dtype != GDN_BF16 ||
+      a->policy.read_fmt != 0)
     return op;
   const int len = a->prefix_len > 0 ? std::min(a->T, a->prefix_len) : a->T;
   const int maxc = (len + 63) / 64;
@@ -667,6 +678,7 @@ gdn::DecodeKernelArgs decode_kernel_args(const gdn_decode_args* a) {
   k.Dv = a->Dv;
   k.block_v = a->state_fmt != GDN_QDQ_OFF ? a->block_v : 64;
   k.readout = a->readout;
+  k.num_seqs = a->num_seqs;
   k.scale = a->scale;
   k.total_tokens = (int32_t)((int64_t)a->B * a->T);
   return k;
@@ -791,8 +803,8 @@ gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream) {
     const int len = a->fwd.prefix_len > 0 ? std::min(a->fwd.T, a->fwd.prefix_len) : a->fwd.T;
     const int maxc = (len + 63) / 64;
     OverlapRes* r = nullptr;
-    if (!c.f32_io && !a->fwd.cu_seqlens && maxc >= 4 && gdn::bwd_overlap_fits(c) &&
-        (r = overlap_res())) {
+    if (!overlap_disabled() && !c.f32_io && !a->fwd.cu_seqlens && maxc >= 4 &&
+        gdn::bwd_overlap_fits(c) && (r = overlap_res())) {
       k.flags = reinterpret_cast<uint32_t*>(ws + W.flags);
       k.rev_maxc = maxc;
       k.rev_done = bwd_head_chunks(maxc, (int64_t)a->fwd.num_seqs * a->fwd.Hv);

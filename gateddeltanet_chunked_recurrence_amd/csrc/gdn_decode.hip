@@ -16,10 +16,13 @@
 // QDQ is the FP32 definition in gdn.h (IEEE division for d and 1/d), the
 // identity when the state format is off. All arithmetic is FP32.
 //
-// One workgroup per (sequence, value head): NS = Dv / 64 column slabs, each
-// split over four waves by key rows. Wave w: slab s = w / 4, row quarter
-// r = w % 4. Lane l holds an RPL x 8 block of S (RPL = Dk / 32): columns
-// 64 s + 8 (l & 7) .. + 7, rows r Dk / 4 + (l >> 3) RPL .. + RPL - 1, so a
+// The forward takes one workgroup per (sequence, value head, group of NS
+// 64-column slabs), NS the slabs of one scale tile (1 up to block_v 64); the
+// backward one per (sequence, value head) with NS = Dv / 64, as its dq, dk,
+// dbeta and dg sum over every column. Each slab is split over four waves by
+// key rows. Wave w: slab s = w / 4, row quarter r = w % 4. Lane l holds an
+// RPL x 8 block of S (RPL = Dk / 32): the workgroup's columns 64 s + 8 (l & 7)
+// .. + 7, rows r Dk / 4 + (l >> 3) RPL .. + RPL - 1, so a
 // sum over key rows is three lane exchanges and one LDS exchange across the
 // four row quarters, and a sum over value columns is three DPP steps within
 // eight lanes plus an LDS exchange across slabs. The per-token work is a few
@@ -258,11 +261,17 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_fwd_kernel(DecodeKernelArg
   __shared__ float xp[NS][4][64];   // S^T k per row quarter
   __shared__ float xo[NS][4][64];   // S^T q per row quarter
   __shared__ float xa[NS][4][8];    // tile amax per row quarter and column group
-  const int Hv = a.Hv, Dv = a.Dv, h = blockIdx.x % Hv, n = blockIdx.x / Hv;
+  // workgroup -> (head index, group of NS slabs): the slab groups of a head
+  // share an XCD (workgroups go round-robin over the eight)
+  const int Hv = a.Hv, Dv = a.Dv, ng = Dv / (64 * NS), VW = 64 * NS;
+  const int bid = blockIdx.x, r8 = bid >> 3, gi = r8 % ng, hidx = (bid & 7) + 8 * (r8 / ng);
+  if (hidx >= a.num_seqs * Hv) return;
+  const int h = hidx % Hv, n = hidx / Hv;
   const int hk = h / (Hv / a.Hqk);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = wave >> 2, r = wave & 3, lane = __lane_id(), cg = lane & 7, rg = lane >> 3;
-  const int row0 = r * (DK / 4) + rg * RPL, col0 = 64 * s + 8 * cg;
+  // lcol: first of the lane's 8 columns within this workgroup's slabs; col0 within the head
+  const int row0 = r * (DK / 4) + rg * RPL, lcol = 64 * s + 8 * cg, col0 = VW * gi + lcol;
   const Span sp = decode_span(a, n);
   const int bv = a.block_v, nsl = bv > 64 ? bv / 64 : 1, sb = (s / nsl) * nsl;
   const bool before = a.readout == 0;
@@ -339,10 +348,11 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_fwd_kernel(DecodeKernelArg
         const int tok = min(t0 + o / (DK * ES), sp.eos - 1);
         src = reinterpret_cast<const char*>(off < KB ? a.k : a.q) +
               ((int64_t)tok * a.Hqk + hk) * (DK * ES) + o % (DK * ES);
-      } else {
+      } else {                                      // this workgroup's VW columns of v
         const int o = off - 2 * KB;
-        const int tok = min(t0 + o / (Dv * ES), sp.eos - 1);
-        src = reinterpret_cast<const char*>(a.v) + ((int64_t)tok * Hv + h) * (Dv * ES) + o % (Dv * ES);
+        const int tok = min(t0 + o / (VW * ES), sp.eos - 1);
+        src = reinterpret_cast<const char*>(a.v) + (((int64_t)tok * Hv + h) * Dv + VW * gi) * ES +
+              o % (VW * ES);
       }
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src),
                                        reinterpret_cast<uint4*>(base + 1024 * j), 16, 0, 0);
@@ -374,7 +384,7 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_fwd_kernel(DecodeKernelArg
     float kk[RPL], qq[RPL], vv[8];
     lds_vec<RPL, F32>(wb, (tok * DK + row0) * ES, kk);
     lds_vec<RPL, F32>(wb, KB + (tok * DK + row0) * ES, qq);
-    lds_vec<8, F32>(wb, 2 * KB + (tok * Dv + col0) * ES, vv);
+    lds_vec<8, F32>(wb, 2 * KB + (tok * VW + lcol) * ES, vv);
     const float* gb = reinterpret_cast<const float*>(wb + 2 * KB + VB);
     const float eg = expf(gb[tok]), bt = gb[W + tok];
 
@@ -755,10 +765,16 @@ __global__ void decode_group(DecodeKernelArgs a, int N, int G) {
   }
 }
 
+// The forward's 64-column slabs are independent (the prediction, the write,
+// the readout and each scale tile are per column or per tile), so a
+// workgroup takes as few as hold whole scale tiles, and the slab groups of
+// a head run on separate CUs.
 template <int DK, bool F32, int SF>
 hipError_t launch_fwd_dk(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t st) {
-  const dim3 grid(c.N * c.Hv);
-  switch (c.Dv / 64) {
+  const int ns = SF != 0 && a.block_v > 64 ? a.block_v / 64 : 1;
+  const int64_t heads = (int64_t)c.N * c.Hv;
+  const dim3 grid((unsigned)((c.Dv / 64 / ns) * 8 * ((heads + 7) / 8)));
+  switch (ns) {
     case 1: hipLaunchKernelGGL((decode_fwd_kernel<DK, F32, SF, 1>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((decode_fwd_kernel<DK, F32, SF, 2>), grid, dim3(512), 0, st, a); break;
     default: hipLaunchKernelGGL((decode_fwd_kernel<DK, F32, SF, 4>), grid, dim3(1024), 0, st, a); break;

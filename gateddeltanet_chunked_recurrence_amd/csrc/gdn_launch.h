@@ -216,6 +216,7 @@ struct DecodeKernelArgs {
   float* s_scale;             // their tile scales, nullable
   float* s_f32;               // saved written states (state QDQ off), nullable
   int32_t T, start, Hqk, Hv, Dv, block_v, readout;
+  int32_t num_seqs;
   float scale;
   // backward
   const void* dout;

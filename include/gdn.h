@@ -205,7 +205,10 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
  * those of gdn_chunk_fwd_prep then gdn_chunk_fwd_state, so the results are
  * the same bits. Host threads enqueue it under a per-device lock. Code under
  * HIP graph capture uses gdn_chunk_fwd_noalloc, which always runs on
- * `stream` alone. */
+ * `stream` alone. With the environment variable GDN_NO_OVERLAP set (any
+ * value, read once) this call and gdn_chunk_bwd run their stages one after
+ * the other on `stream`: for profilers that serialize kernels, under which a
+ * kernel waiting for another's ready flags would wait out its bound. */
 gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
 
 /* The schedule gdn_chunk_fwd takes for these arguments on a device of `cus`
@@ -264,6 +267,12 @@ typedef struct {
 } gdn_bwd_args;
 
 size_t gdn_bwd_workspace_bytes(const gdn_bwd_args* a);
+/* With bf16 inputs and equal-length sequences (at least 4 chunks each), where
+ * the operand build of the reverse recurrence and the recurrence fit on one
+ * CU together, the build of all but the last chunks' operands runs beside
+ * the recurrence, on the second stream of gdn_chunk_fwd's overlapped
+ * schedule (same lock, same join into `stream`, same GDN_NO_OVERLAP switch),
+ * with the same kernels and arithmetic: the gradients are the same bits. */
 gdn_status gdn_chunk_bwd(const gdn_bwd_args* a, void* stream);
 
 /* Standalone state QDQ (the function used at the state site), bit-exact to

@@ -125,6 +125,25 @@ def test_forward_schedule_host_logic():
         B.fwd_schedule(_args(Hv=3), 256)
 
 
+def test_no_overlap_switch_makes_the_schedule_serial():
+    """GDN_NO_OVERLAP (read once per process) turns the overlapped schedules
+    off: checked in a child process that loads the library with it set."""
+    import subprocess
+    import sys
+    code = ("import ctypes, sys; sys.path.insert(0, %r); "
+            "from tests.test_abi_cpu import _args; "
+            "from gateddeltanet_chunked_recurrence_amd import binding as B; "
+            "print(B.fwd_schedule(_args(B=4, T=4096, Hqk=16, Hv=16, num_seqs=4), 256)['overlapped'])"
+            % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    for env, want in ((dict(GDN_NO_OVERLAP='1'), 'False'), (dict(), 'True')):
+        e = {k: v for k, v in os.environ.items() if k != 'GDN_NO_OVERLAP'}
+        e.update(env)
+        out = subprocess.run([sys.executable, '-c', code], env=e, capture_output=True, text=True,
+                             timeout=120)
+        assert out.returncode == 0, out.stderr
+        assert out.stdout.strip().splitlines()[-1] == want
+
+
 def test_forward_workspace_is_sized_and_required():
     """bf16 inputs need the prep kernel's scratch: its size follows the
     per-(slot, head) image sizes, a missing or short workspace is rejected
