@@ -852,8 +852,10 @@ gdn_status gdn_decode_fwd(const gdn_decode_args* a, void* stream) {
 
 size_t gdn_decode_bwd_workspace_bytes(const gdn_decode_bwd_args* a) {
   if (!a || check_decode(&a->fwd) != GDN_OK) return 0;
-  if (a->fwd.Hv == a->fwd.Hqk) return 0;
-  return (size_t)round256((int64_t)a->fwd.B * a->fwd.T * a->fwd.Hv * 2 * a->fwd.Dk * 4);
+  // partial dq, dk, dg, dbeta per (token, value head, group of slabs)
+  const int ng = a->fwd.Dv / 64 / gdn::decode_slabs_per_group(a->fwd.state_fmt, a->fwd.block_v);
+  if (a->fwd.Hv == a->fwd.Hqk && ng == 1) return 0;
+  return (size_t)round256((int64_t)a->fwd.B * a->fwd.T * a->fwd.Hv * ng * (2 * a->fwd.Dk + 4) * 4);
 }
 
 gdn_status gdn_decode_bwd(const gdn_decode_bwd_args* a, void* stream) {

@@ -16,10 +16,11 @@
 // QDQ is the FP32 definition in gdn.h (IEEE division for d and 1/d), the
 // identity when the state format is off. All arithmetic is FP32.
 //
-// The forward takes one workgroup per (sequence, value head, group of NS
-// 64-column slabs), NS the slabs of one scale tile (1 up to block_v 64); the
-// backward one per (sequence, value head) with NS = Dv / 64, as its dq, dk,
-// dbeta and dg sum over every column. Each slab is split over four waves by
+// One workgroup per (sequence, value head, group of NS 64-column slabs), NS
+// the slabs of one scale tile (1 up to block_v 64): the columns are
+// independent but for the tile amax, and the backward's dq, dk, dbeta and dg,
+// which sum over every column, leave per-group partial sums that a second
+// kernel adds up in a fixed order. Each slab is split over four waves by
 // key rows. Wave w: slab s = w / 4, row quarter r = w % 4. Lane l holds an
 // RPL x 8 block of S (RPL = Dk / 32): the workgroup's columns 64 s + 8 (l & 7)
 // .. + 7, rows r Dk / 4 + (l >> 3) RPL .. + RPL - 1, so a
@@ -478,16 +479,25 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
   __shared__ float xq[NS][DK];      // dq rows per slab
   __shared__ float xk[NS][DK];      // dk rows per slab
   __shared__ float xs[NS * 4][4];   // per wave: [0] u . do, [1] dbeta, [2] dg
-  const int Hv = a.Hv, Dv = a.Dv, h = blockIdx.x % Hv, n = blockIdx.x / Hv;
+  // workgroup -> (head index, group of NS slabs), as in the forward
+  const int Hv = a.Hv, Dv = a.Dv, ng = Dv / (64 * NS);
+  const int bid = blockIdx.x, r8 = bid >> 3, gi = r8 % ng, hidx = (bid & 7) + 8 * (r8 / ng);
+  if (hidx >= a.num_seqs * Hv) return;
+  const int h = hidx % Hv, n = hidx / Hv;
   const int hk = h / (Hv / a.Hqk);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int s = wave >> 2, r = wave & 3, lane = __lane_id(), cg = lane & 7, rg = lane >> 3;
-  const int row0 = r * (DK / 4) + rg * RPL, col0 = 64 * s + 8 * cg;
+  const int row0 = r * (DK / 4) + rg * RPL, col0 = 64 * (NS * gi + s) + 8 * cg;
   const Span sp = decode_span(a, n);
   const int bv = a.block_v;
   const bool before = a.readout == 0;
   const int64_t st_base = ((int64_t)n * Hv + h) * DK * Dv;
+  // partial sums (this workgroup's columns) of dq, dk, dg, dbeta go to the
+  // workspace when a head's columns span several workgroups or its dq, dk
+  // sum over a group of value heads: [token, value head, slab group][PW]
   const bool group = a.ws_dqk != nullptr;
+  constexpr int PW = 2 * DK + 4;
+  auto part = [&](int64_t tv) { return a.ws_dqk + (tv * ng + gi) * PW; };
 
   float dS[RPL][8];
 #pragma unroll
@@ -667,7 +677,7 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
         dq[i] = a.scale * (before ? fmaf(kk[i], ud, x) : x);
       }
       if (group) {
-        st_vec<RPL, true>(a.ws_dqk, (tv * 2) * DK + row0, dq);
+        st_vec<RPL, true>(part(tv), row0, dq);
       } else {
         const int64_t off = ((int64_t)t * a.Hqk + hk) * DK + row0;
         if (a.grad_f32) st_vec<RPL, true>(a.dq, off, dq);
@@ -707,7 +717,7 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
         dk[i] = x;
       }
       if (group) {
-        st_vec<RPL, true>(a.ws_dqk, (tv * 2 + 1) * DK + row0, dk);
+        st_vec<RPL, true>(part(tv), DK + row0, dk);
       } else {
         const int64_t off = ((int64_t)t * a.Hqk + hk) * DK + row0;
         if (a.grad_f32) st_vec<RPL, true>(a.dk, off, dk);
@@ -720,8 +730,13 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
       for (int w = 0; w < NS * 4; ++w) dg += xs[w][2];
 #pragma unroll
       for (int ss = 0; ss < NS; ++ss) dbt += xs[4 * ss][1];
-      a.dg[tv] = dg;
-      a.dbeta[tv] = dbt;
+      if (group) {
+        part(tv)[2 * DK] = dg;
+        part(tv)[2 * DK + 1] = dbt;
+      } else {
+        a.dg[tv] = dg;
+        a.dbeta[tv] = dbt;
+      }
     }
     cur = prev;
   }
@@ -732,10 +747,12 @@ __global__ void __launch_bounds__(256 * NS, 1) decode_bwd_kernel(DecodeKernelArg
   }
 }
 
-// dq, dk of each query/key head: the sum over its value heads, for decode
-// tokens only (the tokens before `start` belong to the prefill).
+// The backward's partial sums: dq, dk of each query/key head over its G value
+// heads and their ng slab groups, dg and dbeta of each of those value heads
+// over its slab groups, in a fixed order; for decode tokens only (the tokens
+// before `start` belong to the prefill).
 template <int DK>
-__global__ void decode_group(DecodeKernelArgs a, int N, int G) {
+__global__ void decode_group(DecodeKernelArgs a, int N, int G, int ng) {
   const int tok = blockIdx.x, hk = blockIdx.y, d = threadIdx.x;
   int bos;
   if (a.cu_seqlens) {
@@ -749,11 +766,24 @@ __global__ void decode_group(DecodeKernelArgs a, int N, int G) {
     bos = tok - tok % a.T;
   }
   if (d >= DK || tok - bos < a.start) return;
+  constexpr int PW = 2 * DK + 4;
   float sq = 0.f, sk = 0.f;
   for (int j = 0; j < G; ++j) {
-    const float* p = a.ws_dqk + (((int64_t)tok * a.Hv + hk * G + j) * 2) * DK;
-    sq += p[d];
-    sk += p[DK + d];
+    const int64_t tv = (int64_t)tok * a.Hv + hk * G + j;
+    for (int gi = 0; gi < ng; ++gi) {
+      const float* p = a.ws_dqk + (tv * ng + gi) * PW;
+      sq += p[d];
+      sk += p[DK + d];
+    }
+    if (d == 0) {
+      float dg = 0.f, db = 0.f;
+      for (int gi = 0; gi < ng; ++gi) {
+        dg += a.ws_dqk[(tv * ng + gi) * PW + 2 * DK];
+        db += a.ws_dqk[(tv * ng + gi) * PW + 2 * DK + 1];
+      }
+      a.dg[tv] = dg;
+      a.dbeta[tv] = db;
+    }
   }
   const int64_t off = ((int64_t)tok * a.Hqk + hk) * DK + d;
   if (a.grad_f32) {
@@ -771,7 +801,7 @@ __global__ void decode_group(DecodeKernelArgs a, int N, int G) {
 // a head run on separate CUs.
 template <int DK, bool F32, int SF>
 hipError_t launch_fwd_dk(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t st) {
-  const int ns = SF != 0 && a.block_v > 64 ? a.block_v / 64 : 1;
+  const int ns = decode_slabs_per_group(SF, a.block_v);
   const int64_t heads = (int64_t)c.N * c.Hv;
   const dim3 grid((unsigned)((c.Dv / 64 / ns) * 8 * ((heads + 7) / 8)));
   switch (ns) {
@@ -782,10 +812,15 @@ hipError_t launch_fwd_dk(const DecodeConfig& c, const DecodeKernelArgs& a, hipSt
   return hipGetLastError();
 }
 
+// As the forward: a workgroup per group of the slabs of one scale tile; the
+// partial sums over each group's columns are then added up by decode_group.
 template <int DK, bool F32, int SF>
 hipError_t launch_bwd_dk(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t st) {
-  const dim3 grid(c.N * c.Hv);
-  switch (c.Dv / 64) {
+  const int ns = decode_slabs_per_group(c.state_fmt, a.block_v), ng = c.Dv / 64 / ns;
+  if ((ng > 1 || c.Hv > c.Hqk) != (a.ws_dqk != nullptr)) return hipErrorInvalidValue;
+  const int64_t heads = (int64_t)c.N * c.Hv;
+  const dim3 grid((unsigned)(ng * 8 * ((heads + 7) / 8)));
+  switch (ns) {
     case 1: hipLaunchKernelGGL((decode_bwd_kernel<DK, F32, SF, 1>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((decode_bwd_kernel<DK, F32, SF, 2>), grid, dim3(512), 0, st, a); break;
     default: hipLaunchKernelGGL((decode_bwd_kernel<DK, F32, SF, 4>), grid, dim3(1024), 0, st, a); break;
@@ -793,7 +828,7 @@ hipError_t launch_bwd_dk(const DecodeConfig& c, const DecodeKernelArgs& a, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.ws_dqk) return e;
   hipLaunchKernelGGL((decode_group<DK>), dim3(a.total_tokens, c.Hqk), dim3(DK), 0, st, a, c.N,
-                     c.Hv / c.Hqk);
+                     c.Hv / c.Hqk, ng);
   return hipGetLastError();
 }
 

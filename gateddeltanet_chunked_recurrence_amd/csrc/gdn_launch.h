@@ -236,6 +236,11 @@ struct DecodeConfig {
   int Dk, Dv, N, Hv, Hqk, state_fmt, f32_io;
 };
 
+// 64-column slabs per decode workgroup: those of one state scale tile.
+inline int decode_slabs_per_group(int state_fmt, int block_v) {
+  return state_fmt != 0 && block_v > 64 ? block_v / 64 : 1;
+}
+
 hipError_t launch_decode_fwd(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t s);
 hipError_t launch_decode_bwd(const DecodeConfig& c, const DecodeKernelArgs& a, hipStream_t s);
 

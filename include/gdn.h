@@ -367,9 +367,11 @@ typedef struct {
   float* dg;                   /* out [B, T, Hv]                              */
   float* dbeta;                /* out [B, T, Hv]                              */
   float* dh_in;                /* out [N, Hv, Dk, Dv], or NULL                */
-  void* workspace;             /* gdn_decode_bwd_workspace_bytes() bytes (per
-                                  value head dq, dk before the group sum when
-                                  Hv > Hqk; 0 bytes otherwise)               */
+  void* workspace;             /* gdn_decode_bwd_workspace_bytes() bytes:
+                                  partial dq, dk, dg, dbeta per token, value
+                                  head and group of 64-column slabs (those of
+                                  one scale tile), when a head has several
+                                  groups or Hv > Hqk; 0 bytes otherwise      */
   size_t workspace_bytes;
 } gdn_decode_bwd_args;
 

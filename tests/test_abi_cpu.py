@@ -337,9 +337,14 @@ def test_decode_saved_bytes_and_backward_checks():
     assert 'saved' in lib.gdn_last_error().decode()
     b.fwd.saved = fake
     need = lib.gdn_decode_bwd_workspace_bytes(ctypes.byref(b))
-    assert need == r256(257 * 4 * 2 * 128 * 4)                   # per value head dq, dk
+    # partial dq, dk, dg, dbeta per token, value head and group of 64-column
+    # slabs (Dv 128 with 64-wide scale tiles: two groups), 2 Dk + 4 floats each
+    assert need == r256(257 * 4 * 2 * (2 * 128 + 4) * 4)
     assert lib.gdn_decode_bwd(ctypes.byref(b), None) == B.GDN_E_WORKSPACE
-    b.fwd.Hqk = 4                                                 # no groups: no workspace
+    b.fwd.Hqk = 4                                                 # no head groups, two slab groups
+    assert lib.gdn_decode_bwd_workspace_bytes(ctypes.byref(b)) == r256(257 * 4 * 2 * 260 * 4)
+    b.fwd.block_v = 128                                           # one tile spans the head
     assert lib.gdn_decode_bwd_workspace_bytes(ctypes.byref(b)) == 0
+    b.fwd.block_v = 64
     b.grad_dtype = 9
     assert lib.gdn_decode_bwd(ctypes.byref(b), None) == B.GDN_E_INVALID
