@@ -172,6 +172,10 @@ def test_bwd_qdq_effect_matches_oracle():
     ('fwd_bwd_e4m3_b2_t8192_h16_d128', dict()),
     ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=1000, Hqk=4, Hv=8, state_fmt=INT8, h0=True)),
     ('fwd_e4m3_b4_t4096_h16_d128', dict(B=3, T=700, Hqk=2, Hv=2, Dk=64, Dv=256, w_fmt=INT8)),
+    # 128-wide state scale tiles (the forward runs in series, the backward overlapped)
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=640, Hqk=2, Hv=4, block_v=128, h0=True)),
+    # W QDQ off: the image and state kernels no longer fit one CU together, so serial
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=640, Hqk=2, Hv=4, w_fmt=OFF)),
 ])
 def test_bwd_overlapped_equals_serial(name, over):
     """With equal-length sequences gdn_chunk_bwd runs the image kernel beside

@@ -233,6 +233,11 @@ def test_fwd_fp16_operand_range_is_checked():
     ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=1000, Hqk=4, Hv=8, state_fmt=INT8)),
     ('long_e4m3_t65536_h32_dk128_dv256', dict(T=8192)),
     ('fwd_bwd_e4m3_b2_t8192_h16_d128', dict()),
+    # four items only: fewer than the CUs the chain leaves, no head
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=1, T=256, Hqk=1, Hv=1)),
+    # Dk 64, INT8 W, 32-wide scale tiles, ragged last chunk, h0
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=3, T=777, Hqk=2, Hv=6, Dk=64, Dv=64, w_fmt=INT8,
+                                        block_v=32, h0=True)),
 ])
 def test_fwd_overlapped_schedule_equals_serial(name, over):
     """gdn_chunk_fwd runs the prep's remainder concurrently with the state
