@@ -481,7 +481,6 @@ hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn:
   gdn::FwdKernelArgs prep = k;
   prep.chunk_major = 1;
   prep.flags = flags;
-  prep.publish = 1;
   prep.ticket = flags + nflags;
   prep.item_lo = 0;
   prep.item_hi = op.items;
@@ -490,7 +489,6 @@ hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn:
   prep.prep_blocks = op.head > 0 ? 0 : op.rest_blocks;   // every CU while there is a head
   gdn::FwdKernelArgs state = k;
   state.flags = flags;
-  state.c_split = 0;
   // The fork and join events are recorded by the launches themselves, at
   // their end, with no marker packet of their own.
   std::lock_guard<std::mutex> lk(r->mu);

@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       // the gate block follows the single fp16 P plane in the byte variant
       const int goff = a.w_img_bytes ? I::template p_at<NW>() + I::P1 : I::template g_at<NW>();
       float* G = reinterpret_cast<float*>(img + goff);
-      const bool coh = a.publish != 0;
+      const bool coh = a.flags != nullptr;
       st_out(G + lane, eg, coh);
       st_out(G + 64 + lane, lane < nc ? fexp2(g2n - g2) : 0.f, coh);
       if (lane != 1) st_out(G + 128 + lane, lane == 0 ? fexp2(g2n) : 0.f, coh);   // [129]: the W scale, below
@@ -506,7 +506,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       const u32x4* ksrc = reinterpret_cast<const u32x4*>(&sm.Kt[0]);
       const u32x4* psrc = reinterpret_cast<const u32x4*>(&sm.c.P[0][0]);
       u32x4* kdst = reinterpret_cast<u32x4*>(img + I::template kt_at<NW>());
-      const bool coh = a.publish != 0;
+      const bool coh = a.flags != nullptr;
 #pragma unroll
       for (int k = 0; k < NCP; ++k) {
         const int e = t + (NT - 64) * k;
@@ -747,7 +747,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
             acc = mfma(tl[m][kk], vbk[kk], acc);
           }
           st_out16(a.ws_u + u_off(ch, NVB, vb, w4, m, 0), 16 * lane, __builtin_bit_cast(u32x4, acc),
-                   a.publish != 0);
+                   a.flags != nullptr);
         }
       }
     }
@@ -790,9 +790,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         }
       }
       if (tid == 0) {
-        st_out(a.ws_wscale + ch, dW, a.publish != 0);
+        st_out(a.ws_wscale + ch, dW, a.flags != nullptr);
         const int goff = a.w_img_bytes ? I::template p_at<NW>() + I::P1 : I::template g_at<NW>();
-        st_out(reinterpret_cast<float*>(img + goff) + 129, dW, a.publish != 0);
+        st_out(reinterpret_cast<float*>(img + goff) + 129, dW, a.flags != nullptr);
         if (save) a.w_scale[ch] = dW;
       }
     }
@@ -803,7 +803,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       u32x4* dst = reinterpret_cast<u32x4*>(img);
       constexpr int NWP = NW * I::WQ / 8;          // 16-byte pieces of the W planes
       constexpr int NWB = I::WQ / 16;              // ... of the code bytes
-      const bool coh = a.publish != 0;
+      const bool coh = a.flags != nullptr;
       if (WF != 0 && a.w_img_bytes) {
 #pragma unroll
         for (int k = 0; k < (NWB + NT - 1) / NT; ++k)
@@ -816,7 +816,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     }
     // publishing to a concurrent state kernel: every wave waits for its
     // device-scope stores of this item, then after the barrier one flag store
-    if (a.publish) vm_drain();
+    if (a.flags) vm_drain();
     lds_barrier();                              // LDS is reused by the next item
     if (a.flags && tid == 0)
       __hip_atomic_store(a.flags + (int64_t)cur.slot * Hv + h, 1u, __ATOMIC_RELAXED,

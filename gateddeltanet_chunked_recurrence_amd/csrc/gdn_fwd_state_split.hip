@@ -474,7 +474,7 @@ gdn_state_split_kernel(FwdKernelArgs a, int N, int num_heads) {
     // flags (bounded to about 2^27 clocks per chunk, some 60 ms: on give-up
     // the error flag is set and the copies go on)
     auto wait_ready = [&](int c) {
-      if (!a.flags || c < a.c_split) return;
+      if (!a.flags) return;
       uint32_t* f = a.flags + chunk_ch(c);
       const uint64_t t0 = __builtin_amdgcn_s_memtime();
       while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {

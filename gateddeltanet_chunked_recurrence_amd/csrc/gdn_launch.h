@@ -32,12 +32,11 @@ struct FwdKernelArgs {
   int32_t w_img_bytes;        // 1: the W plane of the images holds code bytes (both QDQ sites on)
   // overlapped forward (gdn_chunk_fwd with equal-length sequences): the prep
   // kernel runs items [item_lo, item_hi) of the chunk-major order (chunk c of
-  // every sequence and head before chunk c + 1) and, when flags is set,
-  // sets each item's flag [slot * Hv + head] after its outputs; the state
-  // kernel waits for the flag of every chunk c >= c_split
+  // every sequence and head before chunk c + 1) and, when flags is set (a
+  // state kernel runs meanwhile), stores its outputs at device scope, drains
+  // them and then sets each item's flag [slot * Hv + head]; the state kernel
+  // waits for the flag of every chunk
   uint32_t* flags;            // nullable
-  int32_t publish;            // with flags: a state kernel runs meanwhile, so outputs are stored at
-                              // device scope and drained before the flag
   uint32_t* ticket;           // nullable: items are taken from this counter (zeroed per call), so
                               // the resident workgroups always hold the lowest items left; with
                               // item_split > 0, [0] over items below item_split (every workgroup),
@@ -46,7 +45,6 @@ struct FwdKernelArgs {
   int32_t item_split, prep_rest;
   int32_t item_lo, item_hi;   // item_hi == 0: every slot-major item [0, slots * Hv)
   int32_t chunk_major;        // 1: items in chunk-major order (no cu_seqlens)
-  int32_t c_split;            // chunks below this were finished before the state kernel started
   int32_t prep_blocks;        // prep grid size (0: one workgroup per CU)
   int32_t solve_degree;       // 0: exact (I + L)^-1; else the Neumann polynomial of this degree (2^j - 1)
   int32_t T;                  // tokens per sequence (no cu_seqlens)
