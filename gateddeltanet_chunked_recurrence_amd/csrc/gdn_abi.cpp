@@ -369,8 +369,8 @@ namespace {
 
 // Stages of the forward: 1 = prep (every chunk and head), 2 = state recurrence.
 // ------------------------------------------------------- overlapped forward
-// With equal-length sequences and both QDQ sites on (the split state
-// kernel), the state kernel's U = N Hv Dv / 64 workgroups leave CUs idle.
+// With equal-length sequences, the state kernel's U workgroups (N Hv Dv / 64,
+// or fewer with 128- or 256-wide scale tiles) leave CUs idle.
 // The forward then runs one prep launch on the caller's stream, taking the
 // (chunk, head) items in chunk-major order (chunk c of every sequence and
 // head before chunk c + 1) from a shared counter: the first H items on every
@@ -389,6 +389,13 @@ struct OverlapPlan {
   int items = -1;             // -1: run serially
   int head = 0, rest_blocks = 0;
 };
+
+// Prep time per (chunk, head) item over the state kernel's time per chunk
+// step beside it, measured on the B4 x T4096 x H16 x D128 workload: for the
+// split kernel about 10.1 us against 2.7 us; for the general kernel (QDQ off,
+// INT8 state with W off, 128-wide tiles) about 9.9 us against 5.5 to 5.8 us.
+constexpr double kSplitItemPerChunk = 3.7;
+constexpr double kGeneralItemPerChunk = 1.75;
 
 // GDN_NO_OVERLAP in the environment (read once): every call runs its stages
 // one after the other on the caller's stream. For profilers that serialize
@@ -409,17 +416,23 @@ int w_img_bytes_of(const gdn_fwd_args* a) {
 
 OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
   OverlapPlan op;
-  if (overlap_disabled() || !w_img_bytes_of(a) || a->cu_seqlens || a->io_dtype != GDN_BF16 ||
-      a->policy.read_fmt != 0)
+  if (overlap_disabled() || a->cu_seqlens || a->io_dtype != GDN_BF16 || a->policy.read_fmt != 0)
     return op;
   const int len = a->prefix_len > 0 ? std::min(a->T, a->prefix_len) : a->T;
   const int maxc = (len + 63) / 64;
   const int64_t nh = (int64_t)a->num_seqs * a->Hv;
-  const int64_t units = nh * (a->Dv / 64);                  // state workgroups
+  // state workgroups: 64 value columns each, or a whole 128- or 256-wide
+  // scale tile in the general kernel; and the measured prep time per item
+  // over the kernel's time per chunk step
+  const bool split = w_img_bytes_of(a) != 0;
+  const int cols = !split && a->policy.state_fmt != GDN_QDQ_OFF && a->policy.block_v > 64
+                       ? a->policy.block_v : 64;
+  const double item_per_chunk = split ? kSplitItemPerChunk : kGeneralItemPerChunk;
+  const int64_t units = nh * (a->Dv / cols);
   const int64_t rest = cus - units;
   if (maxc < 4 || rest < 16) return op;
   const int64_t items = (int64_t)maxc * nh;
-  const double h = (double)items - (double)rest * maxc / 3.7;
+  const double h = (double)items - (double)rest * maxc / item_per_chunk;
   const int64_t head = h <= 0.0 ? 0 : (int64_t)(h / cus + 0.5) * cus;
   if (head >= items) return op;
   op.items = (int)items;

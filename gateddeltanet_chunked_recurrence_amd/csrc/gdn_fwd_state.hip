@@ -21,6 +21,8 @@
 // Launch order pairs the value blocks of one head on one XCD (workgroup ids
 // congruent mod 8), so the second block's reads of Q and the images hit the
 // XCD's L2.
+#include <hip/hip_ext.h>
+
 #include "gdn_device.h"
 #include "gdn_images.h"
 #include "gdn_launch.h"
@@ -186,8 +188,25 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
     dW = a.ws_wscale[ch];
   };
 
+  // Beside a concurrent prep kernel (flags set): before its loads of chunk
+  // c's operands every wave sees that chunk's ready flag, bounded to about
+  // 2^27 clocks (on give-up the error flag is set and the work goes on).
+  auto wait_ready = [&](int c) {
+    if (!a.flags) return;
+    const uint32_t* fl = a.flags + chunk_ch(c);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (__builtin_amdgcn_s_memtime() - t0 > (1ull << 27)) {
+        if (lane == 0) __hip_atomic_fetch_or(a.err, kErrFlagWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+
   Stager<DK, NW, NWV> stg;
   stg.load_q(a, chunk_t0(0), chunk_nc(0), hk, tid);
+  wait_ready(0);
   Stager<DK, NW, NWV>::template dma_img<1>(a, chunk_ch(0), sm.buf[0], wave, lane, 0);
   load_small(0, Ucur, dWcur);
   stg.store_q(sm.buf[0], tid);
@@ -215,6 +234,7 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
     // staging of chunk c + 1 into the other buffer, issued in three parts
     // between the phases below so the loads drain while the chunk computes
     const bool more = C::NBUF == 2 && c + 1 < nchunks;
+    if (c + 1 < nchunks) wait_ready(c + 1);       // before any load of chunk c + 1's operands
     auto stage_part = [&](int part) {
       if constexpr (C::NBUF == 2) {
         if (more) Stager<DK, NW, NWV>::template dma_img<3>(a, chunk_ch(c + 1), sm.buf[(c + 1) & 1], wave, lane, part);
@@ -465,33 +485,40 @@ __global__ void __launch_bounds__(64 * NWV, 1) gdn_state_kernel(FwdKernelArgs a,
 }  // namespace
 
 template <int DK, int SF, int WF, int NWV, bool RF = false>
-static hipError_t launch_state_w(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+static hipError_t launch_state_w(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                                 hipEvent_t stop) {
   const int num_heads = cfg.N * cfg.Hv, nwb = cfg.Dv / (16 * NWV);
   const int64_t nblk = (int64_t)nwb * 8 * ((num_heads + 7) / 8);
-  hipLaunchKernelGGL((gdn_state_kernel<DK, SF, WF, NWV, RF>), dim3((unsigned)nblk), dim3(64 * NWV), 0,
-                     s, a, cfg.N, num_heads);
+  if (stop)
+    hipExtLaunchKernelGGL((gdn_state_kernel<DK, SF, WF, NWV, RF>), dim3((unsigned)nblk),
+                          dim3(64 * NWV), 0, s, nullptr, stop, 0, a, cfg.N, num_heads);
+  else
+    hipLaunchKernelGGL((gdn_state_kernel<DK, SF, WF, NWV, RF>), dim3((unsigned)nblk), dim3(64 * NWV),
+                       0, s, a, cfg.N, num_heads);
   return hipGetLastError();
 }
 
 // Value block width: the state scale tile when it is wider than 64 columns.
 template <int DK, int SF, int WF>
-static hipError_t launch_state_one(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+static hipError_t launch_state_one(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                                   hipEvent_t stop) {
   if constexpr (SF != 0) {
-    if (cfg.block_v == 256) return launch_state_w<DK, SF, WF, 16>(cfg, a, s);
-    if (cfg.block_v == 128) return launch_state_w<DK, SF, WF, 8>(cfg, a, s);
+    if (cfg.block_v == 256) return launch_state_w<DK, SF, WF, 16>(cfg, a, s, stop);
+    if (cfg.block_v == 128) return launch_state_w<DK, SF, WF, 8>(cfg, a, s, stop);
   } else {
     if (cfg.read_fmt != 0) {
-      if constexpr (DK == 128) return launch_state_w<DK, SF, WF, 4, true>(cfg, a, s);
+      if constexpr (DK == 128) return launch_state_w<DK, SF, WF, 4, true>(cfg, a, s, stop);
       return hipErrorInvalidValue;                 // the read copy is built for Dk = 128
     }
   }
-  return launch_state_w<DK, SF, WF, 4>(cfg, a, s);
+  return launch_state_w<DK, SF, WF, 4>(cfg, a, s, stop);
 }
 
 template <int DK>
-static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s) {
+static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
+                                  hipEvent_t stop) {
 #define GDN_CASE(SFv, WFv) \
-  if (cfg.state_fmt == SFv && cfg.w_fmt == WFv) return launch_state_one<DK, SFv, WFv>(cfg, a, s);
+  if (cfg.state_fmt == SFv && cfg.w_fmt == WFv) return launch_state_one<DK, SFv, WFv>(cfg, a, s, stop);
   GDN_CASE(0, 0) GDN_CASE(0, 1) GDN_CASE(0, 2)
   GDN_CASE(1, 0) GDN_CASE(1, 1) GDN_CASE(1, 2)
   GDN_CASE(2, 0) GDN_CASE(2, 1) GDN_CASE(2, 2)
@@ -502,9 +529,8 @@ static hipError_t launch_state_dk(const FwdConfig& cfg, const FwdKernelArgs& a, 
 hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t s,
                             hipEvent_t stop) {
   if (a.w_img_bytes) return launch_fwd_state_split(cfg, a, s, stop);
-  if (stop) return hipErrorInvalidValue;           // only the split kernel runs beside the prep
-  if (cfg.Dk == 128) return launch_state_dk<128>(cfg, a, s);
-  if (cfg.Dk == 64) return launch_state_dk<64>(cfg, a, s);
+  if (cfg.Dk == 128) return launch_state_dk<128>(cfg, a, s, stop);
+  if (cfg.Dk == 64) return launch_state_dk<64>(cfg, a, s, stop);
   return hipErrorInvalidValue;
 }
 

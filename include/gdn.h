@@ -193,9 +193,10 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
  * a->workspace of gdn_fwd_workspace_bytes(a) bytes (GDN_E_WORKSPACE if
  * missing or too small).
  * Overlapped schedule: with bf16 inputs, equal-length sequences (no
- * cu_seqlens), both QDQ sites on with block_v <= 64 and full-precision reads,
- * at least 4 chunks per sequence and at least 16 CUs that the state
- * recurrence's N * Hv * Dv / 64 workgroups leave free, the state recurrence
+ * cu_seqlens), full-precision reads (read_fmt off), at least 4 chunks per
+ * sequence and at least 16 CUs that the state recurrence's workgroups
+ * (N * Hv * Dv / 64, or N * Hv * Dv / block_v for 128- and 256-wide scale
+ * tiles) leave free, the state recurrence
  * starts once the first chunks' operands are built, and the remaining ones
  * are built meanwhile on those free CUs. The operand build runs on `stream`;
  * the state recurrence runs on a second stream that the library creates on

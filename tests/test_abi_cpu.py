@@ -92,8 +92,10 @@ def test_forward_rejects_before_launch(kw, status, msg):
 def test_forward_schedule_host_logic():
     """gdn_fwd_schedule: where gdn_chunk_fwd overlaps the operand build with
     the state recurrence, and how it splits the (chunk, head) items. The head
-    is items - R * chunks / 3.7 (R = CUs - N Hv Dv / 64) in whole rounds of
-    CUs; numbers worked by hand here."""
+    is items - R * chunks / r in whole rounds of CUs, R = CUs - the state
+    workgroups (N Hv Dv / 64, or Dv / block_v per head for 128- and 256-wide
+    tiles), r = 3.7 for the split state kernel (both QDQ sites on, tiles up
+    to 64 wide) and 1.75 for the general one; numbers worked by hand here."""
     big = dict(B=4, T=4096, Hqk=16, Hv=16, num_seqs=4)
     sch = B.fwd_schedule(_args(**big), 256)
     # 64 chunks x 64 (sequence, head) pairs; 128 state workgroups leave R = 128;
@@ -105,10 +107,21 @@ def test_forward_schedule_host_logic():
     # a long sequence: the remainder alone outlasts the chain, so no head
     sch = B.fwd_schedule(_args(B=1, T=65536, Hqk=32, Hv=32, Dv=256, num_seqs=1), 256)
     assert sch == dict(overlapped=True, items=32768, head_items=0, rest_blocks=128)
+    # the general state kernel: its chain alone outlasts the remainder
+    for kw in (dict(big, state_fmt=B.QDQ_OFF), dict(big, w_fmt=B.QDQ_OFF),
+               dict(big, state_fmt=B.QDQ_OFF, w_fmt=B.QDQ_OFF)):
+        assert B.fwd_schedule(_args(**kw), 256) == dict(overlapped=True, items=4096, head_items=0,
+                                                         rest_blocks=128), kw
+    # 128-wide tiles: one workgroup per head and tile, 64 in all, R = 192
+    assert B.fwd_schedule(_args(**dict(big, block_v=128)), 256) == dict(
+        overlapped=True, items=4096, head_items=0, rest_blocks=192)
+    # QDQ off with Dv 64 and 128 heads: 8192 items, R = 128;
+    # 8192 - 128 * 64 / 1.75 = 3510.9 -> 14 rounds of 256
+    many = dict(B=8, T=4096, Hqk=16, Hv=16, Dv=64, num_seqs=8, state_fmt=B.QDQ_OFF,
+                w_fmt=B.QDQ_OFF)
+    assert B.fwd_schedule(_args(**many), 256) == dict(overlapped=True, items=8192, head_items=3584,
+                                                       rest_blocks=128)
     serial = [
-        dict(big, state_fmt=B.QDQ_OFF),                     # no split state kernel
-        dict(big, w_fmt=B.QDQ_OFF),
-        dict(big, block_v=128),
         dict(big, state_fmt=B.QDQ_OFF, read_fmt=B.QDQ_E4M3),   # two-precision profile
         dict(big, io_dtype=B.GDN_F32, Dk=64, Dv=64),
         dict(big, T=192),                                   # 3 chunks

@@ -238,6 +238,13 @@ def test_fwd_fp16_operand_range_is_checked():
     # Dk 64, INT8 W, 32-wide scale tiles, ragged last chunk, h0
     ('fwd_e4m3_b4_t4096_h16_d128', dict(B=3, T=777, Hqk=2, Hv=6, Dk=64, Dv=64, w_fmt=INT8,
                                         block_v=32, h0=True)),
+    # the general state kernel: QDQ off, INT8 state with W off, 128- and 256-wide tiles
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=2048, state_fmt=OFF, w_fmt=OFF, h0=True)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=1500, Hqk=4, Hv=8, state_fmt=INT8, w_fmt=OFF)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=1000, Hqk=2, Hv=4, block_v=128, w_fmt=INT8)),
+    ('long_e4m3_t65536_h32_dk128_dv256', dict(T=2048, Hqk=4, Hv=4, block_v=256)),
+    ('fwd_e4m3_b4_t4096_h16_d128', dict(B=2, T=900, Hqk=2, Hv=2, Dk=64, Dv=128, state_fmt=OFF,
+                                        w_fmt=E4M3)),
 ])
 def test_fwd_overlapped_schedule_equals_serial(name, over):
     """gdn_chunk_fwd runs the prep's remainder concurrently with the state
@@ -270,12 +277,13 @@ def test_fwd_overlapped_schedule_equals_serial(name, over):
     say(f"  {name} {over}: overlapped == serial")
 
 
-def test_fwd_overlapped_reads_no_stale_workspace():
+@pytest.mark.parametrize("over", [dict(), dict(state_fmt=OFF, w_fmt=OFF)])
+def test_fwd_overlapped_reads_no_stale_workspace(over):
     """The overlapped forward reads each chunk's operands after its ready
     flag: with the workspace still holding another input's operands from the
     call before, every call equals the serial schedule on its own input."""
     import math
-    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=2, T=2048)
+    spec = gdn_inputs.spec('fwd_e4m3_b4_t4096_h16_d128', B=2, T=2048, **over)
     xs = [draw(spec, 41), draw(spec, 42)]
     kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
     sc = 1.0 / math.sqrt(spec['Dk'])
