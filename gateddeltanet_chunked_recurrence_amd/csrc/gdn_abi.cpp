@@ -191,7 +191,7 @@ gdn_saved_layout_t layout_of(const gdn_fwd_args* a) {
 // sections: the operand image block [W planes | K^T | P] (bf16), U and the W
 // scale (FP32).
 struct FwdWsLayout {
-  int64_t img, u, wscale, flags, total;
+  int64_t img, u, wscale, flags, vplan, total;
 };
 
 template <int DK>
@@ -204,6 +204,8 @@ FwdWsLayout fwd_ws_layout_dk(const gdn_fwd_args* a, int64_t nch) {
   w.u = off;       off += round256(nch * (int64_t)a->Dv * 64 * 4);
   w.wscale = off;  off += round256(nch * 4);
   w.flags = off;   off += round256(nch * 4 + 8);    // ready flags and two item counters of the overlapped forward
+  // its item table for packed sequences: [items, head, -, -] then (n Hv + head, chunk) per item
+  w.vplan = off;   off += a->cu_seqlens ? round256((2 * nch + 4) * 4) : 0;
   w.total = off;
   return w;
 }
@@ -386,8 +388,10 @@ namespace {
 // kernels, their arithmetic and its order are those of the serial schedule,
 // so the results are the same bits.
 struct OverlapPlan {
-  int items = -1;             // -1: run serially
+  int items = -1;             // -1: run serially; packed sequences: the upper bound slots * Hv
   int head = 0, rest_blocks = 0;
+  bool varlen = false;        // packed sequences: items and head are decided on the device
+  float item_per_chunk = 0.f;
 };
 
 // Prep time per (chunk, head) item over the state kernel's time per chunk
@@ -416,8 +420,10 @@ int w_img_bytes_of(const gdn_fwd_args* a) {
 
 OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
   OverlapPlan op;
-  if (overlap_disabled() || a->cu_seqlens || a->io_dtype != GDN_BF16 || a->policy.read_fmt != 0)
-    return op;
+  if (overlap_disabled() || a->io_dtype != GDN_BF16 || a->policy.read_fmt != 0) return op;
+  // packed sequences: the setup kernel's limits (1,024 sequences, 4,095
+  // chunks in the longest, which the total bounds)
+  if (a->cu_seqlens && (a->num_seqs > 1024 || (int64_t)a->B * a->T > 4095LL * 64)) return op;
   const int len = a->prefix_len > 0 ? std::min(a->T, a->prefix_len) : a->T;
   const int maxc = (len + 63) / 64;
   const int64_t nh = (int64_t)a->num_seqs * a->Hv;
@@ -430,7 +436,16 @@ OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
   const double item_per_chunk = split ? kSplitItemPerChunk : kGeneralItemPerChunk;
   const int64_t units = nh * (a->Dv / cols);
   const int64_t rest = cus - units;
-  if (maxc < 4 || rest < 16) return op;
+  if (rest < 16) return op;
+  if (a->cu_seqlens) {
+    op.items = (int)(layout_of(a).num_slots * a->Hv);
+    op.head = -1;
+    op.rest_blocks = (int)rest;
+    op.varlen = true;
+    op.item_per_chunk = (float)item_per_chunk;
+    return op;
+  }
+  if (maxc < 4) return op;
   const int64_t items = (int64_t)maxc * nh;
   const double h = (double)items - (double)rest * maxc / item_per_chunk;
   const int64_t head = h <= 0.0 ? 0 : (int64_t)(h / cus + 0.5) * cus;
@@ -485,7 +500,7 @@ int bwd_head_chunks(int maxc, int64_t nh) {
 }
 
 hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn::FwdKernelArgs k,
-                          const OverlapPlan& op, char* flags_mem, hipStream_t st) {
+                          const OverlapPlan& op, char* flags_mem, char* vplan_mem, hipStream_t st) {
   OverlapRes* r = overlap_res();
   if (!r) return hipErrorNotReady;
   const int num_slots = (int)layout_of(a).num_slots;
@@ -505,7 +520,19 @@ hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn:
   // The fork and join events are recorded by the launches themselves, at
   // their end, with no marker packet of their own.
   std::lock_guard<std::mutex> lk(r->mu);
-  hipError_t e = gdn::launch_fill_u32(flags, nflags + 2, 0u, st, r->fork);   // flags, two counters
+  hipError_t e;
+  if (op.varlen) {
+    // flags and counters zeroed, and the item table and head split built
+    // from the sequence lengths, by one kernel
+    prep.vplan = reinterpret_cast<const int32_t*>(vplan_mem);
+    prep.item_split = 0;
+    prep.prep_blocks = 0;
+    e = gdn::launch_varlen_setup(flags, nflags + 2, reinterpret_cast<int32_t*>(vplan_mem),
+                                 a->cu_seqlens, a->num_seqs, a->prefix_len, a->Hv,
+                                 gdn::device_cus(), op.rest_blocks, op.item_per_chunk, st, r->fork);
+  } else {
+    e = gdn::launch_fill_u32(flags, nflags + 2, 0u, st, r->fork);   // flags, two counters
+  }
   if (e != hipSuccess) return e;
   if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(r->s2, r->fork, 0)) != hipSuccess) return e;
@@ -560,7 +587,7 @@ gdn_status chunk_fwd_stages(const gdn_fwd_args* a, void* stream, int stages, boo
     const OverlapPlan op = overlap_plan(a, gdn::device_cus());
     // (without the second stream the same kernels run one after the other)
     if (op.items >= 0 && overlap_res())
-      return hip_status(run_overlapped(a, cfg, k, op, ws + W.flags, st),
+      return hip_status(run_overlapped(a, cfg, k, op, ws + W.flags, ws + W.vplan, st),
                         "gdn_chunk_fwd overlapped launch");
   }
   if (stages & 1) {
@@ -729,7 +756,7 @@ gdn_status gdn_fwd_schedule(const gdn_fwd_args* a, int32_t cus, int32_t* out) {
   if (cus < 0) return fail(GDN_E_INVALID, "cus %d < 0", cus);
   const OverlapPlan op = overlap_plan(a, cus > 0 ? cus : gdn::device_cus());
   out[0] = op.items >= 0 ? 1 : 0;
-  out[1] = op.items >= 0 ? op.items : 0;
+  out[1] = op.varlen ? -1 : (op.items >= 0 ? op.items : 0);
   out[2] = op.head;
   out[3] = op.rest_blocks;
   return GDN_OK;

@@ -213,6 +213,22 @@ __device__ PrepItem prep_item(const FwdKernelArgs& a, int N, int i) {
   // wave-uniform, so these become scalar loads, which no vector-memory wait
   // covers (a vector load here made every item start by waiting for the
   // previous item's stores)
+  if (a.vplan) {
+    // packed sequences, chunk-major from the setup kernel's table: item i is
+    // (n Hv + h, chunk c)
+    typedef const int32_t __attribute__((address_space(4)))* cptr;
+    const cptr tab = (cptr)a.vplan + 4, cu = (cptr)a.cu_seqlens;
+    const int code = tab[2 * i], c = tab[2 * i + 1], n = code / a.Hv;
+    const int bos = cu[n];
+    int eos = cu[n + 1];
+    if (a.prefix_len > 0) eos = min(eos, bos + a.prefix_len);
+    it.h = code - n * a.Hv;
+    it.slot = n + bos / CHUNK + c;
+    it.t0 = bos + CHUNK * c;
+    it.valid = it.t0 < eos;
+    it.nc = it.valid ? min(CHUNK, eos - it.t0) : 0;
+    return it;
+  }
   if (a.chunk_major) {
     // equal-length sequences, chunk c of every (sequence, head) before chunk
     // c + 1 (the overlapped forward): item = (c N + n) Hv + h
@@ -275,7 +291,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
   __shared__ __align__(16) PrepSmem<DK> sm;
 
   const int Hv = a.Hv, Hqk = a.Hqk;
-  const int total = a.item_hi > 0 ? a.item_hi : num_slots * Hv;
+  // (packed sequences in the overlapped forward: the item count and the head
+  // split come from the setup kernel's table)
+  const int total = a.vplan ? __builtin_amdgcn_readfirstlane(a.vplan[0])
+                            : (a.item_hi > 0 ? a.item_hi : num_slots * Hv);
+  const int split = a.vplan ? __builtin_amdgcn_readfirstlane(a.vplan[1]) : a.item_split;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int lane = fresh_lane(), tid = wave * 64 + lane, r16 = lane & 15, grp = lane >> 4;
   // per-lane LDS addresses are rebuilt in each phase, not kept live across the
@@ -311,9 +331,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
   const bool dyn = a.ticket != nullptr;
   auto take = [&]() -> int {                       // tid 0: the next item, or -1
     const int t = a.item_lo + (int)atomicAdd(a.ticket, 1u);
-    if (a.item_split <= 0 || t < a.item_split) return t < total ? t : -1;
+    if (a.prep_rest <= 0 || t < split) return t < total ? t : -1;
     if ((int)blockIdx.x >= a.prep_rest) return -1;
-    const int r = a.item_split + (int)atomicAdd(a.ticket + 1, 1u);
+    const int r = split + (int)atomicAdd(a.ticket + 1, 1u);
     return r < total ? r : -1;
   };
   PrepItem cur;

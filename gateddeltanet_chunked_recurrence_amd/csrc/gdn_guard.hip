@@ -60,7 +60,73 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
+// Zeroes n words at `zero` (grid-strided) and, in workgroup 0, builds the
+// overlapped forward's item table for packed sequences from their lengths.
+constexpr int kMaxSeqs = 1024, kMaxChunks = 4096;
+__global__ void __launch_bounds__(256) varlen_setup_kernel(uint32_t* zero, int64_t n, int32_t* plan,
+                                                           const int32_t* cu, int N, int prefix_len,
+                                                           int Hv, int cus, int rest, float ipc) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) zero[i] = 0u;
+  if (blockIdx.x != 0) return;
+  __shared__ int nc[kMaxSeqs], perm[kMaxSeqs], first[kMaxChunks + 1], mx;
+  const int tid = threadIdx.x;
+  if (tid == 0) mx = 0;
+  __syncthreads();
+  for (int s = tid; s < N; s += 256) {          // chunks of each sequence (prefix cap)
+    int len = cu[s + 1] - cu[s];
+    if (prefix_len > 0) len = min(len, prefix_len);
+    nc[s] = (len + 63) / 64;
+    atomicMax(&mx, nc[s]);
+  }
+  __syncthreads();
+  const int maxc = mx;
+  for (int s = tid; s < N; s += 256) {          // longest first, ties in sequence order
+    int r = 0;
+    for (int m = 0; m < N; ++m) r += nc[m] > nc[s] || (nc[m] == nc[s] && m < s);
+    perm[r] = s;
+  }
+  for (int c = tid; c <= maxc; c += 256) {      // items of the chunk indices below c
+    int k = 0;
+    for (int m = 0; m < N; ++m) k += min(nc[m], c);
+    first[c] = k * Hv;
+  }
+  __syncthreads();
+  const int items = first[maxc];
+  int32_t* tab = plan + 4;
+  for (int i = tid; i < items; i += 256) {
+    int lo = 0, hi = maxc - 1;                  // the chunk index c with first[c] <= i < first[c + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int idx = i - first[lo];              // (rank among the sequences that reach chunk lo, head)
+    tab[2 * i] = perm[idx / Hv] * Hv + idx % Hv;
+    tab[2 * i + 1] = lo;
+  }
+  if (tid == 0) {
+    const double h = (double)items - (double)rest * maxc / ipc;
+    int head = h <= 0.0 ? 0 : (int)(h / cus + 0.5) * cus;
+    if (head > items) head = items;
+    plan[0] = items;
+    plan[1] = head;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_varlen_setup(uint32_t* zero, int64_t n, int32_t* plan, const int32_t* cu_seqlens,
+                               int num_seqs, int prefix_len, int Hv, int cus, int rest,
+                               float item_per_chunk, hipStream_t s, hipEvent_t stop) {
+  if (num_seqs < 1 || num_seqs > kMaxSeqs) return hipErrorInvalidValue;
+  const int64_t blocks = (n + 255) / 256 < 1024 ? ((n + 255) / 256 > 0 ? (n + 255) / 256 : 1) : 1024;
+  if (stop)
+    hipExtLaunchKernelGGL(varlen_setup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, nullptr, stop, 0,
+                          zero, n, plan, cu_seqlens, num_seqs, prefix_len, Hv, cus, rest, item_per_chunk);
+  else
+    hipLaunchKernelGGL(varlen_setup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, zero, n, plan,
+                       cu_seqlens, num_seqs, prefix_len, Hv, cus, rest, item_per_chunk);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s, hipEvent_t stop) {
   if (n <= 0) return stop ? hipEventRecord(stop, s) : hipSuccess;

@@ -43,6 +43,10 @@ struct FwdKernelArgs {
                               // then [1] over the rest (only workgroups below prep_rest: the
                               // others end, and free their CUs)
   int32_t item_split, prep_rest;
+  // packed sequences (cu_seqlens): the chunk-major order comes from a table
+  // that varlen_setup_kernel builds from the lengths: [0] items, [1] the head
+  // (taking the place of item_split), then per item (n Hv + head, chunk)
+  const int32_t* vplan;       // nullable
   int32_t item_lo, item_hi;   // item_hi == 0: every slot-major item [0, slots * Hv)
   int32_t chunk_major;        // 1: items in chunk-major order (no cu_seqlens)
   int32_t prep_blocks;        // prep grid size (0: one workgroup per CU)
@@ -186,6 +190,15 @@ hipError_t launch_bwd_read_anchor(const BwdConfig& cfg, const BwdKernelArgs& a, 
 
 // Sets n words to v (a fill kernel: safe under graph capture, unlike a memset node).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s, hipEvent_t stop = nullptr);
+// Overlapped forward over packed sequences: zeroes the n words at `zero` (the
+// ready flags and item counters) and writes the prep's item table to `plan`
+// (see FwdKernelArgs::vplan): chunk-major, the sequences of each chunk index
+// longest first, and the head split H = items - rest maxc / item_per_chunk in
+// whole rounds of `cus` items (0 when negative, all items when past them).
+// Needs num_seqs <= 1024 and at most 4095 chunks per sequence.
+hipError_t launch_varlen_setup(uint32_t* zero, int64_t n, int32_t* plan, const int32_t* cu_seqlens,
+                               int num_seqs, int prefix_len, int Hv, int cus, int rest,
+                               float item_per_chunk, hipStream_t s, hipEvent_t stop);
 
 // Writes the stamp into the saved buffer's meta section.
 hipError_t launch_write_stamp(uint32_t* meta, const SavedStamp& st, hipStream_t s);

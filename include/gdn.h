@@ -192,9 +192,11 @@ size_t gdn_fwd_workspace_bytes(const gdn_fwd_args* a);
 /* Chunked forward. Writes o, and ht / saved when not NULL. Needs
  * a->workspace of gdn_fwd_workspace_bytes(a) bytes (GDN_E_WORKSPACE if
  * missing or too small).
- * Overlapped schedule: with bf16 inputs, equal-length sequences (no
- * cu_seqlens), full-precision reads (read_fmt off), at least 4 chunks per
- * sequence and at least 16 CUs that the state recurrence's workgroups
+ * Overlapped schedule: with bf16 inputs, full-precision reads (read_fmt off),
+ * either equal-length sequences with at least 4 chunks each, or packed
+ * sequences (cu_seqlens; at most 1,024 of them and 262,080 tokens in all,
+ * whose chunk order and split a setup kernel derives from the lengths on the
+ * device), and at least 16 CUs that the state recurrence's workgroups
  * (N * Hv * Dv / 64, or N * Hv * Dv / block_v for 128- and 256-wide scale
  * tiles) leave free, the state recurrence
  * starts once the first chunks' operands are built, and the remaining ones
@@ -217,7 +219,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
  * 0 one stage after the other; out[1] the (chunk, head) items of the
  * operand build; out[2] how many of them (whole rounds of cus, chunk-major)
  * run on every CU before the state recurrence starts; out[3] the workgroups
- * that build the rest meanwhile. Checks the shapes only; launches nothing.
+ * that build the rest meanwhile. For packed sequences out[1] and out[2] are
+ * -1: the device derives them from the sequence lengths. Checks the shapes only; launches nothing.
  * The call itself runs one stage after the other if it cannot create its
  * second stream. */
 gdn_status gdn_fwd_schedule(const gdn_fwd_args* a, int32_t cus, int32_t* out);

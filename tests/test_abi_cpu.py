@@ -127,11 +127,17 @@ def test_forward_schedule_host_logic():
         dict(big, T=192),                                   # 3 chunks
         dict(big, prefix_len=128),                          # 2 chunks
         dict(B=2, T=4096, Hqk=32, Hv=32, Dv=256, num_seqs=2),   # 256 state workgroups
-        dict(B=1, T=4096, Hqk=16, Hv=16, num_seqs=2, cu_seqlens=ctypes.c_void_p(0x20000)),
+        # packed sequences beyond the setup kernel's limits
+        dict(B=1, T=4096, Hqk=16, Hv=16, num_seqs=1025, cu_seqlens=ctypes.c_void_p(0x20000)),
+        dict(B=1, T=4095 * 64 + 1, Hqk=1, Hv=1, num_seqs=2, cu_seqlens=ctypes.c_void_p(0x20000)),
     ]
     for kw in serial:
         sch = B.fwd_schedule(_args(**kw), 256)
         assert sch['overlapped'] is False, kw
+    # packed sequences: the device derives the items and the head from the lengths
+    packed = dict(B=1, T=4096, Hqk=16, Hv=16, num_seqs=2, cu_seqlens=ctypes.c_void_p(0x20000))
+    assert B.fwd_schedule(_args(**packed), 256) == dict(overlapped=True, items=-1, head_items=-1,
+                                                         rest_blocks=192)
     with pytest.raises(B.GdnError):
         B.fwd_schedule(_args(**big), -1)
     with pytest.raises(B.GdnError):

@@ -304,3 +304,40 @@ def test_fwd_overlapped_reads_no_stale_workspace(over):
         assert B.device_errors() == 0
         assert torch.equal(plan.o, ref[i][0]) and torch.equal(plan.ht, ref[i][1]), i
     say("  overlapped calls alternating inputs on one workspace: each equals its serial run")
+
+
+@pytest.mark.parametrize("over", [
+    dict(),                                             # INT8 state, W off: the general kernel
+    dict(state_fmt=E4M3, w_fmt=E4M3),                   # both sites on: the split kernel
+    dict(lengths=[0, 700, 1, 130, 0, 2048], state_fmt=E4M3, w_fmt=INT8, block_v=32),
+])
+def test_fwd_overlapped_packed_equals_serial(over):
+    """Packed sequences (cu_seqlens) take the overlapped forward with an item
+    order and split that a setup kernel derives from the lengths on the
+    device (longest sequences first within each chunk index); o, ht and the
+    saved buffer equal the two stages run one after the other, with empty
+    and one-token sequences too, and no bounded wait gives up."""
+    import math
+    spec = gdn_inputs.spec('varlen_int8_gqa4x16_d128', **over)
+    x = draw(spec, 71)
+    kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+    sc = 1.0 / math.sqrt(spec['Dk'])
+    plan = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], sc, x['h0'], x['cu_seqlens'],
+                     save=True, **kw)
+    sch = plan.schedule()
+    assert sch['overlapped'] and sch['items'] == -1 and sch['head_items'] == -1
+    plan.saved.zero_()
+    plan.prep()
+    plan.state()
+    torch.cuda.synchronize()
+    assert B.device_errors() == 0
+    o_s, h_s, s_s = plan.o.clone(), plan.ht.clone(), plan.saved.clone()
+    for _ in range(2):
+        plan.saved.zero_()
+        plan.o.zero_()
+        plan.forward()
+        torch.cuda.synchronize()
+        assert B.device_errors() == 0
+        assert torch.equal(plan.o, o_s) and torch.equal(plan.ht, h_s)
+        assert torch.equal(plan.saved, s_s)
+    say(f"  packed {over}: overlapped == serial")
