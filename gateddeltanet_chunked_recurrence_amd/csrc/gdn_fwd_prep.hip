@@ -329,9 +329,17 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
   // so the state kernel never waits on an item no running workgroup holds.
   __shared__ int tk_next;
   const bool dyn = a.ticket != nullptr;
+  // With a split, counter [0] hands out the head (items below the split) to
+  // every workgroup and counter [1] the rest to the first prep_rest ones. Once
+  // counter [0] has passed the split it only grows, so a workgroup that has
+  // seen that goes straight to counter [1]: one atomic round trip per item.
+  bool in_rest = a.prep_rest > 0 && split <= 0;    // tid 0's: the head is gone
   auto take = [&]() -> int {                       // tid 0: the next item, or -1
-    const int t = a.item_lo + (int)atomicAdd(a.ticket, 1u);
-    if (a.prep_rest <= 0 || t < split) return t < total ? t : -1;
+    if (!in_rest) {
+      const int t = a.item_lo + (int)atomicAdd(a.ticket, 1u);
+      if (a.prep_rest <= 0 || t < split) return t < total ? t : -1;
+      in_rest = true;
+    }
     if ((int)blockIdx.x >= a.prep_rest) return -1;
     const int r = split + (int)atomicAdd(a.ticket + 1, 1u);
     return r < total ? r : -1;

@@ -39,9 +39,9 @@ struct FwdKernelArgs {
   uint32_t* flags;            // nullable
   uint32_t* ticket;           // nullable: items are taken from this counter (zeroed per call), so
                               // the resident workgroups always hold the lowest items left; with
-                              // item_split > 0, [0] over items below item_split (every workgroup),
-                              // then [1] over the rest (only workgroups below prep_rest: the
-                              // others end, and free their CUs)
+                              // prep_rest > 0, [0] over the items below item_split (every
+                              // workgroup), then [1] over the rest (only workgroups below
+                              // prep_rest: the others end, and free their CUs)
   int32_t item_split, prep_rest;
   // packed sequences (cu_seqlens): the chunk-major order comes from a table
   // that varlen_setup_kernel builds from the lengths: [0] items, [1] the head
