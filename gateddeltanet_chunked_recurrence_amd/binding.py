@@ -245,11 +245,12 @@ class FwdPlan:
     the two forward stages (prep, state) as separate calls on the current
     stream: plan.prep(); plan.state(), or both in one call: plan.forward().
     Outputs: plan.o, plan.ht, and plan.saved (the backward's saved buffer)
-    with save=True."""
+    with save=True; prefix_len > 0 runs only the first prefix_len tokens of
+    every sequence (the other rows of plan.o are not written)."""
 
     def __init__(self, q, k, v, g, beta, scale=None, h0=None, cu_seqlens=None,
                  state_fmt=QDQ_OFF, w_fmt=QDQ_OFF, block_v=64, solve_degree=0, read_fmt=QDQ_OFF,
-                 save=False):
+                 save=False, prefix_len=0):
         lib = load_library()
         dev = q.device
         B, T, Hqk, Dk = q.shape
@@ -260,7 +261,7 @@ class FwdPlan:
         self._keep = (q, k, v, g, beta, h0, cu_seqlens)
         self.args = make_fwd_args(q, k, v, g, beta, scale, h0, cu_seqlens, state_fmt, w_fmt,
                                   block_v, self.o, self.ht, solve_degree=solve_degree,
-                                  read_fmt=read_fmt)
+                                  read_fmt=read_fmt, prefix_len=prefix_len)
         self.saved = None
         if save:
             self.saved = torch.empty(lib.gdn_saved_bytes(ctypes.byref(self.args)), dtype=torch.uint8,

@@ -341,3 +341,41 @@ def test_fwd_overlapped_packed_equals_serial(over):
         assert torch.equal(plan.o, o_s) and torch.equal(plan.ht, h_s)
         assert torch.equal(plan.saved, s_s)
     say(f"  packed {over}: overlapped == serial")
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_fwd_overlapped_prefix_equals_serial(packed):
+    """With prefix_len (the prefill of a decode continuation) the overlapped
+    forward builds and consumes only the chunks of each sequence's prefix:
+    equal-length sequences size the schedule from the prefix, packed ones
+    cap every length in the setup kernel. o (prefix rows), ht and the saved
+    buffer equal the two stages in series."""
+    import math
+    over = dict(lengths=[300, 1500, 64, 2048, 0, 777]) if packed else dict(B=2, T=1024)
+    name = 'varlen_int8_gqa4x16_d128' if packed else 'fwd_e4m3_b4_t4096_h16_d128'
+    spec = gdn_inputs.spec(name, state_fmt=E4M3, w_fmt=E4M3, **over)
+    x = draw(spec, 73)
+    kw = dict(state_fmt=spec['state_fmt'], w_fmt=spec['w_fmt'], block_v=spec['block_v'])
+    sc = 1.0 / math.sqrt(spec['Dk'])
+    plan = B.FwdPlan(x['q'], x['k'], x['v'], x['g'], x['beta'], sc, x['h0'], x['cu_seqlens'],
+                     save=True, prefix_len=700, **kw)
+    sch = plan.schedule()
+    assert sch['overlapped']
+    if not packed:
+        assert sch['items'] == 11 * 2 * spec['Hv']      # 700 tokens: 11 chunks per sequence
+    plan.saved.zero_()
+    plan.o.zero_()
+    plan.prep()
+    plan.state()
+    torch.cuda.synchronize()
+    assert B.device_errors() == 0
+    o_s, h_s, s_s = plan.o.clone(), plan.ht.clone(), plan.saved.clone()
+    for _ in range(2):
+        plan.saved.zero_()
+        plan.o.zero_()
+        plan.forward()
+        torch.cuda.synchronize()
+        assert B.device_errors() == 0
+        assert torch.equal(plan.o, o_s) and torch.equal(plan.ht, h_s)
+        assert torch.equal(plan.saved, s_s)
+    say(f"  prefix 700, packed={packed}: overlapped == serial")
