@@ -203,7 +203,8 @@ FwdWsLayout fwd_ws_layout_dk(const gdn_fwd_args* a, int64_t nch) {
   w.img = off;     off += round256(nch * img * 2);
   w.u = off;       off += round256(nch * (int64_t)a->Dv * 64 * 4);
   w.wscale = off;  off += round256(nch * 4);
-  w.flags = off;   off += round256(nch * 4 + 8);    // ready flags and two item counters of the overlapped forward
+  // ready flags, two item counters and the CU admission table of the overlapped forward
+  w.flags = off;   off += round256(nch * 4 + 8 + gdn::kAdmitWords * 4);
   // its item table for packed sequences: [items, head, -, -] then (n Hv + head, chunk) per item
   w.vplan = off;   off += a->cu_seqlens ? round256((2 * nch + 4) * 4) : 0;
   w.total = off;
@@ -388,6 +389,7 @@ namespace {
 // kernels, their arithmetic and its order are those of the serial schedule,
 // so the results are the same bits.
 struct OverlapPlan {
+  bool two = false;   // two prep workgroups per CU, the rest on admitted CUs
   int items = -1;             // -1: run serially; packed sequences: the upper bound slots * Hv
   int head = 0, rest_blocks = 0;
   bool varlen = false;        // packed sequences: items and head are decided on the device
@@ -400,6 +402,9 @@ struct OverlapPlan {
 // INT8 state with W off, 128-wide tiles) about 9.9 us against 5.5 to 5.8 us.
 constexpr double kSplitItemPerChunk = 3.7;
 constexpr double kGeneralItemPerChunk = 1.75;
+// the same with two prep workgroups per CU (its CUs build items faster)
+constexpr double kSplitItemPerChunk2 = 3.0;
+constexpr double kGeneralItemPerChunk2 = 1.75;
 
 // GDN_NO_OVERLAP in the environment (read once): every call runs its stages
 // one after the other on the caller's stream. For profilers that serialize
@@ -447,9 +452,17 @@ OverlapPlan overlap_plan(const gdn_fwd_args* a, int cus) {
   }
   if (maxc < 4) return op;
   const int64_t items = (int64_t)maxc * nh;
-  const double h = (double)items - (double)rest * maxc / item_per_chunk;
+  // with two prep workgroups per CU (its CUs build items faster) where
+  // there is a head; the rest then runs on whole CUs that the admission
+  // table picks. Without a head one workgroup per CU builds every item
+  // beside the chain, which measured faster than two.
+  const bool two = gdn::prep_workgroups_per_cu(fwd_config(a), a->policy.solve_degree) == 2;
+  const double r2 = split ? kSplitItemPerChunk2 : kGeneralItemPerChunk2;
+  const double h2 = (double)items - (double)rest * maxc / r2;
+  const double h = two && h2 > 0.0 ? h2 : (double)items - (double)rest * maxc / item_per_chunk;
   const int64_t head = h <= 0.0 ? 0 : (int64_t)(h / cus + 0.5) * cus;
   if (head >= items) return op;
+  op.two = two && head > 0;
   op.items = (int)items;
   op.head = (int)head;
   op.rest_blocks = (int)rest;
@@ -514,6 +527,10 @@ hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn:
   prep.item_hi = op.items;
   prep.item_split = op.head;
   prep.prep_rest = op.rest_blocks;
+  // with two prep workgroups per CU the rest is built on the CUs that the
+  // admission table picks, from a launch over every CU; with one, by the
+  // first rest_blocks workgroups
+  prep.admit = op.two ? flags + nflags + 2 : nullptr;
   prep.prep_blocks = op.head > 0 ? 0 : op.rest_blocks;   // every CU while there is a head
   gdn::FwdKernelArgs state = k;
   state.flags = flags;
@@ -527,11 +544,11 @@ hipError_t run_overlapped(const gdn_fwd_args* a, const gdn::FwdConfig& cfg, gdn:
     prep.vplan = reinterpret_cast<const int32_t*>(vplan_mem);
     prep.item_split = 0;
     prep.prep_blocks = 0;
-    e = gdn::launch_varlen_setup(flags, nflags + 2, reinterpret_cast<int32_t*>(vplan_mem),
+    e = gdn::launch_varlen_setup(flags, nflags + 2 + gdn::kAdmitWords, reinterpret_cast<int32_t*>(vplan_mem),
                                  a->cu_seqlens, a->num_seqs, a->prefix_len, a->Hv,
                                  gdn::device_cus(), op.rest_blocks, op.item_per_chunk, st, r->fork);
   } else {
-    e = gdn::launch_fill_u32(flags, nflags + 2, 0u, st, r->fork);   // flags, two counters
+    e = gdn::launch_fill_u32(flags, nflags + 2 + gdn::kAdmitWords, 0u, st, r->fork);   // flags, counters, table
   }
   if (e != hipSuccess) return e;
   if ((e = gdn::launch_fwd_prep(cfg, prep, num_slots, st)) != hipSuccess) return e;

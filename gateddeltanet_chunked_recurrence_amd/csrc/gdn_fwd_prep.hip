@@ -17,10 +17,14 @@
 // split as hi + lo bf16 (two passes), so W and U carry ~16 mantissa bits of T
 // with FP32 accumulation. L, X and the merges stay FP32 throughout.
 //
-// Launch: persistent, one 8-wave workgroup per CU (two waves per SIMD), each
-// walking (chunk, head) items in slot-major order and loading the next item's
-// q, k, v, g, beta into registers while it computes the current one.
+// Launch: persistent 8-wave workgroups, each walking (chunk, head) items and
+// loading the next item's q, k, v, g, beta into registers while it computes
+// the current one. Two workgroups share a CU where the compact LDS layout
+// below fits (Dv <= 128, exact solve); the full layout runs one per CU (the
+// opt-in Neumann solve, Dv = 256, and overlapped launches without a head).
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_images.h"
@@ -32,16 +36,74 @@ namespace {
 
 constexpr int NT = 512;
 constexpr int NWAVE = NT / 64;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8 bytes at base + off (base wave-uniform, off < 2^31, 8-byte aligned): a
+// device-scope buffer store (cache policy sc1) when a concurrent kernel reads
+// them after a ready flag, else a plain store.
+__device__ __forceinline__ void st_out8(void* base, int off, u32x2 v, bool coh) {
+  if (coh) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFF0, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, off, 0, 16);
+  } else {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(base) + off) = v;
+  }
+}
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <int DK>
-struct PrepSmem {
+// One item's LDS, in one of two layouts with the same accessors.
+//
+// Compact (Dv <= 128, exact solve): regions are reused as their contents
+// die, so that it stays under 80 KB and two workgroups share a CU:
+//   a: K and Q rows (phase 1 to the L / P tiles), then K^T and V^T (written
+//      in the solve phase, read by W and U), then the W image planes;
+//   l: L (until the 32-block merge), then the T' hi / lo planes;
+//   x: X = (I + L)^-1 (until T is formed), then the T hi / lo planes.
+// P leaves for the image straight from the tiles' accumulators.
+template <int DK, int DV>
+struct PrepSmemTwo {
+  static constexpr bool TWO = true;
   static constexpr int LDK = DK + 8;             // K, Q rows (pperm over dk)
+  static constexpr int LS = 68;                  // row stride of the FP32 64 x 64 solve matrices
+  union {
+    struct { bf16 K[64 * LDK]; bf16 Q[64 * LDK]; } kq;
+    struct { bf16 Kt[DK * 64]; bf16 Vt[DV * 72]; } tv;   // K^T (r64_off), V^T (pperm over tokens)
+    bf16 W[2 * Img<DK>::WQ];                              // W image planes
+  } a;
+  union { float L[64 * LS]; bf16 T[2][64 * 64]; } l;      // L; T' hi / lo (r64_off)
+  union { float X[64 * LS]; bf16 T[2][64 * 64]; } x;      // X; T hi / lo (r64_off)
+  float Y[32 * 33];                              // 32-block merge scratch
+  alignas(16) float Ld[4][16 * 16];              // diagonal 16x16 blocks of L, row-major
+  alignas(16) float gam2[64];                    // log2-scaled gamma
+  alignas(16) float bet[64];
+  alignas(16) float eg[64];                      // exp(gamma)
+  alignas(16) float red[NWAVE];
+  __device__ bf16* Kt() { return a.tv.Kt; }
+  __device__ bf16* Vt() { return a.tv.Vt; }
+  __device__ float* Lm() { return l.L; }
+  __device__ float* Xm() { return x.X; }
+  __device__ float* Ym() { return Y; }
+  __device__ bf16* Wm() { return a.W; }
+  __device__ bf16* Tp(int i) { return l.T[i]; }   // T' hi, lo
+  __device__ bf16* Tt(int i) { return x.T[i]; }   // T hi, lo
+  __device__ static int t_off(int row, int c0) { return r64_off(row, pperm(c0)); }
+  __device__ static bf16x8 t_frag(const bf16* t, int row, int kk, int grp) { return ld_r64(t, row, 32 * kk, grp); }
+};
+
+// Full (Dv = 256, or the approximate inverse's four 64 x 64 buffers): every
+// operand in its own place, one workgroup per CU. P, and the T planes of
+// both kinds, sit in region c, and K^T leaves for the image with P during
+// the solve.
+template <int DK>
+struct PrepSmemOne {
+  static constexpr bool TWO = false;
+  static constexpr int LDK = DK + 8;
+  static constexpr int LS = 65;
   union {
     struct { bf16 K[64 * LDK]; bf16 Q[64 * LDK]; } kq;   // until the L / P tiles
     bf16 Vt[256 * 72];                                    // V^T (pperm over tokens)
   } a;
-  bf16 Kt[DK * 64];                              // K^T (pperm over tokens, r64_off)
+  bf16 Kt_[DK * 64];                             // K^T (pperm over tokens, r64_off)
   union {
     struct { float L[64 * 65]; float X[64 * 65]; } s;    // solve
     bf16 W[2 * Img<DK>::WQ];                              // W image planes
@@ -50,13 +112,30 @@ struct PrepSmem {
     bf16 P[2][64 * 64];                          // P hi / lo (r64_off), until copied out
     float Y[32 * 33];                            // 32-block merge scratch
     bf16 T[4][64 * 72];                          // T hi, T lo, T' hi, T' lo
+    float C[2][64 * 65];                         // the approximate inverse's two extra buffers
   } c;
-  alignas(16) float Ld[4][16 * 16];              // diagonal 16x16 blocks of L, row-major
-  alignas(16) float gam2[64];                    // log2-scaled gamma
+  alignas(16) float Ld[4][16 * 16];
+  alignas(16) float gam2[64];
   alignas(16) float bet[64];
-  alignas(16) float eg[64];                      // exp(gamma)
+  alignas(16) float eg[64];
   alignas(16) float red[NWAVE];
+  __device__ bf16* Kt() { return Kt_; }
+  __device__ bf16* Vt() { return a.Vt; }
+  __device__ float* Lm() { return b.s.L; }
+  __device__ float* Xm() { return b.s.X; }
+  __device__ float* Ym() { return c.Y; }
+  __device__ bf16* Wm() { return b.W; }
+  __device__ bf16* Tp(int i) { return c.T[2 + i]; }
+  __device__ bf16* Tt(int i) { return c.T[i]; }
+  __device__ static int t_off(int row, int c0) { return row * 72 + pperm(c0); }
+  __device__ static bf16x8 t_frag(const bf16* t, int row, int kk, int grp) { return lds_nat(t, row, 72, 32 * kk, grp); }
 };
+
+// Whether the compact layout fits two workgroups per CU (Dv <= 128).
+template <int DK, int DV>
+constexpr bool prep_fits_two() { return sizeof(PrepSmemTwo<DK, DV>) <= 80 * 1024; }
+template <int DK, int DV, bool CMP>
+using PrepSmem = std::conditional_t<CMP, PrepSmemTwo<DK, DV>, PrepSmemOne<DK>>;
 
 // The L and P tiles (mi >= mj) of one wave: all share the key block mj; kind
 // 0 is L(mi, mj), 1 is P(mi, mj). Every lower tile of each matrix appears once
@@ -89,8 +168,9 @@ __device__ __forceinline__ f32x4 mm32(const float* A, int ars, const float* B, i
 }
 
 // acc += A(16 ti + r, k) B(k, 16 tj + c) over the key blocks tj..ti of two
-// lower triangular FP32 64x65 matrices; a block's eight reads are issued
+// lower triangular FP32 64 x 64 matrices (row stride LS); a block's eight reads are issued
 // before its four products.
+template <int LS>
 __device__ __forceinline__ f32x4 mm_lower(const float* A, const float* B, int ti, int tj, int r16,
                                           int grp, f32x4 acc) {
 #pragma unroll
@@ -99,8 +179,8 @@ __device__ __forceinline__ f32x4 mm_lower(const float* A, const float* B, int ti
     float av[4], bv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      av[s] = A[(16 * ti + r16) * 65 + 16 * kb + 4 * s + grp];
-      bv[s] = B[(16 * kb + 4 * s + grp) * 65 + 16 * tj + r16];
+      av[s] = A[(16 * ti + r16) * LS + 16 * kb + 4 * s + grp];
+      bv[s] = B[(16 * kb + 4 * s + grp) * LS + 16 * tj + r16];
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma_f32(av[s], bv[s], acc);
@@ -279,16 +359,57 @@ __device__ PrepItem next_item(const FwdKernelArgs& a, int N, int i, int stride, 
   return it;
 }
 
+// Whether this workgroup's CU builds the rest of the items beside the state
+// kernel (two prep workgroups per CU). A CU is named by its XCC (XCC_ID) and
+// HW_ID bits 15:8 (cu, sh and se within the XCC). The state kernel's
+// workgroups are spread evenly over the XCCs and, within each, over its four
+// shader engines, and a workgroup can only start on a free CU of the engine
+// it is sent to; so the rest is kept on prep_rest / 32 CUs of every engine
+// (the remainder to the first engines). The first of a CU's workgroups to ask
+// takes one of its engine's places, or finds them gone; the other reads that
+// decision (bounded wait: on give-up it records kErrFlagWait and leaves the
+// rest to the others).
+__device__ bool admit_cu(const FwdKernelArgs& a) {
+  const uint32_t key = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 8) & 0xFFu;   // HW_ID
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 7u;            // XCC_ID
+  const int se = (int)(key >> 5) & 3, slot = (int)xcc * 4 + se;
+  uint32_t* tab = a.admit + xcc * kAdmitPerXcc;
+  const int quota = a.prep_rest / 32 + (slot < a.prep_rest % 32 ? 1 : 0);
+  uint32_t st = atomicCAS(tab + key, 0u, 3u);      // 0 open, 3 deciding, 1 admitted, 2 refused
+  if (st == 0u) {
+    st = (int)atomicAdd(tab + 256 + se, 1u) < quota ? 1u : 2u;
+    __hip_atomic_store(tab + key, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return st == 1u;
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  while (st == 3u) {
+    if (__builtin_amdgcn_s_memtime() - t0 > (1ull << 27)) {
+      __hip_atomic_fetch_or(a.err, kErrFlagWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    st = __hip_atomic_load(tab + key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return st == 1u;
+}
+
 // NEU: the instantiation that carries the approximate inverse (the exact-solve
-// instantiation does not contain its code).
-template <int DK, int DV, int WF, bool NEU>
-__global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
+// instantiation does not contain its code). CMP: the compact layout, two
+// workgroups per CU.
+// (the second launch bound is the minimum of waves per SIMD: two 8-wave
+// workgroups per CU need four, which caps a wave at 128 VGPRs)
+template <int DK, int DV, int WF, bool NEU, bool CMP>
+__global__ void __launch_bounds__(NT, (CMP ? 4 : 1))
+gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
   using I = Img<DK>;
-  constexpr int LDK = PrepSmem<DK>::LDK;
+  static_assert(!CMP || (!NEU && prep_fits_two<DK, DV>()), "the compact layout: exact solve, Dv <= 128");
+  using Sm = PrepSmem<DK, DV, CMP>;
+  constexpr int LDK = Sm::LDK;
+  constexpr int LS = Sm::LS;
   constexpr int NW = WF == 0 ? 2 : 1;
   constexpr int NCTW = DK / 32;                   // W column tiles per wave (two waves per row tile)
   constexpr int NVB = DV / 64;
-  __shared__ __align__(16) PrepSmem<DK> sm;
+  __shared__ __align__(16) Sm sm;
 
   const int Hv = a.Hv, Hqk = a.Hqk;
   // (packed sequences in the overlapped forward: the item count and the head
@@ -334,13 +455,17 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
   // counter [0] has passed the split it only grows, so a workgroup that has
   // seen that goes straight to counter [1]: one atomic round trip per item.
   bool in_rest = a.prep_rest > 0 && split <= 0;    // tid 0's: the head is gone
+  // tid 0's: whether this workgroup builds the rest (by workgroup index with
+  // one per CU, by CU with two; decided when the head is gone)
+  int member = a.admit ? -1 : ((int)blockIdx.x < a.prep_rest ? 1 : 0);
   auto take = [&]() -> int {                       // tid 0: the next item, or -1
     if (!in_rest) {
       const int t = a.item_lo + (int)atomicAdd(a.ticket, 1u);
       if (a.prep_rest <= 0 || t < split) return t < total ? t : -1;
       in_rest = true;
     }
-    if ((int)blockIdx.x >= a.prep_rest) return -1;
+    if (member < 0) member = admit_cu(a) ? 1 : 0;
+    if (member == 0) return -1;
     const int r = split + (int)atomicAdd(a.ticket + 1, 1u);
     return r < total ? r : -1;
   };
@@ -372,17 +497,27 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     const int64_t ch = (int64_t)cur.slot * Hv + h;
     bf16* img = a.ws_img + ch * I::template img<NW>();   // [W planes | K^T | P | gates]
 
-    // ---- 1. K, Q rows (pperm over dk), K^T (LDS + image) and gates from registers
-    // P upper tiles (0, 1) and (2, 3) are read as zeros by the state kernel
+    // ---- 1. K, Q rows (pperm over dk) and gates from registers (the full
+    // layout: K^T too). P upper tiles (0, 1) and (2, 3), which the state
+    // kernel reads as zeros, are zeroed: in the image (compact layout; one
+    // plane in the byte variant) or in the LDS P tile
+    if constexpr (Sm::TWO) {
+      const bool coh = a.flags != nullptr;
+      const int pl = tid >> 7, e = tid & 127, t = e >> 6, r = (e >> 2) & 15, g = e & 3;
+      if (tid < (a.w_img_bytes ? 128 : 256))
+        st_out8(img, 2 * (I::template p_at<NW>() + pl * I::P1 + r64_off(32 * t + r, pperm(32 * t + 16 + 4 * g))),
+                u32x2{0u, 0u}, coh);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 2 * 2 * 256 / NT; ++k) {
-      const int e = tid + NT * k;
-      const int pl = e >> 9, t = (e >> 8) & 1, r = (e >> 4) & 15, cc = e & 15;
-      sm.c.P[pl][r64_off(32 * t + r, pperm(32 * t + 16 + cc))] = to_bf16(0.f);
+      for (int k = 0; k < 2 * 2 * 256 / NT; ++k) {
+        const int e = tid + NT * k;
+        const int pl = e >> 9, t = (e >> 8) & 1, r = (e >> 4) & 15, cc = e & 15;
+        sm.c.P[pl][r64_off(32 * t + r, pperm(32 * t + 16 + cc))] = to_bf16(0.f);
+      }
     }
     ks.store_rows(sm.a.kq.K, LDK, wave, lane);
     qs.store_rows(sm.a.kq.Q, LDK, wave, lane);
-    ks.template store_t<true>(sm.Kt, nullptr, wave, lane);   // the image copy goes out during the solve
+    if constexpr (!Sm::TWO) ks.template store_t<true>(sm.Kt(), nullptr, wave, lane);   // the image copy goes out during the solve
     if (wave == 0) {
       const float gv = lane < nc ? graw : 0.f;
       const float g2 = wave_incl_scan(gv * LOG2E);
@@ -449,7 +584,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
           const int row = 16 * mi + 4 * grp + i;
           const float e = fexp2(gr4[i] - gj);
           const float lv = row > cj ? br4[i] * acc[i] * e : 0.f;
-          sm.b.s.L[row * 65 + cj] = lv;
+          sm.Lm()[row * LS + cj] = lv;
           if (mi == mj) sm.Ld[mi][(4 * grp + i) * 16 + r16] = lv;   // aligned copy for the substitution
         }
       } else {
@@ -461,6 +596,16 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = row >= c0 + i ? acc[i] * fexp2(gr1 - gc[i]) : 0.f;
+        // straight to the image (8 bytes per lane and plane) in the compact
+        // layout, else to the LDS tile, copied out during the solve
+        const int po = 2 * (I::template p_at<NW>() + r64_off(row, pperm(c0)));
+        const bool coh = a.flags != nullptr;
+        auto put = [&](int plane, u32x2 v) {
+          if constexpr (Sm::TWO)
+            st_out8(img, po + 2 * plane * I::P1, v, coh);
+          else
+            *reinterpret_cast<u32x2*>(&sm.c.P[plane][r64_off(row, pperm(c0))]) = v;
+        };
         if (a.w_img_bytes) {
           // one fp16 plane (11-bit significand: relative error <= 2^-12). Its
           // range is +-65504: an entry beyond it (|q . k| that large, which
@@ -470,13 +615,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
             __hip_atomic_fetch_or(a.err, kErrPRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
           const f16x4 h = f16x4{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
-          *reinterpret_cast<f16x4*>(&sm.c.P[0][r64_off(row, pperm(c0))]) = h;
+          put(0, __builtin_bit_cast(u32x2, h));
         } else {
           bf16 hi[4], lo[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) split2(pv[i], hi[i], lo[i]);
-          st4(&sm.c.P[0][r64_off(row, pperm(c0))], hi[0], hi[1], hi[2], hi[3]);
-          st4(&sm.c.P[1][r64_off(row, pperm(c0))], lo[0], lo[1], lo[2], lo[3]);
+          put(0, __builtin_bit_cast(u32x2, bf16x4{hi[0], hi[1], hi[2], hi[3]}));
+          put(1, __builtin_bit_cast(u32x2, bf16x4{lo[0], lo[1], lo[2], lo[3]}));
         }
       }
     }
@@ -484,10 +629,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     lds_barrier();
     GDN_REFRESH();
 
-    // ---- 3. wave 0: diagonal blocks of X; others: P image out, X upper zero, V^T in
+    // ---- 3. wave 0: diagonal blocks of X; others: X upper zero, V^T in, and
+    // (full layout) the K^T and P images out; in the compact layout every
+    // wave writes its part of K^T (the K, Q rows are dead)
     // (the approximate-inverse instantiation skips the solve's arithmetic here
     // and in the merges below, keeping their loads and barriers: X is formed
     // from L after this phase)
+    if constexpr (Sm::TWO) ks.template store_t<true>(sm.Kt(), nullptr, wave, lane);   // copied out in the merges
     if (wave == 0) {
       if constexpr (!NEU) {
       // lane (b, cc): column cc of the inverse of diagonal block b, by rows;
@@ -521,36 +669,38 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         x[r] = s;
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.b.s.X[(16 * b + r) * 65 + 16 * b + cc] = x[r];
+      for (int r = 0; r < 16; ++r) sm.Xm()[(16 * b + r) * LS + 16 * b + cc] = x[r];
       }
     } else {
       const int t = tid - 64;
-      // K^T and P images: 16-byte copies of the LDS tiles (adjacent in the
-      // image, as they are in LDS), fixed trip counts
-      static_assert(sizeof(sm.c.P) == 2 * I::P1 * 2, "P tile is the image's P section");
-      constexpr int NKP = (I::KT + 2 * I::P1) / 8, NCP = (NKP + NT - 65) / (NT - 64);
-      // one P plane in the byte variant: its second slot holds the gate block
-      const int nkp = a.w_img_bytes ? (I::KT + I::P1) / 8 : NKP;
-      const u32x4* ksrc = reinterpret_cast<const u32x4*>(&sm.Kt[0]);
-      const u32x4* psrc = reinterpret_cast<const u32x4*>(&sm.c.P[0][0]);
-      u32x4* kdst = reinterpret_cast<u32x4*>(img + I::template kt_at<NW>());
-      const bool coh = a.flags != nullptr;
+      if constexpr (!Sm::TWO) {
+        // K^T and P images: 16-byte copies of the LDS tiles (adjacent in the
+        // image, as they are in LDS), fixed trip counts
+        static_assert(sizeof(sm.c.P) == 2 * I::P1 * 2, "P tile is the image's P section");
+        constexpr int NKP = (I::KT + 2 * I::P1) / 8, NCP = (NKP + NT - 65) / (NT - 64);
+        // one P plane in the byte variant: its second slot holds the gate block
+        const int nkp = a.w_img_bytes ? (I::KT + I::P1) / 8 : NKP;
+        const u32x4* ksrc = reinterpret_cast<const u32x4*>(sm.Kt());
+        const u32x4* psrc = reinterpret_cast<const u32x4*>(&sm.c.P[0][0]);
+        u32x4* kdst = reinterpret_cast<u32x4*>(img + I::template kt_at<NW>());
+        const bool coh = a.flags != nullptr;
 #pragma unroll
-      for (int k = 0; k < NCP; ++k) {
-        const int e = t + (NT - 64) * k;
-        if (e < nkp) st_out16(kdst, 16 * e, e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8], coh);
+        for (int k = 0; k < NCP; ++k) {
+          const int e = t + (NT - 64) * k;
+          if (e < nkp) st_out16(kdst, 16 * e, e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8], coh);
+        }
       }
       for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
         const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
         const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
         const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        sm.b.s.X[(16 * bi + r) * 65 + 16 * bj + cc] = 0.f;
+        sm.Xm()[(16 * bi + r) * LS + 16 * bj + cc] = 0.f;
       }
-      vs.store_t(sm.a.Vt, nullptr, wave, lane);   // K, Q rows are dead; V^T for U
+      vs.store_t(sm.Vt(), nullptr, wave, lane);   // V^T for U
     }
     lds_barrier();
     GDN_REFRESH();
-    if (wave == 0) vs.store_t(sm.a.Vt, nullptr, wave, lane);
+    if (wave == 0) vs.store_t(sm.Vt(), nullptr, wave, lane);
     // The next item's loads are issued where most waves have no other work
     // (issue stalls while the CU's memory path is busy): K, Q, g, beta here,
     // the merging waves after their merge; V in the X_BA phase. Every
@@ -561,16 +711,27 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     if (merger) {
       if constexpr (!NEU) {
         const int A = 2 * (wave - 1), B = A + 1;
-        const f32x4 y = mm32(&sm.b.s.L[(16 * B) * 65 + 16 * A], 65, &sm.b.s.X[(16 * A) * 65 + 16 * A],
-                             65, 0, 0, 0, 16, r16, grp, zero4());
+        const f32x4 y = mm32(&sm.Lm()[(16 * B) * LS + 16 * A], LS, &sm.Xm()[(16 * A) * LS + 16 * A],
+                             LS, 0, 0, 0, 16, r16, grp, zero4());
         f32x4 z = zero4();
 #pragma unroll
         for (int i = 0; i < 4; ++i)               // K order 4 grp + i
-          z = mfma_f32(sm.b.s.X[(16 * B + r16) * 65 + 16 * B + 4 * grp + i], y[i], z);
+          z = mfma_f32(sm.Xm()[(16 * B + r16) * LS + 16 * B + 4 * grp + i], y[i], z);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.b.s.X[(16 * B + 4 * grp + i) * 65 + 16 * A + r16] = -z[i];
+        for (int i = 0; i < 4; ++i) sm.Xm()[(16 * B + 4 * grp + i) * LS + 16 * A + r16] = -z[i];
       }
       if (nxt.valid) load_kqg(nxt);
+    } else if constexpr (Sm::TWO) {
+      // K^T image: 16-byte copies of the LDS tile by the six other waves
+      const int t = wave == 0 ? lane : tid - 128;
+      constexpr int NKT = I::KT / 8, NCK = (NKT + 383) / 384;
+      const u32x4* ksrc = reinterpret_cast<const u32x4*>(sm.Kt());
+      const bool coh = a.flags != nullptr;
+#pragma unroll
+      for (int k = 0; k < NCK; ++k) {
+        const int e = t + 384 * k;
+        if (e < NKT) st_out16(img + I::template kt_at<NW>(), 16 * e, ksrc[e], coh);
+      }
     }
     lds_barrier();
     GDN_REFRESH();
@@ -580,9 +741,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       const int t4 = wave & 3, ti = t4 >> 1, tj = t4 & 1, kh = wave >> 2;
       const int k0 = 16 * tj, km = 16 + 8 * tj;    // X_AA rows < 16 tj are zero in column tile tj
       f32x4 y = zero4();
-      float* yp = &sm.c.Y[(16 * ti + 4 * grp) * 33 + 16 * tj + r16];
+      float* yp = &sm.Ym()[(16 * ti + 4 * grp) * 33 + 16 * tj + r16];
       if constexpr (!NEU) {
-        y = mm32(&sm.b.s.L[32 * 65], 65, sm.b.s.X, 65, 16 * ti, 16 * tj, kh ? km : k0, kh ? 32 : km,
+        y = mm32(&sm.Lm()[32 * LS], LS, sm.Xm(), LS, 16 * ti, 16 * tj, kh ? km : k0, kh ? 32 : km,
                  r16, grp, zero4());
         if (kh == 0) {
 #pragma unroll
@@ -602,10 +763,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     if (wave < 4) {
       if constexpr (!NEU) {
         const int ti = wave >> 1, tj = wave & 1;
-        const f32x4 z = mm32(&sm.b.s.X[32 * 65 + 32], 65, sm.c.Y, 33, 16 * ti, 16 * tj, 0,
+        const f32x4 z = mm32(&sm.Xm()[32 * LS + 32], LS, sm.Ym(), 33, 16 * ti, 16 * tj, 0,
                              16 * ti + 16, r16, grp, zero4());
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.b.s.X[(32 + 16 * ti + 4 * grp + i) * 65 + 16 * tj + r16] = -z[i];
+        for (int i = 0; i < 4; ++i) sm.Xm()[(32 + 16 * ti + 4 * grp + i) * LS + 16 * tj + r16] = -z[i];
       }
       if (nxt.valid) load_v(nxt);
     }
@@ -618,19 +779,19 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     // (-L)^(2^i), each step squares P and sets X <- X + X P. The factors are
     // lower triangular, so an output tile (ti, tj), ti >= tj, sums the key
     // blocks tj..ti only; upper tiles of X are written as zero, those of P are
-    // never read. FP32 MFMA; four 64x65 buffers rotate: L, X and two in the
-    // T-plane area, which phase 4 fills only after this.
+    // never read. FP32 MFMA; four 64 x 64 buffers rotate: L, X and the two
+    // extra ones of this instantiation.
     if constexpr (NEU) {
-      static_assert(sizeof(sm.c) >= 2 * 64 * 65 * sizeof(float), "two FP32 64x65 buffers");
-      float* const C0 = reinterpret_cast<float*>(&sm.c);
+      static_assert(!Sm::TWO, "the approximate inverse runs in the full layout");
+      float* const C0 = sm.c.C[0];
       auto buf = [&](int b) -> float* {
-        return b == 0 ? sm.b.s.L : (b == 1 ? sm.b.s.X : (b == 2 ? C0 : C0 + 64 * 65));
+        return b == 0 ? sm.Lm() : (b == 1 ? sm.Xm() : (b == 2 ? C0 : sm.c.C[1]));
       };
       for (int e = tid; e < 64 * 64; e += NT) {
         const int i = e >> 6, j = e & 63;
-        const float l = (i >> 4) >= (j >> 4) ? sm.b.s.L[i * 65 + j] : 0.f;   // strict lower (masked)
-        C0[i * 65 + j] = -l;
-        sm.b.s.X[i * 65 + j] = j > i ? 0.f : (i == j ? 1.f : -l);
+        const float l = (i >> 4) >= (j >> 4) ? sm.Lm()[i * LS + j] : 0.f;   // strict lower (masked)
+        C0[i * LS + j] = -l;
+        sm.Xm()[i * LS + j] = j > i ? 0.f : (i == j ? 1.f : -l);
       }
       lds_barrier();
       int ip = 2, ix = 1;                          // P = -L in buffer 2, X = I - L in buffer 1
@@ -643,9 +804,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           if (ti[hh] >= tj[hh]) {
-            const f32x4 z = mm_lower(P, P, ti[hh], tj[hh], r16, grp, zero4());
+            const f32x4 z = mm_lower<LS>(P, P, ti[hh], tj[hh], r16, grp, zero4());
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Pn[(16 * ti[hh] + 4 * grp + i) * 65 + 16 * tj[hh] + r16] = z[i];
+            for (int i = 0; i < 4; ++i) Pn[(16 * ti[hh] + 4 * grp + i) * LS + 16 * tj[hh] + r16] = z[i];
           }
         }
         lds_barrier();
@@ -656,11 +817,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
           f32x4 z = zero4();
           if (ti[hh] >= tj[hh]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = X[(16 * ti[hh] + 4 * grp + i) * 65 + 16 * tj[hh] + r16];
-            z = mm_lower(X, Pn, ti[hh], tj[hh], r16, grp, z);
+            for (int i = 0; i < 4; ++i) z[i] = X[(16 * ti[hh] + 4 * grp + i) * LS + 16 * tj[hh] + r16];
+            z = mm_lower<LS>(X, Pn, ti[hh], tj[hh], r16, grp, z);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Xn[(16 * ti[hh] + 4 * grp + i) * 65 + 16 * tj[hh] + r16] = z[i];
+          for (int i = 0; i < 4; ++i) Xn[(16 * ti[hh] + 4 * grp + i) * LS + 16 * tj[hh] + r16] = z[i];
         }
         lds_barrier();
         ip = np;
@@ -670,7 +831,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         const float* X = buf(ix);
         for (int e = tid; e < 64 * 64; e += NT) {
           const int i = e >> 6, j = e & 63;
-          sm.b.s.X[i * 65 + j] = X[i * 65 + j];
+          sm.Xm()[i * LS + j] = X[i * LS + j];
         }
         lds_barrier();
       }
@@ -682,30 +843,53 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       float* xg = a.s_X + ch * 4096;
       for (int e = tid; e < 1024; e += NT) {
         const int row = e >> 4, c4 = e & 15;
-        const float* xs = &sm.b.s.X[row * 65 + 4 * c4];
+        const float* xs = &sm.Xm()[row * LS + 4 * c4];
         *reinterpret_cast<f32x4*>(xg + row * 64 + 4 * c4) = f32x4{xs[0], xs[1], xs[2], xs[3]};
       }
     }
-    // ---- 4. T = X diag(beta), T' = T diag(exp(gamma)) as hi / lo planes (pperm over columns)
+    // ---- 4. T = X diag(beta), T' = T diag(exp(gamma)) as hi / lo planes (pperm
+    // over columns). In the compact layout T' goes over L (dead since the
+    // merges) and T over X once every wave has read its part of X.
     {
       const int row = tid >> 3, q = tid & 7;
+      bf16 th[2][4], tl[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c0 = 8 * q + 4 * u;
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sm.bet[c0]);
         const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sm.eg[c0]);
-        bf16 th[4], tl[4], ph[4], pl[4];
+        float xv[4];
+        if constexpr (Sm::TWO) {
+          const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sm.Xm()[row * LS + c0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[e] = x4[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[e] = sm.Xm()[row * LS + c0 + e];
+        }
+        bf16 ph[4], pl[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float t = sm.b.s.X[row * 65 + c0 + e] * b4[e];
-          split2(t, th[e], tl[e]);
+          const float t = xv[e] * b4[e];
+          split2(t, th[u][e], tl[u][e]);
           split2(t * e4[e], ph[e], pl[e]);
         }
-        const int o = row * 72 + pperm(c0);
-        st4(&sm.c.T[0][o], th[0], th[1], th[2], th[3]);
-        st4(&sm.c.T[1][o], tl[0], tl[1], tl[2], tl[3]);
-        st4(&sm.c.T[2][o], ph[0], ph[1], ph[2], ph[3]);
-        st4(&sm.c.T[3][o], pl[0], pl[1], pl[2], pl[3]);
+        const int o = Sm::t_off(row, c0);
+        if constexpr (!Sm::TWO) {
+          st4(sm.Tt(0) + o, th[u][0], th[u][1], th[u][2], th[u][3]);
+          st4(sm.Tt(1) + o, tl[u][0], tl[u][1], tl[u][2], tl[u][3]);
+        }
+        st4(sm.Tp(0) + o, ph[0], ph[1], ph[2], ph[3]);
+        st4(sm.Tp(1) + o, pl[0], pl[1], pl[2], pl[3]);
+      }
+      if constexpr (Sm::TWO) {
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int o = Sm::t_off(row, 8 * q + 4 * u);
+          st4(sm.Tt(0) + o, th[u][0], th[u][1], th[u][2], th[u][3]);
+          st4(sm.Tt(1) + o, tl[u][0], tl[u][1], tl[u][2], tl[u][3]);
+        }
       }
     }
     lds_barrier();
@@ -718,8 +902,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
       bf16x8 ah[2], al[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        ah[kk] = lds_nat(sm.c.T[2], 16 * mt + r16, 72, 32 * kk, grp);
-        al[kk] = lds_nat(sm.c.T[3], 16 * mt + r16, 72, 32 * kk, grp);
+        ah[kk] = Sm::t_frag(sm.Tp(0), 16 * mt + r16, kk, grp);
+        al[kk] = Sm::t_frag(sm.Tp(1), 16 * mt + r16, kk, grp);
       }
       // computed transposed (W^T = K^T T'^T, the same fragments with A and B
       // swapped): a lane then holds four adjacent dk of one token, which go
@@ -731,7 +915,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (kk > mt / 2) continue;              // T' is lower triangular
-          const bf16x8 b = ld_r64(sm.Kt, 16 * ct + r16, 32 * kk, grp);
+          const bf16x8 b = ld_r64(sm.Kt(), 16 * ct + r16, 32 * kk, grp);
           acc = mfma(b, ah[kk], acc);
           acc = mfma(b, al[kk], acc);
         }
@@ -757,14 +941,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (kk > m / 2) continue;
-          th[m][kk] = lds_nat(sm.c.T[0], 16 * m + r16, 72, 32 * kk, grp);
-          tl[m][kk] = lds_nat(sm.c.T[1], 16 * m + r16, 72, 32 * kk, grp);
+          th[m][kk] = Sm::t_frag(sm.Tt(0), 16 * m + r16, kk, grp);
+          tl[m][kk] = Sm::t_frag(sm.Tt(1), 16 * m + r16, kk, grp);
         }
       for (int vb = wave >> 2; vb < NVB; vb += 2) {
         const int ct = 4 * vb + w4;
         bf16x8 vbk[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) vbk[kk] = lds_nat(sm.a.Vt, 16 * ct + r16, 72, 32 * kk, grp);
+        for (int kk = 0; kk < 2; ++kk) vbk[kk] = lds_nat(sm.Vt(), 16 * ct + r16, 72, 32 * kk, grp);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           f32x4 acc = zero4();
@@ -779,7 +963,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
         }
       }
     }
-    lds_barrier();                              // W amax partials; X, L dead
+    lds_barrier();                              // W amax partials; K^T, V^T, T dead
     GDN_REFRESH();
     {
       float dW = 1.f, rW = 1.f;
@@ -804,17 +988,17 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
           uint32_t bytes;
           quant4<WF>(w, rW, cq, bytes);
           if (a.w_img_bytes)                      // the code bytes, same element order
-            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sm.b.W) + o) = bytes;
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sm.Wm()) + o) = bytes;
           else
-            st4(&sm.b.W[o], to_bf16(cq[0]), to_bf16(cq[1]), to_bf16(cq[2]), to_bf16(cq[3]));
+            st4(sm.Wm() + o, to_bf16(cq[0]), to_bf16(cq[1]), to_bf16(cq[2]), to_bf16(cq[3]));
           if (save && tok < nc)
             *reinterpret_cast<uint32_t*>(a.w_codes + ((int64_t)(t0 + tok) * Hv + h) * DK + dk0) = bytes;
         } else {
           bf16 hi[4], lo[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) split2(w[i], hi[i], lo[i]);
-          st4(&sm.b.W[o], hi[0], hi[1], hi[2], hi[3]);
-          st4(&sm.b.W[I::WQ + o], lo[0], lo[1], lo[2], lo[3]);
+          st4(sm.Wm() + o, hi[0], hi[1], hi[2], hi[3]);
+          st4(sm.Wm() + I::WQ + o, lo[0], lo[1], lo[2], lo[3]);
         }
       }
       if (tid == 0) {
@@ -827,7 +1011,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_prep_kernel(FwdKernelArgs a, int N,
     lds_barrier();
     GDN_REFRESH();
     {
-      const u32x4* src = reinterpret_cast<const u32x4*>(sm.b.W);
+      const u32x4* src = reinterpret_cast<const u32x4*>(sm.Wm());
       u32x4* dst = reinterpret_cast<u32x4*>(img);
       constexpr int NWP = NW * I::WQ / 8;          // 16-byte pieces of the W planes
       constexpr int NWB = I::WQ / 16;              // ... of the code bytes
@@ -875,23 +1059,48 @@ template <int DK, int DV, int WF>
 static hipError_t launch_prep_one(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
                                   hipStream_t s, hipEvent_t stop) {
   const int64_t items = a.item_hi > 0 ? (int64_t)a.item_hi - a.item_lo : (int64_t)num_slots * cfg.Hv;
-  const int64_t cap = a.prep_blocks > 0 ? a.prep_blocks : device_cus();   // one workgroup per CU
+  // The compact layout, two workgroups per CU, where it fits (Dv <= 128,
+  // exact solve), on its own and beside the state kernel with the CU
+  // admission table; else the full layout, one per CU (beside the state
+  // kernel the workgroups that end after the head then free whole CUs).
+  const bool neu = a.solve_degree > 0;
+  const bool cmp = !neu && prep_fits_two<DK, DV>() && !(a.ticket != nullptr && !a.admit);
+  const int64_t cap = a.prep_blocks > 0 ? a.prep_blocks : (cmp ? 2 : 1) * (int64_t)device_cus();
   const int64_t nblk = items < cap ? items : cap;
   if (nblk <= 0) return stop ? hipEventRecord(stop, s) : hipSuccess;
   const dim3 grid((unsigned)nblk), block(NT);
-  if (stop) {
-    if (a.solve_degree > 0)
-      hipExtLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), grid, block, 0, s, nullptr, stop, 0, a,
-                            cfg.N, num_slots);
+  auto go = [&](auto kernel) {
+    if (stop)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, s, nullptr, stop, 0, a, cfg.N, num_slots);
     else
-      hipExtLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, false>), grid, block, 0, s, nullptr, stop, 0, a,
-                            cfg.N, num_slots);
-  } else if (a.solve_degree > 0) {
-    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, true>), grid, block, 0, s, a, cfg.N, num_slots);
+      hipLaunchKernelGGL(kernel, grid, block, 0, s, a, cfg.N, num_slots);
+  };
+  if (neu) {
+    go(gdn_prep_kernel<DK, DV, WF, true, false>);
+  } else if (cmp) {
+    if constexpr (prep_fits_two<DK, DV>()) go(gdn_prep_kernel<DK, DV, WF, false, true>);
   } else {
-    hipLaunchKernelGGL((gdn_prep_kernel<DK, DV, WF, false>), grid, block, 0, s, a, cfg.N, num_slots);
+    go(gdn_prep_kernel<DK, DV, WF, false, false>);
   }
   return hipGetLastError();
+}
+
+template <int DK, int DV>
+static int prep_per_cu_dk_dv(int solve_degree) {
+  return solve_degree == 0 && prep_fits_two<DK, DV>() ? 2 : 1;
+}
+
+int prep_workgroups_per_cu(const FwdConfig& cfg, int solve_degree) {
+  if (cfg.Dk == 128) {
+    if (cfg.Dv == 64) return prep_per_cu_dk_dv<128, 64>(solve_degree);
+    if (cfg.Dv == 128) return prep_per_cu_dk_dv<128, 128>(solve_degree);
+    if (cfg.Dv == 256) return prep_per_cu_dk_dv<128, 256>(solve_degree);
+  } else if (cfg.Dk == 64) {
+    if (cfg.Dv == 64) return prep_per_cu_dk_dv<64, 64>(solve_degree);
+    if (cfg.Dv == 128) return prep_per_cu_dk_dv<64, 128>(solve_degree);
+    if (cfg.Dv == 256) return prep_per_cu_dk_dv<64, 256>(solve_degree);
+  }
+  return 1;
 }
 
 template <int DK, int DV>

@@ -43,6 +43,12 @@ struct FwdKernelArgs {
                               // workgroup), then [1] over the rest (only workgroups below
                               // prep_rest: the others end, and free their CUs)
   int32_t item_split, prep_rest;
+  // nullable: with two prep workgroups per CU, the rest is built on whole
+  // CUs: the first of a CU's workgroups to reach it admits the CU or not
+  // (prep_rest CUs in all, spread evenly over the XCCs and their shader
+  // engines), and the other follows; kAdmitWords words zeroed per call (per
+  // XCC: one slot per CU key, then the count admitted per engine)
+  uint32_t* admit;
   // packed sequences (cu_seqlens): the chunk-major order comes from a table
   // that varlen_setup_kernel builds from the lengths: [0] items, [1] the head
   // (taking the place of item_split), then per item (n Hv + head, chunk)
@@ -111,6 +117,11 @@ hipError_t launch_fwd_fused(const FwdConfig& cfg, const FwdKernelArgs& a, hipStr
 // bf16 io: prep kernel over every (chunk, head), then the state kernel.
 // stop (nullable): an event that the launch itself records at its end, with
 // no marker of its own on the stream
+constexpr int kAdmitPerXcc = 256 + 8;
+constexpr int kAdmitWords = 8 * kAdmitPerXcc;
+// Prep workgroups that can share a CU: 2 where an item's compact LDS layout
+// fits in half of it (Dv <= 128, exact solve), else 1.
+int prep_workgroups_per_cu(const FwdConfig& cfg, int solve_degree);
 hipError_t launch_fwd_prep(const FwdConfig& cfg, const FwdKernelArgs& a, int num_slots,
                            hipStream_t stream, hipEvent_t stop = nullptr);
 hipError_t launch_fwd_state(const FwdConfig& cfg, const FwdKernelArgs& a, hipStream_t stream,

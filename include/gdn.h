@@ -218,8 +218,10 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_args* a, void* stream);
  * compute units (0: the current device's count): out[0] = 1 overlapped,
  * 0 one stage after the other; out[1] the (chunk, head) items of the
  * operand build; out[2] how many of them (whole rounds of cus, chunk-major)
- * run on every CU before the state recurrence starts; out[3] the workgroups
- * that build the rest meanwhile. For packed sequences out[1] and out[2] are
+ * run on every CU before the state recurrence starts; out[3] the CUs that
+ * build the rest meanwhile (with a head and Dv <= 128, two operand-build
+ * workgroups on each, on CUs picked on the device so that the recurrence's
+ * workgroups find free CUs on every shader engine; else one workgroup each). For packed sequences out[1] and out[2] are
  * -1: the device derives them from the sequence lengths. Checks the shapes only; launches nothing.
  * The call itself runs one stage after the other if it cannot create its
  * second stream. */

@@ -95,14 +95,15 @@ def test_forward_schedule_host_logic():
     is items - R * chunks / r in whole rounds of CUs, R = CUs - the state
     workgroups (N Hv Dv / 64, or Dv / block_v per head for 128- and 256-wide
     tiles), r = 3.7 for the split state kernel (both QDQ sites on, tiles up
-    to 64 wide) and 1.75 for the general one; numbers worked by hand here."""
+    to 64 wide; 3.0 where two prep workgroups share a CU: Dv <= 128 with the
+    exact solve) and 1.75 for the general one; numbers worked by hand here."""
     big = dict(B=4, T=4096, Hqk=16, Hv=16, num_seqs=4)
     sch = B.fwd_schedule(_args(**big), 256)
     # 64 chunks x 64 (sequence, head) pairs; 128 state workgroups leave R = 128;
-    # 4096 - 128 * 64 / 3.7 = 1881.9 -> 7 rounds of 256
-    assert sch == dict(overlapped=True, items=4096, head_items=1792, rest_blocks=128)
-    # 304 CUs: R = 176; 4096 - 176 * 64 / 3.7 = 1051.7 -> 3 rounds of 304
-    assert B.fwd_schedule(_args(**big), 304) == dict(overlapped=True, items=4096, head_items=912,
+    # 4096 - 128 * 64 / 3.0 = 1365.3 -> 5 rounds of 256
+    assert sch == dict(overlapped=True, items=4096, head_items=1280, rest_blocks=128)
+    # 304 CUs: R = 176; 4096 - 176 * 64 / 3.0 = 341.3 -> 1 round of 304
+    assert B.fwd_schedule(_args(**big), 304) == dict(overlapped=True, items=4096, head_items=304,
                                                       rest_blocks=176)
     # a long sequence: the remainder alone outlasts the chain, so no head
     sch = B.fwd_schedule(_args(B=1, T=65536, Hqk=32, Hv=32, Dv=256, num_seqs=1), 256)
@@ -172,9 +173,11 @@ def test_forward_workspace_is_sized_and_required():
     n = lib.gdn_fwd_workspace_bytes(ctypes.byref(a))
     slots = 1 + 2                                       # N + ceil(128 / 64)
     # W codes, K^T, P hi/lo (bf16, K^T and P rows unpadded), gate block (1 KB), U (FP32), W
-    # scale, the ready flag of the overlapped schedule
+    # scale, the ready flag of the overlapped schedule; once per call the two item counters
+    # and the CU admission table (8 x 264 words)
     per = 64 * 128 * 2 + 128 * 64 * 2 + 2 * 64 * 64 * 2 + 1024 + 128 * 64 * 4 + 4 + 4
-    assert n >= slots * 4 * per and n <= slots * 4 * per + 4 * 256
+    fixed = 8 + 8 * 264 * 4
+    assert n >= slots * 4 * per + fixed and n <= slots * 4 * per + fixed + 5 * 256
     assert lib.gdn_chunk_fwd(ctypes.byref(a), None) == B.GDN_E_WORKSPACE
     assert 'workspace' in lib.gdn_last_error().decode()
     a.workspace = ctypes.c_void_p(0x40000)
