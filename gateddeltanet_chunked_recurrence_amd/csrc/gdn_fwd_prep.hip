@@ -58,8 +58,15 @@ constexpr float LOG2E = 1.4426950408889634f;
 //   a: K and Q rows (phase 1 to the L / P tiles), then K^T and V^T (written
 //      in the solve phase, read by W and U), then the W image planes;
 //   l: L (until the 32-block merge), then the T' hi / lo planes;
-//   x: X = (I + L)^-1 (until T is formed), then the T hi / lo planes.
-// P leaves for the image straight from the tiles' accumulators.
+//   x: the P planes (the tile phase; copied out at the start of the solve),
+//      X = (I + L)^-1 (written from the 16-block merges on), then the T hi /
+//      lo planes;
+//   Y: the diagonal 16x16 blocks of X (the solve phase and the 16-block
+//      merges), then the 32-block merge's scratch.
+// Offset between the diagonal 16x16 blocks of X that the compact layout keeps
+// in Y (row stride 16): four of them fill Y's 32 x 33 floats.
+constexpr int kDiagY = 264;
+
 template <int DK, int DV>
 struct PrepSmemTwo {
   static constexpr bool TWO = true;
@@ -72,12 +79,14 @@ struct PrepSmemTwo {
   } a;
   union { float L[64 * LS]; bf16 T[2][64 * 64]; } l;      // L; T' hi / lo (r64_off)
   union { float X[64 * LS]; bf16 T[2][64 * 64]; } x;      // X; T hi / lo (r64_off)
-  float Y[32 * 33];                              // 32-block merge scratch
+  float Y[32 * 33];                              // X's diagonal blocks, then 32-block merge scratch
+  static_assert(4 * kDiagY <= 32 * 33, "diagonal blocks of X in Y");
   alignas(16) float Ld[4][16 * 16];              // diagonal 16x16 blocks of L, row-major
   alignas(16) float gam2[64];                    // log2-scaled gamma
   alignas(16) float bet[64];
   alignas(16) float eg[64];                      // exp(gamma)
   alignas(16) float red[NWAVE];
+  __device__ bf16* Pl(int i) { return reinterpret_cast<bf16*>(x.X) + i * 64 * 64; }
   __device__ bf16* Kt() { return a.tv.Kt; }
   __device__ bf16* Vt() { return a.tv.Vt; }
   __device__ float* Lm() { return l.L; }
@@ -119,6 +128,7 @@ struct PrepSmemOne {
   alignas(16) float bet[64];
   alignas(16) float eg[64];
   alignas(16) float red[NWAVE];
+  __device__ bf16* Pl(int i) { return c.P[i]; }
   __device__ bf16* Kt() { return Kt_; }
   __device__ bf16* Vt() { return a.Vt; }
   __device__ float* Lm() { return b.s.L; }
@@ -499,14 +509,11 @@ gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
 
     // ---- 1. K, Q rows (pperm over dk) and gates from registers (the full
     // layout: K^T too). P upper tiles (0, 1) and (2, 3), which the state
-    // kernel reads as zeros, are zeroed: in the image (compact layout; one
-    // plane in the byte variant) or in the LDS P tile
+    // kernel reads as zeros, are zeroed in the LDS P planes
     if constexpr (Sm::TWO) {
-      const bool coh = a.flags != nullptr;
       const int pl = tid >> 7, e = tid & 127, t = e >> 6, r = (e >> 2) & 15, g = e & 3;
       if (tid < (a.w_img_bytes ? 128 : 256))
-        st_out8(img, 2 * (I::template p_at<NW>() + pl * I::P1 + r64_off(32 * t + r, pperm(32 * t + 16 + 4 * g))),
-                u32x2{0u, 0u}, coh);
+        *reinterpret_cast<u32x2*>(sm.Pl(pl) + r64_off(32 * t + r, pperm(32 * t + 16 + 4 * g))) = u32x2{0u, 0u};
     } else {
 #pragma unroll
       for (int k = 0; k < 2 * 2 * 256 / NT; ++k) {
@@ -596,15 +603,9 @@ gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = row >= c0 + i ? acc[i] * fexp2(gr1 - gc[i]) : 0.f;
-        // straight to the image (8 bytes per lane and plane) in the compact
-        // layout, else to the LDS tile, copied out during the solve
-        const int po = 2 * (I::template p_at<NW>() + r64_off(row, pperm(c0)));
-        const bool coh = a.flags != nullptr;
+        // to the LDS P planes, copied out during the solve
         auto put = [&](int plane, u32x2 v) {
-          if constexpr (Sm::TWO)
-            st_out8(img, po + 2 * plane * I::P1, v, coh);
-          else
-            *reinterpret_cast<u32x2*>(&sm.c.P[plane][r64_off(row, pperm(c0))]) = v;
+          *reinterpret_cast<u32x2*>(sm.Pl(plane) + r64_off(row, pperm(c0))) = v;
         };
         if (a.w_img_bytes) {
           // one fp16 plane (11-bit significand: relative error <= 2^-12). Its
@@ -629,9 +630,10 @@ gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
     lds_barrier();
     GDN_REFRESH();
 
-    // ---- 3. wave 0: diagonal blocks of X; others: X upper zero, V^T in, and
-    // (full layout) the K^T and P images out; in the compact layout every
-    // wave writes its part of K^T (the K, Q rows are dead)
+    // ---- 3. wave 0: diagonal blocks of X; others: V^T in, the P image out,
+    // and (full layout) X's upper blocks zero and the K^T image out; in the
+    // compact layout every wave writes its part of K^T (the K, Q rows are
+    // dead) and the diagonal blocks go to Y (the P planes are in X's place)
     // (the approximate-inverse instantiation skips the solve's arithmetic here
     // and in the merges below, keeping their loads and barriers: X is formed
     // from L after this phase)
@@ -668,8 +670,15 @@ gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
         }
         x[r] = s;
       }
+      // (compact layout: to Y, as the P planes in X's place are being copied
+      // out; X gets them in the 16-block merge phase)
+      if constexpr (Sm::TWO) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Xm()[(16 * b + r) * LS + 16 * b + cc] = x[r];
+        for (int r = 0; r < 16; ++r) sm.Ym()[kDiagY * b + 16 * r + cc] = x[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.Xm()[(16 * b + r) * LS + 16 * b + cc] = x[r];
+      }
       }
     } else {
       const int t = tid - 64;
@@ -689,12 +698,27 @@ gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
           const int e = t + (NT - 64) * k;
           if (e < nkp) st_out16(kdst, 16 * e, e < I::KT / 8 ? ksrc[e] : psrc[e - I::KT / 8], coh);
         }
+      } else {
+        // P image: 16-byte copies of the LDS planes (one plane in the byte
+        // variant, whose second slot holds the gate block); then, once all
+        // seven waves have read theirs, X's upper blocks go over them
+        constexpr int NPC = 2 * I::P1 / 8, NCP = (NPC + NT - 65) / (NT - 64);
+        const int npc = a.w_img_bytes ? I::P1 / 8 : NPC;
+        const u32x4* psrc = reinterpret_cast<const u32x4*>(sm.Pl(0));
+        const bool coh = a.flags != nullptr;
+#pragma unroll
+        for (int k = 0; k < NCP; ++k) {
+          const int e = t + (NT - 64) * k;
+          if (e < npc) st_out16(img + I::template p_at<NW>(), 16 * e, psrc[e], coh);
+        }
       }
-      for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
-        const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        sm.Xm()[(16 * bi + r) * LS + 16 * bj + cc] = 0.f;
+      if constexpr (!Sm::TWO) {
+        for (int e = t; e < 6 * 256; e += NT - 64) {  // upper blocks (bi < bj) of X
+          const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+          const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+          const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+          sm.Xm()[(16 * bi + r) * LS + 16 * bj + cc] = 0.f;
+        }
       }
       vs.store_t(sm.Vt(), nullptr, wave, lane);   // V^T for U
     }
@@ -711,19 +735,35 @@ gdn_prep_kernel(FwdKernelArgs a, int N, int num_slots) {
     if (merger) {
       if constexpr (!NEU) {
         const int A = 2 * (wave - 1), B = A + 1;
-        const f32x4 y = mm32(&sm.Lm()[(16 * B) * LS + 16 * A], LS, &sm.Xm()[(16 * A) * LS + 16 * A],
-                             LS, 0, 0, 0, 16, r16, grp, zero4());
+        // the diagonal blocks X_AA, X_BB: in Y (row stride 16) in the compact
+        // layout, in X otherwise
+        const float* xaa = Sm::TWO ? &sm.Ym()[kDiagY * A] : &sm.Xm()[(16 * A) * LS + 16 * A];
+        const float* xbb = Sm::TWO ? &sm.Ym()[kDiagY * B] : &sm.Xm()[(16 * B) * LS + 16 * B];
+        const int xs = Sm::TWO ? 16 : LS;
+        const f32x4 y = mm32(&sm.Lm()[(16 * B) * LS + 16 * A], LS, xaa, xs, 0, 0, 0, 16, r16, grp, zero4());
         f32x4 z = zero4();
 #pragma unroll
         for (int i = 0; i < 4; ++i)               // K order 4 grp + i
-          z = mfma_f32(sm.Xm()[(16 * B + r16) * LS + 16 * B + 4 * grp + i], y[i], z);
+          z = mfma_f32(xbb[r16 * xs + 4 * grp + i], y[i], z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.Xm()[(16 * B + 4 * grp + i) * LS + 16 * A + r16] = -z[i];
       }
       if (nxt.valid) load_kqg(nxt);
     } else if constexpr (Sm::TWO) {
-      // K^T image: 16-byte copies of the LDS tile by the six other waves
-      const int t = wave == 0 ? lane : tid - 128;
+      const int t = wave == 0 ? lane : tid - 128;   // the six other waves
+      // X: its diagonal blocks from Y, its upper blocks (bi < bj) zero
+      for (int e = t; e < 10 * 256; e += 384) {
+        const int blk = e >> 8, r = (e >> 4) & 15, cc = e & 15;
+        if (blk < 4) {
+          sm.Xm()[(16 * blk + r) * LS + 16 * blk + cc] = sm.Ym()[kDiagY * blk + 16 * r + cc];
+        } else {
+          const int u = blk - 4;
+          const int bi = u < 3 ? 0 : (u < 5 ? 1 : 2);
+          const int bj = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+          sm.Xm()[(16 * bi + r) * LS + 16 * bj + cc] = 0.f;
+        }
+      }
+      // K^T image: 16-byte copies of the LDS tile
       constexpr int NKT = I::KT / 8, NCK = (NKT + 383) / 384;
       const u32x4* ksrc = reinterpret_cast<const u32x4*>(sm.Kt());
       const bool coh = a.flags != nullptr;
