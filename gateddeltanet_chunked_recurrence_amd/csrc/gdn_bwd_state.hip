@@ -68,12 +68,19 @@ struct ImgSmem {
   static constexpr int LDO = DV + 8;
   static constexpr int QB = 64 * LD * 2;           // bytes of the Q rows
   static constexpr int OB = 2 * (DV / 16) * 64 * 16;   // bytes of the dO operands
-  bf16 Kn[64 * LD];
-  union {                                          // Q rows, then the dO operands
-    bf16 Qn[64 * LD];
-    bf16x8 dOB[2 * (DV / 16) * 64];                // [kk][value tile][lane]
-    char raw[QB > OB ? QB : OB];
-  } u;
+  union {
+    struct {
+      bf16 Kn[64 * LD];
+      union {                                      // Q rows, then the dO operands
+        bf16 Qn[64 * LD];
+        bf16x8 dOB[2 * (DV / 16) * 64];            // [kk][value tile][lane]
+        char raw[QB > OB ? QB : OB];
+      } u;
+    };
+    // one W^T image plane [DK][72], staged once K's image copy and the
+    // products are done with K and the dO operands (one W plane only)
+    bf16 wt[NW == 1 ? DK * 72 : 8];
+  };
   bf16 Wn[NW][64 * LD];                            // W codes, or W hi and lo
   bf16 dOn[64 * LDO];
   float gam2[64], eg[64];
@@ -299,13 +306,31 @@ __global__ void __launch_bounds__(NT, 2) bwd_img_kernel(BwdKernelArgs a, int N) 
     const uint2 hi = *reinterpret_cast<const uint2*>(&sm.Kn[row * LD + 32 * b + 16 + 4 * g4]);
     st_out16(img, 2 * (row * I::RS + ((cs ^ (row & I::SWZ)) << 3)), u32x4{lo.x, lo.y, hi.x, hi.y}, coh);
   }
-  // ---- W^T image: dk rows, tokens paired along the row
-  for (int fi = wave; fi < 2 * MK; fi += 4) {
-    const int dt = fi >> 1, kk = fi & 1;
+  // ---- W^T image: dk rows, tokens paired along the row. With one W plane it
+  // is staged in LDS in the image's own layout and copied out as whole
+  // 16-byte pieces (a wave's store covers whole lines; the fragments alone
+  // cover 64 of a row's 144 bytes, which beside the reverse recurrence costs
+  // more as device-scope write-through stores)
+  if constexpr (NW == 1) {
+    static_assert(DK * 72 * 2 <= sizeof(sm.Kn) + sizeof(sm.u) && I::R64 == 72, "W^T staging");
+    __syncthreads();                               // K and the dO operands are dead
+    for (int fi = wave; fi < 2 * MK; fi += 4) {
+      const int dt = fi >> 1, kk = fi & 1;
+      *reinterpret_cast<bf16x8*>(&sm.wt[(16 * dt + r16) * I::R64 + 32 * kk + 8 * grp]) =
+          lds_col8(sm.Wn[0], LD, 32 * kk, 16 * dt, r16, grp);
+    }
+    __syncthreads();
+    constexpr int NPW = BI::WT / 8;                // 16-byte pieces of the plane
+    const u32x4* src = reinterpret_cast<const u32x4*>(sm.wt);
+    for (int e = tid; e < NPW; e += NT) st_out16(img, 2 * BI::KI + 16 * e, src[e], coh);
+  } else {
+    for (int fi = wave; fi < 2 * MK; fi += 4) {
+      const int dt = fi >> 1, kk = fi & 1;
 #pragma unroll
-    for (int pl = 0; pl < NW; ++pl) {
-      st_out16(img, 2 * (BI::KI + pl * BI::WT + (16 * dt + r16) * I::R64 + 32 * kk + 8 * grp),
-               __builtin_bit_cast(u32x4, lds_col8(sm.Wn[pl], LD, 32 * kk, 16 * dt, r16, grp)), coh);
+      for (int pl = 0; pl < NW; ++pl) {
+        st_out16(img, 2 * (BI::KI + pl * BI::WT + (16 * dt + r16) * I::R64 + 32 * kk + 8 * grp),
+                 __builtin_bit_cast(u32x4, lds_col8(sm.Wn[pl], LD, 32 * kk, 16 * dt, r16, grp)), coh);
+      }
     }
   }
   if (coh) {
